@@ -1,0 +1,325 @@
+"""Pins of the oracle's drafter forward and its number formats.
+
+Each pin rests on something other than the oracle's own formula: closed forms,
+a library routine (torch's float32 -> bfloat16 conversion), an independently
+written token-by-token EAGLE step, and invariants the pages fix (K=1 is one
+EAGLE step; t_1 does not depend on K; rejected slots write no KV; MASK slots
+carry emb(mask) and h_shared)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from drafting_pe_prepare_amd import configs, synth
+
+
+# --------------------------------------------------------------------------
+# number formats and closed forms
+# --------------------------------------------------------------------------
+def test_round_bf16_known_values():
+    u = 2.0 ** -8
+    cases = {
+        1.0: 1.0,
+        1 + u: 1.0,                      # tie -> even (mantissa 0)
+        1 + 3 * u: 1 + 4 * u,            # tie -> even (mantissa 2)
+        1 + u + 2.0 ** -30: 1 + 2 * u,   # just above the tie
+        2 - 2.0 ** -9: 2.0,              # carry into the exponent
+        -(1 + 3 * u): -(1 + 4 * u),
+        0.0: 0.0,
+        3.0e-30: 3.0e-30,                # exactly representable? checked below
+    }
+    for x, want in list(cases.items())[:-1]:
+        assert O.round_bf16(np.array([x]))[0] == want, x
+
+
+def test_round_bf16_matches_torch_on_float32_values():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    # include exact ties
+    x[:1000] = (np.arange(1000, dtype=np.float32) * 2 + 1) * np.float32(2.0 ** -8) + 1
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_widen_bf16_bits():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x4049], np.uint16)
+    np.testing.assert_array_equal(O.widen(bits), [1.0, -2.0, 0.0, 3.140625])
+
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 64)) * 3
+    eps = 1e-5
+    y = O.rmsnorm(x, np.ones(64), eps)
+    ms = (x * x).mean(1)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(1)), np.sqrt(ms / (ms + eps)), rtol=1e-12)
+    g = rng.standard_normal(64)
+    np.testing.assert_allclose(O.rmsnorm(x, g, eps), y * g, rtol=1e-12)
+    np.testing.assert_allclose(O.rmsnorm(7 * x, np.ones(64), 0.0), O.rmsnorm(x, np.ones(64), 0.0), rtol=1e-12)
+
+
+def test_rope_closed_forms():
+    rng = np.random.default_rng(2)
+    # hd = 2: (1, 0) at position p turns into (cos p, sin p)
+    for p in [0, 1, 5, 1000]:
+        np.testing.assert_allclose(O.rope(np.array([[[1.0, 0.0]]]), [p], 10000.0)[0, 0],
+                                   [np.cos(p), np.sin(p)], atol=1e-12)
+    # hd = 4: dims (0,2) turn at rate 1, dims (1,3) at rate theta^(-1/2)
+    th = 10000.0
+    out = O.rope(np.array([[[0.0, 1.0, 0.0, 0.0]]]), [3], th)[0, 0]
+    np.testing.assert_allclose(out, [0, np.cos(3 / 100), 0, np.sin(3 / 100)], atol=1e-12)
+    x = rng.standard_normal((4, 3, 64))
+    np.testing.assert_allclose(O.rope(x, [0, 0, 0, 0], th), x)
+    y = O.rope(x, [7, 90, 4000, 16383], th)
+    np.testing.assert_allclose(np.linalg.norm(y[..., :32] ** 2 + y[..., 32:] ** 2, axis=-1),
+                               np.linalg.norm(x[..., :32] ** 2 + x[..., 32:] ** 2, axis=-1), rtol=1e-10)
+    # relative position: <rope(q, p1), rope(k, p2)> depends on p1 - p2 only
+    q, k = rng.standard_normal((1, 1, 64)), rng.standard_normal((1, 1, 64))
+    d1 = (O.rope(q, [50], th) * O.rope(k, [20], th)).sum()
+    d2 = (O.rope(q, [1030], th) * O.rope(k, [1000], th)).sum()
+    assert abs(d1 - d2) < 1e-9
+
+
+def test_attend_closed_forms():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((1, 64))
+    np.testing.assert_allclose(O.attend(rng.standard_normal(64), rng.standard_normal((1, 64)), v), v[0])
+    keys = np.tile(rng.standard_normal(64), (9, 1))
+    vals = rng.standard_normal((9, 64))
+    np.testing.assert_allclose(O.attend(rng.standard_normal(64), keys, vals), vals.mean(0), atol=1e-12)
+    # scores ln 3 and 0 give weights 3/4 and 1/4 (scale 1/sqrt(hd) = 1/8)
+    q = np.zeros(64)
+    q[0] = 8 * np.log(3.0)
+    keys = np.zeros((2, 64))
+    keys[0, 0] = 1.0
+    vals = np.array([[1.0] + [0.0] * 63, [0.0, 1.0] + [0.0] * 62])
+    np.testing.assert_allclose(O.attend(q, keys, vals)[:2], [0.75, 0.25], atol=1e-12)
+
+
+def test_silu_closed_forms():
+    x = np.linspace(-30, 30, 101)
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, atol=1e-12)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(O.silu(np.array([2.0])), [2.0 / (1 + np.exp(-2.0))])
+
+
+# --------------------------------------------------------------------------
+# whole-forward pins on small shapes
+# --------------------------------------------------------------------------
+SMALL = configs.TINY.with_(d=128, mlp=256, vocab=512, dtype="bf16", weight_std=1 / 11.3,
+                           prefix=("fixed", 37, 0))
+
+
+def _case(w, a=None, seed=None):
+    prm = synth.weights(w, seed)
+    inp = synth.step_inputs(w, seed)
+    if a is not None:
+        inp["num_accepted"][:] = a
+    b = O.prepare(inp["verify_tokens"], inp["verify_positions"], inp["num_accepted"],
+                  inp["bonus_tokens"], inp["block_table"], inp["num_kv_blocks"],
+                  w.K, w.vocab, w.mask_id, w.block_size)
+    hd = O.gather_hidden(b["hidden_src"], inp["target_hidden"], prm["h_shared"])
+    return prm, inp, b, hd
+
+
+def _prefix_kv(w, inp, r):
+    p0 = int(inp["verify_positions"][r, 0])
+    slots = np.array([O.slot_of(inp["block_table"][r], p, w.block_size) for p in range(p0)])
+    ks, vs = [], []
+    for kc, vc in inp["kv"]:
+        ks.append(O.widen(kc[slots]))
+        vs.append(O.widen(vc[slots // w.block_size, :, :, slots % w.block_size]))
+    return ks, vs
+
+
+@pytest.mark.parametrize("precision", ["f64", "bf16"])
+@pytest.mark.parametrize("a", [0, 1])
+def test_k1_is_one_eagle_step(precision, a):
+    """With K=1 the draft batch is two copied slots and no MASK slot; its
+    output must equal one ordinary EAGLE drafter pass over the accepted
+    tokens and the bonus token (written token by token, without slots)."""
+    w = SMALL.with_(K=1)
+    prm, inp, b, hd = _case(w, a=a)
+    out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], precision)
+    ks, vs = _prefix_kv(w, inp, 0)
+    toks = list(inp["verify_tokens"][0, 1:a + 1]) + [inp["bonus_tokens"][0]]
+    hid = inp["target_hidden"][:a + 1]
+    ar = O.eagle_step(prm, w, ks, vs, toks, hid, int(inp["verify_positions"][0, 0]), precision)
+    np.testing.assert_allclose(out["logits"][0], ar[-1], rtol=0, atol=1e-9 * np.abs(ar).max())
+    assert out["tokens"][0] == np.argmax(ar[-1])
+
+
+@pytest.mark.parametrize("precision", ["f64", "bf16"])
+def test_t1_is_the_autoregressive_first_pass(precision):
+    """t_1 comes from the NTP slot; causally it sees only the prefix and the
+    accepted slots, so it equals the first pass of AR drafting."""
+    w = SMALL.with_(K=4, batch=2, accepted="uniform")
+    prm, inp, b, hd = _case(w, seed=77)
+    out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], precision)
+    for r in range(2):
+        a = int(inp["num_accepted"][r])
+        ks, vs = _prefix_kv(w, inp, r)
+        toks = list(inp["verify_tokens"][r, 1:a + 1]) + [inp["bonus_tokens"][r]]
+        hid = inp["target_hidden"][r * 5:r * 5 + a + 1]
+        ar = O.eagle_step(prm, w, ks, vs, toks, hid, int(inp["verify_positions"][r, 0]), precision)
+        np.testing.assert_allclose(out["logits"][r * 4], ar[-1], atol=1e-9 * np.abs(ar).max())
+
+
+def test_t1_does_not_depend_on_K():
+    base = SMALL.with_(K=2)
+    prm = synth.weights(base)
+    logits = []
+    for K in (2, 3, 6):
+        w = base.with_(K=K)
+        inp = synth.step_inputs(w, seed=base.seed)
+        # identical accepted prefix, bonus and hidden rows 0..a for every K
+        inp["verify_tokens"][0, :3] = [5, 6, 7]
+        inp["num_accepted"][:] = 2
+        inp["bonus_tokens"][:] = 9
+        inp["target_hidden"][:3] = synth.normal(1, "h3", (3, w.d))
+        b = O.prepare(inp["verify_tokens"], inp["verify_positions"], inp["num_accepted"],
+                      inp["bonus_tokens"], inp["block_table"], inp["num_kv_blocks"],
+                      w.K, w.vocab, w.mask_id, w.block_size)
+        hd = O.gather_hidden(b["hidden_src"], inp["target_hidden"], prm["h_shared"])
+        # the prefix pool must hold the same values: rebuild it by position
+        kv0 = synth.kv_pool(base, 64, 5)
+        kc, vc = inp["kv"][0]
+        for p in range(37):
+            s = O.slot_of(inp["block_table"][0], p, 16)
+            kc[s] = kv0[0][0][p]
+            vc[s // 16, :, :, s % 16] = kv0[0][1][p // 16, :, :, p % 16]
+        logits.append(O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")["logits"][0])
+    np.testing.assert_allclose(logits[0], logits[1], atol=1e-9)
+    np.testing.assert_allclose(logits[0], logits[2], atol=1e-9)
+
+
+def test_kv_writes_exactly_the_valid_positions():
+    """Rejected slots never write; every position in [p0, p0+a+K) is written
+    once, and a position shared by a rejected slot and a MASK slot holds the
+    MASK slot's K/V."""
+    w = SMALL.with_(K=5, batch=3, accepted="uniform")
+    prm, inp, b, hd = _case(w, seed=11)
+    out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")
+    slots, krows, vrows = out["kv_writes"][0]
+    want = []
+    for r in range(3):
+        p0, a = int(inp["verify_positions"][r, 0]), int(inp["num_accepted"][r])
+        want += [O.slot_of(inp["block_table"][r], p, 16) for p in range(p0, p0 + a + w.K)]
+    assert sorted(slots.tolist()) == sorted(want)
+    assert len(set(slots.tolist())) == len(slots)
+    # no written slot belongs to a rejected slot of the batch
+    rej_pos = set()
+    for s in np.nonzero(b["is_rejected"])[0]:
+        r = s // w.slots
+        rej_pos.add((r, int(b["positions"][s])))
+    for r, p in rej_pos:
+        s_k = O.slot_of(inp["block_table"][r], p, 16)
+        if p >= b["seq_lens"][r]:
+            assert s_k not in slots
+
+
+def test_mask_slots_share_emb_mask_and_h_shared():
+    """All MASK slots of a request have the same input (emb(mask), h_shared),
+    so their layer-1 V rows are equal and their K rows are equal once the
+    position rotation is undone."""
+    w = SMALL.with_(K=6, batch=2, accepted="uniform")
+    prm, inp, b, hd = _case(w, seed=12)
+    out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "f64")
+    slots, krows, vrows = out["kv_writes"][0]
+    by_slot = {int(s): i for i, s in enumerate(slots)}
+    for r in range(2):
+        idx = [by_slot[int(b["slot_mapping"][r * w.slots + w.K + m])] for m in range(1, w.K)]
+        pos = [int(b["positions"][r * w.slots + w.K + m]) for m in range(1, w.K)]
+        for i in idx[1:]:
+            np.testing.assert_allclose(vrows[i], vrows[idx[0]], atol=1e-12)
+        unrot = [O.rope(krows[i][None], [-p], w.rope_theta)[0] for i, p in zip(idx, pos)]
+        for u in unrot[1:]:
+            np.testing.assert_allclose(u, unrot[0], atol=1e-9)
+    # and the embedding row used is the MASK id's
+    assert np.all(b["input_ids"][b["is_masked"] == 1] == w.mask_id)
+
+
+def test_paging_is_invisible():
+    """The same logical cache under two block tables gives the same logits."""
+    w = SMALL.with_(K=3, batch=2, accepted="uniform")
+    prm, inp, b, hd = _case(w, seed=13)
+    out1 = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")
+    bt2 = inp["block_table"].copy()
+    nb = inp["num_kv_blocks"]
+    perm = np.random.default_rng(9).permutation(nb)
+    bt2 = perm[bt2]
+    kv2 = []
+    for kc, vc in inp["kv"]:
+        kc2 = np.empty_like(kc)
+        vc2 = np.empty_like(vc)
+        for blk in range(nb):
+            kc2[perm[blk] * 16:(perm[blk] + 1) * 16] = kc[blk * 16:(blk + 1) * 16]
+            vc2[perm[blk]] = vc[blk]
+        kv2.append((kc2, vc2))
+    b2 = O.prepare(inp["verify_tokens"], inp["verify_positions"], inp["num_accepted"],
+                   inp["bonus_tokens"], bt2, nb, w.K, w.vocab, w.mask_id, 16)
+    out2 = O.draft_forward(prm, w, b2, hd, kv2, bt2, "bf16")
+    np.testing.assert_array_equal(out1["logits"], out2["logits"])
+
+
+def test_concat_order_embedding_first():
+    """fc reads [emb; hidden]: with the hidden half of W_fc zeroed the output
+    ignores the hidden states, with the embedding half zeroed it ignores the
+    tokens."""
+    w = SMALL.with_(K=2)
+    prm, inp, b, hd = _case(w, a=2)
+    d = w.d
+    wfc = prm["w_fc"].copy()
+    prm_e = dict(prm, w_fc=np.where(np.arange(2 * d)[None, :] < d, wfc, 0).astype(wfc.dtype))
+    prm_h = dict(prm, w_fc=np.where(np.arange(2 * d)[None, :] >= d, wfc, 0).astype(wfc.dtype))
+    hd2 = synth.normal(3, "other", hd.shape)
+    b2 = dict(b, input_ids=(b["input_ids"] + 1) % (w.vocab - 1))
+    run = lambda p, bb, h: O.draft_forward(p, w, bb, h, inp["kv"], inp["block_table"], "f64")["logits"]
+    np.testing.assert_array_equal(run(prm_e, b, hd), run(prm_e, b, hd2))
+    assert not np.allclose(run(prm_e, b, hd), run(prm_e, b2, hd))
+    np.testing.assert_array_equal(run(prm_h, b, hd), run(prm_h, b2, hd))
+    assert not np.allclose(run(prm_h, b, hd), run(prm_h, b, hd2))
+
+
+def test_layers_are_residual():
+    """With Wo and W_down zeroed every decoder layer is the identity on the
+    residual stream, so the logits are W_lm RMSNorm(W_fc [emb; hidden])."""
+    w = SMALL.with_(K=2)
+    prm, inp, b, hd = _case(w, a=1)
+    lay = [dict(l, wo=np.zeros_like(l["wo"]), w_down=np.zeros_like(l["w_down"])) for l in prm["layers"]]
+    prm0 = dict(prm, layers=lay)
+    out = O.draft_forward(prm0, w, b, hd, inp["kv"], inp["block_table"], "f64")
+    rows = b["draft_rows"]
+    wide = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    E = wide(prm["embed"][b["input_ids"][rows]])
+    H = wide(hd[rows])
+    x = np.concatenate([E, H], 1) @ wide(prm["w_fc"]).T
+    g = wide(prm["final_norm"])
+    z = x / np.sqrt((x * x).mean(1, keepdims=True) + w.rms_eps) * g
+    np.testing.assert_allclose(out["logits"], z @ wide(prm["lm_head"]).T, rtol=1e-10, atol=1e-10)
+
+
+def test_argmax_lowest_index_on_ties():
+    w = SMALL.with_(K=2)
+    prm, inp, b, hd = _case(w, a=0)
+    lm = np.zeros_like(prm["lm_head"])
+    row = prm["lm_head"][5]
+    neg = synth.bf16_bits(-synth.bf16_to_f32(row))
+    lm[:] = neg
+    lm[3] = row
+    lm[7] = row
+    out = O.draft_forward(dict(prm, lm_head=lm), w, b, hd, inp["kv"], inp["block_table"], "bf16")
+    for i in range(len(out["tokens"])):
+        lg = out["logits"][i]
+        assert lg[3] == lg[7]
+        assert out["tokens"][i] == (3 if lg[3] > 0 else 0)
+
+
+def test_bf16_mode_is_close_to_f64():
+    w = SMALL.with_(K=4, batch=2, accepted="uniform")
+    prm, inp, b, hd = _case(w, seed=21)
+    l64 = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "f64")["logits"]
+    l16 = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")["logits"]
+    rel = np.abs(l64 - l16).max() / np.sqrt((l64 ** 2).mean())
+    assert 1e-4 < rel < 5e-2
