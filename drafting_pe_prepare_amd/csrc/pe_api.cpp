@@ -1,0 +1,510 @@
+// Host runtime of libpe: the C ABI declared in include/pe.h.
+//
+// A context owns the workspace of one drafter (activations sized for
+// max_num_seqs requests, split-KV attention partials, argmax keys, the device
+// error word) and at most one captured step graph.  Every entry point
+// validates its arguments on the host, then only enqueues kernels on the
+// context's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pe.h"
+#include "pe_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pe_status fail(pe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pe_status fail(pe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+pe_status hipfail(hipError_t e, const char* what) {
+  return fail(PE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define PE_HIP(call, what)                        \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hipfail(e_, what); \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+struct pe_ctx {
+  pe_config cfg;
+  pe_weights w;
+  std::vector<pe_layer_weights> layers;
+  hipStream_t stream = nullptr;
+  int device = 0;
+  int num_cus = 256;
+  size_t esz = 2;
+  // workspace
+  void* x = nullptr;     // [R, d]   residual stream
+  void* u = nullptr;     // [R, d]   normalised rows
+  void* q = nullptr;     // [R, Hq*hd] rotated queries
+  void* attn = nullptr;  // [R, Hq*hd] attention output
+  void* mlp = nullptr;   // [R, I]   SiLU(gate) * up
+  void* z = nullptr;     // [D, d]   final-norm draft rows
+  uint64_t* keys = nullptr;   // [D] argmax keys (kept zero between launches)
+  uint32_t* counter = nullptr;
+  uint32_t* err = nullptr;    // [2] kinds, first request
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  float* rope_inv = nullptr;
+  double* rope_inv_d = nullptr;
+  int target_items = 1024;
+  long long items_max = 0;
+  // step graph
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  hipStream_t capture_stream = nullptr;  // private: the default stream cannot be captured
+  int graph_B = -1;
+  pe_step_args graph_args;
+  std::vector<void*> graph_kv;
+};
+
+namespace {
+
+void free_ctx(pe_ctx* c) {
+  if (!c) return;
+  if (c->gexec) (void)hipGraphExecDestroy(c->gexec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->capture_stream) (void)hipStreamDestroy(c->capture_stream);
+  void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->counter, c->err,
+                  c->part_o, c->part_ml, c->rope_inv, c->rope_inv_d};
+  for (void* p : bufs)
+    if (p) (void)hipFree(p);
+  delete c;
+}
+
+pe_status check_cfg(const pe_config* c) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->dtype != PE_F32 && c->dtype != PE_BF16) return fail(PE_ERR_INVALID_ARG, "dtype %d", c->dtype);
+  if (c->K < 1 || c->K > 32) return fail(PE_ERR_INVALID_ARG, "K=%d outside [1,32]", c->K);
+  if (c->max_num_seqs < 1 || c->max_num_seqs > 1024)
+    return fail(PE_ERR_INVALID_ARG, "max_num_seqs=%d outside [1,1024]", c->max_num_seqs);
+  if (c->d < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 || c->mlp < 1 ||
+      c->layers < 1 || c->vocab < 1 || c->block_size < 1)
+    return fail(PE_ERR_INVALID_ARG, "non-positive dimension");
+  if (c->n_q_heads % c->n_kv_heads) return fail(PE_ERR_INVALID_ARG, "n_q_heads %% n_kv_heads != 0");
+  if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(PE_ERR_INVALID_ARG, "mask_id outside [0,vocab)");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(PE_ERR_INVALID_ARG, "rms_eps/rope_theta");
+  if (c->vocab % 16) return fail(PE_ERR_UNSUPPORTED, "vocab must be a multiple of 16");
+  if (c->block_size % 16) return fail(PE_ERR_UNSUPPORTED, "block_size must be a multiple of 16");
+  if (c->head_dim % 32) return fail(PE_ERR_UNSUPPORTED, "head_dim must be a multiple of 32");
+  if (c->dtype == PE_BF16) {
+    if (c->head_dim != 64) return fail(PE_ERR_UNSUPPORTED, "bf16 kernels need head_dim 64");
+    if (c->d % 64) return fail(PE_ERR_UNSUPPORTED, "bf16 kernels need d %% 64 == 0");
+    if (c->mlp % 64) return fail(PE_ERR_UNSUPPORTED, "bf16 kernels need mlp %% 64 == 0");
+  } else {
+    if (c->head_dim > 128) return fail(PE_ERR_UNSUPPORTED, "fp32 kernels need head_dim <= 128");
+    if (c->d % 4) return fail(PE_ERR_UNSUPPORTED, "fp32 kernels need d %% 4 == 0");
+    if (c->mlp % 16) return fail(PE_ERR_UNSUPPORTED, "fp32 kernels need mlp %% 16 == 0");
+  }
+  return PE_OK;
+}
+
+pe_status check_w(const pe_config* c, const pe_weights* w) {
+  if (!w) return fail(PE_ERR_INVALID_ARG, "weights is NULL");
+  const void* top[] = {w->embed, w->w_fc, w->final_norm, w->lm_head};
+  for (const void* p : top)
+    if (!p || !aligned(p, 16)) return fail(PE_ERR_INVALID_ARG, "weight pointer NULL or not 16-byte aligned");
+  if (!w->layers) return fail(PE_ERR_INVALID_ARG, "weights.layers is NULL");
+  for (int l = 0; l < c->layers; ++l) {
+    const pe_layer_weights& L = w->layers[l];
+    const void* ps[] = {L.attn_norm, L.wq, L.wk, L.wv, L.wo, L.mlp_norm, L.w_gate, L.w_up, L.w_down};
+    for (const void* p : ps)
+      if (!p || !aligned(p, 16))
+        return fail(PE_ERR_INVALID_ARG, "layer %d weight pointer NULL or not 16-byte aligned", l);
+  }
+  return PE_OK;
+}
+
+template <typename T>
+pe_status alloc(T** p, size_t bytes, const char* what) {
+  if (bytes == 0) bytes = 16;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(p), bytes);
+  if (e != hipSuccess) return fail(PE_ERR_NOMEM, "hipMalloc %s (%zu bytes): %s", what, bytes, hipGetErrorString(e));
+  return PE_OK;
+}
+
+pe_status check_B(const pe_ctx* c, int32_t B) {
+  if (!c) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  if (B < 0 || B > c->cfg.max_num_seqs)
+    return fail(PE_ERR_INVALID_ARG, "B=%d outside [0, max_num_seqs=%d]", B, c->cfg.max_num_seqs);
+  return PE_OK;
+}
+
+pe_status check_batch(const pe_batch* b) {
+  if (!b) return fail(PE_ERR_INVALID_ARG, "batch is NULL");
+  if (!b->input_ids || !b->positions || !b->hidden_src || !b->is_rejected || !b->is_masked ||
+      !b->slot_mapping || !b->draft_rows || !b->seq_lens)
+    return fail(PE_ERR_INVALID_ARG, "a batch buffer is NULL");
+  if (!aligned(b->input_ids, 4) || !aligned(b->positions, 4) || !aligned(b->hidden_src, 4) ||
+      !aligned(b->draft_rows, 4) || !aligned(b->seq_lens, 4) || !aligned(b->slot_mapping, 8))
+    return fail(PE_ERR_INVALID_ARG, "a batch buffer is misaligned");
+  return PE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pe_last_error(void) { return g_err.c_str(); }
+
+const char* pe_status_string(pe_status s) {
+  switch (s) {
+    case PE_OK: return "PE_OK";
+    case PE_ERR_INVALID_ARG: return "PE_ERR_INVALID_ARG";
+    case PE_ERR_NOMEM: return "PE_ERR_NOMEM";
+    case PE_ERR_HIP: return "PE_ERR_HIP";
+    case PE_ERR_UNSUPPORTED: return "PE_ERR_UNSUPPORTED";
+  }
+  return "unknown";
+}
+
+pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_ctx** out) {
+  g_err.clear();
+  if (!out) return fail(PE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  pe_status s = check_cfg(cfg);
+  if (s != PE_OK) return s;
+  if ((s = check_w(cfg, w)) != PE_OK) return s;
+
+  pe_ctx* c = new pe_ctx();
+  c->cfg = *cfg;
+  c->w = *w;
+  c->layers.assign(w->layers, w->layers + cfg->layers);
+  c->w.layers = c->layers.data();
+  c->stream = reinterpret_cast<hipStream_t>(stream);
+  c->esz = cfg->dtype == PE_BF16 ? 2 : 4;
+  hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
+  if (e != hipSuccess) {
+    free_ctx(c);
+    return hipfail(e, "device query");
+  }
+  c->target_items = 4 * c->num_cus;
+
+  const pe_config& k = c->cfg;
+  const size_t R = size_t(k.max_num_seqs) * 2 * k.K, D = size_t(k.max_num_seqs) * k.K;
+  const size_t qd = size_t(k.n_q_heads) * k.head_dim;
+  const size_t QN = size_t(2 * k.K) * (k.n_q_heads / k.n_kv_heads);
+  c->items_max = pe::attn_max_items(k.max_num_seqs, k.n_kv_heads, c->target_items);
+  struct { void** p; size_t bytes; const char* what; } plan[] = {
+      {&c->x, R * k.d * c->esz, "x"},
+      {&c->u, R * k.d * c->esz, "u"},
+      {&c->q, R * qd * c->esz, "q"},
+      {&c->attn, R * qd * c->esz, "attn"},
+      {&c->mlp, R * size_t(k.mlp) * c->esz, "mlp"},
+      {&c->z, D * k.d * c->esz, "z"},
+      {reinterpret_cast<void**>(&c->keys), D * 8, "keys"},
+      {reinterpret_cast<void**>(&c->counter), 16, "counter"},
+      {reinterpret_cast<void**>(&c->err), 16, "err"},
+      {reinterpret_cast<void**>(&c->rope_inv), size_t(k.head_dim / 2) * 4, "rope"},
+      {reinterpret_cast<void**>(&c->rope_inv_d), size_t(k.head_dim / 2) * 8, "rope_d"},
+  };
+  for (auto& p : plan) {
+    if ((s = alloc(p.p, p.bytes, p.what)) != PE_OK) { free_ctx(c); return s; }
+  }
+  if (k.dtype == PE_BF16) {
+    if ((s = alloc(&c->part_o, size_t(c->items_max) * QN * k.head_dim * 4, "attn partials")) != PE_OK ||
+        (s = alloc(&c->part_ml, size_t(c->items_max) * QN * 2 * 4, "attn stats")) != PE_OK) {
+      free_ctx(c);
+      return s;
+    }
+  }
+  // RoPE inverse frequencies theta^(-2i/hd), computed in double
+  std::vector<float> inv(k.head_dim / 2);
+  std::vector<double> invd(k.head_dim / 2);
+  for (int i = 0; i < k.head_dim / 2; ++i) {
+    invd[i] = std::pow(double(k.rope_theta), -2.0 * i / double(k.head_dim));
+    inv[i] = float(invd[i]);
+  }
+  const uint32_t err0[4] = {0u, 0xFFFFFFFFu, 0u, 0u};
+  e = hipMemcpy(c->rope_inv, inv.data(), inv.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(c->rope_inv_d, invd.data(), invd.size() * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(c->keys, 0, D * 8);
+  if (e == hipSuccess) e = hipMemset(c->counter, 0, 16);
+  if (e == hipSuccess) e = hipMemcpy(c->err, err0, 16, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    free_ctx(c);
+    return hipfail(e, "workspace init");
+  }
+  *out = c;
+  return PE_OK;
+}
+
+pe_status pe_destroy(pe_ctx* ctx) {
+  if (!ctx) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  (void)hipStreamSynchronize(ctx->stream);
+  free_ctx(ctx);
+  return PE_OK;
+}
+
+pe_status pe_set_stream(pe_ctx* ctx, void* stream) {
+  if (!ctx) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  ctx->stream = reinterpret_cast<hipStream_t>(stream);
+  return PE_OK;
+}
+
+pe_status pe_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_tokens,
+                     const int32_t* verify_positions, const int32_t* num_accepted,
+                     const int32_t* bonus_tokens, const int32_t* block_table, int32_t max_blocks,
+                     int32_t num_kv_blocks, const pe_batch* out) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if ((s = check_batch(out)) != PE_OK) return s;
+  if (B == 0) return PE_OK;
+  if (!verify_tokens || !verify_positions || !num_accepted || !bonus_tokens || !block_table)
+    return fail(PE_ERR_INVALID_ARG, "a prepare input is NULL");
+  if (max_blocks < 1 || num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "max_blocks/num_kv_blocks < 1");
+  pe::PrepareArgs a;
+  a.B = B;
+  a.K = ctx->cfg.K;
+  a.vocab = ctx->cfg.vocab;
+  a.mask_id = ctx->cfg.mask_id;
+  a.block_size = ctx->cfg.block_size;
+  a.max_blocks = max_blocks;
+  a.num_kv_blocks = num_kv_blocks;
+  a.vt = verify_tokens;
+  a.vp = verify_positions;
+  a.acc = num_accepted;
+  a.bonus = bonus_tokens;
+  a.bt = block_table;
+  a.ids = out->input_ids;
+  a.pos = out->positions;
+  a.hsrc = out->hidden_src;
+  a.draft_rows = out->draft_rows;
+  a.seq_lens = out->seq_lens;
+  a.rej = out->is_rejected;
+  a.msk = out->is_masked;
+  a.slots = out->slot_mapping;
+  a.err = ctx->err;
+  PE_HIP(pe::launch_prepare(a, ctx->stream), "prepare launch");
+  return PE_OK;
+}
+
+pe_status pe_gather_hidden(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* target_hidden,
+                           const void* h_shared, void* draft_hidden) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if (!batch || !batch->hidden_src) return fail(PE_ERR_INVALID_ARG, "batch.hidden_src is NULL");
+  if (B == 0) return PE_OK;
+  if (!target_hidden || !h_shared || !draft_hidden || !aligned(target_hidden, 16) ||
+      !aligned(h_shared, 16) || !aligned(draft_hidden, 16))
+    return fail(PE_ERR_INVALID_ARG, "hidden buffers NULL or not 16-byte aligned");
+  const int K = ctx->cfg.K;
+  PE_HIP(pe::launch_gather(B * 2 * K, B * (K + 1), int(ctx->cfg.d * ctx->esz), batch->hidden_src,
+                           target_hidden, h_shared, draft_hidden, ctx->stream),
+         "gather launch");
+  return PE_OK;
+}
+
+pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* draft_hidden,
+                           const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                           void* const* k_cache, void* const* v_cache, int32_t* draft_tokens,
+                           float* logits) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if ((s = check_batch(batch)) != PE_OK) return s;
+  if (B == 0) return PE_OK;
+  const pe_config& k = ctx->cfg;
+  if (!draft_hidden || !aligned(draft_hidden, 16)) return fail(PE_ERR_INVALID_ARG, "draft_hidden");
+  if (!block_table || max_blocks < 1 || num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "block table");
+  if (!k_cache || !v_cache) return fail(PE_ERR_INVALID_ARG, "k_cache/v_cache arrays are NULL");
+  for (int l = 0; l < k.layers; ++l)
+    if (!k_cache[l] || !v_cache[l] || !aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
+      return fail(PE_ERR_INVALID_ARG, "KV cache of layer %d NULL or misaligned", l);
+  if (!draft_tokens) return fail(PE_ERR_INVALID_ARG, "draft_tokens is NULL");
+  if (logits && !aligned(logits, 4)) return fail(PE_ERR_INVALID_ARG, "logits misaligned");
+
+  const int S = 2 * k.K, R = B * S, D = B * k.K, d = k.d;
+  const int qd = k.n_q_heads * k.head_dim, kvd = k.n_kv_heads * k.head_dim;
+  const long long num_slots = (long long)num_kv_blocks * k.block_size;
+  hipStream_t st = ctx->stream;
+  const int dt = k.dtype;
+
+  pe::GemmArgs g0;
+  std::memset(&g0, 0, sizeof g0);
+  g0.d = d;
+  g0.vocab = k.vocab;
+  g0.hd = k.head_dim;
+  g0.Hkv = k.n_kv_heads;
+  g0.block_size = k.block_size;
+  g0.num_slots = num_slots;
+
+  // fc over concat(emb(token), hidden)
+  {
+    pe::GemmArgs g = g0;
+    g.M = R; g.N = d; g.K = 2 * d;
+    g.embed = ctx->w.embed; g.ids = batch->input_ids; g.hid = draft_hidden;
+    g.W0 = ctx->w.w_fc;
+    g.out = ctx->x; g.ldo = d;
+    PE_HIP(pe::launch_gemm(dt, pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, ctx->num_cus, st), "fc");
+  }
+  for (int l = 0; l < k.layers; ++l) {
+    const pe_layer_weights& L = ctx->layers[l];
+    PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.attn_norm, ctx->u, nullptr, R, k.rms_eps, st), "attn norm");
+    {
+      pe::GemmArgs g = g0;
+      g.M = R; g.N = qd + 2 * kvd; g.K = d;
+      g.A = ctx->u; g.lda = d;
+      g.W0 = L.wq; g.W1 = L.wk; g.W2 = L.wv; g.nq = qd; g.nk = kvd;
+      g.positions = batch->positions; g.slots = batch->slot_mapping;
+      g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
+      g.rope_inv = ctx->rope_inv; g.rope_inv_d = ctx->rope_inv_d;
+      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, ctx->num_cus, st), "qkv");
+    }
+    {
+      pe::AttnArgs a;
+      std::memset(&a, 0, sizeof a);
+      a.B = B; a.S = S; a.Hq = k.n_q_heads; a.Hkv = k.n_kv_heads; a.hd = k.head_dim;
+      a.block_size = k.block_size; a.max_blocks = max_blocks; a.num_slots = num_slots;
+      a.scale = 1.0f / std::sqrt(float(k.head_dim));
+      a.q = ctx->q; a.kcache = k_cache[l]; a.vcache = v_cache[l];
+      a.positions = batch->positions; a.rej = batch->is_rejected; a.seq_lens = batch->seq_lens;
+      a.bt = block_table; a.out = ctx->attn;
+      a.part_o = ctx->part_o; a.part_ml = ctx->part_ml;
+      a.target_items = ctx->target_items;
+      long long grid = 4LL * ctx->num_cus;
+      const long long mx = pe::attn_max_items(B, k.n_kv_heads, ctx->target_items);
+      a.grid = int(grid < mx ? grid : mx);
+      PE_HIP(pe::launch_attention(dt, a, st), "attention");
+    }
+    {
+      pe::GemmArgs g = g0;
+      g.M = R; g.N = d; g.K = qd;
+      g.A = ctx->attn; g.lda = qd;
+      g.W0 = L.wo;
+      g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
+      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, ctx->num_cus, st), "o proj");
+    }
+    PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.mlp_norm, ctx->u, nullptr, R, k.rms_eps, st), "mlp norm");
+    {
+      pe::GemmArgs g = g0;
+      g.M = R; g.N = 2 * k.mlp; g.K = d;
+      g.A = ctx->u; g.lda = d;
+      g.W0 = L.w_gate; g.W1 = L.w_up;
+      g.out = ctx->mlp; g.ldo = k.mlp;
+      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, ctx->num_cus, st), "gate/up");
+    }
+    {
+      pe::GemmArgs g = g0;
+      g.M = R; g.N = d; g.K = k.mlp;
+      g.A = ctx->mlp; g.lda = k.mlp;
+      g.W0 = L.w_down;
+      g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
+      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, ctx->num_cus, st), "down");
+    }
+  }
+  PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, ctx->w.final_norm, ctx->z, batch->draft_rows, R,
+                            k.rms_eps, st),
+         "final norm");
+  {
+    pe::GemmArgs g = g0;
+    g.M = D; g.N = k.vocab; g.K = d;
+    g.A = ctx->z; g.lda = d;
+    g.W0 = ctx->w.lm_head;
+    g.keys = ctx->keys; g.counter = ctx->counter; g.tokens = draft_tokens; g.logits = logits;
+    g.seq_lens = batch->seq_lens; g.Kd = k.K;
+    PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
+  }
+  return PE_OK;
+}
+
+pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens, const int32_t* target_tokens,
+                    int32_t* num_accepted, int32_t* bonus_tokens) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if (B == 0) return PE_OK;
+  if (!draft_tokens || !target_tokens || !num_accepted || !bonus_tokens)
+    return fail(PE_ERR_INVALID_ARG, "a verify buffer is NULL");
+  PE_HIP(pe::launch_verify(B, ctx->cfg.K, draft_tokens, target_tokens, num_accepted, bonus_tokens,
+                           ctx->stream),
+         "verify launch");
+  return PE_OK;
+}
+
+static pe_status run_step(pe_ctx* ctx, int32_t B, const pe_step_args* a) {
+  pe_status s = pe_prepare(ctx, B, a->verify_tokens, a->verify_positions, a->num_accepted,
+                           a->bonus_tokens, a->block_table, a->max_blocks, a->num_kv_blocks, &a->batch);
+  if (s != PE_OK) return s;
+  s = pe_gather_hidden(ctx, B, &a->batch, a->target_hidden, a->h_shared, a->draft_hidden);
+  if (s != PE_OK) return s;
+  s = pe_draft_forward(ctx, B, &a->batch, a->draft_hidden, a->block_table, a->max_blocks,
+                       a->num_kv_blocks, a->k_cache, a->v_cache, a->draft_tokens, a->logits);
+  if (s != PE_OK) return s;
+  return pe_verify(ctx, B, a->draft_tokens, a->target_tokens, a->accepted_out, a->bonus_out);
+}
+
+pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if (!args || !args->k_cache || !args->v_cache) return fail(PE_ERR_INVALID_ARG, "step args");
+  const int nl = ctx->cfg.layers;
+  std::vector<void*> kv(2 * nl);
+  for (int l = 0; l < nl; ++l) {
+    kv[l] = args->k_cache[l];
+    kv[nl + l] = args->v_cache[l];
+  }
+  const bool same = ctx->gexec && ctx->graph_B == B &&
+                    std::memcmp(&ctx->graph_args, args, sizeof *args) == 0 && ctx->graph_kv == kv;
+  if (!same) {
+    if (ctx->gexec) { (void)hipGraphExecDestroy(ctx->gexec); ctx->gexec = nullptr; }
+    if (ctx->graph) { (void)hipGraphDestroy(ctx->graph); ctx->graph = nullptr; }
+    if (!ctx->capture_stream)
+      PE_HIP(hipStreamCreateWithFlags(&ctx->capture_stream, hipStreamNonBlocking), "capture stream");
+    // work queued on ctx->stream before this call must not be reordered with the graph
+    PE_HIP(hipStreamSynchronize(ctx->stream), "sync before capture");
+    PE_HIP(hipStreamBeginCapture(ctx->capture_stream, hipStreamCaptureModeRelaxed), "begin capture");
+    hipStream_t user = ctx->stream;
+    ctx->stream = ctx->capture_stream;
+    s = run_step(ctx, B, args);
+    ctx->stream = user;
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamEndCapture(ctx->capture_stream, &graph);
+    if (s != PE_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return s;
+    }
+    if (e != hipSuccess) return hipfail(e, "end capture");
+    ctx->graph = graph;
+    PE_HIP(hipGraphInstantiate(&ctx->gexec, graph, nullptr, nullptr, 0), "graph instantiate");
+    ctx->graph_B = B;
+    ctx->graph_args = *args;
+    ctx->graph_kv = kv;
+  }
+  PE_HIP(hipGraphLaunch(ctx->gexec, ctx->stream), "graph launch");
+  return PE_OK;
+}
+
+pe_status pe_get_device_error(pe_ctx* ctx, uint32_t* kinds, int32_t* first_request) {
+  if (!ctx || !kinds || !first_request) return fail(PE_ERR_INVALID_ARG, "NULL argument");
+  uint32_t h[4] = {0, 0, 0, 0};
+  const uint32_t err0[4] = {0u, 0xFFFFFFFFu, 0u, 0u};
+  PE_HIP(hipStreamSynchronize(ctx->stream), "sync");
+  PE_HIP(hipMemcpy(h, ctx->err, 16, hipMemcpyDeviceToHost), "read error word");
+  PE_HIP(hipMemcpy(ctx->err, err0, 16, hipMemcpyHostToDevice), "clear error word");
+  *kinds = h[0];
+  *first_request = h[0] ? int32_t(h[1]) : -1;
+  return PE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Device-side helpers shared by the libpe kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// bfloat16 is stored as its 16-bit pattern (the high half of an IEEE float32).
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+// float32 -> bfloat16, round to nearest, ties to even.  Inputs here are finite.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Storage access for the two element types the library handles.
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ float cvt(float v) { return v; }
+};
+template <> struct Elt<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(uint16_t* p, float v) { *p = f2bf(v); }
+  static __device__ __forceinline__ float cvt(float v) { return bf2f(f2bf(v)); }
+};
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%16][8(l/16)..+8]
+// and B[8(l/16)..+8][l%16]; it receives C[4(l/16)+i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Streaming 16-byte load for data read once (weights): non-temporal hint.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Order-preserving 32-bit image of a float: larger float -> larger unsigned.
+__device__ __forceinline__ uint32_t float_order(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Argmax key: value in the high word, (0xFFFFFFFF - index) in the low word, so
+// the largest key holds the largest value and, among equal values, the lowest index.
+__device__ __forceinline__ uint64_t argmax_key(float v, int idx) {
+  return (uint64_t(float_order(v)) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(idx));
+}
+__device__ __forceinline__ int argmax_key_index(uint64_t k) {
+  return int(0xFFFFFFFFu - uint32_t(k & 0xFFFFFFFFull));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace pe

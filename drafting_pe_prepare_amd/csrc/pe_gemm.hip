@@ -1,0 +1,559 @@
+// Dense contractions of the drafter: out[m, n] = sum_k A[m, k] W[n, k] with a
+// fused epilogue.  "P-EAGLE: parallel speculative decoding in vLLM",
+// Architecture and mechanism, Step 2: an fc over concat(emb, h), an N-layer
+// Transformer and the LM head, over all K positions in one pass.  These are the
+// dense parts of that pass: fc, QKV (+ RoPE + KV write), O (+ residual),
+// gate/up (+ SiLU-and-mul), down (+ residual), LM head (+ row argmax).
+//
+// gfx950 design
+//  * bf16 operands, fp32 accumulation on v_mfma_f32_16x16x32_bf16.  Both
+//    operands are K-contiguous, so every lane feeds the MFMA straight from one
+//    16-byte load (A row l%16 / W row l%16, k chunk l/16).
+//  * M <= 64 (a draft batch of a few requests): the weights are the whole
+//    traffic.  gemm_skinny splits K across the 16 waves of a workgroup, streams
+//    W with non-temporal 16-byte loads, and reduces the wave partials through
+//    LDS in a fixed order (deterministic), then runs the epilogue.
+//  * LM head with M <= 16 rows: lmhead_wide keeps the rows in LDS, gives every
+//    wave whole 16-column tiles over the full K, and keeps a running argmax key
+//    per row in registers -- logits never reach memory unless asked for.
+//  * M > 64: gemm_tiled, 128x128x64 LDS-tiled, double-buffered, 4 waves of
+//    64x64; workgroups that share a weight tile are placed on one XCD (one L2)
+//    back to back.
+//  * Epilogues run on an fp32 tile staged in LDS, so every variant shares them.
+//    Column pairs that an epilogue needs together (RoPE rotate-half partners,
+//    gate/up partners) are placed 16 logical columns apart inside one 32-column
+//    block by the weight-row mapping (B_QKV, B_GATEUP).
+//  * fp32 storage: gemm_f32, plain FMA, for the small fp32 workload only.
+#include "pe_common.h"
+#include "pe_internal.h"
+
+namespace pe {
+
+// ---------------------------------------------------------------------------
+// operand addressing
+// ---------------------------------------------------------------------------
+// Rotate-half partner layout: inside each head of hd dims, logical 16-column
+// group s maps to dims (s%2)*hd/2 + (s/2)*16 + [0,16), so groups 2j and 2j+1
+// hold dims i and i + hd/2 for the same i.
+__device__ __forceinline__ int rope_phys(int j, int hd) {
+  const int jb = j % hd, s = jb >> 4, c = jb & 15;
+  return (j - jb) + (s & 1) * (hd >> 1) + (s >> 1) * 16 + c;
+}
+
+template <typename T, int BMAP>
+__device__ __forceinline__ const T* weight_row(const GemmArgs& g, int n) {
+  const long long K = g.K;
+  if (BMAP == B_GATEUP) {
+    const int t = n >> 5, r = n & 31;
+    return (r < 16 ? (const T*)g.W0 : (const T*)g.W1) + (long long)(t * 16 + (r & 15)) * K;
+  } else if (BMAP == B_QKV) {
+    if (n >= g.nq + g.nk) return (const T*)g.W2 + (long long)(n - g.nq - g.nk) * K;
+    if (n < g.nq) return (const T*)g.W0 + (long long)rope_phys(n, g.hd) * K;
+    return (const T*)g.W1 + (long long)rope_phys(n - g.nq, g.hd) * K;
+  }
+  return (const T*)g.W0 + (long long)n * K;
+}
+
+// A row m: `lo` serves k < d (or every k for A_PLAIN), `hi` serves k >= d.
+template <typename T, int AL>
+struct ARow {
+  const T* lo;
+  const T* hi;
+  __device__ __forceinline__ void init(const GemmArgs& g, int m) {
+    if (AL == A_FC) {
+      int id = g.ids[m];
+      id = id < 0 ? 0 : (id >= g.vocab ? g.vocab - 1 : id);
+      lo = (const T*)g.embed + (long long)id * g.d;
+      hi = (const T*)g.hid + (long long)m * g.d - g.d;
+    } else {
+      lo = (const T*)g.A + (long long)m * g.lda;
+      hi = lo;
+    }
+  }
+  __device__ __forceinline__ const T* at(int k, int d) const {
+    return (AL == A_FC && k >= d) ? hi + k : lo + k;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// epilogues on an fp32 tile in LDS: tile[i*ldt + c] = out[m0+i, n0+c] (logical)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rope_sincos(const GemmArgs& g, int pos, int i, float& cs,
+                                            float& sn) {
+  // angle = pos * theta^(-2i/hd), reduced to [-pi, pi] in double, then fp32 sincos
+  const double TWO_PI = 6.283185307179586476925286766559;
+  double ang = double(pos) * g.rope_inv_d[i];
+  ang -= TWO_PI * rint(ang / TWO_PI);
+  sincosf(float(ang), &sn, &cs);
+}
+
+template <typename T, int EPI>
+__device__ void epilogue(const GemmArgs& g, const float* tile, int ldt, int m0, int TM, int n0,
+                         int TN) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int mrows = min(TM, g.M - m0);
+  const int ncols = min(TN, g.N - n0);
+  if (mrows <= 0 || ncols <= 0) return;
+  if (EPI == E_STORE || EPI == E_RESID) {
+    for (int e = tid; e < mrows * ncols; e += nt) {
+      const int i = e / ncols, c = e - i * ncols;
+      const long long o = (long long)(m0 + i) * g.ldo + n0 + c;
+      float v = tile[i * ldt + c];
+      if (EPI == E_RESID) v += Elt<T>::ld((const T*)g.resid + o);
+      Elt<T>::st((T*)g.out + o, v);
+    }
+  } else if (EPI == E_SILU) {
+    // block b of 32 logical columns = 16 gate columns then their 16 up columns
+    const int np = ncols >> 1;
+    for (int e = tid; e < mrows * np; e += nt) {
+      const int i = e / np, p = e - i * np, b = p >> 4, c = p & 15;
+      const float gt = tile[i * ldt + b * 32 + c], up = tile[i * ldt + b * 32 + 16 + c];
+      const float v = gt / (1.0f + expf(-gt)) * up;
+      Elt<T>::st((T*)g.out + (long long)(m0 + i) * g.ldo + (n0 >> 1) + p, v);
+    }
+  } else if (EPI == E_QKV) {
+    const int np = ncols >> 1;
+    const int hq = g.nq / g.hd;
+    for (int e = tid; e < mrows * np; e += nt) {
+      const int i = e / np, p = e - i * np, b = p >> 4, c = p & 15;
+      const int m = m0 + i, nb = n0 + b * 32;
+      const float lo = tile[i * ldt + b * 32 + c], hi = tile[i * ldt + b * 32 + 16 + c];
+      if (nb < g.nq + g.nk) {
+        const bool isq = nb < g.nq;
+        const int j = isq ? nb : nb - g.nq;
+        const int head = j / g.hd, s = (j % g.hd) >> 4;
+        const int dlo = (s >> 1) * 16 + c, dhi = dlo + (g.hd >> 1);
+        float cs, sn;
+        rope_sincos(g, g.positions[m], dlo, cs, sn);
+        const float olo = lo * cs - hi * sn, ohi = hi * cs + lo * sn;
+        if (isq) {
+          T* q = (T*)g.qout + ((long long)m * hq + head) * g.hd;
+          Elt<T>::st(q + dlo, olo);
+          Elt<T>::st(q + dhi, ohi);
+        } else {
+          const long long slot = g.slots[m];
+          if (slot >= 0 && slot < g.num_slots) {
+            T* kp = (T*)g.kcache + (slot * g.Hkv + head) * g.hd;
+            Elt<T>::st(kp + dlo, olo);
+            Elt<T>::st(kp + dhi, ohi);
+          }
+        }
+      } else {
+        const long long slot = g.slots[m];
+        if (slot >= 0 && slot < g.num_slots) {
+          const int j = nb - g.nq - g.nk;
+          const int head = j / g.hd, jb = j % g.hd;
+          const long long blk = slot / g.block_size, off = slot % g.block_size;
+          T* vp = (T*)g.vcache + ((blk * g.Hkv + head) * g.hd) * g.block_size + off;
+          Elt<T>::st(vp + (long long)(jb + c) * g.block_size, lo);
+          Elt<T>::st(vp + (long long)(jb + 16 + c) * g.block_size, hi);
+        }
+      }
+    }
+  }
+}
+
+// Row argmax of a tile: one wave per row, lanes over columns, 64-bit keys.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor(uint32_t(v), o, 64), hi = __shfl_xor(uint32_t(v >> 32), o, 64);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+__device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, int m0, int TM,
+                                int n0, int TN) {
+  const int mrows = min(TM, g.M - m0), ncols = min(TN, g.N - n0);
+  if (mrows <= 0 || ncols <= 0) return;
+  if (g.logits)
+    for (int e = threadIdx.x; e < mrows * ncols; e += blockDim.x) {
+      const int i = e / ncols, c = e - i * ncols;
+      g.logits[(long long)(m0 + i) * g.N + n0 + c] = tile[i * ldt + c];
+    }
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
+  for (int i = w; i < mrows; i += nw) {
+    uint64_t best = 0;
+    for (int c = l; c < ncols; c += 64) {
+      const uint64_t k = argmax_key(tile[i * ldt + c], n0 + c);
+      best = k > best ? k : best;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t k = shfl_xor_u64(best, o);
+      best = k > best ? k : best;
+    }
+    if (l == 0) atomicMax((unsigned long long*)&g.keys[m0 + i], (unsigned long long)best);
+  }
+}
+
+// The last workgroup to finish turns the argmax keys into tokens and resets the
+// keys and the counter for the next launch (so no memset is needed).
+__device__ void argmax_finalize(const GemmArgs& g, unsigned nblocks) {
+  __threadfence();
+  __syncthreads();
+  __shared__ int s_last;
+  if (threadIdx.x == 0) {
+    const unsigned t = atomicAdd(g.counter, 1u);
+    s_last = (t == nblocks - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int i = threadIdx.x; i < g.M; i += blockDim.x) {
+    const uint64_t k =
+        __hip_atomic_load((unsigned long long*)&g.keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int tok = argmax_key_index(k);
+    if (g.seq_lens && g.seq_lens[i / g.Kd] == 0) tok = -1;
+    g.tokens[i] = tok;
+    __hip_atomic_store((unsigned long long*)&g.keys[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(g.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// bf16, M <= 64: split-K across the waves of a workgroup
+// ---------------------------------------------------------------------------
+template <int EPI, int AL, int BMAP, int MT, int NTW>
+__global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
+  extern __shared__ float smem[];
+  const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int col = l & 15, kg = l >> 4;
+  const int n0 = blockIdx.x * (NTW * 16);
+  const int ksteps = g.K >> 5;
+  const int ks0 = (ksteps * w) / nw, ks1 = (ksteps * (w + 1)) / nw;
+
+  const uint16_t* wp[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    int n = n0 + t * 16 + col;
+    n = n < g.N ? n : g.N - 1;
+    wp[t] = weight_row<uint16_t, BMAP>(g, n) + kg * 8;
+  }
+  ARow<uint16_t, AL> ar[MT];
+  bool av[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + col;
+    av[mt] = m < g.M;
+    ar[mt].init(g, av[mt] ? m : 0);
+  }
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const int k = ks * 32;
+    uint4 b[NTW], a[MT];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) b[t] = ld_stream(wp[t] + k);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = av[mt] ? ld16(ar[mt].at(k + kg * 8, g.d)) : zero;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[mt][t] = mfma16(a[mt], b[t], acc[mt][t]);
+  }
+
+  // fixed-order reduction of the wave partials
+  constexpr int PER = MT * NTW * 256;
+  float* red = smem;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[w * PER + ((mt * NTW + t) * 4 + i) * 64 + l] = acc[mt][t][i];
+  __syncthreads();
+  constexpr int LDT = NTW * 16 + 4;
+  float* tile = smem + nw * PER;
+  for (int e = threadIdx.x; e < PER; e += blockDim.x) {
+    float s = 0.f;
+    for (int ww = 0; ww < nw; ++ww) s += red[ww * PER + e];
+    const int lane = e & 63, i = (e >> 6) & 3, mtt = e >> 8;
+    const int t = mtt % NTW, mt = mtt / NTW;
+    tile[(mt * 16 + (lane >> 4) * 4 + i) * LDT + t * 16 + (lane & 15)] = s;
+  }
+  __syncthreads();
+  if (EPI == E_ARGMAX) {
+    epilogue_argmax(g, tile, LDT, 0, MT * 16, n0, NTW * 16);
+    argmax_finalize(g, gridDim.x);
+  } else {
+    epilogue<uint16_t, EPI>(g, tile, LDT, 0, MT * 16, n0, NTW * 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 LM head, M <= 16 rows: rows in LDS, whole tiles per wave, argmax in
+// registers
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void lmhead_wide_kernel(GemmArgs g) {
+  extern __shared__ uint4 xs[];
+  const int K = g.K, kc = K >> 3, ldx = kc + 1;
+  for (int c = threadIdx.x; c < g.M * kc; c += blockDim.x) {
+    const int m = c / kc, j = c - m * kc;
+    xs[m * ldx + j] = ld16((const uint16_t*)g.A + (long long)m * g.lda + j * 8);
+  }
+  __syncthreads();
+  const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int col = l & 15, kg = l >> 4;
+  const long long gw = (long long)blockIdx.x * nw + w, GW = (long long)gridDim.x * nw;
+  const int ntiles = g.N >> 4;
+  const int t0 = int(ntiles * gw / GW), t1 = int(ntiles * (gw + 1) / GW);
+  const bool arow = col < g.M;
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  const uint4* xrow = xs + col * ldx + kg;
+  uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
+  const int ksteps = K >> 5;
+  for (int t = t0; t < t1; ++t) {
+    const uint16_t* wp = (const uint16_t*)g.W0 + (long long)(t * 16 + col) * K + kg * 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const uint4 b = ld_stream(wp + ks * 32);
+      const uint4 a = arow ? xrow[ks * 4] : zero;
+      acc = mfma16(a, b, acc);
+    }
+    const int n = t * 16 + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = kg * 4 + i;
+      if (row < g.M) {
+        if (g.logits) g.logits[(long long)row * g.N + n] = acc[i];
+        const uint64_t key = argmax_key(acc[i], n);
+        best[i] = key > best[i] ? key : best[i];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    for (int o = 1; o < 16; o <<= 1) {
+      const uint64_t k = shfl_xor_u64(best[i], o);
+      best[i] = k > best[i] ? k : best[i];
+    }
+    const int row = kg * 4 + i;
+    if (col == 0 && row < g.M && best[i] != 0ull)
+      atomicMax((unsigned long long*)&g.keys[row], (unsigned long long)best[i]);
+  }
+  argmax_finalize(g, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// bf16, M > 64: 128x128x64 tiles, LDS double buffer, 4 waves of 64x64
+// ---------------------------------------------------------------------------
+template <int EPI, int AL, int BMAP>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
+  constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+  constexpr int ACH = BM * BK / 8 / 256, BCH = BN * BK / 8 / 256;  // 16B chunks per thread
+  extern __shared__ uint16_t lds[];
+  uint16_t* As = lds;                    // [2][BM][LDK]
+  uint16_t* Bs = lds + 2 * BM * LDK;     // [2][BN][LDK]
+
+  // XCD-aware order: the m-tiles of one n-tile run back to back on one XCD
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  const int mt = j % mtiles, nt = (j / mtiles) * 8 + xcd;
+  if (nt >= ntiles) {
+    // padding workgroup of the XCD-aligned grid; it still counts for the argmax
+    if (EPI == E_ARGMAX) argmax_finalize(g, gridDim.x);
+    return;
+  }
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
+  const int wm = w >> 1, wn = w & 1;
+
+  ARow<uint16_t, AL> ar[ACH];
+  bool av[ACH];
+  const uint16_t* bp[BCH];
+  bool bv[BCH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int c = tid + i * 256, m = m0 + (c >> 3);
+    av[i] = m < g.M;
+    ar[i].init(g, av[i] ? m : 0);
+  }
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int c = tid + i * 256, n = n0 + (c >> 3);
+    bv[i] = n < g.N;
+    bp[i] = weight_row<uint16_t, BMAP>(g, bv[i] ? n : 0);
+  }
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  uint4 ra[ACH], rb[BCH];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int c = tid + i * 256;
+      ra[i] = av[i] ? ld16(ar[i].at(k0 + (c & 7) * 8, g.d)) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int c = tid + i * 256;
+      rb[i] = bv[i] ? ld_stream(bp[i] + k0 + (c & 7) * 8) : zero;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4*>(As + (buf * BM + (c >> 3)) * LDK + (c & 7) * 8) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4*>(Bs + (buf * BN + (c >> 3)) * LDK + (c & 7) * 8) = rb[i];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = g.K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(As + (cur * BM + wm * 64 + i * 16 + col) * LDK + kk * 32 + kg * 8);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        bf[jj] = *reinterpret_cast<const uint4*>(Bs + (cur * BN + wn * 64 + jj * 16 + col) * LDK + kk * 32 + kg * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = mfma16(af[i], bf[jj], acc[i][jj]);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  constexpr int LDT = BN + 4;
+  float* tile = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        tile[(wm * 64 + i * 16 + kg * 4 + r) * LDT + wn * 64 + jj * 16 + col] = acc[i][jj][r];
+  __syncthreads();
+  if (EPI == E_ARGMAX) {
+    epilogue_argmax(g, tile, LDT, m0, BM, n0, BN);
+  } else {
+    epilogue<uint16_t, EPI>(g, tile, LDT, m0, BM, n0, BN);
+  }
+  if (EPI == E_ARGMAX) argmax_finalize(g, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// fp32: plain FMA, 16x32 output tile per workgroup
+// ---------------------------------------------------------------------------
+template <int EPI, int AL, int BMAP>
+__global__ __launch_bounds__(512) void gemm_f32_kernel(GemmArgs g) {
+  __shared__ float tile[16 * 33];
+  const int i = threadIdx.x >> 5, c = threadIdx.x & 31;
+  const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 32;
+  const int m = m0 + i, n = n0 + c;
+  float s = 0.f;
+  if (m < g.M && n < g.N) {
+    const float* w = weight_row<float, BMAP>(g, n);
+    ARow<float, AL> ar;
+    ar.init(g, m);
+    for (int k = 0; k < g.K; ++k) s = fmaf(*ar.at(k, g.d), w[k], s);
+  }
+  tile[i * 33 + c] = s;
+  __syncthreads();
+  if (EPI == E_ARGMAX) {
+    epilogue_argmax(g, tile, 33, m0, 16, n0, 32);
+    argmax_finalize(g, gridDim.x * gridDim.y);
+  } else {
+    epilogue<float, EPI>(g, tile, 33, m0, 16, n0, 32);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+template <typename F>
+static hipError_t set_lds(F* fn, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
+
+template <int EPI, int AL, int BMAP, int MT>
+static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
+  constexpr int NTW = (BMAP == B_PLAIN) ? 1 : 2;
+  const int ksteps = g.K / 32;
+  int nw = ksteps / 4;
+  nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
+  while (nw > 1 && nw * MT * NTW > 128) --nw;
+  const size_t lds = size_t(nw) * MT * NTW * 256 * 4 + size_t(MT * 16) * (NTW * 16 + 4) * 4;
+  auto fn = gemm_skinny_kernel<EPI, AL, BMAP, MT, NTW>;
+  hipError_t e = set_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  const int grid = (g.N + NTW * 16 - 1) / (NTW * 16);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * nw), lds, st, g);
+  return hipGetLastError();
+}
+
+template <int EPI, int AL, int BMAP>
+static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
+  const size_t wide_lds = size_t(g.M) * (g.K / 8 + 1) * 16;
+  if (EPI == E_ARGMAX && g.M <= 16 && wide_lds <= 150 * 1024) {
+    const size_t lds = wide_lds;
+    hipError_t e = set_lds(lmhead_wide_kernel, lds);
+    if (e != hipSuccess) return e;
+    int grid = num_cus;
+    const int ntiles = g.N / 16;
+    if (grid * 16 > ntiles) grid = (ntiles + 15) / 16;
+    hipLaunchKernelGGL(lmhead_wide_kernel, dim3(grid), dim3(1024), lds, st, g);
+    return hipGetLastError();
+  }
+  if (g.M <= 16) return run_skinny<EPI, AL, BMAP, 1>(g, st);
+  if (g.M <= 32) return run_skinny<EPI, AL, BMAP, 2>(g, st);
+  if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
+  if (g.M <= 64) return run_skinny<EPI, AL, BMAP, 4>(g, st);
+  const int mtiles = (g.M + 127) / 128, ntiles = (g.N + 127) / 128;
+  const int grid = mtiles * ((ntiles + 7) / 8) * 8;
+  const size_t lds = 2 * size_t(128 + 128) * 72 * 2;
+  auto fn = gemm_tiled_kernel<EPI, AL, BMAP>;
+  hipError_t e = set_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, st, g, mtiles, ntiles);
+  return hipGetLastError();
+}
+
+template <int EPI, int AL, int BMAP>
+static hipError_t run_f32(const GemmArgs& g, hipStream_t st) {
+  dim3 grid((g.N + 31) / 32, (g.M + 15) / 16);
+  hipLaunchKernelGGL((gemm_f32_kernel<EPI, AL, BMAP>), grid, dim3(512), 0, st, g);
+  return hipGetLastError();
+}
+
+template <int EPI, int AL, int BMAP>
+static hipError_t run(int dtype, const GemmArgs& g, int num_cus, hipStream_t st) {
+  return dtype == 1 ? run_bf16<EPI, AL, BMAP>(g, num_cus, st) : run_f32<EPI, AL, BMAP>(g, st);
+}
+
+hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,
+                       hipStream_t st) {
+  if (g.M <= 0) return hipSuccess;
+  if (aload == A_FC && bmap == B_PLAIN && epi == E_STORE) return run<E_STORE, A_FC, B_PLAIN>(dtype, g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_QKV && epi == E_QKV) return run<E_QKV, A_PLAIN, B_QKV>(dtype, g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_RESID) return run<E_RESID, A_PLAIN, B_PLAIN>(dtype, g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_GATEUP && epi == E_SILU) return run<E_SILU, A_PLAIN, B_GATEUP>(dtype, g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_ARGMAX) return run<E_ARGMAX, A_PLAIN, B_PLAIN>(dtype, g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_STORE) return run<E_STORE, A_PLAIN, B_PLAIN>(dtype, g, num_cus, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pe

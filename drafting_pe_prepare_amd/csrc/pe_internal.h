@@ -1,0 +1,75 @@
+// Launchers of the libpe kernels, called by the host runtime (pe_api.cpp).
+// Every launcher only enqueues work on `st`; shapes were validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pe {
+
+// ---- metadata -------------------------------------------------------------
+struct PrepareArgs {
+  int B, K, vocab, mask_id, block_size, max_blocks, num_kv_blocks;
+  const int32_t *vt, *vp, *acc, *bonus, *bt;
+  int32_t *ids, *pos, *hsrc, *draft_rows, *seq_lens;
+  uint8_t *rej, *msk;
+  int64_t* slots;
+  uint32_t* err;  // [0] kinds (OR), [1] first failing request (min)
+};
+hipError_t launch_prepare(const PrepareArgs& a, hipStream_t st);
+
+hipError_t launch_gather(int rows, int nsrc, int row_bytes, const int32_t* hsrc, const void* H,
+                         const void* h_shared, void* out, hipStream_t st);
+
+hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32_t* acc,
+                         int32_t* bonus, hipStream_t st);
+
+// ---- normalisation --------------------------------------------------------
+// out[i] = x[row(i)] * rsqrt(mean(x^2) + eps) * gain; row(i) = rows_idx ? rows_idx[i] : i
+hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void* gain, void* out,
+                          const int32_t* rows_idx, int rows_bound, float eps, hipStream_t st);
+
+// ---- GEMM  out[m, n] = sum_k A[m, k] W[n, k]  + fused epilogue -------------
+enum ALoad { A_PLAIN = 0, A_FC = 1 };
+enum BMap { B_PLAIN = 0, B_QKV = 1, B_GATEUP = 2 };
+enum Epi { E_STORE = 0, E_RESID = 1, E_SILU = 2, E_QKV = 3, E_ARGMAX = 4 };
+
+struct GemmArgs {
+  int M, N, K;  // N counts logical columns (2*I for gate/up; q+k+v dims for QKV)
+  // A operand
+  const void* A;  int lda;                        // A_PLAIN: A[m*lda + k]
+  const void* embed; const int32_t* ids;          // A_FC: k < d -> embed[ids[m]*d + k]
+  const void* hid; int d; int vocab;              //       k >= d -> hid[m*d + k - d]
+  // B operand (weights, row-major [rows, K])
+  const void* W0; const void* W1; const void* W2;
+  int nq, nk;                                     // B_QKV: rows of Wq, Wk (Wv follows)
+  // epilogue
+  void* out; int ldo; const void* resid;          // E_STORE / E_RESID / E_SILU
+  const int32_t* positions; const int64_t* slots; // E_QKV
+  void* qout; void* kcache; void* vcache;
+  int Hkv, hd, block_size; long long num_slots;
+  const float* rope_inv;  // [hd/2] inverse frequencies (float)
+  const double* rope_inv_d;  // [hd/2] the same in double (angle reduction)
+  uint64_t* keys; uint32_t* counter;              // E_ARGMAX
+  int32_t* tokens; float* logits; const int32_t* seq_lens; int Kd;
+};
+hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,
+                       hipStream_t st);
+
+// ---- attention ------------------------------------------------------------
+struct AttnArgs {
+  int B, S, Hq, Hkv, hd, block_size, max_blocks;
+  long long num_slots;
+  float scale;
+  const void* q;                  // [B*S, Hq, hd]
+  const void* kcache; const void* vcache;
+  const int32_t* positions; const uint8_t* rej; const int32_t* seq_lens; const int32_t* bt;
+  void* out;                      // [B*S, Hq*hd]
+  float* part_o; float* part_ml;  // split-KV partials (bf16 path)
+  int target_items;               // desired work items per launch
+  int grid;                       // persistent grid size
+};
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+// Upper bound on split-KV work items for B requests (sizes the partials).
+long long attn_max_items(int B, int Hkv, int target_items);
+
+}  // namespace pe

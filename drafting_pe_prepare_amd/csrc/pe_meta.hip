@@ -1,0 +1,166 @@
+// Batch preparation, hidden-state gather and greedy verification.
+//
+// "P-EAGLE: parallel speculative decoding in vLLM", vLLM implementation
+// details: one fused pass copies the previous token ids and positions, inserts
+// the bonus token, fills the parallel-draft slots with the MASK id and emits
+// the rejected-token mask, the masked-token mask and the hidden-state map
+// (Fused Triton kernel); rejected tokens map to PADDING_SLOT_ID = -1 so they
+// make no KV-cache write (KV cache); a separate copy moves hidden states and
+// broadcasts the learned placeholder into MASK slots (Hidden-state management).
+//
+// gfx950 design: one wavefront per request.  Slot j of the request is lane j
+// (2K <= 64), so every per-slot field is written by one coalesced store per
+// wave; validation uses wave ballots, not loops.  The gather is a plain 16-byte
+// vector copy, grid-strided over all rows.
+#include "pe_common.h"
+#include "pe_internal.h"
+
+namespace pe {
+
+__global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (r >= a.B) return;
+  const int K = a.K, S = 2 * K, base = r * S;
+  const int32_t* vt = a.vt + (long long)r * (K + 1);
+  const int32_t* vp = a.vp + (long long)r * (K + 1);
+  const int acc = a.acc[r];
+  const int p0 = vp[0];
+
+  uint32_t kinds = 0;
+  if (acc < 0 || acc > K) kinds |= 1u;
+  // accepted drafts (lanes j < a read d_{j+1}) and the bonus token
+  bool bad_tok = false;
+  if (!(kinds & 1u)) {
+    if (lane < acc) { int t = vt[lane + 1]; bad_tok = (t < 0 || t >= a.vocab); }
+    if (lane == acc) { int t = a.bonus[r]; bad_tok = (t < 0 || t >= a.vocab); }
+  }
+  if (__ballot(bad_tok)) kinds |= 2u;
+  bool bad_pos = (lane <= K) && (vp[lane] != p0 + lane);
+  if (__ballot(bad_pos)) kinds |= 8u;
+  if (p0 < 0 || p0 > 0x7FFFFFFF - 2 * K - 1) kinds |= 4u;  // position range
+  int seq_len = 0;
+  if (kinds == 0) {
+    seq_len = p0 + acc + K;
+    const int nb = (seq_len + a.block_size - 1) / a.block_size;
+    if (nb > a.max_blocks) {
+      kinds |= 4u;
+    } else {
+      bool bad_blk = false;
+      const int32_t* btr = a.bt + (long long)r * a.max_blocks;
+      for (int b = lane; b < nb; b += 64) {
+        int id = btr[b];
+        bad_blk |= (id < 0 || id >= a.num_kv_blocks);
+      }
+      if (__ballot(bad_blk)) kinds |= 4u;
+    }
+  }
+
+  if (kinds) {
+    if (lane < S) {
+      a.ids[base + lane] = 0;
+      a.pos[base + lane] = 0;
+      a.hsrc[base + lane] = -1;
+      a.rej[base + lane] = 1;
+      a.msk[base + lane] = 0;
+      a.slots[base + lane] = -1;
+    }
+    if (lane < K) a.draft_rows[r * K + lane] = base + lane;
+    if (lane == 0) {
+      a.seq_lens[r] = 0;
+      atomicOr(&a.err[0], kinds);
+      atomicMin(&a.err[1], uint32_t(r));
+    }
+    return;
+  }
+
+  const int32_t* btr = a.bt + (long long)r * a.max_blocks;
+  if (lane < S) {
+    int tok, p, src;
+    uint8_t rej = 0, msk = 0;
+    if (lane <= K) {
+      p = vp[lane];
+      src = r * (K + 1) + lane;
+      if (lane < acc) tok = vt[lane + 1];
+      else if (lane == acc) tok = a.bonus[r];
+      else { tok = 0; rej = 1; }
+    } else {
+      const int m = lane - K;
+      tok = a.mask_id;
+      p = p0 + acc + m;
+      src = -1;
+      msk = 1;
+    }
+    long long slot = -1;
+    if (!rej) slot = (long long)btr[p / a.block_size] * a.block_size + p % a.block_size;
+    a.ids[base + lane] = tok;
+    a.pos[base + lane] = p;
+    a.hsrc[base + lane] = src;
+    a.rej[base + lane] = rej;
+    a.msk[base + lane] = msk;
+    a.slots[base + lane] = slot;
+  }
+  if (lane < K) a.draft_rows[r * K + lane] = (lane == 0) ? base + acc : base + K + lane;
+  if (lane == 0) a.seq_lens[r] = seq_len;
+}
+
+hipError_t launch_prepare(const PrepareArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  const int per = 4;  // requests (waves) per workgroup
+  hipLaunchKernelGGL(prepare_kernel, dim3((a.B + per - 1) / per), dim3(64 * per), 0, st, a);
+  return hipGetLastError();
+}
+
+// draft_hidden[s] = src >= 0 ? H[src] : h_shared, as 16-byte chunks.
+__global__ __launch_bounds__(256) void gather_kernel(int rows, int nsrc, int cpr,
+                                                     const int32_t* __restrict__ hsrc,
+                                                     const uint4* __restrict__ H,
+                                                     const uint4* __restrict__ hs,
+                                                     uint4* __restrict__ out) {
+  const long long total = (long long)rows * cpr;
+  for (long long c = blockIdx.x * (long long)blockDim.x + threadIdx.x; c < total;
+       c += (long long)gridDim.x * blockDim.x) {
+    const int row = int(c / cpr), k = int(c % cpr);
+    const int src = hsrc[row];
+    const uint4* p = (src >= 0 && src < nsrc) ? H + (long long)src * cpr : hs;
+    out[c] = p[k];
+  }
+}
+
+hipError_t launch_gather(int rows, int nsrc, int row_bytes, const int32_t* hsrc, const void* H,
+                         const void* h_shared, void* out, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int cpr = row_bytes / 16;
+  const long long total = (long long)rows * cpr;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(gather_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, rows, nsrc, cpr,
+                     hsrc, (const uint4*)H, (const uint4*)h_shared, (uint4*)out);
+  return hipGetLastError();
+}
+
+// a' = first j with t[j] != g[j] (else K); bonus' = g[a'].  One wave per request.
+__global__ __launch_bounds__(256) void verify_kernel(int B, int K, const int32_t* __restrict__ t,
+                                                     const int32_t* __restrict__ g,
+                                                     int32_t* __restrict__ acc,
+                                                     int32_t* __restrict__ bonus) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (r >= B) return;
+  const bool miss = lane < K && t[(long long)r * K + lane] != g[(long long)r * (K + 1) + lane];
+  const unsigned long long m = __ballot(miss);
+  const int a = m ? (__ffsll((long long)m) - 1) : K;
+  if (lane == 0) {
+    acc[r] = a;
+    bonus[r] = g[(long long)r * (K + 1) + a];
+  }
+}
+
+hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32_t* acc,
+                         int32_t* bonus, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(verify_kernel, dim3((B + 3) / 4), dim3(256), 0, st, B, K, t, g, acc, bonus);
+  return hipGetLastError();
+}
+
+}  // namespace pe

@@ -1,0 +1,62 @@
+// RMSNorm: y = x / sqrt(mean(x^2) + eps) * gain, fp32 arithmetic, one
+// workgroup per output row, 16-byte loads.  The drafter is a pre-norm
+// Transformer ("P-EAGLE: parallel speculative decoding in vLLM", Architecture
+// and mechanism: N-layer Transformer, then the LM head); the final norm runs
+// only on the draft rows that feed the LM head.
+#include "pe_common.h"
+#include "pe_internal.h"
+
+namespace pe {
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const T* __restrict__ x,
+                                                      const T* __restrict__ gain,
+                                                      T* __restrict__ out,
+                                                      const int32_t* __restrict__ rows_idx,
+                                                      int rows_bound, float eps) {
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
+  const int i = blockIdx.x;
+  int src = rows_idx ? rows_idx[i] : i;
+  if (src < 0 || src >= rows_bound) src = 0;
+  const T* xr = x + (long long)src * d;
+  T* yr = out + (long long)i * d;
+  const int nc = d / V;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+    uint4 raw = ld16(xr + c * V);
+    const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int j = 0; j < V; ++j) { float v = Elt<T>::ld(e + j); ss += v * v; }
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < int(blockDim.x >> 6); ++w) tot += red[w];
+  const float rs = rsqrtf(tot / float(d) + eps);
+  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+    uint4 raw = ld16(xr + c * V), gr = ld16(gain + c * V), o;
+    const T* e = reinterpret_cast<const T*>(&raw);
+    const T* g = reinterpret_cast<const T*>(&gr);
+    T* oe = reinterpret_cast<T*>(&o);
+#pragma unroll
+    for (int j = 0; j < V; ++j) Elt<T>::st(oe + j, Elt<T>::ld(e + j) * rs * Elt<T>::ld(g + j));
+    *reinterpret_cast<uint4*>(yr + c * V) = o;
+  }
+}
+
+hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void* gain, void* out,
+                          const int32_t* rows_idx, int rows_bound, float eps, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(rows), dim3(256), 0, st, d,
+                       (const uint16_t*)x, (const uint16_t*)gain, (uint16_t*)out, rows_idx,
+                       rows_bound, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, st, d, (const float*)x,
+                       (const float*)gain, (float*)out, rows_idx, rows_bound, eps);
+  return hipGetLastError();
+}
+
+}  // namespace pe

@@ -1,0 +1,226 @@
+/*
+ * pe.h -- C ABI of libpe, the MI355X (gfx950) P-EAGLE parallel-draft step.
+ *
+ * One draft step is four calls, in this order, on one stream:
+ *   pe_prepare        batch metadata for the draft batch
+ *   pe_gather_hidden  target hidden states into their slots, h_shared into MASK slots
+ *   pe_draft_forward  one drafter pass over every slot, LM head + argmax -> t_1..t_K
+ *   pe_verify         greedy verification -> accepted length and bonus token
+ * pe_step_graph captures the four into one hipGraph and replays it.
+ *
+ * Sources (page titles as published):
+ *   [P1] "P-EAGLE: parallel speculative decoding in vLLM" -- sections
+ *        "Architecture and mechanism" (Step 2, Parallel Drafting), "vLLM
+ *        implementation details" (Fused Triton kernel; Hidden-state
+ *        management; KV cache and CUDA Graphs), "Benchmarks" (Acceptance length).
+ *   [P3] "AWS and vLLM ship P-EAGLE" -- "How it works", "Integration and numbers".
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers must point to device memory (any
+ *     allocator; the library never frees caller memory).  Float/bf16 tensors
+ *     and the KV caches must be 16-byte aligned; int32 arrays 4-byte aligned;
+ *     int64 arrays 8-byte aligned.
+ *   - Storage type of weights, hidden states and KV caches is cfg.dtype:
+ *     PE_F32 (IEEE float32) or PE_BF16 (bfloat16 bit patterns).  Row-major.
+ *   - Every call is asynchronous on the context's stream; nothing
+ *     synchronizes except pe_get_device_error.
+ *   - Host-detectable argument errors (null pointers, sizes out of range,
+ *     misalignment) return PE_ERR_INVALID_ARG and launch nothing.
+ *   - Data-dependent errors found on the device (see PE_DEVERR_*) never fault:
+ *     the offending request turns into padding (all slots rejected, KV slot
+ *     -1, seq_len 0, draft tokens -1) and a sticky device error word records
+ *     the kinds and the lowest failing request; pe_get_device_error reads it.
+ *   - One context per stream; calls on one context must not overlap.
+ *   - B == 0 is valid and launches nothing.
+ */
+#ifndef PE_H
+#define PE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pe_status {
+  PE_OK = 0,
+  PE_ERR_INVALID_ARG = 1,
+  PE_ERR_NOMEM = 2,
+  PE_ERR_HIP = 3,          /* a HIP runtime call failed; pe_last_error() has text */
+  PE_ERR_UNSUPPORTED = 4   /* a shape the kernels do not implement */
+} pe_status;
+
+typedef enum pe_dtype { PE_F32 = 0, PE_BF16 = 1 } pe_dtype;
+
+/* Device error kinds (bitmask), see pe_get_device_error. */
+#define PE_DEVERR_ACCEPTED 1u  /* num_accepted outside [0, K] */
+#define PE_DEVERR_TOKEN    2u  /* an accepted draft or the bonus token outside [0, vocab) */
+#define PE_DEVERR_BLOCK    4u  /* p0 < 0, block table too short, or a block id outside [0, num_kv_blocks) */
+#define PE_DEVERR_LAYOUT   8u  /* verify positions are not p0, p0+1, ..., p0+K */
+
+#define PE_PADDING_SLOT_ID (-1) /* KV slot of a slot that must not write the cache [P1, KV cache] */
+#define PE_PAD_TOKEN 0          /* token id written into rejected slots */
+
+/* Drafter shape and step parameters, fixed for the life of a context. */
+typedef struct pe_config {
+  int32_t K;            /* draft depth (num_speculative_tokens), 1..32 */
+  int32_t max_num_seqs; /* largest B any call may pass, >= 1 */
+  int32_t d;            /* hidden size, multiple of 64 */
+  int32_t n_q_heads;    /* query heads */
+  int32_t n_kv_heads;   /* KV heads; n_q_heads % n_kv_heads == 0 */
+  int32_t head_dim;     /* 64 for PE_BF16; even and <= 128 for PE_F32 */
+  int32_t mlp;          /* MLP size I, multiple of 32 */
+  int32_t layers;       /* decoder layers N >= 1 */
+  int32_t vocab;        /* V, multiple of 16 */
+  int32_t block_size;   /* KV page size in tokens, multiple of 16 */
+  int32_t mask_id;      /* token id of MASK; its embedding row is emb(mask) [P1, Step 2] */
+  int32_t dtype;        /* pe_dtype */
+  float rms_eps;        /* RMSNorm epsilon */
+  float rope_theta;     /* RoPE base */
+} pe_config;
+
+/* Device pointers of one decoder layer.  Linear weights are [out, in]. */
+typedef struct pe_layer_weights {
+  const void* attn_norm; /* [d] */
+  const void* wq;        /* [n_q_heads*head_dim, d] */
+  const void* wk;        /* [n_kv_heads*head_dim, d] */
+  const void* wv;        /* [n_kv_heads*head_dim, d] */
+  const void* wo;        /* [d, n_q_heads*head_dim] */
+  const void* mlp_norm;  /* [d] */
+  const void* w_gate;    /* [mlp, d] */
+  const void* w_up;      /* [mlp, d] */
+  const void* w_down;    /* [d, mlp] */
+} pe_layer_weights;
+
+/* Drafter weights.  Device pointers, borrowed for the context's life;
+ * `layers` is a host array of cfg.layers entries, copied by pe_create. */
+typedef struct pe_weights {
+  const void* embed;      /* [vocab, d] token embeddings; row mask_id is emb(mask) */
+  const void* w_fc;       /* [d, 2d] fc over concat(emb, hidden), embedding first */
+  const pe_layer_weights* layers;
+  const void* final_norm; /* [d] */
+  const void* lm_head;    /* [vocab, d] */
+} pe_weights;
+
+/* The draft batch: caller-allocated device buffers that pe_prepare fills and
+ * the later calls read.  S = 2K slots per request, request r at base r*S:
+ * slots 0..K are the copied region (slot j at the previous verify position
+ * p0+j), slots K+1..2K-1 are the K-1 MASK slots [P1, Fused Triton kernel]. */
+typedef struct pe_batch {
+  int32_t* input_ids;    /* [B*S]  token per slot */
+  int32_t* positions;    /* [B*S]  sequence position per slot */
+  int32_t* hidden_src;   /* [B*S]  row of target_hidden, -1 = h_shared (hidden-state map) */
+  uint8_t* is_rejected;  /* [B*S]  1 for copied slots beyond the accepted prefix + 1 */
+  uint8_t* is_masked;    /* [B*S]  1 for MASK slots (by role, not by token) */
+  int64_t* slot_mapping; /* [B*S]  paged KV slot, PE_PADDING_SLOT_ID if rejected */
+  int32_t* draft_rows;   /* [B*K]  slots whose outputs are t_1..t_K: NTP slot, then MASK slots */
+  int32_t* seq_lens;     /* [B]    p0 + a + K (0 for a request turned into padding) */
+} pe_batch;
+
+typedef struct pe_ctx pe_ctx;
+
+/* Creates a context on the current HIP device.  Validates the shape (returns
+ * PE_ERR_UNSUPPORTED for shapes the kernels do not cover), copies cfg and the
+ * weight pointers, and allocates the workspace for max_num_seqs requests
+ * (activations, attention partials, argmax keys, the device error word).
+ * stream: a hipStream_t (NULL = the default stream). */
+pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_ctx** out);
+pe_status pe_destroy(pe_ctx* ctx);
+pe_status pe_set_stream(pe_ctx* ctx, void* stream);
+
+/* Batch preparation, one fused pass [P1, Fused Triton kernel; KV cache].
+ * Per request r (a = num_accepted[r], p0 = verify_positions[r*(K+1)]):
+ *   copied slot j=0..K: position verify_positions[r][j], hidden_src r(K+1)+j,
+ *     token verify_tokens[r][j+1] if j<a, bonus_tokens[r] if j==a (the NTP
+ *     slot), else PE_PAD_TOKEN and rejected;
+ *   MASK slot K+m, m=1..K-1: token mask_id, position p0+a+m, hidden_src -1;
+ *   slot_mapping = block_table[r][pos/bs]*bs + pos%bs, or -1 when rejected;
+ *   draft_rows[r] = {r*S+a, r*S+K+1, ..., r*S+2K-1}; seq_lens[r] = p0+a+K.
+ * Inputs (device): verify_tokens, verify_positions [B, K+1] int32 -- the
+ * previous verify batch x0, d_1..d_K and its positions; num_accepted,
+ * bonus_tokens [B]; block_table [B, max_blocks] int32.  num_kv_blocks is the
+ * size of the KV pool in blocks (for validation).  out: filled. */
+pe_status pe_prepare(pe_ctx* ctx, int32_t B,
+                     const int32_t* verify_tokens, const int32_t* verify_positions,
+                     const int32_t* num_accepted, const int32_t* bonus_tokens,
+                     const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                     const pe_batch* out);
+
+/* Hidden-state copy [P1, Hidden-state management]: draft_hidden[s] =
+ * target_hidden[hidden_src[s]] when hidden_src[s] >= 0, else h_shared; a bit
+ * copy.  target_hidden [B*(K+1), d], h_shared [d], draft_hidden [B*S, d],
+ * all cfg.dtype, device.  batch must come from pe_prepare. */
+pe_status pe_gather_hidden(pe_ctx* ctx, int32_t B, const pe_batch* batch,
+                           const void* target_hidden, const void* h_shared, void* draft_hidden);
+
+/* One drafter forward over all B*S slots [P1, Step 2: every position goes
+ * through the N-layer Transformer and the LM head, predicting t_1..t_K at
+ * once].  x = W_fc[emb(token); hidden]; per layer pre-norm attention (RoPE,
+ * KV written at slot_mapping, skipped for -1 [P1, KV cache], causal over the
+ * request's positions [0, position] through block_table) and SwiGLU MLP;
+ * final RMSNorm on the draft rows; argmax of W_lm z (lowest index on ties).
+ * k_cache, v_cache: host arrays of cfg.layers device pointers.
+ *   K cache layer l: [num_kv_blocks*block_size, n_kv_heads, head_dim]
+ *   V cache layer l: [num_kv_blocks, n_kv_heads, head_dim, block_size]
+ *                    (d-major inside a block)
+ * draft_tokens [B*K] int32 out (t_1..t_K per request, -1 for padding).
+ * logits: NULL, or [B*K, vocab] float32 out (debug/parity; costs bandwidth). */
+pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch,
+                           const void* draft_hidden,
+                           const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                           void* const* k_cache, void* const* v_cache,
+                           int32_t* draft_tokens, float* logits);
+
+/* Greedy verification [P1, Benchmarks, Acceptance length; P3, Integration
+ * and numbers]: num_accepted[r] = first j in 0..K-1 with draft_tokens[r][j]
+ * != target_tokens[r][j], or K; bonus_tokens[r] = target_tokens[r][that j].
+ * draft_tokens [B, K], target_tokens [B, K+1] int32 in; outputs [B] int32. */
+pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens,
+                    const int32_t* target_tokens, int32_t* num_accepted, int32_t* bonus_tokens);
+
+/* All buffers of one step, for pe_step_graph. */
+typedef struct pe_step_args {
+  const int32_t* verify_tokens;
+  const int32_t* verify_positions;
+  const int32_t* num_accepted;
+  const int32_t* bonus_tokens;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t num_kv_blocks;
+  pe_batch batch;
+  const void* target_hidden;
+  const void* h_shared;
+  void* draft_hidden;
+  void* const* k_cache;      /* host array, cfg.layers entries */
+  void* const* v_cache;
+  int32_t* draft_tokens;
+  float* logits;             /* NULL unless wanted */
+  const int32_t* target_tokens;
+  int32_t* accepted_out;     /* pe_verify outputs; may alias nothing above */
+  int32_t* bonus_out;
+} pe_step_args;
+
+/* Captures prepare -> gather -> forward -> verify for (B, *args) into a
+ * hipGraph on the first call and replays it on later calls with the same B
+ * and the same pointers (values inside the buffers may change between
+ * replays: a, p0, tokens and block tables are read on the device).  A call
+ * with different pointers or B recaptures: capture runs on a private
+ * non-blocking stream of the context (the legacy default stream cannot be
+ * captured) after the context's stream has drained; every launch of the graph
+ * is enqueued on the context's stream.  The graph holds no memset node.  [P1, KV cache and CUDA Graphs: one graph covers the draft
+ * batch of K x max_num_seqs draft rows.] */
+pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args);
+
+/* Synchronizes the context's stream, reads and clears the sticky device error
+ * word.  kinds: OR of PE_DEVERR_*; first_request: lowest failing request
+ * index, or -1 when kinds == 0. */
+pe_status pe_get_device_error(pe_ctx* ctx, uint32_t* kinds, int32_t* first_request);
+
+/* Text of the last error on this thread ("" if none). */
+const char* pe_last_error(void);
+const char* pe_status_string(pe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PE_H */

@@ -1,0 +1,122 @@
+"""Helpers for the GPU parity tests: run one draft step through the C ABI on
+seeded synthetic inputs and compare with the CPU oracle."""
+import numpy as np
+import torch
+
+import oracle as O
+from drafting_pe_prepare_amd import binding as pb
+from drafting_pe_prepare_amd import synth
+
+LOGIT_TOL = {"bf16": 2e-2, "f32": 1e-4}   # max |dlogit| / RMS(oracle logits)
+GAP = 1e-2                                  # top-2 gap above which tokens must match
+
+
+def oracle_precision(w):
+    return "bf16" if w.dtype == "bf16" else "f64"
+
+
+class Setup:
+    """Weights and a context for workload `w` (weights uploaded once)."""
+
+    def __init__(self, w, seed=None, max_B=None, prm=None):
+        self.w = w
+        self.prm = synth.weights(w, seed) if prm is None else prm
+        self.dev = pb.upload_weights(self.prm)
+        self.ctx = pb.Context(w, self.dev, max_num_seqs=max_B or w.batch)
+
+    def close(self):
+        self.ctx.close()
+
+
+def run_step(st: Setup, inp: dict, want_logits=True, B=None):
+    """prepare -> gather -> forward -> verify on the GPU; returns host copies."""
+    w = st.w
+    B = w.batch if B is None else B
+    K, d = w.K, w.d
+    t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+         ("verify_tokens", "verify_positions", "num_accepted", "bonus_tokens", "block_table",
+          "target_tokens", "target_hidden")}
+    kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+    batch = pb.Batch(max(B, 1), K)
+    nkv = int(inp["num_kv_blocks"])
+    pb.pe_prepare(st.ctx, B, t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                  t["bonus_tokens"], t["block_table"], nkv, batch)
+    sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dh = torch.zeros((max(B, 1) * 2 * K, d), dtype=sdt, device="cuda")
+    pb.pe_gather_hidden(st.ctx, B, batch, t["target_hidden"], st.dev["h_shared"], dh)
+    tok = torch.full((max(B, 1) * K,), -7, dtype=torch.int32, device="cuda")
+    lg = torch.zeros((max(B, 1) * K, w.vocab), dtype=torch.float32, device="cuda") if want_logits else None
+    pb.pe_draft_forward(st.ctx, B, batch, dh, t["block_table"], nkv,
+                        [k for k, _ in kv], [v for _, v in kv], tok, lg)
+    acc = torch.full((max(B, 1),), -7, dtype=torch.int32, device="cuda")
+    bon = torch.full((max(B, 1),), -7, dtype=torch.int32, device="cuda")
+    pb.pe_verify(st.ctx, B, tok, t["target_tokens"], acc, bon)
+    torch.cuda.synchronize()
+    out = {
+        "batch": batch.host(B, K),
+        "draft_hidden": pb.to_host(dh)[:B * 2 * K],
+        "tokens": tok.cpu().numpy()[:B * K],
+        "logits": lg.cpu().numpy()[:B * K] if want_logits else None,
+        "kv": [(pb.to_host(k), pb.to_host(v)) for k, v in kv],
+        "accepted": acc.cpu().numpy()[:B],
+        "bonus": bon.cpu().numpy()[:B],
+        "error": pb.pe_get_device_error(st.ctx),
+    }
+    return out
+
+
+def oracle_step(w, prm, inp, requests=None, precision=None):
+    b = O.prepare(inp["verify_tokens"], inp["verify_positions"], inp["num_accepted"],
+                  inp["bonus_tokens"], inp["block_table"], inp["num_kv_blocks"],
+                  w.K, w.vocab, w.mask_id, w.block_size)
+    hd = O.gather_hidden(b["hidden_src"], inp["target_hidden"], prm["h_shared"])
+    fw = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"],
+                         precision or oracle_precision(w), requests=requests)
+    return b, hd, fw
+
+
+def assert_metadata_equal(gpu_batch, ob):
+    for f in pb.BATCH_FIELDS:
+        np.testing.assert_array_equal(gpu_batch[f], ob[f], err_msg=f)
+
+
+def assert_tokens_logits(tokens, logits, o_logits, tol_rel, rows=None):
+    """Logits within tol_rel * RMS; tokens equal wherever the oracle's top-2
+    gap exceeds GAP, otherwise the GPU token must be near-maximal in the
+    oracle's logits.  Returns the number of rows with a tight gap."""
+    if rows is not None:
+        tokens, logits = tokens[rows], logits[rows]
+    rms = float(np.sqrt(np.mean(o_logits ** 2)))
+    tol = tol_rel * rms
+    err = float(np.max(np.abs(logits.astype(np.float64) - o_logits)))
+    assert err <= tol, f"max |dlogit| {err:.3e} > {tol:.3e} (rms {rms:.3e})"
+    tight = 0
+    for i in range(o_logits.shape[0]):
+        srt = np.sort(o_logits[i])
+        gap = srt[-1] - srt[-2]
+        if gap > GAP:
+            assert tokens[i] == int(np.argmax(o_logits[i])), (i, tokens[i], np.argmax(o_logits[i]), gap)
+        else:
+            tight += 1
+            assert o_logits[i, tokens[i]] >= srt[-1] - 2 * tol, (i, tokens[i])
+    return tight
+
+
+def assert_kv(w, gpu_kv, inp, fw, rtol_ulps=2):
+    """The caches after the step equal the caches before everywhere except at
+    the slots the oracle wrote; there they match the oracle's rows."""
+    bs = w.block_size
+    for li, ((kc_g, vc_g), (kc0, vc0)) in enumerate(zip(gpu_kv, inp["kv"])):
+        slots, kr, vr = fw["kv_writes"][li]
+        mask = np.ones(kc0.shape[0], bool)
+        mask[slots] = False
+        np.testing.assert_array_equal(kc_g[mask], kc0[mask], err_msg=f"K cache layer {li} changed off-slot")
+        vg = vc_g.transpose(0, 3, 1, 2).reshape(-1, w.n_kv_heads, w.head_dim)
+        v0 = vc0.transpose(0, 3, 1, 2).reshape(-1, w.n_kv_heads, w.head_dim)
+        np.testing.assert_array_equal(vg[mask], v0[mask], err_msg=f"V cache layer {li} changed off-slot")
+        if len(slots):
+            gk = O.widen(kc_g[slots])
+            gv = O.widen(vg[slots])
+            scale = 2.0 ** -7 if w.dtype == "bf16" else 1e-5
+            np.testing.assert_allclose(gk, kr, atol=rtol_ulps * scale * max(1.0, np.abs(kr).max()))
+            np.testing.assert_allclose(gv, vr, atol=rtol_ulps * scale * max(1.0, np.abs(vr).max()))

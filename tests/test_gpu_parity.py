@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Bit-exact for ids, positions, masks, slot maps, draft
+rows, seq_lens, gathered hidden rows, accepted lengths and bonus tokens;
+draft tokens bit-exact where the oracle's top-2 gap exceeds 1e-2; logits within
+2e-2 x RMS (bf16) / 1e-4 x RMS (fp32)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from drafting_pe_prepare_amd import configs, synth
+from drafting_pe_prepare_amd import binding as pb
+
+from pe_gpu import (LOGIT_TOL, Setup, assert_kv, assert_metadata_equal, assert_tokens_logits,
+                    oracle_step, run_step)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pb.load()
+
+
+# small bf16 shapes that still span several tiles and ragged tails
+SMALL_BF16 = configs.TINY.with_(dtype="bf16", d=256, mlp=1024, vocab=1024, prefix=("fixed", 64, 0),
+                                weight_std=1 / 16)
+
+
+def _full_check(w, seed=None, requests=None, logits=True):
+    _say(f"case {w.name} B={w.batch} K={w.K} d={w.d} dtype={w.dtype} seed={seed}")
+    st = Setup(w, seed)
+    try:
+        inp = synth.step_inputs(w, seed)
+        g = run_step(st, inp, want_logits=logits)
+        ob, ohd, fw = oracle_step(w, st.prm, inp, requests=requests)
+        assert_metadata_equal(g["batch"], ob)
+        np.testing.assert_array_equal(g["draft_hidden"], ohd)
+        assert g["error"] == (0, -1)
+        K = w.K
+        rows = None if requests is None else np.concatenate([np.arange(r * K, (r + 1) * K) for r in requests])
+        tight = assert_tokens_logits(g["tokens"], g["logits"], fw["logits"], LOGIT_TOL[w.dtype], rows)
+        if requests is None:
+            assert_kv(w, g["kv"], inp, fw)
+        acc, bon = O.verify(g["tokens"].reshape(w.batch, K), inp["target_tokens"])
+        np.testing.assert_array_equal(g["accepted"], acc)
+        np.testing.assert_array_equal(g["bonus"], bon)
+        return tight
+    finally:
+        st.close()
+
+
+def test_tiny_f32():
+    _full_check(configs.TINY)
+
+
+@pytest.mark.parametrize("K,B,seed", [(4, 1, 1), (1, 3, 2), (3, 4, 3), (7, 2, 4), (15, 2, 5), (32, 1, 6)])
+def test_small_bf16(K, B, seed):
+    _full_check(SMALL_BF16.with_(K=K, batch=B, accepted="uniform"), seed=seed)
+
+
+@pytest.mark.parametrize("B", [5, 12])
+def test_small_bf16_tiled_path(B):
+    """B*2K > 64 rows: the LDS-tiled GEMM path and the tiled LM head."""
+    _full_check(SMALL_BF16.with_(K=7, batch=B, accepted="uniform",
+                                 prefix=("lognormal", 300.0, 0.8)), seed=40 + B)
+
+
+@pytest.mark.parametrize("K", [2, 5])
+def test_small_f32_shapes(K):
+    _full_check(configs.TINY.with_(K=K, batch=3, accepted="uniform", prefix=("uniform", 20, 200)),
+                seed=50 + K)
+
+
+def test_prepare_fuzz_and_errors():
+    """Random B, K, a, p0 and block tables, with planted invalid requests:
+    metadata and the device error word match the oracle bit for bit."""
+    rng = np.random.default_rng(123)
+    w0 = SMALL_BF16
+    st = Setup(w0.with_(K=32), max_B=64)
+    try:
+        for trial in range(40):
+            K = int(rng.integers(1, 33))
+            B = int(rng.integers(1, 64))
+            w = w0.with_(K=K, batch=B, accepted="uniform", prefix=("uniform", 0, 500))
+            inp = synth.step_inputs(w, seed=1000 + trial, kv=False)
+            if trial % 3 == 0:
+                r = int(rng.integers(0, B))
+                kind = trial % 4
+                if kind == 0:
+                    inp["num_accepted"][r] = K + 1 + trial
+                elif kind == 1:
+                    inp["bonus_tokens"][r] = w.vocab + 5
+                elif kind == 2:
+                    inp["block_table"][r, 0] = -1
+                else:
+                    inp["verify_positions"][r, -1] += 3
+            # a context is per K: prepare only needs K, so make one per trial
+            ctx = pb.Context(w, st.dev, max_num_seqs=64)
+            batch = pb.Batch(B, K)
+            t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+                 ("verify_tokens", "verify_positions", "num_accepted", "bonus_tokens", "block_table")}
+            pb.pe_prepare(ctx, B, t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                          t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], batch)
+            err = pb.pe_get_device_error(ctx)
+            ob = O.prepare(inp["verify_tokens"], inp["verify_positions"], inp["num_accepted"],
+                           inp["bonus_tokens"], inp["block_table"], inp["num_kv_blocks"], K,
+                           w.vocab, w.mask_id, w.block_size)
+            assert_metadata_equal(batch.host(B, K), ob)
+            assert err == (ob["error_kinds"], ob["error_first"]), (trial, err, ob["error_kinds"], ob["error_first"])
+            ctx.close()
+    finally:
+        st.close()
+
+
+def test_padded_request_gets_no_kv_write_and_token_minus_one():
+    w = SMALL_BF16.with_(K=4, batch=3, accepted="uniform")
+    st = Setup(w, seed=7)
+    try:
+        inp = synth.step_inputs(w, seed=7)
+        inp["num_accepted"][1] = 9
+        g = run_step(st, inp)
+        ob, ohd, fw = oracle_step(w, st.prm, inp)
+        assert_metadata_equal(g["batch"], ob)
+        assert g["error"] == (O.ERR_ACCEPTED, 1)
+        assert np.all(g["tokens"][4:8] == -1)
+        assert np.all(fw["tokens"][4:8] == -1)
+        assert_kv(w, g["kv"], inp, fw)
+        keep = np.r_[0:4, 8:12]
+        assert_tokens_logits(g["tokens"], g["logits"], fw["logits"][keep], LOGIT_TOL["bf16"], keep)
+    finally:
+        st.close()
+
+
+def test_verify_exhaustive_small_alphabet():
+    import itertools
+    w = SMALL_BF16.with_(K=4)
+    st = Setup(w, max_B=1024)
+    try:
+        K = 4
+        t = np.array(list(itertools.product(range(3), repeat=K)), np.int32)
+        g = np.array(list(itertools.product(range(3), repeat=K + 1)), np.int32)
+        for lo in range(0, len(t) * len(g), 1024):
+            idx = np.arange(lo, min(lo + 1024, len(t) * len(g)))
+            T = t[idx // len(g)]
+            G = g[idx % len(g)]
+            B = len(idx)
+            acc = torch.empty(B, dtype=torch.int32, device="cuda")
+            bon = torch.empty(B, dtype=torch.int32, device="cuda")
+            pb.pe_verify(st.ctx, B, pb.to_device(T), pb.to_device(G), acc, bon)
+            oa, ob = O.verify(T, G)
+            np.testing.assert_array_equal(acc.cpu().numpy(), oa)
+            np.testing.assert_array_equal(bon.cpu().numpy(), ob)
+    finally:
+        st.close()
+
+
+def test_empty_batch_is_a_no_op():
+    w = SMALL_BF16
+    st = Setup(w)
+    try:
+        inp = synth.step_inputs(w.with_(batch=1))
+        z = torch.zeros(16, dtype=torch.int32, device="cuda")
+        pb.pe_verify(st.ctx, 0, z, z, z, z)
+        batch = pb.Batch(1, w.K)
+        bt = pb.to_device(inp["block_table"])
+        pb.pe_prepare(st.ctx, 0, z, z, z, z, bt, 1, batch)
+        torch.cuda.synchronize()
+    finally:
+        st.close()
+
+
+def test_invalid_arguments_are_rejected_on_the_host():
+    w = SMALL_BF16
+    st = Setup(w)
+    try:
+        z = torch.zeros(16, dtype=torch.int32, device="cuda")
+        with pytest.raises(pb.PeError) as e:
+            pb.pe_verify(st.ctx, w.batch + 5, z, z, z, z)
+        assert e.value.status == 1
+        with pytest.raises(pb.PeError):
+            pb._check(pb._lib.pe_verify(st.ctx.h, 1, None, None, None, None))
+    finally:
+        st.close()
+
+
+def test_closed_loop_rounds():
+    """Verify outputs feed the next prepare; targets are planted so chosen
+    accept counts happen; every round matches the oracle."""
+    w = SMALL_BF16.with_(K=5, batch=3, accepted="uniform", prefix=("uniform", 30, 90))
+    st = Setup(w, seed=9)
+    try:
+        inp = synth.step_inputs(w, seed=9)
+        B, K = w.batch, w.K
+        nb = 16
+        inp["block_table"] = (np.arange(B * nb, dtype=np.int32).reshape(B, nb) * 7) % (B * nb)
+        inp["num_kv_blocks"] = B * nb
+        inp["kv"] = synth.kv_pool(w, B * nb, 3)
+        rng = np.random.default_rng(2)
+        for rnd in range(4):
+            _say(f"closed loop round {rnd}")
+            inp["target_hidden"] = synth.normal(60 + rnd, "H", (B * (K + 1), w.d))
+            og_b, og_hd, fw = oracle_step(w, st.prm, inp)
+            t = fw["tokens"].reshape(B, K)
+            want = rng.integers(0, K + 1, size=B)
+            gt = rng.integers(0, w.vocab - 1, size=(B, K + 1)).astype(np.int32)
+            for r in range(B):
+                gt[r, :want[r]] = t[r, :want[r]]
+                if want[r] < K and gt[r, want[r]] == t[r, want[r]]:
+                    gt[r, want[r]] = (t[r, want[r]] + 1) % (w.vocab - 1)
+            inp["target_tokens"] = gt
+            g = run_step(st, inp)
+            assert_metadata_equal(g["batch"], og_b)
+            assert_tokens_logits(g["tokens"], g["logits"], fw["logits"], LOGIT_TOL["bf16"])
+            # verify on the GPU's own drafts; where those equal the oracle's
+            # (every row whose top-2 gap is wide), the planted count happens
+            oa, obn = O.verify(g["tokens"].reshape(B, K), gt)
+            np.testing.assert_array_equal(g["accepted"], oa)
+            np.testing.assert_array_equal(g["bonus"], obn)
+            same = np.all(g["tokens"].reshape(B, K) == t, axis=1)
+            np.testing.assert_array_equal(g["accepted"][same], want[same])
+            t = g["tokens"].reshape(B, K)
+            # next round: the GPU's caches, verify batch [bonus, t_1..t_K]
+            inp["kv"] = g["kv"]
+            p0 = inp["verify_positions"][:, 0] + inp["num_accepted"] + 1
+            inp["verify_tokens"] = np.concatenate([inp["bonus_tokens"][:, None], t], 1).astype(np.int32)
+            inp["verify_positions"] = (p0[:, None] + np.arange(K + 1)[None]).astype(np.int32)
+            inp["num_accepted"] = g["accepted"].astype(np.int32)
+            inp["bonus_tokens"] = g["bonus"].astype(np.int32)
+    finally:
+        st.close()
+
+
+def test_step_graph_replays_match_eager():
+    """One captured graph (prepare+gather+forward+verify) replayed several
+    times, with eager work and synchronization in between; every replay
+    equals the eager result."""
+    w = SMALL_BF16.with_(K=7, batch=6, accepted="uniform", prefix=("uniform", 40, 400))
+    st = Setup(w, seed=11)
+    try:
+        inp = synth.step_inputs(w, seed=11)
+        eager = run_step(st, inp)
+        B, K = w.batch, w.K
+        t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+             ("verify_tokens", "verify_positions", "num_accepted", "bonus_tokens", "block_table",
+              "target_tokens", "target_hidden")}
+        kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+        kv0 = [(k.clone(), v.clone()) for k, v in kv]
+        batch = pb.Batch(B, K)
+        dh = torch.zeros((B * 2 * K, w.d), dtype=torch.bfloat16, device="cuda")
+        tok = torch.zeros(B * K, dtype=torch.int32, device="cuda")
+        acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+        bon = torch.zeros(B, dtype=torch.int32, device="cuda")
+        args = pb.make_step_args(t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                                 t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], batch,
+                                 t["target_hidden"], st.dev["h_shared"], dh,
+                                 [k for k, _ in kv], [v for _, v in kv], tok, t["target_tokens"],
+                                 acc, bon)
+        for rep in range(4):
+            for (k, v), (k0, v0) in zip(kv, kv0):
+                k.copy_(k0)
+                v.copy_(v0)
+            tok.fill_(-5)
+            pb.pe_step_graph(st.ctx, B, args)
+            torch.cuda.synchronize()
+            _ = torch.randn(1000, device="cuda").sum().item()  # eager work between replays
+            np.testing.assert_array_equal(tok.cpu().numpy(), eager["tokens"], err_msg=f"replay {rep}")
+            np.testing.assert_array_equal(acc.cpu().numpy(), eager["accepted"])
+            np.testing.assert_array_equal(bon.cpu().numpy(), eager["bonus"])
+            for (k, v), (ke, ve) in zip(kv, eager["kv"]):
+                np.testing.assert_array_equal(pb.to_host(k), ke)
+                np.testing.assert_array_equal(pb.to_host(v), ve)
+    finally:
+        st.close()
+
+
+@pytest.mark.slow
+def test_full_c1():
+    """The c=1 20B-class workload at full size, every output checked."""
+    _full_check(configs.C1)
+
+
+@pytest.mark.slow
+def test_full_c64_sampled():
+    """The c=64 20B-class workload at full size: metadata and verify for all
+    requests, logits/tokens for sampled requests (the oracle computes those
+    requests alone; rows are independent apart from attention)."""
+    tight = _full_check(configs.C64, requests=[0, 17, 63])
+    assert tight <= 3
