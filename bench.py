@@ -1,0 +1,282 @@
+#!/usr/bin/env python
+"""Throughput of the P-EAGLE parallel-draft step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: pe_prepare ->
+pe_gather_hidden -> pe_draft_forward -> pe_verify, replayed as one hipGraph
+(pe_step_graph).  Inputs are seeded synthetic tensors already resident in
+HBM when the timed region starts.
+
+Default workload: the c=1 20B-class drafter (B=1, K=7, d=2880, 64q/8kv x 64,
+MLP 7680, 1 layer, V=201088, bf16, prefix 2048).  The same run also measures
+the c=64 workload (B=64, lognormal prefixes) and reports it under "c64".
+
+Output: one JSON line.  `roofline` is for the dominant kernel (the LM head):
+algorithmic bytes (or flops) per launch divided by its average duration, taken
+from HIP events around each launch on the library's stream during an eager
+timed pass of the same steps.  `cpu_baseline` times the CPU oracle on the
+host on a bounded sample of the c=1 step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "draft tokens/s and us per parallel-draft step, K=7, c=1 and c=64 (1 GPU)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="c1_20b")
+    p.add_argument("--no-c64", action="store_true", help="skip the c=64 measurement")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one step (measurement section)
+# ---------------------------------------------------------------------------
+def weight_bytes(w):
+    e = 2 if w.dtype == "bf16" else 4
+    d, qd, kvd = w.d, w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    layer = (qd * d + 2 * kvd * d + d * qd + 3 * w.mlp * d + 2 * d) * e
+    return {"fc": 2 * d * d * e, "layers": w.layers * layer, "lm_head": w.vocab * d * e,
+            "final_norm": d * e}
+
+
+def step_work(w, inp):
+    """Algorithmic HBM bytes and flops of one step on these inputs."""
+    e = 2 if w.dtype == "bf16" else 4
+    B, K, d = w.batch, w.K, w.d
+    a = inp["num_accepted"].astype(int)
+    p0 = inp["verify_positions"][:, 0].astype(int)
+    seq = p0 + a + K
+    kvrow = w.n_kv_heads * w.head_dim * e * 2          # K and V of one position
+    wb = weight_bytes(w)
+    bytes_ = sum(wb.values())
+    bytes_ += B * 2 * K * d * e                          # embedding rows
+    bytes_ += B * (K + 1) * d * e + d * e                # target hidden + h_shared
+    bytes_ += 2 * B * 2 * K * d * e                      # draft hidden write + read
+    bytes_ += w.layers * int(seq.sum()) * kvrow          # KV read
+    bytes_ += w.layers * int((a + K).sum()) * kvrow      # KV write (valid slots)
+    valid = int((a + K).sum())
+    qd, kvd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    dense = 2 * d * d + w.layers * (qd * d + 2 * kvd * d + d * qd + 3 * w.mlp * d)
+    flops = 2 * valid * dense + 2 * B * K * w.vocab * d
+    # attention: each valid slot at position q scores and mixes q+1 positions
+    att = 0
+    for r in range(B):
+        pos = list(range(p0[r], p0[r] + a[r] + 1)) + [p0[r] + a[r] + m for m in range(1, K)]
+        att += sum(q + 1 for q in pos)
+    flops += w.layers * 4 * w.head_dim * w.n_q_heads * att
+    return {"bytes": bytes_, "flops": flops, "weight_bytes": sum(wb.values())}
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+def measure(w, steps, warmup, prm=None, dev=None, label=""):
+    import numpy as np
+    import torch
+    from drafting_pe_prepare_amd import binding as pb
+    from drafting_pe_prepare_amd import synth
+
+    t_setup = time.time()
+    if prm is None:
+        prm = synth.weights(w)
+    if dev is None:
+        dev = pb.upload_weights(prm)
+    inp = synth.step_inputs(w)
+    B, K = w.batch, w.K
+    ctx = pb.Context(w, dev, max_num_seqs=B)
+    t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+         ("verify_tokens", "verify_positions", "num_accepted", "bonus_tokens", "block_table",
+          "target_tokens", "target_hidden")}
+    kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+    batch = pb.Batch(B, K)
+    sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dh = torch.zeros((B * 2 * K, w.d), dtype=sdt, device="cuda")
+    tok = torch.zeros(B * K, dtype=torch.int32, device="cuda")
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    bon = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ks, vs = [k for k, _ in kv], [v for _, v in kv]
+    args = pb.make_step_args(t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                             t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], batch,
+                             t["target_hidden"], dev["h_shared"], dh, ks, vs, tok,
+                             t["target_tokens"], acc, bon)
+    torch.cuda.synchronize()
+    print(f"[bench] {label} setup {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    for _ in range(warmup):
+        pb.pe_step_graph(ctx, B, args)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        pb.pe_step_graph(ctx, B, args)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_step = wall * 1e3 / steps
+    err = pb.pe_get_device_error(ctx)
+    assert err == (0, -1), f"device error word {err}"
+    print(f"[bench] {label} graph: {ms_step * 1e3:.1f} us/step (events {ev_ms * 1e3 / steps:.1f})",
+          file=sys.stderr, flush=True)
+
+    # eager pass with per-phase HIP events on the library's stream
+    pb.pe_profile_enable(ctx, True)
+    pb.pe_profile_read(ctx, reset=True)
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    for _ in range(steps):
+        pb.pe_prepare(ctx, B, t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                      t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], batch)
+        pb.pe_gather_hidden(ctx, B, batch, t["target_hidden"], dev["h_shared"], dh)
+        pb.pe_draft_forward(ctx, B, batch, dh, t["block_table"], inp["num_kv_blocks"], ks, vs, tok)
+        pb.pe_verify(ctx, B, tok, t["target_tokens"], acc, bon)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - te) * 1e3 / steps
+    prof = pb.pe_profile_read(ctx, reset=True)
+    pb.pe_profile_enable(ctx, False)
+    phases_us = {p: (ms / n * 1e3 if n else 0.0) for p, (ms, n) in prof.items()}
+    per_step_us = {p: ms / steps * 1e3 for p, (ms, n) in prof.items()}
+
+    work = step_work(w, inp)
+    D = B * K
+    lm_us = phases_us["lmhead"]
+    lm_bytes = w.vocab * w.d * 2 + D * w.d * 2 + D * 4
+    lm_flops = 2 * D * w.vocab * w.d
+    if w.batch <= 4:
+        roof = {"kernel": "lm_head+argmax", "bound": "hbm",
+                "achieved": lm_bytes / (lm_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"kernel": "lm_head+argmax", "bound": "mfma",
+                "achieved": lm_flops / (lm_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["avg_launch_us"] = lm_us
+    roof["algorithmic_per_launch"] = lm_bytes if roof["bound"] == "hbm" else lm_flops
+    step_s = ms_step * 1e-3
+    out = {
+        "value": B * K / step_s,
+        "ms_per_step": ms_step,
+        "us_per_step": ms_step * 1e3,
+        "event_us_per_step": ev_ms * 1e3 / steps,
+        "eager_us_per_step": eager_ms * 1e3,
+        "roofline": roof,
+        "step": {"algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
+                 "hbm_GBs": work["bytes"] / step_s / 1e9,
+                 "hbm_frac": work["bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
+                 "mfma_TFs": work["flops"] / step_s / 1e12,
+                 "mfma_frac": work["flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFS},
+        "phases_us_per_launch": {p: round(v, 2) for p, v in phases_us.items()},
+        "phases_us_per_step": {p: round(v, 2) for p, v in per_step_us.items()},
+        "config": {"workload": w.name, "batch": B, "K": K, "d": w.d, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "mlp": w.mlp,
+                   "layers": w.layers, "vocab": w.vocab, "prefix": list(w.prefix),
+                   "mean_seq_len": float((inp["verify_positions"][:, 0] + inp["num_accepted"] + K).mean()),
+                   "seed": w.seed, "graph": True},
+    }
+    ctx.close()
+    del kv, t
+    torch.cuda.empty_cache()
+    return out, prm, dev
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, prm, seconds):
+    import numpy as np
+    import oracle as O
+    from drafting_pe_prepare_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    inp = synth.step_inputs(w)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        b = O.prepare(inp["verify_tokens"], inp["verify_positions"], inp["num_accepted"],
+                      inp["bonus_tokens"], inp["block_table"], inp["num_kv_blocks"], w.K,
+                      w.vocab, w.mask_id, w.block_size)
+        hd = O.gather_hidden(b["hidden_src"], inp["target_hidden"], prm["h_shared"])
+        fw = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16", want_logits=False)
+        O.verify(fw["tokens"].reshape(w.batch, w.K), inp["target_tokens"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or el / n * (n + 1) > 3 * seconds:
+            break
+    return {"value": w.batch * w.K * n / el, "unit": "draft tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} full {w.name} step(s) (B={w.batch}, K={w.K}; prepare+gather+forward"
+                      f"+verify, fp64 with bf16 storage rounding) in {el:.1f}s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by request across GPUs with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from drafting_pe_prepare_amd import binding as pb
+    from drafting_pe_prepare_amd import configs
+    pb.load()
+    assert torch.cuda.is_available(), "no GPU"
+    w = configs.BY_NAME[args.workload]
+    main_res, prm, dev = measure(w, args.steps, args.warmup, label=w.name)
+    line = {
+        "metric": METRIC,
+        "value": main_res["value"],
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "us_per_step": main_res["us_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) hidden/KV; no trained weights)",
+        "config": main_res["config"],
+        "roofline": main_res["roofline"],
+        "step": main_res["step"],
+        "phases_us_per_step": main_res["phases_us_per_step"],
+        "event_us_per_step": main_res["event_us_per_step"],
+        "eager_us_per_step": main_res["eager_us_per_step"],
+    }
+    if not args.no_c64 and w.name == "c1_20b":
+        c64, _, _ = measure(configs.C64, max(20, args.steps // 4), max(5, args.warmup // 4),
+                            prm=prm, dev=dev, label="c64_20b")
+        line["c64"] = {k: c64[k] for k in ("value", "us_per_step", "roofline", "step",
+                                            "phases_us_per_step", "config")}
+        line["c64"]["config"]["weights"] = "same drafter weights as the c=1 workload"
+    if not args.no_cpu_baseline:
+        del dev
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline(w, prm, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line, default=lambda o: o.item() if hasattr(o, "item") else str(o)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,9 @@ DEVERR_ACCEPTED, DEVERR_TOKEN, DEVERR_BLOCK, DEVERR_LAYOUT = 1, 2, 4, 8
 
 EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_hidden",
            "pe_draft_forward", "pe_verify", "pe_step_graph", "pe_get_device_error",
-           "pe_last_error", "pe_status_string")
+           "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
+PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
+          "verify")
 
 vp, i32 = ctypes.c_void_p, ctypes.c_int32
 
@@ -91,6 +93,8 @@ def load(path: str = LIB_PATH):
     lib.pe_verify.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.pe_step_graph.argtypes = [vp, i32, P(PeStepArgs)]
     lib.pe_get_device_error.argtypes = [vp, P(ctypes.c_uint32), P(i32)]
+    lib.pe_profile_enable.argtypes = [vp, ctypes.c_int]
+    lib.pe_profile_read.argtypes = [vp, P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int]
     lib.pe_last_error.restype = ctypes.c_char_p
     lib.pe_status_string.restype = ctypes.c_char_p
     for n in EXPORTS[:-2]:
@@ -262,3 +266,15 @@ def upload_weights(w: dict, device="cuda") -> dict:
     out = {k: to_device(v, device) for k, v in w.items() if k != "layers"}
     out["layers"] = [{k: to_device(v, device) for k, v in lw.items()} for lw in w["layers"]]
     return out
+
+
+def pe_profile_enable(ctx: Context, on: bool = True):
+    _check(_lib.pe_profile_enable(ctx.h, 1 if on else 0))
+
+
+def pe_profile_read(ctx: Context, reset: bool = True) -> dict:
+    """{phase: (total ms, launches)} since the last reset; synchronizes."""
+    ms = (ctypes.c_double * len(PHASES))()
+    n = (ctypes.c_int64 * len(PHASES))()
+    _check(_lib.pe_profile_read(ctx.h, ms, n, 1 if reset else 0))
+    return {p: (ms[i], n[i]) for i, p in enumerate(PHASES)}

@@ -77,7 +77,47 @@ struct pe_ctx {
   int graph_B = -1;
   pe_step_args graph_args;
   std::vector<void*> graph_kv;
+  // profiling
+  bool prof_on = false;
+  bool capturing = false;
+  std::vector<hipEvent_t> ev_free;
+  struct Rec { int phase; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+  double prof_ms[PE_PH_COUNT] = {};
+  int64_t prof_n[PE_PH_COUNT] = {};
 };
+
+namespace {
+
+// Brackets one phase's launches with an event pair when profiling is on.
+struct Timed {
+  pe_ctx* c;
+  int phase;
+  hipEvent_t a = nullptr, b = nullptr;
+  static hipEvent_t take(pe_ctx* c) {
+    if (!c->ev_free.empty()) { hipEvent_t e = c->ev_free.back(); c->ev_free.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  Timed(pe_ctx* ctx, int ph) : c(ctx), phase(ph) {
+    if (!c->prof_on || c->capturing || c->recs.size() > 200000) return;
+    a = take(c);
+    b = take(c);
+    if (a && b) (void)hipEventRecord(a, c->stream);
+  }
+  ~Timed() {
+    if (a && b) {
+      (void)hipEventRecord(b, c->stream);
+      c->recs.push_back({phase, a, b});
+    } else {
+      if (a) c->ev_free.push_back(a);
+      if (b) c->ev_free.push_back(b);
+    }
+  }
+};
+
+}  // namespace
 
 namespace {
 
@@ -86,6 +126,8 @@ void free_ctx(pe_ctx* c) {
   if (c->gexec) (void)hipGraphExecDestroy(c->gexec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
   if (c->capture_stream) (void)hipStreamDestroy(c->capture_stream);
+  for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+  for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->counter, c->err,
                   c->part_o, c->part_ml, c->rope_inv, c->rope_inv_d};
   for (void* p : bufs)
@@ -297,6 +339,7 @@ pe_status pe_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_tokens,
   a.msk = out->is_masked;
   a.slots = out->slot_mapping;
   a.err = ctx->err;
+  Timed tm(ctx, PE_PH_PREPARE);
   PE_HIP(pe::launch_prepare(a, ctx->stream), "prepare launch");
   return PE_OK;
 }
@@ -311,6 +354,7 @@ pe_status pe_gather_hidden(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       !aligned(h_shared, 16) || !aligned(draft_hidden, 16))
     return fail(PE_ERR_INVALID_ARG, "hidden buffers NULL or not 16-byte aligned");
   const int K = ctx->cfg.K;
+  Timed tm(ctx, PE_PH_GATHER);
   PE_HIP(pe::launch_gather(B * 2 * K, B * (K + 1), int(ctx->cfg.d * ctx->esz), batch->hidden_src,
                            target_hidden, h_shared, draft_hidden, ctx->stream),
          "gather launch");
@@ -357,11 +401,15 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
     g.embed = ctx->w.embed; g.ids = batch->input_ids; g.hid = draft_hidden;
     g.W0 = ctx->w.w_fc;
     g.out = ctx->x; g.ldo = d;
+    Timed tm(ctx, PE_PH_FC);
     PE_HIP(pe::launch_gemm(dt, pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, ctx->num_cus, st), "fc");
   }
   for (int l = 0; l < k.layers; ++l) {
     const pe_layer_weights& L = ctx->layers[l];
-    PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.attn_norm, ctx->u, nullptr, R, k.rms_eps, st), "attn norm");
+    {
+      Timed tm(ctx, PE_PH_NORM);
+      PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.attn_norm, ctx->u, nullptr, R, k.rms_eps, st), "attn norm");
+    }
     {
       pe::GemmArgs g = g0;
       g.M = R; g.N = qd + 2 * kvd; g.K = d;
@@ -370,6 +418,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       g.positions = batch->positions; g.slots = batch->slot_mapping;
       g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
       g.rope_inv = ctx->rope_inv; g.rope_inv_d = ctx->rope_inv_d;
+      Timed tm(ctx, PE_PH_QKV);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, ctx->num_cus, st), "qkv");
     }
     {
@@ -386,6 +435,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       long long grid = 4LL * ctx->num_cus;
       const long long mx = pe::attn_max_items(B, k.n_kv_heads, ctx->target_items);
       a.grid = int(grid < mx ? grid : mx);
+      Timed tm(ctx, PE_PH_ATTN);
       PE_HIP(pe::launch_attention(dt, a, st), "attention");
     }
     {
@@ -394,15 +444,20 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       g.A = ctx->attn; g.lda = qd;
       g.W0 = L.wo;
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
+      Timed tm(ctx, PE_PH_O);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, ctx->num_cus, st), "o proj");
     }
-    PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.mlp_norm, ctx->u, nullptr, R, k.rms_eps, st), "mlp norm");
+    {
+      Timed tm(ctx, PE_PH_NORM);
+      PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.mlp_norm, ctx->u, nullptr, R, k.rms_eps, st), "mlp norm");
+    }
     {
       pe::GemmArgs g = g0;
       g.M = R; g.N = 2 * k.mlp; g.K = d;
       g.A = ctx->u; g.lda = d;
       g.W0 = L.w_gate; g.W1 = L.w_up;
       g.out = ctx->mlp; g.ldo = k.mlp;
+      Timed tm(ctx, PE_PH_GATEUP);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, ctx->num_cus, st), "gate/up");
     }
     {
@@ -411,12 +466,16 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       g.A = ctx->mlp; g.lda = k.mlp;
       g.W0 = L.w_down;
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
+      Timed tm(ctx, PE_PH_DOWN);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, ctx->num_cus, st), "down");
     }
   }
-  PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, ctx->w.final_norm, ctx->z, batch->draft_rows, R,
-                            k.rms_eps, st),
-         "final norm");
+  {
+    Timed tm(ctx, PE_PH_NORM);
+    PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, ctx->w.final_norm, ctx->z, batch->draft_rows, R,
+                              k.rms_eps, st),
+           "final norm");
+  }
   {
     pe::GemmArgs g = g0;
     g.M = D; g.N = k.vocab; g.K = d;
@@ -424,6 +483,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
     g.W0 = ctx->w.lm_head;
     g.keys = ctx->keys; g.counter = ctx->counter; g.tokens = draft_tokens; g.logits = logits;
     g.seq_lens = batch->seq_lens; g.Kd = k.K;
+    Timed tm(ctx, PE_PH_LMHEAD);
     PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
   }
   return PE_OK;
@@ -436,6 +496,7 @@ pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens, const i
   if (B == 0) return PE_OK;
   if (!draft_tokens || !target_tokens || !num_accepted || !bonus_tokens)
     return fail(PE_ERR_INVALID_ARG, "a verify buffer is NULL");
+  Timed tm(ctx, PE_PH_VERIFY);
   PE_HIP(pe::launch_verify(B, ctx->cfg.K, draft_tokens, target_tokens, num_accepted, bonus_tokens,
                            ctx->stream),
          "verify launch");
@@ -476,7 +537,9 @@ pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args) {
     PE_HIP(hipStreamBeginCapture(ctx->capture_stream, hipStreamCaptureModeRelaxed), "begin capture");
     hipStream_t user = ctx->stream;
     ctx->stream = ctx->capture_stream;
+    ctx->capturing = true;
     s = run_step(ctx, B, args);
+    ctx->capturing = false;
     ctx->stream = user;
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamEndCapture(ctx->capture_stream, &graph);
@@ -504,6 +567,33 @@ pe_status pe_get_device_error(pe_ctx* ctx, uint32_t* kinds, int32_t* first_reque
   PE_HIP(hipMemcpy(ctx->err, err0, 16, hipMemcpyHostToDevice), "clear error word");
   *kinds = h[0];
   *first_request = h[0] ? int32_t(h[1]) : -1;
+  return PE_OK;
+}
+
+pe_status pe_profile_enable(pe_ctx* ctx, int on) {
+  if (!ctx) return fail(PE_ERR_INVALID_ARG, "ctx is NULL");
+  ctx->prof_on = on != 0;
+  return PE_OK;
+}
+
+pe_status pe_profile_read(pe_ctx* ctx, double* ms, int64_t* launches, int reset) {
+  if (!ctx || !ms || !launches) return fail(PE_ERR_INVALID_ARG, "NULL argument");
+  PE_HIP(hipStreamSynchronize(ctx->stream), "sync");
+  for (auto& r : ctx->recs) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+      ctx->prof_ms[r.phase] += t;
+      ctx->prof_n[r.phase] += 1;
+    }
+    ctx->ev_free.push_back(r.a);
+    ctx->ev_free.push_back(r.b);
+  }
+  ctx->recs.clear();
+  for (int i = 0; i < PE_PH_COUNT; ++i) {
+    ms[i] = ctx->prof_ms[i];
+    launches[i] = ctx->prof_n[i];
+    if (reset) { ctx->prof_ms[i] = 0.0; ctx->prof_n[i] = 0; }
+  }
   return PE_OK;
 }
 

@@ -216,6 +216,19 @@ pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args);
  * index, or -1 when kinds == 0. */
 pe_status pe_get_device_error(pe_ctx* ctx, uint32_t* kinds, int32_t* first_request);
 
+/* Per-phase kernel timing.  With profiling on, every eager launch of a phase
+ * is bracketed by a pair of HIP events on the context's stream; nothing is
+ * recorded while a step graph is being captured.  pe_profile_read
+ * synchronizes the stream and returns, per phase, the summed event time in ms
+ * and the number of launches since the last reset. */
+typedef enum pe_phase {
+  PE_PH_PREPARE = 0, PE_PH_GATHER, PE_PH_FC, PE_PH_NORM, PE_PH_QKV, PE_PH_ATTN,
+  PE_PH_O, PE_PH_GATEUP, PE_PH_DOWN, PE_PH_LMHEAD, PE_PH_VERIFY, PE_PH_COUNT
+} pe_phase;
+pe_status pe_profile_enable(pe_ctx* ctx, int on);
+pe_status pe_profile_read(pe_ctx* ctx, double* ms /* [PE_PH_COUNT] */,
+                          int64_t* launches /* [PE_PH_COUNT] */, int reset);
+
 /* Text of the last error on this thread ("" if none). */
 const char* pe_last_error(void);
 const char* pe_status_string(pe_status s);
