@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpe.so")
+LIB_PATH = os.environ.get("PE_LIB") or os.path.join(_HERE, "libpe.so")
 
 PE_F32, PE_BF16 = 0, 1
 DEVERR_ACCEPTED, DEVERR_TOKEN, DEVERR_BLOCK, DEVERR_LAYOUT = 1, 2, 4, 8
@@ -25,7 +25,7 @@ EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_
            "pe_draft_forward", "pe_verify", "pe_step_graph", "pe_get_device_error",
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
-          "verify")
+          "verify", "argmax")
 
 vp, i32 = ctypes.c_void_p, ctypes.c_int32
 

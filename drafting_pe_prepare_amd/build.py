@@ -44,22 +44,36 @@ def _compile(src):
     return obj, msgs
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, out: str = None, objdir: str = None, defines=()) -> str:
+    """Compile every source and link libpe.so (or `out`).  `defines` are
+    extra -D macros for experimental variants."""
+    global OBJDIR, FLAGS
+    out = out or OUT
+    saved = (OBJDIR, FLAGS)
+    OBJDIR = objdir or OBJDIR
+    FLAGS = FLAGS + [f"-D{d}" for d in defines]
+    try:
+        return _build(verbose, out)
+    finally:
+        OBJDIR, FLAGS = saved
+
+
+def _build(verbose, out):
     os.makedirs(OBJDIR, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         results = list(ex.map(_compile, SOURCES))
     for obj, msgs in results:
         if verbose and msgs:
             print("\n".join(msgs), file=sys.stderr)
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

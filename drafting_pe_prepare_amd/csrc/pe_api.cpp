@@ -62,7 +62,6 @@ struct pe_ctx {
   void* mlp = nullptr;   // [R, I]   SiLU(gate) * up
   void* z = nullptr;     // [D, d]   final-norm draft rows
   uint64_t* keys = nullptr;   // [D] argmax keys (kept zero between launches)
-  uint32_t* counter = nullptr;
   uint32_t* err = nullptr;    // [2] kinds, first request
   float* part_o = nullptr;
   float* part_ml = nullptr;
@@ -128,7 +127,7 @@ void free_ctx(pe_ctx* c) {
   if (c->capture_stream) (void)hipStreamDestroy(c->capture_stream);
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
-  void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->counter, c->err,
+  void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
                   c->part_o, c->part_ml, c->rope_inv, c->rope_inv_d};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
@@ -257,7 +256,6 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {&c->mlp, R * size_t(k.mlp) * c->esz, "mlp"},
       {&c->z, D * k.d * c->esz, "z"},
       {reinterpret_cast<void**>(&c->keys), D * 8, "keys"},
-      {reinterpret_cast<void**>(&c->counter), 16, "counter"},
       {reinterpret_cast<void**>(&c->err), 16, "err"},
       {reinterpret_cast<void**>(&c->rope_inv), size_t(k.head_dim / 2) * 4, "rope"},
       {reinterpret_cast<void**>(&c->rope_inv_d), size_t(k.head_dim / 2) * 8, "rope_d"},
@@ -283,7 +281,6 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   e = hipMemcpy(c->rope_inv, inv.data(), inv.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->rope_inv_d, invd.data(), invd.size() * 8, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemset(c->keys, 0, D * 8);
-  if (e == hipSuccess) e = hipMemset(c->counter, 0, 16);
   if (e == hipSuccess) e = hipMemcpy(c->err, err0, 16, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     free_ctx(c);
@@ -481,10 +478,14 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
     g.M = D; g.N = k.vocab; g.K = d;
     g.A = ctx->z; g.lda = d;
     g.W0 = ctx->w.lm_head;
-    g.keys = ctx->keys; g.counter = ctx->counter; g.tokens = draft_tokens; g.logits = logits;
+    g.keys = ctx->keys; g.tokens = draft_tokens; g.logits = logits;
     g.seq_lens = batch->seq_lens; g.Kd = k.K;
-    Timed tm(ctx, PE_PH_LMHEAD);
-    PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
+    {
+      Timed tm(ctx, PE_PH_LMHEAD);
+      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
+    }
+    Timed tm(ctx, PE_PH_ARGMAX);
+    PE_HIP(pe::launch_argmax_tokens(D, k.K, ctx->keys, draft_tokens, batch->seq_lens, st), "argmax");
   }
   return PE_OK;
 }

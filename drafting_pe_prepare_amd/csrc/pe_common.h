@@ -42,8 +42,12 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c)
 // Streaming 16-byte load for data read once (weights): non-temporal hint.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream(const void* p) {
+#if defined(PE_W_PLAIN)
+  return *reinterpret_cast<const uint4*>(p);
+#else
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return uint4{v[0], v[1], v[2], v[3]};
+#endif
 }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 

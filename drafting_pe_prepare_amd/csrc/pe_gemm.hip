@@ -183,34 +183,24 @@ __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, i
   }
 }
 
-// The last workgroup to finish turns the argmax keys into tokens and resets the
-// keys and the counter for the next launch (so no memset is needed).
-__device__ void argmax_finalize(const GemmArgs& g, unsigned nblocks) {
-  __threadfence();
-  __syncthreads();
-  __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    const unsigned t = atomicAdd(g.counter, 1u);
-    s_last = (t == nblocks - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int i = threadIdx.x; i < g.M; i += blockDim.x) {
-    const uint64_t k =
-        __hip_atomic_load((unsigned long long*)&g.keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int tok = argmax_key_index(k);
-    if (g.seq_lens && g.seq_lens[i / g.Kd] == 0) tok = -1;
-    g.tokens[i] = tok;
-    __hip_atomic_store((unsigned long long*)&g.keys[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(g.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Argmax keys -> tokens, run as its own small kernel after the LM head: the
+// kernel boundary orders every atomicMax before the reads, so the GEMM needs no
+// grid-wide fence.  It also clears the keys for the next launch.
+__global__ __launch_bounds__(256) void argmax_tokens_kernel(int M, int Kd, uint64_t* keys,
+                                                            int32_t* tokens,
+                                                            const int32_t* seq_lens) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M) return;
+  int tok = argmax_key_index(keys[i]);
+  if (seq_lens && seq_lens[i / Kd] == 0) tok = -1;
+  tokens[i] = tok;
+  keys[i] = 0ull;
 }
 
 // ---------------------------------------------------------------------------
 // bf16, M <= 64: split-K across the waves of a workgroup
 // ---------------------------------------------------------------------------
-template <int EPI, int AL, int BMAP, int MT, int NTW>
+template <int EPI, int AL, int BMAP, int MT, int NTW, int U>
 __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
   extern __shared__ float smem[];
   const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -241,18 +231,29 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
     for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll 4
-  for (int ks = ks0; ks < ks1; ++ks) {
-    const int k = ks * 32;
-    uint4 b[NTW], a[MT];
+  // U k-steps of loads in flight per batch, then their MFMAs
+  for (int ks = ks0; ks < ks1; ks += U) {
+    const int n = min(U, ks1 - ks);
+    uint4 b[U][NTW], a[U][MT];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) b[t] = ld_stream(wp[t] + k);
+    for (int u = 0; u < U; ++u) {
+      if (u < n) {
+        const int k = (ks + u) * 32;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a[mt] = av[mt] ? ld16(ar[mt].at(k + kg * 8, g.d)) : zero;
+        for (int t = 0; t < NTW; ++t) b[u][t] = ld_stream(wp[t] + k);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? ld16(ar[mt].at(k + kg * 8, g.d)) : zero;
+      }
+    }
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) acc[mt][t] = mfma16(a[mt], b[t], acc[mt][t]);
+    for (int u = 0; u < U; ++u) {
+      if (u < n) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) acc[mt][t] = mfma16(a[u][mt], b[u][t], acc[mt][t]);
+      }
+    }
   }
 
   // fixed-order reduction of the wave partials
@@ -277,7 +278,6 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
   __syncthreads();
   if (EPI == E_ARGMAX) {
     epilogue_argmax(g, tile, LDT, 0, MT * 16, n0, NTW * 16);
-    argmax_finalize(g, gridDim.x);
   } else {
     epilogue<uint16_t, EPI>(g, tile, LDT, 0, MT * 16, n0, NTW * 16);
   }
@@ -287,34 +287,42 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
 // bf16 LM head, M <= 16 rows: rows in LDS, whole tiles per wave, argmax in
 // registers
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void lmhead_wide_kernel(GemmArgs g) {
+// One workgroup per CU over a contiguous, tile-aligned range of 16-column
+// tiles.  The range is cut into units of U k-steps (tile-major) and every wave
+// takes an equal run of units, so all waves finish together.  A tile cut
+// between waves leaves partial sums in LDS; after the barrier the wave that
+// holds the tile's first unit adds them up and folds the tile into its argmax.
+template <int U>
+__global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
   extern __shared__ uint4 xs[];
+  constexpr int MAXW = 8;
+  __shared__ float part[MAXW][2][4][64];   // [wave][head/tail][i][lane]
+  __shared__ int part_tile[MAXW][2];
+  __shared__ uint64_t s_best[MAXW][16];
   const int K = g.K, kc = K >> 3, ldx = kc + 1;
   for (int c = threadIdx.x; c < g.M * kc; c += blockDim.x) {
     const int m = c / kc, j = c - m * kc;
     xs[m * ldx + j] = ld16((const uint16_t*)g.A + (long long)m * g.lda + j * 8);
   }
-  __syncthreads();
   const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int col = l & 15, kg = l >> 4;
-  const long long gw = (long long)blockIdx.x * nw + w, GW = (long long)gridDim.x * nw;
+  if (l < 2) part_tile[w][l] = -1;
+  __syncthreads();
   const int ntiles = g.N >> 4;
-  const int t0 = int(ntiles * gw / GW), t1 = int(ntiles * (gw + 1) / GW);
+  const int T0 = int((long long)ntiles * blockIdx.x / gridDim.x);
+  const int T1 = int((long long)ntiles * (blockIdx.x + 1) / gridDim.x);
+  const int cpt = (K >> 5) / U;  // units per tile
+  const int nunits = (T1 - T0) * cpt;
+  const int u0 = int((long long)nunits * w / nw), u1 = int((long long)nunits * (w + 1) / nw);
   const bool arow = col < g.M;
   const uint4 zero = {0u, 0u, 0u, 0u};
   const uint4* xrow = xs + col * ldx + kg;
+  const uint16_t* wbase = (const uint16_t*)g.W0 + (long long)col * K + kg * 8;
   uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
-  const int ksteps = K >> 5;
-  for (int t = t0; t < t1; ++t) {
-    const uint16_t* wp = (const uint16_t*)g.W0 + (long long)(t * 16 + col) * K + kg * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const uint4 b = ld_stream(wp + ks * 32);
-      const uint4 a = arow ? xrow[ks * 4] : zero;
-      acc = mfma16(a, b, acc);
-    }
-    const int n = t * 16 + col;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  auto fold = [&](int tile) {  // full 16x16 sums of `tile` are in acc
+    const int n = tile * 16 + col;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = kg * 4 + i;
@@ -324,18 +332,74 @@ __global__ __launch_bounds__(1024) void lmhead_wide_kernel(GemmArgs g) {
         best[i] = key > best[i] ? key : best[i];
       }
     }
+  };
+  auto issue = [&](uint4 (&b)[U], int u) {
+    const int tile = T0 + u / cpt, k0 = (u % cpt) * U * 32;
+    const uint16_t* wp = wbase + (long long)tile * 16 * K + k0;
+#pragma unroll
+    for (int j = 0; j < U; ++j) b[j] = ld_stream(wp + j * 32);
+  };
+  auto consume = [&](uint4 (&b)[U], int u) {
+    const int c = u % cpt, tile = T0 + u / cpt;
+    const uint4* xr = xrow + c * U * 4;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint4 a = arow ? xr[j * 4] : zero;
+      acc = mfma16(a, b[j], acc);
+    }
+    if (c == cpt - 1 || u == u1 - 1) {
+      const bool head = (u - c < u0);      // the tile began before this wave's range
+      const bool tail = (c != cpt - 1);    // the tile continues after it
+      if (!head && !tail) {
+        fold(tile);
+      } else {
+        const int slot = head ? 0 : 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[w][slot][i][l] = acc[i];
+        if (l == 0) part_tile[w][slot] = tile;
+      }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  uint4 b0[U], b1[U];
+  if (u0 < u1) issue(b0, u0);
+  for (int u = u0; u < u1; u += 2) {
+    if (u + 1 < u1) issue(b1, u + 1);
+    consume(b0, u);
+    if (u + 1 < u1) {
+      if (u + 2 < u1) issue(b0, u + 2);
+      consume(b1, u + 1);
+    }
   }
+  __syncthreads();
+  // tiles cut between waves: the wave holding the tile's first unit (its tail
+  // slot) adds the head slots of the following waves that hold the same tile
+  const int tt = part_tile[w][1];
+  if (tt >= 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = part[w][1][i][l];
+    for (int v = w + 1; v < nw && part_tile[v][0] == tt; ++v) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += part[v][0][i][l];
+      if (part_tile[v][1] == tt) break;  // cannot happen: a run longer than a tile
+    }
+    fold(tt);
+  }
+  // row maxima: 16 lanes per row group, then across waves, one atomic per row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     for (int o = 1; o < 16; o <<= 1) {
       const uint64_t k = shfl_xor_u64(best[i], o);
       best[i] = k > best[i] ? k : best[i];
     }
-    const int row = kg * 4 + i;
-    if (col == 0 && row < g.M && best[i] != 0ull)
-      atomicMax((unsigned long long*)&g.keys[row], (unsigned long long)best[i]);
+    if (col == 0) s_best[w][kg * 4 + i] = best[i];
   }
-  argmax_finalize(g, gridDim.x);
+  __syncthreads();
+  if (threadIdx.x < g.M) {
+    uint64_t b = 0ull;
+    for (int v = 0; v < nw; ++v) b = s_best[v][threadIdx.x] > b ? s_best[v][threadIdx.x] : b;
+    if (b) atomicMax((unsigned long long*)&g.keys[threadIdx.x], (unsigned long long)b);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -352,11 +416,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g, int mtiles,
   // XCD-aware order: the m-tiles of one n-tile run back to back on one XCD
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
   const int mt = j % mtiles, nt = (j / mtiles) * 8 + xcd;
-  if (nt >= ntiles) {
-    // padding workgroup of the XCD-aligned grid; it still counts for the argmax
-    if (EPI == E_ARGMAX) argmax_finalize(g, gridDim.x);
-    return;
-  }
+  if (nt >= ntiles) return;  // padding workgroup of the XCD-aligned grid
   const int m0 = mt * BM, n0 = nt * BN;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
   const int wm = w >> 1, wn = w & 1;
@@ -451,7 +511,6 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g, int mtiles,
   } else {
     epilogue<uint16_t, EPI>(g, tile, LDT, m0, BM, n0, BN);
   }
-  if (EPI == E_ARGMAX) argmax_finalize(g, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -474,7 +533,6 @@ __global__ __launch_bounds__(512) void gemm_f32_kernel(GemmArgs g) {
   __syncthreads();
   if (EPI == E_ARGMAX) {
     epilogue_argmax(g, tile, 33, m0, 16, n0, 32);
-    argmax_finalize(g, gridDim.x * gridDim.y);
   } else {
     epilogue<float, EPI>(g, tile, 33, m0, 16, n0, 32);
   }
@@ -492,12 +550,13 @@ static hipError_t set_lds(F* fn, size_t bytes) {
 template <int EPI, int AL, int BMAP, int MT>
 static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
   constexpr int NTW = (BMAP == B_PLAIN) ? 1 : 2;
+  constexpr int U = (NTW + MT <= 3) ? 8 : 4;
   const int ksteps = g.K / 32;
   int nw = ksteps / 4;
   nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
   while (nw > 1 && nw * MT * NTW > 128) --nw;
   const size_t lds = size_t(nw) * MT * NTW * 256 * 4 + size_t(MT * 16) * (NTW * 16 + 4) * 4;
-  auto fn = gemm_skinny_kernel<EPI, AL, BMAP, MT, NTW>;
+  auto fn = gemm_skinny_kernel<EPI, AL, BMAP, MT, NTW, U>;
   hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
   const int grid = (g.N + NTW * 16 - 1) / (NTW * 16);
@@ -505,19 +564,40 @@ static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int U>
+static hipError_t run_wide(const GemmArgs& g, int num_cus, hipStream_t st) {
+  const size_t lds = size_t(g.M) * (g.K / 8 + 1) * 16;
+  auto fn = lmhead_wide_kernel<U>;
+  hipError_t e = set_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  int grid = num_cus;
+  const int ntiles = g.N / 16;
+  if (grid > ntiles) grid = ntiles;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(512), lds, st, g);
+  return hipGetLastError();
+}
+
+// widest chunk (<= 16 k-steps) that divides the k-step count
+static hipError_t run_wide_any(const GemmArgs& g, int num_cus, hipStream_t st) {
+  const int ks = g.K / 32;
+  if (ks % 16 == 0) return run_wide<16>(g, num_cus, st);
+  if (ks % 15 == 0) return run_wide<15>(g, num_cus, st);
+  if (ks % 12 == 0) return run_wide<12>(g, num_cus, st);
+  if (ks % 10 == 0) return run_wide<10>(g, num_cus, st);
+  if (ks % 9 == 0) return run_wide<9>(g, num_cus, st);
+  if (ks % 8 == 0) return run_wide<8>(g, num_cus, st);
+  if (ks % 6 == 0) return run_wide<6>(g, num_cus, st);
+  if (ks % 5 == 0) return run_wide<5>(g, num_cus, st);
+  if (ks % 4 == 0) return run_wide<4>(g, num_cus, st);
+  if (ks % 3 == 0) return run_wide<3>(g, num_cus, st);
+  if (ks % 2 == 0) return run_wide<2>(g, num_cus, st);
+  return run_wide<1>(g, num_cus, st);
+}
+
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
   const size_t wide_lds = size_t(g.M) * (g.K / 8 + 1) * 16;
-  if (EPI == E_ARGMAX && g.M <= 16 && wide_lds <= 150 * 1024) {
-    const size_t lds = wide_lds;
-    hipError_t e = set_lds(lmhead_wide_kernel, lds);
-    if (e != hipSuccess) return e;
-    int grid = num_cus;
-    const int ntiles = g.N / 16;
-    if (grid * 16 > ntiles) grid = (ntiles + 15) / 16;
-    hipLaunchKernelGGL(lmhead_wide_kernel, dim3(grid), dim3(1024), lds, st, g);
-    return hipGetLastError();
-  }
+  if (EPI == E_ARGMAX && g.M <= 16 && wide_lds <= 140 * 1024) return run_wide_any(g, num_cus, st);
   if (g.M <= 16) return run_skinny<EPI, AL, BMAP, 1>(g, st);
   if (g.M <= 32) return run_skinny<EPI, AL, BMAP, 2>(g, st);
   if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
@@ -542,6 +622,14 @@ static hipError_t run_f32(const GemmArgs& g, hipStream_t st) {
 template <int EPI, int AL, int BMAP>
 static hipError_t run(int dtype, const GemmArgs& g, int num_cus, hipStream_t st) {
   return dtype == 1 ? run_bf16<EPI, AL, BMAP>(g, num_cus, st) : run_f32<EPI, AL, BMAP>(g, st);
+}
+
+hipError_t launch_argmax_tokens(int M, int Kd, uint64_t* keys, int32_t* tokens,
+                                const int32_t* seq_lens, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_tokens_kernel, dim3((M + 255) / 256), dim3(256), 0, st, M, Kd, keys,
+                     tokens, seq_lens);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,

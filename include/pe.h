@@ -223,7 +223,7 @@ pe_status pe_get_device_error(pe_ctx* ctx, uint32_t* kinds, int32_t* first_reque
  * and the number of launches since the last reset. */
 typedef enum pe_phase {
   PE_PH_PREPARE = 0, PE_PH_GATHER, PE_PH_FC, PE_PH_NORM, PE_PH_QKV, PE_PH_ATTN,
-  PE_PH_O, PE_PH_GATEUP, PE_PH_DOWN, PE_PH_LMHEAD, PE_PH_VERIFY, PE_PH_COUNT
+  PE_PH_O, PE_PH_GATEUP, PE_PH_DOWN, PE_PH_LMHEAD, PE_PH_VERIFY, PE_PH_ARGMAX, PE_PH_COUNT
 } pe_phase;
 pe_status pe_profile_enable(pe_ctx* ctx, int on);
 pe_status pe_profile_read(pe_ctx* ctx, double* ms /* [PE_PH_COUNT] */,
