@@ -7,6 +7,7 @@
 // context's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -61,7 +62,7 @@ struct pe_ctx {
   void* attn = nullptr;  // [R, Hq*hd] attention output
   void* mlp = nullptr;   // [R, I]   SiLU(gate) * up
   void* z = nullptr;     // [D, d]   final-norm draft rows
-  uint64_t* keys = nullptr;   // [D] argmax keys (kept zero between launches)
+  uint64_t* keys = nullptr;   // [D, parts] partial argmax keys of the LM head
   uint32_t* err = nullptr;    // [2] kinds, first request
   float* part_o = nullptr;
   float* part_ml = nullptr;
@@ -248,6 +249,11 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   const size_t qd = size_t(k.n_q_heads) * k.head_dim;
   const size_t QN = size_t(2 * k.K) * (k.n_q_heads / k.n_kv_heads);
   c->items_max = pe::attn_max_items(k.max_num_seqs, k.n_kv_heads, c->target_items);
+  // partial argmax keys: the largest parts count any B <= max_num_seqs can need
+  size_t key_slots = 0;
+  for (int b = 1; b <= k.max_num_seqs; ++b)
+    key_slots = std::max(key_slots, size_t(b) * k.K *
+                                        pe::gemm_argmax_parts(k.dtype, b * k.K, k.vocab, k.d, c->num_cus));
   struct { void** p; size_t bytes; const char* what; } plan[] = {
       {&c->x, R * k.d * c->esz, "x"},
       {&c->u, R * k.d * c->esz, "u"},
@@ -255,7 +261,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {&c->attn, R * qd * c->esz, "attn"},
       {&c->mlp, R * size_t(k.mlp) * c->esz, "mlp"},
       {&c->z, D * k.d * c->esz, "z"},
-      {reinterpret_cast<void**>(&c->keys), D * 8, "keys"},
+      {reinterpret_cast<void**>(&c->keys), key_slots * 8, "argmax keys"},
       {reinterpret_cast<void**>(&c->err), 16, "err"},
       {reinterpret_cast<void**>(&c->rope_inv), size_t(k.head_dim / 2) * 4, "rope"},
       {reinterpret_cast<void**>(&c->rope_inv_d), size_t(k.head_dim / 2) * 8, "rope_d"},
@@ -280,7 +286,6 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   const uint32_t err0[4] = {0u, 0xFFFFFFFFu, 0u, 0u};
   e = hipMemcpy(c->rope_inv, inv.data(), inv.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->rope_inv_d, invd.data(), invd.size() * 8, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(c->keys, 0, D * 8);
   if (e == hipSuccess) e = hipMemcpy(c->err, err0, 16, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     free_ctx(c);
@@ -479,13 +484,15 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
     g.A = ctx->z; g.lda = d;
     g.W0 = ctx->w.lm_head;
     g.keys = ctx->keys; g.tokens = draft_tokens; g.logits = logits;
+    g.parts = pe::gemm_argmax_parts(dt, D, k.vocab, d, ctx->num_cus);
     g.seq_lens = batch->seq_lens; g.Kd = k.K;
     {
       Timed tm(ctx, PE_PH_LMHEAD);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
     }
     Timed tm(ctx, PE_PH_ARGMAX);
-    PE_HIP(pe::launch_argmax_tokens(D, k.K, ctx->keys, draft_tokens, batch->seq_lens, st), "argmax");
+    PE_HIP(pe::launch_argmax_tokens(D, k.K, g.parts, ctx->keys, draft_tokens, batch->seq_lens, st),
+           "argmax");
   }
   return PE_OK;
 }

@@ -24,6 +24,8 @@
 //    gate/up partners) are placed 16 logical columns apart inside one 32-column
 //    block by the weight-row mapping (B_QKV, B_GATEUP).
 //  * fp32 storage: gemm_f32, plain FMA, for the small fp32 workload only.
+#include <algorithm>
+
 #include "pe_common.h"
 #include "pe_internal.h"
 
@@ -78,8 +80,8 @@ struct ARow {
 // ---------------------------------------------------------------------------
 // epilogues on an fp32 tile in LDS: tile[i*ldt + c] = out[m0+i, n0+c] (logical)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rope_sincos(const GemmArgs& g, int pos, int i, float& cs,
-                                            float& sn) {
+__device__ __attribute__((noinline)) void rope_sincos(const GemmArgs& g, int pos, int i, float& cs,
+                                                     float& sn) {
   // angle = pos * theta^(-2i/hd), reduced to [-pi, pi] in double, then fp32 sincos
   const double TWO_PI = 6.283185307179586476925286766559;
   double ang = double(pos) * g.rope_inv_d[i];
@@ -87,6 +89,58 @@ __device__ __forceinline__ void rope_sincos(const GemmArgs& g, int pos, int i, f
   sincosf(float(ang), &sn, &cs);
 }
 
+// Per-element epilogues.  epi_one: one logical column n of row m (E_STORE,
+// E_RESID).  epi_pair: a 32-column logical block starting at nb, column c in
+// [0,16) paired with c+16 (E_SILU: gate, up; E_QKV: RoPE partners or two V dims).
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_one(const GemmArgs& g, int m, int n, float v) {
+  const long long o = (long long)m * g.ldo + n;
+  if (EPI == E_RESID) v += Elt<T>::ld((const T*)g.resid + o);
+  Elt<T>::st((T*)g.out + o, v);
+}
+
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_pair(const GemmArgs& g, int m, int nb, int c, float lo, float hi) {
+  if (EPI == E_SILU) {
+    const float v = lo / (1.0f + expf(-lo)) * hi;
+    Elt<T>::st((T*)g.out + (long long)m * g.ldo + (nb >> 1) + c, v);
+  } else if (EPI == E_QKV) {
+    if (nb < g.nq + g.nk) {
+      const bool isq = nb < g.nq;
+      const int j = isq ? nb : nb - g.nq;
+      const int head = j / g.hd, s = (j % g.hd) >> 4;
+      const int dlo = (s >> 1) * 16 + c, dhi = dlo + (g.hd >> 1);
+      float cs, sn;
+      rope_sincos(g, g.positions[m], dlo, cs, sn);
+      const float olo = lo * cs - hi * sn, ohi = hi * cs + lo * sn;
+      if (isq) {
+        T* q = (T*)g.qout + ((long long)m * (g.nq / g.hd) + head) * g.hd;
+        Elt<T>::st(q + dlo, olo);
+        Elt<T>::st(q + dhi, ohi);
+      } else {
+        const long long slot = g.slots[m];
+        if (slot >= 0 && slot < g.num_slots) {
+          T* kp = (T*)g.kcache + (slot * g.Hkv + head) * g.hd;
+          Elt<T>::st(kp + dlo, olo);
+          Elt<T>::st(kp + dhi, ohi);
+        }
+      }
+    } else {
+      const long long slot = g.slots[m];
+      if (slot >= 0 && slot < g.num_slots) {
+        const int j = nb - g.nq - g.nk;
+        const int head = j / g.hd, jb = j % g.hd;
+        const long long blk = slot / g.block_size, off = slot % g.block_size;
+        T* vp = (T*)g.vcache + ((blk * g.Hkv + head) * g.hd) * g.block_size + off;
+        Elt<T>::st(vp + (long long)(jb + c) * g.block_size, lo);
+        Elt<T>::st(vp + (long long)(jb + 16 + c) * g.block_size, hi);
+      }
+    }
+  }
+}
+
+// The same epilogues over an fp32 tile staged in LDS: tile[i*ldt + c] holds
+// out[m0+i, n0+c] (logical columns).
 template <typename T, int EPI>
 __device__ void epilogue(const GemmArgs& g, const float* tile, int ldt, int m0, int TM, int n0,
                          int TN) {
@@ -97,58 +151,14 @@ __device__ void epilogue(const GemmArgs& g, const float* tile, int ldt, int m0, 
   if (EPI == E_STORE || EPI == E_RESID) {
     for (int e = tid; e < mrows * ncols; e += nt) {
       const int i = e / ncols, c = e - i * ncols;
-      const long long o = (long long)(m0 + i) * g.ldo + n0 + c;
-      float v = tile[i * ldt + c];
-      if (EPI == E_RESID) v += Elt<T>::ld((const T*)g.resid + o);
-      Elt<T>::st((T*)g.out + o, v);
+      epi_one<T, EPI>(g, m0 + i, n0 + c, tile[i * ldt + c]);
     }
-  } else if (EPI == E_SILU) {
-    // block b of 32 logical columns = 16 gate columns then their 16 up columns
+  } else {
     const int np = ncols >> 1;
     for (int e = tid; e < mrows * np; e += nt) {
       const int i = e / np, p = e - i * np, b = p >> 4, c = p & 15;
-      const float gt = tile[i * ldt + b * 32 + c], up = tile[i * ldt + b * 32 + 16 + c];
-      const float v = gt / (1.0f + expf(-gt)) * up;
-      Elt<T>::st((T*)g.out + (long long)(m0 + i) * g.ldo + (n0 >> 1) + p, v);
-    }
-  } else if (EPI == E_QKV) {
-    const int np = ncols >> 1;
-    const int hq = g.nq / g.hd;
-    for (int e = tid; e < mrows * np; e += nt) {
-      const int i = e / np, p = e - i * np, b = p >> 4, c = p & 15;
-      const int m = m0 + i, nb = n0 + b * 32;
-      const float lo = tile[i * ldt + b * 32 + c], hi = tile[i * ldt + b * 32 + 16 + c];
-      if (nb < g.nq + g.nk) {
-        const bool isq = nb < g.nq;
-        const int j = isq ? nb : nb - g.nq;
-        const int head = j / g.hd, s = (j % g.hd) >> 4;
-        const int dlo = (s >> 1) * 16 + c, dhi = dlo + (g.hd >> 1);
-        float cs, sn;
-        rope_sincos(g, g.positions[m], dlo, cs, sn);
-        const float olo = lo * cs - hi * sn, ohi = hi * cs + lo * sn;
-        if (isq) {
-          T* q = (T*)g.qout + ((long long)m * hq + head) * g.hd;
-          Elt<T>::st(q + dlo, olo);
-          Elt<T>::st(q + dhi, ohi);
-        } else {
-          const long long slot = g.slots[m];
-          if (slot >= 0 && slot < g.num_slots) {
-            T* kp = (T*)g.kcache + (slot * g.Hkv + head) * g.hd;
-            Elt<T>::st(kp + dlo, olo);
-            Elt<T>::st(kp + dhi, ohi);
-          }
-        }
-      } else {
-        const long long slot = g.slots[m];
-        if (slot >= 0 && slot < g.num_slots) {
-          const int j = nb - g.nq - g.nk;
-          const int head = j / g.hd, jb = j % g.hd;
-          const long long blk = slot / g.block_size, off = slot % g.block_size;
-          T* vp = (T*)g.vcache + ((blk * g.Hkv + head) * g.hd) * g.block_size + off;
-          Elt<T>::st(vp + (long long)(jb + c) * g.block_size, lo);
-          Elt<T>::st(vp + (long long)(jb + 16 + c) * g.block_size, hi);
-        }
-      }
+      epi_pair<T, EPI>(g, m0 + i, n0 + b * 32, c, tile[i * ldt + b * 32 + c],
+                       tile[i * ldt + b * 32 + 16 + c]);
     }
   }
 }
@@ -159,8 +169,12 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   return (uint64_t(hi) << 32) | lo;
 }
 
+// Row argmax of a staged tile: one wave per row, lanes over columns.  The
+// best 64-bit key of the tile is stored at keys[row * parts + part]; every
+// (row, part) is written by exactly one workgroup, so no atomics are needed and
+// the keys need no clearing between launches.
 __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, int m0, int TM,
-                                int n0, int TN) {
+                                int n0, int TN, int part) {
   const int mrows = min(TM, g.M - m0), ncols = min(TN, g.N - n0);
   if (mrows <= 0 || ncols <= 0) return;
   if (g.logits)
@@ -179,22 +193,35 @@ __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, i
       const uint64_t k = shfl_xor_u64(best, o);
       best = k > best ? k : best;
     }
-    if (l == 0) atomicMax((unsigned long long*)&g.keys[m0 + i], (unsigned long long)best);
+    if (l == 0) g.keys[(long long)(m0 + i) * g.parts + part] = best;
   }
 }
 
-// Argmax keys -> tokens, run as its own small kernel after the LM head: the
-// kernel boundary orders every atomicMax before the reads, so the GEMM needs no
-// grid-wide fence.  It also clears the keys for the next launch.
-__global__ __launch_bounds__(256) void argmax_tokens_kernel(int M, int Kd, uint64_t* keys,
-                                                            int32_t* tokens,
-                                                            const int32_t* seq_lens) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= M) return;
-  int tok = argmax_key_index(keys[i]);
-  if (seq_lens && seq_lens[i / Kd] == 0) tok = -1;
-  tokens[i] = tok;
-  keys[i] = 0ull;
+// Argmax partial keys -> tokens, run as its own small kernel after the LM head
+// (the kernel boundary orders the GEMM's stores before these reads).  One
+// workgroup per draft row reduces that row's `parts` keys.
+__global__ __launch_bounds__(256) void argmax_tokens_kernel(int M, int Kd, int parts,
+                                                            const uint64_t* __restrict__ keys,
+                                                            int32_t* __restrict__ tokens,
+                                                            const int32_t* __restrict__ seq_lens) {
+  __shared__ uint64_t red[4];
+  const int row = blockIdx.x;
+  const uint64_t* kr = keys + (long long)row * parts;
+  uint64_t best = 0;
+  for (int p = threadIdx.x; p < parts; p += blockDim.x) best = kr[p] > best ? kr[p] : best;
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t k = shfl_xor_u64(best, o);
+    best = k > best ? k : best;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < int(blockDim.x >> 6); ++w) best = red[w] > best ? red[w] : best;
+    best = red[0] > best ? red[0] : best;
+    int tok = argmax_key_index(best);
+    if (seq_lens && seq_lens[row / Kd] == 0) tok = -1;
+    tokens[row] = tok;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -277,7 +304,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
   }
   __syncthreads();
   if (EPI == E_ARGMAX) {
-    epilogue_argmax(g, tile, LDT, 0, MT * 16, n0, NTW * 16);
+    epilogue_argmax(g, tile, LDT, 0, MT * 16, n0, NTW * 16, blockIdx.x);
   } else {
     epilogue<uint16_t, EPI>(g, tile, LDT, 0, MT * 16, n0, NTW * 16);
   }
@@ -398,22 +425,55 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
   if (threadIdx.x < g.M) {
     uint64_t b = 0ull;
     for (int v = 0; v < nw; ++v) b = s_best[v][threadIdx.x] > b ? s_best[v][threadIdx.x] : b;
-    if (b) atomicMax((unsigned long long*)&g.keys[threadIdx.x], (unsigned long long)b);
+    g.keys[(long long)threadIdx.x * g.parts + blockIdx.x] = b;
   }
 }
 
 // ---------------------------------------------------------------------------
-// bf16, M > 64: 128x128x64 tiles, LDS double buffer, 4 waves of 64x64
+// bf16, M > 64: BM x BN tiles, k-tiles of 32, a 4-stage LDS ring filled by
+// global_load_lds_dwordx4 (global -> LDS with no staging registers), 2 x 2
+// waves of (BM/2) x (BN/2).
+//
+// LDS layout of one operand tile (R rows x 32 k, 64 B per row): rows pair up
+// into 128-byte lines; 16-byte chunk c of row r sits in line r/2 at position
+// ((r%2)*4 + c) XOR ((r/2)%4).  A 16-row MFMA fragment read then touches 8
+// distinct positions per 8 lanes (no bank conflicts), and one wave-wide
+// global_load_lds (lane i -> LDS base + 16 i) fills 8 whole lines.
 // ---------------------------------------------------------------------------
-template <int EPI, int AL, int BMAP>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
-  constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
-  constexpr int ACH = BM * BK / 8 / 256, BCH = BN * BK / 8 / 256;  // 16B chunks per thread
-  extern __shared__ uint16_t lds[];
-  uint16_t* As = lds;                    // [2][BM][LDK]
-  uint16_t* Bs = lds + 2 * BM * LDK;     // [2][BN][LDK]
+constexpr int kStages = 4;
 
-  // XCD-aware order: the m-tiles of one n-tile run back to back on one XCD
+__device__ __forceinline__ int swz(int row, int c) {
+  const int p = row >> 1;
+  return p * 128 + ((((row & 1) << 2) | c) ^ (p & 3)) * 16;
+}
+// inverse: lane i of the load instruction filling lines 8*ii .. 8*ii+7
+__device__ __forceinline__ void unswz(int ii, int lane, int& row, int& c) {
+  const int p = ii * 8 + (lane >> 3);
+  const int q = (lane & 7) ^ (p & 3);
+  row = 2 * p + (q >> 2);
+  c = q & 3;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int EPI, int AL, int BMAP, int BM, int BN>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(BM * BN >= 256 * 256 ? 1 : 2, BM * BN >= 256 * 256 ? 1 : 2)))
+void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
+  constexpr int TI = BM / 32, TJ = BN / 32;          // MFMA tiles per wave
+  constexpr int LA = BM / 64, LB = BN / 64;          // load instructions per wave per k-tile
+  constexpr int LW = LA + LB;
+  constexpr int STAGE = (BM + BN) * 64;              // bytes per stage
+  static_assert(kStages == 4, "the k loop is unrolled by 4");
+  // four distinct LDS objects, so the compiler sees that the DMA into one stage
+  // and the fragment reads of another do not alias
+  __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
   const int mt = j % mtiles, nt = (j / mtiles) * 8 + xcd;
   if (nt >= ntiles) return;  // padding workgroup of the XCD-aligned grid
@@ -421,95 +481,140 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g, int mtiles,
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
   const int wm = w >> 1, wn = w & 1;
 
-  ARow<uint16_t, AL> ar[ACH];
-  bool av[ACH];
-  const uint16_t* bp[BCH];
-  bool bv[BCH];
+  // per load instruction: this lane's source row pointer and chunk
+  ARow<uint16_t, AL> ar[LA];
+  int ac[LA];
+  const uint16_t* bp[LB];
+  int bc[LB];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int c = tid + i * 256, m = m0 + (c >> 3);
-    av[i] = m < g.M;
-    ar[i].init(g, av[i] ? m : 0);
+  for (int i = 0; i < LA; ++i) {
+    int row, c;
+    unswz(w + 4 * i, l, row, c);
+    ar[i].init(g, min(m0 + row, g.M - 1));
+    ac[i] = c * 8;
   }
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int c = tid + i * 256, n = n0 + (c >> 3);
-    bv[i] = n < g.N;
-    bp[i] = weight_row<uint16_t, BMAP>(g, bv[i] ? n : 0);
+  for (int i = 0; i < LB; ++i) {
+    int row, c;
+    unswz(w + 4 * i, l, row, c);
+    bp[i] = weight_row<uint16_t, BMAP>(g, min(n0 + row, g.N - 1));
+    bc[i] = c * 8;
   }
-  const uint4 zero = {0u, 0u, 0u, 0u};
-  uint4 ra[ACH], rb[BCH];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
+  auto issue = [&](unsigned char* st, int kt) {
+    const int k0 = kt * 32;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int c = tid + i * 256;
-      ra[i] = av[i] ? ld16(ar[i].at(k0 + (c & 7) * 8, g.d)) : zero;
-    }
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)ar[i].at(k0 + ac[i], g.d),
+          (__attribute__((address_space(3))) void*)(st + (w + 4 * i) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int c = tid + i * 256;
-      rb[i] = bv[i] ? ld_stream(bp[i] + k0 + (c & 7) * 8) : zero;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(As + (buf * BM + (c >> 3)) * LDK + (c & 7) * 8) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(Bs + (buf * BN + (c >> 3)) * LDK + (c & 7) * 8) = rb[i];
-    }
+    for (int i = 0; i < LB; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(bp[i] + k0 + bc[i]),
+          (__attribute__((address_space(3))) void*)(st + BM * 64 + (w + 4 * i) * 1024), 16, 0, 0);
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int aoff[TI], boff[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) aoff[i] = swz(wm * (BM / 2) + i * 16 + col, kg);
+#pragma unroll
+  for (int jj = 0; jj < TJ; ++jj) boff[jj] = BM * 64 + swz(wn * (BN / 2) + jj * 16 + col, kg);
 
-  const int nk = g.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  const int nk = g.K / 32;
+  if (0 < nk) issue(st0, 0);
+  if (1 < nk) issue(st1, 1);
+  if (2 < nk) issue(st2, 2);
+  // one k-tile: wait for this wave's DMA of stage `cur`, barrier, refill the
+  // stage freed by the previous k-tile, then the fragment reads and TI*TJ MFMAs.
+  // `cur` and `refill` are distinct stages; saying so (restrict) lets the
+  // compiler keep the refill DMA in flight across the fragment reads.
+  auto step = [&](unsigned char* __restrict__ cur, unsigned char* __restrict__ refill, int kt) {
+    const int later = min(kStages - 2, nk - 1 - kt);
+    if (later >= 2) wait_vmcnt<2 * LW>();
+    else if (later == 1) wait_vmcnt<LW>();
+    else wait_vmcnt<0>();
+    // Plain s_barrier: this wave's DMA of `cur` has landed (the wait above), every
+    // wave's reads of `refill` completed before it reached here (they fed the
+    // previous k-tile's MFMAs).  A fenced __syncthreads would also wait for the
+    // DMA into the stages still in flight and serialize the pipeline.
+    asm volatile("s_barrier" ::: "memory");
+    uint4 bf[TJ], af[TI];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint4 af[4], bf[4];
+    for (int jj = 0; jj < TJ; ++jj) bf[jj] = *reinterpret_cast<const uint4*>(cur + boff[jj]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(As + (cur * BM + wm * 64 + i * 16 + col) * LDK + kk * 32 + kg * 8);
+    for (int i = 0; i < TI; ++i) af[i] = *reinterpret_cast<const uint4*>(cur + aoff[i]);
+    if (kt + kStages - 1 < nk) issue(refill, kt + kStages - 1);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        bf[jj] = *reinterpret_cast<const uint4*>(Bs + (cur * BN + wn * 64 + jj * 16 + col) * LDK + kk * 32 + kg * 8);
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = mfma16(af[i], bf[jj], acc[i][jj]);
-    }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+      for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = mfma16(af[i], bf[jj], acc[i][jj]);
+  };
+  for (int kt = 0; kt < nk; kt += 4) {
+    step(st0, st3, kt);
+    if (kt + 1 < nk) step(st1, st0, kt + 1);
+    if (kt + 2 < nk) step(st2, st1, kt + 2);
+    if (kt + 3 < nk) step(st3, st2, kt + 3);
   }
 
-  constexpr int LDT = BN + 4;
-  float* tile = reinterpret_cast<float*>(lds);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        tile[(wm * 64 + i * 16 + kg * 4 + r) * LDT + wn * 64 + jj * 16 + col] = acc[i][jj][r];
-  __syncthreads();
+  // lane (kg, col) holds C[row 4kg + r of MFMA tile i][col of tile jj]
   if (EPI == E_ARGMAX) {
-    epilogue_argmax(g, tile, LDT, m0, BM, n0, BN);
+    __syncthreads();
+    uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [2][BM]
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lrow = wm * (BM / 2) + i * 16 + kg * 4 + r;
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int jj = 0; jj < TJ; ++jj) {
+          const int n = n0 + wn * (BN / 2) + jj * 16 + col;
+          if (n < g.N) {
+            if (g.logits && m0 + lrow < g.M) g.logits[(long long)(m0 + lrow) * g.N + n] = acc[i][jj][r];
+            const uint64_t k = argmax_key(acc[i][jj][r], n);
+            best = k > best ? k : best;
+          }
+        }
+        for (int o = 1; o < 16; o <<= 1) {
+          const uint64_t k = shfl_xor_u64(best, o);
+          best = k > best ? k : best;
+        }
+        if (col == 0) s_best[wn * BM + lrow] = best;
+      }
+    __syncthreads();
+    for (int lr = tid; lr < BM; lr += 256) {
+      if (m0 + lr < g.M) {
+        const uint64_t a = s_best[lr], c = s_best[BM + lr];
+        g.keys[(long long)(m0 + lr) * g.parts + nt] = a > c ? a : c;
+      }
+    }
   } else {
-    epilogue<uint16_t, EPI>(g, tile, LDT, m0, BM, n0, BN);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BM / 2) + i * 16 + kg * 4 + r;
+        if (m >= g.M) continue;
+        if (EPI == E_STORE || EPI == E_RESID) {
+#pragma unroll
+          for (int jj = 0; jj < TJ; ++jj) {
+            const int n = n0 + wn * (BN / 2) + jj * 16 + col;
+            if (n < g.N) epi_one<uint16_t, EPI>(g, m, n, acc[i][jj][r]);
+          }
+        } else {
+          // a wave's BN/2 columns are whole 32-column blocks: tiles (2q, 2q+1) pair up
+#pragma unroll
+          for (int q = 0; q < TJ / 2; ++q) {
+            const int nb = n0 + wn * (BN / 2) + q * 32;
+            if (nb < g.N) epi_pair<uint16_t, EPI>(g, m, nb, col, acc[i][2 * q][r], acc[i][2 * q + 1][r]);
+          }
+        }
+      }
   }
 }
 
@@ -532,7 +637,7 @@ __global__ __launch_bounds__(512) void gemm_f32_kernel(GemmArgs g) {
   tile[i * 33 + c] = s;
   __syncthreads();
   if (EPI == E_ARGMAX) {
-    epilogue_argmax(g, tile, 33, m0, 16, n0, 32);
+    epilogue_argmax(g, tile, 33, m0, 16, n0, 32, blockIdx.x);
   } else {
     epilogue<float, EPI>(g, tile, 33, m0, 16, n0, 32);
   }
@@ -547,6 +652,24 @@ static hipError_t set_lds(F* fn, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
 }
 
+// Which kernel serves a bf16 GEMM of this shape.
+enum Variant { V_WIDE, V_SKINNY, V_TILED };
+static Variant pick(int epi, int M, int K) {
+  const size_t wide_lds = size_t(M) * (K / 8 + 1) * 16;
+  if (epi == E_ARGMAX && M <= 16 && wide_lds <= 140 * 1024) return V_WIDE;
+  return M <= 64 ? V_SKINNY : V_TILED;
+}
+constexpr int kArgmaxBN = 256;
+
+int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus) {
+  if (dtype != 1) return (N + 31) / 32;
+  switch (pick(E_ARGMAX, M, K)) {
+    case V_WIDE: return std::min(num_cus, N / 16);
+    case V_SKINNY: return (N + 15) / 16;
+    default: return (N + kArgmaxBN - 1) / kArgmaxBN;
+  }
+}
+
 template <int EPI, int AL, int BMAP, int MT>
 static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
   constexpr int NTW = (BMAP == B_PLAIN) ? 1 : 2;
@@ -556,10 +679,11 @@ static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
   nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
   while (nw > 1 && nw * MT * NTW > 128) --nw;
   const size_t lds = size_t(nw) * MT * NTW * 256 * 4 + size_t(MT * 16) * (NTW * 16 + 4) * 4;
+  const int grid = (g.N + NTW * 16 - 1) / (NTW * 16);
+  if (EPI == E_ARGMAX && g.parts != grid) return hipErrorInvalidValue;
   auto fn = gemm_skinny_kernel<EPI, AL, BMAP, MT, NTW, U>;
   hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
-  const int grid = (g.N + NTW * 16 - 1) / (NTW * 16);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * nw), lds, st, g);
   return hipGetLastError();
 }
@@ -567,12 +691,11 @@ static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
 template <int U>
 static hipError_t run_wide(const GemmArgs& g, int num_cus, hipStream_t st) {
   const size_t lds = size_t(g.M) * (g.K / 8 + 1) * 16;
+  const int grid = std::min(num_cus, g.N / 16);
+  if (g.parts != grid) return hipErrorInvalidValue;
   auto fn = lmhead_wide_kernel<U>;
   hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
-  int grid = num_cus;
-  const int ntiles = g.N / 16;
-  if (grid > ntiles) grid = ntiles;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(512), lds, st, g);
   return hipGetLastError();
 }
@@ -594,27 +717,35 @@ static hipError_t run_wide_any(const GemmArgs& g, int num_cus, hipStream_t st) {
   return run_wide<1>(g, num_cus, st);
 }
 
+template <int EPI, int AL, int BMAP, int BM, int BN>
+static hipError_t run_tiled(const GemmArgs& g, hipStream_t st) {
+  const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN;
+  if (EPI == E_ARGMAX && g.parts != ntiles) return hipErrorInvalidValue;
+  const int grid = mtiles * ((ntiles + 7) / 8) * 8;
+  hipLaunchKernelGGL((gemm_tiled_kernel<EPI, AL, BMAP, BM, BN>), dim3(grid), dim3(256), 0, st, g,
+                     mtiles, ntiles);
+  return hipGetLastError();
+}
+
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
-  const size_t wide_lds = size_t(g.M) * (g.K / 8 + 1) * 16;
-  if (EPI == E_ARGMAX && g.M <= 16 && wide_lds <= 140 * 1024) return run_wide_any(g, num_cus, st);
-  if (g.M <= 16) return run_skinny<EPI, AL, BMAP, 1>(g, st);
-  if (g.M <= 32) return run_skinny<EPI, AL, BMAP, 2>(g, st);
-  if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
-  if (g.M <= 64) return run_skinny<EPI, AL, BMAP, 4>(g, st);
-  const int mtiles = (g.M + 127) / 128, ntiles = (g.N + 127) / 128;
-  const int grid = mtiles * ((ntiles + 7) / 8) * 8;
-  const size_t lds = 2 * size_t(128 + 128) * 72 * 2;
-  auto fn = gemm_tiled_kernel<EPI, AL, BMAP>;
-  hipError_t e = set_lds(fn, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, st, g, mtiles, ntiles);
-  return hipGetLastError();
+  switch (pick(EPI, g.M, g.K)) {
+    case V_WIDE: return run_wide_any(g, num_cus, st);
+    case V_SKINNY:
+      if (g.M <= 16) return run_skinny<EPI, AL, BMAP, 1>(g, st);
+      if (g.M <= 32) return run_skinny<EPI, AL, BMAP, 2>(g, st);
+      if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
+      return run_skinny<EPI, AL, BMAP, 4>(g, st);
+    default:
+      if constexpr (EPI == E_ARGMAX) return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN>(g, st);
+      else return run_tiled<EPI, AL, BMAP, 128, 128>(g, st);
+  }
 }
 
 template <int EPI, int AL, int BMAP>
 static hipError_t run_f32(const GemmArgs& g, hipStream_t st) {
   dim3 grid((g.N + 31) / 32, (g.M + 15) / 16);
+  if (EPI == E_ARGMAX && g.parts != int(grid.x)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_f32_kernel<EPI, AL, BMAP>), grid, dim3(512), 0, st, g);
   return hipGetLastError();
 }
@@ -624,11 +755,11 @@ static hipError_t run(int dtype, const GemmArgs& g, int num_cus, hipStream_t st)
   return dtype == 1 ? run_bf16<EPI, AL, BMAP>(g, num_cus, st) : run_f32<EPI, AL, BMAP>(g, st);
 }
 
-hipError_t launch_argmax_tokens(int M, int Kd, uint64_t* keys, int32_t* tokens,
+hipError_t launch_argmax_tokens(int M, int Kd, int parts, const uint64_t* keys, int32_t* tokens,
                                 const int32_t* seq_lens, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_tokens_kernel, dim3((M + 255) / 256), dim3(256), 0, st, M, Kd, keys,
-                     tokens, seq_lens);
+  hipLaunchKernelGGL(argmax_tokens_kernel, dim3(M), dim3(256), 0, st, M, Kd, parts, keys, tokens,
+                     seq_lens);
   return hipGetLastError();
 }
 

@@ -49,13 +49,16 @@ struct GemmArgs {
   int Hkv, hd, block_size; long long num_slots;
   const float* rope_inv;  // [hd/2] inverse frequencies (float)
   const double* rope_inv_d;  // [hd/2] the same in double (angle reduction)
-  uint64_t* keys;                                 // E_ARGMAX (zero between launches)
+  uint64_t* keys; int parts;                      // E_ARGMAX: keys[row * parts + part]
   int32_t* tokens; float* logits; const int32_t* seq_lens; int Kd;
 };
 hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,
                        hipStream_t st);
-// After an E_ARGMAX GEMM: keys -> tokens (-1 for padded requests), keys cleared.
-hipError_t launch_argmax_tokens(int M, int Kd, uint64_t* keys, int32_t* tokens,
+// Number of partial argmax keys per row the E_ARGMAX GEMM of this shape writes.
+int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus);
+// After an E_ARGMAX GEMM: max over each row's partial keys -> token (-1 for a
+// padded request).
+hipError_t launch_argmax_tokens(int M, int Kd, int parts, const uint64_t* keys, int32_t* tokens,
                                 const int32_t* seq_lens, hipStream_t st);
 
 // ---- attention ------------------------------------------------------------
