@@ -434,7 +434,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       a.bt = block_table; a.out = ctx->attn;
       a.part_o = ctx->part_o; a.part_ml = ctx->part_ml;
       a.target_items = ctx->target_items;
-      long long grid = 4LL * ctx->num_cus;
+      long long grid = 2LL * ctx->num_cus;  // two 512-thread workgroups fit per CU
       const long long mx = pe::attn_max_items(B, k.n_kv_heads, ctx->target_items);
       a.grid = int(grid < mx ? grid : mx);
       Timed tm(ctx, PE_PH_ATTN);

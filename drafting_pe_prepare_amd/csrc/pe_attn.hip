@@ -39,17 +39,19 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Split-KV plan shared by the partial and merge kernels: total context ->
 // chunk size CH (multiple of 32, >= 64); off[r] = first chunk of request r.
+// Any blockDim that is a multiple of 64 and <= 512.
 __device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, int* off,
                           int& CH) {
-  __shared__ long long s_tot[4];
-  __shared__ int s_part[256];
-  const int tid = threadIdx.x, nt = blockDim.x;  // nt == 256
+  __shared__ long long s_tot[8];
+  __shared__ int s_part[512];
+  const int tid = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
   long long tot = 0;
   for (int r = tid; r < B; r += nt) tot += max(seq_lens[r], 0);
   for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
   if ((tid & 63) == 0) s_tot[tid >> 6] = tot;
   __syncthreads();
-  tot = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+  tot = 0;
+  for (int w = 0; w < nw; ++w) tot += s_tot[w];
   long long ch = (tot * Hkv + target - 1) / (target > 0 ? target : 1);
   ch = (ch + 31) / 32 * 32;
   if (ch < 64) ch = 64;
@@ -80,9 +82,36 @@ long long attn_max_items(int B, int Hkv, int target_items) {
   return (long long)target_items + (long long)(B + 1) * Hkv;
 }
 
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+// LDS tiles of one 32-position step for one KV head.
+//  K: 32 positions x 128 B; chunk c (16 B, 8 dims) of position p sits at
+//     p*128 + (c ^ kswz(p))*16.  kswz makes the 8 rows a score fragment read
+//     together (positions 8(r/4) + 4t + r%4, r = 0..7) land in 8 distinct
+//     16-byte bank groups.
+//  V: 64 dims x 64 B (d-major: 32 positions x 2 B per dim row), laid out with
+//     the same pair-of-rows swizzle as the GEMM tiles (vswz).
+__device__ __forceinline__ int kswz(int p) { return (p & 3) | (((p >> 3) & 1) << 2); }
+__device__ __forceinline__ int vswz(int row, int c) {
+  const int q = row >> 1;
+  return q * 128 + ((((row & 1) << 2) | c) ^ (q & 3)) * 16;
+}
+
+template <int N>
+__device__ __forceinline__ void attn_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One workgroup of 8 waves per (request, chunk, KV head) item.  Every step the
+// 8 waves each issue one 1 KB LDS DMA (4 fill the K tile, 4 the V tile) three
+// steps ahead, then each wave runs its QPW query tiles of 16 (S*G queries =
+// S slots x G heads of the group) against the shared tile.
+template <int QPW>
+__global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
   __shared__ int s_off[kMaxB + 1];
-  __shared__ float s_ot[4][64][17];
+  __shared__ __attribute__((aligned(16))) unsigned char k0[4096], k1[4096], k2[4096], k3[4096];
+  __shared__ __attribute__((aligned(16))) unsigned char v0[4096], v1[4096], v2[4096], v3[4096];
+  __shared__ float s_ot[8][64][17];
+  constexpr int WIN = 8192;                 // positions per block-id window
+  __shared__ int s_bt[WIN / 16 + 2];        // block ids of the window (block_size >= 16)
   int CH;
   attn_plan(a.seq_lens, a.B, a.Hkv, a.target_items, s_off, CH);
   const int G = a.Hq / a.Hkv, QN = a.S * G, QT = (QN + 15) >> 4;
@@ -94,6 +123,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const uint16_t* Vc = (const uint16_t*)a.vcache;
   const int bs = a.block_size;
   const uint4 zero = {0u, 0u, 0u, 0u};
+  // fragment offsets inside a stage
+  int koff[2][2], voff[4];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int p = 8 * (c >> 2) + 4 * pt + (c & 3);
+      koff[pt][ks] = p * 128 + (((gq + 4 * ks)) ^ kswz(p)) * 16;
+    }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) voff[dt] = vswz(c + 16 * dt, gq);
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int rc = item / a.Hkv, g = item - rc * a.Hkv;
@@ -104,50 +144,97 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     }
     const int r = lo, chunk = rc - s_off[r];
     const int L = a.seq_lens[r];
-    const int pb = chunk * CH, pe = min(L, pb + CH);
+    const int cb = chunk * CH, ce = min(L, cb + CH);
     const int32_t* btr = a.bt + (long long)r * a.max_blocks;
 
-    for (int t = w; t < QT; t += 4) {
-      const int q = t * 16 + c;
-      bool qv = q < QN;
-      const int s = qv ? q / G : 0, hh = qv ? q % G : 0, row = r * a.S + s;
-      qv = qv && !a.rej[row];
-      const int qpos = qv ? a.positions[row] : -1;
-      uint4 qf[2];
+    // query tiles of this wave
+    uint4 qf[QPW][2];
+    float m[QPW], lsum[QPW];
+    int qpos[QPW];
+    bool qv[QPW];
+    f32x4 o[QPW][4];
+#pragma unroll
+    for (int qq = 0; qq < QPW; ++qq) {
+      const int q = (w + 8 * qq) * 16 + c;
+      bool v = q < QN;
+      const int s = v ? q / G : 0, hh = v ? q % G : 0, row = r * a.S + s;
+      v = v && !a.rej[row];
+      qv[qq] = v;
+      qpos[qq] = v ? a.positions[row] : -1;
       const uint16_t* qp = Q + ((long long)row * a.Hq + g * G + hh) * 64 + gq * 8;
-      qf[0] = qv ? ld16(qp) : zero;
-      qf[1] = qv ? ld16(qp + 32) : zero;
-      float m = -INFINITY, lsum = 0.f;
-      f32x4 o[4];
+      qf[qq][0] = v ? ld16(qp) : zero;
+      qf[qq][1] = v ? ld16(qp + 32) : zero;
+      m[qq] = -INFINITY;
+      lsum[qq] = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < 4; ++dt) o[qq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-      for (int p = pb; p < pe; p += 32) {
-        uint4 kf[2][2];
+    // positions [cb, ce) in windows of WIN; the block ids of a window are
+    // staged in LDS first, so no global load sits between the DMAs (vmcnt
+    // retires in order: a block-table load would wait for every DMA before it)
+    for (int pb = cb; pb < ce; pb += WIN) {
+    const int pe = min(ce, pb + WIN);
+    const int nsteps = (pe - pb + 31) >> 5;
+    const int wb0 = pb / bs, wb1 = (pe - 1) / bs;
+    for (int i = threadIdx.x; i <= wb1 - wb0; i += blockDim.x) s_bt[i] = btr[wb0 + i];
+    __syncthreads();
+    // this wave's DMA instruction of a step: w < 4 fills K rows 8w..8w+7, w >= 4
+    // fills V lines 8(w-4)..8(w-4)+7
+    auto issue = [&](unsigned char* __restrict__ kst, unsigned char* __restrict__ vst, int step) {
+      const int p = pb + step * 32;
+      if (w < 4) {
+        const int pos = 8 * w + (l >> 3);
+        const int ch = (l & 7) ^ kswz(pos);
+        int pp = p + pos;
+        pp = pp < pe ? pp : pe - 1;  // past the window: masked, but stay on staged blocks
+        const long long slot = (long long)s_bt[pp / bs - wb0] * bs + pp % bs;
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)(Kc + (slot * a.Hkv + g) * 64 + ch * 8),
+            (__attribute__((address_space(3))) void*)(kst + w * 1024), 16, 0, 0);
+      } else {
+        const int line = 8 * (w - 4) + (l >> 3);
+        const int x = (l & 7) ^ (line & 3);
+        const int d = 2 * line + (x >> 2), ch = x & 3;
+        int pp = p + (ch >> 1) * 16;
+        pp = pp < pe ? pp : ((pe - 1) & ~15);
+        const long long blk = s_bt[pp / bs - wb0];
+        const int off = pp % bs + (ch & 1) * 8;
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)(Vc + ((blk * a.Hkv + g) * 64 + d) * bs + off),
+            (__attribute__((address_space(3))) void*)(vst + (w - 4) * 1024), 16, 0, 0);
+      }
+    };
+
+    if (0 < nsteps) issue(k0, v0, 0);
+    if (1 < nsteps) issue(k1, v1, 1);
+    if (2 < nsteps) issue(k2, v2, 2);
+    auto step = [&](const unsigned char* __restrict__ kcur, const unsigned char* __restrict__ vcur,
+                    unsigned char* __restrict__ kref, unsigned char* __restrict__ vref, int st) {
+      const int later = min(2, nsteps - 1 - st);
+      if (later >= 2) attn_wait_vmcnt<2>();
+      else if (later == 1) attn_wait_vmcnt<1>();
+      else attn_wait_vmcnt<0>();
+      asm volatile("s_barrier" ::: "memory");  // see the GEMM: no fence, DMA stays in flight
+      uint4 kf[2][2], vf[4];
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) kf[pt][ks] = *reinterpret_cast<const uint4*>(kcur + koff[pt][ks]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) vf[dt] = *reinterpret_cast<const uint4*>(vcur + voff[dt]);
+      if (st + 3 < nsteps) issue(kref, vref, st + 3);
+      const int pv0 = pb + st * 32 + 8 * gq;
+#pragma unroll
+      for (int qq = 0; qq < QPW; ++qq) {
+        if (w + 8 * qq >= QT) break;
+        f32x4 sc[2];
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
-          int pp = p + 8 * (c >> 2) + 4 * pt + (c & 3);
-          pp = pp < L ? pp : L - 1;
-          const long long slot = (long long)btr[pp / bs] * bs + pp % bs;
-          const uint16_t* kp = Kc + (slot * a.Hkv + g) * 64 + gq * 8;
-          kf[pt][0] = ld16(kp);
-          kf[pt][1] = ld16(kp + 32);
+          sc[pt] = mfma16(kf[pt][0], qf[qq][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          sc[pt] = mfma16(kf[pt][1], qf[qq][1], sc[pt]);
         }
-        const int pv0 = p + 8 * gq;
-        const int pvc = pv0 < L ? pv0 : ((L - 1) & ~7);
-        const long long blk = btr[pvc / bs];
-        const uint16_t* vb = Vc + ((blk * a.Hkv + g) * 64) * bs + (pvc % bs);
-        uint4 vf[4];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) vf[dt] = ld16(vb + (long long)(c + 16 * dt) * bs);
-
-        f32x4 st[2];
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          st[pt] = mfma16(kf[pt][0], qf[0], f32x4{0.f, 0.f, 0.f, 0.f});
-          st[pt] = mfma16(kf[pt][1], qf[1], st[pt]);
-        }
-        // lane (gq, c): st[pt][i] is the score of position p + 8gq + 4pt + i for query c
+        // lane (gq, c): sc[pt][i] scores position pv0 + 4pt + i for query c
         float v[8];
         float mloc = -INFINITY;
 #pragma unroll
@@ -155,16 +242,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int pos = pv0 + 4 * pt + i;
-            const bool ok = qv && pos < pe && pos <= qpos;
-            const float x = ok ? st[pt][i] * sl2 : -INFINITY;
+            const bool ok = qv[qq] && pos < pe && pos <= qpos[qq];
+            const float x = ok ? sc[pt][i] * sl2 : -INFINITY;
             v[4 * pt + i] = x;
             mloc = fmaxf(mloc, x);
           }
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const float mnew = fmaxf(m, mloc);
+        const float mnew = fmaxf(m[qq], mloc);
         const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = exp2f(m - mref);
+        const float alpha = exp2f(m[qq] - mref);
         uint32_t pk[4];
         float ps = 0.f;
 #pragma unroll
@@ -174,49 +261,65 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
           ps += bf2f(b0) + bf2f(b1);
           pk[jj] = uint32_t(b0) | (uint32_t(b1) << 16);
         }
-        lsum = lsum * alpha + ps;
-        m = mnew;
+        lsum[qq] = lsum[qq] * alpha + ps;
+        m[qq] = mnew;
         const uint4 pf = {pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          o[dt] = o[dt] * alpha;
-          o[dt] = mfma16(vf[dt], pf, o[dt]);
+          o[qq][dt] = o[qq][dt] * alpha;
+          o[qq][dt] = mfma16(vf[dt], pf, o[qq][dt]);
         }
       }
-      lsum += __shfl_xor(lsum, 16, 64);
-      lsum += __shfl_xor(lsum, 32, 64);
+    };
+    for (int st = 0; st < nsteps; st += 4) {
+      step(k0, v0, k3, v3, st);
+      if (st + 1 < nsteps) step(k1, v1, k0, v0, st + 1);
+      if (st + 2 < nsteps) step(k2, v2, k1, v1, st + 2);
+      if (st + 3 < nsteps) step(k3, v3, k2, v2, st + 3);
+    }
+    __syncthreads();  // stages and s_bt are reused by the next window
+    }  // windows
 
-      // O^T lane (gq, c): o[dt][i] = O[q = c][d = 16dt + 4gq + i]; transpose via LDS
+    // partials: O (un-normalised), running max m (base 2) and sum l per query
+#pragma unroll
+    for (int qq = 0; qq < QPW; ++qq) {
+      const int t = w + 8 * qq;
+      if (t >= QT) break;
+      float ls = lsum[qq];
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_ot[w][16 * dt + 4 * gq + i][c] = o[dt][i];
-      wave_lds_sync();  // s_ot[w] is private to this wave; waves run different tile counts
-      {
-        const int qq = l >> 2, d0 = (l & 3) * 16;
-        const int qg = t * 16 + qq;
-        if (qg < QN) {
-          float* dst = a.part_o + ((long long)item * QN + qg) * 64 + d0;
+        for (int i = 0; i < 4; ++i) s_ot[w][16 * dt + 4 * gq + i][c] = o[qq][dt][i];
+      wave_lds_sync();
+      const int qi = l >> 2, d0 = (l & 3) * 16, qg = t * 16 + qi;
+      if (qg < QN) {
+        float* dst = a.part_o + ((long long)item * QN + qg) * 64 + d0;
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            float4 f;
-            f.x = s_ot[w][d0 + 4 * v4 + 0][qq];
-            f.y = s_ot[w][d0 + 4 * v4 + 1][qq];
-            f.z = s_ot[w][d0 + 4 * v4 + 2][qq];
-            f.w = s_ot[w][d0 + 4 * v4 + 3][qq];
-            *reinterpret_cast<float4*>(dst + 4 * v4) = f;
-          }
+        for (int v4 = 0; v4 < 4; ++v4) {
+          float4 f;
+          f.x = s_ot[w][d0 + 4 * v4 + 0][qi];
+          f.y = s_ot[w][d0 + 4 * v4 + 1][qi];
+          f.z = s_ot[w][d0 + 4 * v4 + 2][qi];
+          f.w = s_ot[w][d0 + 4 * v4 + 3][qi];
+          *reinterpret_cast<float4*>(dst + 4 * v4) = f;
         }
-        if (gq == 0 && q < QN) {
-          a.part_ml[((long long)item * QN + q) * 2 + 0] = m;
-          a.part_ml[((long long)item * QN + q) * 2 + 1] = lsum;
-        }
+      }
+      const int q = t * 16 + c;
+      if (gq == 0 && q < QN) {
+        a.part_ml[((long long)item * QN + q) * 2 + 0] = m[qq];
+        a.part_ml[((long long)item * QN + q) * 2 + 1] = ls;
       }
       wave_lds_sync();
     }
+    __syncthreads();  // the stages are reused by the next item
   }
 }
 
+// One wave per (slot, query head): lane = dim.  Lanes first share out the
+// chunks to find the max, then every chunk's weight is broadcast and the
+// weighted partial rows are summed with independent loads.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   __shared__ int s_off[kMaxB + 1];
   int CH;
@@ -231,18 +334,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     uint16_t* dst = out + (long long)row * a.Hq * 64 + h * 64 + l;
     if (a.rej[row] || a.seq_lens[r] <= 0) { *dst = 0; continue; }
     const int c0 = s_off[r], nc = s_off[r + 1] - c0;
+    auto ml = [&](int ch) { return a.part_ml + ((long long)((c0 + ch) * a.Hkv + g) * QN + q) * 2; };
     float M = -INFINITY;
-    for (int ch = 0; ch < nc; ++ch)
-      M = fmaxf(M, a.part_ml[((long long)((c0 + ch) * a.Hkv + g) * QN + q) * 2]);
+    for (int ch = l; ch < nc; ch += 64) M = fmaxf(M, ml(ch)[0]);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float Lsum = 0.f, O = 0.f;
-    if (M != -INFINITY)
-      for (int ch = 0; ch < nc; ++ch) {
-        const long long it = (long long)(c0 + ch) * a.Hkv + g;
-        const float mc = a.part_ml[(it * QN + q) * 2];
-        const float wgt = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
-        Lsum += wgt * a.part_ml[(it * QN + q) * 2 + 1];
-        O += wgt * a.part_o[(it * QN + q) * 64 + l];
+    if (M != -INFINITY) {
+      for (int base = 0; base < nc; base += 64) {
+        const int ch = base + l;
+        float wl = 0.f, lc = 0.f;
+        if (ch < nc) {
+          const float mc = ml(ch)[0];
+          wl = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
+          lc = ml(ch)[1];
+        }
+        Lsum += wl * lc;
+        const int n = min(64, nc - base);
+#pragma unroll 4
+        for (int j = 0; j < n; ++j) {
+          const float wj = __shfl(wl, j, 64);
+          const long long it = (long long)(c0 + base + j) * a.Hkv + g;
+          O += wj * a.part_o[(it * QN + q) * 64 + l];
+        }
       }
+      for (int o = 32; o > 0; o >>= 1) Lsum += __shfl_xor(Lsum, o, 64);
+    }
     *dst = f2bf(Lsum > 0.f ? O / Lsum : 0.f);
   }
 }
@@ -308,7 +424,15 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.B * a.S * a.Hq), dim3(64), 0, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(attn_partial_kernel, dim3(a.grid), dim3(256), 0, st, a);
+  const int QT = (a.S * (a.Hq / a.Hkv) + 15) / 16;
+  if (QT <= 8)
+    hipLaunchKernelGGL(attn_partial_kernel<1>, dim3(a.grid), dim3(512), 0, st, a);
+  else if (QT <= 16)
+    hipLaunchKernelGGL(attn_partial_kernel<2>, dim3(a.grid), dim3(512), 0, st, a);
+  else if (QT <= 32)
+    hipLaunchKernelGGL(attn_partial_kernel<4>, dim3(a.grid), dim3(512), 0, st, a);
+  else
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   long long waves = (long long)a.B * a.S * a.Hq;
