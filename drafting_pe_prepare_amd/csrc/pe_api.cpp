@@ -68,6 +68,7 @@ struct pe_ctx {
   float* part_ml = nullptr;
   float* rope_inv = nullptr;
   double* rope_inv_d = nullptr;
+  void* lm_packed = nullptr;  // fragment-order copy of the LM head (bf16)
   int target_items = 1024;
   long long items_max = 0;
   // step graph
@@ -129,7 +130,7 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->rope_inv, c->rope_inv_d};
+                  c->part_o, c->part_ml, c->rope_inv, c->rope_inv_d, c->lm_packed};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   delete c;
@@ -290,6 +291,20 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   if (e != hipSuccess) {
     free_ctx(c);
     return hipfail(e, "workspace init");
+  }
+  if (k.dtype == PE_BF16) {
+    // The LM head streams V*d*2 bytes per step; a copy in MFMA-fragment order lets
+    // every wave load one contiguous 1 KB per k-step (full lines, non-temporal).
+    if ((s = alloc(&c->lm_packed, size_t(k.vocab) * k.d * 2, "packed LM head")) != PE_OK) {
+      free_ctx(c);
+      return s;
+    }
+    e = pe::launch_pack_frag16(w->lm_head, c->lm_packed, k.vocab, k.d, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) {
+      free_ctx(c);
+      return hipfail(e, "pack LM head");
+    }
   }
   *out = c;
   return PE_OK;
@@ -483,6 +498,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
     g.M = D; g.N = k.vocab; g.K = d;
     g.A = ctx->z; g.lda = d;
     g.W0 = ctx->w.lm_head;
+    g.Wp = ctx->lm_packed;
     g.keys = ctx->keys; g.tokens = draft_tokens; g.logits = logits;
     g.parts = pe::gemm_argmax_parts(dt, D, k.vocab, d, ctx->num_cus);
     g.seq_lens = batch->seq_lens; g.Kd = k.K;

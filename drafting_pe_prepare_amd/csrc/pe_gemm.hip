@@ -267,7 +267,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
       if (u < n) {
         const int k = (ks + u) * 32;
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) b[u][t] = ld_stream(wp[t] + k);
+        for (int t = 0; t < NTW; ++t) b[u][t] = ld16(wp[t] + k);  // plain: stays cache-resident
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? ld16(ar[mt].at(k + kg * 8, g.d)) : zero;
       }
@@ -344,7 +344,10 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
   const bool arow = col < g.M;
   const uint4 zero = {0u, 0u, 0u, 0u};
   const uint4* xrow = xs + col * ldx + kg;
-  const uint16_t* wbase = (const uint16_t*)g.W0 + (long long)col * K + kg * 8;
+  // fragment-order copy (contiguous 1 KB per k-step) when the context made one
+  const int ksteps = K >> 5;
+  const uint16_t* wbase = g.Wp ? (const uint16_t*)g.Wp + l * 8
+                               : (const uint16_t*)g.W0 + (long long)col * K + kg * 8;
   uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
@@ -361,10 +364,16 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
     }
   };
   auto issue = [&](uint4 (&b)[U], int u) {
-    const int tile = T0 + u / cpt, k0 = (u % cpt) * U * 32;
-    const uint16_t* wp = wbase + (long long)tile * 16 * K + k0;
+    const int tile = T0 + u / cpt, s0 = (u % cpt) * U;
+    if (g.Wp) {
+      const uint16_t* wp = wbase + ((long long)tile * ksteps + s0) * 512;
 #pragma unroll
-    for (int j = 0; j < U; ++j) b[j] = ld_stream(wp + j * 32);
+      for (int j = 0; j < U; ++j) b[j] = ld_stream(wp + j * 512);
+    } else {
+      const uint16_t* wp = wbase + (long long)tile * 16 * K + s0 * 32;
+#pragma unroll
+      for (int j = 0; j < U; ++j) b[j] = ld_stream(wp + j * 32);
+    }
   };
   auto consume = [&](uint4 (&b)[U], int u) {
     const int c = u % cpt, tile = T0 + u / cpt;
@@ -461,12 +470,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int EPI, int AL, int BMAP, int BM, int BN>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(BM * BN >= 256 * 256 ? 1 : 2, BM * BN >= 256 * 256 ? 1 : 2)))
+template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
-  constexpr int TI = BM / 32, TJ = BN / 32;          // MFMA tiles per wave
-  constexpr int LA = BM / 64, LB = BN / 64;          // load instructions per wave per k-tile
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;   // MFMA tiles per wave
+  constexpr int LA = BM / 16 / NW, LB = BN / 16 / NW;   // load instructions per wave per k-tile
+  static_assert(LA * 16 * NW == BM && LB * 16 * NW == BN, "tile rows must split over the waves");
+  static_assert((BN / WN) % 32 == 0, "a wave's columns must be whole 32-column blocks");
   constexpr int LW = LA + LB;
   constexpr int STAGE = (BM + BN) * 64;              // bytes per stage
   static_assert(kStages == 4, "the k loop is unrolled by 4");
@@ -479,7 +490,7 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   if (nt >= ntiles) return;  // padding workgroup of the XCD-aligned grid
   const int m0 = mt * BM, n0 = nt * BN;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
 
   // per load instruction: this lane's source row pointer and chunk
   ARow<uint16_t, AL> ar[LA];
@@ -489,14 +500,14 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     int row, c;
-    unswz(w + 4 * i, l, row, c);
+    unswz(w + NW * i, l, row, c);
     ar[i].init(g, min(m0 + row, g.M - 1));
     ac[i] = c * 8;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     int row, c;
-    unswz(w + 4 * i, l, row, c);
+    unswz(w + NW * i, l, row, c);
     bp[i] = weight_row<uint16_t, BMAP>(g, min(n0 + row, g.N - 1));
     bc[i] = c * 8;
   }
@@ -506,12 +517,12 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
     for (int i = 0; i < LA; ++i)
       __builtin_amdgcn_global_load_lds(
           (__attribute__((address_space(1))) void*)ar[i].at(k0 + ac[i], g.d),
-          (__attribute__((address_space(3))) void*)(st + (w + 4 * i) * 1024), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(st + (w + NW * i) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
       __builtin_amdgcn_global_load_lds(
           (__attribute__((address_space(1))) void*)(bp[i] + k0 + bc[i]),
-          (__attribute__((address_space(3))) void*)(st + BM * 64 + (w + 4 * i) * 1024), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(st + BM * 64 + (w + NW * i) * 1024), 16, 0, 0);
   };
 
   f32x4 acc[TI][TJ];
@@ -521,9 +532,9 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
     for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
   int aoff[TI], boff[TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) aoff[i] = swz(wm * (BM / 2) + i * 16 + col, kg);
+  for (int i = 0; i < TI; ++i) aoff[i] = swz(wm * (BM / WM) + i * 16 + col, kg);
 #pragma unroll
-  for (int jj = 0; jj < TJ; ++jj) boff[jj] = BM * 64 + swz(wn * (BN / 2) + jj * 16 + col, kg);
+  for (int jj = 0; jj < TJ; ++jj) boff[jj] = BM * 64 + swz(wn * (BN / WN) + jj * 16 + col, kg);
 
   const int nk = g.K / 32;
   if (0 < nk) issue(st0, 0);
@@ -564,16 +575,17 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   // lane (kg, col) holds C[row 4kg + r of MFMA tile i][col of tile jj]
   if (EPI == E_ARGMAX) {
     __syncthreads();
-    uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [2][BM]
+    uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [WN][BM]
+    static_assert(WN * BM * 8 <= STAGE, "argmax scratch fits one stage");
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int lrow = wm * (BM / 2) + i * 16 + kg * 4 + r;
+        const int lrow = wm * (BM / WM) + i * 16 + kg * 4 + r;
         uint64_t best = 0ull;
 #pragma unroll
         for (int jj = 0; jj < TJ; ++jj) {
-          const int n = n0 + wn * (BN / 2) + jj * 16 + col;
+          const int n = n0 + wn * (BN / WN) + jj * 16 + col;
           if (n < g.N) {
             if (g.logits && m0 + lrow < g.M) g.logits[(long long)(m0 + lrow) * g.N + n] = acc[i][jj][r];
             const uint64_t k = argmax_key(acc[i][jj][r], n);
@@ -587,10 +599,11 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
         if (col == 0) s_best[wn * BM + lrow] = best;
       }
     __syncthreads();
-    for (int lr = tid; lr < BM; lr += 256) {
+    for (int lr = tid; lr < BM; lr += NT) {
       if (m0 + lr < g.M) {
-        const uint64_t a = s_best[lr], c = s_best[BM + lr];
-        g.keys[(long long)(m0 + lr) * g.parts + nt] = a > c ? a : c;
+        uint64_t bk = s_best[lr];
+        for (int v = 1; v < WN; ++v) bk = s_best[v * BM + lr] > bk ? s_best[v * BM + lr] : bk;
+        g.keys[(long long)(m0 + lr) * g.parts + nt] = bk;
       }
     }
   } else {
@@ -598,19 +611,19 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * (BM / 2) + i * 16 + kg * 4 + r;
+        const int m = m0 + wm * (BM / WM) + i * 16 + kg * 4 + r;
         if (m >= g.M) continue;
         if (EPI == E_STORE || EPI == E_RESID) {
 #pragma unroll
           for (int jj = 0; jj < TJ; ++jj) {
-            const int n = n0 + wn * (BN / 2) + jj * 16 + col;
+            const int n = n0 + wn * (BN / WN) + jj * 16 + col;
             if (n < g.N) epi_one<uint16_t, EPI>(g, m, n, acc[i][jj][r]);
           }
         } else {
           // a wave's BN/2 columns are whole 32-column blocks: tiles (2q, 2q+1) pair up
 #pragma unroll
           for (int q = 0; q < TJ / 2; ++q) {
-            const int nb = n0 + wn * (BN / 2) + q * 32;
+            const int nb = n0 + wn * (BN / WN) + q * 32;
             if (nb < g.N) epi_pair<uint16_t, EPI>(g, m, nb, col, acc[i][2 * q][r], acc[i][2 * q + 1][r]);
           }
         }
@@ -650,6 +663,35 @@ template <typename F>
 static hipError_t set_lds(F* fn, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
+
+// ---------------------------------------------------------------------------
+// Fragment-order copy of a row-major weight [N, K] (bf16): 1 KB block (t, s)
+// holds, for lane l, W[16t + l%16][32s + 8(l/16) .. +8] at bytes 16 l.  A wave
+// that streams tile t then reads one contiguous 1 KB per MFMA k-step.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_frag16_kernel(const uint4* __restrict__ W,
+                                                          uint4* __restrict__ out, int N, int K) {
+  const int ks = K >> 5, kc = K >> 3;  // k-steps, 16 B chunks per row
+  const long long total = (long long)(N >> 4) * ks * 64;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int l = int(i & 63);
+    const long long ts = i >> 6;
+    const int s = int(ts % ks);
+    const long long t = ts / ks;
+    const long long row = t * 16 + (l & 15);
+    out[i] = W[row * kc + s * 4 + (l >> 4)];
+  }
+}
+
+hipError_t launch_pack_frag16(const void* W, void* out, int N, int K, hipStream_t st) {
+  const long long total = (long long)(N / 16) * (K / 32) * 64;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(pack_frag16_kernel, dim3(unsigned(blocks)), dim3(256), 0, st,
+                     (const uint4*)W, (uint4*)out, N, K);
+  return hipGetLastError();
 }
 
 // Which kernel serves a bf16 GEMM of this shape.
@@ -717,13 +759,13 @@ static hipError_t run_wide_any(const GemmArgs& g, int num_cus, hipStream_t st) {
   return run_wide<1>(g, num_cus, st);
 }
 
-template <int EPI, int AL, int BMAP, int BM, int BN>
+template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN>
 static hipError_t run_tiled(const GemmArgs& g, hipStream_t st) {
   const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN;
   if (EPI == E_ARGMAX && g.parts != ntiles) return hipErrorInvalidValue;
   const int grid = mtiles * ((ntiles + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_tiled_kernel<EPI, AL, BMAP, BM, BN>), dim3(grid), dim3(256), 0, st, g,
-                     mtiles, ntiles);
+  hipLaunchKernelGGL((gemm_tiled_kernel<EPI, AL, BMAP, BM, BN, WM, WN>), dim3(grid), dim3(64 * WM * WN),
+                     0, st, g, mtiles, ntiles);
   return hipGetLastError();
 }
 
@@ -737,8 +779,8 @@ static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
       if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
       return run_skinny<EPI, AL, BMAP, 4>(g, st);
     default:
-      if constexpr (EPI == E_ARGMAX) return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN>(g, st);
-      else return run_tiled<EPI, AL, BMAP, 128, 128>(g, st);
+      if constexpr (EPI == E_ARGMAX) return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN, 4, 2>(g, st);
+      else return run_tiled<EPI, AL, BMAP, 128, 128, 2, 2>(g, st);
   }
 }
 

@@ -41,6 +41,7 @@ struct GemmArgs {
   const void* hid; int d; int vocab;              //       k >= d -> hid[m*d + k - d]
   // B operand (weights, row-major [rows, K])
   const void* W0; const void* W1; const void* W2;
+  const void* Wp;  // optional fragment-order copy of W0 (see launch_pack_frag16)
   int nq, nk;                                     // B_QKV: rows of Wq, Wk (Wv follows)
   // epilogue
   void* out; int ldo; const void* resid;          // E_STORE / E_RESID / E_SILU
@@ -54,6 +55,9 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,
                        hipStream_t st);
+// Copies a row-major bf16 weight [N, K] (N % 16 == 0, K % 32 == 0) into
+// fragment order: 1 KB block (tile t, k-step s), lane l's 16 B at 16 l.
+hipError_t launch_pack_frag16(const void* W, void* out, int N, int K, hipStream_t st);
 // Number of partial argmax keys per row the E_ARGMAX GEMM of this shape writes.
 int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus);
 // After an E_ARGMAX GEMM: max over each row's partial keys -> token (-1 for a

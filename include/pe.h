@@ -93,7 +93,10 @@ typedef struct pe_layer_weights {
 } pe_layer_weights;
 
 /* Drafter weights.  Device pointers, borrowed for the context's life;
- * `layers` is a host array of cfg.layers entries, copied by pe_create. */
+ * `layers` is a host array of cfg.layers entries, copied by pe_create.
+ * For PE_BF16, pe_create also makes a context-owned copy of lm_head in MFMA
+ * fragment order (V*d*2 bytes), read by the draft step at small batch: the
+ * weights must not change after pe_create. */
 typedef struct pe_weights {
   const void* embed;      /* [vocab, d] token embeddings; row mask_id is emb(mask) */
   const void* w_fc;       /* [d, 2d] fc over concat(emb, hidden), embedding first */
