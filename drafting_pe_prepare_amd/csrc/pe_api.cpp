@@ -69,6 +69,10 @@ struct pe_ctx {
   float* rope_inv = nullptr;
   double* rope_inv_d = nullptr;
   void* lm_packed = nullptr;  // fragment-order copy of the LM head (bf16)
+  // fragment-order copies of the small-batch GEMM weights (bf16): fc, then per
+  // layer qkv (RoPE-paired columns), o, gate/up (paired), down
+  void* fc_packed = nullptr;
+  std::vector<void*> layer_packed;  // 4 per layer
   int target_items = 1024;
   long long items_max = 0;
   // step graph
@@ -132,6 +136,9 @@ void free_ctx(pe_ctx* c) {
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
                   c->part_o, c->part_ml, c->rope_inv, c->rope_inv_d, c->lm_packed};
   for (void* p : bufs)
+    if (p) (void)hipFree(p);
+  if (c->fc_packed) (void)hipFree(c->fc_packed);
+  for (void* p : c->layer_packed)
     if (p) (void)hipFree(p);
   delete c;
 }
@@ -295,15 +302,33 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   if (k.dtype == PE_BF16) {
     // The LM head streams V*d*2 bytes per step; a copy in MFMA-fragment order lets
     // every wave load one contiguous 1 KB per k-step (full lines, non-temporal).
-    if ((s = alloc(&c->lm_packed, size_t(k.vocab) * k.d * 2, "packed LM head")) != PE_OK) {
+    pe::GemmArgs pg;
+    std::memset(&pg, 0, sizeof pg);
+    pg.hd = k.head_dim;
+    auto pack = [&](int bmap, const void* w0, const void* w1, const void* w2, int N, int K, int nq,
+                    int nk, void** dst, const char* what) -> pe_status {
+      pe_status st2 = alloc(dst, size_t(N) * K * 2, what);
+      if (st2 != PE_OK) return st2;
+      pg.W0 = w0; pg.W1 = w1; pg.W2 = w2; pg.N = N; pg.K = K; pg.nq = nq; pg.nk = nk;
+      hipError_t e2 = pe::launch_pack_frag16(bmap, pg, *dst, c->stream);
+      return e2 == hipSuccess ? PE_OK : hipfail(e2, what);
+    };
+    const int qd = k.n_q_heads * k.head_dim, kvd = k.n_kv_heads * k.head_dim;
+    s = pack(pe::B_PLAIN, w->lm_head, nullptr, nullptr, k.vocab, k.d, 0, 0, &c->lm_packed, "pack LM head");
+    if (s == PE_OK) s = pack(pe::B_PLAIN, w->w_fc, nullptr, nullptr, k.d, 2 * k.d, 0, 0, &c->fc_packed, "pack fc");
+    c->layer_packed.assign(size_t(4) * k.layers, nullptr);
+    for (int l = 0; l < k.layers && s == PE_OK; ++l) {
+      const pe_layer_weights& L = c->layers[l];
+      void** lp = &c->layer_packed[4 * l];
+      s = pack(pe::B_QKV, L.wq, L.wk, L.wv, qd + 2 * kvd, k.d, qd, kvd, &lp[0], "pack qkv");
+      if (s == PE_OK) s = pack(pe::B_PLAIN, L.wo, nullptr, nullptr, k.d, qd, 0, 0, &lp[1], "pack o");
+      if (s == PE_OK) s = pack(pe::B_GATEUP, L.w_gate, L.w_up, nullptr, 2 * k.mlp, k.d, 0, 0, &lp[2], "pack gate/up");
+      if (s == PE_OK) s = pack(pe::B_PLAIN, L.w_down, nullptr, nullptr, k.d, k.mlp, 0, 0, &lp[3], "pack down");
+    }
+    if (s == PE_OK && (e = hipStreamSynchronize(c->stream)) != hipSuccess) s = hipfail(e, "pack sync");
+    if (s != PE_OK) {
       free_ctx(c);
       return s;
-    }
-    e = pe::launch_pack_frag16(w->lm_head, c->lm_packed, k.vocab, k.d, c->stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
-    if (e != hipSuccess) {
-      free_ctx(c);
-      return hipfail(e, "pack LM head");
     }
   }
   *out = c;
@@ -378,6 +403,10 @@ pe_status pe_gather_hidden(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
   return PE_OK;
 }
 
+static const void* packed(const pe_ctx* c, int layer, int which) {
+  return c->layer_packed.empty() ? nullptr : c->layer_packed[4 * layer + which];
+}
+
 pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* draft_hidden,
                            const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
                            void* const* k_cache, void* const* v_cache, int32_t* draft_tokens,
@@ -416,7 +445,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
     pe::GemmArgs g = g0;
     g.M = R; g.N = d; g.K = 2 * d;
     g.embed = ctx->w.embed; g.ids = batch->input_ids; g.hid = draft_hidden;
-    g.W0 = ctx->w.w_fc;
+    g.W0 = ctx->w.w_fc; g.Wp = ctx->fc_packed;
     g.out = ctx->x; g.ldo = d;
     Timed tm(ctx, PE_PH_FC);
     PE_HIP(pe::launch_gemm(dt, pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, ctx->num_cus, st), "fc");
@@ -432,6 +461,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       g.M = R; g.N = qd + 2 * kvd; g.K = d;
       g.A = ctx->u; g.lda = d;
       g.W0 = L.wq; g.W1 = L.wk; g.W2 = L.wv; g.nq = qd; g.nk = kvd;
+      g.Wp = packed(ctx, l, 0);
       g.positions = batch->positions; g.slots = batch->slot_mapping;
       g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
       g.rope_inv = ctx->rope_inv; g.rope_inv_d = ctx->rope_inv_d;
@@ -459,7 +489,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       pe::GemmArgs g = g0;
       g.M = R; g.N = d; g.K = qd;
       g.A = ctx->attn; g.lda = qd;
-      g.W0 = L.wo;
+      g.W0 = L.wo; g.Wp = packed(ctx, l, 1);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       Timed tm(ctx, PE_PH_O);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, ctx->num_cus, st), "o proj");
@@ -472,7 +502,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       pe::GemmArgs g = g0;
       g.M = R; g.N = 2 * k.mlp; g.K = d;
       g.A = ctx->u; g.lda = d;
-      g.W0 = L.w_gate; g.W1 = L.w_up;
+      g.W0 = L.w_gate; g.W1 = L.w_up; g.Wp = packed(ctx, l, 2);
       g.out = ctx->mlp; g.ldo = k.mlp;
       Timed tm(ctx, PE_PH_GATEUP);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, ctx->num_cus, st), "gate/up");
@@ -481,7 +511,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       pe::GemmArgs g = g0;
       g.M = R; g.N = d; g.K = k.mlp;
       g.A = ctx->mlp; g.lda = k.mlp;
-      g.W0 = L.w_down;
+      g.W0 = L.w_down; g.Wp = packed(ctx, l, 3);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       Timed tm(ctx, PE_PH_DOWN);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, ctx->num_cus, st), "down");

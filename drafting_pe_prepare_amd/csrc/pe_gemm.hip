@@ -236,13 +236,18 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
   const int ksteps = g.K >> 5;
   const int ks0 = (ksteps * w) / nw, ks1 = (ksteps * (w + 1)) / nw;
 
+  // weight fragment of (tile t, k-step ks) for this lane: from the
+  // fragment-order copy (one contiguous 1 KB per wave load) when there is one
   const uint16_t* wp[NTW];
+  long long wstep;  // elements between consecutive k-steps
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     int n = n0 + t * 16 + col;
     n = n < g.N ? n : g.N - 1;
-    wp[t] = weight_row<uint16_t, BMAP>(g, n) + kg * 8;
+    if (g.Wp) wp[t] = (const uint16_t*)g.Wp + (long long)(n0 / 16 + t) * ksteps * 512 + l * 8;
+    else wp[t] = weight_row<uint16_t, BMAP>(g, n) + kg * 8;
   }
+  wstep = g.Wp ? 512 : 32;
   ARow<uint16_t, AL> ar[MT];
   bool av[MT];
 #pragma unroll
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
       if (u < n) {
         const int k = (ks + u) * 32;
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) b[u][t] = ld16(wp[t] + k);  // plain: stays cache-resident
+        for (int t = 0; t < NTW; ++t) b[u][t] = ld16(wp[t] + (ks + u) * wstep);  // plain: stays cache-resident
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? ld16(ar[mt].at(k + kg * 8, g.d)) : zero;
       }
@@ -670,27 +675,31 @@ static hipError_t set_lds(F* fn, size_t bytes) {
 // holds, for lane l, W[16t + l%16][32s + 8(l/16) .. +8] at bytes 16 l.  A wave
 // that streams tile t then reads one contiguous 1 KB per MFMA k-step.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void pack_frag16_kernel(const uint4* __restrict__ W,
-                                                          uint4* __restrict__ out, int N, int K) {
-  const int ks = K >> 5, kc = K >> 3;  // k-steps, 16 B chunks per row
-  const long long total = (long long)(N >> 4) * ks * 64;
+template <int BMAP>
+__global__ __launch_bounds__(256) void pack_frag16_kernel(GemmArgs g, uint4* __restrict__ out) {
+  const int ks = g.K >> 5;
+  const long long total = (long long)(g.N >> 4) * ks * 64;
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
        i += (long long)gridDim.x * blockDim.x) {
     const int l = int(i & 63);
     const long long ts = i >> 6;
     const int s = int(ts % ks);
-    const long long t = ts / ks;
-    const long long row = t * 16 + (l & 15);
-    out[i] = W[row * kc + s * 4 + (l >> 4)];
+    const int t = int(ts / ks);
+    const uint16_t* row = weight_row<uint16_t, BMAP>(g, t * 16 + (l & 15));
+    out[i] = ld16(row + s * 32 + (l >> 4) * 8);
   }
 }
 
-hipError_t launch_pack_frag16(const void* W, void* out, int N, int K, hipStream_t st) {
-  const long long total = (long long)(N / 16) * (K / 32) * 64;
+hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_t st) {
+  const long long total = (long long)(g.N / 16) * (g.K / 32) * 64;
   long long blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(pack_frag16_kernel, dim3(unsigned(blocks)), dim3(256), 0, st,
-                     (const uint4*)W, (uint4*)out, N, K);
+  if (bmap == B_QKV)
+    hipLaunchKernelGGL(pack_frag16_kernel<B_QKV>, dim3(unsigned(blocks)), dim3(256), 0, st, g, (uint4*)out);
+  else if (bmap == B_GATEUP)
+    hipLaunchKernelGGL(pack_frag16_kernel<B_GATEUP>, dim3(unsigned(blocks)), dim3(256), 0, st, g, (uint4*)out);
+  else
+    hipLaunchKernelGGL(pack_frag16_kernel<B_PLAIN>, dim3(unsigned(blocks)), dim3(256), 0, st, g, (uint4*)out);
   return hipGetLastError();
 }
 

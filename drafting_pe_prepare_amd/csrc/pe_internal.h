@@ -55,9 +55,11 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,
                        hipStream_t st);
-// Copies a row-major bf16 weight [N, K] (N % 16 == 0, K % 32 == 0) into
-// fragment order: 1 KB block (tile t, k-step s), lane l's 16 B at 16 l.
-hipError_t launch_pack_frag16(const void* W, void* out, int N, int K, hipStream_t st);
+// Copies the logical bf16 weight of a GEMM (W0/W1/W2 through the bmap row
+// mapping; N % 16 == 0, K % 32 == 0) into fragment order: 1 KB block (16-row
+// tile t, k-step s) holds lane l's 16 B at byte 16 l, i.e.
+// W[16t + l%16][32s + 8(l/16) .. +8].
+hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_t st);
 // Number of partial argmax keys per row the E_ARGMAX GEMM of this shape writes.
 int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus);
 // After an E_ARGMAX GEMM: max over each row's partial keys -> token (-1 for a
