@@ -39,7 +39,22 @@ def parse():
     p.add_argument("--no-c64", action="store_true", help="skip the c=64 measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run three plain 1 GiB device-to-device copies (the reference "
+                        "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    x = torch.empty(2 ** 29, dtype=torch.bfloat16, device="cuda")
+    x.fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 2 ** 30, "copies": 3}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -79,6 +94,22 @@ def step_work(w, inp):
         att += sum(q + 1 for q in pos)
     flops += w.layers * 4 * w.head_dim * w.n_q_heads * att
     return {"bytes": bytes_, "flops": flops, "weight_bytes": sum(wb.values())}
+
+
+def measured_traffic(workload):
+    """HBM bytes per LM-head launch from the committed rocprofv3 counter runs
+    (profiles/traffic.json: FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy
+    calibration), or None when the GEMM source changed since they were taken."""
+    import hashlib
+    try:
+        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        src = open(os.path.join(ROOT, "drafting_pe_prepare_amd", "csrc", "pe_gemm.hip"), "rb").read()
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest() != t.get("pe_gemm_sha256") or workload not in t:
+        return None
+    e = t[workload]
+    return e["fetch_bytes"] + e["write_bytes"]
 
 
 # ---------------------------------------------------------------------------
@@ -167,7 +198,7 @@ def measure(w, steps, warmup, prm=None, dev=None, label=""):
                 "achieved": lm_flops / (lm_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name)
     roof["avg_launch_us"] = lm_us
     roof["algorithmic_per_launch"] = lm_bytes if roof["bound"] == "hbm" else lm_flops
     step_s = ms_step * 1e-3
@@ -230,6 +261,9 @@ def cpu_baseline(w, prm, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by request across GPUs with no exchange; see DESIGN.md)",
