@@ -22,10 +22,11 @@ PE_F32, PE_BF16 = 0, 1
 DEVERR_ACCEPTED, DEVERR_TOKEN, DEVERR_BLOCK, DEVERR_LAYOUT = 1, 2, 4, 8
 
 EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_hidden",
-           "pe_draft_forward", "pe_verify", "pe_step_graph", "pe_get_device_error",
+           "pe_draft_forward", "pe_ar_draft", "pe_verify", "pe_step_graph", "pe_get_device_error",
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
-          "verify", "argmax")
+          "verify", "argmax", "ar")
+STEP_PARALLEL, STEP_AUTOREGRESSIVE = 0, 1
 
 vp, i32 = ctypes.c_void_p, ctypes.c_int32
 
@@ -60,7 +61,8 @@ class PeStepArgs(ctypes.Structure):
                 ("num_kv_blocks", i32), ("batch", PeBatch), ("target_hidden", vp),
                 ("h_shared", vp), ("draft_hidden", vp), ("k_cache", ctypes.POINTER(vp)),
                 ("v_cache", ctypes.POINTER(vp)), ("draft_tokens", vp), ("logits", vp),
-                ("target_tokens", vp), ("accepted_out", vp), ("bonus_out", vp)]
+                ("target_tokens", vp), ("accepted_out", vp), ("bonus_out", vp),
+                ("mode", i32)]
 
 
 class PeError(RuntimeError):
@@ -90,11 +92,14 @@ def load(path: str = LIB_PATH):
     lib.pe_prepare.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, P(PeBatch)]
     lib.pe_gather_hidden.argtypes = [vp, i32, P(PeBatch), vp, vp, vp]
     lib.pe_draft_forward.argtypes = [vp, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp), vp, vp]
+    lib.pe_ar_draft.argtypes = [vp, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp), vp, vp]
     lib.pe_verify.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.pe_step_graph.argtypes = [vp, i32, P(PeStepArgs)]
     lib.pe_get_device_error.argtypes = [vp, P(ctypes.c_uint32), P(i32)]
     lib.pe_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.pe_profile_read.argtypes = [vp, P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int]
+    lib.pe_last_error.argtypes = []
+    lib.pe_status_string.argtypes = [ctypes.c_int]
     lib.pe_last_error.restype = ctypes.c_char_p
     lib.pe_status_string.restype = ctypes.c_char_p
     for n in EXPORTS[:-2]:
@@ -211,6 +216,14 @@ def pe_draft_forward(ctx: Context, B, batch: Batch, draft_hidden, block_table, n
                                  kc, vc, _ptr(draft_tokens), _ptr(logits)))
 
 
+def pe_ar_draft(ctx: Context, B, batch: Batch, draft_hidden, block_table, num_kv_blocks,
+                k_caches, v_caches, draft_tokens, logits=None):
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    _check(_lib.pe_ar_draft(ctx.h, B, ctypes.byref(batch.c), _ptr(draft_hidden),
+                            _ptr(block_table), block_table.shape[1], num_kv_blocks,
+                            kc, vc, _ptr(draft_tokens), _ptr(logits)))
+
+
 def pe_verify(ctx: Context, B, draft_tokens, target_tokens, num_accepted, bonus_tokens):
     _check(_lib.pe_verify(ctx.h, B, _ptr(draft_tokens), _ptr(target_tokens),
                           _ptr(num_accepted), _ptr(bonus_tokens)))
@@ -219,14 +232,14 @@ def pe_verify(ctx: Context, B, draft_tokens, target_tokens, num_accepted, bonus_
 def make_step_args(verify_tokens, verify_positions, num_accepted, bonus_tokens, block_table,
                    num_kv_blocks, batch: Batch, target_hidden, h_shared, draft_hidden,
                    k_caches, v_caches, draft_tokens, target_tokens, accepted_out, bonus_out,
-                   logits=None) -> PeStepArgs:
+                   logits=None, mode=STEP_PARALLEL) -> PeStepArgs:
     kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
     a = PeStepArgs(_ptr(verify_tokens), _ptr(verify_positions), _ptr(num_accepted),
                    _ptr(bonus_tokens), _ptr(block_table), block_table.shape[1], num_kv_blocks,
                    batch.c, _ptr(target_hidden), _ptr(h_shared), _ptr(draft_hidden),
                    ctypes.cast(kc, ctypes.POINTER(vp)), ctypes.cast(vc, ctypes.POINTER(vp)),
                    _ptr(draft_tokens), _ptr(logits), _ptr(target_tokens), _ptr(accepted_out),
-                   _ptr(bonus_out))
+                   _ptr(bonus_out), mode)
     a._keep = (kc, vc)
     return a
 

@@ -73,6 +73,11 @@ struct pe_ctx {
   // layer qkv (RoPE-paired columns), o, gate/up (paired), down
   void* fc_packed = nullptr;
   std::vector<void*> layer_packed;  // 4 per layer
+  // autoregressive comparison: the batch of one sequential pass (B*(K+1) slots)
+  int32_t *ar_ids = nullptr, *ar_pos = nullptr, *ar_rows = nullptr, *ar_seq = nullptr;
+  uint8_t* ar_rej = nullptr;
+  int64_t* ar_slots = nullptr;
+  void* ar_hidden = nullptr;
   int target_items = 1024;
   long long items_max = 0;
   // step graph
@@ -138,6 +143,9 @@ void free_ctx(pe_ctx* c) {
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   if (c->fc_packed) (void)hipFree(c->fc_packed);
+  void* ar[] = {c->ar_ids, c->ar_pos, c->ar_rows, c->ar_seq, c->ar_rej, c->ar_slots, c->ar_hidden};
+  for (void* p : ar)
+    if (p) (void)hipFree(p);
   for (void* p : c->layer_packed)
     if (p) (void)hipFree(p);
   delete c;
@@ -257,11 +265,12 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   const size_t qd = size_t(k.n_q_heads) * k.head_dim;
   const size_t QN = size_t(2 * k.K) * (k.n_q_heads / k.n_kv_heads);
   c->items_max = pe::attn_max_items(k.max_num_seqs, k.n_kv_heads, c->target_items);
-  // partial argmax keys: the largest parts count any B <= max_num_seqs can need
+  // partial argmax keys: the most any LM-head launch can need (B*K draft rows
+  // of a parallel pass, B of a sequential one)
   size_t key_slots = 0;
-  for (int b = 1; b <= k.max_num_seqs; ++b)
-    key_slots = std::max(key_slots, size_t(b) * k.K *
-                                        pe::gemm_argmax_parts(k.dtype, b * k.K, k.vocab, k.d, c->num_cus));
+  for (int m = 1; m <= k.max_num_seqs * k.K; ++m)
+    key_slots = std::max(key_slots, size_t(m) * pe::gemm_argmax_parts(k.dtype, m, k.vocab, k.d, c->num_cus));
+  const size_t R1 = size_t(k.max_num_seqs) * (k.K + 1);
   struct { void** p; size_t bytes; const char* what; } plan[] = {
       {&c->x, R * k.d * c->esz, "x"},
       {&c->u, R * k.d * c->esz, "u"},
@@ -273,6 +282,13 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {reinterpret_cast<void**>(&c->err), 16, "err"},
       {reinterpret_cast<void**>(&c->rope_inv), size_t(k.head_dim / 2) * 4, "rope"},
       {reinterpret_cast<void**>(&c->rope_inv_d), size_t(k.head_dim / 2) * 8, "rope_d"},
+      {reinterpret_cast<void**>(&c->ar_ids), R1 * 4, "ar ids"},
+      {reinterpret_cast<void**>(&c->ar_pos), R1 * 4, "ar positions"},
+      {reinterpret_cast<void**>(&c->ar_rows), size_t(k.max_num_seqs) * 4, "ar rows"},
+      {reinterpret_cast<void**>(&c->ar_seq), size_t(k.max_num_seqs) * 4, "ar seq_lens"},
+      {reinterpret_cast<void**>(&c->ar_rej), R1, "ar rejected"},
+      {reinterpret_cast<void**>(&c->ar_slots), R1 * 8, "ar slots"},
+      {&c->ar_hidden, R1 * k.d * c->esz, "ar hidden"},
   };
   for (auto& p : plan) {
     if ((s = alloc(p.p, p.bytes, p.what)) != PE_OK) { free_ctx(c); return s; }
@@ -407,25 +423,25 @@ static const void* packed(const pe_ctx* c, int layer, int which) {
   return c->layer_packed.empty() ? nullptr : c->layer_packed[4 * layer + which];
 }
 
-pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* draft_hidden,
-                           const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
-                           void* const* k_cache, void* const* v_cache, int32_t* draft_tokens,
-                           float* logits) {
-  pe_status s = check_B(ctx, B);
-  if (s != PE_OK) return s;
-  if ((s = check_batch(batch)) != PE_OK) return s;
-  if (B == 0) return PE_OK;
-  const pe_config& k = ctx->cfg;
-  if (!draft_hidden || !aligned(draft_hidden, 16)) return fail(PE_ERR_INVALID_ARG, "draft_hidden");
-  if (!block_table || max_blocks < 1 || num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "block table");
-  if (!k_cache || !v_cache) return fail(PE_ERR_INVALID_ARG, "k_cache/v_cache arrays are NULL");
-  for (int l = 0; l < k.layers; ++l)
-    if (!k_cache[l] || !v_cache[l] || !aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
-      return fail(PE_ERR_INVALID_ARG, "KV cache of layer %d NULL or misaligned", l);
-  if (!draft_tokens) return fail(PE_ERR_INVALID_ARG, "draft_tokens is NULL");
-  if (logits && !aligned(logits, 4)) return fail(PE_ERR_INVALID_ARG, "logits misaligned");
+// One drafter pass over B requests of S slots each: fc -> decoder layers ->
+// final norm on the Kd draft rows per request -> LM head + argmax.
+struct Pass {
+  int B, S, Kd;
+  const int32_t *ids, *pos, *draft_rows, *seq_lens;
+  const uint8_t* rej;
+  const int64_t* slots;
+  const void* hidden;  // [B*S, d]
+  int32_t* tokens;     // draft row i -> tokens[i * tstride]
+  int tstride;
+  float* logits;       // draft row i -> logits[i * ldl ...], or NULL
+  int ldl;
+};
 
-  const int S = 2 * k.K, R = B * S, D = B * k.K, d = k.d;
+static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_table,
+                              int32_t max_blocks, int32_t num_kv_blocks, void* const* k_cache,
+                              void* const* v_cache) {
+  const pe_config& k = ctx->cfg;
+  const int B = P.B, S = P.S, R = B * S, D = B * P.Kd, d = k.d;
   const int qd = k.n_q_heads * k.head_dim, kvd = k.n_kv_heads * k.head_dim;
   const long long num_slots = (long long)num_kv_blocks * k.block_size;
   hipStream_t st = ctx->stream;
@@ -444,7 +460,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
   {
     pe::GemmArgs g = g0;
     g.M = R; g.N = d; g.K = 2 * d;
-    g.embed = ctx->w.embed; g.ids = batch->input_ids; g.hid = draft_hidden;
+    g.embed = ctx->w.embed; g.ids = P.ids; g.hid = P.hidden;
     g.W0 = ctx->w.w_fc; g.Wp = ctx->fc_packed;
     g.out = ctx->x; g.ldo = d;
     Timed tm(ctx, PE_PH_FC);
@@ -462,7 +478,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       g.A = ctx->u; g.lda = d;
       g.W0 = L.wq; g.W1 = L.wk; g.W2 = L.wv; g.nq = qd; g.nk = kvd;
       g.Wp = packed(ctx, l, 0);
-      g.positions = batch->positions; g.slots = batch->slot_mapping;
+      g.positions = P.pos; g.slots = P.slots;
       g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
       g.rope_inv = ctx->rope_inv; g.rope_inv_d = ctx->rope_inv_d;
       Timed tm(ctx, PE_PH_QKV);
@@ -475,7 +491,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
       a.block_size = k.block_size; a.max_blocks = max_blocks; a.num_slots = num_slots;
       a.scale = 1.0f / std::sqrt(float(k.head_dim));
       a.q = ctx->q; a.kcache = k_cache[l]; a.vcache = v_cache[l];
-      a.positions = batch->positions; a.rej = batch->is_rejected; a.seq_lens = batch->seq_lens;
+      a.positions = P.pos; a.rej = P.rej; a.seq_lens = P.seq_lens;
       a.bt = block_table; a.out = ctx->attn;
       a.part_o = ctx->part_o; a.part_ml = ctx->part_ml;
       a.target_items = ctx->target_items;
@@ -519,7 +535,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
   }
   {
     Timed tm(ctx, PE_PH_NORM);
-    PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, ctx->w.final_norm, ctx->z, batch->draft_rows, R,
+    PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, ctx->w.final_norm, ctx->z, P.draft_rows, R,
                               k.rms_eps, st),
            "final norm");
   }
@@ -529,16 +545,99 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
     g.A = ctx->z; g.lda = d;
     g.W0 = ctx->w.lm_head;
     g.Wp = ctx->lm_packed;
-    g.keys = ctx->keys; g.tokens = draft_tokens; g.logits = logits;
+    g.keys = ctx->keys; g.logits = P.logits; g.ldl = P.ldl;
     g.parts = pe::gemm_argmax_parts(dt, D, k.vocab, d, ctx->num_cus);
-    g.seq_lens = batch->seq_lens; g.Kd = k.K;
+    g.seq_lens = P.seq_lens; g.Kd = P.Kd;
     {
       Timed tm(ctx, PE_PH_LMHEAD);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
     }
     Timed tm(ctx, PE_PH_ARGMAX);
-    PE_HIP(pe::launch_argmax_tokens(D, k.K, g.parts, ctx->keys, draft_tokens, batch->seq_lens, st),
+    PE_HIP(pe::launch_argmax_tokens(D, P.Kd, g.parts, ctx->keys, P.tokens, P.tstride, P.seq_lens, st),
            "argmax");
+  }
+  return PE_OK;
+}
+
+
+static pe_status check_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* draft_hidden,
+                               const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                               void* const* k_cache, void* const* v_cache, int32_t* draft_tokens,
+                               float* logits) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if ((s = check_batch(batch)) != PE_OK) return s;
+  if (B == 0) return PE_OK;
+  const pe_config& k = ctx->cfg;
+  if (!draft_hidden || !aligned(draft_hidden, 16)) return fail(PE_ERR_INVALID_ARG, "draft_hidden");
+  if (!block_table || max_blocks < 1 || num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "block table");
+  if (!k_cache || !v_cache) return fail(PE_ERR_INVALID_ARG, "k_cache/v_cache arrays are NULL");
+  for (int l = 0; l < k.layers; ++l)
+    if (!k_cache[l] || !v_cache[l] || !aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
+      return fail(PE_ERR_INVALID_ARG, "KV cache of layer %d NULL or misaligned", l);
+  if (!draft_tokens) return fail(PE_ERR_INVALID_ARG, "draft_tokens is NULL");
+  if (logits && !aligned(logits, 4)) return fail(PE_ERR_INVALID_ARG, "logits misaligned");
+  return PE_OK;
+}
+
+pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* draft_hidden,
+                           const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                           void* const* k_cache, void* const* v_cache, int32_t* draft_tokens,
+                           float* logits) {
+  pe_status s = check_forward(ctx, B, batch, draft_hidden, block_table, max_blocks, num_kv_blocks,
+                              k_cache, v_cache, draft_tokens, logits);
+  if (s != PE_OK || B == 0) return s;
+  const int K = ctx->cfg.K;
+  Pass P;
+  P.B = B; P.S = 2 * K; P.Kd = K;
+  P.ids = batch->input_ids; P.pos = batch->positions; P.draft_rows = batch->draft_rows;
+  P.seq_lens = batch->seq_lens; P.rej = batch->is_rejected; P.slots = batch->slot_mapping;
+  P.hidden = draft_hidden;
+  P.tokens = draft_tokens; P.tstride = 1;
+  P.logits = logits; P.ldl = ctx->cfg.vocab;
+  return forward_pass(ctx, P, block_table, max_blocks, num_kv_blocks, k_cache, v_cache);
+}
+
+pe_status pe_ar_draft(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* draft_hidden,
+                      const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                      void* const* k_cache, void* const* v_cache, int32_t* draft_tokens,
+                      float* logits) {
+  pe_status s = check_forward(ctx, B, batch, draft_hidden, block_table, max_blocks, num_kv_blocks,
+                              k_cache, v_cache, draft_tokens, logits);
+  if (s != PE_OK || B == 0) return s;
+  const pe_config& k = ctx->cfg;
+  const int K = k.K;
+  pe::ArArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.B = B; a.K = K; a.row_bytes = int(k.d * ctx->esz); a.block_size = k.block_size;
+  a.max_blocks = max_blocks; a.num_kv_blocks = num_kv_blocks;
+  a.ids = batch->input_ids; a.pos = batch->positions; a.draft_rows = batch->draft_rows;
+  a.seq_lens = batch->seq_lens; a.rej = batch->is_rejected; a.slots = batch->slot_mapping;
+  a.bt = block_table; a.tokens = draft_tokens;
+  a.p_ids = ctx->ar_ids; a.p_pos = ctx->ar_pos; a.p_rows = ctx->ar_rows; a.p_seq = ctx->ar_seq;
+  a.p_rej = ctx->ar_rej; a.p_slots = ctx->ar_slots; a.p_hidden = ctx->ar_hidden;
+  Pass P;
+  P.B = B; P.Kd = 1;
+  P.ids = ctx->ar_ids; P.pos = ctx->ar_pos; P.draft_rows = ctx->ar_rows; P.seq_lens = ctx->ar_seq;
+  P.rej = ctx->ar_rej; P.slots = ctx->ar_slots; P.hidden = ctx->ar_hidden;
+  P.tstride = K; P.ldl = K * k.vocab;
+  for (int step = 0; step < K; ++step) {
+    {
+      Timed tm(ctx, PE_PH_AR);
+      if (step == 0) {
+        a.hidden = draft_hidden;
+        PE_HIP(pe::launch_ar_first(a, ctx->stream), "ar first pass batch");
+      } else {
+        a.hidden = ctx->x;  // residual stream after the last layer of the previous pass
+        a.k = step;
+        PE_HIP(pe::launch_ar_next(a, ctx->stream), "ar pass batch");
+      }
+    }
+    P.S = step == 0 ? K + 1 : 1;
+    P.tokens = draft_tokens + step;
+    P.logits = logits ? logits + (size_t)step * k.vocab : nullptr;
+    s = forward_pass(ctx, P, block_table, max_blocks, num_kv_blocks, k_cache, v_cache);
+    if (s != PE_OK) return s;
   }
   return PE_OK;
 }
@@ -563,8 +662,9 @@ static pe_status run_step(pe_ctx* ctx, int32_t B, const pe_step_args* a) {
   if (s != PE_OK) return s;
   s = pe_gather_hidden(ctx, B, &a->batch, a->target_hidden, a->h_shared, a->draft_hidden);
   if (s != PE_OK) return s;
-  s = pe_draft_forward(ctx, B, &a->batch, a->draft_hidden, a->block_table, a->max_blocks,
-                       a->num_kv_blocks, a->k_cache, a->v_cache, a->draft_tokens, a->logits);
+  auto fwd = a->mode == PE_STEP_AUTOREGRESSIVE ? pe_ar_draft : pe_draft_forward;
+  s = fwd(ctx, B, &a->batch, a->draft_hidden, a->block_table, a->max_blocks, a->num_kv_blocks,
+          a->k_cache, a->v_cache, a->draft_tokens, a->logits);
   if (s != PE_OK) return s;
   return pe_verify(ctx, B, a->draft_tokens, a->target_tokens, a->accepted_out, a->bonus_out);
 }
@@ -573,6 +673,8 @@ pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args) {
   pe_status s = check_B(ctx, B);
   if (s != PE_OK) return s;
   if (!args || !args->k_cache || !args->v_cache) return fail(PE_ERR_INVALID_ARG, "step args");
+  if (args->mode != PE_STEP_PARALLEL && args->mode != PE_STEP_AUTOREGRESSIVE)
+    return fail(PE_ERR_INVALID_ARG, "step mode %d", args->mode);
   const int nl = ctx->cfg.layers;
   std::vector<void*> kv(2 * nl);
   for (int l = 0; l < nl; ++l) {

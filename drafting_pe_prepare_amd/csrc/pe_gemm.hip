@@ -180,7 +180,7 @@ __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, i
   if (g.logits)
     for (int e = threadIdx.x; e < mrows * ncols; e += blockDim.x) {
       const int i = e / ncols, c = e - i * ncols;
-      g.logits[(long long)(m0 + i) * g.N + n0 + c] = tile[i * ldt + c];
+      g.logits[(long long)(m0 + i) * g.ldl + n0 + c] = tile[i * ldt + c];
     }
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
   for (int i = w; i < mrows; i += nw) {
@@ -202,7 +202,7 @@ __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, i
 // workgroup per draft row reduces that row's `parts` keys.
 __global__ __launch_bounds__(256) void argmax_tokens_kernel(int M, int Kd, int parts,
                                                             const uint64_t* __restrict__ keys,
-                                                            int32_t* __restrict__ tokens,
+                                                            int32_t* __restrict__ tokens, int tstride,
                                                             const int32_t* __restrict__ seq_lens) {
   __shared__ uint64_t red[4];
   const int row = blockIdx.x;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void argmax_tokens_kernel(int M, int Kd, int p
     best = red[0] > best ? red[0] : best;
     int tok = argmax_key_index(best);
     if (seq_lens && seq_lens[row / Kd] == 0) tok = -1;
-    tokens[row] = tok;
+    tokens[(long long)row * tstride] = tok;
   }
 }
 
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i) {
       const int row = kg * 4 + i;
       if (row < g.M) {
-        if (g.logits) g.logits[(long long)row * g.N + n] = acc[i];
+        if (g.logits) g.logits[(long long)row * g.ldl + n] = acc[i];
         const uint64_t key = argmax_key(acc[i], n);
         best[i] = key > best[i] ? key : best[i];
       }
@@ -592,7 +592,7 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
         for (int jj = 0; jj < TJ; ++jj) {
           const int n = n0 + wn * (BN / WN) + jj * 16 + col;
           if (n < g.N) {
-            if (g.logits && m0 + lrow < g.M) g.logits[(long long)(m0 + lrow) * g.N + n] = acc[i][jj][r];
+            if (g.logits && m0 + lrow < g.M) g.logits[(long long)(m0 + lrow) * g.ldl + n] = acc[i][jj][r];
             const uint64_t k = argmax_key(acc[i][jj][r], n);
             best = k > best ? k : best;
           }
@@ -807,10 +807,10 @@ static hipError_t run(int dtype, const GemmArgs& g, int num_cus, hipStream_t st)
 }
 
 hipError_t launch_argmax_tokens(int M, int Kd, int parts, const uint64_t* keys, int32_t* tokens,
-                                const int32_t* seq_lens, hipStream_t st) {
+                                int tstride, const int32_t* seq_lens, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   hipLaunchKernelGGL(argmax_tokens_kernel, dim3(M), dim3(256), 0, st, M, Kd, parts, keys, tokens,
-                     seq_lens);
+                     tstride, seq_lens);
   return hipGetLastError();
 }
 

@@ -23,6 +23,28 @@ hipError_t launch_gather(int rows, int nsrc, int row_bytes, const int32_t* hsrc,
 hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32_t* acc,
                          int32_t* bonus, hipStream_t st);
 
+// ---- autoregressive comparison --------------------------------------------
+// Pass batches of sequential drafting, built on the device from the parallel
+// batch (stride 2K) so that a captured graph replays them.
+struct ArArgs {
+  int B, K, row_bytes, block_size, max_blocks, num_kv_blocks;
+  // parallel batch
+  const int32_t *ids, *pos, *draft_rows, *seq_lens;
+  const uint8_t* rej;
+  const int64_t* slots;
+  const int32_t* bt;
+  const void* hidden;     // first pass: draft hidden [B*2K, d]; later: residual stream of the previous pass
+  const int32_t* tokens;  // [B, K] drafted so far; pass k reads column k-1
+  int k;
+  // pass batch (workspace)
+  int32_t *p_ids, *p_pos, *p_rows, *p_seq;
+  uint8_t* p_rej;
+  int64_t* p_slots;
+  void* p_hidden;
+};
+hipError_t launch_ar_first(const ArArgs& a, hipStream_t st);
+hipError_t launch_ar_next(const ArArgs& a, hipStream_t st);
+
 // ---- normalisation --------------------------------------------------------
 // out[i] = x[row(i)] * rsqrt(mean(x^2) + eps) * gain; row(i) = rows_idx ? rows_idx[i] : i
 hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void* gain, void* out,
@@ -51,7 +73,8 @@ struct GemmArgs {
   const float* rope_inv;  // [hd/2] inverse frequencies (float)
   const double* rope_inv_d;  // [hd/2] the same in double (angle reduction)
   uint64_t* keys; int parts;                      // E_ARGMAX: keys[row * parts + part]
-  int32_t* tokens; float* logits; const int32_t* seq_lens; int Kd;
+  int32_t* tokens; float* logits; int ldl;         // logits[row * ldl + n]
+  const int32_t* seq_lens; int Kd;
 };
 hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,
                        hipStream_t st);
@@ -62,10 +85,10 @@ hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& 
 hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_t st);
 // Number of partial argmax keys per row the E_ARGMAX GEMM of this shape writes.
 int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus);
-// After an E_ARGMAX GEMM: max over each row's partial keys -> token (-1 for a
-// padded request).
+// After an E_ARGMAX GEMM: max over each row's partial keys -> tokens[row *
+// tstride] (-1 for a padded request, seq_lens[row / Kd] == 0).
 hipError_t launch_argmax_tokens(int M, int Kd, int parts, const uint64_t* keys, int32_t* tokens,
-                                const int32_t* seq_lens, hipStream_t st);
+                                int tstride, const int32_t* seq_lens, hipStream_t st);
 
 // ---- attention ------------------------------------------------------------
 struct AttnArgs {

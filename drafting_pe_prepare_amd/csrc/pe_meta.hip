@@ -163,4 +163,82 @@ hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Autoregressive comparison: the batches of EAGLE's sequential drafting passes
+// ("P-EAGLE: parallel speculative decoding in vLLM", Solving the
+// autoregressive drafting bottleneck: one drafter pass per draft token).
+// ---------------------------------------------------------------------------
+
+// First pass: the K+1 copied slots of every request, compacted to stride K+1,
+// with their hidden rows; the draft row is the NTP slot.  One 64-thread
+// workgroup per (request, copied slot).
+__global__ __launch_bounds__(64) void ar_first_kernel(ArArgs a) {
+  const int K = a.K, S = 2 * K, S1 = K + 1;
+  const int r = blockIdx.x / S1, j = blockIdx.x - r * S1;
+  const long long src = (long long)r * S + j, dst = blockIdx.x;
+  const int cpr = a.row_bytes / 16;
+  const uint4* h = (const uint4*)a.hidden + src * cpr;
+  uint4* o = (uint4*)a.p_hidden + dst * cpr;
+  for (int i = threadIdx.x; i < cpr; i += 64) o[i] = h[i];
+  if (threadIdx.x == 0) {
+    a.p_ids[dst] = a.ids[src];
+    a.p_pos[dst] = a.pos[src];
+    a.p_rej[dst] = a.rej[src];
+    a.p_slots[dst] = a.slots[src];
+    if (j == 0) {
+      int acc = a.draft_rows[(long long)r * K] - r * S;  // the NTP slot is copied slot a
+      acc = acc < 0 ? 0 : (acc > K ? K : acc);
+      a.p_rows[r] = r * S1 + acc;
+      const int L = a.seq_lens[r];  // p0 + a + K; the first pass sees p0 + a + 1
+      a.p_seq[r] = L > 0 ? L - (K - 1) : 0;
+    }
+  }
+}
+
+// Pass k (drafts t_{k+1}, k = 1..K-1): one slot per request holding t_k at the
+// next position, paired with the drafter's output hidden state of the previous
+// pass's draft row.  One 64-thread workgroup per request.
+__global__ __launch_bounds__(64) void ar_next_kernel(ArArgs a) {
+  const int r = blockIdx.x;
+  const int cpr = a.row_bytes / 16;
+  const int prev = a.p_rows[r];
+  const uint4* h = (const uint4*)a.hidden + (long long)prev * cpr;
+  uint4* o = (uint4*)a.p_hidden + (long long)r * cpr;
+  for (int i = threadIdx.x; i < cpr; i += 64) o[i] = h[i];
+  __syncthreads();  // every lane has read p_rows[r] before it is replaced
+  if (threadIdx.x == 0) {
+    const int L = a.p_seq[r];
+    const int tok = a.tokens[(long long)r * a.K + a.k - 1];
+    const int p = L;  // the previous pass saw positions [0, L)
+    const int blk = (L > 0 && p / a.block_size < a.max_blocks)
+                        ? a.bt[(long long)r * a.max_blocks + p / a.block_size] : -1;
+    if (L <= 0 || tok < 0 || blk < 0 || blk >= a.num_kv_blocks) {
+      a.p_ids[r] = 0;
+      a.p_pos[r] = 0;
+      a.p_rej[r] = 1;
+      a.p_slots[r] = -1;
+      a.p_seq[r] = 0;
+    } else {
+      a.p_ids[r] = tok;
+      a.p_pos[r] = p;
+      a.p_rej[r] = 0;
+      a.p_slots[r] = (long long)blk * a.block_size + p % a.block_size;
+      a.p_seq[r] = L + 1;
+    }
+    a.p_rows[r] = r;
+  }
+}
+
+hipError_t launch_ar_first(const ArArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ar_first_kernel, dim3(a.B * (a.K + 1)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ar_next(const ArArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ar_next_kernel, dim3(a.B), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace pe

@@ -7,6 +7,8 @@
  *   pe_draft_forward  one drafter pass over every slot, LM head + argmax -> t_1..t_K
  *   pe_verify         greedy verification -> accepted length and bonus token
  * pe_step_graph captures the four into one hipGraph and replays it.
+ * pe_ar_draft runs the same kernels as K sequential drafting passes, the
+ * autoregressive baseline, in place of pe_draft_forward.
  *
  * Sources (page titles as published):
  *   [P1] "P-EAGLE: parallel speculative decoding in vLLM" -- sections
@@ -174,12 +176,38 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch,
                            void* const* k_cache, void* const* v_cache,
                            int32_t* draft_tokens, float* logits);
 
+/* Autoregressive drafting with the same kernels, the sequential baseline
+ * the parallel pass replaces [P1, Solving the autoregressive drafting
+ * bottleneck: an EAGLE drafter runs one forward pass per draft token].
+ * Same arguments and outputs as pe_draft_forward; batch and draft_hidden come
+ * from pe_prepare and pe_gather_hidden.
+ *   pass 1: the K+1 copied slots of every request (rejected slots attend to
+ *     nothing and write no KV); t_1 is drafted at the NTP slot;
+ *   pass k = 2..K: one slot per request holding t_{k-1} at position
+ *     p0+a+k-1, paired with the drafter's own output hidden state (the
+ *     residual stream after the last layer) of the previous pass's draft row;
+ *     it drafts t_k.
+ * Feeding back the drafter's hidden state is EAGLE's drafting loop; the pages
+ * describe only its cost, so this is a reading of it.  KV is written at
+ * positions p0..p0+a+K-1, the positions the parallel pass writes (with
+ * different values at the MASK positions).  The MASK slots of batch and rows
+ * K+1..2K-1 of draft_hidden are not read.  logits, when not NULL, is
+ * [B*K, vocab] as for pe_draft_forward. */
+pe_status pe_ar_draft(pe_ctx* ctx, int32_t B, const pe_batch* batch,
+                      const void* draft_hidden,
+                      const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                      void* const* k_cache, void* const* v_cache,
+                      int32_t* draft_tokens, float* logits);
+
 /* Greedy verification [P1, Benchmarks, Acceptance length; P3, Integration
  * and numbers]: num_accepted[r] = first j in 0..K-1 with draft_tokens[r][j]
  * != target_tokens[r][j], or K; bonus_tokens[r] = target_tokens[r][that j].
  * draft_tokens [B, K], target_tokens [B, K+1] int32 in; outputs [B] int32. */
 pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens,
                     const int32_t* target_tokens, int32_t* num_accepted, int32_t* bonus_tokens);
+
+/* Drafting pass of a step graph: pe_draft_forward or pe_ar_draft. */
+typedef enum pe_step_mode { PE_STEP_PARALLEL = 0, PE_STEP_AUTOREGRESSIVE = 1 } pe_step_mode;
 
 /* All buffers of one step, for pe_step_graph. */
 typedef struct pe_step_args {
@@ -201,9 +229,11 @@ typedef struct pe_step_args {
   const int32_t* target_tokens;
   int32_t* accepted_out;     /* pe_verify outputs; may alias nothing above */
   int32_t* bonus_out;
+  int32_t mode;              /* pe_step_mode */
 } pe_step_args;
 
-/* Captures prepare -> gather -> forward -> verify for (B, *args) into a
+/* Captures prepare -> gather -> forward (args->mode picks the parallel pass
+ * or the sequential passes) -> verify for (B, *args) into a
  * hipGraph on the first call and replays it on later calls with the same B
  * and the same pointers (values inside the buffers may change between
  * replays: a, p0, tokens and block tables are read on the device).  A call
@@ -226,7 +256,9 @@ pe_status pe_get_device_error(pe_ctx* ctx, uint32_t* kinds, int32_t* first_reque
  * and the number of launches since the last reset. */
 typedef enum pe_phase {
   PE_PH_PREPARE = 0, PE_PH_GATHER, PE_PH_FC, PE_PH_NORM, PE_PH_QKV, PE_PH_ATTN,
-  PE_PH_O, PE_PH_GATEUP, PE_PH_DOWN, PE_PH_LMHEAD, PE_PH_VERIFY, PE_PH_ARGMAX, PE_PH_COUNT
+  PE_PH_O, PE_PH_GATEUP, PE_PH_DOWN, PE_PH_LMHEAD, PE_PH_VERIFY, PE_PH_ARGMAX,
+  PE_PH_AR, /* batch of a sequential pass (pe_ar_draft) */
+  PE_PH_COUNT
 } pe_phase;
 pe_status pe_profile_enable(pe_ctx* ctx, int on);
 pe_status pe_profile_read(pe_ctx* ctx, double* ms /* [PE_PH_COUNT] */,

@@ -25,5 +25,5 @@ unpinned (no trained weights exist here).
 from .pe_oracle import (  # noqa: F401
     PAD_TOKEN, PADDING_SLOT_ID, ERR_ACCEPTED, ERR_TOKEN, ERR_BLOCK, ERR_LAYOUT,
     round_bf16, widen, prepare, gather_hidden, rmsnorm, rope, silu,
-    attend, draft_forward, verify, eagle_step, slot_of,
+    attend, draft_forward, verify, eagle_step, ar_draft, slot_of,
 )

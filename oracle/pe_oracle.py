@@ -432,12 +432,14 @@ def verify(draft_tokens, target_tokens):
 # layout, for the K=1 and causality pins
 # ----------------------------------------------------------------------------
 def eagle_step(params, cfg, prefix_k, prefix_v, tokens, hiddens, start_pos,
-               precision="bf16"):
+               precision="bf16", return_hidden=False):
     """One request, token by token: input i pairs emb(tokens[i]) with
     hiddens[i] at position start_pos+i, appended after a contiguous cached
     prefix (prefix_k/prefix_v per layer: [p0, Hkv, hd] fp64, p0 = start_pos).
     Each token runs every layer, appends its K/V and attends to everything
-    cached so far.  Returns the logits of every input token [n, V].
+    cached so far.  Returns the logits of every input token [n, V] (and, with
+    return_hidden, the residual stream after the last layer [n, d] and the
+    per-layer caches grown by the new tokens).
 
     This is EAGLE drafting as "P-EAGLE: parallel speculative decoding in vLLM"
     describes it before the parallel change (Solving the autoregressive
@@ -448,7 +450,7 @@ def eagle_step(params, cfg, prefix_k, prefix_v, tokens, hiddens, start_pos,
     caches = [[list(np.asarray(prefix_k[li])), list(np.asarray(prefix_v[li]))]
               for li in range(len(params["layers"]))]
     wfc = widen(params["w_fc"])
-    out = []
+    out, xs = [], []
     for i, (tok, h) in enumerate(zip(tokens, hiddens)):
         p = start_pos + i
         inp = np.concatenate([widen(np.asarray(params["embed"])[int(tok)]), widen(h)])
@@ -470,6 +472,44 @@ def eagle_step(params, cfg, prefix_k, prefix_v, tokens, hiddens, start_pos,
             u = R(rmsnorm(x[None], widen(lw["mlp_norm"]), cfg.rms_eps)[0])
             m = R(silu(widen(lw["w_gate"]) @ u) * (widen(lw["w_up"]) @ u))
             x = R(x + widen(lw["w_down"]) @ m)
+        xs.append(x)
         z = R(rmsnorm(x[None], widen(params["final_norm"]), cfg.rms_eps))
         out.append(_matmul_rows(z, np.asarray(params["lm_head"]))[0])
+    if return_hidden:
+        return np.asarray(out), np.asarray(xs), caches
     return np.asarray(out)
+
+
+def ar_draft(params, cfg, prefix_k, prefix_v, accepted_tokens, bonus, hiddens, start_pos,
+             precision="bf16", return_state=False):
+    """Autoregressive EAGLE drafting of K tokens for one request: the first
+    pass runs over the accepted drafts and the bonus token (paired with the
+    target's hidden states); every later pass feeds back the token it just
+    drafted together with the drafter's own output hidden state (the residual
+    stream after the last layer) of the previous position.  This is the
+    sequential baseline of "P-EAGLE: parallel speculative decoding in vLLM",
+    Solving the autoregressive drafting bottleneck (K drafts need K passes).
+    Returns (tokens [K], logits [K, V]), and with return_state also the
+    hidden states fed into passes 2..K [K-1, d] and the per-layer K/V of
+    positions 0..start_pos+len(accepted)+K-1 (lists of [Hkv, hd] rows)."""
+    toks = list(accepted_tokens) + [bonus]
+    lg, xs, caches = eagle_step(params, cfg, prefix_k, prefix_v, toks, hiddens, start_pos,
+                                precision, return_hidden=True)
+    out_t, out_l = [int(np.argmax(lg[-1]))], [lg[-1]]
+    h = xs[-1]
+    fed = []
+    pos = start_pos + len(toks)
+    for _ in range(1, cfg.K):
+        fed.append(h)
+        ks = [np.asarray(c[0]) for c in caches]
+        vs = [np.asarray(c[1]) for c in caches]
+        lg, xs, caches = eagle_step(params, cfg, ks, vs, [out_t[-1]], [h], pos, precision,
+                                    return_hidden=True)
+        out_t.append(int(np.argmax(lg[-1])))
+        out_l.append(lg[-1])
+        h = xs[-1]
+        pos += 1
+    if return_state:
+        return (np.asarray(out_t, np.int32), np.asarray(out_l),
+                np.asarray(fed).reshape(-1, cfg.d), caches)
+    return np.asarray(out_t, np.int32), np.asarray(out_l)

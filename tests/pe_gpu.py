@@ -28,8 +28,9 @@ class Setup:
         self.ctx.close()
 
 
-def run_step(st: Setup, inp: dict, want_logits=True, B=None):
-    """prepare -> gather -> forward -> verify on the GPU; returns host copies."""
+def run_step(st: Setup, inp: dict, want_logits=True, B=None, ar=False):
+    """prepare -> gather -> forward -> verify on the GPU; returns host copies.
+    ar=True drafts with the sequential passes (pe_ar_draft)."""
     w = st.w
     B = w.batch if B is None else B
     K, d = w.K, w.d
@@ -46,8 +47,8 @@ def run_step(st: Setup, inp: dict, want_logits=True, B=None):
     pb.pe_gather_hidden(st.ctx, B, batch, t["target_hidden"], st.dev["h_shared"], dh)
     tok = torch.full((max(B, 1) * K,), -7, dtype=torch.int32, device="cuda")
     lg = torch.zeros((max(B, 1) * K, w.vocab), dtype=torch.float32, device="cuda") if want_logits else None
-    pb.pe_draft_forward(st.ctx, B, batch, dh, t["block_table"], nkv,
-                        [k for k, _ in kv], [v for _, v in kv], tok, lg)
+    fwd = pb.pe_ar_draft if ar else pb.pe_draft_forward
+    fwd(st.ctx, B, batch, dh, t["block_table"], nkv, [k for k, _ in kv], [v for _, v in kv], tok, lg)
     acc = torch.full((max(B, 1),), -7, dtype=torch.int32, device="cuda")
     bon = torch.full((max(B, 1),), -7, dtype=torch.int32, device="cuda")
     pb.pe_verify(st.ctx, B, tok, t["target_tokens"], acc, bon)
@@ -120,3 +121,83 @@ def assert_kv(w, gpu_kv, inp, fw, rtol_ulps=2):
             scale = 2.0 ** -7 if w.dtype == "bf16" else 1e-5
             np.testing.assert_allclose(gk, kr, atol=rtol_ulps * scale * max(1.0, np.abs(kr).max()))
             np.testing.assert_allclose(gv, vr, atol=rtol_ulps * scale * max(1.0, np.abs(vr).max()))
+
+
+def prefix_kv(w, inp, r):
+    """The cached prefix of request r as per-layer [p0, Hkv, hd] fp64 arrays."""
+    p0 = int(inp["verify_positions"][r, 0])
+    slots = np.array([O.slot_of(inp["block_table"][r], p, w.block_size) for p in range(p0)], np.int64)
+    ks, vs = [], []
+    for kc, vc in inp["kv"]:
+        ks.append(O.widen(kc[slots]))
+        vs.append(O.widen(vc[slots // w.block_size, :, :, slots % w.block_size]))
+    return ks, vs
+
+
+def oracle_ar(w, prm, inp, r, precision=None):
+    """Sequential drafting of request r by the oracle: tokens, logits, and
+    the per-layer K/V rows of positions [0, p0 + a + K)."""
+    a = int(inp["num_accepted"][r])
+    ks, vs = prefix_kv(w, inp, r)
+    toks = list(inp["verify_tokens"][r, 1:a + 1])
+    hid = inp["target_hidden"][r * (w.K + 1):r * (w.K + 1) + a + 1]
+    t, lg, _, caches = O.ar_draft(prm, w, ks, vs, toks, inp["bonus_tokens"][r], hid,
+                                  int(inp["verify_positions"][r, 0]),
+                                  precision or oracle_precision(w), return_state=True)
+    return t, lg, caches
+
+
+def assert_ar_request(w, out, inp, prm, r, tol_rel):
+    """Pass by pass, the GPU's sequential drafts of request r against the
+    oracle's.  Pass 1 has exact inputs and takes the parallel step's bound;
+    pass k > 1 takes the drafter's own rounded residual stream of pass k-1 as
+    input, so the rounding differences of the earlier passes enter as input
+    perturbations and the bound is k times the one-pass bound (each pass adds
+    at most one pass's worth).  Tokens are equal wherever the oracle's top-2
+    gap exceeds max(GAP, 2 x that bound); below it the GPU token must be
+    near-maximal, and since pass k+1 depends on t_k the later passes are then
+    not compared.  KV rows of every position written from agreeing inputs are
+    compared.  Returns the number of passes compared."""
+    K, V = w.K, w.vocab
+    t, lg, caches = oracle_ar(w, prm, inp, r)
+    got_t = out["tokens"][r * K:(r + 1) * K]
+    got_l = out["logits"][r * K:(r + 1) * K]
+    rms = float(np.sqrt(np.mean(lg ** 2)))
+    n = 0
+    for k in range(K):
+        tol = tol_rel * rms * (k + 1)
+        err = float(np.max(np.abs(got_l[k].astype(np.float64) - lg[k])))
+        print(f"  request {r} pass {k + 1}: max |dlogit| / rms = {err / rms:.4f}", flush=True)
+        assert err <= tol, f"request {r} pass {k + 1}: max |dlogit| {err:.3e} > {tol:.3e}"
+        n += 1
+        srt = np.sort(lg[k])
+        if got_t[k] != t[k]:
+            assert srt[-1] - srt[-2] <= max(GAP, 2 * tol), (r, k, got_t[k], t[k], srt[-1] - srt[-2])
+            assert lg[k, got_t[k]] >= srt[-1] - 2 * tol, (r, k)
+            break
+    a = int(inp["num_accepted"][r])
+    p0 = int(inp["verify_positions"][r, 0])
+    last = p0 + a + n  # positions [p0, last) were written from agreeing inputs
+    bs = w.block_size
+    scale = 2.0 ** -7 if w.dtype == "bf16" else 1e-5
+    for li, (kc_g, vc_g) in enumerate(out["kv"]):
+        for p in range(p0, last):
+            k = max(1, p - (p0 + a) + 1)  # the pass that wrote position p
+            sl = O.slot_of(inp["block_table"][r], p, bs)
+            kr, vr = caches[li][0][p], caches[li][1][p]
+            np.testing.assert_allclose(O.widen(kc_g[sl]), kr,
+                                       atol=2 * k * scale * max(1.0, np.abs(kr).max()))
+            np.testing.assert_allclose(O.widen(vc_g[sl // bs, :, :, sl % bs]), vr,
+                                       atol=2 * k * scale * max(1.0, np.abs(vr).max()))
+    return n
+
+
+def written_slots_ar(w, inp, requests):
+    """Slots the sequential passes write: positions [p0, p0 + a + K) of every
+    valid request."""
+    out = []
+    for r in requests:
+        a = int(inp["num_accepted"][r])
+        p0 = int(inp["verify_positions"][r, 0])
+        out += [O.slot_of(inp["block_table"][r], p, w.block_size) for p in range(p0, p0 + a + w.K)]
+    return np.array(out, np.int64)

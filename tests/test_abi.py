@@ -49,3 +49,20 @@ def test_binding_names_match_the_abi():
               "pe_step_graph", "pe_get_device_error"):
         assert callable(getattr(binding, n))
     assert set(binding.EXPORTS) <= set(declared())
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libpe.so not built")
+def test_binding_declares_argument_types_of_every_entry_point():
+    """Without argtypes ctypes passes a Python int as a 32-bit C int and
+    silently truncates 64-bit device pointers, so every entry point must carry
+    argument types, as many as its prototype in the header has parameters."""
+    from drafting_pe_prepare_amd import binding
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = dict(re.findall(r"\b(pe_[a-z_]+)\s*\(([^)]*)\)\s*;", text))
+    assert set(binding.EXPORTS) == set(declared()) == set(protos)
+    lib = binding.load()
+    for name, params in protos.items():
+        n = 0 if params.strip() in ("", "void") else params.count(",") + 1
+        at = getattr(lib, name).argtypes
+        assert at is not None, f"{name} has no argtypes"
+        assert len(at) == n, (name, len(at), n)

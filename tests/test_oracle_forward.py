@@ -166,6 +166,58 @@ def test_t1_is_the_autoregressive_first_pass(precision):
         np.testing.assert_allclose(out["logits"][r * 4], ar[-1], atol=1e-9 * np.abs(ar).max())
 
 
+def _ar_inputs(w, inp, r):
+    a = int(inp["num_accepted"][r])
+    ks, vs = _prefix_kv(w, inp, r)
+    toks = list(inp["verify_tokens"][r, 1:a + 1])
+    hid = inp["target_hidden"][r * (w.K + 1):r * (w.K + 1) + a + 1]
+    return ks, vs, toks, inp["bonus_tokens"][r], hid, int(inp["verify_positions"][r, 0])
+
+
+@pytest.mark.parametrize("precision", ["f64", "bf16"])
+def test_ar_draft_first_token_is_the_parallel_t1(precision):
+    """Both drafting schemes see the same prefix and accepted slots for t_1."""
+    w = SMALL.with_(K=3, batch=2, accepted="uniform")
+    prm, inp, b, hd = _case(w, seed=78)
+    out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], precision)
+    for r in range(2):
+        t, lg = O.ar_draft(prm, w, *_ar_inputs(w, inp, r), precision)
+        np.testing.assert_allclose(lg[0], out["logits"][r * w.K], atol=1e-9 * np.abs(lg[0]).max())
+        assert t[0] == out["tokens"][r * w.K]
+        assert len(t) == w.K and lg.shape == (w.K, w.vocab)
+        np.testing.assert_array_equal(t, np.argmax(lg, axis=1))
+
+
+@pytest.mark.parametrize("a", [0, 1])
+def test_ar_draft_k1_is_the_parallel_pass(a):
+    w = SMALL.with_(K=1)
+    prm, inp, b, hd = _case(w, a=a)
+    out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")
+    t, lg = O.ar_draft(prm, w, *_ar_inputs(w, inp, 0), "bf16")
+    np.testing.assert_allclose(lg[0], out["logits"][0], atol=1e-9 * np.abs(lg[0]).max())
+    assert t[0] == out["tokens"][0]
+
+
+def test_ar_draft_feeds_back_the_residual_stream_and_chains_the_cache():
+    """The hidden state fed into pass 2 is the residual stream after the last
+    layer at the NTP slot, which the parallel forward also computes there; and
+    K incremental passes equal one token-by-token run over the accepted
+    tokens, the bonus and t_1..t_{K-1} paired with the fed-back states."""
+    w = SMALL.with_(K=4, batch=1)
+    prm, inp, b, hd = _case(w, a=1, seed=79)
+    out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")
+    ks, vs, toks, bonus, hid, p0 = _ar_inputs(w, inp, 0)
+    t, lg, fed, caches = O.ar_draft(prm, w, ks, vs, toks, bonus, hid, p0, "bf16", return_state=True)
+    assert all(len(kc) == len(vc) == p0 + len(toks) + w.K for kc, vc in caches)
+    ntp = int(b["draft_rows"][0])
+    np.testing.assert_array_equal(fed[0], out["x_final"][ntp])
+    seq = toks + [bonus] + list(t[:-1])
+    hs = np.concatenate([O.widen(hid), fed])
+    one = O.eagle_step(prm, w, ks, vs, seq, hs, p0, "bf16")
+    a = len(toks)
+    np.testing.assert_allclose(one[a:], lg, atol=1e-9 * np.abs(lg).max())
+
+
 def test_t1_does_not_depend_on_K():
     base = SMALL.with_(K=2)
     prm = synth.weights(base)
