@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="c1_20b")
     p.add_argument("--no-c64", action="store_true", help="skip the c=64 measurement")
+    p.add_argument("--no-ksweep", action="store_true",
+                   help="skip the K sweep of the 4-layer d=2048 drafter")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -94,6 +96,23 @@ def step_work(w, inp):
         att += sum(q + 1 for q in pos)
     flops += w.layers * 4 * w.head_dim * w.n_q_heads * att
     return {"bytes": bytes_, "flops": flops, "weight_bytes": sum(wb.values())}
+
+
+def ar_work(w, inp):
+    """Algorithmic HBM bytes of the sequential comparison: every pass
+    streams the whole drafter; pass 1 reads the context [0, p0+a] and writes
+    the accepted slots' KV, pass k > 1 reads [0, p0+a+k-1] and writes one
+    position."""
+    e = 2 if w.dtype == "bf16" else 4
+    B, K, d = w.batch, w.K, w.d
+    a = inp["num_accepted"].astype(int)
+    p0 = inp["verify_positions"][:, 0].astype(int)
+    kvrow = w.n_kv_heads * w.head_dim * e * 2
+    passes_bytes = K * sum(weight_bytes(w).values())
+    ctx_read = int((K * (p0 + a) + K * (K + 1) // 2).sum())
+    writes = int((a + K).sum())
+    act = B * (K + 1) * d * e * 3 + (K - 1) * B * d * e * 3  # emb, hidden in, hidden copy
+    return passes_bytes + w.layers * (ctx_read + writes) * kvrow + act
 
 
 def measured_traffic(workload):
@@ -167,6 +186,32 @@ def measure(w, steps, warmup, prm=None, dev=None, label=""):
     print(f"[bench] {label} graph: {ms_step * 1e3:.1f} us/step (events {ev_ms * 1e3 / steps:.1f})",
           file=sys.stderr, flush=True)
 
+    # the sequential comparison: the same kernels as K drafting passes, one graph
+    ar_args = pb.make_step_args(t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                                t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], batch,
+                                t["target_hidden"], dev["h_shared"], dh, ks, vs, tok,
+                                t["target_tokens"], acc, bon, mode=pb.STEP_AUTOREGRESSIVE)
+    ar_steps = max(10, steps // 4)
+    for _ in range(max(3, warmup // 4)):
+        pb.pe_step_graph(ctx, B, ar_args)
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for _ in range(ar_steps):
+        pb.pe_step_graph(ctx, B, ar_args)
+    torch.cuda.synchronize()
+    ar_ms = (time.perf_counter() - ta) * 1e3 / ar_steps
+    err = pb.pe_get_device_error(ctx)
+    assert err == (0, -1), f"device error word {err}"
+    print(f"[bench] {label} sequential: {ar_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    ar_bytes = ar_work(w, inp)
+    ar = {"value": B * K / (ar_ms * 1e-3), "us_per_step": ar_ms * 1e3, "steps": ar_steps,
+          "passes": K, "algorithmic_bytes": ar_bytes,
+          "hbm_GBs": ar_bytes / (ar_ms * 1e-3) / 1e9,
+          "hbm_frac": ar_bytes / (ar_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+          "parallel_speedup": ar_ms / ms_step,
+          "mode": "pe_ar_draft: copied slots, then K-1 one-slot passes fed with the drafter's "
+                  "residual stream; same kernels, one graph per step"}
+
     # eager pass with per-phase HIP events on the library's stream
     pb.pe_profile_enable(ctx, True)
     pb.pe_profile_read(ctx, reset=True)
@@ -214,6 +259,7 @@ def measure(w, steps, warmup, prm=None, dev=None, label=""):
                  "hbm_frac": work["bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
                  "mfma_TFs": work["flops"] / step_s / 1e12,
                  "mfma_frac": work["flops"] / step_s / 1e12 / MFMA_BF16_PEAK_TFS},
+        "autoregressive": ar,
         "phases_us_per_launch": {p: round(v, 2) for p, v in phases_us.items()},
         "phases_us_per_step": {p: round(v, 2) for p, v in per_step_us.items()},
         "config": {"workload": w.name, "batch": B, "K": K, "d": w.d, "n_q_heads": w.n_q_heads,
@@ -226,6 +272,32 @@ def measure(w, steps, warmup, prm=None, dev=None, label=""):
     del kv, t
     torch.cuda.empty_cache()
     return out, prm, dev
+
+
+def ksweep(steps, warmup):
+    """Step cost against draft depth on the deeper drafter (B=16, d=2048,
+    32q/4kv x 64, MLP 6144, 4 layers, V=151936, prefix 4096), parallel and
+    sequential, same weights at every K."""
+    import torch
+    from drafting_pe_prepare_amd import binding as pb
+    from drafting_pe_prepare_amd import configs, synth
+    base = configs.KSWEEP
+    prm = synth.weights(base)
+    dev = pb.upload_weights(prm)
+    rows = []
+    for K in base.Ks:
+        r, _, _ = measure(base.with_(K=K), steps, warmup, prm=prm, dev=dev, label=f"ksweep K={K}")
+        ar = r["autoregressive"]
+        rows.append({"K": K, "us_per_step": r["us_per_step"], "draft_tokens_per_s": r["value"],
+                     "hbm_frac": r["step"]["hbm_frac"], "mfma_frac": r["step"]["mfma_frac"],
+                     "sequential_us_per_step": ar["us_per_step"],
+                     "sequential_draft_tokens_per_s": ar["value"],
+                     "parallel_speedup": ar["parallel_speedup"],
+                     "lm_head_us": r["phases_us_per_step"]["lmhead"]})
+    del dev
+    torch.cuda.empty_cache()
+    return {"workload": base.name, "batch": base.batch, "d": base.d, "layers": base.layers,
+            "vocab": base.vocab, "prefix": list(base.prefix), "seed": base.seed, "rows": rows}
 
 
 # ---------------------------------------------------------------------------
@@ -296,13 +368,16 @@ def main():
         "phases_us_per_step": main_res["phases_us_per_step"],
         "event_us_per_step": main_res["event_us_per_step"],
         "eager_us_per_step": main_res["eager_us_per_step"],
+        "autoregressive": main_res["autoregressive"],
     }
     if not args.no_c64 and w.name == "c1_20b":
         c64, _, _ = measure(configs.C64, max(20, args.steps // 4), max(5, args.warmup // 4),
                             prm=prm, dev=dev, label="c64_20b")
         line["c64"] = {k: c64[k] for k in ("value", "us_per_step", "roofline", "step",
-                                            "phases_us_per_step", "config")}
+                                            "autoregressive", "phases_us_per_step", "config")}
         line["c64"]["config"]["weights"] = "same drafter weights as the c=1 workload"
+    if not args.no_ksweep and w.name == "c1_20b":
+        line["ksweep"] = ksweep(max(20, args.steps // 5), max(3, args.warmup // 4))
     if not args.no_cpu_baseline:
         del dev
         torch.cuda.empty_cache()

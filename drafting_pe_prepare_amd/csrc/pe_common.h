@@ -12,11 +12,16 @@ constexpr int kWave = 64;
 
 // bfloat16 is stored as its 16-bit pattern (the high half of an IEEE float32).
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-// float32 -> bfloat16, round to nearest, ties to even.  Inputs here are finite.
+// float32 -> bfloat16, round to nearest, ties to even: gfx950's
+// v_cvt_pk_bf16_f32 (one instruction converts a pair).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Storage access for the two element types the library handles.

@@ -7,8 +7,20 @@ import oracle as O
 from drafting_pe_prepare_amd import binding as pb
 from drafting_pe_prepare_amd import synth
 
-LOGIT_TOL = {"bf16": 2e-2, "f32": 1e-4}   # max |dlogit| / RMS(oracle logits)
+LOGIT_TOL = {"bf16": 2e-2, "f32": 1e-4}   # max |dlogit| / RMS(oracle logits), one layer
 GAP = 1e-2                                  # top-2 gap above which tokens must match
+
+
+def logit_tol(w):
+    """Logit bound for workload w.  In bf16, once the GPU (fp32
+    accumulation) and the fp64 oracle round one stored value of a row to
+    different neighbours, the row's later bf16 values differ at the one-ulp
+    level; each layer's residual adds contribute independent noise of that
+    size, so the bound grows as sqrt(layers) (measured: ~1% of RMS at one
+    layer, 2.2-3.2% at four).  fp32 rounds nothing and keeps its bound."""
+    if w.dtype == "bf16":
+        return LOGIT_TOL["bf16"] * float(np.sqrt(w.layers))
+    return LOGIT_TOL["f32"]
 
 
 def oracle_precision(w):
@@ -83,19 +95,22 @@ def assert_metadata_equal(gpu_batch, ob):
 
 def assert_tokens_logits(tokens, logits, o_logits, tol_rel, rows=None):
     """Logits within tol_rel * RMS; tokens equal wherever the oracle's top-2
-    gap exceeds GAP, otherwise the GPU token must be near-maximal in the
+    gap exceeds GAP (or twice the logit bound, when that bound is above the
+    one-layer bf16 one), otherwise the GPU token must be near-maximal in the
     oracle's logits.  Returns the number of rows with a tight gap."""
     if rows is not None:
         tokens, logits = tokens[rows], logits[rows]
     rms = float(np.sqrt(np.mean(o_logits ** 2)))
     tol = tol_rel * rms
     err = float(np.max(np.abs(logits.astype(np.float64) - o_logits)))
+    print(f"  logits: max |dlogit| / rms = {err / rms:.5f}", flush=True)
     assert err <= tol, f"max |dlogit| {err:.3e} > {tol:.3e} (rms {rms:.3e})"
     tight = 0
+    gap_min = GAP if tol_rel <= LOGIT_TOL["bf16"] else max(GAP, 2 * tol)
     for i in range(o_logits.shape[0]):
         srt = np.sort(o_logits[i])
         gap = srt[-1] - srt[-2]
-        if gap > GAP:
+        if gap > gap_min:
             assert tokens[i] == int(np.argmax(o_logits[i])), (i, tokens[i], np.argmax(o_logits[i]), gap)
         else:
             tight += 1

@@ -134,12 +134,12 @@ def _prefix_kv(w, inp, r):
 
 
 @pytest.mark.parametrize("precision", ["f64", "bf16"])
-@pytest.mark.parametrize("a", [0, 1])
-def test_k1_is_one_eagle_step(precision, a):
+@pytest.mark.parametrize("a,layers", [(0, 1), (1, 1), (1, 3)])
+def test_k1_is_one_eagle_step(precision, a, layers):
     """With K=1 the draft batch is two copied slots and no MASK slot; its
     output must equal one ordinary EAGLE drafter pass over the accepted
     tokens and the bonus token (written token by token, without slots)."""
-    w = SMALL.with_(K=1)
+    w = SMALL.with_(K=1, layers=layers)
     prm, inp, b, hd = _case(w, a=a)
     out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], precision)
     ks, vs = _prefix_kv(w, inp, 0)
@@ -375,3 +375,13 @@ def test_bf16_mode_is_close_to_f64():
     l16 = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")["logits"]
     rel = np.abs(l64 - l16).max() / np.sqrt((l64 ** 2).mean())
     assert 1e-4 < rel < 5e-2
+
+
+def test_sampled_requests_equal_the_full_batch():
+    """Computing only some requests (as the full-size checks do) leaves their
+    outputs unchanged: requests interact only through nothing."""
+    w = SMALL.with_(K=3, batch=4, layers=3, accepted="uniform")
+    prm, inp, b, hd = _case(w, seed=5)
+    full = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")
+    sub = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16", requests=[0, 2, 3])
+    np.testing.assert_array_equal(sub["logits"], full["logits"][np.r_[0:3, 6:12]])
