@@ -444,29 +444,24 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16, M > 64: BM x BN tiles, k-tiles of 32, a 4-stage LDS ring filled by
-// global_load_lds_dwordx4 (global -> LDS with no staging registers), 2 x 2
-// waves of (BM/2) x (BN/2).
+// bf16, M > 16: BM x BN tiles over k-tiles of 64 in an S-stage LDS ring filled
+// by global_load_lds_dwordx4 (global -> LDS with no staging registers).
+// S = 2 leaves room for two workgroups per CU; S = 3 prefetches one k-tile
+// further for grids that put at most one workgroup on a CU.
 //
-// LDS layout of one operand tile (R rows x 32 k, 64 B per row): rows pair up
-// into 128-byte lines; 16-byte chunk c of row r sits in line r/2 at position
-// ((r%2)*4 + c) XOR ((r/2)%4).  A 16-row MFMA fragment read then touches 8
-// distinct positions per 8 lanes (no bank conflicts), and one wave-wide
-// global_load_lds (lane i -> LDS base + 16 i) fills 8 whole lines.
+// One DMA instruction moves 8 whole tile rows: 128 bytes (64 bf16 of k) per
+// row, 16 bytes per lane.  Rows split into half lines (32-wide k-tiles) stream
+// ~1.4x slower through this path (measured on a loads-only copy of the loop).
+// LDS: tile row r takes 128 bytes and its 16-byte chunk c sits at slot
+// c ^ (r & 7), so the 8 lanes of a fragment-read phase hit 8 distinct slots.
+// Every fragment row of a wave has r & 7 == col & 7, so fragment i is one base
+// offset plus i * 2 KB.
+//
+// A k-tile feeds two 32-wide MFMA substeps; the fragments of the next substep
+// are read while the MFMAs of the current one run, and there is one barrier
+// per k-tile.
 // ---------------------------------------------------------------------------
-constexpr int kStages = 4;
-
-__device__ __forceinline__ int swz(int row, int c) {
-  const int p = row >> 1;
-  return p * 128 + ((((row & 1) << 2) | c) ^ (p & 3)) * 16;
-}
-// inverse: lane i of the load instruction filling lines 8*ii .. 8*ii+7
-__device__ __forceinline__ void unswz(int ii, int lane, int& row, int& c) {
-  const int p = ii * 8 + (lane >> 3);
-  const int q = (lane & 7) ^ (p & 3);
-  row = 2 * p + (q >> 2);
-  c = q & 3;
-}
+__device__ __forceinline__ int swz64(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -474,21 +469,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt_hi[15:14]
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+// lgkmcnt(0) only: every LDS read issued so far has returned
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(S == 2 ? 2 : 1, S == 2 ? 2 : 1)))
 void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;   // MFMA tiles per wave
-  constexpr int LA = BM / 16 / NW, LB = BN / 16 / NW;   // load instructions per wave per k-tile
-  static_assert(LA * 16 * NW == BM && LB * 16 * NW == BN, "tile rows must split over the waves");
+  constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;     // DMA instructions per wave per k-tile
+  static_assert(LA * 8 * NW == BM && LB * 8 * NW == BN, "tile rows must split over the waves");
   static_assert((BN / WN) % 32 == 0, "a wave's columns must be whole 32-column blocks");
-  constexpr int LW = LA + LB;
-  constexpr int STAGE = (BM + BN) * 64;              // bytes per stage
-  static_assert(kStages == 4, "the k loop is unrolled by 4");
-  // four distinct LDS objects, so the compiler sees that the DMA into one stage
-  // and the fragment reads of another do not alias
-  __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+  constexpr int STAGE = (BM + BN) * 128;                // bytes per stage
+  static_assert(S == 2 || S == 3, "two or three stages");
+  // distinct LDS objects, so the compiler sees that the DMA into one stage and
+  // the fragment reads of another do not alias
+  __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE], st1[STAGE], st2[S == 3 ? STAGE : 16];
 
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
   const int mt = j % mtiles, nt = (j / mtiles) * 8 + xcd;
@@ -497,37 +493,27 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
   const int wm = w / WN, wn = w % WN;
 
-  // per load instruction: this lane's source row pointer and chunk
+  // DMA instruction i of this wave fills tile rows 8 (w + NW i) .. +7; lane l
+  // takes row + l/8 and LDS slot l%8, i.e. global chunk (l%8) ^ (row & 7)
   ARow<uint16_t, AL> ar[LA];
-  int ac[LA];
   const uint16_t* bp[LB];
-  int bc[LB];
+  const int lr = l >> 3, lc = ((l & 7) ^ (lr & 7)) * 8;  // rows are 8-aligned: row & 7 == lr
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    int row, c;
-    unswz(w + NW * i, l, row, c);
-    ar[i].init(g, min(m0 + row, g.M - 1));
-    ac[i] = c * 8;
-  }
+  for (int i = 0; i < LA; ++i) ar[i].init(g, min(m0 + 8 * (w + NW * i) + lr, g.M - 1));
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    int row, c;
-    unswz(w + NW * i, l, row, c);
-    bp[i] = weight_row<uint16_t, BMAP>(g, min(n0 + row, g.N - 1));
-    bc[i] = c * 8;
-  }
+  for (int i = 0; i < LB; ++i) bp[i] = weight_row<uint16_t, BMAP>(g, min(n0 + 8 * (w + NW * i) + lr, g.N - 1)) + lc;
   auto issue = [&](unsigned char* st, int kt) {
-    const int k0 = kt * 32;
+    const int k0 = kt * 64;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
       __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void*)ar[i].at(k0 + ac[i], g.d),
+          (__attribute__((address_space(1))) void*)ar[i].at(k0 + lc, g.d),
           (__attribute__((address_space(3))) void*)(st + (w + NW * i) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
       __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void*)(bp[i] + k0 + bc[i]),
-          (__attribute__((address_space(3))) void*)(st + BM * 64 + (w + NW * i) * 1024), 16, 0, 0);
+          (__attribute__((address_space(1))) void*)(bp[i] + k0),
+          (__attribute__((address_space(3))) void*)(st + BM * 128 + (w + NW * i) * 1024), 16, 0, 0);
   };
 
   f32x4 acc[TI][TJ];
@@ -535,51 +521,74 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int aoff[TI], boff[TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i) aoff[i] = swz(wm * (BM / WM) + i * 16 + col, kg);
-#pragma unroll
-  for (int jj = 0; jj < TJ; ++jj) boff[jj] = BM * 64 + swz(wn * (BN / WN) + jj * 16 + col, kg);
+  // substep s reads 16-byte chunk 4s + kg of each fragment row
+  const int ar0 = wm * (BM / WM) + col, br0 = wn * (BN / WN) + col;
+  const int aoff0 = swz64(ar0, kg), aoff1 = swz64(ar0, 4 + kg);
+  const int boff0 = BM * 128 + swz64(br0, kg), boff1 = BM * 128 + swz64(br0, 4 + kg);
 
-  const int nk = g.K / 32;
-  if (0 < nk) issue(st0, 0);
+  const int nk = g.K / 64;
+  issue(st0, 0);
   if (1 < nk) issue(st1, 1);
-  if (2 < nk) issue(st2, 2);
-  // one k-tile: wait for this wave's DMA of stage `cur`, barrier, refill the
-  // stage freed by the previous k-tile, then the fragment reads and TI*TJ MFMAs.
-  // `cur` and `refill` are distinct stages; saying so (restrict) lets the
-  // compiler keep the refill DMA in flight across the fragment reads.
-  auto step = [&](unsigned char* __restrict__ cur, unsigned char* __restrict__ refill, int kt) {
-    const int later = min(kStages - 2, nk - 1 - kt);
-    if (later >= 2) wait_vmcnt<2 * LW>();
-    else if (later == 1) wait_vmcnt<LW>();
-    else wait_vmcnt<0>();
-    // Plain s_barrier: this wave's DMA of `cur` has landed (the wait above), every
-    // wave's reads of `refill` completed before it reached here (they fed the
-    // previous k-tile's MFMAs).  A fenced __syncthreads would also wait for the
-    // DMA into the stages still in flight and serialize the pipeline.
-    asm volatile("s_barrier" ::: "memory");
-    uint4 bf[TJ], af[TI];
+  if (S == 3 && 2 < nk) issue(st2, 2);
+  uint4 fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
+  // k-tile 0 must land; the later prologue tiles may stay in flight
+  if (S == 3 && 2 < nk) wait_vmcnt<2 * (LA + LB)>();
+  else if (1 < nk) wait_vmcnt<LA + LB>();
+  else wait_vmcnt<0>();
+  // Plain s_barrier: this wave's DMA of the stage has landed (the wait above).
+  // A fenced __syncthreads would also wait for the DMA still in flight.
+  asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-    for (int jj = 0; jj < TJ; ++jj) bf[jj] = *reinterpret_cast<const uint4*>(cur + boff[jj]);
+  for (int i = 0; i < TI; ++i) fa0[i] = *reinterpret_cast<const uint4*>(st0 + aoff0 + i * 2048);
 #pragma unroll
-    for (int i = 0; i < TI; ++i) af[i] = *reinterpret_cast<const uint4*>(cur + aoff[i]);
-    if (kt + kStages - 1 < nk) issue(refill, kt + kStages - 1);
+  for (int jj = 0; jj < TJ; ++jj) fb0[jj] = *reinterpret_cast<const uint4*>(st0 + boff0 + jj * 2048);
+
+  auto mfmas = [&](const uint4 (&xa)[TI], const uint4 (&xb)[TJ]) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = mfma16(af[i], bf[jj], acc[i][jj]);
+      for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = mfma16(xa[i], xb[jj], acc[i][jj]);
   };
-  for (int kt = 0; kt < nk; kt += 4) {
-    step(st0, st3, kt);
-    if (kt + 1 < nk) step(st1, st0, kt + 1);
-    if (kt + 2 < nk) step(st2, st1, kt + 2);
-    if (kt + 3 < nk) step(st3, st2, kt + 3);
+  // k-tile kt in stage `cur`; on entry fa0/fb0 hold its first substep.  `cur`
+  // and `nxt` are distinct stages; saying so (restrict) lets the compiler keep
+  // the DMA into `cur` in flight across the reads of `nxt`.
+  auto step = [&](unsigned char* __restrict__ cur, const unsigned char* __restrict__ nxt, int kt) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa1[i] = *reinterpret_cast<const uint4*>(cur + aoff1 + i * 2048);
+#pragma unroll
+    for (int jj = 0; jj < TJ; ++jj) fb1[jj] = *reinterpret_cast<const uint4*>(cur + boff1 + jj * 2048);
+    mfmas(fa0, fb0);
+    wait_lgkm0();  // this wave's reads of `cur` are done
+    if (kt + 1 < nk) {
+      // the DMA of k-tile kt+1 (this wave's part) has landed; with three stages
+      // the one of kt+2 may still be in flight
+      if (S == 3 && kt + 2 < nk) wait_vmcnt<LA + LB>();
+      else wait_vmcnt<0>();
+      asm volatile("s_barrier" ::: "memory");  // ... everyone's, and `cur` is free
+      if (kt + S < nk) issue(cur, kt + S);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) fa0[i] = *reinterpret_cast<const uint4*>(nxt + aoff0 + i * 2048);
+#pragma unroll
+      for (int jj = 0; jj < TJ; ++jj) fb0[jj] = *reinterpret_cast<const uint4*>(nxt + boff0 + jj * 2048);
+    }
+    mfmas(fa1, fb1);
+  };
+  if constexpr (S == 2) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(st0, st1, kt);
+      if (kt + 1 < nk) step(st1, st0, kt + 1);
+    }
+  } else {
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(st0, st1, kt);
+      if (kt + 1 < nk) step(st1, st2, kt + 1);
+      if (kt + 2 < nk) step(st2, st0, kt + 2);
+    }
   }
 
   // lane (kg, col) holds C[row 4kg + r of MFMA tile i][col of tile jj]
-  if (EPI == E_ARGMAX) {
-    __syncthreads();
+  if constexpr (EPI == E_ARGMAX) {
+    __syncthreads();  // every fragment read is done; no DMA is in flight
     uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [WN][BM]
     static_assert(WN * BM * 8 <= STAGE, "argmax scratch fits one stage");
 #pragma unroll
@@ -609,6 +618,74 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
         uint64_t bk = s_best[lr];
         for (int v = 1; v < WN; ++v) bk = s_best[v * BM + lr] > bk ? s_best[v * BM + lr] : bk;
         g.keys[(long long)(m0 + lr) * g.parts + nt] = bk;
+      }
+    }
+  } else if constexpr (EPI != E_QKV && (BN / WN == 32 || BN / WN == 64)) {
+    // Row-vector epilogue.  Each wave stages its fp32 (BM/WM) x (BN/WN) tile
+    // in a private LDS region (the stages are free: every fragment read has
+    // returned and no DMA is in flight after the barrier), then writes rows as
+    // 16-byte pieces of 8 bf16 (and reads the residual the same way).
+    // Rows 4kg+r of a C fragment land 4 rows apart; a 64-float row stride
+    // gets an XOR of 16 (row/4 % 4) floats, a 32-float one a 4-float pad,
+    // so the 4 row groups of a store fall in distinct banks.
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int LD = WTN == 64 ? 64 : WTN + 4;
+    constexpr int WBYTES = WTM * LD * 4;
+    constexpr int PER = STAGE / WBYTES;  // wave regions per stage object
+    static_assert(PER >= 1 && (NW + PER - 1) / PER <= S, "wave regions fit the stages");
+    auto cpos = [&](int r, int c) { return r * LD + (WTN == 64 ? (c ^ (((r >> 2) & 3) << 4)) : c); };
+    __syncthreads();
+    unsigned char* reg = (w / PER == 0) ? st0 : (w / PER == 1 ? st1 : st2);
+    float* ct = reinterpret_cast<float*>(reg + (w % PER) * WBYTES);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TJ; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ct[cpos(i * 16 + kg * 4 + r, jj * 16 + col)] = acc[i][jj][r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int mw = m0 + wm * WTM, nw0 = n0 + wn * WTN;
+    if constexpr (EPI == E_SILU) {
+      // logical columns (32q + c, 32q + 16 + c) -> output column nw0/2 + 16q + c
+      constexpr int SEG = WTN / 16;  // 8-output pieces per row
+      for (int e = l; e < WTM * SEG; e += 64) {
+        const int rr = e / SEG, sg = e % SEG, q = sg >> 1, c0 = (sg & 1) * 8;
+        const int m = mw + rr;
+        if (m >= g.M || nw0 + 32 * q >= g.N) continue;
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float gt = ct[cpos(rr, 32 * q + c0 + t)], up = ct[cpos(rr, 32 * q + 16 + c0 + t)];
+          v[t] = gt / (1.0f + expf(-gt)) * up;
+        }
+        uint4 o;
+        o.x = f2bf2(v[0], v[1]); o.y = f2bf2(v[2], v[3]); o.z = f2bf2(v[4], v[5]); o.w = f2bf2(v[6], v[7]);
+        *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)m * g.ldo + (nw0 >> 1) + 16 * q + c0) = o;
+      }
+    } else {
+      constexpr int SEG = WTN / 8;
+      for (int e = l; e < WTM * SEG; e += 64) {
+        const int rr = e / SEG, c0 = (e % SEG) * 8;
+        const int m = mw + rr, n = nw0 + c0;
+        if (m >= g.M || n >= g.N) continue;
+        const float4 a0 = *reinterpret_cast<const float4*>(ct + cpos(rr, c0));
+        const float4 a1 = *reinterpret_cast<const float4*>(ct + cpos(rr, c0 + 4));
+        float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const long long o = (long long)m * g.ldo + n;
+        if constexpr (EPI == E_RESID) {
+          const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + o);
+          const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v[2 * t] += __uint_as_float(rw[t] << 16);
+            v[2 * t + 1] += __uint_as_float(rw[t] & 0xFFFF0000u);
+          }
+        }
+        uint4 ov;
+        ov.x = f2bf2(v[0], v[1]); ov.y = f2bf2(v[2], v[3]); ov.z = f2bf2(v[4], v[5]); ov.w = f2bf2(v[6], v[7]);
+        *reinterpret_cast<uint4*>((uint16_t*)g.out + o) = ov;
       }
     }
   } else {
@@ -703,18 +780,33 @@ hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_
   return hipGetLastError();
 }
 
-// Which kernel serves a bf16 GEMM of this shape.
-enum Variant { V_WIDE, V_SKINNY, V_TILED };
-static Variant pick(int epi, int M, int K) {
-  const size_t wide_lds = size_t(M) * (K / 8 + 1) * 16;
-  if (epi == E_ARGMAX && M <= 16 && wide_lds <= 140 * 1024) return V_WIDE;
-  return M <= 64 ? V_SKINNY : V_TILED;
+// Which kernel serves a bf16 GEMM of this shape (M rows, N logical columns).
+//  * LM head (E_ARGMAX): the LDS-resident wide kernel up to 16 rows; tiled
+//    64x256, 128x256 or 256x256 above (a 64-row tile streams the weights once
+//    at ~4.9 TB/s where the split-K kernel managed ~1.4 TB/s).
+//  * Dense, up to 16 rows: split-K over waves (weights from the fragment-order copy).
+//  * Dense, 17..64 rows: tiled 64x128 when there are >= 32 column tiles,
+//    split-K otherwise (few tiles leave most CUs idle).
+//  * Dense, more rows: tiled 128x128; two stages and two workgroups per CU when
+//    the tiles outnumber the CUs, three stages and one workgroup otherwise.
+enum Variant { V_WIDE, V_SKINNY, V_A64, V_A128, V_A256, V_D64, V_D128S2, V_D128S3 };
+static Variant pick(int epi, int M, int N, int K, int num_cus) {
+  if (epi == E_ARGMAX) {
+    const size_t wide_lds = size_t(M) * (K / 8 + 1) * 16;
+    if (M <= 16 && wide_lds <= 140 * 1024) return V_WIDE;
+    if (M <= 64) return V_A64;
+    return M <= 128 ? V_A128 : V_A256;
+  }
+  if (M <= 16) return V_SKINNY;
+  if (M <= 64) return (N + 127) / 128 >= 32 ? V_D64 : V_SKINNY;
+  const long long tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
+  return tiles > num_cus ? V_D128S2 : V_D128S3;
 }
-constexpr int kArgmaxBN = 256;
+constexpr int kArgmaxBN = 256;  // columns per tile of every tiled LM-head variant
 
 int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus) {
   if (dtype != 1) return (N + 31) / 32;
-  switch (pick(E_ARGMAX, M, K)) {
+  switch (pick(E_ARGMAX, M, N, K, num_cus)) {
     case V_WIDE: return std::min(num_cus, N / 16);
     case V_SKINNY: return (N + 15) / 16;
     default: return (N + kArgmaxBN - 1) / kArgmaxBN;
@@ -768,28 +860,38 @@ static hipError_t run_wide_any(const GemmArgs& g, int num_cus, hipStream_t st) {
   return run_wide<1>(g, num_cus, st);
 }
 
-template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN>
+template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int S>
 static hipError_t run_tiled(const GemmArgs& g, hipStream_t st) {
+  if (g.K % 64) return hipErrorInvalidValue;  // whole 64-wide k-tiles (and A_FC halves)
   const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN;
   if (EPI == E_ARGMAX && g.parts != ntiles) return hipErrorInvalidValue;
   const int grid = mtiles * ((ntiles + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_tiled_kernel<EPI, AL, BMAP, BM, BN, WM, WN>), dim3(grid), dim3(64 * WM * WN),
-                     0, st, g, mtiles, ntiles);
+  hipLaunchKernelGGL((gemm_tiled_kernel<EPI, AL, BMAP, BM, BN, WM, WN, S>), dim3(grid),
+                     dim3(64 * WM * WN), 0, st, g, mtiles, ntiles);
   return hipGetLastError();
 }
 
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
-  switch (pick(EPI, g.M, g.K)) {
-    case V_WIDE: return run_wide_any(g, num_cus, st);
-    case V_SKINNY:
-      if (g.M <= 16) return run_skinny<EPI, AL, BMAP, 1>(g, st);
-      if (g.M <= 32) return run_skinny<EPI, AL, BMAP, 2>(g, st);
-      if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
-      return run_skinny<EPI, AL, BMAP, 4>(g, st);
-    default:
-      if constexpr (EPI == E_ARGMAX) return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN, 4, 2>(g, st);
-      else return run_tiled<EPI, AL, BMAP, 128, 128, 2, 2>(g, st);
+  const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);
+  if constexpr (EPI == E_ARGMAX) {
+    switch (v) {
+      case V_WIDE: return run_wide_any(g, num_cus, st);
+      case V_A64: return run_tiled<EPI, AL, BMAP, 64, kArgmaxBN, 1, 4, 2>(g, st);
+      case V_A128: return run_tiled<EPI, AL, BMAP, 128, kArgmaxBN, 2, 4, 2>(g, st);
+      default: return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN, 4, 2, 2>(g, st);
+    }
+  } else {
+    switch (v) {
+      case V_SKINNY:
+        if (g.M <= 16) return run_skinny<EPI, AL, BMAP, 1>(g, st);
+        if (g.M <= 32) return run_skinny<EPI, AL, BMAP, 2>(g, st);
+        if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
+        return run_skinny<EPI, AL, BMAP, 4>(g, st);
+      case V_D64: return run_tiled<EPI, AL, BMAP, 64, 128, 1, 4, 3>(g, st);
+      case V_D128S2: return run_tiled<EPI, AL, BMAP, 128, 128, 2, 2, 2>(g, st);
+      default: return run_tiled<EPI, AL, BMAP, 128, 128, 2, 2, 3>(g, st);
+    }
   }
 }
 

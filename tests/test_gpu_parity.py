@@ -86,6 +86,15 @@ def test_small_multilayer(dtype, layers, K, B, seed):
     _full_check(w, seed)
 
 
+@pytest.mark.parametrize("K,B,mlp,seed", [(4, 5, 2048, 81), (7, 12, 16384, 82)])
+def test_small_bf16_tile_variants(K, B, mlp, seed):
+    """A wider MLP reaches the other GEMM variants: 40 rows with a 4096-column
+    gate/up (64-row tiles), and 168 rows with a 32768-column gate/up (more
+    128x128 tiles than CUs: two stages, two workgroups per CU)."""
+    w = SMALL_BF16.with_(K=K, batch=B, mlp=mlp, accepted="uniform", prefix=("uniform", 30, 200))
+    _full_check(w, seed)
+
+
 @pytest.mark.parametrize("B", [5, 12])
 def test_small_bf16_tiled_path(B):
     """B*2K > 64 rows: the LDS-tiled GEMM path and the tiled LM head."""
