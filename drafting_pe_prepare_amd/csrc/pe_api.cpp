@@ -164,7 +164,8 @@ pe_status check_cfg(const pe_config* c) {
   if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(PE_ERR_INVALID_ARG, "mask_id outside [0,vocab)");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(PE_ERR_INVALID_ARG, "rms_eps/rope_theta");
   if (c->vocab % 16) return fail(PE_ERR_UNSUPPORTED, "vocab must be a multiple of 16");
-  if (c->block_size % 16) return fail(PE_ERR_UNSUPPORTED, "block_size must be a multiple of 16");
+  if (c->block_size < 16 || (c->block_size & (c->block_size - 1)))
+    return fail(PE_ERR_UNSUPPORTED, "block_size must be a power of two >= 16");
   if (c->head_dim % 32) return fail(PE_ERR_UNSUPPORTED, "head_dim must be a multiple of 32");
   if (c->dtype == PE_BF16) {
     if (c->head_dim != 64) return fail(PE_ERR_UNSUPPORTED, "bf16 kernels need head_dim 64");

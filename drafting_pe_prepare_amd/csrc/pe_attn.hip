@@ -41,7 +41,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Split-KV plan shared by the partial and merge kernels: total context ->
-// chunk size CH (multiple of 32, >= 64); off[r] = first chunk of request r.
+// chunk size CH (multiple of 64, >= 256); off[r] = first chunk of request r.
 // Any blockDim that is a multiple of 64 and <= 512.
 __device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, int* off,
                           int& CH) {
@@ -56,8 +56,8 @@ __device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, i
   tot = 0;
   for (int w = 0; w < nw; ++w) tot += s_tot[w];
   long long ch = (tot * Hkv + target - 1) / (target > 0 ? target : 1);
-  ch = (ch + 31) / 32 * 32;
-  if (ch < 64) ch = 64;
+  ch = (ch + 63) / 64 * 64;
+  if (ch < 256) ch = 256;  // fewer, longer items when the batch is small (each item pays a DMA ramp-up)
   if (ch > (1 << 30)) ch = 1 << 30;
   CH = int(ch);
   const int per = (B + nt - 1) / nt;
@@ -103,16 +103,19 @@ __device__ __forceinline__ void attn_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One workgroup of 8 waves per (request, chunk, KV head) item.  Every step the
-// 8 waves each issue one 1 KB LDS DMA (4 fill the K tile, 4 the V tile) three
-// steps ahead, then each wave runs its QPW query tiles of 16 (S*G queries =
-// S slots x G heads of the group) against the shared tile.
+// One workgroup of 8 waves per (request, chunk, KV head) item.  A step covers
+// 64 positions (two 32-position halves).  Every step each wave issues two
+// 1 KB LDS DMAs three steps ahead: K rows 8(w%4).. of half w/4 and V lines
+// 8(w%4).. of half w/4, so up to three 16 KB steps are in flight per
+// workgroup.  Then each wave runs its QPW query tiles of 16 (S*G queries = S
+// slots x G heads of the group) against the shared tiles.
 template <int QPW>
-__global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QPW == 1 ? 4 : 1, QPW == 1 ? 4 : 2)))
+void attn_partial_kernel(AttnArgs a) {
   __shared__ int s_off[kMaxB + 1];
-  __shared__ __attribute__((aligned(16))) unsigned char k0[4096], k1[4096], k2[4096], k3[4096];
-  __shared__ __attribute__((aligned(16))) unsigned char v0[4096], v1[4096], v2[4096], v3[4096];
-  __shared__ float s_ot[8][64][17];
+  constexpr int HALF = 4096;                // one 32-position half of a K or V tile
+  __shared__ __attribute__((aligned(16))) unsigned char k0[2 * HALF], k1[2 * HALF], k2[2 * HALF], k3[2 * HALF];
+  __shared__ __attribute__((aligned(16))) unsigned char v0[2 * HALF], v1[2 * HALF], v2[2 * HALF], v3[2 * HALF];
   constexpr int WIN = 8192;                 // positions per block-id window
   __shared__ int s_bt[WIN / 16 + 2];        // block ids of the window (block_size >= 16)
   int CH;
@@ -124,9 +127,9 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
   const uint16_t* Q = (const uint16_t*)a.q;
   const uint16_t* Kc = (const uint16_t*)a.kcache;
   const uint16_t* Vc = (const uint16_t*)a.vcache;
-  const int bs = a.block_size;
+  const int bs = a.block_size, bsl = __builtin_ctz(bs);  // power of two (checked on the host)
   const uint4 zero = {0u, 0u, 0u, 0u};
-  // fragment offsets inside a stage
+  // fragment offsets inside a 32-position half
   int koff[2][2], voff[4];
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt)
@@ -137,6 +140,17 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) voff[dt] = vswz(c + 16 * dt, gq);
+  // this wave's DMA lanes: half dh of the step; K row kpos (in the half) and
+  // chunk kch; V line of dims vd, chunk vch
+  const int dh = w >> 2, ww = w & 3;
+  const int kpos = 8 * ww + (l >> 3), kch = (l & 7) ^ kswz(kpos);
+  const int vline = 8 * ww + (l >> 3), vx = (l & 7) ^ (vline & 3);
+  const int vd = 2 * vline + (vx >> 2), vch = vx & 3;
+  // each wave's partial-output transpose buffer reuses one stage object once
+  // an item's positions are done (64 x 17 floats per wave)
+  unsigned char* const sto = w == 0 ? k0 : w == 1 ? k1 : w == 2 ? k2 : w == 3 ? k3
+                           : w == 4 ? v0 : w == 5 ? v1 : w == 6 ? v2 : v3;
+  float* const s_ot = reinterpret_cast<float*>(sto);
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int rc = item / a.Hkv, g = item - rc * a.Hkv;
@@ -153,8 +167,8 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     // query tiles of this wave
     uint4 qf[QPW][2];
     float m[QPW], lsum[QPW];
-    int qpos[QPW];
-    bool qv[QPW];
+    int qpos[QPW], qmin[QPW];
+    bool qv[QPW], qany[QPW];
     f32x4 o[QPW][4];
 #pragma unroll
     for (int qq = 0; qq < QPW; ++qq) {
@@ -171,6 +185,13 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
       lsum[qq] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[qq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // lowest position among the tile's valid queries (wave-uniform): steps
+      // that end at or before it need no causal mask
+      int mn = v ? qpos[qq] : 0x7FFFFFFF;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mn = min(mn, __shfl_xor(mn, off, 64));
+      qmin[qq] = mn;
+      qany[qq] = __ballot(v) != 0;  // a tile whose slots are all rejected is skipped
     }
 
     // positions [cb, ce) in windows of WIN; the block ids of a window are
@@ -178,103 +199,131 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     // retires in order: a block-table load would wait for every DMA before it)
     for (int pb = cb; pb < ce; pb += WIN) {
     const int pe = min(ce, pb + WIN);
-    const int nsteps = (pe - pb + 31) >> 5;
-    const int wb0 = pb / bs, wb1 = (pe - 1) / bs;
+    const int nsteps = (pe - pb + 63) >> 6;
+    const int wb0 = pb >> bsl, wb1 = (pe - 1) >> bsl;
     for (int i = threadIdx.x; i <= wb1 - wb0; i += blockDim.x) s_bt[i] = btr[wb0 + i];
     __syncthreads();
-    // this wave's DMA instruction of a step: w < 4 fills K rows 8w..8w+7, w >= 4
-    // fills V lines 8(w-4)..8(w-4)+7
-    auto issue = [&](unsigned char* __restrict__ kst, unsigned char* __restrict__ vst, int step) {
-      const int p = pb + step * 32;
-      if (w < 4) {
-        const int pos = 8 * w + (l >> 3);
-        const int ch = (l & 7) ^ kswz(pos);
-        int pp = p + pos;
-        pp = pp < pe ? pp : pe - 1;  // past the window: masked, but stay on staged blocks
-        const long long slot = (long long)s_bt[pp / bs - wb0] * bs + pp % bs;
-        __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void*)(Kc + (slot * a.Hkv + g) * 64 + ch * 8),
-            (__attribute__((address_space(3))) void*)(kst + w * 1024), 16, 0, 0);
-      } else {
-        const int line = 8 * (w - 4) + (l >> 3);
-        const int x = (l & 7) ^ (line & 3);
-        const int d = 2 * line + (x >> 2), ch = x & 3;
-        int pp = p + (ch >> 1) * 16;
-        pp = pp < pe ? pp : ((pe - 1) & ~15);
-        const long long blk = s_bt[pp / bs - wb0];
-        const int off = pp % bs + (ch & 1) * 8;
-        __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void*)(Vc + ((blk * a.Hkv + g) * 64 + d) * bs + off),
-            (__attribute__((address_space(3))) void*)(vst + (w - 4) * 1024), 16, 0, 0);
-      }
+    // the step position this lane fetches, clamped to the window: past its end
+    // the scores are masked, but the block id must be a staged one.  Its block
+    // id is read from LDS before the step's fragment reads, so waiting for it
+    // does not wait for them.
+    auto kpp = [&](int step) { return min(pb + step * 64 + 32 * dh + kpos, pe - 1); };
+    auto vpp = [&](int step) {
+      const int pp = pb + step * 64 + 32 * dh + (vch >> 1) * 16;
+      return pp < pe ? pp : ((pe - 1) & ~15);
+    };
+    auto issue = [&](unsigned char* __restrict__ kst, unsigned char* __restrict__ vst, int kp, int kb,
+                     int vp, int vb) {
+      const long long slot = ((long long)kb << bsl) + (kp & (bs - 1));
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(Kc + (slot * a.Hkv + g) * 64 + kch * 8),
+          (__attribute__((address_space(3))) void*)(kst + dh * HALF + ww * 1024), 16, 0, 0);
+      const int off = (vp & (bs - 1)) + (vch & 1) * 8;
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(Vc + ((((long long)vb * a.Hkv + g) * 64 + vd) << bsl) + off),
+          (__attribute__((address_space(3))) void*)(vst + dh * HALF + ww * 1024), 16, 0, 0);
+    };
+    auto issue_step = [&](unsigned char* __restrict__ kst, unsigned char* __restrict__ vst, int step) {
+      const int kp = kpp(step), vp = vpp(step);
+      issue(kst, vst, kp, s_bt[(kp >> bsl) - wb0], vp, s_bt[(vp >> bsl) - wb0]);
     };
 
-    if (0 < nsteps) issue(k0, v0, 0);
-    if (1 < nsteps) issue(k1, v1, 1);
-    if (2 < nsteps) issue(k2, v2, 2);
+    if (0 < nsteps) issue_step(k0, v0, 0);
+    if (1 < nsteps) issue_step(k1, v1, 1);
+    if (2 < nsteps) issue_step(k2, v2, 2);
     auto step = [&](const unsigned char* __restrict__ kcur, const unsigned char* __restrict__ vcur,
                     unsigned char* __restrict__ kref, unsigned char* __restrict__ vref, int st) {
+      // two DMA instructions per wave per step
       const int later = min(2, nsteps - 1 - st);
-      if (later >= 2) attn_wait_vmcnt<2>();
-      else if (later == 1) attn_wait_vmcnt<1>();
+      if (later >= 2) attn_wait_vmcnt<4>();
+      else if (later == 1) attn_wait_vmcnt<2>();
       else attn_wait_vmcnt<0>();
       asm volatile("s_barrier" ::: "memory");  // see the GEMM: no fence, DMA stays in flight
-      uint4 kf[2][2], vf[4];
+      const bool refill = st + 3 < nsteps;
+      int kp = 0, kb = 0, vp = 0, vb = 0;
+      if (refill) {
+        kp = kpp(st + 3);
+        vp = vpp(st + 3);
+        kb = s_bt[(kp >> bsl) - wb0];
+        vb = s_bt[(vp >> bsl) - wb0];
+      }
+      // the two 32-position halves of the step, one after the other (each with
+      // its own online-softmax update) so only one half's fragments are live
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) kf[pt][ks] = *reinterpret_cast<const uint4*>(kcur + koff[pt][ks]);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) vf[dt] = *reinterpret_cast<const uint4*>(vcur + voff[dt]);
-      if (st + 3 < nsteps) issue(kref, vref, st + 3);
-      const int pv0 = pb + st * 32 + 8 * gq;
-#pragma unroll
-      for (int qq = 0; qq < QPW; ++qq) {
-        if (w + 8 * qq >= QT) break;
-        f32x4 sc[2];
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          sc[pt] = mfma16(kf[pt][0], qf[qq][0], f32x4{0.f, 0.f, 0.f, 0.f});
-          sc[pt] = mfma16(kf[pt][1], qf[qq][1], sc[pt]);
-        }
-        // lane (gq, c): sc[pt][i] scores position pv0 + 4pt + i for query c
-        float v[8];
-        float mloc = -INFINITY;
+      for (int h = 0; h < 2; ++h) {
+        uint4 kf[2][2], vf[4];
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int pos = pv0 + 4 * pt + i;
-            const bool ok = qv[qq] && pos < pe && pos <= qpos[qq];
-            const float x = ok ? sc[pt][i] * sl2 : -INFINITY;
-            v[4 * pt + i] = x;
-            mloc = fmaxf(mloc, x);
+          for (int ks = 0; ks < 2; ++ks)
+            kf[pt][ks] = *reinterpret_cast<const uint4*>(kcur + h * HALF + koff[pt][ks]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vf[dt] = *reinterpret_cast<const uint4*>(vcur + h * HALF + voff[dt]);
+        if (h == 0 && refill) issue(kref, vref, kp, kb, vp, vb);
+        const int ph0 = pb + st * 64 + 32 * h, pv0 = ph0 + 8 * gq;
+#pragma unroll
+        for (int qq = 0; qq < QPW; ++qq) {
+          if (w + 8 * qq >= QT) break;
+          if (!qany[qq]) continue;  // every slot of this tile was rejected
+          f32x4 sc[2];
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt) {
+            sc[pt] = mfma16(kf[pt][0], qf[qq][0], f32x4{0.f, 0.f, 0.f, 0.f});
+            sc[pt] = mfma16(kf[pt][1], qf[qq][1], sc[pt]);
           }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const float mnew = fmaxf(m[qq], mloc);
-        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = exp2f(m[qq] - mref);
-        // P = hi + lo, both bf16: the PV product sees P to ~16 bits, the row
-        // sum takes the fp32 values themselves
-        uint32_t ph[4], pl[4];
-        float ps = 0.f;
+          // lane (gq, c): sc[pt][i] scores position pv0 + 4pt + i for query c
+          float v[8];
+          float mloc = -INFINITY;
+          if (ph0 + 31 < pe && ph0 + 31 <= qmin[qq]) {
+            // the whole half lies inside the window and before every valid
+            // query of the tile: no mask (invalid queries' results are unused)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float p0 = exp2f(v[2 * jj] - mref), p1 = exp2f(v[2 * jj + 1] - mref);
-          ps += p0 + p1;
-          ph[jj] = f2bf2(p0, p1);
-          pl[jj] = f2bf2(p0 - __uint_as_float(ph[jj] << 16), p1 - __uint_as_float(ph[jj] & 0xFFFF0000u));
-        }
-        lsum[qq] = lsum[qq] * alpha + ps;
-        m[qq] = mnew;
-        const uint4 pfh = {ph[0], ph[1], ph[2], ph[3]};
-        const uint4 pfl = {pl[0], pl[1], pl[2], pl[3]};
+            for (int t = 0; t < 8; ++t) {
+              v[t] = sc[t >> 2][t & 3] * sl2;
+              mloc = fmaxf(mloc, v[t]);
+            }
+          } else {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          o[qq][dt] = o[qq][dt] * alpha;
-          o[qq][dt] = mfma16(vf[dt], pfh, o[qq][dt]);
-          o[qq][dt] = mfma16(vf[dt], pfl, o[qq][dt]);
+            for (int t = 0; t < 8; ++t) {
+              const int pos = pv0 + t;
+              const bool ok = qv[qq] && pos < pe && pos <= qpos[qq];
+              v[t] = ok ? sc[t >> 2][t & 3] * sl2 : -INFINITY;
+              mloc = fmaxf(mloc, v[t]);
+            }
+          }
+          mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+          mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+          const float mnew = fmaxf(m[qq], mloc);
+          const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+          // P = hi + lo, both bf16: the PV product sees P to ~16 bits, the row
+          // sum takes the fp32 values themselves.  exp2 of a non-positive
+          // argument: v_exp_f32 flushes results below 2^-126 to 0.
+          uint32_t ph[4], pl[4];
+          float ps = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float p0 = __builtin_amdgcn_exp2f(v[2 * jj] - mref);
+            const float p1 = __builtin_amdgcn_exp2f(v[2 * jj + 1] - mref);
+            ps += p0 + p1;
+            ph[jj] = f2bf2(p0, p1);
+            pl[jj] = f2bf2(p0 - __uint_as_float(ph[jj] << 16), p1 - __uint_as_float(ph[jj] & 0xFFFF0000u));
+          }
+          if (__ballot(mnew != m[qq])) {  // some query's running max moved: rescale
+            const float alpha = __builtin_amdgcn_exp2f(m[qq] - mref);
+            lsum[qq] = lsum[qq] * alpha + ps;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[qq][dt] = o[qq][dt] * alpha;
+          } else {
+            lsum[qq] += ps;
+          }
+          m[qq] = mnew;
+          const uint4 pfh = {ph[0], ph[1], ph[2], ph[3]};
+          const uint4 pfl = {pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            o[qq][dt] = mfma16(vf[dt], pfh, o[qq][dt]);
+            o[qq][dt] = mfma16(vf[dt], pfl, o[qq][dt]);
+          }
         }
       }
     };
@@ -284,7 +333,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
       if (st + 2 < nsteps) step(k2, v2, k1, v1, st + 2);
       if (st + 3 < nsteps) step(k3, v3, k2, v2, st + 3);
     }
-    __syncthreads();  // stages and s_bt are reused by the next window
+    __syncthreads();  // stages and s_bt are reused by the next window (or the transpose below)
     }  // windows
 
     // partials: O (un-normalised), running max m (base 2) and sum l per query
@@ -298,7 +347,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_ot[w][16 * dt + 4 * gq + i][c] = o[qq][dt][i];
+        for (int i = 0; i < 4; ++i) s_ot[(16 * dt + 4 * gq + i) * 17 + c] = o[qq][dt][i];
       wave_lds_sync();
       const int qi = l >> 2, d0 = (l & 3) * 16, qg = t * 16 + qi;
       if (qg < QN) {
@@ -306,10 +355,10 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
           float4 f;
-          f.x = s_ot[w][d0 + 4 * v4 + 0][qi];
-          f.y = s_ot[w][d0 + 4 * v4 + 1][qi];
-          f.z = s_ot[w][d0 + 4 * v4 + 2][qi];
-          f.w = s_ot[w][d0 + 4 * v4 + 3][qi];
+          f.x = s_ot[(d0 + 4 * v4 + 0) * 17 + qi];
+          f.y = s_ot[(d0 + 4 * v4 + 1) * 17 + qi];
+          f.z = s_ot[(d0 + 4 * v4 + 2) * 17 + qi];
+          f.w = s_ot[(d0 + 4 * v4 + 3) * 17 + qi];
           *reinterpret_cast<float4*>(dst + 4 * v4) = f;
         }
       }

@@ -74,7 +74,7 @@ typedef struct pe_config {
   int32_t mlp;          /* MLP size I, multiple of 32 */
   int32_t layers;       /* decoder layers N >= 1 */
   int32_t vocab;        /* V, multiple of 16 */
-  int32_t block_size;   /* KV page size in tokens, multiple of 16 */
+  int32_t block_size;   /* KV page size in tokens, a power of two >= 16 */
   int32_t mask_id;      /* token id of MASK; its embedding row is emb(mask) [P1, Step 2] */
   int32_t dtype;        /* pe_dtype */
   float rms_eps;        /* RMSNorm epsilon */

@@ -216,6 +216,11 @@ def test_invalid_arguments_are_rejected_on_the_host():
         assert e.value.status == 1
         with pytest.raises(pb.PeError):
             pb._check(pb._lib.pe_verify(st.ctx.h, 1, None, None, None, None))
+        # KV pages must be a power of two of at least 16 tokens
+        for bsz in (48, 8):
+            with pytest.raises(pb.PeError) as e:
+                pb.Context(w.with_(block_size=bsz), st.dev, max_num_seqs=1)
+            assert e.value.status == 4  # PE_ERR_UNSUPPORTED
     finally:
         st.close()
 
