@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--no-c64", action="store_true", help="skip the c=64 measurement")
     p.add_argument("--no-ksweep", action="store_true",
                    help="skip the K sweep of the 4-layer d=2048 drafter")
+    p.add_argument("--no-ar", action="store_true",
+                   help="skip the sequential (autoregressive) comparison")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -134,7 +136,7 @@ def measured_traffic(workload):
 # ---------------------------------------------------------------------------
 # GPU measurement
 # ---------------------------------------------------------------------------
-def measure(w, steps, warmup, prm=None, dev=None, label=""):
+def measure(w, steps, warmup, prm=None, dev=None, label="", with_ar=True):
     import numpy as np
     import torch
     from drafting_pe_prepare_amd import binding as pb
@@ -187,30 +189,32 @@ def measure(w, steps, warmup, prm=None, dev=None, label=""):
           file=sys.stderr, flush=True)
 
     # the sequential comparison: the same kernels as K drafting passes, one graph
-    ar_args = pb.make_step_args(t["verify_tokens"], t["verify_positions"], t["num_accepted"],
-                                t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], batch,
-                                t["target_hidden"], dev["h_shared"], dh, ks, vs, tok,
-                                t["target_tokens"], acc, bon, mode=pb.STEP_AUTOREGRESSIVE)
-    ar_steps = max(10, steps // 4)
-    for _ in range(max(3, warmup // 4)):
-        pb.pe_step_graph(ctx, B, ar_args)
-    torch.cuda.synchronize()
-    ta = time.perf_counter()
-    for _ in range(ar_steps):
-        pb.pe_step_graph(ctx, B, ar_args)
-    torch.cuda.synchronize()
-    ar_ms = (time.perf_counter() - ta) * 1e3 / ar_steps
-    err = pb.pe_get_device_error(ctx)
-    assert err == (0, -1), f"device error word {err}"
-    print(f"[bench] {label} sequential: {ar_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-    ar_bytes = ar_work(w, inp)
-    ar = {"value": B * K / (ar_ms * 1e-3), "us_per_step": ar_ms * 1e3, "steps": ar_steps,
-          "passes": K, "algorithmic_bytes": ar_bytes,
-          "hbm_GBs": ar_bytes / (ar_ms * 1e-3) / 1e9,
-          "hbm_frac": ar_bytes / (ar_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-          "parallel_speedup": ar_ms / ms_step,
-          "mode": "pe_ar_draft: copied slots, then K-1 one-slot passes fed with the drafter's "
-                  "residual stream; same kernels, one graph per step"}
+    ar = None
+    if with_ar:
+        ar_args = pb.make_step_args(t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                                    t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], batch,
+                                    t["target_hidden"], dev["h_shared"], dh, ks, vs, tok,
+                                    t["target_tokens"], acc, bon, mode=pb.STEP_AUTOREGRESSIVE)
+        ar_steps = max(10, steps // 4)
+        for _ in range(max(3, warmup // 4)):
+            pb.pe_step_graph(ctx, B, ar_args)
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for _ in range(ar_steps):
+            pb.pe_step_graph(ctx, B, ar_args)
+        torch.cuda.synchronize()
+        ar_ms = (time.perf_counter() - ta) * 1e3 / ar_steps
+        err = pb.pe_get_device_error(ctx)
+        assert err == (0, -1), f"device error word {err}"
+        print(f"[bench] {label} sequential: {ar_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        ar_bytes = ar_work(w, inp)
+        ar = {"value": B * K / (ar_ms * 1e-3), "us_per_step": ar_ms * 1e3, "steps": ar_steps,
+              "passes": K, "algorithmic_bytes": ar_bytes,
+              "hbm_GBs": ar_bytes / (ar_ms * 1e-3) / 1e9,
+              "hbm_frac": ar_bytes / (ar_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+              "parallel_speedup": ar_ms / ms_step,
+              "mode": "pe_ar_draft: copied slots, then K-1 one-slot passes fed with the drafter's "
+                      "residual stream; same kernels, one graph per step"}
 
     # eager pass with per-phase HIP events on the library's stream
     pb.pe_profile_enable(ctx, True)
@@ -347,7 +351,7 @@ def main():
     pb.load()
     assert torch.cuda.is_available(), "no GPU"
     w = configs.BY_NAME[args.workload]
-    main_res, prm, dev = measure(w, args.steps, args.warmup, label=w.name)
+    main_res, prm, dev = measure(w, args.steps, args.warmup, label=w.name, with_ar=not args.no_ar)
     line = {
         "metric": METRIC,
         "value": main_res["value"],
@@ -372,7 +376,7 @@ def main():
     }
     if not args.no_c64 and w.name == "c1_20b":
         c64, _, _ = measure(configs.C64, max(20, args.steps // 4), max(5, args.warmup // 4),
-                            prm=prm, dev=dev, label="c64_20b")
+                            prm=prm, dev=dev, label="c64_20b", with_ar=not args.no_ar)
         line["c64"] = {k: c64[k] for k in ("value", "us_per_step", "roofline", "step",
                                             "autoregressive", "phases_us_per_step", "config")}
         line["c64"]["config"]["weights"] = "same drafter weights as the c=1 workload"
