@@ -419,6 +419,65 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
+// One wave per (slot, KV head): lane l combines query head (l G)/64 of the
+// group, dims (l G) % 64 .. +G.  A chunk's partials for the G heads of a slot
+// are one contiguous block of G x 64 floats, so every lane reads G consecutive
+// floats per chunk and the chunks' loads are independent.  G is a power of
+// two <= 16 (attn_merge_kernel serves other groupings).
+template <int G>
+__global__ __launch_bounds__(256) void attn_merge_group_kernel(AttnArgs a) {
+  __shared__ int s_off[kMaxB + 1];
+  int CH;
+  attn_plan(a.seq_lens, a.B, a.Hkv, a.target_items, s_off, CH);
+  const int QN = a.S * G;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int hl = (l * G) >> 6, d0 = (l * G) & 63;
+  const long long total = (long long)a.B * a.S * a.Hkv;
+  uint16_t* out = (uint16_t*)a.out;
+  for (long long x = (long long)blockIdx.x * 4 + w; x < total; x += (long long)gridDim.x * 4) {
+    const int row = int(x / a.Hkv), g = int(x % a.Hkv);
+    const int r = row / a.S, s = row % a.S, q = s * G + hl;
+    uint16_t* dst = out + ((long long)row * a.Hq + g * G + hl) * 64 + d0;
+    float O[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) O[j] = 0.f;
+    float L = 0.f;
+    if (!a.rej[row] && a.seq_lens[r] > 0) {
+      const int c0 = s_off[r], nc = s_off[r + 1] - c0;
+      auto item = [&](int ch) { return (long long)(c0 + ch) * a.Hkv + g; };
+      float M = -INFINITY;
+      for (int ch = 0; ch < nc; ++ch) M = fmaxf(M, a.part_ml[(item(ch) * QN + q) * 2]);
+      if (M != -INFINITY) {
+#pragma unroll 4
+        for (int ch = 0; ch < nc; ++ch) {
+          const long long it = item(ch);
+          const float mc = a.part_ml[(it * QN + q) * 2], lc = a.part_ml[(it * QN + q) * 2 + 1];
+          const float wgt = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+          L += wgt * lc;
+          const float* po = a.part_o + (it * QN + q) * 64 + d0;
+          if constexpr (G % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < G; j += 4) {
+              const float4 v = *reinterpret_cast<const float4*>(po + j);
+              O[j] += wgt * v.x; O[j + 1] += wgt * v.y; O[j + 2] += wgt * v.z; O[j + 3] += wgt * v.w;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j) O[j] += wgt * po[j];
+          }
+        }
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if constexpr (G == 1) {
+      dst[0] = f2bf(O[0] * inv);
+    } else {
+#pragma unroll
+      for (int j = 0; j < G; j += 2) *reinterpret_cast<uint32_t*>(dst + j) = f2bf2(O[j] * inv, O[j + 1] * inv);
+    }
+  }
+}
+
 // fp32, any head_dim <= 128: one 64-thread workgroup per (slot, query head),
 // threads stride over positions with their own online softmax, then combine.
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
@@ -491,10 +550,19 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  long long waves = (long long)a.B * a.S * a.Hq;
+  const int G = a.Hq / a.Hkv;
+  const long long waves = (long long)a.B * a.S * (G <= 16 && (G & (G - 1)) == 0 ? a.Hkv : a.Hq);
   long long blocks = (waves + 3) / 4;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, a);
+  const dim3 mg((unsigned)blocks), mb(256);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(attn_merge_group_kernel<1>, mg, mb, 0, st, a); break;
+    case 2: hipLaunchKernelGGL(attn_merge_group_kernel<2>, mg, mb, 0, st, a); break;
+    case 4: hipLaunchKernelGGL(attn_merge_group_kernel<4>, mg, mb, 0, st, a); break;
+    case 8: hipLaunchKernelGGL(attn_merge_group_kernel<8>, mg, mb, 0, st, a); break;
+    case 16: hipLaunchKernelGGL(attn_merge_group_kernel<16>, mg, mb, 0, st, a); break;
+    default: hipLaunchKernelGGL(attn_merge_kernel, mg, mb, 0, st, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -86,6 +86,14 @@ def test_small_multilayer(dtype, layers, K, B, seed):
     _full_check(w, seed)
 
 
+@pytest.mark.parametrize("hq,hkv,seed", [(2, 2, 91), (8, 2, 92), (16, 1, 93)])
+def test_small_bf16_head_groups(hq, hkv, seed):
+    """1, 4 and 16 query heads per KV head (the merge combines a whole group per wave)."""
+    w = SMALL_BF16.with_(K=5, batch=3, n_q_heads=hq, n_kv_heads=hkv, accepted="uniform",
+                         prefix=("uniform", 30, 600))
+    _full_check(w, seed)
+
+
 @pytest.mark.parametrize("K,B,mlp,seed", [(4, 5, 2048, 81), (7, 12, 16384, 82)])
 def test_small_bf16_tile_variants(K, B, mlp, seed):
     """A wider MLP reaches the other GEMM variants: 40 rows with a 4096-column
