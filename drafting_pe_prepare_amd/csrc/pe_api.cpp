@@ -259,7 +259,10 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
     free_ctx(c);
     return hipfail(e, "device query");
   }
-  c->target_items = 4 * c->num_cus;
+#ifndef PE_ATTN_ITEMS_PER_CU
+#define PE_ATTN_ITEMS_PER_CU 4
+#endif
+  c->target_items = PE_ATTN_ITEMS_PER_CU * c->num_cus;  // split-KV work items per attention launch
 
   const pe_config& k = c->cfg;
   const size_t R = size_t(k.max_num_seqs) * 2 * k.K, D = size_t(k.max_num_seqs) * k.K;

@@ -86,6 +86,25 @@ def test_small_multilayer(dtype, layers, K, B, seed):
     _full_check(w, seed)
 
 
+@pytest.mark.parametrize("prefix,seed", [(("fixed", 0, 0), 101), (("uniform", 8150, 9300), 102)])
+def test_small_bf16_prefix_edges(prefix, seed):
+    """An empty cached prefix (the first draft round after the prompt: every
+    position comes from this pass), and prefixes that cross the 8192-position
+    block-id window of the attention kernel."""
+    w = SMALL_BF16.with_(K=4, batch=3, n_q_heads=8, n_kv_heads=1, accepted="uniform", prefix=prefix)
+    _full_check(w, seed)
+
+
+@pytest.mark.slow
+def test_max_batch_and_depth_sampled():
+    """The largest shape the context takes: 1024 requests at K=32 (65536
+    forward rows, 32768 draft rows) on a small drafter; metadata, gathered
+    hidden rows and verify for all requests, tokens and logits for sampled
+    requests."""
+    w = SMALL_BF16.with_(K=32, batch=1024, accepted="uniform", prefix=("uniform", 16, 80))
+    _full_check(w, 103, requests=[0, 511, 1023], logits=True)
+
+
 @pytest.mark.parametrize("hq,hkv,seed", [(2, 2, 91), (8, 2, 92), (16, 1, 93)])
 def test_small_bf16_head_groups(hq, hkv, seed):
     """1, 4 and 16 query heads per KV head (the merge combines a whole group per wave)."""
