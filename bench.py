@@ -41,6 +41,8 @@ def parse():
                    help="skip the K sweep of the 4-layer d=2048 drafter")
     p.add_argument("--no-ar", action="store_true",
                    help="skip the sequential (autoregressive) comparison")
+    p.add_argument("--no-maxbatch", action="store_true",
+                   help="skip the B=256 largest-graph workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -380,6 +382,11 @@ def main():
         line["c64"] = {k: c64[k] for k in ("value", "us_per_step", "roofline", "step",
                                             "autoregressive", "phases_us_per_step", "config")}
         line["c64"]["config"]["weights"] = "same drafter weights as the c=1 workload"
+    if not args.no_maxbatch and w.name == "c1_20b":
+        mb, _, _ = measure(configs.MAXB, max(10, args.steps // 10), 3, prm=prm, dev=dev,
+                           label="maxbatch_20b", with_ar=False)
+        line["maxbatch"] = {k: mb[k] for k in ("value", "us_per_step", "step", "phases_us_per_step", "config")}
+        line["maxbatch"]["config"]["weights"] = "same drafter weights as the c=1 workload"
     if not args.no_ksweep and w.name == "c1_20b":
         line["ksweep"] = ksweep(max(20, args.steps // 5), max(3, args.warmup // 4))
     if not args.no_cpu_baseline:
