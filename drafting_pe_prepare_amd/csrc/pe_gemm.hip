@@ -446,8 +446,8 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // bf16, M > 16: BM x BN tiles over k-tiles of 64 in an S-stage LDS ring filled
 // by global_load_lds_dwordx4 (global -> LDS with no staging registers).
-// S = 2 leaves room for two workgroups per CU; S = 3 prefetches one k-tile
-// further for grids that put at most one workgroup on a CU.
+// S = 3 prefetches one k-tile further; the 64-row tiles that use it still fit
+// two workgroups per CU.
 //
 // One DMA instruction moves 8 whole tile rows: 128 bytes (64 bf16 of k) per
 // row, 16 bytes per lane.  Rows split into half lines (32-wide k-tiles) stream
@@ -473,7 +473,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int S>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(S == 2 ? 2 : 1, S == 2 ? 2 : 1)))
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;   // MFMA tiles per wave
@@ -787,9 +787,11 @@ hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_
 //  * Dense, up to 16 rows: split-K over waves (weights from the fragment-order copy).
 //  * Dense, 17..64 rows: tiled 64x128 when there are >= 32 column tiles,
 //    split-K otherwise (few tiles leave most CUs idle).
-//  * Dense, more rows: tiled 128x128; two stages and two workgroups per CU when
-//    the tiles outnumber the CUs, three stages and one workgroup otherwise.
-enum Variant { V_WIDE, V_SKINNY, V_A64, V_A128, V_A256, V_D64, V_D128S2, V_D128S3 };
+//  * Dense, more rows: tiled 128x128 with two stages and two workgroups per CU
+//    when those tiles outnumber the CUs; otherwise 64x128 tiles (three stages,
+//    two workgroups per CU), which spread a small grid over more CUs (fc, O and
+//    down at c=64, cache-cold weights: 50/38/69 us against 59/43/76 us).
+enum Variant { V_WIDE, V_SKINNY, V_A64, V_A128, V_A256, V_D64, V_D128S2 };
 static Variant pick(int epi, int M, int N, int K, int num_cus) {
   if (epi == E_ARGMAX) {
     const size_t wide_lds = size_t(M) * (K / 8 + 1) * 16;
@@ -800,7 +802,7 @@ static Variant pick(int epi, int M, int N, int K, int num_cus) {
   if (M <= 16) return V_SKINNY;
   if (M <= 64) return (N + 127) / 128 >= 32 ? V_D64 : V_SKINNY;
   const long long tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
-  return tiles > num_cus ? V_D128S2 : V_D128S3;
+  return tiles > num_cus ? V_D128S2 : V_D64;
 }
 constexpr int kArgmaxBN = 256;  // columns per tile of every tiled LM-head variant
 
@@ -889,8 +891,7 @@ static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
         if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
         return run_skinny<EPI, AL, BMAP, 4>(g, st);
       case V_D64: return run_tiled<EPI, AL, BMAP, 64, 128, 1, 4, 3>(g, st);
-      case V_D128S2: return run_tiled<EPI, AL, BMAP, 128, 128, 2, 2, 2>(g, st);
-      default: return run_tiled<EPI, AL, BMAP, 128, 128, 2, 2, 3>(g, st);
+      default: return run_tiled<EPI, AL, BMAP, 128, 128, 2, 2, 2>(g, st);
     }
   }
 }
