@@ -66,8 +66,7 @@ struct pe_ctx {
   uint32_t* err = nullptr;    // [2] kinds, first request
   float* part_o = nullptr;
   float* part_ml = nullptr;
-  float* rope_inv = nullptr;
-  double* rope_inv_d = nullptr;
+  double* rope_turns = nullptr;  // RoPE frequencies in turns per position
   void* lm_packed = nullptr;  // fragment-order copy of the LM head (bf16)
   // fragment-order copies of the small-batch GEMM weights (bf16): fc, then per
   // layer qkv (RoPE-paired columns), o, gate/up (paired), down
@@ -139,7 +138,7 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->rope_inv, c->rope_inv_d, c->lm_packed};
+                  c->part_o, c->part_ml, c->rope_turns, c->lm_packed};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   if (c->fc_packed) (void)hipFree(c->fc_packed);
@@ -284,8 +283,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {&c->z, D * k.d * c->esz, "z"},
       {reinterpret_cast<void**>(&c->keys), key_slots * 8, "argmax keys"},
       {reinterpret_cast<void**>(&c->err), 16, "err"},
-      {reinterpret_cast<void**>(&c->rope_inv), size_t(k.head_dim / 2) * 4, "rope"},
-      {reinterpret_cast<void**>(&c->rope_inv_d), size_t(k.head_dim / 2) * 8, "rope_d"},
+      {reinterpret_cast<void**>(&c->rope_turns), size_t(k.head_dim / 2) * 8, "rope"},
       {reinterpret_cast<void**>(&c->ar_ids), R1 * 4, "ar ids"},
       {reinterpret_cast<void**>(&c->ar_pos), R1 * 4, "ar positions"},
       {reinterpret_cast<void**>(&c->ar_rows), size_t(k.max_num_seqs) * 4, "ar rows"},
@@ -304,16 +302,13 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       return s;
     }
   }
-  // RoPE inverse frequencies theta^(-2i/hd), computed in double
-  std::vector<float> inv(k.head_dim / 2);
-  std::vector<double> invd(k.head_dim / 2);
-  for (int i = 0; i < k.head_dim / 2; ++i) {
-    invd[i] = std::pow(double(k.rope_theta), -2.0 * i / double(k.head_dim));
-    inv[i] = float(invd[i]);
-  }
+  // RoPE frequencies theta^(-2i/hd) in turns per position (divided by 2 pi), in double
+  std::vector<double> turns(k.head_dim / 2);
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < k.head_dim / 2; ++i)
+    turns[i] = std::pow(double(k.rope_theta), -2.0 * i / double(k.head_dim)) / two_pi;
   const uint32_t err0[4] = {0u, 0xFFFFFFFFu, 0u, 0u};
-  e = hipMemcpy(c->rope_inv, inv.data(), inv.size() * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(c->rope_inv_d, invd.data(), invd.size() * 8, hipMemcpyHostToDevice);
+  e = hipMemcpy(c->rope_turns, turns.data(), turns.size() * 8, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->err, err0, 16, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     free_ctx(c);
@@ -484,7 +479,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.Wp = packed(ctx, l, 0);
       g.positions = P.pos; g.slots = P.slots;
       g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
-      g.rope_inv = ctx->rope_inv; g.rope_inv_d = ctx->rope_inv_d;
+      g.rope_turns = ctx->rope_turns;
       Timed tm(ctx, PE_PH_QKV);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, ctx->num_cus, st), "qkv");
     }

@@ -80,13 +80,14 @@ struct ARow {
 // ---------------------------------------------------------------------------
 // epilogues on an fp32 tile in LDS: tile[i*ldt + c] = out[m0+i, n0+c] (logical)
 // ---------------------------------------------------------------------------
-__device__ __attribute__((noinline)) void rope_sincos(const GemmArgs& g, int pos, int i, float& cs,
-                                                     float& sn) {
-  // angle = pos * theta^(-2i/hd), reduced to [-pi, pi] in double, then fp32 sincos
-  const double TWO_PI = 6.283185307179586476925286766559;
-  double ang = double(pos) * g.rope_inv_d[i];
-  ang -= TWO_PI * rint(ang / TWO_PI);
-  sincosf(float(ang), &sn, &cs);
+__device__ __forceinline__ void rope_sincos(const GemmArgs& g, int pos, int i, float& cs, float& sn) {
+  // angle pos * theta^(-2i/hd) in turns: the fp64 product minus its nearest
+  // integer is the exact fraction of a turn for any position; v_sin_f32 and
+  // v_cos_f32 take turns (max abs error 1.3e-7 on [-1/2, 1/2], measured)
+  const double t = double(pos) * g.rope_turns[i];
+  const float x = float(t - rint(t));
+  sn = __builtin_amdgcn_sinf(x);
+  cs = __builtin_amdgcn_cosf(x);
 }
 
 // Per-element epilogues.  epi_one: one logical column n of row m (E_STORE,
@@ -105,22 +106,24 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& g, int m, int nb, int c
     const float v = lo / (1.0f + expf(-lo)) * hi;
     Elt<T>::st((T*)g.out + (long long)m * g.ldo + (nb >> 1) + c, v);
   } else if (EPI == E_QKV) {
+    // bf16 storage implies head_dim 64 (checked at context creation)
+    const int hd = sizeof(T) == 2 ? 64 : g.hd;
     if (nb < g.nq + g.nk) {
       const bool isq = nb < g.nq;
       const int j = isq ? nb : nb - g.nq;
-      const int head = j / g.hd, s = (j % g.hd) >> 4;
-      const int dlo = (s >> 1) * 16 + c, dhi = dlo + (g.hd >> 1);
+      const int head = j / hd, s = (j % hd) >> 4;
+      const int dlo = (s >> 1) * 16 + c, dhi = dlo + (hd >> 1);
       float cs, sn;
       rope_sincos(g, g.positions[m], dlo, cs, sn);
       const float olo = lo * cs - hi * sn, ohi = hi * cs + lo * sn;
       if (isq) {
-        T* q = (T*)g.qout + ((long long)m * (g.nq / g.hd) + head) * g.hd;
+        T* q = (T*)g.qout + ((long long)m * (g.nq / hd) + head) * hd;
         Elt<T>::st(q + dlo, olo);
         Elt<T>::st(q + dhi, ohi);
       } else {
         const long long slot = g.slots[m];
         if (slot >= 0 && slot < g.num_slots) {
-          T* kp = (T*)g.kcache + (slot * g.Hkv + head) * g.hd;
+          T* kp = (T*)g.kcache + (slot * g.Hkv + head) * hd;
           Elt<T>::st(kp + dlo, olo);
           Elt<T>::st(kp + dhi, ohi);
         }
@@ -129,11 +132,12 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& g, int m, int nb, int c
       const long long slot = g.slots[m];
       if (slot >= 0 && slot < g.num_slots) {
         const int j = nb - g.nq - g.nk;
-        const int head = j / g.hd, jb = j % g.hd;
-        const long long blk = slot / g.block_size, off = slot % g.block_size;
-        T* vp = (T*)g.vcache + ((blk * g.Hkv + head) * g.hd) * g.block_size + off;
-        Elt<T>::st(vp + (long long)(jb + c) * g.block_size, lo);
-        Elt<T>::st(vp + (long long)(jb + 16 + c) * g.block_size, hi);
+        const int head = j / hd, jb = j % hd;
+        const int bsl = __builtin_ctz(g.block_size);  // a power of two (checked at context creation)
+        const long long blk = slot >> bsl, off = slot & (g.block_size - 1);
+        T* vp = (T*)g.vcache + (((blk * g.Hkv + head) * hd) << bsl) + off;
+        Elt<T>::st(vp + ((long long)(jb + c) << bsl), lo);
+        Elt<T>::st(vp + ((long long)(jb + 16 + c) << bsl), hi);
       }
     }
   }

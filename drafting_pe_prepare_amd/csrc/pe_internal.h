@@ -70,8 +70,7 @@ struct GemmArgs {
   const int32_t* positions; const int64_t* slots; // E_QKV
   void* qout; void* kcache; void* vcache;
   int Hkv, hd, block_size; long long num_slots;
-  const float* rope_inv;  // [hd/2] inverse frequencies (float)
-  const double* rope_inv_d;  // [hd/2] the same in double (angle reduction)
+  const double* rope_turns;  // [hd/2] theta^(-2i/hd) / (2 pi): RoPE angle per position, in turns
   uint64_t* keys; int parts;                      // E_ARGMAX: keys[row * parts + part]
   int32_t* tokens; float* logits; int ldl;         // logits[row * ldl + n]
   const int32_t* seq_lens; int Kd;
