@@ -363,10 +363,14 @@ pe_status pe_set_stream(pe_ctx* ctx, void* stream) {
   return PE_OK;
 }
 
-pe_status pe_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_tokens,
-                     const int32_t* verify_positions, const int32_t* num_accepted,
-                     const int32_t* bonus_tokens, const int32_t* block_table, int32_t max_blocks,
-                     int32_t num_kv_blocks, const pe_batch* out) {
+}  // extern "C"
+
+// Checks the arguments of a preparation and fills its kernel arguments.
+static pe_status prepare_args(pe_ctx* ctx, int32_t B, const int32_t* verify_tokens,
+                              const int32_t* verify_positions, const int32_t* num_accepted,
+                              const int32_t* bonus_tokens, const int32_t* block_table,
+                              int32_t max_blocks, int32_t num_kv_blocks, const pe_batch* out,
+                              pe::PrepareArgs& a) {
   pe_status s = check_B(ctx, B);
   if (s != PE_OK) return s;
   if ((s = check_batch(out)) != PE_OK) return s;
@@ -374,7 +378,6 @@ pe_status pe_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_tokens,
   if (!verify_tokens || !verify_positions || !num_accepted || !bonus_tokens || !block_table)
     return fail(PE_ERR_INVALID_ARG, "a prepare input is NULL");
   if (max_blocks < 1 || num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "max_blocks/num_kv_blocks < 1");
-  pe::PrepareArgs a;
   a.B = B;
   a.K = ctx->cfg.K;
   a.vocab = ctx->cfg.vocab;
@@ -396,13 +399,11 @@ pe_status pe_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_tokens,
   a.msk = out->is_masked;
   a.slots = out->slot_mapping;
   a.err = ctx->err;
-  Timed tm(ctx, PE_PH_PREPARE);
-  PE_HIP(pe::launch_prepare(a, ctx->stream), "prepare launch");
   return PE_OK;
 }
 
-pe_status pe_gather_hidden(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* target_hidden,
-                           const void* h_shared, void* draft_hidden) {
+static pe_status check_gather(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* target_hidden,
+                              const void* h_shared, void* draft_hidden) {
   pe_status s = check_B(ctx, B);
   if (s != PE_OK) return s;
   if (!batch || !batch->hidden_src) return fail(PE_ERR_INVALID_ARG, "batch.hidden_src is NULL");
@@ -410,6 +411,28 @@ pe_status pe_gather_hidden(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
   if (!target_hidden || !h_shared || !draft_hidden || !aligned(target_hidden, 16) ||
       !aligned(h_shared, 16) || !aligned(draft_hidden, 16))
     return fail(PE_ERR_INVALID_ARG, "hidden buffers NULL or not 16-byte aligned");
+  return PE_OK;
+}
+
+extern "C" {
+
+pe_status pe_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_tokens,
+                     const int32_t* verify_positions, const int32_t* num_accepted,
+                     const int32_t* bonus_tokens, const int32_t* block_table, int32_t max_blocks,
+                     int32_t num_kv_blocks, const pe_batch* out) {
+  pe::PrepareArgs a;
+  pe_status s = prepare_args(ctx, B, verify_tokens, verify_positions, num_accepted, bonus_tokens,
+                             block_table, max_blocks, num_kv_blocks, out, a);
+  if (s != PE_OK || B == 0) return s;
+  Timed tm(ctx, PE_PH_PREPARE);
+  PE_HIP(pe::launch_prepare(a, ctx->stream), "prepare launch");
+  return PE_OK;
+}
+
+pe_status pe_gather_hidden(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* target_hidden,
+                           const void* h_shared, void* draft_hidden) {
+  pe_status s = check_gather(ctx, B, batch, target_hidden, h_shared, draft_hidden);
+  if (s != PE_OK || B == 0) return s;
   const int K = ctx->cfg.K;
   Timed tm(ctx, PE_PH_GATHER);
   PE_HIP(pe::launch_gather(B * 2 * K, B * (K + 1), int(ctx->cfg.d * ctx->esz), batch->hidden_src,
@@ -434,6 +457,9 @@ struct Pass {
   int tstride;
   float* logits;       // draft row i -> logits[i * ldl ...], or NULL
   int ldl;
+  // when set (tstride 1, Kd = K): greedy verification fused into the argmax
+  const int32_t* vtarget = nullptr;
+  int32_t *vacc = nullptr, *vbonus = nullptr;
 };
 
 static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_table,
@@ -552,8 +578,13 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
     }
     Timed tm(ctx, PE_PH_ARGMAX);
-    PE_HIP(pe::launch_argmax_tokens(D, P.Kd, g.parts, ctx->keys, P.tokens, P.tstride, P.seq_lens, st),
-           "argmax");
+    if (P.vtarget)
+      PE_HIP(pe::launch_argmax_verify(B, P.Kd, g.parts, ctx->keys, P.tokens, P.seq_lens, P.vtarget,
+                                      P.vacc, P.vbonus, st),
+             "argmax + verify");
+    else
+      PE_HIP(pe::launch_argmax_tokens(D, P.Kd, g.parts, ctx->keys, P.tokens, P.tstride, P.seq_lens, st),
+             "argmax");
   }
   return PE_OK;
 }
@@ -655,14 +686,49 @@ pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens, const i
   return PE_OK;
 }
 
+// The parallel step with two launch fusions (preparation + hidden-state copy,
+// argmax + verification); every argument is checked as the four entry points
+// check it, and the results are the same.
+static pe_status run_parallel_step(pe_ctx* ctx, int32_t B, const pe_step_args* a) {
+  pe::PrepareArgs pa;
+  pe_status s = prepare_args(ctx, B, a->verify_tokens, a->verify_positions, a->num_accepted,
+                             a->bonus_tokens, a->block_table, a->max_blocks, a->num_kv_blocks,
+                             &a->batch, pa);
+  if (s != PE_OK) return s;
+  if ((s = check_gather(ctx, B, &a->batch, a->target_hidden, a->h_shared, a->draft_hidden)) != PE_OK)
+    return s;
+  if ((s = check_forward(ctx, B, &a->batch, a->draft_hidden, a->block_table, a->max_blocks,
+                         a->num_kv_blocks, a->k_cache, a->v_cache, a->draft_tokens, a->logits)) != PE_OK)
+    return s;
+  if (B == 0) return PE_OK;
+  if (!a->target_tokens || !a->accepted_out || !a->bonus_out)
+    return fail(PE_ERR_INVALID_ARG, "a verify buffer is NULL");
+  const int K = ctx->cfg.K;
+  {
+    Timed tm(ctx, PE_PH_PREPARE);
+    PE_HIP(pe::launch_prepare_gather(pa, int(ctx->cfg.d * ctx->esz), a->target_hidden, a->h_shared,
+                                     a->draft_hidden, ctx->stream),
+           "prepare + gather launch");
+  }
+  Pass P;
+  P.B = B; P.S = 2 * K; P.Kd = K;
+  P.ids = a->batch.input_ids; P.pos = a->batch.positions; P.draft_rows = a->batch.draft_rows;
+  P.seq_lens = a->batch.seq_lens; P.rej = a->batch.is_rejected; P.slots = a->batch.slot_mapping;
+  P.hidden = a->draft_hidden;
+  P.tokens = a->draft_tokens; P.tstride = 1;
+  P.logits = a->logits; P.ldl = ctx->cfg.vocab;
+  P.vtarget = a->target_tokens; P.vacc = a->accepted_out; P.vbonus = a->bonus_out;
+  return forward_pass(ctx, P, a->block_table, a->max_blocks, a->num_kv_blocks, a->k_cache, a->v_cache);
+}
+
 static pe_status run_step(pe_ctx* ctx, int32_t B, const pe_step_args* a) {
+  if (a->mode == PE_STEP_PARALLEL) return run_parallel_step(ctx, B, a);
   pe_status s = pe_prepare(ctx, B, a->verify_tokens, a->verify_positions, a->num_accepted,
                            a->bonus_tokens, a->block_table, a->max_blocks, a->num_kv_blocks, &a->batch);
   if (s != PE_OK) return s;
   s = pe_gather_hidden(ctx, B, &a->batch, a->target_hidden, a->h_shared, a->draft_hidden);
   if (s != PE_OK) return s;
-  auto fwd = a->mode == PE_STEP_AUTOREGRESSIVE ? pe_ar_draft : pe_draft_forward;
-  s = fwd(ctx, B, &a->batch, a->draft_hidden, a->block_table, a->max_blocks, a->num_kv_blocks,
+  s = pe_ar_draft(ctx, B, &a->batch, a->draft_hidden, a->block_table, a->max_blocks, a->num_kv_blocks,
           a->k_cache, a->v_cache, a->draft_tokens, a->logits);
   if (s != PE_OK) return s;
   return pe_verify(ctx, B, a->draft_tokens, a->target_tokens, a->accepted_out, a->bonus_out);

@@ -29,6 +29,10 @@
 #include "pe_common.h"
 #include "pe_internal.h"
 
+#ifndef PE_ATTN_MIN_CH
+#define PE_ATTN_MIN_CH 256  // shortest split-KV chunk (positions, a multiple of 64)
+#endif
+
 namespace pe {
 
 constexpr int kMaxB = 1024;
@@ -57,7 +61,7 @@ __device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, i
   for (int w = 0; w < nw; ++w) tot += s_tot[w];
   long long ch = (tot * Hkv + target - 1) / (target > 0 ? target : 1);
   ch = (ch + 63) / 64 * 64;
-  if (ch < 256) ch = 256;  // fewer, longer items when the batch is small (each item pays a DMA ramp-up)
+  if (ch < PE_ATTN_MIN_CH) ch = PE_ATTN_MIN_CH;  // fewer, longer items when the batch is small (each item pays a DMA ramp-up)
   if (ch > (1 << 30)) ch = 1 << 30;
   CH = int(ch);
   const int per = (B + nt - 1) / nt;

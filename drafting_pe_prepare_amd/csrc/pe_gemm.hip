@@ -201,6 +201,49 @@ __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, i
   }
 }
 
+// Argmax of the draft rows and greedy verification in one launch, for the step
+// graph: one workgroup per request; wave w reduces draft rows w, w + waves, ...
+// of the request (the same fixed reduction as argmax_tokens_kernel), then wave
+// 0 finds the first draft that differs from the target's token (a' = K when
+// none does) and takes the target's token there as the bonus.
+__global__ __launch_bounds__(1024) void argmax_verify_kernel(int K, int parts,
+                                                             const uint64_t* __restrict__ keys,
+                                                             int32_t* __restrict__ tokens,
+                                                             const int32_t* __restrict__ seq_lens,
+                                                             const int32_t* __restrict__ target,
+                                                             int32_t* __restrict__ acc,
+                                                             int32_t* __restrict__ bonus) {
+  __shared__ int32_t s_tok[64];
+  const int r = blockIdx.x, w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const bool padded = seq_lens[r] == 0;
+  for (int i = w; i < K; i += nw) {
+    const long long row = (long long)r * K + i;
+    const uint64_t* kr = keys + row * parts;
+    uint64_t best = 0;
+    for (int p = l; p < parts; p += 64) best = kr[p] > best ? kr[p] : best;
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t k = shfl_xor_u64(best, o);
+      best = k > best ? k : best;
+    }
+    if (l == 0) {
+      const int tok = padded ? -1 : argmax_key_index(best);
+      tokens[row] = tok;
+      s_tok[i] = tok;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int32_t* g = target + (long long)r * (K + 1);
+    const bool miss = l < K && s_tok[l] != g[l];
+    const unsigned long long m = __ballot(miss);
+    const int a = m ? (__ffsll((long long)m) - 1) : K;
+    if (l == 0) {
+      acc[r] = a;
+      bonus[r] = g[a];
+    }
+  }
+}
+
 // Argmax partial keys -> tokens, run as its own small kernel after the LM head
 // (the kernel boundary orders the GEMM's stores before these reads).  One
 // workgroup per draft row reduces that row's `parts` keys.
@@ -918,6 +961,17 @@ hipError_t launch_argmax_tokens(int M, int Kd, int parts, const uint64_t* keys, 
   if (M <= 0) return hipSuccess;
   hipLaunchKernelGGL(argmax_tokens_kernel, dim3(M), dim3(256), 0, st, M, Kd, parts, keys, tokens,
                      tstride, seq_lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_verify(int B, int K, int parts, const uint64_t* keys, int32_t* tokens,
+                                const int32_t* seq_lens, const int32_t* target, int32_t* acc,
+                                int32_t* bonus, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  if (K < 1 || K > 64) return hipErrorInvalidValue;
+  const int waves = K < 16 ? K : 16;
+  hipLaunchKernelGGL(argmax_verify_kernel, dim3(unsigned(B)), dim3(64 * waves), 0, st, K, parts, keys,
+                     tokens, seq_lens, target, acc, bonus);
   return hipGetLastError();
 }
 

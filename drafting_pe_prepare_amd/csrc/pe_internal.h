@@ -23,6 +23,13 @@ hipError_t launch_gather(int rows, int nsrc, int row_bytes, const int32_t* hsrc,
 hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32_t* acc,
                          int32_t* bonus, hipStream_t st);
 
+// Step-graph fusions: preparation + hidden-state copy; argmax + verification.
+hipError_t launch_prepare_gather(const PrepareArgs& a, int row_bytes, const void* H,
+                                 const void* h_shared, void* out, hipStream_t st);
+hipError_t launch_argmax_verify(int B, int K, int parts, const uint64_t* keys, int32_t* tokens,
+                                const int32_t* seq_lens, const int32_t* target, int32_t* acc,
+                                int32_t* bonus, hipStream_t st);
+
 // ---- autoregressive comparison --------------------------------------------
 // Pass batches of sequential drafting, built on the device from the parallel
 // batch (stride 2K) so that a captured graph replays them.

@@ -17,10 +17,9 @@
 
 namespace pe {
 
-__global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (r >= a.B) return;
+// Validates request r and, when `write`, stores its slot fields; one wave
+// (lane = slot).  Returns the error kinds found (0: valid).
+__device__ uint32_t prepare_request(const PrepareArgs& a, int r, int lane, bool write) {
   const int K = a.K, S = 2 * K, base = r * S;
   const int32_t* vt = a.vt + (long long)r * (K + 1);
   const int32_t* vp = a.vp + (long long)r * (K + 1);
@@ -56,6 +55,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
     }
   }
 
+  if (!write) return kinds;
   if (kinds) {
     if (lane < S) {
       a.ids[base + lane] = 0;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
       atomicOr(&a.err[0], kinds);
       atomicMin(&a.err[1], uint32_t(r));
     }
-    return;
+    return kinds;
   }
 
   const int32_t* btr = a.bt + (long long)r * a.max_blocks;
@@ -102,6 +102,12 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
   }
   if (lane < K) a.draft_rows[r * K + lane] = (lane == 0) ? base + acc : base + K + lane;
   if (lane == 0) a.seq_lens[r] = seq_len;
+  return 0;
+}
+
+__global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
+  const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (r < a.B) (void)prepare_request(a, r, threadIdx.x & 63, true);
 }
 
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t st) {
@@ -136,6 +142,58 @@ hipError_t launch_gather(int rows, int nsrc, int row_bytes, const int32_t* hsrc,
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(gather_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, rows, nsrc, cpr,
                      hsrc, (const uint4*)H, (const uint4*)h_shared, (uint4*)out);
+  return hipGetLastError();
+}
+
+// Preparation and hidden-state copy in one launch, for the step graph: one
+// workgroup per (slot j, request r).  Every workgroup loads its slot's source
+// row (slot j <= K copies target row r(K+1)+j) while wave 0 validates the
+// request; an invalid request gets h_shared in every slot, as its hidden-source
+// map of -1 says.  Workgroup j == 0 also writes the request's batch fields.
+// Row chunks per thread: at most PG_CHUNKS (checked on the host).
+constexpr int PG_CHUNKS = 4;
+__global__ __launch_bounds__(1024) void prepare_gather_kernel(PrepareArgs a, int cpr,
+                                                              const uint4* __restrict__ H,
+                                                              const uint4* __restrict__ hs,
+                                                              uint4* __restrict__ out) {
+  __shared__ uint32_t s_kinds;
+  const int j = blockIdx.x, r = blockIdx.y, K = a.K;
+  const int src = j <= K ? r * (K + 1) + j : -1;
+  const uint4* from = src >= 0 ? H + (long long)src * cpr : hs;
+  uint4 v[PG_CHUNKS];
+#pragma unroll
+  for (int i = 0; i < PG_CHUNKS; ++i) {
+    const int c = threadIdx.x + i * blockDim.x;
+    if (c < cpr) v[i] = from[c];
+  }
+  if (threadIdx.x < 64) {
+    const uint32_t kinds = prepare_request(a, r, threadIdx.x, j == 0);
+    if (threadIdx.x == 0) s_kinds = kinds;
+  }
+  __syncthreads();
+  const bool shared_row = src < 0 || s_kinds != 0;
+  uint4* dst = out + ((long long)r * 2 * K + j) * cpr;
+#pragma unroll
+  for (int i = 0; i < PG_CHUNKS; ++i) {
+    const int c = threadIdx.x + i * blockDim.x;
+    if (c < cpr) dst[c] = (shared_row && src >= 0) ? hs[c] : v[i];
+  }
+}
+
+hipError_t launch_prepare_gather(const PrepareArgs& a, int row_bytes, const void* H,
+                                 const void* h_shared, void* out, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  const int cpr = row_bytes / 16;
+  int threads = (cpr + PG_CHUNKS - 1) / PG_CHUNKS;
+  threads = (threads + 63) / 64 * 64;
+  if (row_bytes % 16) return hipErrorInvalidValue;
+  if (threads > 1024 || a.B > 65535 || 2 * a.K > 64) {  // outside the fused shape: two launches
+    const hipError_t e = launch_prepare(a, st);
+    if (e != hipSuccess) return e;
+    return launch_gather(a.B * 2 * a.K, a.B * (a.K + 1), row_bytes, a.hsrc, H, h_shared, out, st);
+  }
+  hipLaunchKernelGGL(prepare_gather_kernel, dim3(unsigned(2 * a.K), unsigned(a.B)), dim3(threads), 0,
+                     st, a, cpr, (const uint4*)H, (const uint4*)h_shared, (uint4*)out);
   return hipGetLastError();
 }
 

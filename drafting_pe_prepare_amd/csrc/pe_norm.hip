@@ -8,7 +8,9 @@
 
 namespace pe {
 
-template <typename T>
+// The row's chunks and the gain's stay in registers between the two passes
+// (NCH per thread; a row of more than 256 * NCH chunks takes the loop again).
+template <typename T, int NCH>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const T* __restrict__ x,
                                                       const T* __restrict__ gain,
                                                       T* __restrict__ out,
@@ -21,40 +23,60 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const T* __restrict
   const T* xr = x + (long long)src * d;
   T* yr = out + (long long)i * d;
   const int nc = d / V;
+  uint4 xs[NCH], gs[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c < nc) { xs[j] = ld16(xr + c * V); gs[j] = ld16(gain + c * V); }
+  }
   float ss = 0.f;
-  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c < nc) {
+      const T* e = reinterpret_cast<const T*>(&xs[j]);
+#pragma unroll
+      for (int q = 0; q < V; ++q) { float v = Elt<T>::ld(e + q); ss += v * v; }
+    }
+  }
+  for (int c = threadIdx.x + NCH * 256; c < nc; c += 256) {
     uint4 raw = ld16(xr + c * V);
     const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
-    for (int j = 0; j < V; ++j) { float v = Elt<T>::ld(e + j); ss += v * v; }
+    for (int q = 0; q < V; ++q) { float v = Elt<T>::ld(e + q); ss += v * v; }
   }
   __shared__ float red[4];
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  float tot = 0.f;
-  for (int w = 0; w < int(blockDim.x >> 6); ++w) tot += red[w];
+  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
   const float rs = rsqrtf(tot / float(d) + eps);
-  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
-    uint4 raw = ld16(xr + c * V), gr = ld16(gain + c * V), o;
+  auto emit = [&](int c, const uint4& raw, const uint4& gr) {
+    uint4 o;
     const T* e = reinterpret_cast<const T*>(&raw);
     const T* g = reinterpret_cast<const T*>(&gr);
     T* oe = reinterpret_cast<T*>(&o);
 #pragma unroll
-    for (int j = 0; j < V; ++j) Elt<T>::st(oe + j, Elt<T>::ld(e + j) * rs * Elt<T>::ld(g + j));
+    for (int q = 0; q < V; ++q) Elt<T>::st(oe + q, Elt<T>::ld(e + q) * rs * Elt<T>::ld(g + q));
     *reinterpret_cast<uint4*>(yr + c * V) = o;
+  };
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c < nc) emit(c, xs[j], gs[j]);
   }
+  for (int c = threadIdx.x + NCH * 256; c < nc; c += 256) emit(c, ld16(xr + c * V), ld16(gain + c * V));
 }
 
 hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void* gain, void* out,
                           const int32_t* rows_idx, int rows_bound, float eps, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (dtype == 1)
-    hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(rows), dim3(256), 0, st, d,
+    hipLaunchKernelGGL((rmsnorm_kernel<uint16_t, 2>), dim3(rows), dim3(256), 0, st, d,
                        (const uint16_t*)x, (const uint16_t*)gain, (uint16_t*)out, rows_idx,
                        rows_bound, eps);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, st, d, (const float*)x,
+    hipLaunchKernelGGL((rmsnorm_kernel<float, 2>), dim3(rows), dim3(256), 0, st, d, (const float*)x,
                        (const float*)gain, (float*)out, rows_idx, rows_bound, eps);
   return hipGetLastError();
 }

@@ -299,14 +299,22 @@ def test_closed_loop_rounds():
         st.close()
 
 
-def test_step_graph_replays_match_eager():
-    """One captured graph (prepare+gather+forward+verify) replayed several
-    times, with eager work and synchronization in between; every replay
-    equals the eager result."""
-    w = SMALL_BF16.with_(K=7, batch=6, accepted="uniform", prefix=("uniform", 40, 400))
+@pytest.mark.parametrize("case", ["bf16", "bf16_padded", "f32"])
+def test_step_graph_replays_match_eager(case):
+    """One captured graph of the parallel step (preparation and hidden-state
+    copy in one launch, forward, argmax and verification in one launch)
+    replayed several times, with eager work and synchronization in between;
+    every replay equals the four eager entry points bit for bit: batch fields,
+    drafter inputs, tokens, logits, verification, KV cache and error word."""
+    if case == "f32":
+        w = configs.TINY.with_(K=5, batch=3, accepted="uniform", prefix=("uniform", 40, 200))
+    else:
+        w = SMALL_BF16.with_(K=7, batch=6, accepted="uniform", prefix=("uniform", 40, 400))
     st = Setup(w, seed=11)
     try:
         inp = synth.step_inputs(w, seed=11)
+        if case == "bf16_padded":
+            inp["num_accepted"][2] = w.K + 1  # invalid: the request is padded
         eager = run_step(st, inp)
         B, K = w.batch, w.K
         t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
@@ -315,29 +323,42 @@ def test_step_graph_replays_match_eager():
         kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
         kv0 = [(k.clone(), v.clone()) for k, v in kv]
         batch = pb.Batch(B, K)
-        dh = torch.zeros((B * 2 * K, w.d), dtype=torch.bfloat16, device="cuda")
+        sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dh = torch.zeros((B * 2 * K, w.d), dtype=sdt, device="cuda")
         tok = torch.zeros(B * K, dtype=torch.int32, device="cuda")
+        lg = torch.zeros((B * K, w.vocab), dtype=torch.float32, device="cuda")
         acc = torch.zeros(B, dtype=torch.int32, device="cuda")
         bon = torch.zeros(B, dtype=torch.int32, device="cuda")
         args = pb.make_step_args(t["verify_tokens"], t["verify_positions"], t["num_accepted"],
                                  t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], batch,
                                  t["target_hidden"], st.dev["h_shared"], dh,
                                  [k for k, _ in kv], [v for _, v in kv], tok, t["target_tokens"],
-                                 acc, bon)
+                                 acc, bon, logits=lg)
         for rep in range(4):
             for (k, v), (k0, v0) in zip(kv, kv0):
                 k.copy_(k0)
                 v.copy_(v0)
             tok.fill_(-5)
+            dh.fill_(0)
+            lg.fill_(0.0)
             pb.pe_step_graph(st.ctx, B, args)
             torch.cuda.synchronize()
             _ = torch.randn(1000, device="cuda").sum().item()  # eager work between replays
+            got = batch.host(B, K)
+            for f in pb.BATCH_FIELDS:
+                np.testing.assert_array_equal(got[f], eager["batch"][f], err_msg=f"{f} replay {rep}")
+            np.testing.assert_array_equal(pb.to_host(dh), eager["draft_hidden"], err_msg=f"replay {rep}")
             np.testing.assert_array_equal(tok.cpu().numpy(), eager["tokens"], err_msg=f"replay {rep}")
+            np.testing.assert_array_equal(lg.cpu().numpy(), eager["logits"], err_msg=f"replay {rep}")
             np.testing.assert_array_equal(acc.cpu().numpy(), eager["accepted"])
             np.testing.assert_array_equal(bon.cpu().numpy(), eager["bonus"])
             for (k, v), (ke, ve) in zip(kv, eager["kv"]):
                 np.testing.assert_array_equal(pb.to_host(k), ke)
                 np.testing.assert_array_equal(pb.to_host(v), ve)
+            assert pb.pe_get_device_error(st.ctx) == eager["error"]
+        if case == "bf16_padded":
+            assert eager["error"] == (1, 2)
+            assert np.all(eager["tokens"][2 * K:3 * K] == -1)
     finally:
         st.close()
 
