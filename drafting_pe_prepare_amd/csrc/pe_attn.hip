@@ -449,10 +449,12 @@ __global__ __launch_bounds__(256) void attn_merge_group_kernel(AttnArgs a) {
     if (!a.rej[row] && a.seq_lens[r] > 0) {
       const int c0 = s_off[r], nc = s_off[r + 1] - c0;
       auto item = [&](int ch) { return (long long)(c0 + ch) * a.Hkv + g; };
+      // unrolled so that the chunks' loads are in flight together
       float M = -INFINITY;
+#pragma unroll 8
       for (int ch = 0; ch < nc; ++ch) M = fmaxf(M, a.part_ml[(item(ch) * QN + q) * 2]);
       if (M != -INFINITY) {
-#pragma unroll 4
+#pragma unroll 8
         for (int ch = 0; ch < nc; ++ch) {
           const long long it = item(ch);
           const float mc = a.part_ml[(it * QN + q) * 2], lc = a.part_ml[(it * QN + q) * 2 + 1];

@@ -29,6 +29,16 @@
 #include "pe_common.h"
 #include "pe_internal.h"
 
+#ifndef PE_SKINNY_NTW_GU
+#define PE_SKINNY_NTW_GU 4  // 16-column tiles per gate/up workgroup of up to 16 rows
+#endif
+#ifndef PE_SKINNY_U_NARROW
+#define PE_SKINNY_U_NARROW 8  // k-steps of loads in flight per wave, one tile of up to 16 rows
+#endif
+#ifndef PE_SKINNY_U_WIDE
+#define PE_SKINNY_U_WIDE 4  // the same, wider workgroups
+#endif
+
 namespace pe {
 
 // ---------------------------------------------------------------------------
@@ -864,8 +874,8 @@ int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus) {
 
 template <int EPI, int AL, int BMAP, int MT>
 static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
-  constexpr int NTW = (BMAP == B_PLAIN) ? 1 : 2;
-  constexpr int U = (NTW + MT <= 3) ? 8 : 4;
+  constexpr int NTW = BMAP == B_PLAIN ? 1 : (BMAP == B_GATEUP && MT == 1) ? PE_SKINNY_NTW_GU : 2;
+  constexpr int U = NTW + MT <= 2 ? PE_SKINNY_U_NARROW : NTW + MT <= 3 ? 8 : NTW + MT <= 5 ? PE_SKINNY_U_WIDE : 3;
   const int ksteps = g.K / 32;
   int nw = ksteps / 4;
   nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
