@@ -299,7 +299,8 @@ def ksweep(steps, warmup):
                      "sequential_us_per_step": ar["us_per_step"],
                      "sequential_draft_tokens_per_s": ar["value"],
                      "parallel_speedup": ar["parallel_speedup"],
-                     "lm_head_us": r["phases_us_per_step"]["lmhead"]})
+                     "lm_head_us": r["phases_us_per_step"]["lmhead"],
+                     "phases_us_per_step": r["phases_us_per_step"]})
     del dev
     torch.cuda.empty_cache()
     return {"workload": base.name, "batch": base.batch, "d": base.d, "layers": base.layers,

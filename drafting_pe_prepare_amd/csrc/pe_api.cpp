@@ -66,6 +66,8 @@ struct pe_ctx {
   uint32_t* err = nullptr;    // [2] kinds, first request
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  float* splitk = nullptr;      // split-K GEMM partials (bf16 storage)
+  long long splitk_cap = 0;     // floats
   double* rope_turns = nullptr;  // RoPE frequencies in turns per position
   void* lm_packed = nullptr;  // fragment-order copy of the LM head (bf16)
   // fragment-order copies of the small-batch GEMM weights (bf16): fc, then per
@@ -138,7 +140,7 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->rope_turns, c->lm_packed};
+                  c->part_o, c->part_ml, c->rope_turns, c->lm_packed, c->splitk};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   if (c->fc_packed) (void)hipFree(c->fc_packed);
@@ -298,6 +300,13 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   if (k.dtype == PE_BF16) {
     if ((s = alloc(&c->part_o, size_t(c->items_max) * QN * k.head_dim * 4, "attn partials")) != PE_OK ||
         (s = alloc(&c->part_ml, size_t(c->items_max) * QN * 2 * 4, "attn stats")) != PE_OK) {
+      free_ctx(c);
+      return s;
+    }
+    // split-K partials: GEMMs whose output tiles are too few to fill the chip
+    // sum k-ranges into here first (32 MB bounds the split factor)
+    c->splitk_cap = std::min<long long>(8LL << 20, (long long)R * std::max(2 * k.mlp, 4 * k.d) * 8);
+    if ((s = alloc(&c->splitk, size_t(c->splitk_cap) * 4, "split-K partials")) != PE_OK) {
       free_ctx(c);
       return s;
     }
@@ -480,6 +489,8 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   g0.Hkv = k.n_kv_heads;
   g0.block_size = k.block_size;
   g0.num_slots = num_slots;
+  g0.part = ctx->splitk;
+  g0.part_cap = ctx->splitk_cap;
 
   // fc over concat(emb(token), hidden)
   {

@@ -29,6 +29,12 @@
 #include "pe_common.h"
 #include "pe_internal.h"
 
+#ifndef PE_SPLITK_WG_PER_CU
+#define PE_SPLITK_WG_PER_CU 2  // workgroups per CU that a split-K GEMM aims for
+#endif
+#ifndef PE_SPLITK_MIN_KTILES
+#define PE_SPLITK_MIN_KTILES 8  // fewest 64-wide k-tiles per split
+#endif
 #ifndef PE_SKINNY_NTW_GU
 #define PE_SKINNY_NTW_GU 4  // 16-column tiles per gate/up workgroup of up to 16 rows
 #endif
@@ -543,7 +549,18 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   // the fragment reads of another do not alias
   __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE], st1[STAGE], st2[S == 3 ? STAGE : 16];
 
-  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  // split-K (E_PART): the grid holds ksplit copies of the tile grid, copy ks
+  // summing k-tiles [ks nk / ksplit, (ks + 1) nk / ksplit); the copies are
+  // multiples of 8 workgroups, so the XCD of a workgroup is unchanged
+  int bid = blockIdx.x, ks = 0, kbase = 0, nk = g.K / 64;
+  if constexpr (EPI == E_PART) {
+    const int per = mtiles * ((ntiles + 7) / 8) * 8;
+    ks = bid / per;
+    bid -= ks * per;
+    kbase = ks * nk / g.ksplit;
+    nk = (ks + 1) * nk / g.ksplit - kbase;
+  }
+  const int b = bid, xcd = b & 7, j = b >> 3;
   const int mt = j % mtiles, nt = (j / mtiles) * 8 + xcd;
   if (nt >= ntiles) return;  // padding workgroup of the XCD-aligned grid
   const int m0 = mt * BM, n0 = nt * BN;
@@ -560,7 +577,7 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
 #pragma unroll
   for (int i = 0; i < LB; ++i) bp[i] = weight_row<uint16_t, BMAP>(g, min(n0 + 8 * (w + NW * i) + lr, g.N - 1)) + lc;
   auto issue = [&](unsigned char* st, int kt) {
-    const int k0 = kt * 64;
+    const int k0 = (kbase + kt) * 64;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
       __builtin_amdgcn_global_load_lds(
@@ -583,7 +600,6 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   const int aoff0 = swz64(ar0, kg), aoff1 = swz64(ar0, 4 + kg);
   const int boff0 = BM * 128 + swz64(br0, kg), boff1 = BM * 128 + swz64(br0, 4 + kg);
 
-  const int nk = g.K / 64;
   issue(st0, 0);
   if (1 < nk) issue(st1, 1);
   if (S == 3 && 2 < nk) issue(st2, 2);
@@ -644,7 +660,21 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   }
 
   // lane (kg, col) holds C[row 4kg + r of MFMA tile i][col of tile jj]
-  if constexpr (EPI == E_ARGMAX) {
+  if constexpr (EPI == E_PART) {
+    float* P = g.part + (long long)ks * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BM / WM) + i * 16 + kg * 4 + r;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int jj = 0; jj < TJ; ++jj) {
+          const int n = n0 + wn * (BN / WN) + jj * 16 + col;
+          if (n < g.N) P[(long long)m * g.N + n] = acc[i][jj][r];
+        }
+      }
+  } else if constexpr (EPI == E_ARGMAX) {
     __syncthreads();  // every fragment read is done; no DMA is in flight
     uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [WN][BM]
     static_assert(WN * BM * 8 <= STAGE, "argmax scratch fits one stage");
@@ -930,6 +960,104 @@ static hipError_t run_tiled(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Split-K sum and epilogue: the ksplit fp32 partials of each output are added
+// in a fixed order (deterministic), then the epilogue the unsplit kernel would
+// have fused runs on the sum.  Store / residual: 8 consecutive columns per
+// thread; SiLU.mul: 8 outputs from 8 gate and 8 up columns; QKV: one RoPE pair.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
+  const int KS = g.ksplit;
+  const long long MN = (long long)g.M * g.N;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  auto sum8 = [&](int m, int n, float (&v)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = 0.f;
+    for (int k = 0; k < KS; ++k) {
+      const float* p = g.part + k * MN + (long long)m * g.N + n;
+      const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+      v[4] += c.x; v[5] += c.y; v[6] += c.z; v[7] += c.w;
+    }
+  };
+  if constexpr (EPI == E_STORE || EPI == E_RESID) {
+    const int per_row = g.N / 8;
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)g.M * per_row; e += stride) {
+      const int m = int(e / per_row), n = int(e % per_row) * 8;
+      float v[8];
+      sum8(m, n, v);
+      const long long o = (long long)m * g.ldo + n;
+      if constexpr (EPI == E_RESID) {
+        const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + o);
+        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[2 * t] += __uint_as_float(rw[t] << 16);
+          v[2 * t + 1] += __uint_as_float(rw[t] & 0xFFFF0000u);
+        }
+      }
+      uint4 ov;
+      ov.x = f2bf2(v[0], v[1]); ov.y = f2bf2(v[2], v[3]); ov.z = f2bf2(v[4], v[5]); ov.w = f2bf2(v[6], v[7]);
+      *reinterpret_cast<uint4*>((uint16_t*)g.out + o) = ov;
+    }
+  } else if constexpr (EPI == E_SILU) {
+    // logical columns (32q + c, 32q + 16 + c) -> output column 16q + c
+    const int per_row = g.N / 16;
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)g.M * per_row; e += stride) {
+      const int m = int(e / per_row), pc = int(e % per_row), q = pc >> 1, c0 = (pc & 1) * 8;
+      float gt[8], up[8], v[8];
+      sum8(m, 32 * q + c0, gt);
+      sum8(m, 32 * q + 16 + c0, up);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = gt[t] / (1.0f + expf(-gt[t])) * up[t];
+      uint4 o;
+      o.x = f2bf2(v[0], v[1]); o.y = f2bf2(v[2], v[3]); o.z = f2bf2(v[4], v[5]); o.w = f2bf2(v[6], v[7]);
+      *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)m * g.ldo + 16 * q + c0) = o;
+    }
+  } else {
+    static_assert(EPI == E_QKV, "split-K epilogues: store, residual, SiLU.mul, QKV");
+    const int per_row = g.N / 2;
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)g.M * per_row; e += stride) {
+      const int m = int(e / per_row), pr = int(e % per_row), nb = (pr >> 4) * 32, c = pr & 15;
+      float lo = 0.f, hi = 0.f;
+      for (int k = 0; k < KS; ++k) {
+        const float* p = g.part + k * MN + (long long)m * g.N + nb + c;
+        lo += p[0];
+        hi += p[16];
+      }
+      epi_pair<uint16_t, E_QKV>(g, m, nb, c, lo, hi);
+    }
+  }
+}
+
+// Dense tiled GEMM, split over K when its output tiles are fewer than the CUs,
+// into about PE_SPLITK_WG_PER_CU workgroups per CU; each split keeps at least
+// PE_SPLITK_MIN_KTILES k-tiles (splitting grids that already cover the CUs
+// measured slower: c=64 fc/O/down).
+template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int S>
+static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
+  if (g.K % 64) return hipErrorInvalidValue;
+  const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN, nk = g.K / 64;
+  const long long tiles = (long long)mtiles * ntiles, target = (long long)PE_SPLITK_WG_PER_CU * num_cus;
+  long long ks = 1;
+  if (g.part && tiles < num_cus && g.N % 32 == 0) {
+    ks = (target + tiles - 1) / tiles;
+    ks = std::min<long long>(ks, nk / PE_SPLITK_MIN_KTILES);
+    ks = std::min<long long>(ks, g.part_cap / ((long long)g.M * g.N));
+  }
+  if (ks <= 1) return run_tiled<EPI, AL, BMAP, BM, BN, WM, WN, S>(g, st);
+  GemmArgs gp = g;
+  gp.ksplit = int(ks);
+  const long long per = (long long)mtiles * ((ntiles + 7) / 8) * 8;
+  hipLaunchKernelGGL((gemm_tiled_kernel<E_PART, AL, BMAP, BM, BN, WM, WN, S>), dim3(unsigned(per * ks)),
+                     dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long work = (long long)g.M * (EPI == E_QKV ? g.N / 2 : EPI == E_SILU ? g.N / 16 : g.N / 8);
+  const long long blocks = std::min<long long>((work + 255) / 256, 8LL * num_cus);
+  hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, st, gp);
+  return hipGetLastError();
+}
+
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
   const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);
@@ -947,8 +1075,8 @@ static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
         if (g.M <= 32) return run_skinny<EPI, AL, BMAP, 2>(g, st);
         if (g.M <= 48) return run_skinny<EPI, AL, BMAP, 3>(g, st);
         return run_skinny<EPI, AL, BMAP, 4>(g, st);
-      case V_D64: return run_tiled<EPI, AL, BMAP, 64, 128, 1, 4, 3>(g, st);
-      default: return run_tiled<EPI, AL, BMAP, 128, 128, 2, 2, 2>(g, st);
+      case V_D64: return run_tiled_dense<EPI, AL, BMAP, 64, 128, 1, 4, 3>(g, num_cus, st);
+      default: return run_tiled_dense<EPI, AL, BMAP, 128, 128, 2, 2, 2>(g, num_cus, st);
     }
   }
 }

@@ -60,7 +60,7 @@ hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void*
 // ---- GEMM  out[m, n] = sum_k A[m, k] W[n, k]  + fused epilogue -------------
 enum ALoad { A_PLAIN = 0, A_FC = 1 };
 enum BMap { B_PLAIN = 0, B_QKV = 1, B_GATEUP = 2 };
-enum Epi { E_STORE = 0, E_RESID = 1, E_SILU = 2, E_QKV = 3, E_ARGMAX = 4 };
+enum Epi { E_STORE = 0, E_RESID = 1, E_SILU = 2, E_QKV = 3, E_ARGMAX = 4, E_PART = 5 };
 
 struct GemmArgs {
   int M, N, K;  // N counts logical columns (2*I for gate/up; q+k+v dims for QKV)
@@ -81,6 +81,10 @@ struct GemmArgs {
   uint64_t* keys; int parts;                      // E_ARGMAX: keys[row * parts + part]
   int32_t* tokens; float* logits; int ldl;         // logits[row * ldl + n]
   const int32_t* seq_lens; int Kd;
+  // split-K: fp32 partial sums [ksplit][M][N] (logical columns) for GEMMs with
+  // too few output tiles to fill the chip; the epilogue runs after the sum
+  float* part; long long part_cap;  // capacity in floats (0: never split)
+  int ksplit;
 };
 hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,
                        hipStream_t st);

@@ -122,6 +122,16 @@ def test_small_bf16_tile_variants(K, B, mlp, seed):
     _full_check(w, seed)
 
 
+@pytest.mark.parametrize("K,B,seed", [(7, 8, 83), (3, 12, 84)])
+def test_small_bf16_split_k(K, B, seed):
+    """d = 1024, MLP 2048: too few output tiles for the chip, so every dense
+    GEMM sums K-splits into fp32 partials and runs its epilogue on the sum
+    (fc store, RoPE/KV write, residuals, SiLU.mul), 4 to 8 splits."""
+    w = SMALL_BF16.with_(K=K, batch=B, d=1024, mlp=2048, n_q_heads=16, n_kv_heads=2,
+                         weight_std=1 / 32, accepted="uniform", prefix=("uniform", 30, 300))
+    _full_check(w, seed)
+
+
 @pytest.mark.parametrize("B", [5, 12])
 def test_small_bf16_tiled_path(B):
     """B*2K > 64 rows: the LDS-tiled GEMM path and the tiled LM head."""
