@@ -126,7 +126,7 @@ def test_small_bf16_tile_variants(K, B, mlp, seed):
 def test_small_bf16_split_k(K, B, seed):
     """d = 1024, MLP 2048: too few output tiles for the chip, so every dense
     GEMM sums K-splits into fp32 partials and runs its epilogue on the sum
-    (fc store, RoPE/KV write, residuals, SiLU.mul), 4 to 8 splits."""
+    (fc store, RoPE/KV write, residuals, SiLU.mul), 2 to 4 splits."""
     w = SMALL_BF16.with_(K=K, batch=B, d=1024, mlp=2048, n_q_heads=16, n_kv_heads=2,
                          weight_std=1 / 32, accepted="uniform", prefix=("uniform", 30, 300))
     _full_check(w, seed)
