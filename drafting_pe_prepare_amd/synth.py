@@ -169,6 +169,46 @@ def step_inputs(w: Workload, seed: int = None, kv: bool = True) -> dict:
     return out
 
 
+def prefill_inputs(w: Workload, S: int, lens, start, seed: int = None, kv: bool = True) -> dict:
+    """Inputs of a drafting round that follows a prompt (or a chunk of one):
+    per request a chunk of prompt tokens, its length n, the position c0 it
+    starts at, the token after it, the target's hidden states of the chunk
+    [B*L, d] (L = S-K+1 rows per request) and a block table covering
+    c0+n+K-1 positions.  lens: ("fixed", n) or ("uniform", lo, hi) chunk
+    lengths; start: ("fixed", c0) or ("uniform", lo, hi) start positions."""
+    s = w.seed if seed is None else seed
+    B, K, bs = w.batch, w.K, w.block_size
+    L = S - K + 1
+
+    def draw(spec, name):
+        if spec[0] == "fixed":
+            return np.full(B, int(spec[1]), dtype=np.int32)
+        return integers(s, name, int(spec[1]), int(spec[2]) + 1, (B,))
+
+    n = draw(lens, "prefill_lens")
+    c0 = draw(start, "prefill_start")
+    ct = integers(s, "prefill_tokens", 0, w.vocab - 1, (B, L))
+    nt = integers(s, "prefill_new", 0, w.vocab - 1, (B,))
+    need = (c0.astype(np.int64) + n + K - 1 + bs - 1) // bs
+    nblocks = int(need.sum())
+    max_blocks = int(need.max()) if B else 1
+    g = np.random.Generator(np.random.PCG64(_key(s, "prefill_block_table")))
+    perm = g.permutation(nblocks).astype(np.int32)
+    bt = np.zeros((B, max_blocks), dtype=np.int32)
+    off = 0
+    for r in range(B):
+        bt[r, :need[r]] = perm[off:off + need[r]]
+        off += int(need[r])
+    out = {
+        "chunk_tokens": ct, "chunk_lens": n, "start_pos": c0, "new_tokens": nt,
+        "block_table": bt, "num_kv_blocks": nblocks, "S": S,
+        "target_hidden": normal(s, "prefill_hidden", (B * L, w.d), 1.0, dtype=w.dtype),
+    }
+    if kv:
+        out["kv"] = kv_pool(w, nblocks, s)
+    return out
+
+
 def kv_pool(w: Workload, nblocks: int, seed: int) -> list:
     """Per layer: K cache [num_slots, Hkv, hd] and V cache
     [num_blocks, Hkv, hd, block_size] (V is stored d-major inside a block)."""

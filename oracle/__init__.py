@@ -12,7 +12,8 @@ What it follows (page titles as published):
     and MTP positions; one N-layer Transformer + LM head pass predicting
     t_1..t_K), vLLM implementation details (Fused Triton kernel: the batch
     metadata; Hidden-state management: the hidden-state copy; KV cache:
-    PADDING_SLOT_ID = -1 for rejected tokens).
+    PADDING_SLOT_ID = -1 for rejected tokens); Architecture and mechanism,
+    Step 1 (Prefilling) for the drafting round that follows a prompt.
   * "AWS and vLLM ship P-EAGLE" -- How it works (learned mask embedding and
     shared hidden vector for positions that do not exist yet); Integration and
     numbers (acceptance length = drafts the verifier accepts per round).
@@ -24,6 +25,6 @@ unpinned (no trained weights exist here).
 """
 from .pe_oracle import (  # noqa: F401
     PAD_TOKEN, PADDING_SLOT_ID, ERR_ACCEPTED, ERR_TOKEN, ERR_BLOCK, ERR_LAYOUT,
-    round_bf16, widen, prepare, gather_hidden, rmsnorm, rope, silu,
+    round_bf16, widen, prepare, prepare_prefill, gather_hidden, rmsnorm, rope, silu,
     attend, draft_forward, verify, eagle_step, ar_draft, slot_of,
 )

@@ -199,6 +199,115 @@ def prepare(verify_tokens, verify_positions, num_accepted, bonus_tokens,
     }
 
 
+def prepare_prefill(chunk_tokens, chunk_lens, start_pos, new_tokens, block_table,
+                    num_kv_blocks, K, S, vocab, mask_id, block_size):
+    """Draft-batch metadata for the drafting round that follows a prompt.
+
+    Follows "P-EAGLE: parallel speculative decoding in vLLM", Architecture and
+    mechanism: Step 1 (Prefilling: the target returns a hidden state for every
+    prompt position and one new token) and Step 2 (Parallel Drafting: a prompt
+    position pairs the target's hidden state there with the embedding of the
+    token one position later; the NTP position pairs the new token with the
+    last hidden state; positions 2..K take the MASK embedding and h_shared).
+
+    Request r covers prompt positions c0..c0+n-1 in this call (c0 =
+    start_pos[r], n = chunk_lens[r]); positions below c0 were drafted by
+    earlier calls and are in the KV cache.  chunk_tokens[r, j] is the prompt
+    token at position c0+j; new_tokens[r] is the token after the chunk (the
+    target's new token when the chunk ends the prompt, else the next prompt
+    token: an earlier chunk is the same call with its drafts ignored, whose
+    MASK-slot KV the next chunk overwrites).  Readings: the batch has a fixed
+    stride of S slots per request, L = S-K+1 >= n; hidden rows of the chunk
+    are target_hidden[r*L + j]:
+
+      copied slots j = 0..n-1    position c0+j, hidden row r*L+j, token
+                                 chunk_tokens[r, j+1] (j < n-1) or
+                                 new_tokens[r] (j = n-1: the NTP position)
+      MASK slots   j = n..n+K-2  token mask_id, position c0+j, hidden -1
+      padding      j >= n+K-1    rejected: token PAD_TOKEN, position 0,
+                                 hidden -1, KV slot PADDING_SLOT_ID
+
+    draft_rows[r] = r*S+n-1 .. r*S+n+K-2 (NTP, then MASK slots);
+    seq_len = c0+n+K-1.  A request with n outside [1, L] (ERR_ACCEPTED), a
+    token it reads outside [0, V) (ERR_TOKEN), c0 < 0 or a block of
+    [0, seq_len) missing (ERR_BLOCK) becomes padding as in prepare().
+    """
+    ct = np.asarray(chunk_tokens, dtype=np.int64)
+    nl = np.asarray(chunk_lens, dtype=np.int64)
+    c0s = np.asarray(start_pos, dtype=np.int64)
+    nt = np.asarray(new_tokens, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    B = nl.shape[0]
+    L = S - K + 1
+    n_all = B * S
+    ids = np.zeros(n_all, np.int32)
+    pos = np.zeros(n_all, np.int32)
+    hsrc = np.full(n_all, -1, np.int32)
+    rej = np.zeros(n_all, np.uint8)
+    msk = np.zeros(n_all, np.uint8)
+    slots = np.full(n_all, PADDING_SLOT_ID, np.int64)
+    draft_rows = np.zeros(B * K, np.int32)
+    seq_lens = np.zeros(B, np.int32)
+    err_kinds, err_first = 0, -1
+    req_kinds = np.zeros(B, np.int32)
+    max_blocks = bt.shape[1] if bt.ndim == 2 else 0
+
+    for r in range(B):
+        base = r * S
+        n = int(nl[r])
+        c0 = int(c0s[r])
+        kinds = 0
+        if not 1 <= n <= L:
+            kinds |= ERR_ACCEPTED
+        else:
+            for t in list(ct[r, 1:n]) + [nt[r]]:
+                if not 0 <= int(t) < vocab:
+                    kinds |= ERR_TOKEN
+        if c0 < 0:
+            kinds |= ERR_BLOCK
+        if kinds == 0:
+            seq_len = c0 + n + K - 1
+            nb = (seq_len + block_size - 1) // block_size
+            if nb > max_blocks:
+                kinds |= ERR_BLOCK
+            else:
+                for b in range(nb):
+                    if not 0 <= int(bt[r, b]) < num_kv_blocks:
+                        kinds |= ERR_BLOCK
+        req_kinds[r] = kinds
+        rej[base:base + S] = 1
+        if kinds:
+            err_kinds |= kinds
+            if err_first < 0:
+                err_first = r
+            for i in range(K):
+                draft_rows[r * K + i] = base + i
+            continue
+
+        for j in range(n + K - 1):
+            s = base + j
+            rej[s] = 0
+            pos[s] = c0 + j
+            if j < n:
+                hsrc[s] = r * L + j
+                ids[s] = ct[r, j + 1] if j < n - 1 else nt[r]
+            else:
+                ids[s] = mask_id
+                msk[s] = 1
+            slots[s] = slot_of(bt[r], int(pos[s]), block_size)
+        for i in range(K):
+            draft_rows[r * K + i] = base + n - 1 + i
+        seq_lens[r] = c0 + n + K - 1
+
+    return {
+        "input_ids": ids, "positions": pos, "hidden_src": hsrc,
+        "is_rejected": rej, "is_masked": msk, "slot_mapping": slots,
+        "draft_rows": draft_rows, "seq_lens": seq_lens,
+        "error_kinds": err_kinds, "error_first": err_first,
+        "request_kinds": req_kinds,
+    }
+
+
 # ----------------------------------------------------------------------------
 # (b) hidden-state gather
 # ----------------------------------------------------------------------------
@@ -313,6 +422,8 @@ def draft_forward(params, cfg, batch, draft_hidden, kv, block_table,
       lowest index on ties.
 
     params: storage arrays as drawn (uint16 = bf16 bits, or float32).
+    batch: from prepare() (S = 2K slots per request) or prepare_prefill()
+    (any fixed S); the slot count per request is read from its size.
     kv: per layer (K cache, V cache) storage arrays; they are not modified.
     requests: subset of request indices to compute (rows are independent
     apart from attention, which stays inside one request).
@@ -324,11 +435,11 @@ def draft_forward(params, cfg, batch, draft_hidden, kv, block_table,
     """
     R = _rounder(precision)
     K = cfg.K
-    S = 2 * K
     bs = cfg.block_size
     Hq, Hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     group = Hq // Hkv
     B = len(batch["seq_lens"])
+    S = len(batch["input_ids"]) // B if B else 2 * K  # slots per request (2K per decode round)
     reqs = list(range(B)) if requests is None else list(requests)
     rows = np.concatenate([np.arange(r * S, (r + 1) * S) for r in reqs]) if reqs else np.zeros(0, np.int64)
     n = rows.shape[0]
