@@ -477,12 +477,16 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
   }
   __syncthreads();
   // tiles cut between waves: the wave holding the tile's first unit (its tail
-  // slot) adds the head slots of the following waves that hold the same tile
+  // slot) adds the head slots of the following waves that hold the same tile.
+  // Waves with an empty run (fewer units than waves) hold nothing and are
+  // passed over: the tile's later pieces can lie beyond them.
   const int tt = part_tile[w][1];
   if (tt >= 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = part[w][1][i][l];
-    for (int v = w + 1; v < nw && part_tile[v][0] == tt; ++v) {
+    for (int v = w + 1; v < nw; ++v) {
+      if (int((long long)nunits * v / nw) == int((long long)nunits * (v + 1) / nw)) continue;
+      if (part_tile[v][0] != tt) break;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] += part[v][0][i][l];
       if (part_tile[v][1] == tt) break;  // cannot happen: a run longer than a tile
