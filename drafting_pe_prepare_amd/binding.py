@@ -22,7 +22,8 @@ PE_F32, PE_BF16 = 0, 1
 DEVERR_ACCEPTED, DEVERR_TOKEN, DEVERR_BLOCK, DEVERR_LAYOUT = 1, 2, 4, 8
 
 EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_hidden",
-           "pe_draft_forward", "pe_ar_draft", "pe_verify", "pe_step_graph", "pe_get_device_error",
+           "pe_draft_forward", "pe_ar_draft", "pe_verify", "pe_prefill_prepare", "pe_prefill_gather",
+           "pe_prefill_forward", "pe_step_graph", "pe_get_device_error",
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
           "verify", "argmax", "ar")
@@ -34,7 +35,8 @@ vp, i32 = ctypes.c_void_p, ctypes.c_int32
 class PeConfig(ctypes.Structure):
     _fields_ = [(n, i32) for n in ("K", "max_num_seqs", "d", "n_q_heads", "n_kv_heads", "head_dim",
                                    "mlp", "layers", "vocab", "block_size", "mask_id", "dtype")] + \
-               [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+               [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("max_prefill_slots", i32)]
 
 
 class PeLayerWeights(ctypes.Structure):
@@ -94,6 +96,9 @@ def load(path: str = LIB_PATH):
     lib.pe_draft_forward.argtypes = [vp, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp), vp, vp]
     lib.pe_ar_draft.argtypes = [vp, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp), vp, vp]
     lib.pe_verify.argtypes = [vp, i32, vp, vp, vp, vp]
+    lib.pe_prefill_prepare.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, i32, i32, P(PeBatch)]
+    lib.pe_prefill_gather.argtypes = [vp, i32, i32, P(PeBatch), vp, vp, vp]
+    lib.pe_prefill_forward.argtypes = [vp, i32, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp), vp, vp]
     lib.pe_step_graph.argtypes = [vp, i32, P(PeStepArgs)]
     lib.pe_get_device_error.argtypes = [vp, P(ctypes.c_uint32), P(i32)]
     lib.pe_profile_enable.argtypes = [vp, ctypes.c_int]
@@ -130,8 +135,9 @@ def _stream_handle(stream):
 class Batch:
     """Device buffers of a pe_batch for up to `max_B` requests."""
 
-    def __init__(self, max_B: int, K: int, device="cuda"):
-        S = 2 * K
+    def __init__(self, max_B: int, K: int, device="cuda", S: int = None):
+        S = 2 * K if S is None else S
+        self.S = S
         n = max_B * S
         i = dict(dtype=torch.int32, device=device)
         self.input_ids = torch.zeros(n, **i)
@@ -145,7 +151,7 @@ class Batch:
         self.c = PeBatch(*[_ptr(getattr(self, f)) for f in BATCH_FIELDS])
 
     def host(self, B: int, K: int) -> dict:
-        S = 2 * K
+        S = self.S
         n = {f: B * S for f in BATCH_FIELDS}
         n["draft_rows"], n["seq_lens"] = B * K, B
         return {f: getattr(self, f)[:n[f]].cpu().numpy() for f in BATCH_FIELDS}
@@ -154,14 +160,14 @@ class Batch:
 class Context:
     """A libpe context: one drafter's weights (borrowed) and workspace."""
 
-    def __init__(self, cfg, weights: dict, max_num_seqs: int, stream=None):
+    def __init__(self, cfg, weights: dict, max_num_seqs: int, stream=None, max_prefill_slots: int = 0):
         lib = load()
         self.cfg = cfg
         self.weights = weights  # keep the device tensors alive
         dtype = PE_BF16 if cfg.dtype == "bf16" else PE_F32
         self.c_cfg = PeConfig(cfg.K, max_num_seqs, cfg.d, cfg.n_q_heads, cfg.n_kv_heads,
                               cfg.head_dim, cfg.mlp, cfg.layers, cfg.vocab, cfg.block_size,
-                              cfg.mask_id, dtype, cfg.rms_eps, cfg.rope_theta)
+                              cfg.mask_id, dtype, cfg.rms_eps, cfg.rope_theta, max_prefill_slots)
         L = len(weights["layers"])
         self.c_layers = (PeLayerWeights * L)(*[
             PeLayerWeights(*[_ptr(lw[n]) for n, _ in PeLayerWeights._fields_])
@@ -222,6 +228,27 @@ def pe_ar_draft(ctx: Context, B, batch: Batch, draft_hidden, block_table, num_kv
     _check(_lib.pe_ar_draft(ctx.h, B, ctypes.byref(batch.c), _ptr(draft_hidden),
                             _ptr(block_table), block_table.shape[1], num_kv_blocks,
                             kc, vc, _ptr(draft_tokens), _ptr(logits)))
+
+
+def pe_prefill_prepare(ctx: Context, B, S, chunk_tokens, chunk_lens, start_pos, new_tokens,
+                       block_table, num_kv_blocks, batch: Batch):
+    max_blocks = block_table.shape[1] if block_table.dim() == 2 else 1
+    _check(_lib.pe_prefill_prepare(ctx.h, B, S, _ptr(chunk_tokens), _ptr(chunk_lens), _ptr(start_pos),
+                                   _ptr(new_tokens), _ptr(block_table), max_blocks, num_kv_blocks,
+                                   ctypes.byref(batch.c)))
+
+
+def pe_prefill_gather(ctx: Context, B, S, batch: Batch, target_hidden, h_shared, draft_hidden):
+    _check(_lib.pe_prefill_gather(ctx.h, B, S, ctypes.byref(batch.c), _ptr(target_hidden),
+                                  _ptr(h_shared), _ptr(draft_hidden)))
+
+
+def pe_prefill_forward(ctx: Context, B, S, batch: Batch, draft_hidden, block_table, num_kv_blocks,
+                       k_caches, v_caches, draft_tokens, logits=None):
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    _check(_lib.pe_prefill_forward(ctx.h, B, S, ctypes.byref(batch.c), _ptr(draft_hidden),
+                                   _ptr(block_table), block_table.shape[1], num_kv_blocks,
+                                   kc, vc, _ptr(draft_tokens), _ptr(logits)))
 
 
 def pe_verify(ctx: Context, B, draft_tokens, target_tokens, num_accepted, bonus_tokens):

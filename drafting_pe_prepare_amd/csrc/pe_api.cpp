@@ -66,6 +66,9 @@ struct pe_ctx {
   uint32_t* err = nullptr;    // [2] kinds, first request
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  int32_t* group_lens = nullptr; // attention context length per slot group (bf16)
+  int attn_group = 64;           // slots per attention workgroup: 512 / G rounded down to a power of two
+  int groups_max = 0;            // slot groups the attention buffers are sized for
   float* splitk = nullptr;      // split-K GEMM partials (bf16 storage)
   long long splitk_cap = 0;     // floats
   double* rope_turns = nullptr;  // RoPE frequencies in turns per position
@@ -140,7 +143,7 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->rope_turns, c->lm_packed, c->splitk};
+                  c->part_o, c->part_ml, c->rope_turns, c->lm_packed, c->splitk, c->group_lens};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   if (c->fc_packed) (void)hipFree(c->fc_packed);
@@ -158,6 +161,8 @@ pe_status check_cfg(const pe_config* c) {
   if (c->K < 1 || c->K > 32) return fail(PE_ERR_INVALID_ARG, "K=%d outside [1,32]", c->K);
   if (c->max_num_seqs < 1 || c->max_num_seqs > 1024)
     return fail(PE_ERR_INVALID_ARG, "max_num_seqs=%d outside [1,1024]", c->max_num_seqs);
+  if (c->max_prefill_slots < 0 || c->max_prefill_slots > (1 << 26))
+    return fail(PE_ERR_INVALID_ARG, "max_prefill_slots=%d outside [0,2^26]", c->max_prefill_slots);
   if (c->d < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 || c->mlp < 1 ||
       c->layers < 1 || c->vocab < 1 || c->block_size < 1)
     return fail(PE_ERR_INVALID_ARG, "non-positive dimension");
@@ -266,10 +271,24 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   c->target_items = PE_ATTN_ITEMS_PER_CU * c->num_cus;  // split-KV work items per attention launch
 
   const pe_config& k = c->cfg;
-  const size_t R = size_t(k.max_num_seqs) * 2 * k.K, D = size_t(k.max_num_seqs) * k.K;
+  // rows: a decode round (2K slots per request) or a prefill batch
+  const size_t R = std::max(size_t(k.max_num_seqs) * 2 * k.K, size_t(k.max_prefill_slots));
+  const size_t D = size_t(k.max_num_seqs) * k.K;
   const size_t qd = size_t(k.n_q_heads) * k.head_dim;
-  const size_t QN = size_t(2 * k.K) * (k.n_q_heads / k.n_kv_heads);
-  c->items_max = pe::attn_max_items(k.max_num_seqs, k.n_kv_heads, c->target_items);
+  // bf16 attention: a workgroup holds at most 512 query rows (slots x query
+  // heads per KV head); longer requests run as groups of attn_group slots
+  const int G = k.n_q_heads / k.n_kv_heads;
+  c->attn_group = 1;
+  while (c->attn_group * 2 * G <= 512) c->attn_group *= 2;
+  const int Sd = 2 * k.K;
+  const int dec_groups = Sd * G > 512 ? (Sd + c->attn_group - 1) / c->attn_group : 1;
+  c->groups_max = std::max(k.max_num_seqs * dec_groups, k.max_prefill_slots / std::max(c->attn_group, 1));
+  c->groups_max = std::min(std::max(c->groups_max, k.max_num_seqs), 1024);
+  // query rows of one attention item: S*G when that fits a workgroup, else
+  // a group's; a prefill batch may bring any S with S*G <= 512
+  size_t QN = Sd * G <= 512 ? size_t(Sd) * G : size_t(c->attn_group) * G;
+  if (k.max_prefill_slots > 0) QN = 512;
+  c->items_max = pe::attn_max_items(c->groups_max, k.n_kv_heads, c->target_items);
   // partial argmax keys: the most any LM-head launch can need (B*K draft rows
   // of a parallel pass, B of a sequential one)
   size_t key_slots = 0;
@@ -300,6 +319,10 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   if (k.dtype == PE_BF16) {
     if ((s = alloc(&c->part_o, size_t(c->items_max) * QN * k.head_dim * 4, "attn partials")) != PE_OK ||
         (s = alloc(&c->part_ml, size_t(c->items_max) * QN * 2 * 4, "attn stats")) != PE_OK) {
+      free_ctx(c);
+      return s;
+    }
+    if ((s = alloc(&c->group_lens, size_t(c->groups_max) * 4, "attention group lengths")) != PE_OK) {
       free_ctx(c);
       return s;
     }
@@ -531,8 +554,25 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       a.bt = block_table; a.out = ctx->attn;
       a.part_o = ctx->part_o; a.part_ml = ctx->part_ml;
       a.target_items = ctx->target_items;
+      a.vpr = 1;
+      const int G = k.n_q_heads / k.n_kv_heads;
+      if (dt == PE_BF16 && S * G > 512) {
+        // groups of attn_group consecutive slots attend as requests of their
+        // own (same block table row, context up to the group's last position)
+        const int Sv = ctx->attn_group;
+        if (S % Sv || (long long)B * (S / Sv) > ctx->groups_max)
+          return fail(PE_ERR_UNSUPPORTED, "attention: %d slots per request in groups of %d (at most %d groups)",
+                      S, Sv, ctx->groups_max);
+        a.vpr = S / Sv;
+        a.B = B * a.vpr;
+        a.S = Sv;
+        Timed tg(ctx, PE_PH_ATTN);
+        PE_HIP(pe::launch_attn_group_lens(a.B, Sv, a.vpr, P.pos, P.rej, P.seq_lens, ctx->group_lens, st),
+               "attention group lengths");
+        a.seq_lens = ctx->group_lens;
+      }
       long long grid = 2LL * ctx->num_cus;  // two 512-thread workgroups fit per CU
-      const long long mx = pe::attn_max_items(B, k.n_kv_heads, ctx->target_items);
+      const long long mx = pe::attn_max_items(a.B, k.n_kv_heads, ctx->target_items);
       a.grid = int(grid < mx ? grid : mx);
       Timed tm(ctx, PE_PH_ATTN);
       PE_HIP(pe::launch_attention(dt, a, st), "attention");
@@ -681,6 +721,78 @@ pe_status pe_ar_draft(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void*
     if (s != PE_OK) return s;
   }
   return PE_OK;
+}
+
+// ---- drafting round after a prompt ----------------------------------------
+static pe_status check_prefill_shape(pe_ctx* ctx, int32_t B, int32_t S) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if (S < ctx->cfg.K) return fail(PE_ERR_INVALID_ARG, "S=%d below K=%d", S, ctx->cfg.K);
+  if ((long long)B * S > ctx->cfg.max_prefill_slots)
+    return fail(PE_ERR_INVALID_ARG, "B*S=%lld above max_prefill_slots=%d", (long long)B * S,
+                ctx->cfg.max_prefill_slots);
+  return PE_OK;
+}
+
+pe_status pe_prefill_prepare(pe_ctx* ctx, int32_t B, int32_t S, const int32_t* chunk_tokens,
+                             const int32_t* chunk_lens, const int32_t* start_pos,
+                             const int32_t* new_tokens, const int32_t* block_table,
+                             int32_t max_blocks, int32_t num_kv_blocks, const pe_batch* out) {
+  pe_status s = check_prefill_shape(ctx, B, S);
+  if (s != PE_OK) return s;
+  if ((s = check_batch(out)) != PE_OK) return s;
+  if (B == 0) return PE_OK;
+  if (!chunk_tokens || !chunk_lens || !start_pos || !new_tokens || !block_table)
+    return fail(PE_ERR_INVALID_ARG, "a prefill input is NULL");
+  if (max_blocks < 1 || num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "max_blocks/num_kv_blocks < 1");
+  pe::PrefillArgs a;
+  a.B = B; a.K = ctx->cfg.K; a.S = S;
+  a.vocab = ctx->cfg.vocab; a.mask_id = ctx->cfg.mask_id; a.block_size = ctx->cfg.block_size;
+  a.max_blocks = max_blocks; a.num_kv_blocks = num_kv_blocks;
+  a.ct = chunk_tokens; a.lens = chunk_lens; a.start = start_pos; a.newt = new_tokens; a.bt = block_table;
+  a.ids = out->input_ids; a.pos = out->positions; a.hsrc = out->hidden_src;
+  a.draft_rows = out->draft_rows; a.seq_lens = out->seq_lens;
+  a.rej = out->is_rejected; a.msk = out->is_masked; a.slots = out->slot_mapping;
+  a.err = ctx->err;
+  Timed tm(ctx, PE_PH_PREPARE);
+  PE_HIP(pe::launch_prefill_prepare(a, ctx->stream), "prefill prepare launch");
+  return PE_OK;
+}
+
+pe_status pe_prefill_gather(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* batch,
+                            const void* target_hidden, const void* h_shared, void* draft_hidden) {
+  pe_status s = check_prefill_shape(ctx, B, S);
+  if (s != PE_OK) return s;
+  if ((s = check_gather(ctx, B, batch, target_hidden, h_shared, draft_hidden)) != PE_OK || B == 0) return s;
+  const int L = S - ctx->cfg.K + 1;
+  Timed tm(ctx, PE_PH_GATHER);
+  PE_HIP(pe::launch_gather(B * S, B * L, int(ctx->cfg.d * ctx->esz), batch->hidden_src, target_hidden,
+                           h_shared, draft_hidden, ctx->stream),
+         "prefill gather launch");
+  return PE_OK;
+}
+
+pe_status pe_prefill_forward(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* batch,
+                             const void* draft_hidden, const int32_t* block_table, int32_t max_blocks,
+                             int32_t num_kv_blocks, void* const* k_cache, void* const* v_cache,
+                             int32_t* draft_tokens, float* logits) {
+  pe_status s = check_prefill_shape(ctx, B, S);
+  if (s != PE_OK) return s;
+  s = check_forward(ctx, B, batch, draft_hidden, block_table, max_blocks, num_kv_blocks, k_cache, v_cache,
+                    draft_tokens, logits);
+  if (s != PE_OK || B == 0) return s;
+  const int G = ctx->cfg.n_q_heads / ctx->cfg.n_kv_heads, Sv = ctx->attn_group;
+  if (ctx->cfg.dtype == PE_BF16 && S * G > 512 && (S % Sv || (long long)B * (S / Sv) > ctx->groups_max))
+    return fail(PE_ERR_UNSUPPORTED, "attention: %d slots per request in groups of %d (at most %d groups)", S,
+                Sv, ctx->groups_max);
+  Pass P;
+  P.B = B; P.S = S; P.Kd = ctx->cfg.K;
+  P.ids = batch->input_ids; P.pos = batch->positions; P.draft_rows = batch->draft_rows;
+  P.seq_lens = batch->seq_lens; P.rej = batch->is_rejected; P.slots = batch->slot_mapping;
+  P.hidden = draft_hidden;
+  P.tokens = draft_tokens; P.tstride = 1;
+  P.logits = logits; P.ldl = ctx->cfg.vocab;
+  return forward_pass(ctx, P, block_table, max_blocks, num_kv_blocks, k_cache, v_cache);
 }
 
 pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens, const int32_t* target_tokens,

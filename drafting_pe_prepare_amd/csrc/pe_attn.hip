@@ -166,7 +166,7 @@ void attn_partial_kernel(AttnArgs a) {
     const int r = lo, chunk = rc - s_off[r];
     const int L = a.seq_lens[r];
     const int cb = chunk * CH, ce = min(L, cb + CH);
-    const int32_t* btr = a.bt + (long long)r * a.max_blocks;
+    const int32_t* btr = a.bt + (long long)(r / a.vpr) * a.max_blocks;
 
     // query tiles of this wave
     uint4 qf[QPW][2];
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __syncthreads();
   const float* Kc = (const float*)a.kcache;
   const float* Vc = (const float*)a.vcache;
-  const int32_t* btr = a.bt + (long long)r * a.max_blocks;
+  const int32_t* btr = a.bt + (long long)(r / a.vpr) * a.max_blocks;
   const int bs = a.block_size;
   float m = -INFINITY, lsum = 0.f, o[MAXD];
   for (int d = 0; d < hd; ++d) o[d] = 0.f;
@@ -539,8 +539,37 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// Groups of Sv consecutive slots as requests of their own (a prefill batch's
+// slots in query blocks that fit one workgroup): one wave per group.
+__global__ __launch_bounds__(256) void attn_group_lens_kernel(int Bv, int Sv, int vpr,
+                                                              const int32_t* __restrict__ positions,
+                                                              const uint8_t* __restrict__ rej,
+                                                              const int32_t* __restrict__ seq_lens,
+                                                              int32_t* __restrict__ out) {
+  const int v = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (v >= Bv) return;
+  const long long base = (long long)v * Sv;
+  int hi = -1;
+  for (int s = l; s < Sv; s += 64)
+    if (!rej[base + s]) hi = max(hi, positions[base + s]);
+  for (int o = 32; o > 0; o >>= 1) hi = max(hi, __shfl_xor(hi, o, 64));
+  if (l == 0) {
+    const int L = seq_lens[v / vpr];
+    out[v] = (L <= 0 || hi < 0) ? 0 : min(L, hi + 1);
+  }
+}
+
+hipError_t launch_attn_group_lens(int Bv, int Sv, int vpr, const int32_t* positions, const uint8_t* rej,
+                                  const int32_t* seq_lens, int32_t* out, hipStream_t st) {
+  if (Bv <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_group_lens_kernel, dim3(unsigned((Bv + 3) / 4)), dim3(256), 0, st, Bv, Sv, vpr,
+                     positions, rej, seq_lens, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
+  if (a.vpr < 1 || a.B > kMaxB) return hipErrorInvalidValue;
   if (dtype == 0) {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.B * a.S * a.Hq), dim3(64), 0, st, a);
     return hipGetLastError();

@@ -23,6 +23,17 @@ hipError_t launch_gather(int rows, int nsrc, int row_bytes, const int32_t* hsrc,
 hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32_t* acc,
                          int32_t* bonus, hipStream_t st);
 
+// Drafting round after a prompt: one workgroup per request.
+struct PrefillArgs {
+  int B, K, S, vocab, mask_id, block_size, max_blocks, num_kv_blocks;
+  const int32_t *ct, *lens, *start, *newt, *bt;  // chunk_tokens [B, S-K+1]
+  int32_t *ids, *pos, *hsrc, *draft_rows, *seq_lens;
+  uint8_t *rej, *msk;
+  int64_t* slots;
+  uint32_t* err;
+};
+hipError_t launch_prefill_prepare(const PrefillArgs& a, hipStream_t st);
+
 // Step-graph fusions: preparation + hidden-state copy; argmax + verification.
 hipError_t launch_prepare_gather(const PrepareArgs& a, int row_bytes, const void* H,
                                  const void* h_shared, void* out, hipStream_t st);
@@ -110,10 +121,16 @@ struct AttnArgs {
   const int32_t* positions; const uint8_t* rej; const int32_t* seq_lens; const int32_t* bt;
   void* out;                      // [B*S, Hq*hd]
   float* part_o; float* part_ml;  // split-KV partials (bf16 path)
+  int vpr;                        // consecutive (virtual) requests per block-table row
   int target_items;               // desired work items per launch
   int grid;                       // persistent grid size
 };
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+// Context length of each group of Sv consecutive slots (vpr groups per
+// request): 1 + the highest position of a non-rejected slot in the group,
+// capped by the request's seq_len (0 when the group has none).
+hipError_t launch_attn_group_lens(int Bv, int Sv, int vpr, const int32_t* positions, const uint8_t* rej,
+                                  const int32_t* seq_lens, int32_t* out, hipStream_t st);
 // Upper bound on split-KV work items for B requests (sizes the partials).
 long long attn_max_items(int B, int Hkv, int target_items);
 

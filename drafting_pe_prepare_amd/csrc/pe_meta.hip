@@ -145,6 +145,93 @@ hipError_t launch_gather(int rows, int nsrc, int row_bytes, const int32_t* hsrc,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Drafting round after a prompt ("P-EAGLE: parallel speculative decoding in
+// vLLM", Architecture and mechanism, Step 1 and Step 2): request r's S slots
+// are the chunk's prompt positions c0..c0+n-1 (token one position later,
+// the target's hidden state of the position; the last is the NTP slot with
+// the new token), K-1 MASK slots after them, then rejected padding.  One
+// workgroup per request, threads striding over the slots; validation with
+// workgroup-wide votes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefill_prepare_kernel(PrefillArgs a) {
+  const int r = blockIdx.x, tid = threadIdx.x, K = a.K, S = a.S, L = S - K + 1;
+  const long long base = (long long)r * S;
+  const int n = a.lens[r], c0 = a.start[r];
+  const int32_t* ct = a.ct + (long long)r * L;
+  uint32_t kinds = 0;
+  if (n < 1 || n > L) {
+    kinds |= 1u;
+  } else {
+    bool bad = false;
+    for (int j = 1 + tid; j < n; j += blockDim.x) bad |= ct[j] < 0 || ct[j] >= a.vocab;
+    if (tid == 0) bad |= a.newt[r] < 0 || a.newt[r] >= a.vocab;
+    if (__syncthreads_or(bad)) kinds |= 2u;
+  }
+  if (c0 < 0 || c0 > 0x7FFFFFFF - S) kinds |= 4u;
+  if (kinds == 0) {
+    const int seq_len = c0 + n + K - 1;
+    const int nb = (seq_len + a.block_size - 1) / a.block_size;
+    bool bad = nb > a.max_blocks;
+    if (!bad) {
+      const int32_t* btr = a.bt + (long long)r * a.max_blocks;
+      for (int b = tid; b < nb; b += blockDim.x) bad |= btr[b] < 0 || btr[b] >= a.num_kv_blocks;
+    }
+    if (__syncthreads_or(bad)) kinds |= 4u;
+  }
+  if (kinds) {
+    for (int j = tid; j < S; j += blockDim.x) {
+      a.ids[base + j] = 0;
+      a.pos[base + j] = 0;
+      a.hsrc[base + j] = -1;
+      a.rej[base + j] = 1;
+      a.msk[base + j] = 0;
+      a.slots[base + j] = -1;
+    }
+    if (tid < K) a.draft_rows[r * K + tid] = int(base) + tid;
+    if (tid == 0) {
+      a.seq_lens[r] = 0;
+      atomicOr(&a.err[0], kinds);
+      atomicMin(&a.err[1], uint32_t(r));
+    }
+    return;
+  }
+  const int32_t* btr = a.bt + (long long)r * a.max_blocks;
+  const int valid = n + K - 1;
+  for (int j = tid; j < S; j += blockDim.x) {
+    int tok = 0, p = 0, src = -1;
+    uint8_t rej = 0, msk = 0;
+    long long slot = -1;
+    if (j < valid) {
+      p = c0 + j;
+      if (j < n) {
+        src = r * L + j;
+        tok = j < n - 1 ? ct[j + 1] : a.newt[r];
+      } else {
+        tok = a.mask_id;
+        msk = 1;
+      }
+      slot = (long long)btr[p / a.block_size] * a.block_size + p % a.block_size;
+    } else {
+      rej = 1;
+    }
+    a.ids[base + j] = tok;
+    a.pos[base + j] = p;
+    a.hsrc[base + j] = src;
+    a.rej[base + j] = rej;
+    a.msk[base + j] = msk;
+    a.slots[base + j] = slot;
+  }
+  if (tid < K) a.draft_rows[r * K + tid] = int(base) + n - 1 + tid;
+  if (tid == 0) a.seq_lens[r] = c0 + valid;
+}
+
+hipError_t launch_prefill_prepare(const PrefillArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_prepare_kernel, dim3(unsigned(a.B)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // Preparation and hidden-state copy in one launch, for the step graph: one
 // workgroup per (slot j, request r).  Every workgroup loads its slot's source
 // row (slot j <= K copies target row r(K+1)+j) while wave 0 validates the

@@ -9,10 +9,14 @@
  * pe_step_graph captures the four into one hipGraph and replays it.
  * pe_ar_draft runs the same kernels as K sequential drafting passes, the
  * autoregressive baseline, in place of pe_draft_forward.
+ * pe_prefill_prepare / pe_prefill_gather / pe_prefill_forward draft the first
+ * round after a prompt: prompt positions, the NTP position and K-1 MASK
+ * positions in one pass.
  *
  * Sources (page titles as published):
  *   [P1] "P-EAGLE: parallel speculative decoding in vLLM" -- sections
- *        "Architecture and mechanism" (Step 2, Parallel Drafting), "vLLM
+ *        "Architecture and mechanism" (Step 1, Prefilling; Step 2, Parallel
+ *        Drafting), "vLLM
  *        implementation details" (Fused Triton kernel; Hidden-state
  *        management; KV cache and CUDA Graphs), "Benchmarks" (Acceptance length).
  *   [P3] "AWS and vLLM ship P-EAGLE" -- "How it works", "Integration and numbers".
@@ -79,6 +83,8 @@ typedef struct pe_config {
   int32_t dtype;        /* pe_dtype */
   float rms_eps;        /* RMSNorm epsilon */
   float rope_theta;     /* RoPE base */
+  int32_t max_prefill_slots; /* largest B*S of a drafting round after a prompt
+                                (pe_prefill_*); 0 = none */
 } pe_config;
 
 /* Device pointers of one decoder layer.  Linear weights are [out, in]. */
@@ -205,6 +211,58 @@ pe_status pe_ar_draft(pe_ctx* ctx, int32_t B, const pe_batch* batch,
  * draft_tokens [B, K], target_tokens [B, K+1] int32 in; outputs [B] int32. */
 pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens,
                     const int32_t* target_tokens, int32_t* num_accepted, int32_t* bonus_tokens);
+
+/* ---- Drafting round after a prompt ------------------------------------------
+ * [P1, Architecture and mechanism: Step 1, Prefilling -- the target runs the
+ * prompt and returns a hidden state per position and one new token; Step 2,
+ * Parallel Drafting -- a prompt position pairs the embedding of the token one
+ * position later with the target's hidden state there, the NTP position pairs
+ * the new token with the last hidden state, positions 2..K take emb(mask) and
+ * h_shared; all go through the drafter in one pass.]
+ * A prefill batch has a fixed stride of S slots per request (K <= S), and
+ * L = S-K+1 rows per request in chunk_tokens and target_hidden.  Request r
+ * covers prompt positions c0..c0+n-1 (c0 = start_pos[r], n = chunk_lens[r] in
+ * [1, L]); positions below c0 were drafted by earlier calls and are in the KV
+ * cache:
+ *   copied slot j = 0..n-1: position c0+j, hidden_src r*L+j, token
+ *     chunk_tokens[r][j+1] (j < n-1) or new_tokens[r] (j = n-1: the NTP slot);
+ *   MASK slot j = n..n+K-2: token mask_id, position c0+j, hidden_src -1;
+ *   slot j >= n+K-1: rejected padding (PE_PAD_TOKEN, position 0, hidden_src
+ *     -1, KV slot -1);
+ *   draft_rows[r] = {r*S+n-1, ..., r*S+n+K-2}; seq_lens[r] = c0+n+K-1.
+ * A chunk that does not end the prompt is the same call with new_tokens[r] =
+ * the next prompt token: its drafts are ignored, and the next chunk
+ * overwrites the KV its MASK slots wrote.  Device errors: n outside [1, L]
+ * (PE_DEVERR_ACCEPTED), a token the request reads outside [0, vocab)
+ * (PE_DEVERR_TOKEN), c0 < 0 or a block of [0, seq_len) missing
+ * (PE_DEVERR_BLOCK); the request becomes padding as in pe_prepare.
+ * Sizes: B <= max_num_seqs, B*S <= cfg.max_prefill_slots; pe_batch buffers
+ * hold B*S slots (draft_rows B*K, seq_lens B). */
+
+/* Batch preparation of a prefill batch.  chunk_tokens [B, L] int32: column j
+ * is the prompt token at position c0+j; chunk_lens, start_pos, new_tokens
+ * [B] int32; block_table [B, max_blocks] int32; all device. */
+pe_status pe_prefill_prepare(pe_ctx* ctx, int32_t B, int32_t S, const int32_t* chunk_tokens,
+                             const int32_t* chunk_lens, const int32_t* start_pos,
+                             const int32_t* new_tokens, const int32_t* block_table,
+                             int32_t max_blocks, int32_t num_kv_blocks, const pe_batch* out);
+
+/* Hidden-state copy of a prefill batch, as pe_gather_hidden:
+ * target_hidden [B*L, d], draft_hidden [B*S, d]. */
+pe_status pe_prefill_gather(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* batch,
+                            const void* target_hidden, const void* h_shared, void* draft_hidden);
+
+/* One drafter forward over the B*S slots of a prefill batch, as
+ * pe_draft_forward: draft_tokens [B*K] (t_1..t_K per request), logits NULL or
+ * [B*K, vocab].  PE_BF16 attention takes a request's slots in groups of
+ * 512/(n_q_heads/n_kv_heads) rounded down to a power of two: S must be at most
+ * one group or a multiple of it, and B*S/group <= 1024
+ * (PE_ERR_UNSUPPORTED otherwise). */
+pe_status pe_prefill_forward(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* batch,
+                             const void* draft_hidden,
+                             const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                             void* const* k_cache, void* const* v_cache,
+                             int32_t* draft_tokens, float* logits);
 
 /* Drafting pass of a step graph: pe_draft_forward or pe_ar_draft. */
 typedef enum pe_step_mode { PE_STEP_PARALLEL = 0, PE_STEP_AUTOREGRESSIVE = 1 } pe_step_mode;

@@ -30,11 +30,12 @@ def oracle_precision(w):
 class Setup:
     """Weights and a context for workload `w` (weights uploaded once)."""
 
-    def __init__(self, w, seed=None, max_B=None, prm=None):
+    def __init__(self, w, seed=None, max_B=None, prm=None, max_prefill_slots=0):
         self.w = w
         self.prm = synth.weights(w, seed) if prm is None else prm
         self.dev = pb.upload_weights(self.prm)
-        self.ctx = pb.Context(w, self.dev, max_num_seqs=max_B or w.batch)
+        self.ctx = pb.Context(w, self.dev, max_num_seqs=max_B or w.batch,
+                              max_prefill_slots=max_prefill_slots)
 
     def close(self):
         self.ctx.close()

@@ -132,6 +132,16 @@ def test_small_bf16_split_k(K, B, seed):
     _full_check(w, seed)
 
 
+@pytest.mark.parametrize("d,vocab,B", [(1024, 1024, 1), (1536, 2048, 2), (2048, 4096, 1)])
+def test_small_bf16_lm_head_tiles_cut_between_waves(d, vocab, B):
+    """Up to 16 draft rows with few vocabulary tiles per CU and several
+    k-units per tile: the LDS-resident LM head cuts tiles between waves, some
+    waves get no units, and the cut tiles' pieces are summed across them."""
+    w = SMALL_BF16.with_(K=7, batch=B, d=d, vocab=vocab, mlp=1024, weight_std=1 / np.sqrt(d),
+                         accepted="uniform", prefix=("uniform", 30, 200))
+    _full_check(w, seed=85 + B)
+
+
 @pytest.mark.parametrize("B", [5, 12])
 def test_small_bf16_tiled_path(B):
     """B*2K > 64 rows: the LDS-tiled GEMM path and the tiled LM head."""
