@@ -43,6 +43,8 @@ def parse():
                    help="skip the sequential (autoregressive) comparison")
     p.add_argument("--no-maxbatch", action="store_true",
                    help="skip the B=256 largest-graph workload")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the drafting round after a 2048-position prompt")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -307,6 +309,71 @@ def ksweep(steps, warmup):
             "vocab": base.vocab, "prefix": list(base.prefix), "seed": base.seed, "rows": rows}
 
 
+def prefill(w, prm, dev, prompt, steps, warmup):
+    """The drafting round after a prompt of `prompt` positions (one request,
+    the c=1 drafter): prompt positions + NTP + K-1 MASK slots in one pass,
+    S padded to a multiple of the 64-slot attention group; eager calls
+    (prepare, gather, forward), timed with events on the library's stream."""
+    import numpy as np
+    import torch
+    from drafting_pe_prepare_amd import binding as pb
+    from drafting_pe_prepare_amd import synth
+    B, K = 1, w.K
+    S = (prompt + K - 1 + 63) // 64 * 64
+    w1 = w.with_(batch=B)
+    inp = synth.prefill_inputs(w1, S, ("fixed", prompt), ("fixed", 0))
+    ctx = pb.Context(w1, dev, max_num_seqs=B, max_prefill_slots=B * S)
+    t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+         ("chunk_tokens", "chunk_lens", "start_pos", "new_tokens", "block_table", "target_hidden")}
+    kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+    ks, vs = [k for k, _ in kv], [v for _, v in kv]
+    batch = pb.Batch(B, K, S=S)
+    dh = torch.zeros((B * S, w.d), dtype=torch.bfloat16, device="cuda")
+    tok = torch.zeros(B * K, dtype=torch.int32, device="cuda")
+    nkv = int(inp["num_kv_blocks"])
+
+    def round_():
+        pb.pe_prefill_prepare(ctx, B, S, t["chunk_tokens"], t["chunk_lens"], t["start_pos"],
+                              t["new_tokens"], t["block_table"], nkv, batch)
+        pb.pe_prefill_gather(ctx, B, S, batch, t["target_hidden"], dev["h_shared"], dh)
+        pb.pe_prefill_forward(ctx, B, S, batch, dh, t["block_table"], nkv, ks, vs, tok)
+
+    for _ in range(warmup):
+        round_()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        round_()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    err = pb.pe_get_device_error(ctx)
+    assert err == (0, -1), f"device error word {err}"
+    pb.pe_profile_enable(ctx, True)
+    pb.pe_profile_read(ctx, reset=True)
+    for _ in range(max(3, steps // 4)):
+        round_()
+    prof = pb.pe_profile_read(ctx, reset=True)
+    pb.pe_profile_enable(ctx, False)
+    n_prof = max(3, steps // 4)
+    phases = {p: round(ms / n_prof * 1e3, 2) for p, (ms, n) in prof.items() if n}
+    print(f"[bench] prefill {prompt}: {us:.1f} us/round", file=sys.stderr, flush=True)
+    valid = prompt + K - 1
+    qd, kvd, d = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim, w.d
+    dense = 2 * d * d + w.layers * (qd * d + 2 * kvd * d + d * qd + 3 * w.mlp * d)
+    att = sum(q + 1 for q in range(valid))
+    flops = 2 * valid * dense + 2 * B * K * w.vocab * d + w.layers * 4 * w.head_dim * w.n_q_heads * att
+    ctx.close()
+    return {"workload": f"{w.name} drafting round after a {prompt}-position prompt (B=1, K={K}, S={S})",
+            "us_per_round": us, "prompt_positions_per_s": prompt / (us * 1e-6),
+            "draft_tokens_per_s": B * K / (us * 1e-6), "algorithmic_flops": flops,
+            "mfma_TFs": flops / (us * 1e-6) / 1e12,
+            "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS,
+            "phases_us_per_round": phases, "timing": "eager calls, HIP events, inputs resident"}
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
@@ -390,6 +457,8 @@ def main():
         line["maxbatch"]["config"]["weights"] = "same drafter weights as the c=1 workload"
     if not args.no_ksweep and w.name == "c1_20b":
         line["ksweep"] = ksweep(max(20, args.steps // 5), max(3, args.warmup // 4))
+    if not args.no_prefill and w.name == "c1_20b":
+        line["prefill"] = prefill(w, prm, dev, 2048, max(10, args.steps // 10), 3)
     if not args.no_cpu_baseline:
         del dev
         torch.cuda.empty_cache()

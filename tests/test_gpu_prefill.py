@@ -186,3 +186,10 @@ def test_prefill_rejects_oversized_batches():
                                   [k for k, _ in kv], [v for _, v in kv], tok)
     finally:
         st.close()
+
+
+@pytest.mark.slow
+def test_prefill_full_c1():
+    """The c=1 20B-class drafter after a 2048-position prompt (S = 2112: 33
+    slot groups), every output checked."""
+    _check(configs.C1.with_(batch=1), 2112, ("fixed", 2048), ("fixed", 0), seed=71)
