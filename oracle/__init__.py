@@ -14,6 +14,9 @@ What it follows (page titles as published):
     metadata; Hidden-state management: the hidden-state copy; KV cache:
     PADDING_SLOT_ID = -1 for rejected tokens); Architecture and mechanism,
     Step 1 (Prefilling) for the drafting round that follows a prompt.
+  * "vLLM Speculators: parallel drafting for speculative decoding" --
+    Production integration (verification by rejection sampling keeps the
+    verifier's output distribution): pe_sampling.py.
   * "AWS and vLLM ship P-EAGLE" -- How it works (learned mask embedding and
     shared hidden vector for positions that do not exist yet); Integration and
     numbers (acceptance length = drafts the verifier accepts per round).
@@ -23,6 +26,10 @@ that takes it.  Parity status of every function is pinned by tests under
 tests/ (test_oracle_*.py); acceptance length on trained weights is parity
 unpinned (no trained weights exist here).
 """
+from .pe_sampling import (  # noqa: F401
+    STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL, philox4x32, uniform, gumbel, log_softmax,
+    sample_drafts, rejection_verify,
+)
 from .pe_oracle import (  # noqa: F401
     PAD_TOKEN, PADDING_SLOT_ID, ERR_ACCEPTED, ERR_TOKEN, ERR_BLOCK, ERR_LAYOUT,
     round_bf16, widen, prepare, prepare_prefill, gather_hidden, rmsnorm, rope, silu,
