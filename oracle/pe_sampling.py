@@ -17,7 +17,9 @@ Random numbers (the contract both sides implement from the published
 definition): Philox4x32-10 ("Parallel random numbers: as easy as 1, 2, 3",
 Salmon, Moraes, Dror, Shaw, SC 2011) with key (seed mod 2^32, seed >> 32)
 and counter (c0, c1, c2, stream); the first output word x gives
-U = (floor(x / 256) + 1/2) / 2^24 in (0, 1).  Streams:
+U = (floor(x / 512) + 1/2) / 2^23 in (0, 1), a lattice that float32 holds
+exactly (so both sides draw the same U and 1 - U is never rounded to 0).
+Streams:
   STREAM_DRAFT    counter (v, i, 0): Gumbel noise of draft row i = r*K + j, token v
   STREAM_ACCEPT   counter (j, r, 0): the acceptance uniform of request r, draft j
   STREAM_RESIDUAL counter (v, r, 0): Gumbel noise of the token emitted for request r
@@ -62,7 +64,7 @@ def uniform(seed, stream, c0, c1):
     ctr = np.stack([c0, c1, np.zeros_like(c0), np.full_like(c0, stream)], axis=-1)
     key = np.array([int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF], dtype=np.uint64)
     x = philox4x32(ctr, key)[..., 0].astype(np.float64)
-    return (np.floor(x / 256.0) + 0.5) / 2.0 ** 24
+    return (np.floor(x / 512.0) + 0.5) / 2.0 ** 23
 
 
 def gumbel(u):

@@ -33,8 +33,9 @@ def test_uniform_range_and_streams():
     u = O.uniform(1234, O.STREAM_DRAFT, np.arange(200000), 7)
     assert np.all(u > 0) and np.all(u < 1)
     assert abs(u.mean() - 0.5) < 3e-3 and abs(u.var() - 1 / 12) < 2e-3
-    # 24-bit lattice: U * 2^24 - 1/2 is an integer
-    assert np.all(np.abs(u * 2 ** 24 - 0.5 - np.round(u * 2 ** 24 - 0.5)) == 0)
+    # 23-bit lattice, exact in float32: U * 2^23 - 1/2 is an integer
+    assert np.all(np.abs(u * 2 ** 23 - 0.5 - np.round(u * 2 ** 23 - 0.5)) == 0)
+    np.testing.assert_array_equal(u.astype(np.float32).astype(np.float64), u)
     u2 = O.uniform(1234, O.STREAM_ACCEPT, np.arange(1000), 7)
     u3 = O.uniform(1235, O.STREAM_DRAFT, np.arange(1000), 7)
     assert not np.array_equal(u[:1000], u2) and not np.array_equal(u[:1000], u3)
