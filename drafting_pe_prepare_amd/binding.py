@@ -23,7 +23,8 @@ DEVERR_ACCEPTED, DEVERR_TOKEN, DEVERR_BLOCK, DEVERR_LAYOUT = 1, 2, 4, 8
 
 EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_hidden",
            "pe_draft_forward", "pe_ar_draft", "pe_verify", "pe_prefill_prepare", "pe_prefill_gather",
-           "pe_prefill_forward", "pe_step_graph", "pe_get_device_error",
+           "pe_prefill_forward", "pe_draft_forward_sampled", "pe_verify_sampled", "pe_step_graph",
+           "pe_get_device_error",
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
           "verify", "argmax", "ar")
@@ -99,6 +100,9 @@ def load(path: str = LIB_PATH):
     lib.pe_prefill_prepare.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, i32, i32, P(PeBatch)]
     lib.pe_prefill_gather.argtypes = [vp, i32, i32, P(PeBatch), vp, vp, vp]
     lib.pe_prefill_forward.argtypes = [vp, i32, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp), vp, vp]
+    lib.pe_draft_forward_sampled.argtypes = [vp, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp),
+                                             ctypes.c_float, vp, vp, vp]
+    lib.pe_verify_sampled.argtypes = [vp, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.pe_step_graph.argtypes = [vp, i32, P(PeStepArgs)]
     lib.pe_get_device_error.argtypes = [vp, P(ctypes.c_uint32), P(i32)]
     lib.pe_profile_enable.argtypes = [vp, ctypes.c_int]
@@ -249,6 +253,22 @@ def pe_prefill_forward(ctx: Context, B, S, batch: Batch, draft_hidden, block_tab
     _check(_lib.pe_prefill_forward(ctx.h, B, S, ctypes.byref(batch.c), _ptr(draft_hidden),
                                    _ptr(block_table), block_table.shape[1], num_kv_blocks,
                                    kc, vc, _ptr(draft_tokens), _ptr(logits)))
+
+
+def pe_draft_forward_sampled(ctx: Context, B, batch: Batch, draft_hidden, block_table, num_kv_blocks,
+                             k_caches, v_caches, temperature, seed, draft_tokens, logits=None):
+    """seed: a device tensor holding one 64-bit key (int64)."""
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    _check(_lib.pe_draft_forward_sampled(ctx.h, B, ctypes.byref(batch.c), _ptr(draft_hidden),
+                                         _ptr(block_table), block_table.shape[1], num_kv_blocks,
+                                         kc, vc, float(temperature), _ptr(seed), _ptr(draft_tokens),
+                                         _ptr(logits)))
+
+
+def pe_verify_sampled(ctx: Context, B, draft_tokens, draft_logits, target_logits, temperature, seed,
+                      num_accepted, next_tokens):
+    _check(_lib.pe_verify_sampled(ctx.h, B, _ptr(draft_tokens), _ptr(draft_logits), _ptr(target_logits),
+                                  float(temperature), _ptr(seed), _ptr(num_accepted), _ptr(next_tokens)))
 
 
 def pe_verify(ctx: Context, B, draft_tokens, target_tokens, num_accepted, bonus_tokens):

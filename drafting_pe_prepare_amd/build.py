@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpe.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["pe_meta.hip", "pe_norm.hip", "pe_gemm.hip", "pe_attn.hip", "pe_api.cpp"]
+SOURCES = ["pe_meta.hip", "pe_norm.hip", "pe_gemm.hip", "pe_attn.hip", "pe_sample.hip", "pe_api.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -66,6 +66,8 @@ struct pe_ctx {
   uint32_t* err = nullptr;    // [2] kinds, first request
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  float* sample_lse = nullptr;     // rejection sampling: log-sum-exp per logit row
+  uint64_t* sample_keys = nullptr; // rejection sampling: partial draw keys
   int32_t* group_lens = nullptr; // attention context length per slot group (bf16)
   int attn_group = 64;           // slots per attention workgroup: 512 / G rounded down to a power of two
   int groups_max = 0;            // slot groups the attention buffers are sized for
@@ -143,7 +145,8 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->rope_turns, c->lm_packed, c->splitk, c->group_lens};
+                  c->part_o, c->part_ml, c->rope_turns, c->lm_packed, c->splitk, c->group_lens,
+                  c->sample_lse, c->sample_keys};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   if (c->fc_packed) (void)hipFree(c->fc_packed);
@@ -312,6 +315,8 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {reinterpret_cast<void**>(&c->ar_rej), R1, "ar rejected"},
       {reinterpret_cast<void**>(&c->ar_slots), R1 * 8, "ar slots"},
       {&c->ar_hidden, R1 * k.d * c->esz, "ar hidden"},
+      {reinterpret_cast<void**>(&c->sample_lse), size_t(k.max_num_seqs) * (2 * k.K + 1) * 4, "sampling lse"},
+      {reinterpret_cast<void**>(&c->sample_keys), size_t(k.max_num_seqs) * pe::kSampleParts * 8, "sampling keys"},
   };
   for (auto& p : plan) {
     if ((s = alloc(p.p, p.bytes, p.what)) != PE_OK) { free_ctx(c); return s; }
@@ -492,6 +497,9 @@ struct Pass {
   // when set (tstride 1, Kd = K): greedy verification fused into the argmax
   const int32_t* vtarget = nullptr;
   int32_t *vacc = nullptr, *vbonus = nullptr;
+  // when set: draft tokens drawn from softmax(logits / T) instead of argmax
+  const uint64_t* seed = nullptr;
+  float inv_temp = 1.f;
 };
 
 static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_table,
@@ -624,6 +632,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     g.keys = ctx->keys; g.logits = P.logits; g.ldl = P.ldl;
     g.parts = pe::gemm_argmax_parts(dt, D, k.vocab, d, ctx->num_cus);
     g.seq_lens = P.seq_lens; g.Kd = P.Kd;
+    g.seed = P.seed; g.inv_temp = P.inv_temp;
     {
       Timed tm(ctx, PE_PH_LMHEAD);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
@@ -793,6 +802,51 @@ pe_status pe_prefill_forward(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* 
   P.tokens = draft_tokens; P.tstride = 1;
   P.logits = logits; P.ldl = ctx->cfg.vocab;
   return forward_pass(ctx, P, block_table, max_blocks, num_kv_blocks, k_cache, v_cache);
+}
+
+// ---- stochastic drafting and verification by rejection sampling ------------
+static pe_status check_sampling(float temperature, const uint64_t* seed) {
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(PE_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  if (!seed || !aligned(seed, 8)) return fail(PE_ERR_INVALID_ARG, "seed NULL or not 8-byte aligned");
+  return PE_OK;
+}
+
+pe_status pe_draft_forward_sampled(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* draft_hidden,
+                                   const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                                   void* const* k_cache, void* const* v_cache, float temperature,
+                                   const uint64_t* seed, int32_t* draft_tokens, float* logits) {
+  pe_status s = check_forward(ctx, B, batch, draft_hidden, block_table, max_blocks, num_kv_blocks,
+                              k_cache, v_cache, draft_tokens, logits);
+  if (s != PE_OK) return s;
+  if ((s = check_sampling(temperature, seed)) != PE_OK || B == 0) return s;
+  const int K = ctx->cfg.K;
+  Pass P;
+  P.B = B; P.S = 2 * K; P.Kd = K;
+  P.ids = batch->input_ids; P.pos = batch->positions; P.draft_rows = batch->draft_rows;
+  P.seq_lens = batch->seq_lens; P.rej = batch->is_rejected; P.slots = batch->slot_mapping;
+  P.hidden = draft_hidden;
+  P.tokens = draft_tokens; P.tstride = 1;
+  P.logits = logits; P.ldl = ctx->cfg.vocab;
+  P.seed = seed; P.inv_temp = 1.f / temperature;
+  return forward_pass(ctx, P, block_table, max_blocks, num_kv_blocks, k_cache, v_cache);
+}
+
+pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens, const float* draft_logits,
+                            const float* target_logits, float temperature, const uint64_t* seed,
+                            int32_t* num_accepted, int32_t* next_tokens) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if ((s = check_sampling(temperature, seed)) != PE_OK || B == 0) return s;
+  if (!draft_tokens || !num_accepted || !next_tokens) return fail(PE_ERR_INVALID_ARG, "a verify buffer is NULL");
+  if (!draft_logits || !target_logits || !aligned(draft_logits, 16) || !aligned(target_logits, 16))
+    return fail(PE_ERR_INVALID_ARG, "logit rows NULL or not 16-byte aligned");
+  Timed tm(ctx, PE_PH_VERIFY);
+  PE_HIP(pe::launch_verify_sampled(B, ctx->cfg.K, ctx->cfg.vocab, 1.f / temperature, draft_tokens, draft_logits,
+                                   target_logits, seed, ctx->sample_lse, ctx->sample_keys, num_accepted,
+                                   next_tokens, ctx->stream),
+         "sampled verify launch");
+  return PE_OK;
 }
 
 pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens, const int32_t* target_tokens,

@@ -34,6 +34,14 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill_prepare(const PrefillArgs& a, hipStream_t st);
 
+// Verification by rejection sampling over fp32 logits: drafter rows [B*K, V],
+// verifier rows [B*(K+1), V]; workspace lse [B*(2K+1)], keys [B*kSampleParts].
+constexpr int kSampleParts = 64;
+hipError_t launch_verify_sampled(int B, int K, int V, float inv_temp, const int32_t* draft_tokens,
+                                 const float* draft_logits, const float* target_logits,
+                                 const uint64_t* seed, float* lse, uint64_t* keys,
+                                 int32_t* accepted, int32_t* next_tokens, hipStream_t st);
+
 // Step-graph fusions: preparation + hidden-state copy; argmax + verification.
 hipError_t launch_prepare_gather(const PrepareArgs& a, int row_bytes, const void* H,
                                  const void* h_shared, void* out, hipStream_t st);
@@ -92,6 +100,10 @@ struct GemmArgs {
   uint64_t* keys; int parts;                      // E_ARGMAX: keys[row * parts + part]
   int32_t* tokens; float* logits; int ldl;         // logits[row * ldl + n]
   const int32_t* seq_lens; int Kd;
+  // E_ARGMAX with sampling: when seed is set, row m ranks logit * inv_temp +
+  // Gumbel noise of (m, column) (a draw from softmax(logit / T)); logits
+  // stay raw
+  const uint64_t* seed; float inv_temp;
   // split-K: fp32 partial sums [ksplit][M][N] (logical columns) for GEMMs with
   // too few output tiles to fill the chip; the epilogue runs after the sum
   float* part; long long part_cap;  // capacity in floats (0: never split)

@@ -12,6 +12,8 @@
  * pe_prefill_prepare / pe_prefill_gather / pe_prefill_forward draft the first
  * round after a prompt: prompt positions, the NTP position and K-1 MASK
  * positions in one pass.
+ * pe_draft_forward_sampled / pe_verify_sampled draw the drafts and verify them
+ * by rejection sampling instead of greedily.
  *
  * Sources (page titles as published):
  *   [P1] "P-EAGLE: parallel speculative decoding in vLLM" -- sections
@@ -19,6 +21,8 @@
  *        Drafting), "vLLM
  *        implementation details" (Fused Triton kernel; Hidden-state
  *        management; KV cache and CUDA Graphs), "Benchmarks" (Acceptance length).
+ *   [P2] "vLLM Speculators: parallel drafting for speculative decoding" --
+ *        "Production integration" (verification by rejection sampling).
  *   [P3] "AWS and vLLM ship P-EAGLE" -- "How it works", "Integration and numbers".
  *
  * Conventions for every entry point
@@ -263,6 +267,47 @@ pe_status pe_prefill_forward(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* 
                              const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
                              void* const* k_cache, void* const* v_cache,
                              int32_t* draft_tokens, float* logits);
+
+/* ---- Stochastic drafting and verification by rejection sampling -------------
+ * [P2, Production integration: speculative decoding verifies by rejection
+ * sampling, so the output keeps the verifier's distribution.]  With
+ * temperature T, q_j = softmax(z_j / T) is the drafter's distribution at draft
+ * row j of a request and p_j = softmax(y_j / T) the verifier's at the same
+ * position:
+ *   drafts    t_j is a draw from q_j;
+ *   accept    t_j is kept while U_j < min(1, p_j(t_j) / q_j(t_j));
+ *   emit      at the first rejection j: a draw from max(0, p_j - q_j),
+ *             normalised (num_accepted = j); after K kept drafts: a draw from
+ *             p_K (num_accepted = K).
+ * Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011), key = *seed (64 bits, low word
+ * first), counter (c0, c1, 0, stream); U = ((x >> 9) + 1/2) / 2^23 from the
+ * first output word x.  A draw from w is argmax_v(log w(v) - log(-log U_v))
+ * (Gumbel-max; lowest index on ties) with
+ *   drafting: stream 0, counter (v, draft row r*K+j);
+ *   acceptance: stream 1, counter (j, r);
+ *   emitted token: stream 2, counter (v, r).
+ * seed is a device pointer (8-byte aligned), read by the kernels, so a caller
+ * can change it between graph replays. */
+
+/* As pe_draft_forward, with each draft token drawn from softmax(logits / T)
+ * instead of the argmax.  logits (when not NULL) receives the raw logits,
+ * which pe_verify_sampled needs as draft_logits. */
+pe_status pe_draft_forward_sampled(pe_ctx* ctx, int32_t B, const pe_batch* batch,
+                                   const void* draft_hidden,
+                                   const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                                   void* const* k_cache, void* const* v_cache, float temperature,
+                                   const uint64_t* seed, int32_t* draft_tokens, float* logits);
+
+/* Verification by rejection sampling.  draft_tokens [B, K] int32 (a token
+ * outside [0, vocab), e.g. -1 of a padded request, is rejected);
+ * draft_logits [B*K, vocab] float32 (the drafter's rows); target_logits
+ * [B*(K+1), vocab] float32 (the verifier's rows at the K+1 positions);
+ * num_accepted [B] and next_tokens [B] int32 out (the emitted token: the
+ * residual draw or the bonus draw).  All device; logit rows 16-byte aligned. */
+pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens,
+                            const float* draft_logits, const float* target_logits, float temperature,
+                            const uint64_t* seed, int32_t* num_accepted, int32_t* next_tokens);
 
 /* Drafting pass of a step graph: pe_draft_forward or pe_ar_draft. */
 typedef enum pe_step_mode { PE_STEP_PARALLEL = 0, PE_STEP_AUTOREGRESSIVE = 1 } pe_step_mode;
