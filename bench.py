@@ -43,6 +43,8 @@ def parse():
                    help="skip the sequential (autoregressive) comparison")
     p.add_argument("--no-maxbatch", action="store_true",
                    help="skip the B=256 largest-graph workload")
+    p.add_argument("--no-sampling", action="store_true",
+                   help="skip the stochastic drafting / rejection-sampling verification timing")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the drafting round after a 2048-position prompt")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,6 +376,66 @@ def prefill(w, prm, dev, prompt, steps, warmup):
             "phases_us_per_round": phases, "timing": "eager calls, HIP events, inputs resident"}
 
 
+def sampling(w, prm, dev, steps, T=1.0):
+    """Stochastic drafting and rejection-sampling verification on workload w:
+    the parallel forward with logits written, greedy and with Gumbel draws,
+    and pe_verify_sampled over those logits and seeded verifier logits (eager
+    calls, HIP events on the library's stream, inputs resident)."""
+    import numpy as np
+    import torch
+    from drafting_pe_prepare_amd import binding as pb
+    from drafting_pe_prepare_amd import synth
+    B, K, V = w.batch, w.K, w.vocab
+    inp = synth.step_inputs(w)
+    ctx = pb.Context(w, dev, max_num_seqs=B)
+    t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+         ("verify_tokens", "verify_positions", "num_accepted", "bonus_tokens", "block_table", "target_hidden")}
+    kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+    ks, vs = [k for k, _ in kv], [v for _, v in kv]
+    batch = pb.Batch(B, K)
+    nkv = int(inp["num_kv_blocks"])
+    dh = torch.zeros((B * 2 * K, w.d), dtype=torch.bfloat16, device="cuda")
+    tok = torch.zeros(B * K, dtype=torch.int32, device="cuda")
+    lg = torch.zeros((B * K, V), dtype=torch.float32, device="cuda")
+    tl = synth.normal(w.seed, "verifier_logits", (B * (K + 1), V), 2.0, dtype="f32")
+    tl = pb.to_device(np.ascontiguousarray(tl))
+    seed = torch.tensor([12345], dtype=torch.int64, device="cuda")
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    pb.pe_prepare(ctx, B, t["verify_tokens"], t["verify_positions"], t["num_accepted"], t["bonus_tokens"],
+                  t["block_table"], nkv, batch)
+    pb.pe_gather_hidden(ctx, B, batch, t["target_hidden"], dev["h_shared"], dh)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    greedy = timed(lambda: pb.pe_draft_forward(ctx, B, batch, dh, t["block_table"], nkv, ks, vs, tok, lg))
+    sampled = timed(lambda: pb.pe_draft_forward_sampled(ctx, B, batch, dh, t["block_table"], nkv, ks, vs,
+                                                        T, seed, tok, lg))
+    verify = timed(lambda: pb.pe_verify_sampled(ctx, B, tok, lg, tl, T, seed, acc, nxt))
+    err = pb.pe_get_device_error(ctx)
+    assert err == (0, -1), f"device error word {err}"
+    ctx.close()
+    vbytes = B * (2 * K + 1) * V * 4 * 2  # log-sum-exp pass, then the emitting rows (at most twice)
+    print(f"[bench] sampling {w.name}: forward {greedy:.1f} -> {sampled:.1f} us, verify {verify:.1f} us",
+          file=sys.stderr, flush=True)
+    return {"workload": w.name, "temperature": T,
+            "forward_with_logits_greedy_us": greedy, "forward_with_logits_sampled_us": sampled,
+            "verify_sampled_us": verify,
+            "verify_bytes_bound": vbytes, "verify_GBs": vbytes / (verify * 1e-6) / 1e9,
+            "timing": "eager calls, HIP events, inputs resident; verifier logits seeded N(0, 2)"}
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
@@ -457,6 +519,9 @@ def main():
         line["maxbatch"]["config"]["weights"] = "same drafter weights as the c=1 workload"
     if not args.no_ksweep and w.name == "c1_20b":
         line["ksweep"] = ksweep(max(20, args.steps // 5), max(3, args.warmup // 4))
+    if not args.no_sampling and w.name == "c1_20b":
+        line["sampling"] = {"c1": sampling(w, prm, dev, max(10, args.steps // 10)),
+                            "c64": sampling(configs.C64, prm, dev, max(5, args.steps // 20))}
     if not args.no_prefill and w.name == "c1_20b":
         line["prefill"] = prefill(w, prm, dev, 2048, max(10, args.steps // 10), 3)
     if not args.no_cpu_baseline:

@@ -67,6 +67,7 @@ struct pe_ctx {
   float* part_o = nullptr;
   float* part_ml = nullptr;
   float* sample_lse = nullptr;     // rejection sampling: log-sum-exp per logit row
+  float* sample_parts = nullptr;   // rejection sampling: (max, sum exp) per row slice
   uint64_t* sample_keys = nullptr; // rejection sampling: partial draw keys
   int32_t* group_lens = nullptr; // attention context length per slot group (bf16)
   int attn_group = 64;           // slots per attention workgroup: 512 / G rounded down to a power of two
@@ -146,7 +147,7 @@ void free_ctx(pe_ctx* c) {
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
                   c->part_o, c->part_ml, c->rope_turns, c->lm_packed, c->splitk, c->group_lens,
-                  c->sample_lse, c->sample_keys};
+                  c->sample_lse, c->sample_keys, c->sample_parts};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   if (c->fc_packed) (void)hipFree(c->fc_packed);
@@ -316,7 +317,9 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {reinterpret_cast<void**>(&c->ar_slots), R1 * 8, "ar slots"},
       {&c->ar_hidden, R1 * k.d * c->esz, "ar hidden"},
       {reinterpret_cast<void**>(&c->sample_lse), size_t(k.max_num_seqs) * (2 * k.K + 1) * 4, "sampling lse"},
-      {reinterpret_cast<void**>(&c->sample_keys), size_t(k.max_num_seqs) * pe::kSampleParts * 8, "sampling keys"},
+      {reinterpret_cast<void**>(&c->sample_keys), D * pe::kSampleParts * 8, "sampling keys"},
+      {reinterpret_cast<void**>(&c->sample_parts), size_t(k.max_num_seqs) * (2 * k.K + 1) * pe::kLseParts * 8,
+       "sampling row slices"},
   };
   for (auto& p : plan) {
     if ((s = alloc(p.p, p.bytes, p.what)) != PE_OK) { free_ctx(c); return s; }
@@ -632,13 +635,16 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     g.keys = ctx->keys; g.logits = P.logits; g.ldl = P.ldl;
     g.parts = pe::gemm_argmax_parts(dt, D, k.vocab, d, ctx->num_cus);
     g.seq_lens = P.seq_lens; g.Kd = P.Kd;
-    g.seed = P.seed; g.inv_temp = P.inv_temp;
     {
       Timed tm(ctx, PE_PH_LMHEAD);
       PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_ARGMAX, g, ctx->num_cus, st), "lm head");
     }
     Timed tm(ctx, PE_PH_ARGMAX);
-    if (P.vtarget)
+    if (P.seed)
+      PE_HIP(pe::launch_sample_drafts(D, P.Kd, k.vocab, P.ldl, P.inv_temp, P.logits, P.seed, ctx->sample_keys,
+                                      P.tokens, P.tstride, P.seq_lens, st),
+             "draft sampling");
+    else if (P.vtarget)
       PE_HIP(pe::launch_argmax_verify(B, P.Kd, g.parts, ctx->keys, P.tokens, P.seq_lens, P.vtarget,
                                       P.vacc, P.vbonus, st),
              "argmax + verify");
@@ -820,6 +826,8 @@ pe_status pe_draft_forward_sampled(pe_ctx* ctx, int32_t B, const pe_batch* batch
                               k_cache, v_cache, draft_tokens, logits);
   if (s != PE_OK) return s;
   if ((s = check_sampling(temperature, seed)) != PE_OK || B == 0) return s;
+  if (!logits || !aligned(logits, 16))
+    return fail(PE_ERR_INVALID_ARG, "sampled drafting draws from the logits: NULL or not 16-byte aligned");
   const int K = ctx->cfg.K;
   Pass P;
   P.B = B; P.S = 2 * K; P.Kd = K;
@@ -843,7 +851,8 @@ pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens,
     return fail(PE_ERR_INVALID_ARG, "logit rows NULL or not 16-byte aligned");
   Timed tm(ctx, PE_PH_VERIFY);
   PE_HIP(pe::launch_verify_sampled(B, ctx->cfg.K, ctx->cfg.vocab, 1.f / temperature, draft_tokens, draft_logits,
-                                   target_logits, seed, ctx->sample_lse, ctx->sample_keys, num_accepted,
+                                   target_logits, seed, ctx->sample_lse, ctx->sample_parts, ctx->sample_keys,
+                                   num_accepted,
                                    next_tokens, ctx->stream),
          "sampled verify launch");
   return PE_OK;

@@ -71,11 +71,12 @@ __device__ __forceinline__ int argmax_key_index(uint64_t k) {
 }
 
 // Philox4x32-10 ("Parallel random numbers: as easy as 1, 2, 3", Salmon,
-// Moraes, Dror, Shaw, SC 2011): the first output word for counter
+// Moraes, Dror, Shaw, SC 2011): the four output words for counter
 // (c0, c1, 0, stream) under the 64-bit key `seed`.  Ten rounds of two 32x32
 // multiplies (high and low halves), XOR with the other words and the round
 // key, and a word permutation; the key advances by the two Weyl constants.
-__device__ __forceinline__ uint32_t philox_first(uint32_t c0, uint32_t c1, uint32_t stream, uint64_t seed) {
+struct Words4 { uint32_t w[4]; };
+__device__ __forceinline__ Words4 philox4(uint32_t c0, uint32_t c1, uint32_t stream, uint64_t seed) {
   uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = stream;
   uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
 #pragma unroll
@@ -86,13 +87,14 @@ __device__ __forceinline__ uint32_t philox_first(uint32_t c0, uint32_t c1, uint3
     const uint32_t y0 = hi1 ^ x1 ^ k0, y2 = hi0 ^ x3 ^ k1;
     x0 = y0; x1 = lo1; x2 = y2; x3 = lo0;
   }
-  return x0;
+  return Words4{{x0, x1, x2, x3}};
 }
-// Random-number streams of stochastic drafting and verification.
+// Random-number streams of stochastic drafting and verification.  Per-token
+// noise: token v of a row takes word v % 4 of block (v / 4, row).
 enum RngStream : uint32_t { RNG_DRAFT = 0, RNG_ACCEPT = 1, RNG_RESIDUAL = 2 };
-// U in (0, 1): (x / 512 + 1/2) / 2^23, exact in fp32.
-__device__ __forceinline__ float philox_uniform(uint32_t c0, uint32_t c1, uint32_t stream, uint64_t seed) {
-  return (float(philox_first(c0, c1, stream, seed) >> 9) + 0.5f) * 1.1920928955078125e-7f;
+// U in (0, 1) from an output word: (x / 512 + 1/2) / 2^23, exact in fp32.
+__device__ __forceinline__ float word_uniform(uint32_t x) {
+  return (float(x >> 9) + 0.5f) * 1.1920928955078125e-7f;
 }
 // Gumbel noise -log(-log U); -log U as -log1p(U - 1) (U - 1 is exact).
 __device__ __forceinline__ float gumbel_noise(float u) { return -logf(-log1pf(u - 1.0f)); }

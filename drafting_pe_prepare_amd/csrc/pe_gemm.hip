@@ -193,15 +193,6 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
 // best 64-bit key of the tile is stored at keys[row * parts + part]; every
 // (row, part) is written by exactly one workgroup, so no atomics are needed and
 // the keys need no clearing between launches.
-// What the row argmax ranks: the logit (greedy drafting), or with a seed
-// logit / T plus the Gumbel noise of (draft row, token), the Gumbel-max draw
-// from softmax(logit / T).
-__device__ __forceinline__ float draft_score(const GemmArgs& g, uint64_t seed, float logit, int row, int n) {
-  if (!g.seed) return logit;
-  return logit * g.inv_temp + gumbel_noise(philox_uniform(uint32_t(n), uint32_t(row), RNG_DRAFT, seed));
-}
-__device__ __forceinline__ uint64_t draft_seed(const GemmArgs& g) { return g.seed ? *g.seed : 0ull; }
-
 __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, int m0, int TM,
                                 int n0, int TN, int part) {
   const int mrows = min(TM, g.M - m0), ncols = min(TN, g.N - n0);
@@ -212,11 +203,10 @@ __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, i
       g.logits[(long long)(m0 + i) * g.ldl + n0 + c] = tile[i * ldt + c];
     }
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
-  const uint64_t seed = draft_seed(g);
   for (int i = w; i < mrows; i += nw) {
     uint64_t best = 0;
     for (int c = l; c < ncols; c += 64) {
-      const uint64_t k = argmax_key(draft_score(g, seed, tile[i * ldt + c], m0 + i, n0 + c), n0 + c);
+      const uint64_t k = argmax_key(tile[i * ldt + c], n0 + c);
       best = k > best ? k : best;
     }
     for (int o = 32; o > 0; o >>= 1) {
@@ -429,7 +419,6 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
   uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-  const uint64_t seed = draft_seed(g);
   auto fold = [&](int tile) {  // full 16x16 sums of `tile` are in acc
     const int n = tile * 16 + col;
 #pragma unroll
@@ -437,7 +426,7 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
       const int row = kg * 4 + i;
       if (row < g.M) {
         if (g.logits) g.logits[(long long)row * g.ldl + n] = acc[i];
-        const uint64_t key = argmax_key(draft_score(g, seed, acc[i], row, n), n);
+        const uint64_t key = argmax_key(acc[i], n);
         best[i] = key > best[i] ? key : best[i];
       }
     }
@@ -693,7 +682,6 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
     __syncthreads();  // every fragment read is done; no DMA is in flight
     uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [WN][BM]
     static_assert(WN * BM * 8 <= STAGE, "argmax scratch fits one stage");
-    const uint64_t seed = draft_seed(g);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -705,7 +693,7 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
           const int n = n0 + wn * (BN / WN) + jj * 16 + col;
           if (n < g.N) {
             if (g.logits && m0 + lrow < g.M) g.logits[(long long)(m0 + lrow) * g.ldl + n] = acc[i][jj][r];
-            const uint64_t k = argmax_key(draft_score(g, seed, acc[i][jj][r], m0 + lrow, n), n);
+            const uint64_t k = argmax_key(acc[i][jj][r], n);
             best = k > best ? k : best;
           }
         }

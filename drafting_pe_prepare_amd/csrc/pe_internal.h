@@ -35,11 +35,19 @@ struct PrefillArgs {
 hipError_t launch_prefill_prepare(const PrefillArgs& a, hipStream_t st);
 
 // Verification by rejection sampling over fp32 logits: drafter rows [B*K, V],
-// verifier rows [B*(K+1), V]; workspace lse [B*(2K+1)], keys [B*kSampleParts].
+// verifier rows [B*(K+1), V]; workspace lse [B*(2K+1)], part_ms
+// [B*(2K+1)*kLseParts*2], keys [B*kSampleParts].  V % 4 == 0.
 constexpr int kSampleParts = 64;
+constexpr int kLseParts = 16;
+// Draft tokens drawn from softmax(logits / T) of each of M rows (row stride
+// ldl): Gumbel-max over kSampleParts vocabulary slices (keys [M*kSampleParts]),
+// -1 for a padded request (seq_lens[row / Kd] == 0).
+hipError_t launch_sample_drafts(int M, int Kd, int V, int ldl, float inv_temp, const float* logits,
+                                const uint64_t* seed, uint64_t* keys, int32_t* tokens, int tstride,
+                                const int32_t* seq_lens, hipStream_t st);
 hipError_t launch_verify_sampled(int B, int K, int V, float inv_temp, const int32_t* draft_tokens,
                                  const float* draft_logits, const float* target_logits,
-                                 const uint64_t* seed, float* lse, uint64_t* keys,
+                                 const uint64_t* seed, float* lse, float* part_ms, uint64_t* keys,
                                  int32_t* accepted, int32_t* next_tokens, hipStream_t st);
 
 // Step-graph fusions: preparation + hidden-state copy; argmax + verification.
@@ -100,10 +108,6 @@ struct GemmArgs {
   uint64_t* keys; int parts;                      // E_ARGMAX: keys[row * parts + part]
   int32_t* tokens; float* logits; int ldl;         // logits[row * ldl + n]
   const int32_t* seq_lens; int Kd;
-  // E_ARGMAX with sampling: when seed is set, row m ranks logit * inv_temp +
-  // Gumbel noise of (m, column) (a draw from softmax(logit / T)); logits
-  // stay raw
-  const uint64_t* seed; float inv_temp;
   // split-K: fp32 partial sums [ksplit][M][N] (logical columns) for GEMMs with
   // too few output tiles to fill the chip; the epilogue runs after the sum
   float* part; long long part_cap;  // capacity in floats (0: never split)

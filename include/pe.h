@@ -291,8 +291,10 @@ pe_status pe_prefill_forward(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* 
  * can change it between graph replays. */
 
 /* As pe_draft_forward, with each draft token drawn from softmax(logits / T)
- * instead of the argmax.  logits (when not NULL) receives the raw logits,
- * which pe_verify_sampled needs as draft_logits. */
+ * instead of the argmax.  logits ([B*K, vocab] float32, required, 16-byte
+ * aligned) receives the
+ * raw logits the draws are made from; pe_verify_sampled takes them as
+ * draft_logits. */
 pe_status pe_draft_forward_sampled(pe_ctx* ctx, int32_t B, const pe_batch* batch,
                                    const void* draft_hidden,
                                    const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,

@@ -27,7 +27,7 @@ tests/ (test_oracle_*.py); acceptance length on trained weights is parity
 unpinned (no trained weights exist here).
 """
 from .pe_sampling import (  # noqa: F401
-    STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL, philox4x32, uniform, gumbel, log_softmax,
+    STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL, philox4x32, uniform, token_uniforms, gumbel, log_softmax,
     sample_drafts, rejection_verify,
 )
 from .pe_oracle import (  # noqa: F401

@@ -16,13 +16,15 @@ standard speculative-sampling acceptance rule that carries that guarantee:
 Random numbers (the contract both sides implement from the published
 definition): Philox4x32-10 ("Parallel random numbers: as easy as 1, 2, 3",
 Salmon, Moraes, Dror, Shaw, SC 2011) with key (seed mod 2^32, seed >> 32)
-and counter (c0, c1, c2, stream); the first output word x gives
+and counter (c0, c1, 0, stream); an output word x gives
 U = (floor(x / 512) + 1/2) / 2^23 in (0, 1), a lattice that float32 holds
 exactly (so both sides draw the same U and 1 - U is never rounded to 0).
-Streams:
-  STREAM_DRAFT    counter (v, i, 0): Gumbel noise of draft row i = r*K + j, token v
-  STREAM_ACCEPT   counter (j, r, 0): the acceptance uniform of request r, draft j
-  STREAM_RESIDUAL counter (v, r, 0): Gumbel noise of the token emitted for request r
+Per-token noise takes all four output words of a block: token v of a row
+uses word v mod 4 of the block at c0 = v div 4 (the block function is the
+costly part).  Streams:
+  STREAM_DRAFT    counter (v div 4, i): Gumbel noise of draft row i = r*K + j, token v
+  STREAM_ACCEPT   counter (j, r), word 0: the acceptance uniform of request r, draft j
+  STREAM_RESIDUAL counter (v div 4, r): Gumbel noise of the token emitted for request r
 A sample of a distribution w over the vocabulary is argmax_v(log w(v) + G_v)
 with G = -log(-log U) (the Gumbel-max identity); ties go to the lowest index.
 """
@@ -57,14 +59,23 @@ def philox4x32(counter, key, rounds=10):
     return np.stack([x.astype(np.uint32) for x in c], axis=-1)
 
 
-def uniform(seed, stream, c0, c1):
-    """U in (0, 1) for counter (c0, c1, 0, stream) under key `seed` (64-bit)."""
+def uniform(seed, stream, c0, c1, word=0):
+    """U in (0, 1) from output word `word` of counter (c0, c1, 0, stream)
+    under key `seed` (64-bit)."""
     c0 = np.asarray(c0, dtype=np.uint64)
     c1 = np.broadcast_to(np.asarray(c1, dtype=np.uint64), c0.shape)
+    word = np.broadcast_to(np.asarray(word, dtype=np.int64), c0.shape)
     ctr = np.stack([c0, c1, np.zeros_like(c0), np.full_like(c0, stream)], axis=-1)
     key = np.array([int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF], dtype=np.uint64)
-    x = philox4x32(ctr, key)[..., 0].astype(np.float64)
+    out = philox4x32(ctr, key)
+    x = np.take_along_axis(out, word[..., None], axis=-1)[..., 0].astype(np.float64)
     return (np.floor(x / 512.0) + 0.5) / 2.0 ** 23
+
+
+def token_uniforms(seed, stream, V, row):
+    """U of tokens 0..V-1 of one row: word v mod 4 of block (v div 4, row)."""
+    v = np.arange(V)
+    return uniform(seed, stream, v // 4, row, v % 4)
 
 
 def gumbel(u):
@@ -83,9 +94,8 @@ def sample_drafts(draft_logits, T, seed):
     z = np.asarray(draft_logits, dtype=np.float64)
     D, V = z.shape
     out = np.zeros(D, np.int32)
-    v = np.arange(V)
     for i in range(D):
-        g = gumbel(uniform(seed, STREAM_DRAFT, v, i))
+        g = gumbel(token_uniforms(seed, STREAM_DRAFT, V, i))
         out[i] = int(np.argmax(z[i] / T + g))
     return out
 
@@ -101,7 +111,6 @@ def rejection_verify(draft_tokens, draft_logits, target_logits, T, seed):
     V = np.asarray(target_logits).shape[-1]
     acc = np.zeros(B, np.int32)
     nxt = np.zeros(B, np.int32)
-    v = np.arange(V)
     for r in range(B):
         lq = log_softmax(draft_logits[r], T)      # [K, V]
         lp = log_softmax(target_logits[r], T)     # [K+1, V]
@@ -112,7 +121,7 @@ def rejection_verify(draft_tokens, draft_logits, target_logits, T, seed):
             if not u < min(1.0, ratio):
                 a = j
                 break
-        g = gumbel(uniform(seed, STREAM_RESIDUAL, v, r))
+        g = gumbel(token_uniforms(seed, STREAM_RESIDUAL, V, r))
         if a < K:
             w = np.maximum(np.exp(lp[a]) - np.exp(lq[a]), 0.0)
             with np.errstate(divide="ignore"):

@@ -80,7 +80,7 @@ def _margins(tokens, zq, zp, T, seed, a):
 def _emit_scores(zq, zp, T, seed, r, a):
     V = zp.shape[-1]
     lp = O.log_softmax(zp[r], T)
-    g = O.gumbel(O.uniform(seed, O.STREAM_RESIDUAL, np.arange(V), r))
+    g = O.gumbel(O.token_uniforms(seed, O.STREAM_RESIDUAL, V, r))
     if a < zq.shape[1]:
         lq = O.log_softmax(zq[r], T)
         w = np.maximum(np.exp(lp[a]) - np.exp(lq[a]), 0.0)
@@ -201,7 +201,7 @@ def test_draft_forward_sampled_matches_oracle(T):
         V = w.vocab
         compared = 0
         for i in range(B * K):
-            sc = ol[i] / T + O.gumbel(O.uniform(seed, O.STREAM_DRAFT, np.arange(V), i))
+            sc = ol[i] / T + O.gumbel(O.token_uniforms(seed, O.STREAM_DRAFT, V, i))
             srt = np.sort(sc)
             if srt[-1] - srt[-2] > 2 * tol:
                 assert got[i] == want[i], (i, got[i], want[i])

@@ -40,6 +40,10 @@ def test_uniform_range_and_streams():
     u3 = O.uniform(1235, O.STREAM_DRAFT, np.arange(1000), 7)
     assert not np.array_equal(u[:1000], u2) and not np.array_equal(u[:1000], u3)
     np.testing.assert_array_equal(u[:1000], O.uniform(1234, O.STREAM_DRAFT, np.arange(1000), 7))
+    # token uniforms: the four words of block v div 4, in order
+    tu = O.token_uniforms(99, O.STREAM_RESIDUAL, 12, 5)
+    blk = O.philox4x32(np.array([[c, 5, 0, O.STREAM_RESIDUAL] for c in range(3)]), np.array([99, 0]))
+    np.testing.assert_array_equal(tu, (np.floor(blk.reshape(-1).astype(np.float64) / 512) + 0.5) / 2 ** 23)
 
 
 def _chi2_ok(counts, probs):
