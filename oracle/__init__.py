@@ -33,5 +33,5 @@ from .pe_sampling import (  # noqa: F401
 from .pe_oracle import (  # noqa: F401
     PAD_TOKEN, PADDING_SLOT_ID, ERR_ACCEPTED, ERR_TOKEN, ERR_BLOCK, ERR_LAYOUT,
     round_bf16, widen, prepare, prepare_prefill, gather_hidden, rmsnorm, rope, silu,
-    attend, draft_forward, verify, eagle_step, ar_draft, slot_of,
+    attend, draft_forward, verify, eagle_step, ar_draft, slot_of, expected_tokens, choose_depth,
 )

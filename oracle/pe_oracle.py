@@ -624,3 +624,30 @@ def ar_draft(params, cfg, prefix_k, prefix_v, accepted_tokens, bonus, hiddens, s
         return (np.asarray(out_t, np.int32), np.asarray(out_l),
                 np.asarray(fed).reshape(-1, cfg.d), caches)
     return np.asarray(out_t, np.int32), np.asarray(out_l)
+
+
+# ----------------------------------------------------------------------------
+# draft depth selection
+# ----------------------------------------------------------------------------
+def expected_tokens(K, alpha):
+    """Tokens a round emits when each draft is kept with probability alpha
+    given that every earlier one was (reading: the pages give no acceptance
+    model): sum_{i=0..K} alpha^i -- the kept prefix plus the emitted token."""
+    return float(sum(alpha ** i for i in range(K + 1)))
+
+
+def choose_depth(Ks, draft_us, alpha, verify_fixed_us, verify_per_token_us):
+    """The depth with the most tokens per microsecond ("P-EAGLE: parallel
+    speculative decoding in vLLM", Speculative depth efficiency: throughput
+    peaks at the depth where the extra accepted tokens stop paying for the
+    deeper draft; "vLLM Speculators: parallel drafting for speculative
+    decoding", Limits of autoregressive drafting: K is tuned to the drafting
+    cost).  A round at depth K costs draft_us + verify_fixed_us +
+    verify_per_token_us * (K + 1).  Ties go to the smaller K.
+    Returns (K, tokens per microsecond)."""
+    best, best_rate = None, -1.0
+    for K, t in sorted(zip(Ks, draft_us)):
+        rate = expected_tokens(K, alpha) / (t + verify_fixed_us + verify_per_token_us * (K + 1))
+        if rate > best_rate:
+            best, best_rate = K, rate
+    return best, best_rate
