@@ -307,8 +307,20 @@ def ksweep(steps, warmup):
                      "phases_us_per_step": r["phases_us_per_step"]})
     del dev
     torch.cuda.empty_cache()
+    # depth selection from the measured step costs (pe_choose_depth): per-draft
+    # acceptance alpha, verifier cost 0 (drafting-bound) or a nominal 2 ms pass
+    Ks = [r["K"] for r in rows]
+    choice = []
+    for fixed in (0.0, 2000.0):
+        for alpha in (0.6, 0.7, 0.8, 0.9):
+            kp, rp = pb.pe_choose_depth(Ks, [r["us_per_step"] for r in rows], alpha, fixed, 0.0)
+            ka, ra = pb.pe_choose_depth(Ks, [r["sequential_us_per_step"] for r in rows], alpha, fixed, 0.0)
+            choice.append({"alpha": alpha, "verify_fixed_us": fixed, "parallel_K": kp,
+                           "parallel_tokens_per_s": rp * 1e6 * base.batch,
+                           "sequential_K": ka, "sequential_tokens_per_s": ra * 1e6 * base.batch})
     return {"workload": base.name, "batch": base.batch, "d": base.d, "layers": base.layers,
-            "vocab": base.vocab, "prefix": list(base.prefix), "seed": base.seed, "rows": rows}
+            "vocab": base.vocab, "prefix": list(base.prefix), "seed": base.seed, "rows": rows,
+            "depth_choice": choice}
 
 
 def prefill(w, prm, dev, prompt, steps, warmup):

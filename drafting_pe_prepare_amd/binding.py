@@ -23,7 +23,8 @@ DEVERR_ACCEPTED, DEVERR_TOKEN, DEVERR_BLOCK, DEVERR_LAYOUT = 1, 2, 4, 8
 
 EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_hidden",
            "pe_draft_forward", "pe_ar_draft", "pe_verify", "pe_prefill_prepare", "pe_prefill_gather",
-           "pe_prefill_forward", "pe_draft_forward_sampled", "pe_verify_sampled", "pe_step_graph",
+           "pe_prefill_forward", "pe_draft_forward_sampled", "pe_verify_sampled", "pe_choose_depth",
+           "pe_step_graph",
            "pe_get_device_error",
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
@@ -103,6 +104,8 @@ def load(path: str = LIB_PATH):
     lib.pe_draft_forward_sampled.argtypes = [vp, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp),
                                              ctypes.c_float, vp, vp, vp]
     lib.pe_verify_sampled.argtypes = [vp, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    lib.pe_choose_depth.argtypes = [P(i32), P(ctypes.c_double), i32, ctypes.c_double, ctypes.c_double,
+                                    ctypes.c_double, P(i32), P(ctypes.c_double)]
     lib.pe_step_graph.argtypes = [vp, i32, P(PeStepArgs)]
     lib.pe_get_device_error.argtypes = [vp, P(ctypes.c_uint32), P(i32)]
     lib.pe_profile_enable.argtypes = [vp, ctypes.c_int]
@@ -269,6 +272,17 @@ def pe_verify_sampled(ctx: Context, B, draft_tokens, draft_logits, target_logits
                       num_accepted, next_tokens):
     _check(_lib.pe_verify_sampled(ctx.h, B, _ptr(draft_tokens), _ptr(draft_logits), _ptr(target_logits),
                                   float(temperature), _ptr(seed), _ptr(num_accepted), _ptr(next_tokens)))
+
+
+def pe_choose_depth(Ks, draft_us, alpha, verify_fixed_us=0.0, verify_per_token_us=0.0):
+    """Host-only: (best K, tokens per microsecond)."""
+    n = len(Ks)
+    ks = (i32 * n)(*[int(k) for k in Ks])
+    ts = (ctypes.c_double * n)(*[float(t) for t in draft_us])
+    best, rate = i32(0), ctypes.c_double(0.0)
+    _check(load().pe_choose_depth(ks, ts, n, float(alpha), float(verify_fixed_us), float(verify_per_token_us),
+                                  ctypes.byref(best), ctypes.byref(rate)))
+    return int(best.value), float(rate.value)
 
 
 def pe_verify(ctx: Context, B, draft_tokens, target_tokens, num_accepted, bonus_tokens):

@@ -965,6 +965,30 @@ pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args) {
   return PE_OK;
 }
 
+pe_status pe_choose_depth(const int32_t* Ks, const double* draft_us, int32_t n, double alpha,
+                          double verify_fixed_us, double verify_per_token_us, int32_t* best_K,
+                          double* tokens_per_us) {
+  if (!Ks || !draft_us || !best_K || !tokens_per_us || n < 1) return fail(PE_ERR_INVALID_ARG, "depth selection arguments");
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return fail(PE_ERR_INVALID_ARG, "alpha %g outside [0, 1]", alpha);
+  if (!(verify_fixed_us >= 0.0) || !(verify_per_token_us >= 0.0))
+    return fail(PE_ERR_INVALID_ARG, "verifier costs must be >= 0");
+  int best = -1;
+  double best_rate = -1.0;
+  for (int i = 0; i < n; ++i) {
+    const int K = Ks[i];
+    if (K < 1 || K > 32) return fail(PE_ERR_INVALID_ARG, "K=%d outside [1, 32]", K);
+    const double cost = draft_us[i] + verify_fixed_us + verify_per_token_us * (K + 1);
+    if (!(draft_us[i] > 0.0) || !(cost > 0.0)) return fail(PE_ERR_INVALID_ARG, "draft cost of K=%d not positive", K);
+    double e = 0.0, a = 1.0;
+    for (int j = 0; j <= K; ++j) { e += a; a *= alpha; }
+    const double rate = e / cost;
+    if (rate > best_rate || (rate == best_rate && K < best)) { best = K; best_rate = rate; }
+  }
+  *best_K = best;
+  *tokens_per_us = best_rate;
+  return PE_OK;
+}
+
 pe_status pe_get_device_error(pe_ctx* ctx, uint32_t* kinds, int32_t* first_request) {
   if (!ctx || !kinds || !first_request) return fail(PE_ERR_INVALID_ARG, "NULL argument");
   uint32_t h[4] = {0, 0, 0, 0};

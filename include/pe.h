@@ -311,6 +311,21 @@ pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens,
                             const float* draft_logits, const float* target_logits, float temperature,
                             const uint64_t* seed, int32_t* num_accepted, int32_t* next_tokens);
 
+/* Draft depth selection [P1, Speculative depth efficiency: throughput peaks
+ * at the depth where more accepted drafts stop paying for a deeper draft; P2,
+ * Limits of autoregressive drafting: the speculation length is tuned to the
+ * drafting cost].  Reading (the pages give no acceptance model): each draft is
+ * kept with probability alpha while every earlier one was, so a round at
+ * depth K emits E(K) = sum_{i=0..K} alpha^i tokens; it costs draft_us[i] (a
+ * measured step time, e.g. from pe_step_graph) + verify_fixed_us +
+ * verify_per_token_us * (K + 1).  Returns the K of Ks[0..n) with the largest
+ * E(K) / cost (the smaller K on ties) and that rate in tokens per
+ * microsecond.  Host arrays; host-only, nothing is launched.  Errors: n < 1,
+ * alpha outside [0, 1], a cost that is not positive, a K outside [1, 32]. */
+pe_status pe_choose_depth(const int32_t* Ks, const double* draft_us, int32_t n, double alpha,
+                          double verify_fixed_us, double verify_per_token_us,
+                          int32_t* best_K, double* tokens_per_us);
+
 /* Drafting pass of a step graph: pe_draft_forward or pe_ar_draft. */
 typedef enum pe_step_mode { PE_STEP_PARALLEL = 0, PE_STEP_AUTOREGRESSIVE = 1 } pe_step_mode;
 
