@@ -3,7 +3,7 @@
     python -m drafting_pe_prepare_amd.build
 
 Every HIP source is compiled with packed-fp32 instructions disabled; the
-library links only the HIP runtime.  The output lands next to this file, where
+library links the HIP runtime and hipBLASLt (plain GEMMs of large batches).  The output lands next to this file, where
 the Python binding looks for it.
 """
 import os
@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpe.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["pe_meta.hip", "pe_norm.hip", "pe_gemm.hip", "pe_attn.hip", "pe_sample.hip", "pe_api.cpp"]
+SOURCES = ["pe_meta.hip", "pe_norm.hip", "pe_gemm.hip", "pe_attn.hip", "pe_sample.hip", "pe_blas.cpp",
+           "pe_api.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -66,7 +67,8 @@ def _build(verbose, out):
         if verbose and msgs:
             print("\n".join(msgs), file=sys.stderr)
     tmp = out + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results] + \
+          ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

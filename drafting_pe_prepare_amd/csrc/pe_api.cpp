@@ -18,6 +18,10 @@
 #include "pe.h"
 #include "pe_internal.h"
 
+#ifndef PE_BLAS_MIN_ROWS
+#define PE_BLAS_MIN_ROWS 512  // batches this large run their plain GEMMs through hipBLASLt
+#endif
+
 namespace {
 
 thread_local std::string g_err;
@@ -72,6 +76,13 @@ struct pe_ctx {
   int32_t* group_lens = nullptr; // attention context length per slot group (bf16)
   int attn_group = 64;           // slots per attention workgroup: 512 / G rounded down to a power of two
   int groups_max = 0;            // slot groups the attention buffers are sized for
+  // plain GEMMs of large batches through hipBLASLt (bf16 storage): row-major
+  // copies of the weights in logical column order (qkv and gate/up per layer),
+  // the fc A operand and the fp32 result the fused epilogue kernel reads
+  pe::Blas* blas = nullptr;
+  void* fc_a = nullptr;
+  float* blas_c = nullptr;
+  std::vector<void*> rows_qkv, rows_gu;
   float* splitk = nullptr;      // split-K GEMM partials (bf16 storage)
   long long splitk_cap = 0;     // floats
   double* rope_turns = nullptr;  // RoPE frequencies in turns per position
@@ -156,6 +167,13 @@ void free_ctx(pe_ctx* c) {
     if (p) (void)hipFree(p);
   for (void* p : c->layer_packed)
     if (p) (void)hipFree(p);
+  for (void* p : c->rows_qkv)
+    if (p) (void)hipFree(p);
+  for (void* p : c->rows_gu)
+    if (p) (void)hipFree(p);
+  if (c->fc_a) (void)hipFree(c->fc_a);
+  if (c->blas_c) (void)hipFree(c->blas_c);
+  pe::blas_destroy(c->blas);
   delete c;
 }
 
@@ -385,6 +403,34 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       free_ctx(c);
       return s;
     }
+    // batches of PE_BLAS_MIN_ROWS rows and more run their plain GEMMs through
+    // hipBLASLt (without it, or for shapes it declines, the tiled kernels run)
+    if (R >= size_t(PE_BLAS_MIN_ROWS) && (c->blas = pe::blas_create(size_t(32) << 20)) != nullptr) {
+      const size_t maxN = std::max({size_t(k.d), size_t(qd + 2 * kvd), size_t(2 * k.mlp)});
+      s = alloc(&c->fc_a, R * 2 * k.d * 2, "fc operand rows");
+      if (s == PE_OK) s = alloc(&c->blas_c, R * maxN * 4, "GEMM result");
+      c->rows_qkv.assign(k.layers, nullptr);
+      c->rows_gu.assign(k.layers, nullptr);
+      for (int l = 0; l < k.layers && s == PE_OK; ++l) {
+        const pe_layer_weights& L = c->layers[l];
+        pe::GemmArgs pr;
+        std::memset(&pr, 0, sizeof pr);
+        pr.hd = k.head_dim;
+        pr.W0 = L.wq; pr.W1 = L.wk; pr.W2 = L.wv; pr.N = qd + 2 * kvd; pr.K = k.d; pr.nq = qd; pr.nk = kvd;
+        s = alloc(&c->rows_qkv[l], size_t(pr.N) * k.d * 2, "qkv rows");
+        if (s == PE_OK && (e = pe::launch_pack_rows(pe::B_QKV, pr, c->rows_qkv[l], c->stream)) != hipSuccess)
+          s = hipfail(e, "qkv rows");
+        pr.W0 = L.w_gate; pr.W1 = L.w_up; pr.W2 = nullptr; pr.N = 2 * k.mlp; pr.nq = pr.nk = 0;
+        if (s == PE_OK) s = alloc(&c->rows_gu[l], size_t(pr.N) * k.d * 2, "gate/up rows");
+        if (s == PE_OK && (e = pe::launch_pack_rows(pe::B_GATEUP, pr, c->rows_gu[l], c->stream)) != hipSuccess)
+          s = hipfail(e, "gate/up rows");
+      }
+      if (s == PE_OK && (e = hipStreamSynchronize(c->stream)) != hipSuccess) s = hipfail(e, "rows sync");
+      if (s != PE_OK) {
+        free_ctx(c);
+        return s;
+      }
+    }
   }
   *out = c;
   return PE_OK;
@@ -526,6 +572,33 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   g0.part = ctx->splitk;
   g0.part_cap = ctx->splitk_cap;
 
+  // a dense GEMM with its fused epilogue: hipBLASLt + the epilogue kernel for
+  // large batches (w_rows: the weight in logical row order), else the tiled or
+  // skinny kernels
+  auto dense = [&](int aload, int bmap, int epi, const pe::GemmArgs& g, const void* w_rows,
+                   const char* what) -> pe_status {
+    if (dt == PE_BF16 && ctx->blas && g.M >= PE_BLAS_MIN_ROWS && w_rows) {
+      const void* A = g.A;
+      if (aload == pe::A_FC) {
+        PE_HIP(pe::launch_fc_rows(g, ctx->fc_a, st), what);
+        A = ctx->fc_a;
+      }
+      if (epi == pe::E_STORE || epi == pe::E_RESID) {
+        // store / residual: the library rounds its fp32 sums (plus the
+        // residual) to bf16 once, as the fused epilogue does
+        if (g.ldo == g.N &&
+            pe::blas_gemm_bf16(ctx->blas, g.M, g.N, g.K, A, w_rows, epi == pe::E_RESID ? g.resid : nullptr, g.out, st))
+          return PE_OK;
+      } else if (pe::blas_gemm(ctx->blas, g.M, g.N, g.K, A, w_rows, ctx->blas_c, st)) {
+        PE_HIP(pe::launch_epilogue_f32(epi, g, ctx->blas_c, ctx->num_cus, st), what);
+        return PE_OK;
+      }
+    }
+    PE_HIP(pe::launch_gemm(dt, aload, bmap, epi, g, ctx->num_cus, st), what);
+    return PE_OK;
+  };
+  pe_status ds = PE_OK;
+
   // fc over concat(emb(token), hidden)
   {
     pe::GemmArgs g = g0;
@@ -534,7 +607,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     g.W0 = ctx->w.w_fc; g.Wp = ctx->fc_packed;
     g.out = ctx->x; g.ldo = d;
     Timed tm(ctx, PE_PH_FC);
-    PE_HIP(pe::launch_gemm(dt, pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, ctx->num_cus, st), "fc");
+    if ((ds = dense(pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, ctx->w.w_fc, "fc")) != PE_OK) return ds;
   }
   for (int l = 0; l < k.layers; ++l) {
     const pe_layer_weights& L = ctx->layers[l];
@@ -552,7 +625,9 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
       g.rope_turns = ctx->rope_turns;
       Timed tm(ctx, PE_PH_QKV);
-      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, ctx->num_cus, st), "qkv");
+      if ((ds = dense(pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, ctx->rows_qkv.empty() ? nullptr : ctx->rows_qkv[l],
+                      "qkv")) != PE_OK)
+        return ds;
     }
     {
       pe::AttnArgs a;
@@ -595,7 +670,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.wo; g.Wp = packed(ctx, l, 1);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       Timed tm(ctx, PE_PH_O);
-      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, ctx->num_cus, st), "o proj");
+      if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, L.wo, "o proj")) != PE_OK) return ds;
     }
     {
       Timed tm(ctx, PE_PH_NORM);
@@ -608,7 +683,9 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.w_gate; g.W1 = L.w_up; g.Wp = packed(ctx, l, 2);
       g.out = ctx->mlp; g.ldo = k.mlp;
       Timed tm(ctx, PE_PH_GATEUP);
-      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, ctx->num_cus, st), "gate/up");
+      if ((ds = dense(pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, ctx->rows_gu.empty() ? nullptr : ctx->rows_gu[l],
+                      "gate/up")) != PE_OK)
+        return ds;
     }
     {
       pe::GemmArgs g = g0;
@@ -617,7 +694,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.w_down; g.Wp = packed(ctx, l, 3);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       Timed tm(ctx, PE_PH_DOWN);
-      PE_HIP(pe::launch_gemm(dt, pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, ctx->num_cus, st), "down");
+      if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, L.w_down, "down")) != PE_OK) return ds;
     }
   }
   {

@@ -1062,6 +1062,65 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
   return hipGetLastError();
 }
 
+hipError_t launch_epilogue_f32(int epi, const GemmArgs& g, float* C, int num_cus, hipStream_t st) {
+  if (g.M <= 0) return hipSuccess;
+  if (g.N % 32) return hipErrorInvalidValue;
+  GemmArgs gp = g;
+  gp.part = C;
+  gp.ksplit = 1;
+  const long long work = (long long)g.M * (epi == E_QKV ? g.N / 2 : epi == E_SILU ? g.N / 16 : g.N / 8);
+  const dim3 grid(unsigned(std::min<long long>((work + 255) / 256, 8LL * num_cus))), block(256);
+  switch (epi) {
+    case E_STORE: hipLaunchKernelGGL(splitk_reduce_kernel<E_STORE>, grid, block, 0, st, gp); break;
+    case E_RESID: hipLaunchKernelGGL(splitk_reduce_kernel<E_RESID>, grid, block, 0, st, gp); break;
+    case E_SILU: hipLaunchKernelGGL(splitk_reduce_kernel<E_SILU>, grid, block, 0, st, gp); break;
+    case E_QKV: hipLaunchKernelGGL(splitk_reduce_kernel<E_QKV>, grid, block, 0, st, gp); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Row-major copy of the logical weight rows: out[n][k] = weight_row(n)[k].
+template <int BMAP>
+__global__ __launch_bounds__(256) void pack_rows_kernel(GemmArgs g, uint4* __restrict__ out) {
+  const int cpr = g.K >> 3;
+  const long long total = (long long)g.N * cpr;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int n = int(i / cpr), c = int(i - (long long)n * cpr);
+    out[i] = ld16(weight_row<uint16_t, BMAP>(g, n) + c * 8);
+  }
+}
+
+hipError_t launch_pack_rows(int bmap, const GemmArgs& g, void* out, hipStream_t st) {
+  const long long total = (long long)g.N * (g.K / 8);
+  const unsigned blocks = unsigned(std::min<long long>((total + 255) / 256, 8192));
+  if (bmap == B_QKV) hipLaunchKernelGGL(pack_rows_kernel<B_QKV>, dim3(blocks), dim3(256), 0, st, g, (uint4*)out);
+  else if (bmap == B_GATEUP) hipLaunchKernelGGL(pack_rows_kernel<B_GATEUP>, dim3(blocks), dim3(256), 0, st, g, (uint4*)out);
+  else hipLaunchKernelGGL(pack_rows_kernel<B_PLAIN>, dim3(blocks), dim3(256), 0, st, g, (uint4*)out);
+  return hipGetLastError();
+}
+
+// fc A operand rows: [emb(ids[m]) ; hid[m]], 16 bytes per thread
+__global__ __launch_bounds__(256) void fc_rows_kernel(GemmArgs g, uint4* __restrict__ out) {
+  const int cpr = (2 * g.d) >> 3;
+  const long long total = (long long)g.M * cpr;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int m = int(i / cpr), c = int(i - (long long)m * cpr);
+    ARow<uint16_t, A_FC> ar;
+    ar.init(g, m);
+    out[i] = ld16(ar.at(c * 8, g.d));
+  }
+}
+
+hipError_t launch_fc_rows(const GemmArgs& g, void* out, hipStream_t st) {
+  const long long total = (long long)g.M * (2 * g.d / 8);
+  const unsigned blocks = unsigned(std::min<long long>((total + 255) / 256, 8192));
+  hipLaunchKernelGGL(fc_rows_kernel, dim3(blocks), dim3(256), 0, st, g, (uint4*)out);
+  return hipGetLastError();
+}
+
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
   const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);

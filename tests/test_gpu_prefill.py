@@ -131,6 +131,13 @@ def test_prefill_tiled_gemms_and_split_k():
     _check(w, 448, ("fixed", 442), ("fixed", 37), seed=67)
 
 
+def test_prefill_library_gemms():
+    """640 slots: hipBLASLt GEMMs with the fused epilogues on their results,
+    10 slot groups."""
+    w = SMALL_BF16.with_(K=7, batch=1, n_q_heads=8, n_kv_heads=1)
+    _check(w, 640, ("fixed", 600), ("fixed", 21), seed=72)
+
+
 def test_prefill_padded_request():
     _check(SMALL_BF16.with_(K=3, batch=3), 48, ("uniform", 10, 46), ("uniform", 0, 60), seed=68, bad=1)
 
