@@ -19,7 +19,7 @@
 #include "pe_internal.h"
 
 #ifndef PE_BLAS_MIN_ROWS
-#define PE_BLAS_MIN_ROWS 512  // batches this large run their plain GEMMs through hipBLASLt
+#define PE_BLAS_MIN_ROWS 256  // batches this large run their plain GEMMs through hipBLASLt
 #endif
 
 namespace {

@@ -144,9 +144,9 @@ def test_small_bf16_lm_head_tiles_cut_between_waves(d, vocab, B):
 
 @pytest.mark.parametrize("K,B,d,seed", [(7, 40, 256, 88), (4, 72, 512, 89)])
 def test_small_bf16_library_gemms(K, B, d, seed):
-    """560 and 576 forward rows: the plain GEMMs run through hipBLASLt and the
-    fused epilogues (fc store, RoPE/KV write, residuals, SiLU.mul) run on its
-    fp32 results."""
+    """560 and 576 forward rows: the plain GEMMs run through hipBLASLt; the
+    fc and residual GEMMs write bf16 directly, RoPE/KV write and SiLU.mul run
+    on its fp32 results."""
     w = SMALL_BF16.with_(K=K, batch=B, d=d, weight_std=1 / np.sqrt(d), accepted="uniform",
                          prefix=("uniform", 30, 200))
     _full_check(w, seed)
