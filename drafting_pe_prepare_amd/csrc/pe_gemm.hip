@@ -544,8 +544,12 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2,
 void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;   // MFMA tiles per wave
-  constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;     // DMA instructions per wave per k-tile
-  static_assert(LA * 8 * NW == BM && LB * 8 * NW == BN, "tile rows must split over the waves");
+  // DMA instructions per wave per k-tile; A's row groups may not split evenly
+  // (224-row tiles: 28 groups over 8 waves), then the last one is predicated
+  constexpr int LA = (BM / 8 + NW - 1) / NW, LB = BN / 8 / NW;
+  constexpr bool LA_EVEN = LA * 8 * NW == BM;
+  static_assert(LB * 8 * NW == BN, "tile columns must split over the waves");
+  static_assert(LA_EVEN || S == 2, "uneven A rows only with two stages (the step waits drain every DMA)");
   static_assert((BN / WN) % 32 == 0, "a wave's columns must be whole 32-column blocks");
   constexpr int STAGE = (BM + BN) * 128;                // bytes per stage
   static_assert(S == 2 || S == 3, "two or three stages");
@@ -584,9 +588,10 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
     const int k0 = (kbase + kt) * 64;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void*)ar[i].at(k0 + lc, g.d),
-          (__attribute__((address_space(3))) void*)(st + (w + NW * i) * 1024), 16, 0, 0);
+      if (LA_EVEN || w + NW * i < BM / 8)
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)ar[i].at(k0 + lc, g.d),
+            (__attribute__((address_space(3))) void*)(st + (w + NW * i) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
       __builtin_amdgcn_global_load_lds(
@@ -610,8 +615,14 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   uint4 fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
   // k-tile 0 must land; the later prologue tiles may stay in flight
   if (S == 3 && 2 < nk) wait_vmcnt<2 * (LA + LB)>();
-  else if (1 < nk) wait_vmcnt<LA + LB>();
-  else wait_vmcnt<0>();
+  else if (1 < nk) {
+    // this wave's DMAs of k-tile 1 may stay in flight (one fewer A row group
+    // for the waves past the last one of an uneven split)
+    if (LA_EVEN || w + NW * (LA - 1) < BM / 8) wait_vmcnt<LA + LB>();
+    else wait_vmcnt<LA - 1 + LB>();
+  } else {
+    wait_vmcnt<0>();
+  }
   // Plain s_barrier: this wave's DMA of the stage has landed (the wait above).
   // A fenced __syncthreads would also wait for the DMA still in flight.
   asm volatile("s_barrier" ::: "memory");
@@ -882,12 +893,13 @@ hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_
 //    when those tiles outnumber the CUs; otherwise 64x128 tiles (three stages,
 //    two workgroups per CU), which spread a small grid over more CUs (fc, O and
 //    down at c=64, cache-cold weights: 50/38/69 us against 59/43/76 us).
-enum Variant { V_WIDE, V_SKINNY, V_A64, V_A128, V_A256, V_D64, V_D128S2 };
+enum Variant { V_WIDE, V_SKINNY, V_A64, V_A128, V_A224, V_A256, V_D64, V_D128S2 };
 static Variant pick(int epi, int M, int N, int K, int num_cus) {
   if (epi == E_ARGMAX) {
     const size_t wide_lds = size_t(M) * (K / 8 + 1) * 16;
     if (M <= 16 && wide_lds <= 140 * 1024) return V_WIDE;
     if (M <= 64) return V_A64;
+    if (M > 384 && M <= 448) return V_A224;  // two 224-row tiles instead of 256 + 192 valid rows
     return M <= 128 ? V_A128 : V_A256;
   }
   if (M <= 16) return V_SKINNY;
@@ -1129,6 +1141,7 @@ static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
       case V_WIDE: return run_wide_any(g, num_cus, st);
       case V_A64: return run_tiled<EPI, AL, BMAP, 64, kArgmaxBN, 1, 4, 2>(g, st);
       case V_A128: return run_tiled<EPI, AL, BMAP, 128, kArgmaxBN, 2, 4, 2>(g, st);
+      case V_A224: return run_tiled<EPI, AL, BMAP, 224, kArgmaxBN, 2, 4, 2>(g, st);
       default: return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN, 4, 2, 2>(g, st);
     }
   } else {

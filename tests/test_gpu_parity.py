@@ -152,6 +152,13 @@ def test_small_bf16_library_gemms(K, B, d, seed):
     _full_check(w, seed)
 
 
+@pytest.mark.parametrize("B,seed", [(64, 91), (57, 92)])
+def test_small_bf16_lm_head_224_row_tiles(B, seed):
+    """448 and 399 draft rows: the LM head runs two 224-row tiles (28 row
+    groups of A over 8 waves, the last DMA predicated), the second ragged."""
+    _full_check(SMALL_BF16.with_(K=7, batch=B, accepted="uniform", prefix=("uniform", 20, 120)), seed=seed)
+
+
 @pytest.mark.parametrize("B", [5, 12])
 def test_small_bf16_tiled_path(B):
     """B*2K > 64 rows: the LDS-tiled GEMM path and the tiled LM head."""
