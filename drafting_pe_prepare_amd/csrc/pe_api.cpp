@@ -353,8 +353,11 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       return s;
     }
     // split-K partials: GEMMs whose output tiles are too few to fill the chip
-    // sum k-ranges into here first (32 MB bounds the split factor)
+    // sum k-ranges into here first (32 MB bounds the split factor), and the
+    // k-split tail of the LM head writes its partial tiles here (up to one
+    // round of 256 x 256 tiles: 64 MB)
     c->splitk_cap = std::min<long long>(8LL << 20, (long long)R * std::max(2 * k.mlp, 4 * k.d) * 8);
+    c->splitk_cap = std::max<long long>(c->splitk_cap, std::min<long long>(16LL << 20, (long long)D * k.vocab * 8));
     if ((s = alloc(&c->splitk, size_t(c->splitk_cap) * 4, "split-K partials")) != PE_OK) {
       free_ctx(c);
       return s;

@@ -35,6 +35,9 @@
 #ifndef PE_SPLITK_MIN_KTILES
 #define PE_SPLITK_MIN_KTILES 8  // fewest 64-wide k-tiles per split
 #endif
+#ifndef PE_TAIL_MIN_KTILES
+#define PE_TAIL_MIN_KTILES 4  // fewest 64-wide k-tiles per piece of a split LM-head tail
+#endif
 #ifndef PE_SKINNY_NTW_GU
 #define PE_SKINNY_NTW_GU 4  // 16-column tiles per gate/up workgroup of up to 16 rows
 #endif
@@ -541,7 +544,7 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 
 template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
+void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;   // MFMA tiles per wave
   // DMA instructions per wave per k-tile; A's row groups may not split evenly
@@ -560,7 +563,7 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
   // split-K (E_PART): the grid holds ksplit copies of the tile grid, copy ks
   // summing k-tiles [ks nk / ksplit, (ks + 1) nk / ksplit); the copies are
   // multiples of 8 workgroups, so the XCD of a workgroup is unchanged
-  int bid = blockIdx.x, ks = 0, kbase = 0, nk = g.K / 64;
+  int bid = blockIdx.x, ks = 0, kbase = 0, nk = g.K / 64, mt, nt;
   if constexpr (EPI == E_PART) {
     const int per = mtiles * ((ntiles + 7) / 8) * 8;
     ks = bid / per;
@@ -568,9 +571,28 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
     kbase = ks * nk / g.ksplit;
     nk = (ks + 1) * nk / g.ksplit - kbase;
   }
-  const int b = bid, xcd = b & 7, j = b >> 3;
-  const int mt = j % mtiles, nt = (j / mtiles) * 8 + xcd;
-  if (nt >= ntiles) return;  // padding workgroup of the XCD-aligned grid
+  // LM head with a split tail (E_ARGMAX, tail0 < ntiles): column tiles
+  // [0, tail0) run whole; each tile of [tail0, ntiles) runs as ksplit k-range
+  // pieces after them, which write fp32 partial tiles for argmax_tail_kernel.
+  // Piece u = (column tile - tail0) * ksplit + split; the mtiles pieces that
+  // share a weight k-range sit 8 workgroups apart, on one XCD.
+  const int main_grid = mtiles * ((tail0 + 7) / 8) * 8;
+  const bool tail = EPI == E_ARGMAX && bid >= main_grid;
+  if (tail) {
+    const int t = bid - main_grid, j = t >> 3;
+    const int u = (j / mtiles) * 8 + (t & 7);
+    if (u >= (ntiles - tail0) * g.ksplit) return;  // padding workgroup
+    mt = j % mtiles;
+    nt = tail0 + u / g.ksplit;
+    ks = u % g.ksplit;
+    kbase = ks * nk / g.ksplit;
+    nk = (ks + 1) * nk / g.ksplit - kbase;
+  } else {
+    const int j = bid >> 3;
+    mt = j % mtiles;
+    nt = (j / mtiles) * 8 + (bid & 7);
+    if (nt >= tail0) return;  // padding workgroup of the XCD-aligned grid
+  }
   const int m0 = mt * BM, n0 = nt * BN;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
   const int wm = w / WN, wn = w % WN;
@@ -690,6 +712,19 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles) {
         }
       }
   } else if constexpr (EPI == E_ARGMAX) {
+    if (tail) {
+      // partial tile [BM][BN] of piece ks of tail tile (nt - tail0, mt)
+      float* P = g.part + ((long long)((nt - tail0) * mtiles + mt) * g.ksplit + ks) * (BM * BN);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lrow = wm * (BM / WM) + i * 16 + kg * 4 + r;
+#pragma unroll
+          for (int jj = 0; jj < TJ; ++jj) P[lrow * BN + wn * (BN / WN) + jj * 16 + col] = acc[i][jj][r];
+        }
+      return;
+    }
     __syncthreads();  // every fragment read is done; no DMA is in flight
     uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [WN][BM]
     static_assert(WN * BM * 8 <= STAGE, "argmax scratch fits one stage");
@@ -965,15 +1000,87 @@ static hipError_t run_wide_any(const GemmArgs& g, int num_cus, hipStream_t st) {
   return run_wide<1>(g, num_cus, st);
 }
 
+// Tail split of a tiled LM head.  Its tiles run in rounds of `slots`
+// workgroups (CUs x workgroups per CU); when the last round would hold at most
+// half a round, the column tiles it needs run instead as `ks` k-range pieces
+// each (at least PE_TAIL_MIN_KTILES k-tiles per piece, at most one round of
+// pieces, partial tiles within `cap` floats), so the last round is short.
+// Returns ks (1: no split) and the first tail column tile.
+int argmax_tail_split(int mtiles, int ntiles, int nk, int slots, long long tile_floats, long long cap,
+                      int* tail0) {
+  *tail0 = ntiles;
+  const long long T = (long long)mtiles * ntiles, rem = T % slots;
+  if (T < slots || rem == 0 || rem > slots / 2 || tile_floats <= 0) return 1;
+  const int ncols = int((rem + mtiles - 1) / mtiles);
+  const long long tt = (long long)ncols * mtiles;
+  long long ks = slots / tt;
+  ks = std::min<long long>(ks, nk / PE_TAIL_MIN_KTILES);
+  ks = std::min<long long>(ks, cap / (tt * tile_floats));
+  if (ks < 2) return 1;
+  *tail0 = ntiles - ncols;
+  return int(ks);
+}
+
+// Adds the k-split partial tiles of the tail column tiles [tail0, ntiles) in
+// split order and writes each row's partial argmax key (and the logits when
+// they are asked for).  One wave per (tail tile, row), 4 columns per lane.
+template <int BM>
+__global__ __launch_bounds__(256) void argmax_tail_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
+  constexpr int BN = 256;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (wave >= (ntiles - tail0) * mtiles * BM) return;
+  const int tt = wave / BM, lrow = wave - tt * BM;
+  const int mt = tt % mtiles, nt = tail0 + tt / mtiles, m = mt * BM + lrow;
+  if (m >= g.M) return;
+  const float* P = g.part + (long long)tt * g.ksplit * (BM * BN) + lrow * BN + 4 * l;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < g.ksplit; ++s) {
+    const float4 p = *reinterpret_cast<const float4*>(P + (long long)s * (BM * BN));
+    v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+  }
+  const int n0 = nt * BN + 4 * l;
+  uint64_t best = 0ull;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (n0 + t < g.N) {
+      if (g.logits) g.logits[(long long)m * g.ldl + n0 + t] = v[t];
+      const uint64_t k = argmax_key(v[t], n0 + t);
+      best = k > best ? k : best;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t k = shfl_xor_u64(best, o);
+    best = k > best ? k : best;
+  }
+  if (l == 0) g.keys[(long long)m * g.parts + nt] = best;
+}
+
 template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int S>
-static hipError_t run_tiled(const GemmArgs& g, hipStream_t st) {
+static hipError_t run_tiled(const GemmArgs& g, hipStream_t st, int slots = 0) {
   if (g.K % 64) return hipErrorInvalidValue;  // whole 64-wide k-tiles (and A_FC halves)
   const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN;
   if (EPI == E_ARGMAX && g.parts != ntiles) return hipErrorInvalidValue;
-  const int grid = mtiles * ((ntiles + 7) / 8) * 8;
+  GemmArgs ga = g;
+  int tail0 = ntiles, ks = 1;
+  if constexpr (EPI == E_ARGMAX) {
+    static_assert(EPI != E_ARGMAX || BN == 256, "the tail reduction takes 256-column tiles");
+    if (slots > 0 && g.part)
+      ks = argmax_tail_split(mtiles, ntiles, g.K / 64, slots, (long long)BM * BN, g.part_cap, &tail0);
+    ga.ksplit = ks;
+  }
+  const int ntail = (ntiles - tail0) * ks;
+  const int grid = mtiles * ((tail0 + 7) / 8) * 8 + (ntail ? mtiles * ((ntail + 7) / 8) * 8 : 0);
   hipLaunchKernelGGL((gemm_tiled_kernel<EPI, AL, BMAP, BM, BN, WM, WN, S>), dim3(grid),
-                     dim3(64 * WM * WN), 0, st, g, mtiles, ntiles);
-  return hipGetLastError();
+                     dim3(64 * WM * WN), 0, st, ga, mtiles, ntiles, tail0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !ntail) return e;
+  if constexpr (EPI == E_ARGMAX) {
+    const int waves = (ntiles - tail0) * mtiles * BM;
+    hipLaunchKernelGGL(argmax_tail_kernel<BM>, dim3((waves + 3) / 4), dim3(256), 0, st, ga, mtiles, ntiles,
+                       tail0);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 // Split-K sum and epilogue: the ksplit fp32 partials of each output are added
@@ -1065,7 +1172,7 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
   gp.ksplit = int(ks);
   const long long per = (long long)mtiles * ((ntiles + 7) / 8) * 8;
   hipLaunchKernelGGL((gemm_tiled_kernel<E_PART, AL, BMAP, BM, BN, WM, WN, S>), dim3(unsigned(per * ks)),
-                     dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles);
+                     dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles, ntiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long work = (long long)g.M * (EPI == E_QKV ? g.N / 2 : EPI == E_SILU ? g.N / 16 : g.N / 8);
@@ -1139,10 +1246,11 @@ static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
   if constexpr (EPI == E_ARGMAX) {
     switch (v) {
       case V_WIDE: return run_wide_any(g, num_cus, st);
-      case V_A64: return run_tiled<EPI, AL, BMAP, 64, kArgmaxBN, 1, 4, 2>(g, st);
-      case V_A128: return run_tiled<EPI, AL, BMAP, 128, kArgmaxBN, 2, 4, 2>(g, st);
-      case V_A224: return run_tiled<EPI, AL, BMAP, 224, kArgmaxBN, 2, 4, 2>(g, st);
-      default: return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN, 4, 2, 2>(g, st);
+      // workgroups per CU: two 64-row tiles (80 KB of LDS each), one otherwise
+      case V_A64: return run_tiled<EPI, AL, BMAP, 64, kArgmaxBN, 1, 4, 2>(g, st, 2 * num_cus);
+      case V_A128: return run_tiled<EPI, AL, BMAP, 128, kArgmaxBN, 2, 4, 2>(g, st, num_cus);
+      case V_A224: return run_tiled<EPI, AL, BMAP, 224, kArgmaxBN, 2, 4, 2>(g, st, num_cus);
+      default: return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN, 4, 2, 2>(g, st, num_cus);
     }
   } else {
     switch (v) {

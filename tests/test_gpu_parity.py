@@ -159,6 +159,18 @@ def test_small_bf16_lm_head_224_row_tiles(B, seed):
     _full_check(SMALL_BF16.with_(K=7, batch=B, accepted="uniform", prefix=("uniform", 20, 120)), seed=seed)
 
 
+@pytest.mark.parametrize("K,B,vocab,seed", [(7, 64, 33200, 93), (5, 16, 65904, 94), (3, 16, 131504, 95),
+                                             (7, 32, 65904, 96)])
+def test_small_bf16_lm_head_split_tail(K, B, vocab, seed):
+    """LM heads whose last round of vocabulary tiles would hold only a few
+    tiles (448, 80, 48 and 224 draft rows: 224-, 128-, 64- and 256-row tiles):
+    the last column tiles run as k-range pieces whose fp32 partial tiles are
+    summed in split order before the row argmax (ragged last tile)."""
+    w = SMALL_BF16.with_(K=K, batch=B, d=1024, vocab=vocab, mlp=1024, weight_std=1 / 32,
+                         accepted="uniform", prefix=("uniform", 20, 120))
+    _full_check(w, seed=seed)
+
+
 @pytest.mark.parametrize("B", [5, 12])
 def test_small_bf16_tiled_path(B):
     """B*2K > 64 rows: the LDS-tiled GEMM path and the tiled LM head."""
@@ -336,15 +348,20 @@ def test_closed_loop_rounds():
         st.close()
 
 
-@pytest.mark.parametrize("case", ["bf16", "bf16_padded", "f32"])
+@pytest.mark.parametrize("case", ["bf16", "bf16_padded", "f32", "bf16_library"])
 def test_step_graph_replays_match_eager(case):
     """One captured graph of the parallel step (preparation and hidden-state
     copy in one launch, forward, argmax and verification in one launch)
     replayed several times, with eager work and synchronization in between;
     every replay equals the four eager entry points bit for bit: batch fields,
-    drafter inputs, tokens, logits, verification, KV cache and error word."""
+    drafter inputs, tokens, logits, verification, KV cache and error word.
+    The library case (280 forward rows) runs its plain GEMMs through
+    hipBLASLt, whose algorithm is chosen by timing before the capture: the
+    choice must be the same, and deterministic, in both."""
     if case == "f32":
         w = configs.TINY.with_(K=5, batch=3, accepted="uniform", prefix=("uniform", 40, 200))
+    elif case == "bf16_library":
+        w = SMALL_BF16.with_(K=7, batch=20, accepted="uniform", prefix=("uniform", 40, 400))
     else:
         w = SMALL_BF16.with_(K=7, batch=6, accepted="uniform", prefix=("uniform", 40, 400))
     st = Setup(w, seed=11)
