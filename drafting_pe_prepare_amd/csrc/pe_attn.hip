@@ -133,6 +133,7 @@ void attn_partial_kernel(AttnArgs a) {
   const uint16_t* Vc = (const uint16_t*)a.vcache;
   const int bs = a.block_size, bsl = __builtin_ctz(bs);  // power of two (checked on the host)
   const uint4 zero = {0u, 0u, 0u, 0u};
+  const uint4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
   // fragment offsets inside a 32-position half
   int koff[2][2], voff[4];
 #pragma unroll
@@ -170,10 +171,11 @@ void attn_partial_kernel(AttnArgs a) {
 
     // query tiles of this wave
     uint4 qf[QPW][2];
-    float m[QPW], lsum[QPW];
+    float m[QPW];
     int qpos[QPW], qmin[QPW];
     bool qv[QPW], qany[QPW];
     f32x4 o[QPW][4];
+    f32x4 osum[QPW];  // row sums of P: the PV product with an all-ones "V" tile
 #pragma unroll
     for (int qq = 0; qq < QPW; ++qq) {
       const int q = (w + 8 * qq) * 16 + c;
@@ -186,7 +188,7 @@ void attn_partial_kernel(AttnArgs a) {
       qf[qq][0] = v ? ld16(qp) : zero;
       qf[qq][1] = v ? ld16(qp + 32) : zero;
       m[qq] = -INFINITY;
-      lsum[qq] = 0.f;
+      osum[qq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[qq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       // lowest position among the tile's valid queries (wave-uniform): steps
@@ -275,7 +277,9 @@ void attn_partial_kernel(AttnArgs a) {
             sc[pt] = mfma16(kf[pt][0], qf[qq][0], f32x4{0.f, 0.f, 0.f, 0.f});
             sc[pt] = mfma16(kf[pt][1], qf[qq][1], sc[pt]);
           }
-          // lane (gq, c): sc[pt][i] scores position pv0 + 4pt + i for query c
+          // lane (gq, c): sc[pt][i] scores position pv0 + 4pt + i for query c.
+          // The max is taken over raw scores (the scale is positive) and the
+          // scale enters inside the exponent's FMA.
           float v[8];
           float mloc = -INFINITY;
           if (ph0 + 31 < pe && ph0 + 31 <= qmin[qq]) {
@@ -283,7 +287,7 @@ void attn_partial_kernel(AttnArgs a) {
             // query of the tile: no mask (invalid queries' results are unused)
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-              v[t] = sc[t >> 2][t & 3] * sl2;
+              v[t] = sc[t >> 2][t & 3];
               mloc = fmaxf(mloc, v[t]);
             }
           } else {
@@ -291,34 +295,31 @@ void attn_partial_kernel(AttnArgs a) {
             for (int t = 0; t < 8; ++t) {
               const int pos = pv0 + t;
               const bool ok = qv[qq] && pos < pe && pos <= qpos[qq];
-              v[t] = ok ? sc[t >> 2][t & 3] * sl2 : -INFINITY;
+              v[t] = ok ? sc[t >> 2][t & 3] : -INFINITY;
               mloc = fmaxf(mloc, v[t]);
             }
           }
           mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
           mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-          const float mnew = fmaxf(m[qq], mloc);
+          const float mnew = fmaxf(m[qq], mloc * sl2);
           const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-          // P = hi + lo, both bf16: the PV product sees P to ~16 bits, the row
-          // sum takes the fp32 values themselves.  exp2 of a non-positive
-          // argument: v_exp_f32 flushes results below 2^-126 to 0.
+          // P = hi + lo, both bf16: the PV product sees P to ~16 bits, and so
+          // does the row sum, taken by the same MFMAs on an all-ones tile.
+          // exp2 of a non-positive argument: v_exp_f32 flushes results below
+          // 2^-126 to 0.
           uint32_t ph[4], pl[4];
-          float ps = 0.f;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const float p0 = __builtin_amdgcn_exp2f(v[2 * jj] - mref);
-            const float p1 = __builtin_amdgcn_exp2f(v[2 * jj + 1] - mref);
-            ps += p0 + p1;
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(v[2 * jj], sl2, -mref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(v[2 * jj + 1], sl2, -mref));
             ph[jj] = f2bf2(p0, p1);
             pl[jj] = f2bf2(p0 - __uint_as_float(ph[jj] << 16), p1 - __uint_as_float(ph[jj] & 0xFFFF0000u));
           }
           if (__ballot(mnew != m[qq])) {  // some query's running max moved: rescale
             const float alpha = __builtin_amdgcn_exp2f(m[qq] - mref);
-            lsum[qq] = lsum[qq] * alpha + ps;
+            osum[qq] = osum[qq] * alpha;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) o[qq][dt] = o[qq][dt] * alpha;
-          } else {
-            lsum[qq] += ps;
           }
           m[qq] = mnew;
           const uint4 pfh = {ph[0], ph[1], ph[2], ph[3]};
@@ -328,6 +329,8 @@ void attn_partial_kernel(AttnArgs a) {
             o[qq][dt] = mfma16(vf[dt], pfh, o[qq][dt]);
             o[qq][dt] = mfma16(vf[dt], pfl, o[qq][dt]);
           }
+          osum[qq] = mfma16(ones, pfh, osum[qq]);
+          osum[qq] = mfma16(ones, pfl, osum[qq]);
         }
       }
     };
@@ -345,9 +348,7 @@ void attn_partial_kernel(AttnArgs a) {
     for (int qq = 0; qq < QPW; ++qq) {
       const int t = w + 8 * qq;
       if (t >= QT) break;
-      float ls = lsum[qq];
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
+      const float ls = osum[qq][0];  // every row of the ones tile holds query c's sum
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
