@@ -19,23 +19,28 @@ namespace pe {
 
 // Validates request r and, when `write`, stores its slot fields; one wave
 // (lane = slot).  Returns the error kinds found (0: valid).
-__device__ uint32_t prepare_request(const PrepareArgs& a, int r, int lane, bool write) {
+__device__ __forceinline__ uint32_t prepare_request(const PrepareArgs& a, int r, int lane, bool write) {
   const int K = a.K, S = 2 * K, base = r * S;
   const int32_t* vt = a.vt + (long long)r * (K + 1);
   const int32_t* vp = a.vp + (long long)r * (K + 1);
+  // every load the wave needs first, at clamped (valid) addresses, so that
+  // they are in flight together rather than one round trip after another
   const int acc = a.acc[r];
   const int p0 = vp[0];
+  const int bonus = a.bonus[r];
+  const int vt_l = vt[lane < K ? lane + 1 : K];  // d_{lane+1}
+  const int vp_l = vp[lane < K ? lane : K];
 
   uint32_t kinds = 0;
   if (acc < 0 || acc > K) kinds |= 1u;
   // accepted drafts (lanes j < a read d_{j+1}) and the bonus token
   bool bad_tok = false;
   if (!(kinds & 1u)) {
-    if (lane < acc) { int t = vt[lane + 1]; bad_tok = (t < 0 || t >= a.vocab); }
-    if (lane == acc) { int t = a.bonus[r]; bad_tok = (t < 0 || t >= a.vocab); }
+    if (lane < acc) bad_tok = (vt_l < 0 || vt_l >= a.vocab);
+    if (lane == acc) bad_tok = (bonus < 0 || bonus >= a.vocab);
   }
   if (__ballot(bad_tok)) kinds |= 2u;
-  bool bad_pos = (lane <= K) && (vp[lane] != p0 + lane);
+  bool bad_pos = (lane <= K) && (vp_l != p0 + lane);
   if (__ballot(bad_pos)) kinds |= 8u;
   if (p0 < 0 || p0 > 0x7FFFFFFF - 2 * K - 1) kinds |= 4u;  // position range
   int seq_len = 0;
@@ -47,9 +52,13 @@ __device__ uint32_t prepare_request(const PrepareArgs& a, int r, int lane, bool 
     } else {
       bool bad_blk = false;
       const int32_t* btr = a.bt + (long long)r * a.max_blocks;
-      for (int b = lane; b < nb; b += 64) {
-        int id = btr[b];
-        bad_blk |= (id < 0 || id >= a.num_kv_blocks);
+      // 8 loads in flight per lane; indices past nb re-read entry nb - 1
+      for (int b0 = lane; b0 < nb; b0 += 8 * 64) {
+        int id[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) id[i] = btr[min(b0 + 64 * i, nb - 1)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bad_blk |= (id[i] < 0 || id[i] >= a.num_kv_blocks);
       }
       if (__ballot(bad_blk)) kinds |= 4u;
     }
@@ -79,10 +88,10 @@ __device__ uint32_t prepare_request(const PrepareArgs& a, int r, int lane, bool 
     int tok, p, src;
     uint8_t rej = 0, msk = 0;
     if (lane <= K) {
-      p = vp[lane];
+      p = vp_l;
       src = r * (K + 1) + lane;
-      if (lane < acc) tok = vt[lane + 1];
-      else if (lane == acc) tok = a.bonus[r];
+      if (lane < acc) tok = vt_l;
+      else if (lane == acc) tok = bonus;
       else { tok = 0; rej = 1; }
     } else {
       const int m = lane - K;
@@ -251,19 +260,25 @@ __global__ __launch_bounds__(1024) void prepare_gather_kernel(PrepareArgs a, int
 #pragma unroll
   for (int i = 0; i < PG_CHUNKS; ++i) {
     const int c = threadIdx.x + i * blockDim.x;
-    if (c < cpr) v[i] = from[c];
+    v[i] = from[c < cpr ? c : cpr - 1];  // unconditional: the loads go out together
   }
   if (threadIdx.x < 64) {
     const uint32_t kinds = prepare_request(a, r, threadIdx.x, j == 0);
     if (threadIdx.x == 0) s_kinds = kinds;
   }
   __syncthreads();
-  const bool shared_row = src < 0 || s_kinds != 0;
   uint4* dst = out + ((long long)r * 2 * K + j) * cpr;
+  if (src >= 0 && s_kinds != 0) {
+    // an invalid request's copied slot: its -1 map entry means h_shared
+    for (int c = threadIdx.x; c < cpr; c += blockDim.x) dst[c] = hs[c];
+  } else {
+    // (two separate stores: a select between the two sources would take
+    // the address of v and put it in scratch memory)
 #pragma unroll
-  for (int i = 0; i < PG_CHUNKS; ++i) {
-    const int c = threadIdx.x + i * blockDim.x;
-    if (c < cpr) dst[c] = (shared_row && src >= 0) ? hs[c] : v[i];
+    for (int i = 0; i < PG_CHUNKS; ++i) {
+      const int c = threadIdx.x + i * blockDim.x;
+      if (c < cpr) dst[c] = v[i];
+    }
   }
 }
 
