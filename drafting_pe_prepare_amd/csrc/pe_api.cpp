@@ -81,6 +81,7 @@ struct pe_ctx {
   // the fc A operand and the fp32 result the fused epilogue kernel reads
   pe::Blas* blas = nullptr;
   void* fc_a = nullptr;
+  void* xc = nullptr;  // [R, d] first-layer fc output on the MASK-deduplicated rows
   float* blas_c = nullptr;
   std::vector<void*> rows_qkv, rows_gu;
   float* splitk = nullptr;      // split-K GEMM partials (bf16 storage)
@@ -173,6 +174,7 @@ void free_ctx(pe_ctx* c) {
     if (p) (void)hipFree(p);
   if (c->fc_a) (void)hipFree(c->fc_a);
   if (c->blas_c) (void)hipFree(c->blas_c);
+  if (c->xc) (void)hipFree(c->xc);
   pe::blas_destroy(c->blas);
   delete c;
 }
@@ -411,6 +413,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
     if (R >= size_t(PE_BLAS_MIN_ROWS) && (c->blas = pe::blas_create(size_t(32) << 20)) != nullptr) {
       const size_t maxN = std::max({size_t(k.d), size_t(qd + 2 * kvd), size_t(2 * k.mlp)});
       s = alloc(&c->fc_a, R * 2 * k.d * 2, "fc operand rows");
+      if (s == PE_OK) s = alloc(&c->xc, R * k.d * 2, "deduplicated fc rows");
       if (s == PE_OK) s = alloc(&c->blas_c, R * maxN * 4, "GEMM result");
       c->rows_qkv.assign(k.layers, nullptr);
       c->rows_gu.assign(k.layers, nullptr);
@@ -552,6 +555,8 @@ struct Pass {
   // when set: draft tokens drawn from softmax(logits / T) instead of argmax
   const uint64_t* seed = nullptr;
   float inv_temp = 1.f;
+  // the parallel-step layout (S = 2K: copied slots 0..K, MASK slots K+1..2K-1)
+  bool parallel_layout = false;
 };
 
 static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_table,
@@ -602,6 +607,17 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   };
   pe_status ds = PE_OK;
 
+  // MASK-slot deduplication of the first layer.  In the parallel-step layout
+  // the K-1 MASK slots of a request all carry emb(MASK) and h_shared, so the
+  // first layer's fc, norm and (pre-RoPE) QKV rows of those slots are equal:
+  // with library GEMMs they run on K+2 rows per request (copied slots and one
+  // MASK slot), the norm writes the fc rows out to every slot, and the QKV
+  // epilogue (RoPE at each slot's own position, KV write) runs for every slot.
+  const int Kc = k.K, Rc = B * (Kc + 2);
+  const bool dedup = P.parallel_layout && dt == PE_BF16 && ctx->blas && ctx->xc && R >= PE_BLAS_MIN_ROWS &&
+                     Kc >= 3 && !ctx->rows_qkv.empty();
+  bool dd = false;  // the first layer's fc ran deduplicated (its output is in xc)
+
   // fc over concat(emb(token), hidden)
   {
     pe::GemmArgs g = g0;
@@ -610,13 +626,25 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     g.W0 = ctx->w.w_fc; g.Wp = ctx->fc_packed;
     g.out = ctx->x; g.ldo = d;
     Timed tm(ctx, PE_PH_FC);
-    if ((ds = dense(pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, ctx->w.w_fc, "fc")) != PE_OK) return ds;
+    if (dedup) {
+      pe::GemmArgs gc = g;
+      gc.M = Rc;
+      gc.dedup_k = Kc;
+      PE_HIP(pe::launch_fc_rows(gc, ctx->fc_a, st), "fc rows");
+      dd = pe::blas_gemm_bf16(ctx->blas, Rc, d, 2 * d, ctx->fc_a, ctx->w.w_fc, nullptr, ctx->xc, st);
+    }
+    if (!dd && (ds = dense(pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, ctx->w.w_fc, "fc")) != PE_OK) return ds;
   }
   for (int l = 0; l < k.layers; ++l) {
     const pe_layer_weights& L = ctx->layers[l];
+    const bool first_dd = l == 0 && dd;
     {
       Timed tm(ctx, PE_PH_NORM);
-      PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.attn_norm, ctx->u, nullptr, R, k.rms_eps, st), "attn norm");
+      if (first_dd)
+        PE_HIP(pe::launch_rmsnorm_expand(Rc, d, ctx->xc, L.attn_norm, ctx->u, ctx->x, Kc, k.rms_eps, st),
+               "attn norm");
+      else
+        PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.attn_norm, ctx->u, nullptr, R, k.rms_eps, st), "attn norm");
     }
     {
       pe::GemmArgs g = g0;
@@ -628,8 +656,22 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
       g.rope_turns = ctx->rope_turns;
       Timed tm(ctx, PE_PH_QKV);
-      if ((ds = dense(pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, ctx->rows_qkv.empty() ? nullptr : ctx->rows_qkv[l],
-                      "qkv")) != PE_OK)
+      bool done = false;
+      if (first_dd) {
+        // compact rows through the library; the epilogue covers every slot
+        if (pe::blas_gemm(ctx->blas, Rc, g.N, g.K, ctx->u, ctx->rows_qkv[0], ctx->blas_c, st)) {
+          pe::GemmArgs ge = g;
+          ge.dedup_k = Kc;
+          PE_HIP(pe::launch_epilogue_f32(pe::E_QKV, ge, ctx->blas_c, ctx->num_cus, st), "qkv");
+          done = true;
+        } else {
+          // no library plan for the compact shape: normalise every slot
+          PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.attn_norm, ctx->u, nullptr, R, k.rms_eps, st),
+                 "attn norm");
+        }
+      }
+      if (!done && (ds = dense(pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g,
+                               ctx->rows_qkv.empty() ? nullptr : ctx->rows_qkv[l], "qkv")) != PE_OK)
         return ds;
     }
     {
@@ -765,7 +807,7 @@ pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const 
   if (s != PE_OK || B == 0) return s;
   const int K = ctx->cfg.K;
   Pass P;
-  P.B = B; P.S = 2 * K; P.Kd = K;
+  P.B = B; P.S = 2 * K; P.Kd = K; P.parallel_layout = true;
   P.ids = batch->input_ids; P.pos = batch->positions; P.draft_rows = batch->draft_rows;
   P.seq_lens = batch->seq_lens; P.rej = batch->is_rejected; P.slots = batch->slot_mapping;
   P.hidden = draft_hidden;
@@ -910,7 +952,7 @@ pe_status pe_draft_forward_sampled(pe_ctx* ctx, int32_t B, const pe_batch* batch
     return fail(PE_ERR_INVALID_ARG, "sampled drafting draws from the logits: NULL or not 16-byte aligned");
   const int K = ctx->cfg.K;
   Pass P;
-  P.B = B; P.S = 2 * K; P.Kd = K;
+  P.B = B; P.S = 2 * K; P.Kd = K; P.parallel_layout = true;
   P.ids = batch->input_ids; P.pos = batch->positions; P.draft_rows = batch->draft_rows;
   P.seq_lens = batch->seq_lens; P.rej = batch->is_rejected; P.slots = batch->slot_mapping;
   P.hidden = draft_hidden;
@@ -977,7 +1019,7 @@ static pe_status run_parallel_step(pe_ctx* ctx, int32_t B, const pe_step_args* a
            "prepare + gather launch");
   }
   Pass P;
-  P.B = B; P.S = 2 * K; P.Kd = K;
+  P.B = B; P.S = 2 * K; P.Kd = K; P.parallel_layout = true;
   P.ids = a->batch.input_ids; P.pos = a->batch.positions; P.draft_rows = a->batch.draft_rows;
   P.seq_lens = a->batch.seq_lens; P.rej = a->batch.is_rejected; P.slots = a->batch.slot_mapping;
   P.hidden = a->draft_hidden;

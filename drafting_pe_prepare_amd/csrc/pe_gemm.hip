@@ -1141,9 +1141,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
     const int per_row = g.N / 2;
     for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)g.M * per_row; e += stride) {
       const int m = int(e / per_row), pr = int(e % per_row), nb = (pr >> 4) * 32, c = pr & 15;
+      const int cm = g.dedup_k ? dedup_row(m, g.dedup_k) : m;  // row of the sums (one split then)
       float lo = 0.f, hi = 0.f;
       for (int k = 0; k < KS; ++k) {
-        const float* p = g.part + k * MN + (long long)m * g.N + nb + c;
+        const float* p = g.part + k * MN + (long long)cm * g.N + nb + c;
         lo += p[0];
         hi += p[16];
       }
@@ -1227,8 +1228,10 @@ __global__ __launch_bounds__(256) void fc_rows_kernel(GemmArgs g, uint4* __restr
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
        i += (long long)gridDim.x * blockDim.x) {
     const int m = int(i / cpr), c = int(i - (long long)m * cpr);
+    const int K = g.dedup_k;
+    const int slot = K ? (m / (K + 2)) * (2 * K) + m % (K + 2) : m;
     ARow<uint16_t, A_FC> ar;
-    ar.init(g, m);
+    ar.init(g, slot);
     out[i] = ld16(ar.at(c * 8, g.d));
   }
 }

@@ -83,6 +83,11 @@ hipError_t launch_ar_next(const ArArgs& a, hipStream_t st);
 // out[i] = x[row(i)] * rsqrt(mean(x^2) + eps) * gain; row(i) = rows_idx ? rows_idx[i] : i
 hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void* gain, void* out,
                           const int32_t* rows_idx, int rows_bound, float eps, hipStream_t st);
+// bf16 RMSNorm of the compact rows of a MASK-deduplicated first layer (K+2
+// per request, see GemmArgs::dedup_k) that also writes each raw row x[m] to
+// its slots of the full layout: x_full[s] = x[dedup_row(s, K)] for all B*2K s.
+hipError_t launch_rmsnorm_expand(int rows, int d, const void* x, const void* gain, void* out, void* x_full,
+                                 int K, float eps, hipStream_t st);
 
 // ---- GEMM  out[m, n] = sum_k A[m, k] W[n, k]  + fused epilogue -------------
 enum ALoad { A_PLAIN = 0, A_FC = 1 };
@@ -112,7 +117,18 @@ struct GemmArgs {
   // too few output tiles to fill the chip; the epilogue runs after the sum
   float* part; long long part_cap;  // capacity in floats (0: never split)
   int ksplit;
+  // MASK-slot deduplication in the parallel-step layout (K = dedup_k > 0):
+  // the K-1 MASK slots of a request share one input row, so the first layer's
+  // fc and QKV products run on K+2 rows per request (copied slots 0..K and
+  // one MASK slot).  launch_fc_rows: compact row m gathers slot
+  // (m / (K+2)) * 2K + m % (K+2).  E_QKV epilogue over fp32 sums: slot m reads
+  // compact row dedup_row(m, K).
+  int dedup_k;
 };
+__host__ __device__ inline int dedup_row(int slot, int K) {
+  const int j = slot % (2 * K);
+  return (slot / (2 * K)) * (K + 2) + (j < K + 1 ? j : K + 1);
+}
 hipError_t launch_gemm(int dtype, int aload, int bmap, int epi, const GemmArgs& g, int num_cus,
                        hipStream_t st);
 // Copies the logical bf16 weight of a GEMM (W0/W1/W2 through the bmap row

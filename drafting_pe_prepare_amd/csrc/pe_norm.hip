@@ -10,12 +10,16 @@ namespace pe {
 
 // The row's chunks and the gain's stay in registers between the two passes
 // (NCH per thread; a row of more than 256 * NCH chunks takes the loop again).
+// expand_k > 0: row i is compact row i of a MASK-deduplicated first layer,
+// and its raw chunks are also written to its slots of the full layout in
+// x_full (one slot, or the request's K-1 MASK slots for its last compact row).
 template <typename T, int NCH>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const T* __restrict__ x,
                                                       const T* __restrict__ gain,
                                                       T* __restrict__ out,
                                                       const int32_t* __restrict__ rows_idx,
-                                                      int rows_bound, float eps) {
+                                                      int rows_bound, float eps,
+                                                      T* __restrict__ x_full = nullptr, int expand_k = 0) {
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
   const int i = blockIdx.x;
   int src = rows_idx ? rows_idx[i] : i;
@@ -44,6 +48,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const T* __restrict
     const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
     for (int q = 0; q < V; ++q) { float v = Elt<T>::ld(e + q); ss += v * v; }
+  }
+  if (expand_k > 0) {
+    const int K = expand_k, r = i / (K + 2), j = i - r * (K + 2);
+    const int s0 = r * 2 * K + j, ns = j == K + 1 ? K - 1 : 1;
+    for (int t = 0; t < ns; ++t) {
+      T* xf = x_full + (long long)(s0 + t) * d;
+#pragma unroll
+      for (int jj = 0; jj < NCH; ++jj) {
+        const int c = threadIdx.x + jj * 256;
+        if (c < nc) *reinterpret_cast<uint4*>(xf + c * V) = xs[jj];
+      }
+      for (int c = threadIdx.x + NCH * 256; c < nc; c += 256) *reinterpret_cast<uint4*>(xf + c * V) = ld16(xr + c * V);
+    }
   }
   __shared__ float red[4];
   ss = wave_sum(ss);
@@ -78,6 +95,15 @@ hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void*
   else
     hipLaunchKernelGGL((rmsnorm_kernel<float, 2>), dim3(rows), dim3(256), 0, st, d, (const float*)x,
                        (const float*)gain, (float*)out, rows_idx, rows_bound, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_expand(int rows, int d, const void* x, const void* gain, void* out, void* x_full,
+                                 int K, float eps, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (K < 2 || rows % (K + 2)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((rmsnorm_kernel<uint16_t, 2>), dim3(rows), dim3(256), 0, st, d, (const uint16_t*)x,
+                     (const uint16_t*)gain, (uint16_t*)out, nullptr, rows, eps, (uint16_t*)x_full, K);
   return hipGetLastError();
 }
 
