@@ -142,11 +142,13 @@ def test_small_bf16_lm_head_tiles_cut_between_waves(d, vocab, B):
     _full_check(w, seed=85 + B)
 
 
-@pytest.mark.parametrize("K,B,d,seed", [(7, 40, 256, 88), (4, 72, 512, 89)])
+@pytest.mark.parametrize("K,B,d,seed", [(7, 40, 256, 88), (4, 72, 512, 89), (3, 43, 256, 97), (2, 64, 256, 98)])
 def test_small_bf16_library_gemms(K, B, d, seed):
-    """560 and 576 forward rows: the plain GEMMs run through hipBLASLt; the
-    fc and residual GEMMs write bf16 directly, RoPE/KV write and SiLU.mul run
-    on its fp32 results."""
+    """560, 576, 258 and 256 forward rows: the plain GEMMs run through
+    hipBLASLt; the fc and residual GEMMs write bf16 directly, RoPE/KV write
+    and SiLU.mul run on its fp32 results.  For K >= 3 the first layer's fc
+    and QKV products run on K+2 rows per request (one row for the K-1 MASK
+    slots), K = 2 keeps every slot."""
     w = SMALL_BF16.with_(K=K, batch=B, d=d, weight_std=1 / np.sqrt(d), accepted="uniform",
                          prefix=("uniform", 30, 200))
     _full_check(w, seed)
@@ -239,6 +241,28 @@ def test_padded_request_gets_no_kv_write_and_token_minus_one():
         assert np.all(fw["tokens"][4:8] == -1)
         assert_kv(w, g["kv"], inp, fw)
         keep = np.r_[0:4, 8:12]
+        assert_tokens_logits(g["tokens"], g["logits"], fw["logits"][keep], LOGIT_TOL["bf16"], keep)
+    finally:
+        st.close()
+
+
+def test_padded_request_with_library_gemms():
+    """A padded request among 40 (560 forward rows, library GEMMs with the
+    first layer's MASK slots deduplicated): its slots write no KV and draft
+    -1, every other request matches the oracle."""
+    w = SMALL_BF16.with_(K=7, batch=40, accepted="uniform", prefix=("uniform", 30, 200))
+    st = Setup(w, seed=99)
+    try:
+        inp = synth.step_inputs(w, seed=99)
+        inp["num_accepted"][5] = w.K + 3
+        g = run_step(st, inp)
+        ob, ohd, fw = oracle_step(w, st.prm, inp)
+        assert_metadata_equal(g["batch"], ob)
+        assert g["error"] == (O.ERR_ACCEPTED, 5)
+        K = w.K
+        assert np.all(g["tokens"][5 * K:6 * K] == -1)
+        assert_kv(w, g["kv"], inp, fw)
+        keep = np.r_[0:5 * K, 6 * K:w.batch * K]
         assert_tokens_logits(g["tokens"], g["logits"], fw["logits"][keep], LOGIT_TOL["bf16"], keep)
     finally:
         st.close()
