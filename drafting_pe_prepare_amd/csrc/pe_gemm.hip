@@ -225,6 +225,21 @@ __device__ void epilogue_argmax(const GemmArgs& g, const float* tile, int ldt, i
 // of the request (the same fixed reduction as argmax_tokens_kernel), then wave
 // 0 finds the first draft that differs from the target's token (a' = K when
 // none does) and takes the target's token there as the bonus.
+// Max of this lane's keys kr[l], kr[l + stride], ... below `parts`: 8 loads
+// in flight at a time (indices past the end re-read the last key, which
+// leaves the max unchanged).
+__device__ __forceinline__ uint64_t max_keys(const uint64_t* __restrict__ kr, int parts, int l, int stride) {
+  uint64_t best = 0;
+  for (int p0 = l; p0 < parts; p0 += 8 * stride) {
+    uint64_t k[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = kr[min(p0 + i * stride, parts - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) best = k[i] > best ? k[i] : best;
+  }
+  return best;
+}
+
 __global__ __launch_bounds__(1024) void argmax_verify_kernel(int K, int parts,
                                                              const uint64_t* __restrict__ keys,
                                                              int32_t* __restrict__ tokens,
@@ -238,8 +253,7 @@ __global__ __launch_bounds__(1024) void argmax_verify_kernel(int K, int parts,
   for (int i = w; i < K; i += nw) {
     const long long row = (long long)r * K + i;
     const uint64_t* kr = keys + row * parts;
-    uint64_t best = 0;
-    for (int p = l; p < parts; p += 64) best = kr[p] > best ? kr[p] : best;
+    uint64_t best = max_keys(kr, parts, l, 64);
     for (int o = 32; o > 0; o >>= 1) {
       const uint64_t k = shfl_xor_u64(best, o);
       best = k > best ? k : best;
@@ -273,8 +287,7 @@ __global__ __launch_bounds__(256) void argmax_tokens_kernel(int M, int Kd, int p
   __shared__ uint64_t red[4];
   const int row = blockIdx.x;
   const uint64_t* kr = keys + (long long)row * parts;
-  uint64_t best = 0;
-  for (int p = threadIdx.x; p < parts; p += blockDim.x) best = kr[p] > best ? kr[p] : best;
+  uint64_t best = max_keys(kr, parts, threadIdx.x, blockDim.x);
   for (int o = 32; o > 0; o >>= 1) {
     const uint64_t k = shfl_xor_u64(best, o);
     best = k > best ? k : best;

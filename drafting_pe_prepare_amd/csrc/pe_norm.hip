@@ -30,8 +30,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const T* __restrict
   uint4 xs[NCH], gs[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    const int c = threadIdx.x + j * 256;
-    if (c < nc) { xs[j] = ld16(xr + c * V); gs[j] = ld16(gain + c * V); }
+    // unconditional loads (past the row's end: its last chunk, unused), so
+    // that all of them are in flight together
+    const int c = min(threadIdx.x + j * 256, nc - 1);
+    xs[j] = ld16(xr + c * V);
+    gs[j] = ld16(gain + c * V);
   }
   float ss = 0.f;
 #pragma unroll
