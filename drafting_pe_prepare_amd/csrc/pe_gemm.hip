@@ -627,11 +627,14 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
         __builtin_amdgcn_global_load_lds(
             (__attribute__((address_space(1))) void*)ar[i].at(k0 + lc, g.d),
             (__attribute__((address_space(3))) void*)(st + (w + NW * i) * 1024), 16, 0, 0);
+    // the LM head's weights stream once per launch: non-temporal (cache
+    // policy nt), so they do not push A and the layer weights out of the caches
+    constexpr int BPOL = EPI == E_ARGMAX ? 2 : 0;
 #pragma unroll
     for (int i = 0; i < LB; ++i)
       __builtin_amdgcn_global_load_lds(
           (__attribute__((address_space(1))) void*)(bp[i] + k0),
-          (__attribute__((address_space(3))) void*)(st + BM * 128 + (w + NW * i) * 1024), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(st + BM * 128 + (w + NW * i) * 1024), 16, 0, BPOL);
   };
 
   f32x4 acc[TI][TJ];
