@@ -50,12 +50,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, int* off,
                           int& CH) {
   __shared__ long long s_tot[8];
-  __shared__ int s_part[512];
-  const int tid = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
+  __shared__ int s_wsum[8];
+  const int tid = threadIdx.x, nt = blockDim.x, nw = nt >> 6, lane = tid & 63, wid = tid >> 6;
+  // thread tid owns requests [r0, r1)
+  const int per = (B + nt - 1) / nt, r0 = min(B, tid * per), r1 = min(B, r0 + per);
   long long tot = 0;
-  for (int r = tid; r < B; r += nt) tot += max(seq_lens[r], 0);
+  for (int r = r0; r < r1; ++r) tot += max(seq_lens[r], 0);
   for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
-  if ((tid & 63) == 0) s_tot[tid >> 6] = tot;
+  if (lane == 0) s_tot[wid] = tot;
   __syncthreads();
   tot = 0;
   for (int w = 0; w < nw; ++w) tot += s_tot[w];
@@ -64,24 +66,25 @@ __device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, i
   if (ch < PE_ATTN_MIN_CH) ch = PE_ATTN_MIN_CH;  // fewer, longer items when the batch is small (each item pays a DMA ramp-up)
   if (ch > (1 << 30)) ch = 1 << 30;
   CH = int(ch);
-  const int per = (B + nt - 1) / nt;
-  const int r0 = tid * per;
   int sum = 0;
-  for (int r = r0; r < min(B, r0 + per); ++r) sum += (max(seq_lens[r], 0) + CH - 1) / CH;
-  s_part[tid] = sum;
-  __syncthreads();
-  for (int o = 1; o < nt; o <<= 1) {
-    const int v = tid >= o ? s_part[tid - o] : 0;
-    __syncthreads();
-    s_part[tid] += v;
-    __syncthreads();
+  for (int r = r0; r < r1; ++r) sum += (max(seq_lens[r], 0) + CH - 1) / CH;
+  // block-wide exclusive prefix of the chunk counts: a shuffle scan inside
+  // each wave, then the totals of the waves before it
+  int inc = sum;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += v;
   }
-  int run = s_part[tid] - sum;
-  for (int r = r0; r < min(B, r0 + per); ++r) {
+  if (lane == 63) s_wsum[wid] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += s_wsum[w];
+  int run = base + inc - sum;
+  for (int r = r0; r < r1; ++r) {
     off[r] = run;
     run += (max(seq_lens[r], 0) + CH - 1) / CH;
   }
-  if (tid == nt - 1) off[B] = s_part[nt - 1];
+  if (tid == nt - 1) off[B] = base + inc;
   __syncthreads();
 }
 
