@@ -194,6 +194,29 @@ def measure(w, steps, warmup, prm=None, dev=None, label="", with_ar=True):
     print(f"[bench] {label} graph: {ms_step * 1e3:.1f} us/step (events {ev_ms * 1e3 / steps:.1f})",
           file=sys.stderr, flush=True)
 
+    # per-replay distribution (HIP events around each replay, after the timed
+    # region), then the same with the caches flushed before every replay: a
+    # 512 MiB in-place add on the stream ahead of the step evicts L2 and the
+    # 256 MB Infinity Cache, so the step starts with every weight in HBM
+    def replay_us(n, flush=None):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            if flush is not None:
+                flush.add_(1)
+            a.record(stream)
+            pb.pe_step_graph(ctx, B, args)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    dist = replay_us(min(200, max(50, steps)))
+    flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = replay_us(min(50, max(20, steps // 4)), flush_buf)
+    del flush_buf
+    err = pb.pe_get_device_error(ctx)
+    assert err == (0, -1), f"device error word {err}"
+    print(f"[bench] {label} replays: median {np.median(dist):.1f} us, cache-flushed median "
+          f"{np.median(cold):.1f} us", file=sys.stderr, flush=True)
+
     # the sequential comparison: the same kernels as K drafting passes, one graph
     ar = None
     if with_ar:
@@ -262,6 +285,13 @@ def measure(w, steps, warmup, prm=None, dev=None, label="", with_ar=True):
         "ms_per_step": ms_step,
         "us_per_step": ms_step * 1e3,
         "event_us_per_step": ev_ms * 1e3 / steps,
+        "replay_us": {"replays": int(dist.size), "median": float(np.median(dist)),
+                      "p10": float(np.percentile(dist, 10)), "p90": float(np.percentile(dist, 90)),
+                      "timing": "HIP events around each graph replay, after the timed steps"},
+        "cache_flushed": {"replays": int(cold.size), "median_us": float(np.median(cold)),
+                          "p10_us": float(np.percentile(cold, 10)), "p90_us": float(np.percentile(cold, 90)),
+                          "value": B * K / (float(np.median(cold)) * 1e-6),
+                          "flush": "512 MiB in-place add on the stream before each replay (not timed)"},
         "eager_us_per_step": eager_ms * 1e3,
         "roofline": roof,
         "step": {"algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
@@ -516,18 +546,21 @@ def main():
         "phases_us_per_step": main_res["phases_us_per_step"],
         "event_us_per_step": main_res["event_us_per_step"],
         "eager_us_per_step": main_res["eager_us_per_step"],
+        "replay_us": main_res["replay_us"],
+        "cache_flushed": main_res["cache_flushed"],
         "autoregressive": main_res["autoregressive"],
     }
     if not args.no_c64 and w.name == "c1_20b":
         c64, _, _ = measure(configs.C64, max(20, args.steps // 4), max(5, args.warmup // 4),
                             prm=prm, dev=dev, label="c64_20b", with_ar=not args.no_ar)
-        line["c64"] = {k: c64[k] for k in ("value", "us_per_step", "roofline", "step",
-                                            "autoregressive", "phases_us_per_step", "config")}
+        line["c64"] = {k: c64[k] for k in ("value", "us_per_step", "roofline", "step", "replay_us",
+                                            "cache_flushed", "autoregressive", "phases_us_per_step", "config")}
         line["c64"]["config"]["weights"] = "same drafter weights as the c=1 workload"
     if not args.no_maxbatch and w.name == "c1_20b":
         mb, _, _ = measure(configs.MAXB, max(10, args.steps // 10), 3, prm=prm, dev=dev,
                            label="maxbatch_20b", with_ar=False)
-        line["maxbatch"] = {k: mb[k] for k in ("value", "us_per_step", "step", "phases_us_per_step", "config")}
+        line["maxbatch"] = {k: mb[k] for k in ("value", "us_per_step", "step", "phases_us_per_step", "replay_us",
+                                               "cache_flushed", "config")}
         line["maxbatch"]["config"]["weights"] = "same drafter weights as the c=1 workload"
     if not args.no_ksweep and w.name == "c1_20b":
         line["ksweep"] = ksweep(max(20, args.steps // 5), max(3, args.warmup // 4))
