@@ -290,7 +290,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
     return hipfail(e, "device query");
   }
 #ifndef PE_ATTN_SMALLQ_DIV
-#define PE_ATTN_SMALLQ_DIV 2  // fewer split-KV items when a KV head has at most two query tiles
+#define PE_ATTN_SMALLQ_DIV 2  // fewer split-KV items when a KV head has at most four query tiles
 #endif
 #ifndef PE_ATTN_ITEMS_PER_CU
 #define PE_ATTN_ITEMS_PER_CU 4
@@ -690,10 +690,10 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       a.target_items = ctx->target_items;
       a.vpr = 1;
       const int G = k.n_q_heads / k.n_kv_heads;
-      // an item with one or two 16-query tiles does little work per position,
+      // an item with at most four 16-query tiles does little work per position,
       // so its fixed cost (plan, queries, block ids, DMA ramp-up) weighs more:
       // fewer, longer items
-      if ((S * G + 15) / 16 <= 2) a.target_items = ctx->target_items / PE_ATTN_SMALLQ_DIV;
+      if ((S * G + 15) / 16 <= 4) a.target_items = ctx->target_items / PE_ATTN_SMALLQ_DIV;
       if (dt == PE_BF16 && S * G > 512) {
         // groups of attn_group consecutive slots attend as requests of their
         // own (same block table row, context up to the group's last position)
