@@ -1154,17 +1154,68 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
     }
   } else {
     static_assert(EPI == E_QKV, "split-K epilogues: store, residual, SiLU.mul, QKV");
-    const int per_row = g.N / 2;
+    // 8 RoPE pairs per thread: logical columns nb + c0 .. +7 and their
+    // partners 16 further, so q and k leave as 16-byte stores (V is d-major
+    // inside a block: one element per position row)
+    const int per_row = g.N / 16;
     for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)g.M * per_row; e += stride) {
-      const int m = int(e / per_row), pr = int(e % per_row), nb = (pr >> 4) * 32, c = pr & 15;
+      const int m = int(e / per_row), pr = int(e % per_row), nb = (pr >> 1) * 32, c0 = (pr & 1) * 8;
       const int cm = g.dedup_k ? dedup_row(m, g.dedup_k) : m;  // row of the sums (one split then)
-      float lo = 0.f, hi = 0.f;
+      float lo[8], hi[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) lo[t] = hi[t] = 0.f;
       for (int k = 0; k < KS; ++k) {
-        const float* p = g.part + k * MN + (long long)cm * g.N + nb + c;
-        lo += p[0];
-        hi += p[16];
+        const float* p = g.part + k * MN + (long long)cm * g.N + nb + c0;
+        const float4 a0 = *reinterpret_cast<const float4*>(p), a1 = *reinterpret_cast<const float4*>(p + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(p + 16), b1 = *reinterpret_cast<const float4*>(p + 20);
+        lo[0] += a0.x; lo[1] += a0.y; lo[2] += a0.z; lo[3] += a0.w;
+        lo[4] += a1.x; lo[5] += a1.y; lo[6] += a1.z; lo[7] += a1.w;
+        hi[0] += b0.x; hi[1] += b0.y; hi[2] += b0.z; hi[3] += b0.w;
+        hi[4] += b1.x; hi[5] += b1.y; hi[6] += b1.z; hi[7] += b1.w;
       }
-      epi_pair<uint16_t, E_QKV>(g, m, nb, c, lo, hi);
+      constexpr int hd = 64;  // bf16 storage implies head_dim 64 (checked at context creation)
+      if (nb < g.nq + g.nk) {
+        const bool isq = nb < g.nq;
+        const int j = isq ? nb : nb - g.nq;
+        const int head = j / hd, sb = (j % hd) >> 4;
+        const int dlo = (sb >> 1) * 16 + c0, dhi = dlo + (hd >> 1);
+        const int pos = g.positions[m];
+        float olo[8], ohi[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          float cs, sn;
+          rope_sincos(g, pos, dlo + t, cs, sn);
+          olo[t] = lo[t] * cs - hi[t] * sn;
+          ohi[t] = hi[t] * cs + lo[t] * sn;
+        }
+        const uint4 vlo = {f2bf2(olo[0], olo[1]), f2bf2(olo[2], olo[3]), f2bf2(olo[4], olo[5]), f2bf2(olo[6], olo[7])};
+        const uint4 vhi = {f2bf2(ohi[0], ohi[1]), f2bf2(ohi[2], ohi[3]), f2bf2(ohi[4], ohi[5]), f2bf2(ohi[6], ohi[7])};
+        uint16_t* dst = nullptr;
+        if (isq) {
+          dst = (uint16_t*)g.qout + ((long long)m * (g.nq / hd) + head) * hd;
+        } else {
+          const long long slot = g.slots[m];
+          if (slot >= 0 && slot < g.num_slots) dst = (uint16_t*)g.kcache + (slot * g.Hkv + head) * hd;
+        }
+        if (dst) {
+          *reinterpret_cast<uint4*>(dst + dlo) = vlo;
+          *reinterpret_cast<uint4*>(dst + dhi) = vhi;
+        }
+      } else {
+        const long long slot = g.slots[m];
+        if (slot >= 0 && slot < g.num_slots) {
+          const int j = nb - g.nq - g.nk;
+          const int head = j / hd, jb = j % hd;
+          const int bsl = __builtin_ctz(g.block_size);  // a power of two (checked at context creation)
+          const long long blk = slot >> bsl, off = slot & (g.block_size - 1);
+          uint16_t* vp = (uint16_t*)g.vcache + (((blk * g.Hkv + head) * hd) << bsl) + off;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            vp[(long long)(jb + c0 + t) << bsl] = f2bf(lo[t]);
+            vp[(long long)(jb + 16 + c0 + t) << bsl] = f2bf(hi[t]);
+          }
+        }
+      }
     }
   }
 }
@@ -1192,7 +1243,7 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
                      dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles, ntiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long work = (long long)g.M * (EPI == E_QKV ? g.N / 2 : EPI == E_SILU ? g.N / 16 : g.N / 8);
+  const long long work = (long long)g.M * (EPI == E_QKV || EPI == E_SILU ? g.N / 16 : g.N / 8);
   const long long blocks = std::min<long long>((work + 255) / 256, 8LL * num_cus);
   hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, st, gp);
   return hipGetLastError();
@@ -1204,7 +1255,7 @@ hipError_t launch_epilogue_f32(int epi, const GemmArgs& g, float* C, int num_cus
   GemmArgs gp = g;
   gp.part = C;
   gp.ksplit = 1;
-  const long long work = (long long)g.M * (epi == E_QKV ? g.N / 2 : epi == E_SILU ? g.N / 16 : g.N / 8);
+  const long long work = (long long)g.M * (epi == E_QKV || epi == E_SILU ? g.N / 16 : g.N / 8);
   const dim3 grid(unsigned(std::min<long long>((work + 255) / 256, 8LL * num_cus))), block(256);
   switch (epi) {
     case E_STORE: hipLaunchKernelGGL(splitk_reduce_kernel<E_STORE>, grid, block, 0, st, gp); break;
