@@ -709,8 +709,15 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
                "attention group lengths");
         a.seq_lens = ctx->group_lens;
       }
-      long long grid = 2LL * ctx->num_cus;  // two 512-thread workgroups fit per CU
+      // Items go to workgroups statically (item i to workgroup i mod grid, one
+      // split plan per workgroup), two 512-thread workgroups per CU.  With at
+      // least four (request, KV head) pairs per workgroup the items are mostly
+      // whole requests of varied length; then one workgroup per item lets the
+      // hardware hand them out as workgroups finish (largest graph: attention
+      // 767 -> 690 us; c=64 and the K sweep were slower that way).
+      long long grid = 2LL * ctx->num_cus;
       const long long mx = pe::attn_max_items(a.B, k.n_kv_heads, ctx->target_items);
+      if ((long long)a.B * k.n_kv_heads >= 4 * grid) grid = mx;
       a.grid = int(grid < mx ? grid : mx);
       Timed tm(ctx, PE_PH_ATTN);
       PE_HIP(pe::launch_attention(dt, a, st), "attention");
