@@ -70,6 +70,7 @@ struct pe_ctx {
   uint32_t* err = nullptr;    // [2] kinds, first request
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  int32_t* plan_off = nullptr;  // split-KV plan handed from the partial to the merge kernel
   float* sample_lse = nullptr;     // rejection sampling: log-sum-exp per logit row
   float* sample_parts = nullptr;   // rejection sampling: (max, sum exp) per row slice
   uint64_t* sample_keys = nullptr; // rejection sampling: partial draw keys
@@ -158,7 +159,7 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->rope_turns, c->lm_packed, c->splitk, c->group_lens,
+                  c->part_o, c->part_ml, c->plan_off, c->rope_turns, c->lm_packed, c->splitk, c->group_lens,
                   c->sample_lse, c->sample_keys, c->sample_parts};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
@@ -349,7 +350,8 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   }
   if (k.dtype == PE_BF16) {
     if ((s = alloc(&c->part_o, size_t(c->items_max) * QN * k.head_dim * 4, "attn partials")) != PE_OK ||
-        (s = alloc(&c->part_ml, size_t(c->items_max) * QN * 2 * 4, "attn stats")) != PE_OK) {
+        (s = alloc(&c->part_ml, size_t(c->items_max) * QN * 2 * 4, "attn stats")) != PE_OK ||
+        (s = alloc(&c->plan_off, size_t(pe::kAttnMaxB + 1) * 4, "attn plan")) != PE_OK) {
       free_ctx(c);
       return s;
     }
@@ -686,7 +688,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       a.q = ctx->q; a.kcache = k_cache[l]; a.vcache = v_cache[l];
       a.positions = P.pos; a.rej = P.rej; a.seq_lens = P.seq_lens;
       a.bt = block_table; a.out = ctx->attn;
-      a.part_o = ctx->part_o; a.part_ml = ctx->part_ml;
+      a.part_o = ctx->part_o; a.part_ml = ctx->part_ml; a.plan_off = ctx->plan_off;
       a.target_items = ctx->target_items;
       a.vpr = 1;
       const int G = k.n_q_heads / k.n_kv_heads;

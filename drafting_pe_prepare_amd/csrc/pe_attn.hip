@@ -35,7 +35,7 @@
 
 namespace pe {
 
-constexpr int kMaxB = 1024;
+constexpr int kMaxB = kAttnMaxB;
 
 // Orders this wave's LDS writes before its later LDS reads (and the reverse)
 // without a workgroup barrier.
@@ -127,6 +127,8 @@ void attn_partial_kernel(AttnArgs a) {
   __shared__ int s_bt[WIN / 16 + 2];        // block ids of the window (block_size >= 16)
   int CH;
   attn_plan(a.seq_lens, a.B, a.Hkv, a.target_items, s_off, CH);
+  if (blockIdx.x == 0)  // the merge kernel reads the plan instead of recomputing it
+    for (int r = threadIdx.x; r <= a.B; r += blockDim.x) a.plan_off[r] = s_off[r];
   const int G = a.Hq / a.Hkv, QN = a.S * G, QT = (QN + 15) >> 4;
   const int total = s_off[a.B] * a.Hkv;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
@@ -385,9 +387,7 @@ void attn_partial_kernel(AttnArgs a) {
 // chunks to find the max, then every chunk's weight is broadcast and the
 // weighted partial rows are summed with independent loads.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  __shared__ int s_off[kMaxB + 1];
-  int CH;
-  attn_plan(a.seq_lens, a.B, a.Hkv, a.target_items, s_off, CH);
+  const int32_t* s_off = a.plan_off;  // written by the partial kernel
   const int G = a.Hq / a.Hkv, QN = a.S * G;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const long long total = (long long)a.B * a.S * a.Hq;
@@ -434,9 +434,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 // two <= 16 (attn_merge_kernel serves other groupings).
 template <int G>
 __global__ __launch_bounds__(256) void attn_merge_group_kernel(AttnArgs a) {
-  __shared__ int s_off[kMaxB + 1];
-  int CH;
-  attn_plan(a.seq_lens, a.B, a.Hkv, a.target_items, s_off, CH);
+  const int32_t* s_off = a.plan_off;  // written by the partial kernel
   const int QN = a.S * G;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int hl = (l * G) >> 6, d0 = (l * G) & 63;

@@ -144,6 +144,7 @@ hipError_t launch_argmax_tokens(int M, int Kd, int parts, const uint64_t* keys, 
                                 int tstride, const int32_t* seq_lens, hipStream_t st);
 
 // ---- attention ------------------------------------------------------------
+constexpr int kAttnMaxB = 1024;  // requests (or slot groups) per attention launch
 struct AttnArgs {
   int B, S, Hq, Hkv, hd, block_size, max_blocks;
   long long num_slots;
@@ -153,6 +154,7 @@ struct AttnArgs {
   const int32_t* positions; const uint8_t* rej; const int32_t* seq_lens; const int32_t* bt;
   void* out;                      // [B*S, Hq*hd]
   float* part_o; float* part_ml;  // split-KV partials (bf16 path)
+  int32_t* plan_off;              // [B+1] first item row of each request, written by the partial kernel for the merge
   int vpr;                        // consecutive (virtual) requests per block-table row
   int target_items;               // desired work items per launch
   int grid;                       // persistent grid size
