@@ -719,6 +719,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       // 767 -> 690 us; c=64 and the K sweep were slower that way).
       long long grid = 2LL * ctx->num_cus;
       const long long mx = pe::attn_max_items(a.B, k.n_kv_heads, ctx->target_items);
+      a.slots = int(grid);
       if ((long long)a.B * k.n_kv_heads >= 4 * grid) grid = mx;
       a.grid = int(grid < mx ? grid : mx);
       Timed tm(ctx, PE_PH_ATTN);

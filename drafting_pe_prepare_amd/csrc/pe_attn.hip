@@ -30,7 +30,10 @@
 #include "pe_internal.h"
 
 #ifndef PE_ATTN_MIN_CH
-#define PE_ATTN_MIN_CH 256  // shortest split-KV chunk (positions, a multiple of 64)
+#define PE_ATTN_MIN_CH 128  // shortest split-KV chunk (positions, a multiple of 64)
+#endif
+#ifndef PE_ATTN_FILL_CH
+#define PE_ATTN_FILL_CH 512  // chunks stay at least this long while they still fill every workgroup slot
 #endif
 
 namespace pe {
@@ -44,10 +47,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Split-KV plan shared by the partial and merge kernels: total context ->
-// chunk size CH (multiple of 64, >= 256); off[r] = first chunk of request r.
-// Any blockDim that is a multiple of 64 and <= 512.
-__device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, int* off,
+// Split-KV plan: total context -> chunk size CH (a multiple of 64); off[r] =
+// first chunk of request r.  CH aims at `target` items, but is at least the
+// context per resident workgroup (`slots`) clamped to [PE_ATTN_MIN_CH,
+// PE_ATTN_FILL_CH]: an item pays a fixed cost (plan, queries, block ids, DMA
+// ramp-up), so a chunk only shrinks below PE_ATTN_FILL_CH while the workgroup
+// slots would otherwise go idle.  Any blockDim that is a multiple of 64 and
+// <= 512.
+__device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, int slots, int* off,
                           int& CH) {
   __shared__ long long s_tot[8];
   __shared__ int s_wsum[8];
@@ -62,8 +69,10 @@ __device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, i
   tot = 0;
   for (int w = 0; w < nw; ++w) tot += s_tot[w];
   long long ch = (tot * Hkv + target - 1) / (target > 0 ? target : 1);
+  long long fill = (tot * Hkv + slots - 1) / (slots > 0 ? slots : 1);
+  fill = fill < PE_ATTN_MIN_CH ? PE_ATTN_MIN_CH : (fill > PE_ATTN_FILL_CH ? PE_ATTN_FILL_CH : fill);
+  ch = ch > fill ? ch : fill;
   ch = (ch + 63) / 64 * 64;
-  if (ch < PE_ATTN_MIN_CH) ch = PE_ATTN_MIN_CH;  // fewer, longer items when the batch is small (each item pays a DMA ramp-up)
   if (ch > (1 << 30)) ch = 1 << 30;
   CH = int(ch);
   int sum = 0;
@@ -126,7 +135,7 @@ void attn_partial_kernel(AttnArgs a) {
   constexpr int WIN = 8192;                 // positions per block-id window
   __shared__ int s_bt[WIN / 16 + 2];        // block ids of the window (block_size >= 16)
   int CH;
-  attn_plan(a.seq_lens, a.B, a.Hkv, a.target_items, s_off, CH);
+  attn_plan(a.seq_lens, a.B, a.Hkv, a.target_items, a.slots, s_off, CH);
   if (blockIdx.x == 0)  // the merge kernel reads the plan instead of recomputing it
     for (int r = threadIdx.x; r <= a.B; r += blockDim.x) a.plan_off[r] = s_off[r];
   const int G = a.Hq / a.Hkv, QN = a.S * G, QT = (QN + 15) >> 4;

@@ -158,6 +158,7 @@ struct AttnArgs {
   int vpr;                        // consecutive (virtual) requests per block-table row
   int target_items;               // desired work items per launch
   int grid;                       // persistent grid size
+  int slots;                      // workgroups resident at once (2 per CU)
 };
 // ---- plain GEMMs through hipBLASLt (large batches) ---------------------------
 struct Blas;
