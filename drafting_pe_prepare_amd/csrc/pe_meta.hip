@@ -246,56 +246,66 @@ hipError_t launch_prefill_prepare(const PrefillArgs& a, hipStream_t st) {
 // row (slot j <= K copies target row r(K+1)+j) while wave 0 validates the
 // request; an invalid request gets h_shared in every slot, as its hidden-source
 // map of -1 says.  Workgroup j == 0 also writes the request's batch fields.
-// Row chunks per thread: at most PG_CHUNKS (checked on the host).
-constexpr int PG_CHUNKS = 4;
+// One workgroup per request: wave 0 prepares the request's slots while every
+// thread loads its first PG_CHUNKS 16-byte chunks of the request's 2K
+// draft-hidden rows (source row r(K+1)+j for copied slot j, h_shared for the
+// MASK slots); after the verdict the rows are stored (an invalid request's
+// copied slots take h_shared, as its -1 map says), and chunks beyond the first
+// batch are copied in a loop.  One workgroup per request rather than per slot:
+// a launch of many small workgroups is limited by how fast they are
+// dispatched (c=64: 896 slot workgroups took ~20 us).
+constexpr int PG_CHUNKS = 8;
 __global__ __launch_bounds__(1024) void prepare_gather_kernel(PrepareArgs a, int cpr,
                                                               const uint4* __restrict__ H,
                                                               const uint4* __restrict__ hs,
                                                               uint4* __restrict__ out) {
   __shared__ uint32_t s_kinds;
-  const int j = blockIdx.x, r = blockIdx.y, K = a.K;
-  const int src = j <= K ? r * (K + 1) + j : -1;
-  const uint4* from = src >= 0 ? H + (long long)src * cpr : hs;
+  const int r = blockIdx.x, K = a.K, S = 2 * K, total = S * cpr, nt = blockDim.x;
+  // chunk c of the request's rows, as its map says (returned by value: a
+  // pointer select between the two sources would put v in scratch memory)
+  auto source = [&](int c) {
+    const int j = c / cpr, k = c - j * cpr;
+    const long long row = j <= K ? (long long)(r * (K + 1) + j) * cpr : -1;
+    return row >= 0 ? H[row + k] : hs[k];
+  };
   uint4 v[PG_CHUNKS];
 #pragma unroll
-  for (int i = 0; i < PG_CHUNKS; ++i) {
-    const int c = threadIdx.x + i * blockDim.x;
-    v[i] = from[c < cpr ? c : cpr - 1];  // unconditional: the loads go out together
-  }
+  for (int i = 0; i < PG_CHUNKS; ++i) v[i] = source(min(threadIdx.x + i * nt, total - 1));
   if (threadIdx.x < 64) {
-    const uint32_t kinds = prepare_request(a, r, threadIdx.x, j == 0);
+    const uint32_t kinds = prepare_request(a, r, threadIdx.x, true);
     if (threadIdx.x == 0) s_kinds = kinds;
   }
   __syncthreads();
-  uint4* dst = out + ((long long)r * 2 * K + j) * cpr;
-  if (src >= 0 && s_kinds != 0) {
-    // an invalid request's copied slot: its -1 map entry means h_shared
-    for (int c = threadIdx.x; c < cpr; c += blockDim.x) dst[c] = hs[c];
-  } else {
-    // (two separate stores: a select between the two sources would take
-    // the address of v and put it in scratch memory)
+  uint4* dst = out + (long long)r * total;
+  const bool valid = s_kinds == 0;
 #pragma unroll
-    for (int i = 0; i < PG_CHUNKS; ++i) {
-      const int c = threadIdx.x + i * blockDim.x;
-      if (c < cpr) dst[c] = v[i];
-    }
+  for (int i = 0; i < PG_CHUNKS; ++i) {
+    const int c = threadIdx.x + i * nt;
+    if (c < total && valid) dst[c] = v[i];
+  }
+  if (valid) {
+    for (int c = threadIdx.x + PG_CHUNKS * nt; c < total; c += nt) dst[c] = source(c);
+  } else {
+    // an invalid request: every slot takes h_shared
+    for (int c = threadIdx.x; c < total; c += nt) dst[c] = hs[c % cpr];
   }
 }
 
 hipError_t launch_prepare_gather(const PrepareArgs& a, int row_bytes, const void* H,
                                  const void* h_shared, void* out, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
-  const int cpr = row_bytes / 16;
-  int threads = (cpr + PG_CHUNKS - 1) / PG_CHUNKS;
-  threads = (threads + 63) / 64 * 64;
   if (row_bytes % 16) return hipErrorInvalidValue;
-  if (threads > 1024 || a.B > 65535 || 2 * a.K > 64) {  // outside the fused shape: two launches
+  const int cpr = row_bytes / 16;
+  if (2 * a.K > 64) {  // prepare_request takes one lane per slot: two launches
     const hipError_t e = launch_prepare(a, st);
     if (e != hipSuccess) return e;
     return launch_gather(a.B * 2 * a.K, a.B * (a.K + 1), row_bytes, a.hsrc, H, h_shared, out, st);
   }
-  hipLaunchKernelGGL(prepare_gather_kernel, dim3(unsigned(2 * a.K), unsigned(a.B)), dim3(threads), 0,
-                     st, a, cpr, (const uint4*)H, (const uint4*)h_shared, (uint4*)out);
+  const long long total = 2LL * a.K * cpr;
+  long long threads = (total + PG_CHUNKS - 1) / PG_CHUNKS;
+  threads = std::min<long long>(1024, std::max<long long>(64, (threads + 63) / 64 * 64));
+  hipLaunchKernelGGL(prepare_gather_kernel, dim3(unsigned(a.B)), dim3(unsigned(threads)), 0, st, a, cpr,
+                     (const uint4*)H, (const uint4*)h_shared, (uint4*)out);
   return hipGetLastError();
 }
 
