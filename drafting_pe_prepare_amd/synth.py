@@ -118,6 +118,16 @@ def weights(w: Workload, seed: int = None) -> dict:
     return out
 
 
+def inject_weights(w: Workload, seed: int = None) -> list:
+    """Per layer (Wk_inj, Wv_inj) [Hkv*hd, d]: the projections that write
+    verifier hidden states into the drafter's KV cache."""
+    s = w.seed if seed is None else seed
+    kvd = w.n_kv_heads * w.head_dim
+    return [(normal(s, f"layer{li}.wk_inj", (kvd, w.d), w.weight_std, dtype=w.dtype),
+             normal(s, f"layer{li}.wv_inj", (kvd, w.d), w.weight_std, dtype=w.dtype))
+            for li in range(w.layers)]
+
+
 def prefix_lengths(w: Workload, seed: int) -> np.ndarray:
     kind, a, b = w.prefix
     g = np.random.Generator(np.random.PCG64(_key(seed, "prefix")))
@@ -131,10 +141,11 @@ def prefix_lengths(w: Workload, seed: int) -> np.ndarray:
     raise ValueError(kind)
 
 
-def step_inputs(w: Workload, seed: int = None, kv: bool = True) -> dict:
+def step_inputs(w: Workload, seed: int = None, kv: bool = True, extra: int = 0) -> dict:
     """One round's inputs: the previous verify batch, its outcome, the block
     tables, the target hidden states, the cached K/V pool and the target
-    tokens the next verify compares against."""
+    tokens the next verify compares against.  Block tables cover p0 + 2K +
+    extra positions per request."""
     s = w.seed if seed is None else seed
     B, K, bs = w.batch, w.K, w.block_size
     p0 = prefix_lengths(w, s)
@@ -147,7 +158,7 @@ def step_inputs(w: Workload, seed: int = None, kv: bool = True) -> dict:
     bonus = integers(s, "bonus", 0, w.vocab - 1, (B,))
     tgt = integers(s, "target_tokens", 0, w.vocab - 1, (B, K + 1))
 
-    need = (p0.astype(np.int64) + 2 * K + bs - 1) // bs
+    need = (p0.astype(np.int64) + 2 * K + extra + bs - 1) // bs
     nblocks = int(need.sum())
     max_blocks = int(need.max()) if B else 1
     g = np.random.Generator(np.random.PCG64(_key(s, "block_table")))

@@ -35,3 +35,4 @@ from .pe_oracle import (  # noqa: F401
     round_bf16, widen, prepare, prepare_prefill, gather_hidden, rmsnorm, rope, silu,
     attend, draft_forward, verify, eagle_step, ar_draft, slot_of, expected_tokens, choose_depth,
 )
+from .pe_dflash import dflash_prepare, dflash_inject, dflash_forward, apply_writes  # noqa: F401,E402
