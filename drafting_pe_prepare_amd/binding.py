@@ -24,7 +24,7 @@ DEVERR_ACCEPTED, DEVERR_TOKEN, DEVERR_BLOCK, DEVERR_LAYOUT = 1, 2, 4, 8
 EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_hidden",
            "pe_draft_forward", "pe_ar_draft", "pe_verify", "pe_prefill_prepare", "pe_prefill_gather",
            "pe_prefill_forward", "pe_draft_forward_sampled", "pe_verify_sampled", "pe_choose_depth",
-           "pe_step_graph",
+           "pe_dflash_prepare", "pe_dflash_inject", "pe_dflash_forward", "pe_step_graph",
            "pe_get_device_error",
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
@@ -104,6 +104,9 @@ def load(path: str = LIB_PATH):
     lib.pe_draft_forward_sampled.argtypes = [vp, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp),
                                              ctypes.c_float, vp, vp, vp]
     lib.pe_verify_sampled.argtypes = [vp, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    lib.pe_dflash_prepare.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, P(PeBatch), vp, vp]
+    lib.pe_dflash_inject.argtypes = [vp, i32, vp, vp, vp, P(vp), P(vp), i32, P(vp), P(vp)]
+    lib.pe_dflash_forward.argtypes = [vp, i32, P(PeBatch), vp, vp, i32, i32, P(vp), P(vp), vp, vp]
     lib.pe_choose_depth.argtypes = [P(i32), P(ctypes.c_double), i32, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, P(i32), P(ctypes.c_double)]
     lib.pe_step_graph.argtypes = [vp, i32, P(PeStepArgs)]
@@ -272,6 +275,29 @@ def pe_verify_sampled(ctx: Context, B, draft_tokens, draft_logits, target_logits
                       num_accepted, next_tokens):
     _check(_lib.pe_verify_sampled(ctx.h, B, _ptr(draft_tokens), _ptr(draft_logits), _ptr(target_logits),
                                   float(temperature), _ptr(seed), _ptr(num_accepted), _ptr(next_tokens)))
+
+
+def pe_dflash_prepare(ctx: Context, B, verify_positions, num_accepted, bonus_tokens, block_table,
+                      num_kv_blocks, batch: Batch, attn_positions, inject_slots):
+    """batch: a Batch with S = K+1; attn_positions int32 and inject_slots
+    int64 device tensors of B*(K+1) elements."""
+    _check(_lib.pe_dflash_prepare(ctx.h, B, _ptr(verify_positions), _ptr(num_accepted), _ptr(bonus_tokens),
+                                  _ptr(block_table), block_table.shape[1], num_kv_blocks, ctypes.byref(batch.c),
+                                  _ptr(attn_positions), _ptr(inject_slots)))
+
+
+def pe_dflash_inject(ctx: Context, B, verify_positions, inject_slots, target_hidden, wk_inject, wv_inject,
+                     num_kv_blocks, k_caches, v_caches):
+    _check(_lib.pe_dflash_inject(ctx.h, B, _ptr(verify_positions), _ptr(inject_slots), _ptr(target_hidden),
+                                 _ptr_array(wk_inject), _ptr_array(wv_inject), num_kv_blocks,
+                                 _ptr_array(k_caches), _ptr_array(v_caches)))
+
+
+def pe_dflash_forward(ctx: Context, B, batch: Batch, attn_positions, block_table, num_kv_blocks,
+                      k_caches, v_caches, draft_tokens, logits=None):
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    _check(_lib.pe_dflash_forward(ctx.h, B, ctypes.byref(batch.c), _ptr(attn_positions), _ptr(block_table),
+                                  block_table.shape[1], num_kv_blocks, kc, vc, _ptr(draft_tokens), _ptr(logits)))
 
 
 def pe_choose_depth(Ks, draft_us, alpha, verify_fixed_us=0.0, verify_per_token_us=0.0):

@@ -562,6 +562,10 @@ struct Pass {
   float inv_temp = 1.f;
   // the parallel-step layout (S = 2K: copied slots 0..K, MASK slots K+1..2K-1)
   bool parallel_layout = false;
+  // input x = emb(token) alone (no hidden state, no fc)
+  bool embed_input = false;
+  // when set: the position up to which each slot attends (else its own)
+  const int32_t* attn_pos = nullptr;
 };
 
 static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_table,
@@ -623,8 +627,12 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
                      Kc >= 3 && !ctx->rows_qkv.empty();
   bool dd = false;  // the first layer's fc ran deduplicated (its output is in xc)
 
-  // fc over concat(emb(token), hidden)
-  {
+  if (P.embed_input) {
+    Timed tm(ctx, PE_PH_GATHER);
+    PE_HIP(pe::launch_gather(R, k.vocab, int(d * ctx->esz), P.ids, ctx->w.embed, ctx->w.embed, ctx->x, st),
+           "embedding rows");
+  } else {
+    // fc over concat(emb(token), hidden)
     pe::GemmArgs g = g0;
     g.M = R; g.N = d; g.K = 2 * d;
     g.embed = ctx->w.embed; g.ids = P.ids; g.hid = P.hidden;
@@ -686,7 +694,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       a.block_size = k.block_size; a.max_blocks = max_blocks; a.num_slots = num_slots;
       a.scale = 1.0f / std::sqrt(float(k.head_dim));
       a.q = ctx->q; a.kcache = k_cache[l]; a.vcache = v_cache[l];
-      a.positions = P.pos; a.rej = P.rej; a.seq_lens = P.seq_lens;
+      a.positions = P.attn_pos ? P.attn_pos : P.pos; a.rej = P.rej; a.seq_lens = P.seq_lens;
       a.bt = block_table; a.out = ctx->attn;
       a.part_o = ctx->part_o; a.part_ml = ctx->part_ml; a.plan_off = ctx->plan_off;
       a.target_items = ctx->target_items;
@@ -707,7 +715,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
         a.B = B * a.vpr;
         a.S = Sv;
         Timed tg(ctx, PE_PH_ATTN);
-        PE_HIP(pe::launch_attn_group_lens(a.B, Sv, a.vpr, P.pos, P.rej, P.seq_lens, ctx->group_lens, st),
+        PE_HIP(pe::launch_attn_group_lens(a.B, Sv, a.vpr, a.positions, P.rej, P.seq_lens, ctx->group_lens, st),
                "attention group lengths");
         a.seq_lens = ctx->group_lens;
       }
@@ -798,13 +806,13 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
 static pe_status check_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const void* draft_hidden,
                                const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
                                void* const* k_cache, void* const* v_cache, int32_t* draft_tokens,
-                               float* logits) {
+                               float* logits, bool need_hidden = true) {
   pe_status s = check_B(ctx, B);
   if (s != PE_OK) return s;
   if ((s = check_batch(batch)) != PE_OK) return s;
   if (B == 0) return PE_OK;
   const pe_config& k = ctx->cfg;
-  if (!draft_hidden || !aligned(draft_hidden, 16)) return fail(PE_ERR_INVALID_ARG, "draft_hidden");
+  if (need_hidden && (!draft_hidden || !aligned(draft_hidden, 16))) return fail(PE_ERR_INVALID_ARG, "draft_hidden");
   if (!block_table || max_blocks < 1 || num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "block table");
   if (!k_cache || !v_cache) return fail(PE_ERR_INVALID_ARG, "k_cache/v_cache arrays are NULL");
   for (int l = 0; l < k.layers; ++l)
@@ -944,6 +952,89 @@ pe_status pe_prefill_forward(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* 
   P.ids = batch->input_ids; P.pos = batch->positions; P.draft_rows = batch->draft_rows;
   P.seq_lens = batch->seq_lens; P.rej = batch->is_rejected; P.slots = batch->slot_mapping;
   P.hidden = draft_hidden;
+  P.tokens = draft_tokens; P.tstride = 1;
+  P.logits = logits; P.ldl = ctx->cfg.vocab;
+  return forward_pass(ctx, P, block_table, max_blocks, num_kv_blocks, k_cache, v_cache);
+}
+
+// ---- DFlash-style round: KV injection + one bidirectional block --------------
+pe_status pe_dflash_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_positions, const int32_t* num_accepted,
+                            const int32_t* bonus_tokens, const int32_t* block_table, int32_t max_blocks,
+                            int32_t num_kv_blocks, const pe_batch* out, int32_t* attn_positions,
+                            int64_t* inject_slots) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if ((s = check_batch(out)) != PE_OK) return s;
+  if (B == 0) return PE_OK;
+  if (!verify_positions || !num_accepted || !bonus_tokens || !block_table)
+    return fail(PE_ERR_INVALID_ARG, "a prepare input is NULL");
+  if (!attn_positions || !inject_slots || !aligned(attn_positions, 4) || !aligned(inject_slots, 8))
+    return fail(PE_ERR_INVALID_ARG, "attn_positions/inject_slots NULL or misaligned");
+  if (max_blocks < 1 || num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "max_blocks/num_kv_blocks < 1");
+  if (ctx->cfg.K > 63) return fail(PE_ERR_UNSUPPORTED, "K=%d: the block needs K+1 <= 64 slots", ctx->cfg.K);
+  pe::DflashArgs a;
+  a.B = B; a.K = ctx->cfg.K;
+  a.vocab = ctx->cfg.vocab; a.mask_id = ctx->cfg.mask_id; a.block_size = ctx->cfg.block_size;
+  a.max_blocks = max_blocks; a.num_kv_blocks = num_kv_blocks;
+  a.vp = verify_positions; a.acc = num_accepted; a.bonus = bonus_tokens; a.bt = block_table;
+  a.ids = out->input_ids; a.pos = out->positions; a.apos = attn_positions; a.hsrc = out->hidden_src;
+  a.draft_rows = out->draft_rows; a.seq_lens = out->seq_lens;
+  a.rej = out->is_rejected; a.msk = out->is_masked; a.slots = out->slot_mapping; a.inj = inject_slots;
+  a.err = ctx->err;
+  Timed tm(ctx, PE_PH_PREPARE);
+  PE_HIP(pe::launch_dflash_prepare(a, ctx->stream), "dflash prepare launch");
+  return PE_OK;
+}
+
+pe_status pe_dflash_inject(pe_ctx* ctx, int32_t B, const int32_t* verify_positions, const int64_t* inject_slots,
+                           const void* target_hidden, const void* const* wk_inject, const void* const* wv_inject,
+                           int32_t num_kv_blocks, void* const* k_cache, void* const* v_cache) {
+  pe_status s = check_B(ctx, B);
+  if (s != PE_OK) return s;
+  if (B == 0) return PE_OK;
+  const pe_config& k = ctx->cfg;
+  if (!verify_positions || !inject_slots || !aligned(inject_slots, 8))
+    return fail(PE_ERR_INVALID_ARG, "verify_positions/inject_slots NULL or misaligned");
+  if (!target_hidden || !aligned(target_hidden, 16)) return fail(PE_ERR_INVALID_ARG, "target_hidden");
+  if (num_kv_blocks < 1) return fail(PE_ERR_INVALID_ARG, "num_kv_blocks < 1");
+  if (!wk_inject || !wv_inject || !k_cache || !v_cache) return fail(PE_ERR_INVALID_ARG, "a per-layer array is NULL");
+  for (int l = 0; l < k.layers; ++l)
+    if (!wk_inject[l] || !wv_inject[l] || !k_cache[l] || !v_cache[l] || !aligned(wk_inject[l], 16) ||
+        !aligned(wv_inject[l], 16) || !aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
+      return fail(PE_ERR_INVALID_ARG, "injection weights or KV cache of layer %d NULL or misaligned", l);
+  const int kvd = k.n_kv_heads * k.head_dim;
+  for (int l = 0; l < k.layers; ++l) {
+    pe::GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.M = B * (k.K + 1); g.N = 2 * kvd; g.K = k.d;
+    g.A = target_hidden; g.lda = k.d;
+    g.d = k.d; g.vocab = k.vocab;
+    g.W1 = wk_inject[l]; g.W2 = wv_inject[l]; g.nq = 0; g.nk = kvd;
+    g.positions = verify_positions; g.slots = inject_slots;
+    g.kcache = k_cache[l]; g.vcache = v_cache[l];
+    g.Hkv = k.n_kv_heads; g.hd = k.head_dim; g.block_size = k.block_size;
+    g.num_slots = (long long)num_kv_blocks * k.block_size;
+    g.rope_turns = ctx->rope_turns;
+    g.part = ctx->splitk; g.part_cap = ctx->splitk_cap;
+    Timed tm(ctx, PE_PH_QKV);
+    PE_HIP(pe::launch_gemm(k.dtype, pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, ctx->num_cus, ctx->stream), "kv injection");
+  }
+  return PE_OK;
+}
+
+pe_status pe_dflash_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const int32_t* attn_positions,
+                            const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                            void* const* k_cache, void* const* v_cache, int32_t* draft_tokens, float* logits) {
+  // the block's input is the embedding alone: no hidden states
+  pe_status s = check_forward(ctx, B, batch, nullptr, block_table, max_blocks, num_kv_blocks, k_cache, v_cache,
+                              draft_tokens, logits, false);
+  if (s != PE_OK || B == 0) return s;
+  if (!attn_positions || !aligned(attn_positions, 4)) return fail(PE_ERR_INVALID_ARG, "attn_positions");
+  Pass P;
+  P.B = B; P.S = ctx->cfg.K + 1; P.Kd = ctx->cfg.K;
+  P.ids = batch->input_ids; P.pos = batch->positions; P.draft_rows = batch->draft_rows;
+  P.seq_lens = batch->seq_lens; P.rej = batch->is_rejected; P.slots = batch->slot_mapping;
+  P.hidden = nullptr; P.embed_input = true; P.attn_pos = attn_positions;
   P.tokens = draft_tokens; P.tstride = 1;
   P.logits = logits; P.ldl = ctx->cfg.vocab;
   return forward_pass(ctx, P, block_table, max_blocks, num_kv_blocks, k_cache, v_cache);

@@ -57,6 +57,19 @@ hipError_t launch_argmax_verify(int B, int K, int parts, const uint64_t* keys, i
                                 const int32_t* seq_lens, const int32_t* target, int32_t* acc,
                                 int32_t* bonus, hipStream_t st);
 
+// DFlash-style round: the block batch (S = K+1 slots per request), each
+// slot's attention horizon (apos) and the KV slots of the injected context
+// rows [B*(K+1)] (-1: not written).
+struct DflashArgs {
+  int B, K, vocab, mask_id, block_size, max_blocks, num_kv_blocks;
+  const int32_t *vp, *acc, *bonus, *bt;
+  int32_t *ids, *pos, *apos, *hsrc, *draft_rows, *seq_lens;
+  uint8_t *rej, *msk;
+  int64_t *slots, *inj;
+  uint32_t* err;
+};
+hipError_t launch_dflash_prepare(const DflashArgs& a, hipStream_t st);
+
 // ---- autoregressive comparison --------------------------------------------
 // Pass batches of sequential drafting, built on the device from the parallel
 // batch (stride 2K) so that a captured graph replays them.

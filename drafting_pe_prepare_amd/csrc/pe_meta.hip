@@ -411,4 +411,81 @@ hipError_t launch_ar_next(const ArArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---- DFlash-style round ------------------------------------------------------
+// "vLLM Speculators: parallel drafting for speculative decoding", comparison
+// of P-EAGLE, DFlash and DSpark (DFlash: verifier hidden states are projected
+// into the drafter's KV cache; block diffusion drafts the candidates).  Per
+// request, one wave (lane = slot, K+1 <= 64): the block [bonus, MASK x K] at
+// positions p0+a+1.., every slot seeing the whole block (horizon p0+a+K+1),
+// the MASK slots as draft rows, and the KV slots the injection writes (the
+// kept context positions p0..p0+a; -1 for rejected ones).  Validation as the
+// P-EAGLE preparation; an invalid request becomes padding.
+__global__ __launch_bounds__(256) void dflash_prepare_kernel(DflashArgs a) {
+  const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= a.B) return;
+  const int K = a.K, S = K + 1, base = r * S;
+  const int32_t* vp = a.vp + (long long)r * S;
+  const int acc = a.acc[r], p0 = vp[0], bonus = a.bonus[r];
+  const int vp_l = vp[lane < K ? lane : K];
+  uint32_t kinds = 0;
+  if (acc < 0 || acc > K) kinds |= 1u;
+  else if (bonus < 0 || bonus >= a.vocab) kinds |= 2u;
+  if (__ballot(lane <= K && vp_l != p0 + lane)) kinds |= 8u;
+  if (p0 < 0 || p0 > 0x7FFFFFFF - 2 * K - 2) kinds |= 4u;
+  const int32_t* btr = a.bt + (long long)r * a.max_blocks;
+  if (kinds == 0) {
+    const int nb = (p0 + acc + K + 2 + a.block_size - 1) / a.block_size;
+    if (nb > a.max_blocks) {
+      kinds |= 4u;
+    } else {
+      bool bad = false;
+      for (int b = lane; b < nb; b += 64) {
+        const int id = btr[b];
+        bad |= id < 0 || id >= a.num_kv_blocks;
+      }
+      if (__ballot(bad)) kinds |= 4u;
+    }
+  }
+  if (kinds) {
+    if (lane < S) {
+      a.ids[base + lane] = 0;
+      a.pos[base + lane] = 0;
+      a.apos[base + lane] = 0;
+      a.hsrc[base + lane] = -1;
+      a.rej[base + lane] = 1;
+      a.msk[base + lane] = 0;
+      a.slots[base + lane] = -1;
+      a.inj[base + lane] = -1;
+    }
+    if (lane < K) a.draft_rows[r * K + lane] = base + 1 + lane;
+    if (lane == 0) {
+      a.seq_lens[r] = 0;
+      atomicOr(&a.err[0], kinds);
+      atomicMin(&a.err[1], uint32_t(r));
+    }
+    return;
+  }
+  const int bs = a.block_size;
+  if (lane < S) {
+    const int p = p0 + acc + 1 + lane, c = p0 + lane;
+    a.ids[base + lane] = lane == 0 ? bonus : a.mask_id;
+    a.pos[base + lane] = p;
+    a.apos[base + lane] = p0 + acc + K + 1;
+    a.hsrc[base + lane] = -1;
+    a.rej[base + lane] = 0;
+    a.msk[base + lane] = lane == 0 ? 0 : 1;
+    a.slots[base + lane] = (long long)btr[p / bs] * bs + p % bs;
+    a.inj[base + lane] = lane <= acc ? (long long)btr[c / bs] * bs + c % bs : -1LL;
+  }
+  if (lane < K) a.draft_rows[r * K + lane] = base + 1 + lane;
+  if (lane == 0) a.seq_lens[r] = p0 + acc + K + 2;
+}
+
+hipError_t launch_dflash_prepare(const DflashArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  if (a.K < 1 || a.K > 63) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dflash_prepare_kernel, dim3((a.B + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace pe

@@ -14,6 +14,9 @@
  * positions in one pass.
  * pe_draft_forward_sampled / pe_verify_sampled draw the drafts and verify them
  * by rejection sampling instead of greedily.
+ * pe_dflash_prepare / pe_dflash_inject / pe_dflash_forward run a DFlash-style
+ * round: verifier hidden states projected into the KV cache, then one block of
+ * MASK slots drafted in a single pass.
  *
  * Sources (page titles as published):
  *   [P1] "P-EAGLE: parallel speculative decoding in vLLM" -- sections
@@ -272,6 +275,58 @@ pe_status pe_prefill_forward(pe_ctx* ctx, int32_t B, int32_t S, const pe_batch* 
                              const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
                              void* const* k_cache, void* const* v_cache,
                              int32_t* draft_tokens, float* logits);
+
+/* ---- DFlash-style round: KV injection + one bidirectional block -------------
+ * [P2, comparison of P-EAGLE, DFlash and DSpark: DFlash projects the
+ * verifier's hidden states into the drafter's KV cache, so that the drafter's
+ * attention is conditioned on them without a longer input, and drafts the
+ * candidate tokens by block diffusion.]  The page gives no more; this library
+ * takes the following reading.  After a verify batch as for pe_prepare (K+1
+ * tokens at p0..p0+K, a accepted, the bonus token):
+ *   injection  per layer l, the verifier hidden state h_j of each kept
+ *              position p0+j (j <= a) is written to the layer's KV cache as
+ *              k = RoPE(Wk_inj[l] h_j) at p0+j and v = Wv_inj[l] h_j;
+ *   block      K+1 slots [bonus, MASK x K] at positions p0+a+1 .. p0+a+K+1,
+ *              input emb(token) alone, through the drafter's layers (fc and
+ *              h_shared are not used); every slot attends to positions
+ *              [0, p0+a+K+1] (the whole block: one denoising step);
+ *   drafts     the argmax of the LM head at MASK slot i is the draft for that
+ *              slot's own position (K drafts per request).
+ * One round is pe_dflash_prepare, pe_dflash_inject, pe_dflash_forward, in
+ * stream order. */
+
+/* Batch preparation of the block.  verify_positions [B, K+1], num_accepted,
+ * bonus_tokens [B], block_table [B, max_blocks]: as pe_prepare (device int32).
+ * out: a pe_batch with S = K+1 slots per request (input_ids, positions,
+ * hidden_src (all -1), is_rejected, is_masked, slot_mapping, draft_rows
+ * [B*K] = the MASK slots, seq_lens = p0+a+K+2); attn_positions [B*(K+1)]
+ * int32: the last position each slot attends to (p0+a+K+1); inject_slots
+ * [B*(K+1)] int64: the KV slot of verify position j of request r at
+ * r*(K+1)+j when j <= a, else -1.  The block table must cover
+ * [0, p0+a+K+2).  Checks and padding as pe_prepare (the accepted drafts'
+ * token ids are not read).  K <= 63. */
+pe_status pe_dflash_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_positions,
+                            const int32_t* num_accepted, const int32_t* bonus_tokens,
+                            const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                            const pe_batch* out, int32_t* attn_positions, int64_t* inject_slots);
+
+/* KV injection: for every layer, the target_hidden rows [B*(K+1), d]
+ * (cfg.dtype) projected by wk_inject[l], wv_inject[l] ([n_kv_heads*head_dim,
+ * d] row-major, cfg.dtype, borrowed for the call) into k_cache[l], v_cache[l]
+ * at inject_slots (from pe_dflash_prepare; rows with -1 write nothing).  K
+ * takes RoPE at verify_positions; storage and layouts as pe_draft_forward. */
+pe_status pe_dflash_inject(pe_ctx* ctx, int32_t B, const int32_t* verify_positions,
+                           const int64_t* inject_slots, const void* target_hidden,
+                           const void* const* wk_inject, const void* const* wv_inject,
+                           int32_t num_kv_blocks, void* const* k_cache, void* const* v_cache);
+
+/* One drafter pass over the block (B*(K+1) slots), as pe_draft_forward with
+ * the batch and attn_positions of pe_dflash_prepare: draft_tokens [B*K] (-1
+ * for a padded request), logits NULL or [B*K, vocab] fp32. */
+pe_status pe_dflash_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch, const int32_t* attn_positions,
+                            const int32_t* block_table, int32_t max_blocks, int32_t num_kv_blocks,
+                            void* const* k_cache, void* const* v_cache, int32_t* draft_tokens,
+                            float* logits);
 
 /* ---- Stochastic drafting and verification by rejection sampling -------------
  * [P2, Production integration: speculative decoding verifies by rejection
