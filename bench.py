@@ -47,6 +47,8 @@ def parse():
                    help="skip the stochastic drafting / rejection-sampling verification timing")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the drafting round after a 2048-position prompt")
+    p.add_argument("--no-dflash", action="store_true",
+                   help="skip the DFlash-style round (KV injection + one bidirectional block)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -418,6 +420,82 @@ def prefill(w, prm, dev, prompt, steps, warmup):
             "phases_us_per_round": phases, "timing": "eager calls, HIP events, inputs resident"}
 
 
+def dflash(w, prm, dev, steps, warmup):
+    """A DFlash-style round on workload w (same drafter weights, plus seeded
+    per-layer injection projections): pe_dflash_prepare, pe_dflash_inject
+    (verifier hidden states of the kept context positions into every layer's
+    KV cache), pe_dflash_forward (K+1 block slots [bonus, MASK x K], the K
+    MASK slots drafting); eager calls, HIP events on the library's stream,
+    inputs resident."""
+    import numpy as np
+    import torch
+    from drafting_pe_prepare_amd import binding as pb
+    from drafting_pe_prepare_amd import synth
+    B, K, d = w.batch, w.K, w.d
+    inp = synth.step_inputs(w, extra=2)
+    inj_w = synth.inject_weights(w)
+    ctx = pb.Context(w, dev, max_num_seqs=B)
+    t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+         ("verify_positions", "num_accepted", "bonus_tokens", "block_table", "target_hidden")}
+    kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+    ks, vs = [k for k, _ in kv], [v for _, v in kv]
+    wk = [pb.to_device(a) for a, _ in inj_w]
+    wv = [pb.to_device(b) for _, b in inj_w]
+    batch = pb.Batch(B, K, S=K + 1)
+    apos = torch.zeros(B * (K + 1), dtype=torch.int32, device="cuda")
+    inj = torch.zeros(B * (K + 1), dtype=torch.int64, device="cuda")
+    tok = torch.zeros(B * K, dtype=torch.int32, device="cuda")
+    nkv = int(inp["num_kv_blocks"])
+
+    def round_():
+        pb.pe_dflash_prepare(ctx, B, t["verify_positions"], t["num_accepted"], t["bonus_tokens"],
+                             t["block_table"], nkv, batch, apos, inj)
+        pb.pe_dflash_inject(ctx, B, t["verify_positions"], inj, t["target_hidden"], wk, wv, nkv, ks, vs)
+        pb.pe_dflash_forward(ctx, B, batch, apos, t["block_table"], nkv, ks, vs, tok)
+
+    for _ in range(warmup):
+        round_()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        round_()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    err = pb.pe_get_device_error(ctx)
+    assert err == (0, -1), f"device error word {err}"
+    n_prof = max(3, steps // 4)
+    pb.pe_profile_enable(ctx, True)
+    pb.pe_profile_read(ctx, reset=True)
+    for _ in range(n_prof):
+        round_()
+    prof = pb.pe_profile_read(ctx, reset=True)
+    pb.pe_profile_enable(ctx, False)
+    phases = {p: round(ms / n_prof * 1e3, 2) for p, (ms, n) in prof.items() if n}
+    print(f"[bench] dflash {w.name}: {us:.1f} us/round", file=sys.stderr, flush=True)
+    qd, kvd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    acc = inp["num_accepted"].astype(np.int64)
+    p0 = inp["prefix"].astype(np.int64)
+    ctx_len = p0 + acc + K + 2                       # attended positions per request
+    layer_w = qd * d + 2 * kvd * d + d * qd + 3 * w.mlp * d
+    rows_inj, rows = int((acc + 1).sum()), B * (K + 1)
+    flops = (w.layers * (2 * rows_inj * 2 * kvd * d + 2 * rows * layer_w
+                         + 4 * w.head_dim * w.n_q_heads * (K + 1) * int(ctx_len.sum()))
+             + 2 * B * K * w.vocab * d)
+    nbytes = 2 * (w.layers * (2 * kvd * d + layer_w) + w.vocab * d) \
+        + 2 * w.layers * 2 * kvd * int(ctx_len.sum())
+    ctx.close()
+    return {"workload": f"{w.name} DFlash-style round (B={B}, K={K}: {K + 1} block slots, {K} drafts per request)",
+            "us_per_round": us, "draft_tokens_per_s": B * K / (us * 1e-6),
+            "algorithmic_bytes": nbytes, "hbm_GBs": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_flops": flops, "mfma_TFs": flops / (us * 1e-6) / 1e12,
+            "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS,
+            "phases_us_per_round": phases, "timing": "eager calls, HIP events, inputs resident"}
+
+
 def sampling(w, prm, dev, steps, T=1.0):
     """Stochastic drafting and rejection-sampling verification on workload w:
     the parallel forward with logits written, greedy and with Gumbel draws,
@@ -569,6 +647,9 @@ def main():
                             "c64": sampling(configs.C64, prm, dev, max(5, args.steps // 20))}
     if not args.no_prefill and w.name == "c1_20b":
         line["prefill"] = prefill(w, prm, dev, 2048, max(10, args.steps // 10), 3)
+    if not args.no_dflash and w.name == "c1_20b":
+        line["dflash"] = {"c1": dflash(w, prm, dev, max(20, args.steps // 5), 3),
+                          "c64": dflash(configs.C64, prm, dev, max(10, args.steps // 10), 3)}
     if not args.no_cpu_baseline:
         del dev
         torch.cuda.empty_cache()
