@@ -138,3 +138,58 @@ def test_dflash_c1_shape_bf16():
 
 def test_dflash_c64_shape_bf16_sampled_requests():
     _check(configs.C64, seed=76, requests=[0, 29, 63])
+
+
+def test_dflash_argument_errors_and_empty_batch():
+    """Host-side checks fail before any launch; B = 0 is a no-op; a block
+    table that covers p0 + 2K positions but not the block's last two turns
+    requests with a = K into padding (device error word, kind 4)."""
+    w = SMALL_BF16.with_(K=3, batch=2, accepted="3", prefix=("fixed", 58, 0))  # p0 + 2K = 64: 4 blocks
+    _say(f"dflash errors {w.name} K={w.K} B={w.batch}")
+    st = Setup(w, 77)
+    try:
+        inp = synth.step_inputs(w, 77)                     # no room for the block's last two positions
+        inj_w = synth.inject_weights(w, 77)
+        B, K = w.batch, w.K
+        t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+             ("verify_positions", "num_accepted", "bonus_tokens", "block_table", "target_hidden")}
+        kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+        ks, vs = [k for k, _ in kv], [v for _, v in kv]
+        nkv = int(inp["num_kv_blocks"])
+        batch = pb.Batch(B, K, S=K + 1)
+        apos = torch.zeros(B * (K + 1), dtype=torch.int32, device="cuda")
+        inj = torch.zeros(B * (K + 1), dtype=torch.int64, device="cuda")
+        tok = torch.full((B * K,), -7, dtype=torch.int32, device="cuda")
+        with pytest.raises(pb.PeError):
+            pb.pe_dflash_prepare(st.ctx, B, t["verify_positions"], t["num_accepted"], t["bonus_tokens"],
+                                 t["block_table"], nkv, batch, None, inj)
+        wk = [pb.to_device(a) for a, _ in inj_w]
+        wv = [pb.to_device(b) for _, b in inj_w]
+        with pytest.raises(pb.PeError):
+            pb.pe_dflash_inject(st.ctx, B, t["verify_positions"], None, t["target_hidden"], wk, wv, nkv, ks, vs)
+        with pytest.raises(pb.PeError):
+            pb.pe_dflash_forward(st.ctx, B, batch, None, t["block_table"], nkv, ks, vs, tok)
+        with pytest.raises(pb.PeError):
+            pb.pe_dflash_forward(st.ctx, B + 1, batch, apos, t["block_table"], nkv, ks, vs, tok)  # > max_num_seqs
+        pb.pe_dflash_prepare(st.ctx, 0, t["verify_positions"], t["num_accepted"], t["bonus_tokens"],
+                             t["block_table"], nkv, batch, apos, inj)
+        pb.pe_dflash_prepare(st.ctx, B, t["verify_positions"], t["num_accepted"], t["bonus_tokens"],
+                             t["block_table"], nkv, batch, apos, inj)
+        pb.pe_dflash_inject(st.ctx, B, t["verify_positions"], inj, t["target_hidden"], wk, wv, nkv, ks, vs)
+        pb.pe_dflash_forward(st.ctx, B, batch, apos, t["block_table"], nkv, ks, vs, tok)
+        torch.cuda.synchronize()
+        ob = O.dflash_prepare(inp["verify_positions"], inp["num_accepted"], inp["bonus_tokens"],
+                              inp["block_table"], nkv, K, w.vocab, w.mask_id, w.block_size)
+        need = inp["prefix"] + 2 * K + 2
+        short = [r for r in range(B) if (need[r] + w.block_size - 1) // w.block_size > inp["block_table"].shape[1]]
+        assert pb.pe_get_device_error(st.ctx) == ((O.ERR_BLOCK, short[0]) if short else (0, -1))
+        assert_metadata_equal(batch.host(B, K), ob)
+        for r in short:
+            assert np.all(tok.cpu().numpy()[r * K:(r + 1) * K] == -1)
+        # the pool is untouched by padded requests (their slots are all -1)
+        if len(short) == B:
+            for (kc, vc), (kc0, vc0) in zip(kv, inp["kv"]):
+                np.testing.assert_array_equal(pb.to_host(kc), kc0)
+                np.testing.assert_array_equal(pb.to_host(vc), vc0)
+    finally:
+        st.close()
