@@ -426,7 +426,8 @@ def dflash(w, prm, dev, steps, warmup):
     (verifier hidden states of the kept context positions into every layer's
     KV cache), pe_dflash_forward (K+1 block slots [bonus, MASK x K], the K
     MASK slots drafting); eager calls, HIP events on the library's stream,
-    inputs resident."""
+    inputs resident; then the same round as one replayed graph (the timed
+    figure)."""
     import numpy as np
     import torch
     from drafting_pe_prepare_amd import binding as pb
@@ -463,6 +464,22 @@ def dflash(w, prm, dev, steps, warmup):
         round_()
     ev1.record(stream)
     torch.cuda.synchronize()
+    eager_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    # the same round captured once and replayed (pe_step_graph, DFlash mode;
+    # greedy verification against seeded target tokens included)
+    tt = pb.to_device(np.ascontiguousarray(inp["target_tokens"]))
+    acc_o = torch.zeros(B, dtype=torch.int32, device="cuda")
+    bon_o = torch.zeros(B, dtype=torch.int32, device="cuda")
+    args = pb.make_dflash_step_args(t["verify_positions"], t["num_accepted"], t["bonus_tokens"], t["block_table"],
+                                    nkv, batch, t["target_hidden"], ks, vs, wk, wv, apos, inj, tok, tt, acc_o, bon_o)
+    for _ in range(warmup):
+        pb.pe_step_graph(ctx, B, args)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        pb.pe_step_graph(ctx, B, args)
+    ev1.record(stream)
+    torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / steps
     err = pb.pe_get_device_error(ctx)
     assert err == (0, -1), f"device error word {err}"
@@ -474,7 +491,7 @@ def dflash(w, prm, dev, steps, warmup):
     prof = pb.pe_profile_read(ctx, reset=True)
     pb.pe_profile_enable(ctx, False)
     phases = {p: round(ms / n_prof * 1e3, 2) for p, (ms, n) in prof.items() if n}
-    print(f"[bench] dflash {w.name}: {us:.1f} us/round", file=sys.stderr, flush=True)
+    print(f"[bench] dflash {w.name}: graph {us:.1f} us/round (eager {eager_us:.1f})", file=sys.stderr, flush=True)
     qd, kvd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
     acc = inp["num_accepted"].astype(np.int64)
     p0 = inp["prefix"].astype(np.int64)
@@ -488,12 +505,14 @@ def dflash(w, prm, dev, steps, warmup):
         + 2 * w.layers * 2 * kvd * int(ctx_len.sum())
     ctx.close()
     return {"workload": f"{w.name} DFlash-style round (B={B}, K={K}: {K + 1} block slots, {K} drafts per request)",
-            "us_per_round": us, "draft_tokens_per_s": B * K / (us * 1e-6),
+            "us_per_round": us, "eager_us_per_round": eager_us, "draft_tokens_per_s": B * K / (us * 1e-6),
             "algorithmic_bytes": nbytes, "hbm_GBs": nbytes / (us * 1e-6) / 1e9,
             "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_flops": flops, "mfma_TFs": flops / (us * 1e-6) / 1e12,
             "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS,
-            "phases_us_per_round": phases, "timing": "eager calls, HIP events, inputs resident"}
+            "phases_us_per_round": phases,
+            "timing": "graph replays (prepare, injection, block pass, greedy verify), HIP events, inputs resident; "
+                      "phases from an eager pass"}
 
 
 def sampling(w, prm, dev, steps, T=1.0):

@@ -29,7 +29,7 @@ EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
           "verify", "argmax", "ar")
-STEP_PARALLEL, STEP_AUTOREGRESSIVE = 0, 1
+STEP_PARALLEL, STEP_AUTOREGRESSIVE, STEP_DFLASH = 0, 1, 2
 
 vp, i32 = ctypes.c_void_p, ctypes.c_int32
 
@@ -66,7 +66,8 @@ class PeStepArgs(ctypes.Structure):
                 ("h_shared", vp), ("draft_hidden", vp), ("k_cache", ctypes.POINTER(vp)),
                 ("v_cache", ctypes.POINTER(vp)), ("draft_tokens", vp), ("logits", vp),
                 ("target_tokens", vp), ("accepted_out", vp), ("bonus_out", vp),
-                ("mode", i32)]
+                ("mode", i32), ("wk_inject", ctypes.POINTER(vp)), ("wv_inject", ctypes.POINTER(vp)),
+                ("attn_positions", vp), ("inject_slots", vp)]
 
 
 class PeError(RuntimeError):
@@ -328,6 +329,23 @@ def make_step_args(verify_tokens, verify_positions, num_accepted, bonus_tokens, 
                    _ptr(draft_tokens), _ptr(logits), _ptr(target_tokens), _ptr(accepted_out),
                    _ptr(bonus_out), mode)
     a._keep = (kc, vc)
+    return a
+
+
+def make_dflash_step_args(verify_positions, num_accepted, bonus_tokens, block_table, num_kv_blocks,
+                          batch: Batch, target_hidden, k_caches, v_caches, wk_inject, wv_inject,
+                          attn_positions, inject_slots, draft_tokens, target_tokens, accepted_out, bonus_out,
+                          logits=None) -> PeStepArgs:
+    """Step arguments of a DFlash-style round (batch: a Batch with S = K+1)."""
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    wk, wv = _ptr_array(wk_inject), _ptr_array(wv_inject)
+    a = PeStepArgs(None, _ptr(verify_positions), _ptr(num_accepted), _ptr(bonus_tokens), _ptr(block_table),
+                   block_table.shape[1], num_kv_blocks, batch.c, _ptr(target_hidden), None, None,
+                   ctypes.cast(kc, ctypes.POINTER(vp)), ctypes.cast(vc, ctypes.POINTER(vp)),
+                   _ptr(draft_tokens), _ptr(logits), _ptr(target_tokens), _ptr(accepted_out),
+                   _ptr(bonus_out), STEP_DFLASH, ctypes.cast(wk, ctypes.POINTER(vp)),
+                   ctypes.cast(wv, ctypes.POINTER(vp)), _ptr(attn_positions), _ptr(inject_slots))
+    a._keep = (kc, vc, wk, wv)
     return a
 
 

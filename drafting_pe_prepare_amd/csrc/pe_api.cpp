@@ -1139,6 +1139,18 @@ static pe_status run_parallel_step(pe_ctx* ctx, int32_t B, const pe_step_args* a
 
 static pe_status run_step(pe_ctx* ctx, int32_t B, const pe_step_args* a) {
   if (a->mode == PE_STEP_PARALLEL) return run_parallel_step(ctx, B, a);
+  if (a->mode == PE_STEP_DFLASH) {
+    pe_status s = pe_dflash_prepare(ctx, B, a->verify_positions, a->num_accepted, a->bonus_tokens, a->block_table,
+                                    a->max_blocks, a->num_kv_blocks, &a->batch, a->attn_positions, a->inject_slots);
+    if (s != PE_OK) return s;
+    s = pe_dflash_inject(ctx, B, a->verify_positions, a->inject_slots, a->target_hidden, a->wk_inject,
+                         a->wv_inject, a->num_kv_blocks, a->k_cache, a->v_cache);
+    if (s != PE_OK) return s;
+    s = pe_dflash_forward(ctx, B, &a->batch, a->attn_positions, a->block_table, a->max_blocks, a->num_kv_blocks,
+                          a->k_cache, a->v_cache, a->draft_tokens, a->logits);
+    if (s != PE_OK) return s;
+    return pe_verify(ctx, B, a->draft_tokens, a->target_tokens, a->accepted_out, a->bonus_out);
+  }
   pe_status s = pe_prepare(ctx, B, a->verify_tokens, a->verify_positions, a->num_accepted,
                            a->bonus_tokens, a->block_table, a->max_blocks, a->num_kv_blocks, &a->batch);
   if (s != PE_OK) return s;
@@ -1154,13 +1166,20 @@ pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args) {
   pe_status s = check_B(ctx, B);
   if (s != PE_OK) return s;
   if (!args || !args->k_cache || !args->v_cache) return fail(PE_ERR_INVALID_ARG, "step args");
-  if (args->mode != PE_STEP_PARALLEL && args->mode != PE_STEP_AUTOREGRESSIVE)
+  if (args->mode != PE_STEP_PARALLEL && args->mode != PE_STEP_AUTOREGRESSIVE && args->mode != PE_STEP_DFLASH)
     return fail(PE_ERR_INVALID_ARG, "step mode %d", args->mode);
+  const bool dfl = args->mode == PE_STEP_DFLASH;
+  if (dfl && (!args->wk_inject || !args->wv_inject)) return fail(PE_ERR_INVALID_ARG, "injection weight arrays");
   const int nl = ctx->cfg.layers;
-  std::vector<void*> kv(2 * nl);
+  // the captured pointers: KV caches, and the injection weights of a DFlash round
+  std::vector<void*> kv(dfl ? 4 * nl : 2 * nl);
   for (int l = 0; l < nl; ++l) {
     kv[l] = args->k_cache[l];
     kv[nl + l] = args->v_cache[l];
+    if (dfl) {
+      kv[2 * nl + l] = const_cast<void*>(args->wk_inject[l]);
+      kv[3 * nl + l] = const_cast<void*>(args->wv_inject[l]);
+    }
   }
   const bool same = ctx->gexec && ctx->graph_B == B &&
                     std::memcmp(&ctx->graph_args, args, sizeof *args) == 0 && ctx->graph_kv == kv;

@@ -387,7 +387,7 @@ pe_status pe_choose_depth(const int32_t* Ks, const double* draft_us, int32_t n, 
                           int32_t* best_K, double* tokens_per_us);
 
 /* Drafting pass of a step graph: pe_draft_forward or pe_ar_draft. */
-typedef enum pe_step_mode { PE_STEP_PARALLEL = 0, PE_STEP_AUTOREGRESSIVE = 1 } pe_step_mode;
+typedef enum pe_step_mode { PE_STEP_PARALLEL = 0, PE_STEP_AUTOREGRESSIVE = 1, PE_STEP_DFLASH = 2 } pe_step_mode;
 
 /* All buffers of one step, for pe_step_graph. */
 typedef struct pe_step_args {
@@ -410,6 +410,13 @@ typedef struct pe_step_args {
   int32_t* accepted_out;     /* pe_verify outputs; may alias nothing above */
   int32_t* bonus_out;
   int32_t mode;              /* pe_step_mode */
+  /* PE_STEP_DFLASH only (NULL otherwise): the round is pe_dflash_prepare ->
+   * pe_dflash_inject -> pe_dflash_forward -> pe_verify; batch has S = K+1
+   * slots per request; verify_tokens, h_shared and draft_hidden are not read */
+  const void* const* wk_inject;  /* host arrays, cfg.layers entries */
+  const void* const* wv_inject;
+  int32_t* attn_positions;       /* [B*(K+1)] */
+  int64_t* inject_slots;         /* [B*(K+1)] */
 } pe_step_args;
 
 /* Captures prepare -> gather -> forward (args->mode picks the parallel pass

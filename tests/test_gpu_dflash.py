@@ -193,3 +193,81 @@ def test_dflash_argument_errors_and_empty_batch():
                 np.testing.assert_array_equal(pb.to_host(vc), vc0)
     finally:
         st.close()
+
+
+@pytest.mark.parametrize("case", ["bf16_padded", "bf16_library"])
+def test_dflash_step_graph_replays_equal_eager(case):
+    """pe_step_graph in DFlash mode (prepare -> inject -> forward -> verify):
+    four replays, with eager work and the caches reset between them, each
+    equal to the four eager entry points bit for bit (block batch, horizons,
+    injection slots, tokens, logits, verification, KV cache, error word).  The
+    library case (B=40: 320 block rows) runs the block's dense GEMMs through
+    hipBLASLt."""
+    B = 40 if case == "bf16_library" else 5
+    w = SMALL_BF16.with_(K=7, batch=B, accepted="uniform", prefix=("uniform", 40, 400))
+    _say(f"dflash graph case {case} B={B} K={w.K}")
+    st = Setup(w, 79)
+    try:
+        inp = synth.step_inputs(w, 79, extra=2)
+        inj_w = synth.inject_weights(w, 79)
+        if case == "bf16_padded":
+            inp["num_accepted"][2] = w.K + 1
+        K = w.K
+        t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+             ("verify_positions", "num_accepted", "bonus_tokens", "block_table", "target_tokens", "target_hidden")}
+        kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+        kv0 = [(k.clone(), v.clone()) for k, v in kv]
+        ks, vs = [k for k, _ in kv], [v for _, v in kv]
+        wk = [pb.to_device(a) for a, _ in inj_w]
+        wv = [pb.to_device(b) for _, b in inj_w]
+        nkv = int(inp["num_kv_blocks"])
+        batch = pb.Batch(B, K, S=K + 1)
+        apos = torch.zeros(B * (K + 1), dtype=torch.int32, device="cuda")
+        inj = torch.zeros(B * (K + 1), dtype=torch.int64, device="cuda")
+        tok = torch.zeros(B * K, dtype=torch.int32, device="cuda")
+        lg = torch.zeros((B * K, w.vocab), dtype=torch.float32, device="cuda")
+        acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+        bon = torch.zeros(B, dtype=torch.int32, device="cuda")
+        # eager
+        pb.pe_dflash_prepare(st.ctx, B, t["verify_positions"], t["num_accepted"], t["bonus_tokens"],
+                             t["block_table"], nkv, batch, apos, inj)
+        pb.pe_dflash_inject(st.ctx, B, t["verify_positions"], inj, t["target_hidden"], wk, wv, nkv, ks, vs)
+        pb.pe_dflash_forward(st.ctx, B, batch, apos, t["block_table"], nkv, ks, vs, tok, lg)
+        pb.pe_verify(st.ctx, B, tok, t["target_tokens"], acc, bon)
+        torch.cuda.synchronize()
+        eager = {"batch": batch.host(B, K), "apos": apos.cpu().numpy(), "inj": inj.cpu().numpy(),
+                 "tokens": tok.cpu().numpy(), "logits": lg.cpu().numpy(), "acc": acc.cpu().numpy(),
+                 "bon": bon.cpu().numpy(), "kv": [(pb.to_host(k), pb.to_host(v)) for k, v in kv],
+                 "error": pb.pe_get_device_error(st.ctx)}
+        args = pb.make_dflash_step_args(t["verify_positions"], t["num_accepted"], t["bonus_tokens"],
+                                        t["block_table"], nkv, batch, t["target_hidden"], ks, vs, wk, wv,
+                                        apos, inj, tok, t["target_tokens"], acc, bon, logits=lg)
+        for rep in range(4):
+            for (k, v), (k0, v0) in zip(kv, kv0):
+                k.copy_(k0)
+                v.copy_(v0)
+            tok.fill_(-5)
+            lg.fill_(0.0)
+            apos.fill_(-3)
+            inj.fill_(-3)
+            pb.pe_step_graph(st.ctx, B, args)
+            torch.cuda.synchronize()
+            _ = torch.randn(1000, device="cuda").sum().item()  # eager work between replays
+            got = batch.host(B, K)
+            for f in pb.BATCH_FIELDS:
+                np.testing.assert_array_equal(got[f], eager["batch"][f], err_msg=f"{f} replay {rep}")
+            np.testing.assert_array_equal(apos.cpu().numpy(), eager["apos"])
+            np.testing.assert_array_equal(inj.cpu().numpy(), eager["inj"])
+            np.testing.assert_array_equal(tok.cpu().numpy(), eager["tokens"], err_msg=f"replay {rep}")
+            np.testing.assert_array_equal(lg.cpu().numpy(), eager["logits"], err_msg=f"replay {rep}")
+            np.testing.assert_array_equal(acc.cpu().numpy(), eager["acc"])
+            np.testing.assert_array_equal(bon.cpu().numpy(), eager["bon"])
+            for (k, v), (ke, ve) in zip(kv, eager["kv"]):
+                np.testing.assert_array_equal(pb.to_host(k), ke)
+                np.testing.assert_array_equal(pb.to_host(v), ve)
+            assert pb.pe_get_device_error(st.ctx) == eager["error"]
+        if case == "bf16_padded":
+            assert eager["error"] == (O.ERR_ACCEPTED, 2)
+            assert np.all(eager["tokens"][2 * K:3 * K] == -1)
+    finally:
+        st.close()
