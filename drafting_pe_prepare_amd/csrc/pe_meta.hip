@@ -439,9 +439,13 @@ __global__ __launch_bounds__(256) void dflash_prepare_kernel(DflashArgs a) {
       kinds |= 4u;
     } else {
       bool bad = false;
-      for (int b = lane; b < nb; b += 64) {
-        const int id = btr[b];
-        bad |= id < 0 || id >= a.num_kv_blocks;
+      // 8 loads in flight per lane; indices past nb re-read entry nb - 1
+      for (int b0 = lane; b0 < nb; b0 += 8 * 64) {
+        int id[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) id[i] = btr[min(b0 + 64 * i, nb - 1)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bad |= id[i] < 0 || id[i] >= a.num_kv_blocks;
       }
       if (__ballot(bad)) kinds |= 4u;
     }
