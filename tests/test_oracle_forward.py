@@ -368,13 +368,51 @@ def test_argmax_lowest_index_on_ties():
         assert out["tokens"][i] == (3 if lg[3] > 0 else 0)
 
 
-def test_bf16_mode_is_close_to_f64():
+def test_bf16_mode_stores_bf16_values():
+    """In bf16 mode every stored value is a bfloat16 value: the K/V rows the
+    step writes and the residual stream after the last layer are fixed points
+    of the rounding; in f64 mode they are not (nothing is rounded)."""
     w = SMALL.with_(K=4, batch=2, accepted="uniform")
     prm, inp, b, hd = _case(w, seed=21)
-    l64 = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "f64")["logits"]
-    l16 = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], "bf16")["logits"]
-    rel = np.abs(l64 - l16).max() / np.sqrt((l64 ** 2).mean())
-    assert 1e-4 < rel < 5e-2
+    for prec, rounded in (("bf16", True), ("f64", False)):
+        out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], prec)
+        _, kr, vr = out["kv_writes"][0]
+        for a in (kr, vr, out["x_final"]):
+            same = np.array_equal(O.round_bf16(a), a)
+            assert same == rounded, prec
+
+
+@pytest.mark.parametrize("precision", ["f64", "bf16"])
+@pytest.mark.parametrize("K,layers,seed", [(3, 1, 31), (7, 1, 32), (3, 2, 33), (7, 3, 34)])
+def test_every_draft_row_is_a_token_by_token_eagle_step(precision, K, layers, seed):
+    """All K draft rows, not only t_1: the parallel pass must give, at draft
+    row m, the logits of an ordinary EAGLE drafter run position by position
+    over the request's valid slots in position order -- the a accepted drafts
+    with their target hidden states, the bonus token with the last one, then
+    K-1 pairs (emb(MASK), h_shared) ("P-EAGLE: parallel speculative decoding
+    in vLLM", Architecture and mechanism, Step 2: MTP positions 2..K take
+    the MASK embedding and the shared hidden state).  eagle_step knows
+    nothing of slots, rejected rows or the paged write-before-read order, so
+    a wrong MASK position, a MASK slot that misses an earlier MASK slot's K/V,
+    or a rejected slot that leaks into the cache fails here."""
+    w = SMALL.with_(K=K, batch=3, layers=layers, accepted="uniform")
+    prm, inp, b, hd = _case(w, seed=seed)
+    inp["num_accepted"][:3] = [0, K, min(2, K)]   # both ends and one in between
+    b = O.prepare(inp["verify_tokens"], inp["verify_positions"], inp["num_accepted"],
+                  inp["bonus_tokens"], inp["block_table"], inp["num_kv_blocks"],
+                  w.K, w.vocab, w.mask_id, w.block_size)
+    hd = O.gather_hidden(b["hidden_src"], inp["target_hidden"], prm["h_shared"])
+    out = O.draft_forward(prm, w, b, hd, inp["kv"], inp["block_table"], precision)
+    for r in range(3):
+        a = int(inp["num_accepted"][r])
+        ks, vs = _prefix_kv(w, inp, r)
+        toks = list(inp["verify_tokens"][r, 1:a + 1]) + [inp["bonus_tokens"][r]] + [w.mask_id] * (K - 1)
+        hid = np.concatenate([O.widen(inp["target_hidden"][r * (K + 1):r * (K + 1) + a + 1]),
+                              np.tile(O.widen(prm["h_shared"]), (K - 1, 1))])
+        ar = O.eagle_step(prm, w, ks, vs, toks, hid, int(inp["verify_positions"][r, 0]), precision)
+        got = out["logits"][r * K:(r + 1) * K]
+        np.testing.assert_allclose(got, ar[a:], rtol=0, atol=1e-9 * np.abs(ar).max())
+        np.testing.assert_array_equal(out["tokens"][r * K:(r + 1) * K], np.argmax(ar[a:], axis=1))
 
 
 def test_sampled_requests_equal_the_full_batch():
