@@ -25,7 +25,7 @@ EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_
            "pe_draft_forward", "pe_ar_draft", "pe_verify", "pe_prefill_prepare", "pe_prefill_gather",
            "pe_prefill_forward", "pe_draft_forward_sampled", "pe_verify_sampled", "pe_choose_depth",
            "pe_dflash_prepare", "pe_dflash_inject", "pe_dflash_forward", "pe_step_graph",
-           "pe_get_device_error",
+           "pe_step_graph_stats", "pe_get_device_error",
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
           "verify", "argmax", "ar")
@@ -67,7 +67,7 @@ class PeStepArgs(ctypes.Structure):
                 ("v_cache", ctypes.POINTER(vp)), ("draft_tokens", vp), ("logits", vp),
                 ("target_tokens", vp), ("accepted_out", vp), ("bonus_out", vp),
                 ("mode", i32), ("wk_inject", ctypes.POINTER(vp)), ("wv_inject", ctypes.POINTER(vp)),
-                ("attn_positions", vp), ("inject_slots", vp)]
+                ("attn_positions", vp), ("inject_slots", vp), ("num_active", vp)]
 
 
 class PeError(RuntimeError):
@@ -111,6 +111,7 @@ def load(path: str = LIB_PATH):
     lib.pe_choose_depth.argtypes = [P(i32), P(ctypes.c_double), i32, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, P(i32), P(ctypes.c_double)]
     lib.pe_step_graph.argtypes = [vp, i32, P(PeStepArgs)]
+    lib.pe_step_graph_stats.argtypes = [vp, P(ctypes.c_int64), P(ctypes.c_int64)]
     lib.pe_get_device_error.argtypes = [vp, P(ctypes.c_uint32), P(i32)]
     lib.pe_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.pe_profile_read.argtypes = [vp, P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int]
@@ -320,7 +321,9 @@ def pe_verify(ctx: Context, B, draft_tokens, target_tokens, num_accepted, bonus_
 def make_step_args(verify_tokens, verify_positions, num_accepted, bonus_tokens, block_table,
                    num_kv_blocks, batch: Batch, target_hidden, h_shared, draft_hidden,
                    k_caches, v_caches, draft_tokens, target_tokens, accepted_out, bonus_out,
-                   logits=None, mode=STEP_PARALLEL) -> PeStepArgs:
+                   logits=None, mode=STEP_PARALLEL, num_active=None) -> PeStepArgs:
+    """num_active: None, or a device int32 tensor of one element holding the
+    occupancy (requests at or past it are inactive padding)."""
     kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
     a = PeStepArgs(_ptr(verify_tokens), _ptr(verify_positions), _ptr(num_accepted),
                    _ptr(bonus_tokens), _ptr(block_table), block_table.shape[1], num_kv_blocks,
@@ -328,6 +331,7 @@ def make_step_args(verify_tokens, verify_positions, num_accepted, bonus_tokens, 
                    ctypes.cast(kc, ctypes.POINTER(vp)), ctypes.cast(vc, ctypes.POINTER(vp)),
                    _ptr(draft_tokens), _ptr(logits), _ptr(target_tokens), _ptr(accepted_out),
                    _ptr(bonus_out), mode)
+    a.num_active = _ptr(num_active)
     a._keep = (kc, vc)
     return a
 
@@ -335,7 +339,7 @@ def make_step_args(verify_tokens, verify_positions, num_accepted, bonus_tokens, 
 def make_dflash_step_args(verify_positions, num_accepted, bonus_tokens, block_table, num_kv_blocks,
                           batch: Batch, target_hidden, k_caches, v_caches, wk_inject, wv_inject,
                           attn_positions, inject_slots, draft_tokens, target_tokens, accepted_out, bonus_out,
-                          logits=None) -> PeStepArgs:
+                          logits=None, num_active=None) -> PeStepArgs:
     """Step arguments of a DFlash-style round (batch: a Batch with S = K+1)."""
     kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
     wk, wv = _ptr_array(wk_inject), _ptr_array(wv_inject)
@@ -344,13 +348,21 @@ def make_dflash_step_args(verify_positions, num_accepted, bonus_tokens, block_ta
                    ctypes.cast(kc, ctypes.POINTER(vp)), ctypes.cast(vc, ctypes.POINTER(vp)),
                    _ptr(draft_tokens), _ptr(logits), _ptr(target_tokens), _ptr(accepted_out),
                    _ptr(bonus_out), STEP_DFLASH, ctypes.cast(wk, ctypes.POINTER(vp)),
-                   ctypes.cast(wv, ctypes.POINTER(vp)), _ptr(attn_positions), _ptr(inject_slots))
+                   ctypes.cast(wv, ctypes.POINTER(vp)), _ptr(attn_positions), _ptr(inject_slots),
+                   _ptr(num_active))
     a._keep = (kc, vc, wk, wv)
     return a
 
 
 def pe_step_graph(ctx: Context, B, args: PeStepArgs):
     _check(_lib.pe_step_graph(ctx.h, B, ctypes.byref(args)))
+
+
+def pe_step_graph_stats(ctx: Context):
+    """(captures, replays) of pe_step_graph on this context."""
+    c, r = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.pe_step_graph_stats(ctx.h, ctypes.byref(c), ctypes.byref(r)))
+    return int(c.value), int(r.value)
 
 
 def pe_get_device_error(ctx: Context):

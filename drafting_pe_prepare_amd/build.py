@@ -3,8 +3,8 @@
     python -m drafting_pe_prepare_amd.build
 
 Every HIP source is compiled with packed-fp32 instructions disabled; the
-library links the HIP runtime and hipBLASLt (plain GEMMs of large batches).  The output lands next to this file, where
-the Python binding looks for it.
+library links the HIP runtime only (every kernel is the library's own).  The
+output lands next to this file, where the Python binding looks for it.
 """
 import os
 import shutil
@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libpe.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["pe_meta.hip", "pe_norm.hip", "pe_gemm.hip", "pe_attn.hip", "pe_sample.hip", "pe_blas.cpp",
+SOURCES = ["pe_meta.hip", "pe_norm.hip", "pe_gemm.hip", "pe_mm.hip", "pe_attn.hip", "pe_sample.hip",
            "pe_api.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -33,10 +33,10 @@ def _hipcc():
     return exe
 
 
-def _compile(src):
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+def _compile(src, flags, objdir):
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines()
             if "not a recognized feature" not in ln]
@@ -47,28 +47,20 @@ def _compile(src):
 
 def build(verbose: bool = True, out: str = None, objdir: str = None, defines=()) -> str:
     """Compile every source and link libpe.so (or `out`).  `defines` are
-    extra -D macros for experimental variants."""
-    global OBJDIR, FLAGS
+    extra -D macros for experimental variants.  Holds no global state, so
+    several builds (with their own `out` and `objdir`) may run at once."""
     out = out or OUT
-    saved = (OBJDIR, FLAGS)
-    OBJDIR = objdir or OBJDIR
-    FLAGS = FLAGS + [f"-D{d}" for d in defines]
-    try:
-        return _build(verbose, out)
-    finally:
-        OBJDIR, FLAGS = saved
-
-
-def _build(verbose, out):
-    os.makedirs(OBJDIR, exist_ok=True)
+    objdir = objdir or OBJDIR
+    flags = FLAGS + [f"-D{d}" for d in defines]
+    os.makedirs(objdir, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, flags, objdir), SOURCES))
     for obj, msgs in results:
         if verbose and msgs:
             print("\n".join(msgs), file=sys.stderr)
     tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results] + \
-          ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+          ["-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -18,9 +18,6 @@
 #include "pe.h"
 #include "pe_internal.h"
 
-#ifndef PE_BLAS_MIN_ROWS
-#define PE_BLAS_MIN_ROWS 256  // batches this large run their plain GEMMs through hipBLASLt
-#endif
 
 namespace {
 
@@ -77,14 +74,7 @@ struct pe_ctx {
   int32_t* group_lens = nullptr; // attention context length per slot group (bf16)
   int attn_group = 64;           // slots per attention workgroup: 512 / G rounded down to a power of two
   int groups_max = 0;            // slot groups the attention buffers are sized for
-  // plain GEMMs of large batches through hipBLASLt (bf16 storage): row-major
-  // copies of the weights in logical column order (qkv and gate/up per layer),
-  // the fc A operand and the fp32 result the fused epilogue kernel reads
-  pe::Blas* blas = nullptr;
-  void* fc_a = nullptr;
-  void* xc = nullptr;  // [R, d] first-layer fc output on the MASK-deduplicated rows
-  float* blas_c = nullptr;
-  std::vector<void*> rows_qkv, rows_gu;
+  void* xc = nullptr;  // [B(K+2), d] first-layer fc output on the MASK-deduplicated rows (bf16)
   float* splitk = nullptr;      // split-K GEMM partials (bf16 storage)
   long long splitk_cap = 0;     // floats
   double* rope_turns = nullptr;  // RoPE frequencies in turns per position
@@ -101,6 +91,8 @@ struct pe_ctx {
   int target_items = 1024;
   long long items_max = 0;
   // step graph
+  const int32_t* nact = nullptr;  // occupancy of the step being captured (NULL: every request active)
+  int64_t graph_captures = 0, graph_replays = 0;
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
   hipStream_t capture_stream = nullptr;  // private: the default stream cannot be captured
@@ -169,14 +161,7 @@ void free_ctx(pe_ctx* c) {
     if (p) (void)hipFree(p);
   for (void* p : c->layer_packed)
     if (p) (void)hipFree(p);
-  for (void* p : c->rows_qkv)
-    if (p) (void)hipFree(p);
-  for (void* p : c->rows_gu)
-    if (p) (void)hipFree(p);
-  if (c->fc_a) (void)hipFree(c->fc_a);
-  if (c->blas_c) (void)hipFree(c->blas_c);
   if (c->xc) (void)hipFree(c->xc);
-  pe::blas_destroy(c->blas);
   delete c;
 }
 
@@ -360,11 +345,11 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       return s;
     }
     // split-K partials: GEMMs whose output tiles are too few to fill the chip
-    // sum k-ranges into here first (32 MB bounds the split factor), and the
-    // k-split tail of the LM head writes its partial tiles here (up to one
-    // round of 256 x 256 tiles: 64 MB)
-    c->splitk_cap = std::min<long long>(8LL << 20, (long long)R * std::max(2 * k.mlp, 4 * k.d) * 8);
-    c->splitk_cap = std::max<long long>(c->splitk_cap, std::min<long long>(16LL << 20, (long long)D * k.vocab * 8));
+    // sum k-ranges into here first, the k-split tail of a small-batch LM head
+    // writes its partial tiles here, and at large batch the QKV product's
+    // RoPE + KV-write epilogue runs on its fp32 sums here (64 MB, or those
+    // sums over every row when larger)
+    c->splitk_cap = std::max<long long>(16LL << 20, (long long)R * (qd + 2 * k.n_kv_heads * k.head_dim));
     if ((s = alloc(&c->splitk, size_t(c->splitk_cap) * 4, "split-K partials")) != PE_OK) {
       free_ctx(c);
       return s;
@@ -413,31 +398,9 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       free_ctx(c);
       return s;
     }
-    // batches of PE_BLAS_MIN_ROWS rows and more run their plain GEMMs through
-    // hipBLASLt (without it, or for shapes it declines, the tiled kernels run)
-    if (R >= size_t(PE_BLAS_MIN_ROWS) && (c->blas = pe::blas_create(size_t(32) << 20)) != nullptr) {
-      const size_t maxN = std::max({size_t(k.d), size_t(qd + 2 * kvd), size_t(2 * k.mlp)});
-      s = alloc(&c->fc_a, R * 2 * k.d * 2, "fc operand rows");
-      if (s == PE_OK) s = alloc(&c->xc, R * k.d * 2, "deduplicated fc rows");
-      if (s == PE_OK) s = alloc(&c->blas_c, R * maxN * 4, "GEMM result");
-      c->rows_qkv.assign(k.layers, nullptr);
-      c->rows_gu.assign(k.layers, nullptr);
-      for (int l = 0; l < k.layers && s == PE_OK; ++l) {
-        const pe_layer_weights& L = c->layers[l];
-        pe::GemmArgs pr;
-        std::memset(&pr, 0, sizeof pr);
-        pr.hd = k.head_dim;
-        pr.W0 = L.wq; pr.W1 = L.wk; pr.W2 = L.wv; pr.N = qd + 2 * kvd; pr.K = k.d; pr.nq = qd; pr.nk = kvd;
-        s = alloc(&c->rows_qkv[l], size_t(pr.N) * k.d * 2, "qkv rows");
-        if (s == PE_OK && (e = pe::launch_pack_rows(pe::B_QKV, pr, c->rows_qkv[l], c->stream)) != hipSuccess)
-          s = hipfail(e, "qkv rows");
-        pr.W0 = L.w_gate; pr.W1 = L.w_up; pr.W2 = nullptr; pr.N = 2 * k.mlp; pr.nq = pr.nk = 0;
-        if (s == PE_OK) s = alloc(&c->rows_gu[l], size_t(pr.N) * k.d * 2, "gate/up rows");
-        if (s == PE_OK && (e = pe::launch_pack_rows(pe::B_GATEUP, pr, c->rows_gu[l], c->stream)) != hipSuccess)
-          s = hipfail(e, "gate/up rows");
-      }
-      if (s == PE_OK && (e = hipStreamSynchronize(c->stream)) != hipSuccess) s = hipfail(e, "rows sync");
-      if (s != PE_OK) {
+    // the MASK-deduplicated first-layer fc rows of a parallel step (large batches)
+    if (size_t(k.max_num_seqs) * (k.K + 2) > 64 && k.K >= 3) {
+      if ((s = alloc(&c->xc, size_t(k.max_num_seqs) * (k.K + 2) * k.d * 2, "deduplicated fc rows")) != PE_OK) {
         free_ctx(c);
         return s;
       }
@@ -496,6 +459,7 @@ static pe_status prepare_args(pe_ctx* ctx, int32_t B, const int32_t* verify_toke
   a.msk = out->is_masked;
   a.slots = out->slot_mapping;
   a.err = ctx->err;
+  a.nact = ctx->nact;
   return PE_OK;
 }
 
@@ -588,29 +552,11 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   g0.num_slots = num_slots;
   g0.part = ctx->splitk;
   g0.part_cap = ctx->splitk_cap;
+  g0.nact = ctx->nact;
+  g0.rpr = S;
 
-  // a dense GEMM with its fused epilogue: hipBLASLt + the epilogue kernel for
-  // large batches (w_rows: the weight in logical row order), else the tiled or
-  // skinny kernels
-  auto dense = [&](int aload, int bmap, int epi, const pe::GemmArgs& g, const void* w_rows,
-                   const char* what) -> pe_status {
-    if (dt == PE_BF16 && ctx->blas && g.M >= PE_BLAS_MIN_ROWS && w_rows) {
-      const void* A = g.A;
-      if (aload == pe::A_FC) {
-        PE_HIP(pe::launch_fc_rows(g, ctx->fc_a, st), what);
-        A = ctx->fc_a;
-      }
-      if (epi == pe::E_STORE || epi == pe::E_RESID) {
-        // store / residual: the library rounds its fp32 sums (plus the
-        // residual) to bf16 once, as the fused epilogue does
-        if (g.ldo == g.N &&
-            pe::blas_gemm_bf16(ctx->blas, g.M, g.N, g.K, A, w_rows, epi == pe::E_RESID ? g.resid : nullptr, g.out, st))
-          return PE_OK;
-      } else if (pe::blas_gemm(ctx->blas, g.M, g.N, g.K, A, w_rows, ctx->blas_c, st)) {
-        PE_HIP(pe::launch_epilogue_f32(epi, g, ctx->blas_c, ctx->num_cus, st), what);
-        return PE_OK;
-      }
-    }
+  // a dense GEMM with its fused epilogue
+  auto dense = [&](int aload, int bmap, int epi, const pe::GemmArgs& g, const char* what) -> pe_status {
     PE_HIP(pe::launch_gemm(dt, aload, bmap, epi, g, ctx->num_cus, st), what);
     return PE_OK;
   };
@@ -619,13 +565,11 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   // MASK-slot deduplication of the first layer.  In the parallel-step layout
   // the K-1 MASK slots of a request all carry emb(MASK) and h_shared, so the
   // first layer's fc, norm and (pre-RoPE) QKV rows of those slots are equal:
-  // with library GEMMs they run on K+2 rows per request (copied slots and one
-  // MASK slot), the norm writes the fc rows out to every slot, and the QKV
+  // at large batch fc and QKV run on K+2 rows per request (copied slots and
+  // one MASK slot), the norm writes the fc rows out to every slot, and the QKV
   // epilogue (RoPE at each slot's own position, KV write) runs for every slot.
   const int Kc = k.K, Rc = B * (Kc + 2);
-  const bool dedup = P.parallel_layout && dt == PE_BF16 && ctx->blas && ctx->xc && R >= PE_BLAS_MIN_ROWS &&
-                     Kc >= 3 && !ctx->rows_qkv.empty();
-  bool dd = false;  // the first layer's fc ran deduplicated (its output is in xc)
+  const bool dd = P.parallel_layout && dt == PE_BF16 && ctx->xc && Kc >= 3 && Rc > 64;
 
   if (P.embed_input) {
     Timed tm(ctx, PE_PH_GATHER);
@@ -639,14 +583,13 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     g.W0 = ctx->w.w_fc; g.Wp = ctx->fc_packed;
     g.out = ctx->x; g.ldo = d;
     Timed tm(ctx, PE_PH_FC);
-    if (dedup) {
-      pe::GemmArgs gc = g;
-      gc.M = Rc;
-      gc.dedup_k = Kc;
-      PE_HIP(pe::launch_fc_rows(gc, ctx->fc_a, st), "fc rows");
-      dd = pe::blas_gemm_bf16(ctx->blas, Rc, d, 2 * d, ctx->fc_a, ctx->w.w_fc, nullptr, ctx->xc, st);
+    if (dd) {
+      g.M = Rc;
+      g.rpr = Kc + 2;
+      g.dedup_k = Kc;
+      g.out = ctx->xc;
     }
-    if (!dd && (ds = dense(pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, ctx->w.w_fc, "fc")) != PE_OK) return ds;
+    if ((ds = dense(pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, "fc")) != PE_OK) return ds;
   }
   for (int l = 0; l < k.layers; ++l) {
     const pe_layer_weights& L = ctx->layers[l];
@@ -669,23 +612,13 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
       g.rope_turns = ctx->rope_turns;
       Timed tm(ctx, PE_PH_QKV);
-      bool done = false;
       if (first_dd) {
-        // compact rows through the library; the epilogue covers every slot
-        if (pe::blas_gemm(ctx->blas, Rc, g.N, g.K, ctx->u, ctx->rows_qkv[0], ctx->blas_c, st)) {
-          pe::GemmArgs ge = g;
-          ge.dedup_k = Kc;
-          PE_HIP(pe::launch_epilogue_f32(pe::E_QKV, ge, ctx->blas_c, ctx->num_cus, st), "qkv");
-          done = true;
-        } else {
-          // no library plan for the compact shape: normalise every slot
-          PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.attn_norm, ctx->u, nullptr, R, k.rms_eps, st),
-                 "attn norm");
-        }
+        // compact rows; the epilogue covers every slot
+        g.M = Rc;
+        g.rpr = Kc + 2;
+        g.dedup_k = Kc;
       }
-      if (!done && (ds = dense(pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g,
-                               ctx->rows_qkv.empty() ? nullptr : ctx->rows_qkv[l], "qkv")) != PE_OK)
-        return ds;
+      if ((ds = dense(pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, "qkv")) != PE_OK) return ds;
     }
     {
       pe::AttnArgs a;
@@ -740,7 +673,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.wo; g.Wp = packed(ctx, l, 1);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       Timed tm(ctx, PE_PH_O);
-      if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, L.wo, "o proj")) != PE_OK) return ds;
+      if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "o proj")) != PE_OK) return ds;
     }
     {
       Timed tm(ctx, PE_PH_NORM);
@@ -753,9 +686,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.w_gate; g.W1 = L.w_up; g.Wp = packed(ctx, l, 2);
       g.out = ctx->mlp; g.ldo = k.mlp;
       Timed tm(ctx, PE_PH_GATEUP);
-      if ((ds = dense(pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, ctx->rows_gu.empty() ? nullptr : ctx->rows_gu[l],
-                      "gate/up")) != PE_OK)
-        return ds;
+      if ((ds = dense(pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, "gate/up")) != PE_OK) return ds;
     }
     {
       pe::GemmArgs g = g0;
@@ -764,7 +695,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.w_down; g.Wp = packed(ctx, l, 3);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       Timed tm(ctx, PE_PH_DOWN);
-      if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, L.w_down, "down")) != PE_OK) return ds;
+      if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "down")) != PE_OK) return ds;
     }
   }
   {
@@ -780,6 +711,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     g.W0 = ctx->w.lm_head;
     g.Wp = ctx->lm_packed;
     g.keys = ctx->keys; g.logits = P.logits; g.ldl = P.ldl;
+    g.rpr = P.Kd;
     g.parts = pe::gemm_argmax_parts(dt, D, k.vocab, d, ctx->num_cus);
     g.seq_lens = P.seq_lens; g.Kd = P.Kd;
     {
@@ -793,7 +725,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
              "draft sampling");
     else if (P.vtarget)
       PE_HIP(pe::launch_argmax_verify(B, P.Kd, g.parts, ctx->keys, P.tokens, P.seq_lens, P.vtarget,
-                                      P.vacc, P.vbonus, st),
+                                      P.vacc, P.vbonus, ctx->nact, st),
              "argmax + verify");
     else
       PE_HIP(pe::launch_argmax_tokens(D, P.Kd, g.parts, ctx->keys, P.tokens, P.tstride, P.seq_lens, st),
@@ -981,6 +913,7 @@ pe_status pe_dflash_prepare(pe_ctx* ctx, int32_t B, const int32_t* verify_positi
   a.draft_rows = out->draft_rows; a.seq_lens = out->seq_lens;
   a.rej = out->is_rejected; a.msk = out->is_masked; a.slots = out->slot_mapping; a.inj = inject_slots;
   a.err = ctx->err;
+  a.nact = ctx->nact;
   Timed tm(ctx, PE_PH_PREPARE);
   PE_HIP(pe::launch_dflash_prepare(a, ctx->stream), "dflash prepare launch");
   return PE_OK;
@@ -1096,7 +1029,7 @@ pe_status pe_verify(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens, const i
   if (!draft_tokens || !target_tokens || !num_accepted || !bonus_tokens)
     return fail(PE_ERR_INVALID_ARG, "a verify buffer is NULL");
   Timed tm(ctx, PE_PH_VERIFY);
-  PE_HIP(pe::launch_verify(B, ctx->cfg.K, draft_tokens, target_tokens, num_accepted, bonus_tokens,
+  PE_HIP(pe::launch_verify(B, ctx->cfg.K, draft_tokens, target_tokens, num_accepted, bonus_tokens, ctx->nact,
                            ctx->stream),
          "verify launch");
   return PE_OK;
@@ -1184,17 +1117,25 @@ pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args) {
   const bool same = ctx->gexec && ctx->graph_B == B &&
                     std::memcmp(&ctx->graph_args, args, sizeof *args) == 0 && ctx->graph_kv == kv;
   if (!same) {
-    if (ctx->gexec) { (void)hipGraphExecDestroy(ctx->gexec); ctx->gexec = nullptr; }
+    if (ctx->gexec) {
+      // the graph being replaced may still run on the context's stream
+      PE_HIP(hipStreamSynchronize(ctx->stream), "sync before recapture");
+      (void)hipGraphExecDestroy(ctx->gexec);
+      ctx->gexec = nullptr;
+    }
     if (ctx->graph) { (void)hipGraphDestroy(ctx->graph); ctx->graph = nullptr; }
     if (!ctx->capture_stream)
       PE_HIP(hipStreamCreateWithFlags(&ctx->capture_stream, hipStreamNonBlocking), "capture stream");
-    // work queued on ctx->stream before this call must not be reordered with the graph
-    PE_HIP(hipStreamSynchronize(ctx->stream), "sync before capture");
+    // capture records launches without running them, so the work already
+    // queued on the context's stream needs no wait: the graph's launches are
+    // enqueued behind it
     PE_HIP(hipStreamBeginCapture(ctx->capture_stream, hipStreamCaptureModeRelaxed), "begin capture");
     hipStream_t user = ctx->stream;
     ctx->stream = ctx->capture_stream;
     ctx->capturing = true;
+    ctx->nact = args->num_active;
     s = run_step(ctx, B, args);
+    ctx->nact = nullptr;
     ctx->capturing = false;
     ctx->stream = user;
     hipGraph_t graph = nullptr;
@@ -1209,8 +1150,17 @@ pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args) {
     ctx->graph_B = B;
     ctx->graph_args = *args;
     ctx->graph_kv = kv;
+    ++ctx->graph_captures;
   }
   PE_HIP(hipGraphLaunch(ctx->gexec, ctx->stream), "graph launch");
+  ++ctx->graph_replays;
+  return PE_OK;
+}
+
+pe_status pe_step_graph_stats(pe_ctx* ctx, int64_t* captures, int64_t* replays) {
+  if (!ctx || !captures || !replays) return fail(PE_ERR_INVALID_ARG, "NULL argument");
+  *captures = ctx->graph_captures;
+  *replays = ctx->graph_replays;
   return PE_OK;
 }
 

@@ -99,6 +99,16 @@ __device__ __forceinline__ float word_uniform(uint32_t x) {
 // Gumbel noise -log(-log U); -log U as -log1p(U - 1) (U - 1 is exact).
 __device__ __forceinline__ float gumbel_noise(float u) { return -logf(-log1pf(u - 1.0f)); }
 
+// s_waitcnt vmcnt(N) only: at most N vector-memory operations of this wave in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// lgkmcnt(0) only: every LDS read issued so far has returned
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;

@@ -246,9 +246,20 @@ __global__ __launch_bounds__(1024) void argmax_verify_kernel(int K, int parts,
                                                              const int32_t* __restrict__ seq_lens,
                                                              const int32_t* __restrict__ target,
                                                              int32_t* __restrict__ acc,
-                                                             int32_t* __restrict__ bonus) {
+                                                             int32_t* __restrict__ bonus,
+                                                             const int32_t* __restrict__ nact) {
   __shared__ int32_t s_tok[64];
   const int r = blockIdx.x, w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
+  if (nact && r >= nact[0]) {  // an inactive request: no keys were written for its rows
+    if (w == 0) {
+      if (l < K) tokens[(long long)r * K + l] = -1;
+      if (l == 0) {
+        acc[r] = 0;
+        bonus[r] = 0;  // PE_PAD_TOKEN
+      }
+    }
+    return;
+  }
   const bool padded = seq_lens[r] == 0;
   for (int i = w; i < K; i += nw) {
     const long long row = (long long)r * K + i;
@@ -546,14 +557,6 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz64(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt_hi[15:14]
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-// lgkmcnt(0) only: every LDS read issued so far has returned
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -959,9 +962,11 @@ static Variant pick(int epi, int M, int N, int K, int num_cus) {
   return tiles > num_cus ? V_D128S2 : V_D64;
 }
 constexpr int kArgmaxBN = 256;  // columns per tile of every tiled LM-head variant
+constexpr int kMmMinRows = 64;  // larger products run on the 32x32 tiles of pe_mm.hip
 
 int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus) {
   if (dtype != 1) return (N + 31) / 32;
+  if (M > kMmMinRows) return mm_argmax_parts(M, N);
   switch (pick(E_ARGMAX, M, N, K, num_cus)) {
     case V_WIDE: return std::min(num_cus, N / 16);
     case V_SKINNY: return (N + 15) / 16;
@@ -1249,69 +1254,10 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_epilogue_f32(int epi, const GemmArgs& g, float* C, int num_cus, hipStream_t st) {
-  if (g.M <= 0) return hipSuccess;
-  if (g.N % 32) return hipErrorInvalidValue;
-  GemmArgs gp = g;
-  gp.part = C;
-  gp.ksplit = 1;
-  const long long work = (long long)g.M * (epi == E_QKV || epi == E_SILU ? g.N / 16 : g.N / 8);
-  const dim3 grid(unsigned(std::min<long long>((work + 255) / 256, 8LL * num_cus))), block(256);
-  switch (epi) {
-    case E_STORE: hipLaunchKernelGGL(splitk_reduce_kernel<E_STORE>, grid, block, 0, st, gp); break;
-    case E_RESID: hipLaunchKernelGGL(splitk_reduce_kernel<E_RESID>, grid, block, 0, st, gp); break;
-    case E_SILU: hipLaunchKernelGGL(splitk_reduce_kernel<E_SILU>, grid, block, 0, st, gp); break;
-    case E_QKV: hipLaunchKernelGGL(splitk_reduce_kernel<E_QKV>, grid, block, 0, st, gp); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-// Row-major copy of the logical weight rows: out[n][k] = weight_row(n)[k].
-template <int BMAP>
-__global__ __launch_bounds__(256) void pack_rows_kernel(GemmArgs g, uint4* __restrict__ out) {
-  const int cpr = g.K >> 3;
-  const long long total = (long long)g.N * cpr;
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
-       i += (long long)gridDim.x * blockDim.x) {
-    const int n = int(i / cpr), c = int(i - (long long)n * cpr);
-    out[i] = ld16(weight_row<uint16_t, BMAP>(g, n) + c * 8);
-  }
-}
-
-hipError_t launch_pack_rows(int bmap, const GemmArgs& g, void* out, hipStream_t st) {
-  const long long total = (long long)g.N * (g.K / 8);
-  const unsigned blocks = unsigned(std::min<long long>((total + 255) / 256, 8192));
-  if (bmap == B_QKV) hipLaunchKernelGGL(pack_rows_kernel<B_QKV>, dim3(blocks), dim3(256), 0, st, g, (uint4*)out);
-  else if (bmap == B_GATEUP) hipLaunchKernelGGL(pack_rows_kernel<B_GATEUP>, dim3(blocks), dim3(256), 0, st, g, (uint4*)out);
-  else hipLaunchKernelGGL(pack_rows_kernel<B_PLAIN>, dim3(blocks), dim3(256), 0, st, g, (uint4*)out);
-  return hipGetLastError();
-}
-
-// fc A operand rows: [emb(ids[m]) ; hid[m]], 16 bytes per thread
-__global__ __launch_bounds__(256) void fc_rows_kernel(GemmArgs g, uint4* __restrict__ out) {
-  const int cpr = (2 * g.d) >> 3;
-  const long long total = (long long)g.M * cpr;
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
-       i += (long long)gridDim.x * blockDim.x) {
-    const int m = int(i / cpr), c = int(i - (long long)m * cpr);
-    const int K = g.dedup_k;
-    const int slot = K ? (m / (K + 2)) * (2 * K) + m % (K + 2) : m;
-    ARow<uint16_t, A_FC> ar;
-    ar.init(g, slot);
-    out[i] = ld16(ar.at(c * 8, g.d));
-  }
-}
-
-hipError_t launch_fc_rows(const GemmArgs& g, void* out, hipStream_t st) {
-  const long long total = (long long)g.M * (2 * g.d / 8);
-  const unsigned blocks = unsigned(std::min<long long>((total + 255) / 256, 8192));
-  hipLaunchKernelGGL(fc_rows_kernel, dim3(blocks), dim3(256), 0, st, g, (uint4*)out);
-  return hipGetLastError();
-}
-
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
+  if (g.M > kMmMinRows) return launch_mm(AL, BMAP, EPI, g, num_cus, st);
+  if (g.dedup_k) return hipErrorInvalidValue;  // compact first-layer rows: large batches only
   const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);
   if constexpr (EPI == E_ARGMAX) {
     switch (v) {
@@ -1358,12 +1304,12 @@ hipError_t launch_argmax_tokens(int M, int Kd, int parts, const uint64_t* keys, 
 
 hipError_t launch_argmax_verify(int B, int K, int parts, const uint64_t* keys, int32_t* tokens,
                                 const int32_t* seq_lens, const int32_t* target, int32_t* acc,
-                                int32_t* bonus, hipStream_t st) {
+                                int32_t* bonus, const int32_t* nact, hipStream_t st) {
   if (B <= 0) return hipSuccess;
   if (K < 1 || K > 64) return hipErrorInvalidValue;
   const int waves = K < 16 ? K : 16;
   hipLaunchKernelGGL(argmax_verify_kernel, dim3(unsigned(B)), dim3(64 * waves), 0, st, K, parts, keys,
-                     tokens, seq_lens, target, acc, bonus);
+                     tokens, seq_lens, target, acc, bonus, nact);
   return hipGetLastError();
 }
 

@@ -14,14 +14,16 @@ struct PrepareArgs {
   uint8_t *rej, *msk;
   int64_t* slots;
   uint32_t* err;  // [0] kinds (OR), [1] first failing request (min)
+  const int32_t* nact = nullptr;  // occupancy: requests >= *nact are inactive padding (NULL: all active)
 };
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t st);
 
 hipError_t launch_gather(int rows, int nsrc, int row_bytes, const int32_t* hsrc, const void* H,
                          const void* h_shared, void* out, hipStream_t st);
 
+// nact: occupancy (NULL: all active); an inactive request gets accepted 0, bonus 0
 hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32_t* acc,
-                         int32_t* bonus, hipStream_t st);
+                         int32_t* bonus, const int32_t* nact, hipStream_t st);
 
 // Drafting round after a prompt: one workgroup per request.
 struct PrefillArgs {
@@ -55,7 +57,7 @@ hipError_t launch_prepare_gather(const PrepareArgs& a, int row_bytes, const void
                                  const void* h_shared, void* out, hipStream_t st);
 hipError_t launch_argmax_verify(int B, int K, int parts, const uint64_t* keys, int32_t* tokens,
                                 const int32_t* seq_lens, const int32_t* target, int32_t* acc,
-                                int32_t* bonus, hipStream_t st);
+                                int32_t* bonus, const int32_t* nact, hipStream_t st);
 
 // DFlash-style round: the block batch (S = K+1 slots per request), each
 // slot's attention horizon (apos) and the KV slots of the injected context
@@ -67,6 +69,7 @@ struct DflashArgs {
   uint8_t *rej, *msk;
   int64_t *slots, *inj;
   uint32_t* err;
+  const int32_t* nact = nullptr;  // occupancy, as PrepareArgs::nact
 };
 hipError_t launch_dflash_prepare(const DflashArgs& a, hipStream_t st);
 
@@ -133,11 +136,21 @@ struct GemmArgs {
   // MASK-slot deduplication in the parallel-step layout (K = dedup_k > 0):
   // the K-1 MASK slots of a request share one input row, so the first layer's
   // fc and QKV products run on K+2 rows per request (copied slots 0..K and
-  // one MASK slot).  launch_fc_rows: compact row m gathers slot
+  // one MASK slot).  fc (A_FC): compact row m reads slot
   // (m / (K+2)) * 2K + m % (K+2).  E_QKV epilogue over fp32 sums: slot m reads
   // compact row dedup_row(m, K).
   int dedup_k;
+  // occupancy (large-batch kernels): when set, only the first *nact * rpr
+  // rows (rpr rows per request) are computed; later rows are inactive padding
+  const int32_t* nact;
+  int rpr;
 };
+// rows of an M-row operand with rpr rows per request that belong to active requests
+__device__ __forceinline__ int active_rows(const int32_t* nact, int rpr, int M) {
+  if (!nact) return M;
+  const long long n = (long long)max(nact[0], 0) * rpr;
+  return n < M ? int(n) : M;
+}
 __host__ __device__ inline int dedup_row(int slot, int K) {
   const int j = slot % (2 * K);
   return (slot / (2 * K)) * (K + 2) + (j < K + 1 ? j : K + 1);
@@ -173,24 +186,14 @@ struct AttnArgs {
   int grid;                       // persistent grid size
   int slots;                      // workgroups resident at once (2 per CU)
 };
-// ---- plain GEMMs through hipBLASLt (large batches) ---------------------------
-struct Blas;
-Blas* blas_create(size_t ws_bytes);
-void blas_destroy(Blas* b);
-// C[M, N] fp32 row-major = A[M, K] bf16 row-major x W[N, K]^T bf16 row-major;
-// false when no algorithm serves the shape (the caller keeps its own kernels)
-bool blas_gemm(Blas* b, int M, int N, int K, const void* A, const void* W, float* C, hipStream_t st);
-// D[M, N] bf16 = A x W^T (+ R when set; R may alias D), fp32 accumulation,
-// one rounding: the store and residual epilogues
-bool blas_gemm_bf16(Blas* b, int M, int N, int K, const void* A, const void* W, const void* R, void* D,
-                    hipStream_t st);
-// The epilogue of a dense GEMM (E_STORE, E_RESID, E_SILU, E_QKV) over fp32
-// sums C[M, N] in logical column order: the split-K reduction with one split.
-hipError_t launch_epilogue_f32(int epi, const GemmArgs& g, float* C, int num_cus, hipStream_t st);
-// Row-major copy of a GEMM's logical weight rows (the bmap row mapping) [N, K].
-hipError_t launch_pack_rows(int bmap, const GemmArgs& g, void* out, hipStream_t st);
-// The fc A operand [M, 2d] = [emb(ids[m]); hid[m]] (bf16).
-hipError_t launch_fc_rows(const GemmArgs& g, void* out, hipStream_t st);
+// ---- large-batch dense products and LM head (more than 64 rows) -------------
+// 32x32x16 MFMA tiles; QKV and gate/up pair their epilogue columns 32 apart
+// (see pe_mm.hip).  E_QKV runs on fp32 sums (g.part); with g.dedup_k the
+// product covers the K+2 compact rows per request and the epilogue every slot.
+hipError_t launch_mm(int aload, int bmap, int epi, const GemmArgs& g, int num_cus, hipStream_t st);
+// Partial argmax keys per row of the LM head of launch_mm over M draft rows
+// and N vocabulary rows (one per vocabulary tile).
+int mm_argmax_parts(int M, int N);
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 // Context length of each group of Sv consecutive slots (vpr groups per

@@ -19,6 +19,23 @@ namespace pe {
 
 // Validates request r and, when `write`, stores its slot fields; one wave
 // (lane = slot).  Returns the error kinds found (0: valid).
+// An inactive request (r >= occupancy): padding slots, nothing validated or
+// reported.  One wave (lane = slot).
+__device__ __forceinline__ void pad_request(const PrepareArgs& a, int r, int lane) {
+  const int K = a.K, S = 2 * K, base = r * S;
+  if (lane < S) {
+    a.ids[base + lane] = 0;
+    a.pos[base + lane] = 0;
+    a.hsrc[base + lane] = -1;
+    a.rej[base + lane] = 1;
+    a.msk[base + lane] = 0;
+    a.slots[base + lane] = -1;
+  }
+  if (lane < K) a.draft_rows[r * K + lane] = base + lane;
+  if (lane == 0) a.seq_lens[r] = 0;
+}
+__device__ __forceinline__ bool inactive(const int32_t* nact, int r) { return nact && r >= nact[0]; }
+
 __device__ __forceinline__ uint32_t prepare_request(const PrepareArgs& a, int r, int lane, bool write) {
   const int K = a.K, S = 2 * K, base = r * S;
   const int32_t* vt = a.vt + (long long)r * (K + 1);
@@ -116,7 +133,9 @@ __device__ __forceinline__ uint32_t prepare_request(const PrepareArgs& a, int r,
 
 __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
   const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (r < a.B) (void)prepare_request(a, r, threadIdx.x & 63, true);
+  if (r >= a.B) return;
+  if (inactive(a.nact, r)) pad_request(a, r, threadIdx.x & 63);
+  else (void)prepare_request(a, r, threadIdx.x & 63, true);
 }
 
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t st) {
@@ -261,6 +280,10 @@ __global__ __launch_bounds__(1024) void prepare_gather_kernel(PrepareArgs a, int
                                                               uint4* __restrict__ out) {
   __shared__ uint32_t s_kinds;
   const int r = blockIdx.x, K = a.K, S = 2 * K, total = S * cpr, nt = blockDim.x;
+  if (inactive(a.nact, r)) {  // its draft-hidden rows are not read
+    if (threadIdx.x < 64) pad_request(a, r, threadIdx.x);
+    return;
+  }
   // chunk c of the request's rows, as its map says (returned by value: a
   // pointer select between the two sources would put v in scratch memory)
   auto source = [&](int c) {
@@ -313,10 +336,18 @@ hipError_t launch_prepare_gather(const PrepareArgs& a, int row_bytes, const void
 __global__ __launch_bounds__(256) void verify_kernel(int B, int K, const int32_t* __restrict__ t,
                                                      const int32_t* __restrict__ g,
                                                      int32_t* __restrict__ acc,
-                                                     int32_t* __restrict__ bonus) {
+                                                     int32_t* __restrict__ bonus,
+                                                     const int32_t* __restrict__ nact) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (r >= B) return;
+  if (inactive(nact, r)) {  // an inactive request: accepted 0, bonus PE_PAD_TOKEN
+    if (lane == 0) {
+      acc[r] = 0;
+      bonus[r] = 0;
+    }
+    return;
+  }
   const bool miss = lane < K && t[(long long)r * K + lane] != g[(long long)r * (K + 1) + lane];
   const unsigned long long m = __ballot(miss);
   const int a = m ? (__ffsll((long long)m) - 1) : K;
@@ -327,9 +358,9 @@ __global__ __launch_bounds__(256) void verify_kernel(int B, int K, const int32_t
 }
 
 hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32_t* acc,
-                         int32_t* bonus, hipStream_t st) {
+                         int32_t* bonus, const int32_t* nact, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(verify_kernel, dim3((B + 3) / 4), dim3(256), 0, st, B, K, t, g, acc, bonus);
+  hipLaunchKernelGGL(verify_kernel, dim3((B + 3) / 4), dim3(256), 0, st, B, K, t, g, acc, bonus, nact);
   return hipGetLastError();
 }
 
@@ -424,10 +455,11 @@ __global__ __launch_bounds__(256) void dflash_prepare_kernel(DflashArgs a) {
   const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= a.B) return;
   const int K = a.K, S = K + 1, base = r * S;
+  const bool off = inactive(a.nact, r);  // an inactive request: padding, nothing validated or reported
   const int32_t* vp = a.vp + (long long)r * S;
-  const int acc = a.acc[r], p0 = vp[0], bonus = a.bonus[r];
-  const int vp_l = vp[lane < K ? lane : K];
-  uint32_t kinds = 0;
+  const int acc = off ? 0 : a.acc[r], p0 = off ? 0 : vp[0], bonus = off ? 0 : a.bonus[r];
+  const int vp_l = off ? lane : vp[lane < K ? lane : K];
+  uint32_t kinds = off ? 0x80000000u : 0u;
   if (acc < 0 || acc > K) kinds |= 1u;
   else if (bonus < 0 || bonus >= a.vocab) kinds |= 2u;
   if (__ballot(lane <= K && vp_l != p0 + lane)) kinds |= 8u;
@@ -464,8 +496,10 @@ __global__ __launch_bounds__(256) void dflash_prepare_kernel(DflashArgs a) {
     if (lane < K) a.draft_rows[r * K + lane] = base + 1 + lane;
     if (lane == 0) {
       a.seq_lens[r] = 0;
-      atomicOr(&a.err[0], kinds);
-      atomicMin(&a.err[1], uint32_t(r));
+      if (!off) {
+        atomicOr(&a.err[0], kinds);
+        atomicMin(&a.err[1], uint32_t(r));
+      }
     }
     return;
   }

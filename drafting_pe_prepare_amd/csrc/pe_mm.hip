@@ -1,0 +1,617 @@
+// Dense contractions of the drafter at larger batch (more than 64 rows):
+// out[m, n] = sum_k A[m, k] W[n, k] with a fused epilogue, and the LM head with
+// its row argmax.  "P-EAGLE: parallel speculative decoding in vLLM",
+// Architecture and mechanism, Step 2: fc over concat(emb, h), the N-layer
+// Transformer and the LM head, over all K positions of every request in one
+// pass.  At c=64 and beyond these are the step's matrix-core work.
+//
+// gfx950 design
+//  * v_mfma_f32_32x32x16_bf16.  Measured on this chip, the 32x32x16 form
+//    issues at ~2.0-2.1 PFLOP/s, the 16x16x32 form at ~1.3 PFLOP/s (half rate),
+//    so the large tiles use 32x32 outputs.  Lane l supplies A[l%32][8(l/32)+j]
+//    and B^T[l%32][8(l/32)+j] (both operands K-contiguous) and holds
+//    C[8(i/4) + 4(l/32) + i%4][l%32] in accumulator register i.
+//  * Both operands stream through a two-stage LDS ring of 64-wide k-tiles,
+//    filled by global_load_lds_dwordx4 (one instruction moves 8 whole
+//    128-byte rows).  Row r's 16-byte chunk c sits at slot c ^ ((r >> 1) & 7):
+//    gfx950's LDS serves 16 lanes of a 16-byte read per clock (256 B over 64
+//    banks), and under this swizzle the 16 rows a fragment read touches per
+//    clock fall on distinct banks (measured 218 B/clk/CU against 124 with
+//    the 128-byte c ^ (r & 7) swizzle).
+//  * The LM head runs transposed: W_lm rows (vocabulary) are the tile rows and
+//    the draft rows are the tile columns, so every lane holds 16 vocabulary
+//    entries of one draft row and the row argmax is a per-lane max plus one
+//    cross-half exchange; logits never reach memory unless asked for.
+//  * Column pairs an epilogue needs together (rotate-half RoPE partners, gate
+//    and up) sit 32 logical columns apart in one 64-column block, i.e. in the
+//    same lane of two neighbouring 32x32 tiles.  For QKV that is the plain
+//    [Wq; Wk; Wv] row order (head_dim 64: dims i and i + 32 pair up).
+//  * Output tiles fewer than the workgroup slots of the chip are split over k
+//    into fp32 partials, summed in a fixed order by mm_reduce_kernel, which
+//    also runs the RoPE + KV-write epilogue of the QKV product.
+#include <algorithm>
+
+#include "pe_common.h"
+#include "pe_internal.h"
+
+#ifndef PE_MM_SPLIT_MIN_KTILES
+#define PE_MM_SPLIT_MIN_KTILES 6  // fewest 64-wide k-tiles per split
+#endif
+
+namespace pe {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
+
+// logical weight row n of the 32-apart pairings (see above)
+template <int BMAP>
+__device__ __forceinline__ const uint16_t* mm_weight_row(const GemmArgs& g, int n) {
+  const long long K = g.K;
+  if (BMAP == B_GATEUP) {
+    const int t = n >> 6, r = n & 63;
+    return (r < 32 ? (const uint16_t*)g.W0 : (const uint16_t*)g.W1) + (long long)(t * 32 + (r & 31)) * K;
+  } else if (BMAP == B_QKV) {
+    if (n < g.nq) return (const uint16_t*)g.W0 + (long long)n * K;
+    if (n < g.nq + g.nk) return (const uint16_t*)g.W1 + (long long)(n - g.nq) * K;
+    return (const uint16_t*)g.W2 + (long long)(n - g.nq - g.nk) * K;
+  }
+  return (const uint16_t*)g.W0 + (long long)n * K;
+}
+
+// One LDS-DMA instruction: every lane moves 16 bytes from `src` to LDS byte
+// lds + 16 lane (lds wave-uniform).  Written as inline asm on purpose: the
+// compiler tracks the LDS writes of its own global_load_lds and, unable to
+// tell the stage being read from the stages in flight, waits for every DMA
+// before each LDS read (vmcnt(0) at the top of each k-tile, which drains the
+// ring).  Hidden from it, the DMAs are ordered by this file's own vmcnt waits
+// and barriers only.  The asm writes no register (the data goes to LDS), so
+// no output register can be reused while the load is in flight; m0 is set
+// here and read by no other instruction of these kernels.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+// The same with the non-temporal cache policy (data read once).
+__device__ __forceinline__ void dma16_nt(const uint16_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return uint32_t(uintptr_t((__attribute__((address_space(3))) const unsigned char*)p));
+}
+
+// Slot of compact row m of a MASK-deduplicated first layer (K+2 rows per
+// request: copied slots 0..K and one MASK slot).
+__device__ __forceinline__ int dedup_slot(int m, int K) { return (m / (K + 2)) * (2 * K) + m % (K + 2); }
+
+// ---------------------------------------------------------------------------
+// The tiled kernel.  BM x BN output tile, WM x WN waves of (BM/WM) x (BN/WN).
+// TRANS: the LM head -- tile rows are W rows (vocabulary, g.N of them), tile
+// columns are the rows of A (draft rows, g.M); EPI is then E_ARGMAX.
+// KT: k-tile width (64: 128-byte stage rows, 32: 64-byte rows); S: stages in
+// the LDS ring, so S-1 k-tiles are in flight while one is consumed.
+// E_PART: the grid holds g.ksplit copies of the tile grid, copy s summing
+// k-tiles [s nk / ksplit, (s+1) nk / ksplit) into fp32 partials.
+// ---------------------------------------------------------------------------
+// Stage row r (RB bytes) keeps its 16-byte chunk c at slot c ^ swz(r): the
+// 16 rows one clock of a fragment read touches then fall on distinct banks of
+// the 256-byte bank window (two 128-byte rows or four 64-byte rows per window).
+template <int RB>
+__device__ __forceinline__ int mm_swz(int r) {
+  return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
+template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, bool TRANS, int KT, int S, int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN, TI = WTM / 32, TJ = WTN / 32;
+  static_assert(TI * 32 * WM == BM && TJ * 32 * WN == BN, "whole 32x32 tiles per wave");
+  static_assert(KT == 32 || KT == 64, "k-tiles of 32 or 64");
+  constexpr int RB = KT * 2, CPR = RB / 16, RPG = 1024 / RB;  // row bytes, chunks per row, rows per DMA
+  constexpr int GA = BM / RPG, GB = BN / RPG;                 // DMA row groups of each operand
+  static_assert(GA * RPG == BM && GB * RPG == BN, "whole DMA row groups");
+  constexpr int QA = (GA + NW - 1) / NW, QB = (GB + NW - 1) / NW, Q = QA + QB;  // DMAs per wave per k-tile
+  static_assert(S >= 2 && S <= 5 && (S - 1) * Q < 64, "ring depth within the vmcnt range");
+  constexpr int NS = KT / 16;                                  // MFMA substeps per k-tile
+  constexpr int STAGE = (BM + BN) * RB;
+  // distinct LDS objects, so the compiler sees that the DMA into one stage
+  // and the fragment reads of another do not alias
+  __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE], st1[STAGE], st2[S > 2 ? STAGE : 16],
+      st3[S > 3 ? STAGE : 16], st4[S > 4 ? STAGE : 16];
+
+  const int Mk = TRANS ? g.N : g.M, Nk = TRANS ? g.M : g.N;
+  int bid = blockIdx.x, ks = 0, mt, nt;
+  const int ksplit = EPI == E_PART ? g.ksplit : 1;
+  if (EPI == E_PART) {
+    const int per = TRANS ? ntiles * ((mtiles + 7) / 8) * 8 : mtiles * ((ntiles + 7) / 8) * 8;
+    ks = bid / per;
+    bid -= ks * per;
+  }
+  // workgroups that share an operand tile run back to back on one XCD
+  // (workgroup b runs on XCD b % 8): the weight tile of a dense product, the
+  // vocabulary tile of the LM head
+  if (TRANS) {
+    const int j = bid >> 3;
+    nt = j % ntiles;
+    mt = (j / ntiles) * 8 + (bid & 7);
+    if (mt >= mtiles) return;
+  } else {
+    const int j = bid >> 3;
+    mt = j % mtiles;
+    nt = (j / mtiles) * 8 + (bid & 7);
+    if (nt >= ntiles) return;
+  }
+  const int m0 = mt * BM, n0 = nt * BN;
+  // rows of inactive requests (occupancy below the captured batch) are skipped
+  if (TRANS ? n0 >= active_rows(g.nact, g.rpr, Nk) : m0 >= active_rows(g.nact, g.rpr, Mk)) return;
+  const int nkt = g.K / KT;
+  const int kb = ks * nkt / ksplit, nk = (ks + 1) * nkt / ksplit - kb;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wm = w / WN, wn = w % WN;
+
+  // DMA instruction q < QA of this wave fills A-role row group j = w + NW q
+  // (stage rows RPG j .. RPG j + RPG-1), instruction QA + q the B-role group
+  // GA + w + NW q; lane l takes row RPG j + l/CPR and slot l%CPR, i.e. global
+  // chunk (l%CPR) ^ swz(row).  A wave whose group would lie past its operand
+  // repeats another of that operand's groups (the same bytes to the same
+  // place), so every wave issues Q DMAs per k-tile and one vmcnt serves all;
+  // the operand of each instruction is known at compile time.
+  const uint16_t* lo[Q];
+  const uint16_t* hi[QA];
+  uint32_t dst[Q];
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform copy for the LDS addresses
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const bool isa = q < QA;
+    const int jj = wu + NW * (isa ? q : q - QA), gn = isa ? GA : GB;
+    const int j = (isa ? 0 : GA) + (jj < gn ? jj : wu % gn);
+    dst[q] = uint32_t(j * 1024);
+    const int r = RPG * j + l / CPR;
+    const int c = ((l % CPR) ^ mm_swz<RB>(r)) * 8;
+    if (isa) {
+      const int m = min(m0 + r, Mk - 1);
+      if (TRANS) {
+        lo[q] = mm_weight_row<B_PLAIN>(g, m) + c;
+        hi[q] = lo[q];
+      } else if (AL == A_FC) {
+        const int sl = g.dedup_k ? dedup_slot(m, g.dedup_k) : m;
+        int id = g.ids[sl];
+        id = id < 0 ? 0 : (id >= g.vocab ? g.vocab - 1 : id);
+        lo[q] = (const uint16_t*)g.embed + (long long)id * g.d + c;
+        hi[q] = (const uint16_t*)g.hid + (long long)sl * g.d - g.d + c;
+      } else {
+        lo[q] = (const uint16_t*)g.A + (long long)m * g.lda + c;
+        hi[q] = lo[q];
+      }
+    } else {
+      const int n = min(n0 + r - BM, Nk - 1);
+      if (TRANS) lo[q] = (const uint16_t*)g.A + (long long)n * g.lda + c;
+      else lo[q] = mm_weight_row<BMAP>(g, n) + c;
+    }
+  }
+  auto issue = [&](unsigned char* st, int kt) {
+    const int k0 = (kb + kt) * KT;
+    const uint32_t sb = lds_addr(st);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      if (q < QA) {
+        const uint16_t* src = (AL == A_FC && !TRANS && k0 >= g.d) ? hi[q] + k0 : lo[q] + k0;
+        // the LM head's weights stream once per launch: non-temporal, so they
+        // do not push the draft rows and the layer weights out of the caches
+        if (TRANS) dma16_nt(src, sb + dst[q]);
+        else dma16(src, sb + dst[q]);
+      } else {
+        dma16(lo[q] + k0, sb + dst[q]);
+      }
+    }
+  };
+  // wait until at most n k-tiles of this wave's DMAs are in flight
+  auto wait_tiles = [&](int n) {
+    if (n >= 4) wait_vmcnt<(S > 4 ? 4 : 0) * Q>();
+    else if (n == 3) wait_vmcnt<(S > 3 ? 3 : 0) * Q>();
+    else if (n == 2) wait_vmcnt<(S > 2 ? 2 : 0) * Q>();
+    else if (n == 1) wait_vmcnt<Q>();
+    else wait_vmcnt<0>();
+  };
+
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment rows: A-role row wm*WTM + 32 i + l%32, B-role row BM + wn*WTN +
+  // 32 j + l%32; substep s (16 of the tile's k) reads chunk 2s + l/32
+  const int sw = mm_swz<RB>(l & 31);
+  const int abase = (wm * WTM + (l & 31)) * RB, bbase = (BM + wn * WTN + (l & 31)) * RB;
+  uint4 fa[2][TI], fb[2][TJ];
+  auto load = [&](int buf, const unsigned char* st, int s) {
+    const int x = ((2 * s + (l >> 5)) ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa[buf][i] = *reinterpret_cast<const uint4*>(st + abase + x + i * 32 * RB);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fb[buf][j] = *reinterpret_cast<const uint4*>(st + bbase + x + j * 32 * RB);
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32(fa[buf][i], fb[buf][j], acc[i][j]);
+  };
+  auto stage = [&](int j) -> unsigned char* {
+    return j == 0 ? st0 : j == 1 ? st1 : j == 2 ? st2 : j == 3 ? st3 : st4;
+  };
+
+  const int pre = nk < S ? nk : S;
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+    if (j < pre) issue(stage(j), j);
+  wait_tiles(pre - 1);                      // this wave's DMAs of k-tile 0 have landed
+  asm volatile("s_barrier" ::: "memory");   // ... and everyone's
+  load(0, st0, 0);
+  // k-tile kt sits in `cur`; on entry fa[0]/fb[0] hold its first substep.
+  // `cur` and `nxt` are distinct stages (restrict), so the DMA into `cur` can
+  // stay in flight across the reads of `nxt`.
+  // The fragment reads of substep s+1 are issued before the MFMAs of substep
+  // s, and sched_barrier keeps the compiler from sinking each read down to its
+  // first use (it otherwise does, and every MFMA then waits out an LDS round
+  // trip).  Each substep starts with an explicit lgkmcnt(0): the reads it
+  // waits for were issued one MFMA group earlier, and with the counter known
+  // to be clear the compiler puts no wait of its own (a full one, whenever a
+  // scalar load might be in flight) between the new reads and the MFMAs.
+  auto tile = [&](unsigned char* __restrict__ cur, const unsigned char* __restrict__ nxt, int kt) {
+#pragma unroll
+    for (int s = 0; s + 1 < NS; ++s) {
+      wait_lgkm0();
+      load((s + 1) & 1, cur, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lgkm0();  // this wave's reads of `cur` have returned
+    if (kt + 1 < nk) {
+      // k-tile kt+1 must land; kt+2 .. kt+S-1 (those issued) may stay in flight
+      const int later = nk - 2 - kt;
+      wait_tiles(later < S - 2 ? later : S - 2);
+      asm volatile("s_barrier" ::: "memory");   // everyone's, and `cur` is free
+      if (kt + S < nk) issue(cur, kt + S);
+      load(NS & 1, nxt, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma((NS - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int kt0 = 0; kt0 < nk; kt0 += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      if (kt0 + j < nk) tile(stage(j), stage((j + 1) % S), kt0 + j);
+  }
+
+  // lane l holds C[32 i + 8 (r/4) + 4 (l/32) + r%4][32 j + l%32] of the wave tile
+  const int rbase = wm * WTM + 4 * (l >> 5), cbase = wn * WTN + (l & 31);
+  if constexpr (EPI == E_ARGMAX) {
+    static_assert(TRANS, "the LM head runs transposed");
+    // column = draft row n, tile rows = vocabulary entries m
+    __syncthreads();  // every fragment read is done and no DMA is in flight: the stages are free
+    uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [WM][BN]
+    static_assert(WM * BN * 8 <= STAGE, "argmax scratch fits one stage");
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n = n0 + cbase + 32 * j;
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+          if (m < Mk) {
+            if (g.logits && n < Nk) g.logits[(long long)n * g.ldl + m] = acc[i][j][r];
+            const uint64_t k = argmax_key(acc[i][j][r], m);
+            best = k > best ? k : best;
+          }
+        }
+      const uint32_t olo = __shfl_xor(uint32_t(best), 32, 64), ohi = __shfl_xor(uint32_t(best >> 32), 32, 64);
+      const uint64_t other = (uint64_t(ohi) << 32) | olo;
+      best = other > best ? other : best;
+      if (l < 32) s_best[wm * BN + cbase + 32 * j] = best;
+    }
+    __syncthreads();
+    for (int c = tid; c < BN; c += 64 * NW) {
+      const int n = n0 + c;
+      if (n < Nk) {
+        uint64_t b = s_best[c];
+#pragma unroll
+        for (int v = 1; v < WM; ++v) b = s_best[v * BN + c] > b ? s_best[v * BN + c] : b;
+        g.keys[(long long)n * g.parts + mt] = b;
+      }
+    }
+  } else if constexpr (EPI == E_PART) {
+    float* P = g.part + (long long)ks * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int n = n0 + cbase + 32 * j;
+          if (n < g.N) P[(long long)m * g.N + n] = acc[i][j][r];
+        }
+      }
+  } else if constexpr (EPI == E_STORE || EPI == E_RESID) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int n = n0 + cbase + 32 * j;
+          if (n >= g.N) continue;
+          const long long o = (long long)m * g.ldo + n;
+          float v = acc[i][j][r];
+          if (EPI == E_RESID) v += bf2f(((const uint16_t*)g.resid)[o]);
+          ((uint16_t*)g.out)[o] = f2bf(v);
+        }
+      }
+  } else if constexpr (EPI == E_SILU) {
+    static_assert(TJ % 2 == 0, "gate/up pairs are neighbouring 32-column tiles");
+    // logical block 64 t: columns 64 t + c (gate) and 64 t + 32 + c (up) ->
+    // output column 32 t + c
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int q = 0; q < TJ / 2; ++q) {
+          const int n = n0 + cbase + 64 * q;  // gate column
+          if (n >= g.N) continue;
+          const float gt = acc[i][2 * q][r], up = acc[i][2 * q + 1][r];
+          const float v = gt / (1.0f + expf(-gt)) * up;
+          ((uint16_t*)g.out)[(long long)m * g.ldo + ((n >> 6) << 5) + (n & 31)] = f2bf(v);
+        }
+      }
+  } else {
+    static_assert(EPI == E_PART, "epilogues: argmax, partial sums, store, residual, SiLU.mul");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K sum and epilogue over fp32 partials [ksplit][M][N] in the 32-apart
+// logical column order: partials are added in split order (deterministic),
+// then the epilogue runs.  Store / residual: 8 consecutive columns per thread;
+// SiLU.mul: 8 outputs from 8 gate and 8 up columns; QKV: 8 RoPE pairs (q and
+// k leave as 16-byte stores; V is d-major inside a block, one element per
+// position row).  With dedup_k the QKV epilogue covers all `rows` slots of the
+// parallel layout, slot s reading the sums of compact row dedup_row(s).
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, int rpr) {
+  rows = active_rows(g.nact, rpr, rows);  // rows of inactive requests are skipped
+  const int KS = g.ksplit;
+  const long long MN = (long long)g.M * g.N;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  auto sum8 = [&](int m, int n, float (&v)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = 0.f;
+    for (int k = 0; k < KS; ++k) {
+      const float* p = g.part + k * MN + (long long)m * g.N + n;
+      const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+      v[4] += c.x; v[5] += c.y; v[6] += c.z; v[7] += c.w;
+    }
+  };
+  auto pack8 = [](const float (&v)[8]) {
+    return uint4{f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
+  };
+  if constexpr (EPI == E_STORE || EPI == E_RESID) {
+    const int per_row = g.N / 8;
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
+      const int m = int(e / per_row), n = int(e % per_row) * 8;
+      float v[8];
+      sum8(m, n, v);
+      const long long o = (long long)m * g.ldo + n;
+      if constexpr (EPI == E_RESID) {
+        const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + o);
+        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[2 * t] += __uint_as_float(rw[t] << 16);
+          v[2 * t + 1] += __uint_as_float(rw[t] & 0xFFFF0000u);
+        }
+      }
+      *reinterpret_cast<uint4*>((uint16_t*)g.out + o) = pack8(v);
+    }
+  } else if constexpr (EPI == E_SILU) {
+    const int per_row = g.N / 16;  // 8 outputs per thread, 32 per 64-column block
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
+      const int m = int(e / per_row), pc = int(e % per_row), t = pc >> 2, c0 = (pc & 3) * 8;
+      float gt[8], up[8], v[8];
+      sum8(m, 64 * t + c0, gt);
+      sum8(m, 64 * t + 32 + c0, up);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = gt[u] / (1.0f + expf(-gt[u])) * up[u];
+      *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)m * g.ldo + 32 * t + c0) = pack8(v);
+    }
+  } else {
+    static_assert(EPI == E_QKV, "split-K epilogues: store, residual, SiLU.mul, QKV");
+    constexpr int hd = 64;  // bf16 storage implies head_dim 64 (checked at context creation)
+    const int per_row = g.N / 16;  // 8 pairs per thread, 4 per 64-column head
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
+      const int m = int(e / per_row), pc = int(e % per_row), nb = (pc >> 2) * 64, c0 = (pc & 3) * 8;
+      const int cm = g.dedup_k ? dedup_row(m, g.dedup_k) : m;
+      float lo[8], hi[8];
+      sum8(cm, nb + c0, lo);
+      sum8(cm, nb + 32 + c0, hi);
+      if (nb < g.nq + g.nk) {
+        const bool isq = nb < g.nq;
+        const int head = (isq ? nb : nb - g.nq) / hd;
+        const int pos = g.positions[m];
+        float olo[8], ohi[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          // angle pos * theta^(-2i/hd) in turns: the fp64 product minus its
+          // nearest integer is the exact fraction of a turn for any position;
+          // v_sin_f32 / v_cos_f32 take turns
+          const double tt = double(pos) * g.rope_turns[c0 + t];
+          const float x = float(tt - rint(tt));
+          const float sn = __builtin_amdgcn_sinf(x), cs = __builtin_amdgcn_cosf(x);
+          olo[t] = lo[t] * cs - hi[t] * sn;
+          ohi[t] = hi[t] * cs + lo[t] * sn;
+        }
+        uint16_t* dst = nullptr;
+        if (isq) {
+          dst = (uint16_t*)g.qout + ((long long)m * (g.nq / hd) + head) * hd;
+        } else {
+          const long long slot = g.slots[m];
+          if (slot >= 0 && slot < g.num_slots) dst = (uint16_t*)g.kcache + (slot * g.Hkv + head) * hd;
+        }
+        if (dst) {
+          *reinterpret_cast<uint4*>(dst + c0) = pack8(olo);
+          *reinterpret_cast<uint4*>(dst + 32 + c0) = pack8(ohi);
+        }
+      } else {
+        const long long slot = g.slots[m];
+        if (slot >= 0 && slot < g.num_slots) {
+          const int head = (nb - g.nq - g.nk) / hd;
+          const int bsl = __builtin_ctz(g.block_size);  // a power of two (checked at context creation)
+          const long long blk = slot >> bsl, off = slot & (g.block_size - 1);
+          uint16_t* vp = (uint16_t*)g.vcache + (((blk * g.Hkv + head) * hd) << bsl) + off;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            vp[(long long)(c0 + t) << bsl] = f2bf(lo[t]);
+            vp[(long long)(32 + c0 + t) << bsl] = f2bf(hi[t]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+#ifndef PE_MM_LM_VARIANT
+#define PE_MM_LM_VARIANT 1
+#endif
+#ifndef PE_MM_DENSE_VARIANT
+#define PE_MM_DENSE_VARIANT 0
+#endif
+
+// LM head tiles (transposed): BM vocabulary rows x BN draft rows.
+struct LmTile { int bm, bn; };
+static LmTile mm_lm_tile(int D) {
+#if PE_MM_LM_VARIANT == 0 || PE_MM_LM_VARIANT == 4
+  if (D > 256) return {128, 448};
+#elif PE_MM_LM_VARIANT == 3
+  if (D > 256) return {256, 160};
+#else
+  if (D > 256) return {256, 224};
+#endif
+  if (D > 128) return {128, 256};
+  return {128, 128};
+}
+
+int mm_argmax_parts(int M, int N) { return (N + mm_lm_tile(M).bm - 1) / mm_lm_tile(M).bm; }
+
+template <int BM, int BN, int WM, int WN, int KT, int S>
+static hipError_t mm_lm(const GemmArgs& g, hipStream_t st) {
+  const int mtiles = (g.N + BM - 1) / BM, ntiles = (g.M + BN - 1) / BN;
+  if (g.parts != mtiles) return hipErrorInvalidValue;
+  const int grid = ntiles * ((mtiles + 7) / 8) * 8;
+  hipLaunchKernelGGL((mm_kernel<E_ARGMAX, A_PLAIN, B_PLAIN, BM, BN, WM, WN, true, KT, S, WM * WN / 4>), dim3(grid),
+                     dim3(64 * WM * WN), 0, st, g, mtiles, ntiles);
+  return hipGetLastError();
+}
+
+static hipError_t mm_lm_any(const GemmArgs& g, hipStream_t st) {
+  const LmTile t = mm_lm_tile(g.M);
+  if (t.bn == 128) return mm_lm<128, 128, 4, 2, 64, 2>(g, st);
+  if (t.bn == 256) return mm_lm<128, 256, 4, 2, 64, 2>(g, st);
+#if PE_MM_LM_VARIANT == 0
+  return mm_lm<128, 448, 4, 2, 64, 2>(g, st);
+#elif PE_MM_LM_VARIANT == 1
+  return mm_lm<256, 224, 8, 1, 32, 4>(g, st);
+#elif PE_MM_LM_VARIANT == 2
+  return mm_lm<256, 224, 8, 1, 32, 5>(g, st);
+#elif PE_MM_LM_VARIANT == 3
+  return mm_lm<256, 160, 8, 1, 64, 3>(g, st);
+#else
+  return mm_lm<128, 448, 4, 2, 32, 4>(g, st);
+#endif
+}
+
+// Dense tiles: 128 x 128, four waves of 64 x 64.
+#if PE_MM_DENSE_VARIANT == 0
+constexpr int kDKT = 64, kDS = 2, kDWgPerCu = 2;
+#elif PE_MM_DENSE_VARIANT == 1
+constexpr int kDKT = 64, kDS = 3, kDWgPerCu = 1;
+#else
+constexpr int kDKT = 32, kDS = 4, kDWgPerCu = 2;
+#endif
+
+template <int EPI, int AL, int BMAP>
+static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
+  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
+  const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN, nk = g.K / kDKT;
+  const long long tiles = (long long)mtiles * ntiles, slots = (long long)kDWgPerCu * num_cus;
+  // the QKV epilogue always runs on fp32 sums (one split at least); other
+  // products split over k when their tiles leave workgroup slots idle
+  long long ks = 1;
+  if (tiles < slots && g.part) {
+    ks = (slots + tiles - 1) / tiles;
+    ks = std::min<long long>(ks, nk * kDKT / 64 / PE_MM_SPLIT_MIN_KTILES);
+    ks = std::min<long long>(ks, g.part_cap / ((long long)g.M * g.N));
+    ks = std::max<long long>(ks, 1);
+  }
+  // rows the epilogue covers: every slot of a MASK-deduplicated QKV product
+  const bool expand = EPI == E_QKV && g.dedup_k;
+  const int rows = expand ? g.M / (g.dedup_k + 2) * (2 * g.dedup_k) : g.M;
+  const int epi_rpr = expand ? 2 * g.dedup_k : g.rpr;
+  const long long per = (long long)mtiles * ((ntiles + 7) / 8) * 8;
+  if constexpr (EPI != E_QKV) {
+    if (ks == 1) {
+      hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, false, kDKT, kDS, 2>), dim3(unsigned(per)),
+                         dim3(64 * WM * WN), 0, st, g, mtiles, ntiles);
+      return hipGetLastError();
+    }
+  }
+  if (!g.part || (long long)g.M * g.N * ks > g.part_cap) return hipErrorInvalidValue;
+  GemmArgs gp = g;
+  gp.ksplit = int(ks);
+  hipLaunchKernelGGL((mm_kernel<E_PART, AL, BMAP, BM, BN, WM, WN, false, kDKT, kDS, 2>), dim3(unsigned(per * ks)),
+                     dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long work = (long long)rows * (EPI == E_QKV || EPI == E_SILU ? g.N / 16 : g.N / 8);
+  const long long blocks = std::min<long long>((work + 255) / 256, 8LL * num_cus);
+  hipLaunchKernelGGL(mm_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, st, gp, rows, epi_rpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_mm(int aload, int bmap, int epi, const GemmArgs& g, int num_cus, hipStream_t st) {
+  if (g.M <= 0) return hipSuccess;
+  if (g.K % 64) return hipErrorInvalidValue;  // whole 64-wide k-tiles (and fc halves)
+  if (epi == E_ARGMAX) {
+    if (aload != A_PLAIN || bmap != B_PLAIN) return hipErrorInvalidValue;
+    return mm_lm_any(g, st);
+  }
+  if (g.N % 64) return hipErrorInvalidValue;  // whole 64-column pair blocks
+  if (aload == A_FC && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_FC, B_PLAIN>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_QKV && epi == E_QKV) return mm_dense<E_QKV, A_PLAIN, B_QKV>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_RESID) return mm_dense<E_RESID, A_PLAIN, B_PLAIN>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_GATEUP && epi == E_SILU) return mm_dense<E_SILU, A_PLAIN, B_GATEUP>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_PLAIN, B_PLAIN>(g, num_cus, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pe

@@ -417,19 +417,36 @@ typedef struct pe_step_args {
   const void* const* wv_inject;
   int32_t* attn_positions;       /* [B*(K+1)] */
   int64_t* inject_slots;         /* [B*(K+1)] */
+  /* Occupancy: NULL (all B requests active), or a device int32 holding the
+   * number n of active requests; requests n..B-1 are inactive slots of the
+   * batch.  Read on the device at every replay, so one captured graph serves
+   * any occupancy 0..B [P1, KV cache and CUDA Graphs: the graph is captured
+   * for the K x max_num_seqs draft rows of the largest batch].  An inactive
+   * request is not validated and sets nothing in the device error word; its
+   * slots become padding (rejected, KV slot -1, seq_len 0, no KV write), its
+   * draft tokens are -1, accepted_out 0 and bonus_out PE_PAD_TOKEN, and the
+   * dense products, attention and LM head skip its rows where they can.
+   * n is clamped to [0, B]. */
+  const int32_t* num_active;
 } pe_step_args;
 
-/* Captures prepare -> gather -> forward (args->mode picks the parallel pass
- * or the sequential passes) -> verify for (B, *args) into a
- * hipGraph on the first call and replays it on later calls with the same B
- * and the same pointers (values inside the buffers may change between
- * replays: a, p0, tokens and block tables are read on the device).  A call
- * with different pointers or B recaptures: capture runs on a private
- * non-blocking stream of the context (the legacy default stream cannot be
- * captured) after the context's stream has drained; every launch of the graph
- * is enqueued on the context's stream.  The graph holds no memset node.  [P1, KV cache and CUDA Graphs: one graph covers the draft
- * batch of K x max_num_seqs draft rows.] */
+/* Captures prepare -> gather -> forward (args->mode picks the parallel pass,
+ * the sequential passes or a DFlash-style round) -> verify for (B, *args)
+ * into a hipGraph on the first call and replays it on later calls with the
+ * same B and the same pointers.  Values inside the buffers may change between
+ * replays -- a, p0, tokens, block tables and the occupancy *num_active are
+ * read on the device -- so a graph captured at B = max_num_seqs serves every
+ * batch of up to max_num_seqs requests [P1, KV cache and CUDA Graphs: one
+ * graph covers the K x max_num_seqs draft rows].  A call with other pointers
+ * or another B recaptures; capture runs on a private non-blocking stream of
+ * the context (the legacy default stream cannot be captured), and only a
+ * recapture that replaces an earlier graph first waits for the context's
+ * stream (the old graph may still run).  Every launch of the graph is
+ * enqueued on the context's stream.  The graph holds no memset node. */
 pe_status pe_step_graph(pe_ctx* ctx, int32_t B, const pe_step_args* args);
+
+/* Number of captures and of replays pe_step_graph has made on this context. */
+pe_status pe_step_graph_stats(pe_ctx* ctx, int64_t* captures, int64_t* replays);
 
 /* Synchronizes the context's stream, reads and clears the sticky device error
  * word.  kinds: OR of PE_DEVERR_*; first_request: lowest failing request

@@ -79,6 +79,62 @@ def run_step(st: Setup, inp: dict, want_logits=True, B=None, ar=False):
     return out
 
 
+class GraphRun:
+    """Device buffers of one step for pe_step_graph (parallel or sequential
+    mode), captured at B = w.batch; run(n) replays it at occupancy n (None:
+    every request) on fresh copies of the KV caches and returns host copies
+    like run_step."""
+
+    def __init__(self, st: Setup, inp: dict, mode=None, occupancy=False, want_logits=True):
+        w = st.w
+        self.st, self.inp, self.w = st, inp, w
+        B, K, d = w.batch, w.K, w.d
+        self.t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+                  ("verify_tokens", "verify_positions", "num_accepted", "bonus_tokens", "block_table",
+                   "target_tokens", "target_hidden")}
+        self.kv0 = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+        self.kv = [(k.clone(), v.clone()) for k, v in self.kv0]
+        self.batch = pb.Batch(B, K)
+        sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.dh = torch.zeros((B * 2 * K, d), dtype=sdt, device="cuda")
+        self.tok = torch.zeros(B * K, dtype=torch.int32, device="cuda")
+        self.lg = torch.zeros((B * K, w.vocab), dtype=torch.float32, device="cuda") if want_logits else None
+        self.acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+        self.bon = torch.zeros(B, dtype=torch.int32, device="cuda")
+        self.nact = torch.full((1,), B, dtype=torch.int32, device="cuda") if occupancy else None
+        t = self.t
+        self.args = pb.make_step_args(t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                                      t["bonus_tokens"], t["block_table"], inp["num_kv_blocks"], self.batch,
+                                      t["target_hidden"], st.dev["h_shared"], self.dh,
+                                      [k for k, _ in self.kv], [v for _, v in self.kv], self.tok,
+                                      t["target_tokens"], self.acc, self.bon, logits=self.lg,
+                                      mode=pb.STEP_PARALLEL if mode is None else mode, num_active=self.nact)
+
+    def run(self, n=None):
+        w, B, K = self.w, self.w.batch, self.w.K
+        for (k, v), (k0, v0) in zip(self.kv, self.kv0):
+            k.copy_(k0)
+            v.copy_(v0)
+        if n is not None:
+            self.nact.fill_(n)
+        self.tok.fill_(-5)
+        self.dh.fill_(0)
+        if self.lg is not None:
+            self.lg.fill_(0.0)
+        pb.pe_step_graph(self.st.ctx, B, self.args)
+        torch.cuda.synchronize()
+        return {
+            "batch": self.batch.host(B, K),
+            "draft_hidden": pb.to_host(self.dh),
+            "tokens": self.tok.cpu().numpy(),
+            "logits": self.lg.cpu().numpy() if self.lg is not None else None,
+            "kv": [(pb.to_host(k), pb.to_host(v)) for k, v in self.kv],
+            "accepted": self.acc.cpu().numpy(),
+            "bonus": self.bon.cpu().numpy(),
+            "error": pb.pe_get_device_error(self.st.ctx),
+        }
+
+
 def oracle_step(w, prm, inp, requests=None, precision=None):
     b = O.prepare(inp["verify_tokens"], inp["verify_positions"], inp["num_accepted"],
                   inp["bonus_tokens"], inp["block_table"], inp["num_kv_blocks"],
@@ -94,31 +150,46 @@ def assert_metadata_equal(gpu_batch, ob):
         np.testing.assert_array_equal(gpu_batch[f], ob[f], err_msg=f)
 
 
+BAND = {"rows": 0, "differ": 0}  # rows with GAP < top-2 gap <= gap_min, over the session
+
+
 def assert_tokens_logits(tokens, logits, o_logits, tol_rel, rows=None):
     """Logits within tol_rel * RMS; tokens equal wherever the oracle's top-2
-    gap exceeds GAP and twice the measured logit error (or twice the logit
-    bound, when that bound is above the one-layer bf16 one), otherwise the GPU
-    token must be near-maximal in the oracle's logits.  Returns the number of
-    rows with a tight gap."""
+    gap exceeds gap_min = max(GAP, 2 x the measured max logit error) (or
+    max(GAP, 2 x the bound) when the bound is above the one-layer bf16 one);
+    below it the GPU token must be near-maximal in the oracle's logits.
+
+    Why not GAP alone: two logits that each differ from the oracle's by at
+    most err can swap order only when they are within 2 err of each other, and
+    when 2 err > GAP nothing in the logit bound rules out a swap in the band
+    (GAP, 2 err].  Rows in that band are counted (BAND), and those whose token
+    differs are reported, so the strict reading can be checked case by case.
+    Returns the number of rows with a gap of at most gap_min."""
     if rows is not None:
         tokens, logits = tokens[rows], logits[rows]
     rms = float(np.sqrt(np.mean(o_logits ** 2)))
     tol = tol_rel * rms
     err = float(np.max(np.abs(logits.astype(np.float64) - o_logits)))
-    print(f"  logits: max |dlogit| / rms = {err / rms:.5f}", flush=True)
-    assert err <= tol, f"max |dlogit| {err:.3e} > {tol:.3e} (rms {rms:.3e})"
     tight = 0
-    # logits within err of the oracle's can change the argmax only where the
-    # oracle's top-2 gap is below 2 err
     gap_min = max(GAP, 2 * err) if tol_rel <= LOGIT_TOL["bf16"] else max(GAP, 2 * tol)
+    band = differ = 0
     for i in range(o_logits.shape[0]):
         srt = np.sort(o_logits[i])
         gap = srt[-1] - srt[-2]
+        best = int(np.argmax(o_logits[i]))
         if gap > gap_min:
-            assert tokens[i] == int(np.argmax(o_logits[i])), (i, tokens[i], np.argmax(o_logits[i]), gap)
+            assert tokens[i] == best, (i, tokens[i], best, gap)
         else:
             tight += 1
             assert o_logits[i, tokens[i]] >= srt[-1] - 2 * tol, (i, tokens[i])
+            if gap > GAP:
+                band += 1
+                differ += int(tokens[i] != best)
+    BAND["rows"] += band
+    BAND["differ"] += differ
+    print(f"  logits: max |dlogit| / rms = {err / rms:.5f}; tokens: {o_logits.shape[0]} rows, "
+          f"{band} with {GAP} < gap <= {gap_min:.4f} ({differ} of them differ)", flush=True)
+    assert err <= tol, f"max |dlogit| {err:.3e} > {tol:.3e} (rms {rms:.3e})"
     return tight
 
 

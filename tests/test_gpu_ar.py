@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle as O
 from drafting_pe_prepare_amd import configs, synth
 from drafting_pe_prepare_amd import binding as pb
 
@@ -88,7 +89,8 @@ def test_ar_padded_request():
 
 def test_ar_step_graph_replays_match_eager():
     """The step graph in sequential mode equals eager pe_ar_draft on every
-    replay, with eager work and synchronization between replays."""
+    replay, with eager work and synchronization between replays, and the
+    last replay matches the oracle's sequential drafting pass by pass."""
     w = SMALL_BF16.with_(K=5, batch=4, accepted="uniform", prefix=("uniform", 40, 400))
     st = Setup(w, seed=27)
     try:
@@ -127,6 +129,14 @@ def test_ar_step_graph_replays_match_eager():
             for (k, v), (ke, ve) in zip(kv, eager["kv"]):
                 np.testing.assert_array_equal(pb.to_host(k), ke)
                 np.testing.assert_array_equal(pb.to_host(v), ve)
+        # the graph's passes against the oracle's sequential drafting
+        g = {"tokens": tok.cpu().numpy(), "logits": lg.cpu().numpy(),
+             "kv": [(pb.to_host(k), pb.to_host(v)) for k, v in kv]}
+        for r in range(B):
+            assert_ar_request(w, g, inp, st.prm, r, logit_tol(w))
+        acc_o, bon_o = O.verify(g["tokens"].reshape(B, K), inp["target_tokens"])
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_o)
+        np.testing.assert_array_equal(bon.cpu().numpy(), bon_o)
     finally:
         st.close()
 

@@ -195,15 +195,15 @@ def test_dflash_argument_errors_and_empty_batch():
         st.close()
 
 
-@pytest.mark.parametrize("case", ["bf16_padded", "bf16_library"])
+@pytest.mark.parametrize("case", ["bf16_padded", "bf16_large"])
 def test_dflash_step_graph_replays_equal_eager(case):
     """pe_step_graph in DFlash mode (prepare -> inject -> forward -> verify):
     four replays, with eager work and the caches reset between them, each
     equal to the four eager entry points bit for bit (block batch, horizons,
-    injection slots, tokens, logits, verification, KV cache, error word).  The
-    library case (B=40: 320 block rows) runs the block's dense GEMMs through
-    hipBLASLt."""
-    B = 40 if case == "bf16_library" else 5
+    injection slots, tokens, logits, verification, KV cache, error word), and
+    the last replay against the oracle.  The large case (B=40: 320 block rows)
+    runs the block's dense GEMMs on the large-batch 32x32-MFMA tiles."""
+    B = 40 if case == "bf16_large" else 5
     w = SMALL_BF16.with_(K=7, batch=B, accepted="uniform", prefix=("uniform", 40, 400))
     _say(f"dflash graph case {case} B={B} K={w.K}")
     st = Setup(w, 79)
@@ -269,5 +269,25 @@ def test_dflash_step_graph_replays_equal_eager(case):
         if case == "bf16_padded":
             assert eager["error"] == (O.ERR_ACCEPTED, 2)
             assert np.all(eager["tokens"][2 * K:3 * K] == -1)
+        # the graph's outputs against the oracle: block batch, horizons and
+        # injection slots bit for bit, tokens and logits of the round drafted
+        # on the oracle's injected cache, and the greedy verification (the
+        # cache itself equals the eager one above, which _check compares)
+        prec = oracle_precision(w)
+        ob = O.dflash_prepare(inp["verify_positions"], inp["num_accepted"], inp["bonus_tokens"],
+                              inp["block_table"], inp["num_kv_blocks"], w.K, w.vocab, w.mask_id, w.block_size)
+        assert_metadata_equal(batch.host(B, K), ob)
+        np.testing.assert_array_equal(apos.cpu().numpy(), ob["attn_positions"])
+        np.testing.assert_array_equal(inj.cpu().numpy(), ob["inject_slots"])
+        writes = O.dflash_inject(w, inp["verify_positions"], ob["inject_slots"], inp["target_hidden"], inj_w,
+                                 inp["kv"], precision=prec)
+        kv_o = O.apply_writes(inp["kv"], writes, w.block_size, w.dtype)
+        reqs = [0, 1, 3] if case == "bf16_padded" else [0, 17, 39]
+        fw = O.dflash_forward(st.prm, w, ob, kv_o, inp["block_table"], precision=prec, requests=reqs)
+        rows = np.concatenate([np.arange(r * K, (r + 1) * K) for r in reqs])
+        assert_tokens_logits(tok.cpu().numpy()[rows], lg.cpu().numpy()[rows], fw["logits"], logit_tol(w))
+        o_acc, o_bon = O.verify(tok.cpu().numpy().reshape(B, K), inp["target_tokens"])
+        np.testing.assert_array_equal(acc.cpu().numpy(), o_acc)
+        np.testing.assert_array_equal(bon.cpu().numpy(), o_bon)
     finally:
         st.close()

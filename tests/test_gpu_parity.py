@@ -143,12 +143,12 @@ def test_small_bf16_lm_head_tiles_cut_between_waves(d, vocab, B):
 
 
 @pytest.mark.parametrize("K,B,d,seed", [(7, 40, 256, 88), (4, 72, 512, 89), (3, 43, 256, 97), (2, 64, 256, 98)])
-def test_small_bf16_library_gemms(K, B, d, seed):
-    """560, 576, 258 and 256 forward rows: the plain GEMMs run through
-    hipBLASLt; the fc and residual GEMMs write bf16 directly, RoPE/KV write
-    and SiLU.mul run on its fp32 results.  For K >= 3 the first layer's fc
-    and QKV products run on K+2 rows per request (one row for the K-1 MASK
-    slots), K = 2 keeps every slot."""
+def test_small_bf16_large_batch_gemms(K, B, d, seed):
+    """560, 576, 258 and 256 forward rows: the large-batch 32x32-MFMA GEMMs
+    (fc and residual products store from registers, RoPE/KV write and
+    SiLU.mul on split fp32 sums where the tiles are few).  For K >= 3 the
+    first layer's fc and QKV products run on K+2 rows per request (one row
+    for the K-1 MASK slots), K = 2 keeps every slot."""
     w = SMALL_BF16.with_(K=K, batch=B, d=d, weight_std=1 / np.sqrt(d), accepted="uniform",
                          prefix=("uniform", 30, 200))
     _full_check(w, seed)
@@ -246,8 +246,8 @@ def test_padded_request_gets_no_kv_write_and_token_minus_one():
         st.close()
 
 
-def test_padded_request_with_library_gemms():
-    """A padded request among 40 (560 forward rows, library GEMMs with the
+def test_padded_request_with_large_batch_gemms():
+    """A padded request among 40 (560 forward rows, large-batch GEMMs with the
     first layer's MASK slots deduplicated): its slots write no KV and draft
     -1, every other request matches the oracle."""
     w = SMALL_BF16.with_(K=7, batch=40, accepted="uniform", prefix=("uniform", 30, 200))
@@ -372,19 +372,20 @@ def test_closed_loop_rounds():
         st.close()
 
 
-@pytest.mark.parametrize("case", ["bf16", "bf16_padded", "f32", "bf16_library"])
+@pytest.mark.parametrize("case", ["bf16", "bf16_padded", "f32", "bf16_large"])
 def test_step_graph_replays_match_eager(case):
     """One captured graph of the parallel step (preparation and hidden-state
     copy in one launch, forward, argmax and verification in one launch)
     replayed several times, with eager work and synchronization in between;
     every replay equals the four eager entry points bit for bit: batch fields,
     drafter inputs, tokens, logits, verification, KV cache and error word.
-    The library case (280 forward rows) runs its plain GEMMs through
-    hipBLASLt, whose algorithm is chosen by timing before the capture: the
-    choice must be the same, and deterministic, in both."""
+    The last replay is also checked against the oracle directly (the fused
+    preparation + copy and argmax + verification kernels run only in the
+    graph).  The 280-row case runs the large-batch GEMMs with the first
+    layer's MASK slots deduplicated."""
     if case == "f32":
         w = configs.TINY.with_(K=5, batch=3, accepted="uniform", prefix=("uniform", 40, 200))
-    elif case == "bf16_library":
+    elif case == "bf16_large":
         w = SMALL_BF16.with_(K=7, batch=20, accepted="uniform", prefix=("uniform", 40, 400))
     else:
         w = SMALL_BF16.with_(K=7, batch=6, accepted="uniform", prefix=("uniform", 40, 400))
@@ -437,6 +438,17 @@ def test_step_graph_replays_match_eager(case):
         if case == "bf16_padded":
             assert eager["error"] == (1, 2)
             assert np.all(eager["tokens"][2 * K:3 * K] == -1)
+        # the graph's outputs against the oracle
+        ob, ohd, fw = oracle_step(w, st.prm, inp)
+        assert_metadata_equal(batch.host(B, K), ob)
+        np.testing.assert_array_equal(pb.to_host(dh), ohd)
+        keep = np.concatenate([np.arange(r * K, (r + 1) * K) for r in range(B) if ob["seq_lens"][r] > 0])
+        assert_tokens_logits(tok.cpu().numpy(), lg.cpu().numpy(), fw["logits"][keep], logit_tol(w), keep)
+        np.testing.assert_array_equal(tok.cpu().numpy()[np.setdiff1d(np.arange(B * K), keep)], -1)
+        assert_kv(w, [(pb.to_host(k), pb.to_host(v)) for k, v in kv], inp, fw)
+        o_acc, o_bon = O.verify(tok.cpu().numpy().reshape(B, K), inp["target_tokens"])
+        np.testing.assert_array_equal(acc.cpu().numpy(), o_acc)
+        np.testing.assert_array_equal(bon.cpu().numpy(), o_bon)
     finally:
         st.close()
 

@@ -124,16 +124,16 @@ def test_prefill_small_bf16_slot_groups(S, lens, start, seed):
     _check(w, S, lens, start, seed)
 
 
-def test_prefill_library_gemms_d1024():
-    """448 slots of d = 1024: hipBLASLt GEMMs with the fused epilogues, 7 slot
+def test_prefill_large_batch_gemms_d1024():
+    """448 slots of d = 1024: large-batch 32x32-MFMA GEMMs with the fused epilogues, 7 slot
     groups."""
     w = SMALL_BF16.with_(K=7, batch=1, d=1024, mlp=2048, n_q_heads=16, n_kv_heads=2,
                          weight_std=1 / 32)
     _check(w, 448, ("fixed", 442), ("fixed", 37), seed=67)
 
 
-def test_prefill_library_gemms():
-    """640 slots of d = 256: hipBLASLt GEMMs with the fused epilogues, 10 slot
+def test_prefill_large_batch_gemms():
+    """640 slots of d = 256: large-batch 32x32-MFMA GEMMs with the fused epilogues, 10 slot
     groups."""
     w = SMALL_BF16.with_(K=7, batch=1, n_q_heads=8, n_kv_heads=1)
     _check(w, 640, ("fixed", 600), ("fixed", 21), seed=72)
