@@ -211,3 +211,86 @@ def test_draft_forward_sampled_matches_oracle(T):
         assert compared >= B * K // 2
     finally:
         st.close()
+
+
+def test_verify_sampled_full_vocabulary():
+    """The 20B-class vocabulary (201088 tokens: each row's log-sum-exp and
+    draws run over all of its slices, the trip count bench.py times) against
+    the oracle on the same fp32 logits and Philox keys."""
+    V, B, K, T = 201088, 6, 7, 1.0
+    w = SMALL_BF16.with_(K=K, batch=B, vocab=V)
+    st = Setup(w, 94)
+    try:
+        compared = skipped = 0
+        for seed in (31, 32):
+            zq, zp = _logits(B, K, V, seed, 0.95)
+            tokens = O.sample_drafts(zq.reshape(B * K, V), T, seed).reshape(B, K)
+            acc_o, nxt_o = O.rejection_verify(tokens, zq, zp, T, seed)
+            acc_g, nxt_g = _verify_gpu(st.ctx, tokens, zq.reshape(B * K, V), zp.reshape(B * (K + 1), V), T, seed)
+            marg = _margins(tokens, zq, zp, T, seed, acc_o)
+            for r in range(B):
+                if marg[r] < 1e-4:
+                    skipped += 1
+                    continue
+                assert acc_g[r] == acc_o[r], (seed, r, acc_g[r], acc_o[r])
+                sc = _emit_scores(zq, zp, T, seed, r, acc_o[r])
+                srt = np.sort(sc[np.isfinite(sc)])
+                if len(srt) > 1 and srt[-1] - srt[-2] > 1e-3:
+                    assert nxt_g[r] == nxt_o[r], (seed, r)
+                else:
+                    assert sc[nxt_g[r]] >= srt[-1] - 1e-3
+                compared += 1
+        _say(f"  V={V}: {compared} requests compared, {skipped} near-tie")
+        assert compared >= 10
+    finally:
+        st.close()
+
+
+def test_draft_forward_sampled_full_vocabulary():
+    """Sampled drafting over a 201088-token vocabulary (the LM head's
+    argmax-free path and every draw slice at full size) against the oracle's
+    draws from its own logits."""
+    T = 1.0
+    w = SMALL_BF16.with_(K=7, batch=2, vocab=201088, accepted="uniform", prefix=("uniform", 30, 300),
+                         weight_std=1 / 16)
+    st = Setup(w, 95)
+    try:
+        inp = synth.step_inputs(w, seed=95)
+        seed = 777
+        B, K = w.batch, w.K
+        t = {k: pb.to_device(np.ascontiguousarray(inp[k])) for k in
+             ("verify_tokens", "verify_positions", "num_accepted", "bonus_tokens", "block_table",
+              "target_hidden")}
+        kv = [(pb.to_device(kc), pb.to_device(vc)) for kc, vc in inp["kv"]]
+        batch = pb.Batch(B, K)
+        nkv = int(inp["num_kv_blocks"])
+        pb.pe_prepare(st.ctx, B, t["verify_tokens"], t["verify_positions"], t["num_accepted"],
+                      t["bonus_tokens"], t["block_table"], nkv, batch)
+        dh = torch.zeros((B * 2 * K, w.d), dtype=torch.bfloat16, device="cuda")
+        pb.pe_gather_hidden(st.ctx, B, batch, t["target_hidden"], st.dev["h_shared"], dh)
+        tok = torch.full((B * K,), -7, dtype=torch.int32, device="cuda")
+        lg = torch.zeros((B * K, w.vocab), dtype=torch.float32, device="cuda")
+        pb.pe_draft_forward_sampled(st.ctx, B, batch, dh, t["block_table"], nkv, [k for k, _ in kv],
+                                    [v for _, v in kv], T, _seed_dev(seed), tok, lg)
+        torch.cuda.synchronize()
+        _, _, fw = oracle_step(w, st.prm, inp)
+        ol = fw["logits"]
+        rms = float(np.sqrt(np.mean(ol ** 2)))
+        assert np.max(np.abs(lg.cpu().numpy() - ol)) <= logit_tol(w) * rms
+        want = O.sample_drafts(ol, T, seed)
+        got = tok.cpu().numpy()
+        tol = logit_tol(w) * rms / T
+        V = w.vocab
+        compared = 0
+        for i in range(B * K):
+            sc = ol[i] / T + O.gumbel(O.token_uniforms(seed, O.STREAM_DRAFT, V, i))
+            srt = np.sort(sc)
+            if srt[-1] - srt[-2] > 2 * tol:
+                assert got[i] == want[i], (i, got[i], want[i])
+                compared += 1
+            else:
+                assert sc[got[i]] >= srt[-1] - 2 * tol
+        _say(f"  V={V}: {compared} of {B * K} draws compared exactly")
+        assert compared >= B * K // 2
+    finally:
+        st.close()
