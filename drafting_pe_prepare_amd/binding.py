@@ -25,7 +25,7 @@ EXPORTS = ("pe_create", "pe_destroy", "pe_set_stream", "pe_prepare", "pe_gather_
            "pe_draft_forward", "pe_ar_draft", "pe_verify", "pe_prefill_prepare", "pe_prefill_gather",
            "pe_prefill_forward", "pe_draft_forward_sampled", "pe_verify_sampled", "pe_choose_depth",
            "pe_dflash_prepare", "pe_dflash_inject", "pe_dflash_forward", "pe_step_graph",
-           "pe_step_graph_stats", "pe_get_device_error",
+           "pe_step_graph_stats", "pe_verify_sampled_noalloc", "pe_get_device_error",
            "pe_profile_enable", "pe_profile_read", "pe_last_error", "pe_status_string")
 PHASES = ("prepare", "gather", "fc", "norm", "qkv", "attn", "o", "gateup", "down", "lmhead",
           "verify", "argmax", "ar")
@@ -112,6 +112,7 @@ def load(path: str = LIB_PATH):
                                     ctypes.c_double, P(i32), P(ctypes.c_double)]
     lib.pe_step_graph.argtypes = [vp, i32, P(PeStepArgs)]
     lib.pe_step_graph_stats.argtypes = [vp, P(ctypes.c_int64), P(ctypes.c_int64)]
+    lib.pe_verify_sampled_noalloc.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
     lib.pe_get_device_error.argtypes = [vp, P(ctypes.c_uint32), P(i32)]
     lib.pe_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.pe_profile_read.argtypes = [vp, P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int]
@@ -356,6 +357,15 @@ def make_dflash_step_args(verify_positions, num_accepted, bonus_tokens, block_ta
 
 def pe_step_graph(ctx: Context, B, args: PeStepArgs):
     _check(_lib.pe_step_graph(ctx.h, B, ctypes.byref(args)))
+
+
+def pe_verify_sampled_noalloc(B, K, vocab, draft_tokens, draft_logits, target_logits, temperature, seed,
+                              num_accepted, next_tokens, stream=None):
+    """pe_verify_sampled without a context or allocation; stream: a
+    torch.cuda.Stream, or None for torch's current stream."""
+    _check(_lib.pe_verify_sampled_noalloc(B, K, vocab, _ptr(draft_tokens), _ptr(draft_logits),
+                                          _ptr(target_logits), ctypes.c_float(temperature), _ptr(seed),
+                                          _ptr(num_accepted), _ptr(next_tokens), _stream_handle(stream)))
 
 
 def pe_step_graph_stats(ctx: Context):

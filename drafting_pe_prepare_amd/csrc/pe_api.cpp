@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1017,6 +1018,74 @@ pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens,
                                    target_logits, seed, ctx->sample_lse, ctx->sample_parts, ctx->sample_keys,
                                    num_accepted,
                                    next_tokens, ctx->stream),
+         "sampled verify launch");
+  return PE_OK;
+}
+
+}  // extern "C"
+
+// ---- sampled verification without allocation --------------------------------
+// Workspace of pe_verify_sampled_noalloc in a file-scope device array (one copy
+// per GPU, held until the process ends): partial argmax keys [B * kSampleParts]
+// u64, then per-slice (max, sum exp) [rows * kLseParts * 2] and per-row
+// log-sum-exp [rows] fp32, rows = B (2K + 1).
+namespace {
+constexpr int kNaMaxRows = 8192;  // B (2K + 1)
+constexpr int kNaMaxReq = 2048;   // B
+constexpr size_t kNaKeyBytes = size_t(kNaMaxReq) * pe::kSampleParts * 8;
+constexpr size_t kNaPartBytes = size_t(kNaMaxRows) * pe::kLseParts * 2 * 4;
+constexpr size_t kNaLseBytes = size_t(kNaMaxRows) * 4;
+constexpr int kNaMaxDevices = 64;
+std::mutex g_na_mu;
+void* g_na_ptr[kNaMaxDevices] = {};  // device address of `scratch` on each device, once looked up
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNaKeyBytes + kNaPartBytes + kNaLseBytes];
+
+// The device address of this GPU's `scratch`: host code must use it, never the
+// array's name (a host-side stand-in).  Looked up once per device, with that
+// device current.
+static pe_status noalloc_scratch(void** out) {
+  int dev = 0;
+  PE_HIP(hipGetDevice(&dev), "current device");
+  if (dev < 0 || dev >= kNaMaxDevices) return fail(PE_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_na_mu);
+  if (!g_na_ptr[dev]) {
+    void* p = nullptr;
+    PE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address");
+    if (!p) return fail(PE_ERR_HIP, "scratch address is NULL");
+    g_na_ptr[dev] = p;
+  }
+  *out = g_na_ptr[dev];
+  return PE_OK;
+}
+
+extern "C" {
+
+pe_status pe_verify_sampled_noalloc(int32_t B, int32_t K, int32_t vocab, const int32_t* draft_tokens,
+                                    const float* draft_logits, const float* target_logits, float temperature,
+                                    const uint64_t* seed, int32_t* num_accepted, int32_t* next_tokens,
+                                    void* stream) {
+  g_err.clear();
+  if (B < 0 || K < 1 || K > 32) return fail(PE_ERR_INVALID_ARG, "B=%d K=%d (B >= 0, 1 <= K <= 32)", B, K);
+  if (vocab < 4 || vocab % 4) return fail(PE_ERR_INVALID_ARG, "vocab=%d must be a positive multiple of 4", vocab);
+  if (B > kNaMaxReq || (long long)B * (2 * K + 1) > kNaMaxRows)
+    return fail(PE_ERR_UNSUPPORTED, "B=%d, K=%d: beyond the fixed workspace (B <= %d, B (2K+1) <= %d)", B, K,
+                kNaMaxReq, kNaMaxRows);
+  pe_status s = check_sampling(temperature, seed);
+  if (s != PE_OK || B == 0) return s;
+  if (!draft_tokens || !num_accepted || !next_tokens) return fail(PE_ERR_INVALID_ARG, "a verify buffer is NULL");
+  if (!draft_logits || !target_logits || !aligned(draft_logits, 16) || !aligned(target_logits, 16))
+    return fail(PE_ERR_INVALID_ARG, "logit rows NULL or not 16-byte aligned");
+  void* base = nullptr;
+  if ((s = noalloc_scratch(&base)) != PE_OK) return s;
+  unsigned char* b = static_cast<unsigned char*>(base);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(b);
+  float* parts = reinterpret_cast<float*>(b + kNaKeyBytes);
+  float* lse = reinterpret_cast<float*>(b + kNaKeyBytes + kNaPartBytes);
+  PE_HIP(pe::launch_verify_sampled(B, K, vocab, 1.f / temperature, draft_tokens, draft_logits, target_logits, seed,
+                                   lse, parts, keys, num_accepted, next_tokens,
+                                   reinterpret_cast<hipStream_t>(stream)),
          "sampled verify launch");
   return PE_OK;
 }

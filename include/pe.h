@@ -371,6 +371,23 @@ pe_status pe_verify_sampled(pe_ctx* ctx, int32_t B, const int32_t* draft_tokens,
                             const float* draft_logits, const float* target_logits, float temperature,
                             const uint64_t* seed, int32_t* num_accepted, int32_t* next_tokens);
 
+/* Verification by rejection sampling that allocates nothing, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same inputs, outputs and results as
+ * pe_verify_sampled, but no context: K (1..32) and vocab (a multiple of 4) are
+ * arguments, and the work runs on `stream` (a hipStream_t, NULL = the default
+ * stream).  Its workspace (per-row log-sum-exp, per-slice partials, draw keys)
+ * is a fixed device array of the library, about 2.1 MB per GPU, held until
+ * the process ends: B <= 2048 and B*(2K+1) <= 8192, else PE_ERR_UNSUPPORTED
+ * and nothing is launched.  Every call on one GPU uses that GPU's one
+ * workspace: calls that overlap on a GPU (other streams, other threads) race
+ * and must be serialized by the caller.  Argument errors as pe_verify_sampled;
+ * no implicit synchronization. */
+pe_status pe_verify_sampled_noalloc(int32_t B, int32_t K, int32_t vocab, const int32_t* draft_tokens,
+                                    const float* draft_logits, const float* target_logits, float temperature,
+                                    const uint64_t* seed, int32_t* num_accepted, int32_t* next_tokens,
+                                    void* stream);
+
 /* Draft depth selection [P1, Speculative depth efficiency: throughput peaks
  * at the depth where more accepted drafts stop paying for a deeper draft; P2,
  * Limits of autoregressive drafting: the speculation length is tuned to the
