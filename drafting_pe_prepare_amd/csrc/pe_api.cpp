@@ -570,7 +570,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   // one MASK slot), the norm writes the fc rows out to every slot, and the QKV
   // epilogue (RoPE at each slot's own position, KV write) runs for every slot.
   const int Kc = k.K, Rc = B * (Kc + 2);
-  const bool dd = P.parallel_layout && dt == PE_BF16 && ctx->xc && Kc >= 3 && Rc > 64;
+  const bool dd = P.parallel_layout && dt == PE_BF16 && ctx->xc && Kc >= 3 && Rc > pe::kMmMinRows;
 
   if (P.embed_input) {
     Timed tm(ctx, PE_PH_GATHER);

@@ -610,6 +610,8 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
     if (nt >= tail0) return;  // padding workgroup of the XCD-aligned grid
   }
   const int m0 = mt * BM, n0 = nt * BN;
+  // rows of inactive requests (occupancy below the captured batch) are skipped
+  if (m0 >= active_rows(g.nact, g.rpr, g.M)) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
   const int wm = w / WN, wn = w % WN;
 
@@ -962,11 +964,10 @@ static Variant pick(int epi, int M, int N, int K, int num_cus) {
   return tiles > num_cus ? V_D128S2 : V_D64;
 }
 constexpr int kArgmaxBN = 256;  // columns per tile of every tiled LM-head variant
-constexpr int kMmMinRows = 64;  // larger products run on the 32x32 tiles of pe_mm.hip
 
 int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus) {
   if (dtype != 1) return (N + 31) / 32;
-  if (M > kMmMinRows) return mm_argmax_parts(M, N);
+  if (M > kMmLmMinRows) return mm_argmax_parts(M, N);
   switch (pick(E_ARGMAX, M, N, K, num_cus)) {
     case V_WIDE: return std::min(num_cus, N / 16);
     case V_SKINNY: return (N + 15) / 16;
@@ -1256,7 +1257,7 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
 
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
-  if (g.M > kMmMinRows) return launch_mm(AL, BMAP, EPI, g, num_cus, st);
+  if (g.M > (EPI == E_ARGMAX ? kMmLmMinRows : kMmMinRows)) return launch_mm(AL, BMAP, EPI, g, num_cus, st);
   if (g.dedup_k) return hipErrorInvalidValue;  // compact first-layer rows: large batches only
   const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);
   if constexpr (EPI == E_ARGMAX) {

@@ -187,6 +187,18 @@ struct AttnArgs {
   int slots;                      // workgroups resident at once (2 per CU)
 };
 // ---- large-batch dense products and LM head (more than 64 rows) -------------
+// Dense products with more rows than PE_MM_MIN_ROWS run on launch_mm, smaller
+// ones on the kernels of pe_gemm.hip.  The LM head runs on launch_mm only above
+// PE_MM_LM_MIN_ROWS: by default never, since at 448 rows x 201088 x 2880 the
+// 16x16x32 ring of pe_gemm.hip (224 x 256 tiles) measured 524-532 us against
+// 572-684 us for the best 32x32x16 tiles of launch_mm on the same GPU.
+#ifndef PE_MM_MIN_ROWS
+#define PE_MM_MIN_ROWS 64
+#endif
+#ifndef PE_MM_LM_MIN_ROWS
+#define PE_MM_LM_MIN_ROWS (1 << 30)
+#endif
+constexpr int kMmMinRows = PE_MM_MIN_ROWS, kMmLmMinRows = PE_MM_LM_MIN_ROWS;
 // 32x32x16 MFMA tiles; QKV and gate/up pair their epilogue columns 32 apart
 // (see pe_mm.hip).  E_QKV runs on fp32 sums (g.part); with g.dedup_k the
 // product covers the K+2 compact rows per request and the epilogue every slot.
