@@ -967,7 +967,6 @@ constexpr int kArgmaxBN = 256;  // columns per tile of every tiled LM-head varia
 
 int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus) {
   if (dtype != 1) return (N + 31) / 32;
-  if (M > kMmLmMinRows) return mm_argmax_parts(M, N);
   switch (pick(E_ARGMAX, M, N, K, num_cus)) {
     case V_WIDE: return std::min(num_cus, N / 16);
     case V_SKINNY: return (N + 15) / 16;
@@ -1257,7 +1256,7 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
 
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
-  if (g.M > (EPI == E_ARGMAX ? kMmLmMinRows : kMmMinRows)) return launch_mm(AL, BMAP, EPI, g, num_cus, st);
+  if (EPI != E_ARGMAX && g.M > kMmMinRows) return launch_mm(AL, BMAP, EPI, g, num_cus, st);
   if (g.dedup_k) return hipErrorInvalidValue;  // compact first-layer rows: large batches only
   const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);
   if constexpr (EPI == E_ARGMAX) {

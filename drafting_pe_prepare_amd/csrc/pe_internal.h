@@ -186,26 +186,19 @@ struct AttnArgs {
   int grid;                       // persistent grid size
   int slots;                      // workgroups resident at once (2 per CU)
 };
-// ---- large-batch dense products and LM head (more than 64 rows) -------------
+// ---- large-batch dense products (more than 64 rows) --------------------------
 // Dense products with more rows than PE_MM_MIN_ROWS run on launch_mm, smaller
-// ones on the kernels of pe_gemm.hip.  The LM head runs on launch_mm only above
-// PE_MM_LM_MIN_ROWS: by default never, since at 448 rows x 201088 x 2880 the
-// 16x16x32 ring of pe_gemm.hip (224 x 256 tiles) measured 524-532 us against
-// 572-684 us for the best 32x32x16 tiles of launch_mm on the same GPU.
+// ones on the kernels of pe_gemm.hip.  The LM head stays on pe_gemm.hip at
+// every size: at 448 rows x 201088 x 2880 its 16x16x32 ring (224 x 256 tiles)
+// measured 524-568 us against 572-692 us for the best 32x32x16 tiles.
 #ifndef PE_MM_MIN_ROWS
 #define PE_MM_MIN_ROWS 64
 #endif
-#ifndef PE_MM_LM_MIN_ROWS
-#define PE_MM_LM_MIN_ROWS (1 << 30)
-#endif
-constexpr int kMmMinRows = PE_MM_MIN_ROWS, kMmLmMinRows = PE_MM_LM_MIN_ROWS;
+constexpr int kMmMinRows = PE_MM_MIN_ROWS;
 // 32x32x16 MFMA tiles; QKV and gate/up pair their epilogue columns 32 apart
 // (see pe_mm.hip).  E_QKV runs on fp32 sums (g.part); with g.dedup_k the
 // product covers the K+2 compact rows per request and the epilogue every slot.
 hipError_t launch_mm(int aload, int bmap, int epi, const GemmArgs& g, int num_cus, hipStream_t st);
-// Partial argmax keys per row of the LM head of launch_mm over M draft rows
-// and N vocabulary rows (one per vocabulary tile).
-int mm_argmax_parts(int M, int N);
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 // Context length of each group of Sv consecutive slots (vpr groups per

@@ -1,9 +1,9 @@
 // Dense contractions of the drafter at larger batch (more than 64 rows):
-// out[m, n] = sum_k A[m, k] W[n, k] with a fused epilogue, and the LM head with
-// its row argmax.  "P-EAGLE: parallel speculative decoding in vLLM",
-// Architecture and mechanism, Step 2: fc over concat(emb, h), the N-layer
-// Transformer and the LM head, over all K positions of every request in one
-// pass.  At c=64 and beyond these are the step's matrix-core work.
+// out[m, n] = sum_k A[m, k] W[n, k] with a fused epilogue.  "P-EAGLE: parallel
+// speculative decoding in vLLM", Architecture and mechanism, Step 2: fc over
+// concat(emb, h) and the N-layer Transformer, over all K positions of every
+// request in one pass.  (The LM head runs on the 16x16x32 ring of
+// pe_gemm.hip, which measured faster on its shape.)
 //
 // gfx950 design
 //  * v_mfma_f32_32x32x16_bf16.  Measured on this chip, the 32x32x16 form
@@ -18,10 +18,6 @@
 //    banks), and under this swizzle the 16 rows a fragment read touches per
 //    clock fall on distinct banks (measured 218 B/clk/CU against 124 with
 //    the 128-byte c ^ (r & 7) swizzle).
-//  * The LM head runs transposed: W_lm rows (vocabulary) are the tile rows and
-//    the draft rows are the tile columns, so every lane holds 16 vocabulary
-//    entries of one draft row and the row argmax is a per-lane max plus one
-//    cross-half exchange; logits never reach memory unless asked for.
 //  * Column pairs an epilogue needs together (rotate-half RoPE partners, gate
 //    and up) sit 32 logical columns apart in one 64-column block, i.e. in the
 //    same lane of two neighbouring 32x32 tiles.  For QKV that is the plain
@@ -74,10 +70,6 @@ __device__ __forceinline__ const uint16_t* mm_weight_row(const GemmArgs& g, int 
 __device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
 }
-// The same with the non-temporal cache policy (data read once).
-__device__ __forceinline__ void dma16_nt(const uint16_t* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds) : "memory");
-}
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
   return uint32_t(uintptr_t((__attribute__((address_space(3))) const unsigned char*)p));
 }
@@ -88,8 +80,6 @@ __device__ __forceinline__ int dedup_slot(int m, int K) { return (m / (K + 2)) *
 
 // ---------------------------------------------------------------------------
 // The tiled kernel.  BM x BN output tile, WM x WN waves of (BM/WM) x (BN/WN).
-// TRANS: the LM head -- tile rows are W rows (vocabulary, g.N of them), tile
-// columns are the rows of A (draft rows, g.M); EPI is then E_ARGMAX.
 // KT: k-tile width (64: 128-byte stage rows, 32: 64-byte rows); S: stages in
 // the LDS ring, so S-1 k-tiles are in flight while one is consumed.
 // E_PART: the grid holds g.ksplit copies of the tile grid, copy s summing
@@ -103,7 +93,7 @@ __device__ __forceinline__ int mm_swz(int r) {
   return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
-template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, bool TRANS, int KT, int S, int OCC>
+template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int KT, int S, int OCC>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
   constexpr int NW = WM * WN;
@@ -122,23 +112,17 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
   __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE], st1[STAGE], st2[S > 2 ? STAGE : 16],
       st3[S > 3 ? STAGE : 16], st4[S > 4 ? STAGE : 16];
 
-  const int Mk = TRANS ? g.N : g.M, Nk = TRANS ? g.M : g.N;
+  const int Mk = g.M, Nk = g.N;
   int bid = blockIdx.x, ks = 0, mt, nt;
   const int ksplit = EPI == E_PART ? g.ksplit : 1;
   if (EPI == E_PART) {
-    const int per = TRANS ? ntiles * ((mtiles + 7) / 8) * 8 : mtiles * ((ntiles + 7) / 8) * 8;
+    const int per = mtiles * ((ntiles + 7) / 8) * 8;
     ks = bid / per;
     bid -= ks * per;
   }
-  // workgroups that share an operand tile run back to back on one XCD
-  // (workgroup b runs on XCD b % 8): the weight tile of a dense product, the
-  // vocabulary tile of the LM head
-  if (TRANS) {
-    const int j = bid >> 3;
-    nt = j % ntiles;
-    mt = (j / ntiles) * 8 + (bid & 7);
-    if (mt >= mtiles) return;
-  } else {
+  // workgroups that share a weight tile run back to back on one XCD
+  // (workgroup b runs on XCD b % 8)
+  {
     const int j = bid >> 3;
     mt = j % mtiles;
     nt = (j / mtiles) * 8 + (bid & 7);
@@ -146,7 +130,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
   }
   const int m0 = mt * BM, n0 = nt * BN;
   // rows of inactive requests (occupancy below the captured batch) are skipped
-  if (TRANS ? n0 >= active_rows(g.nact, g.rpr, Nk) : m0 >= active_rows(g.nact, g.rpr, Mk)) return;
+  if (m0 >= active_rows(g.nact, g.rpr, Mk)) return;
   const int nkt = g.K / KT;
   const int kb = ks * nkt / ksplit, nk = (ks + 1) * nkt / ksplit - kb;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -173,10 +157,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
     const int c = ((l % CPR) ^ mm_swz<RB>(r)) * 8;
     if (isa) {
       const int m = min(m0 + r, Mk - 1);
-      if (TRANS) {
-        lo[q] = mm_weight_row<B_PLAIN>(g, m) + c;
-        hi[q] = lo[q];
-      } else if (AL == A_FC) {
+      if (AL == A_FC) {
         const int sl = g.dedup_k ? dedup_slot(m, g.dedup_k) : m;
         int id = g.ids[sl];
         id = id < 0 ? 0 : (id >= g.vocab ? g.vocab - 1 : id);
@@ -188,8 +169,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
       }
     } else {
       const int n = min(n0 + r - BM, Nk - 1);
-      if (TRANS) lo[q] = (const uint16_t*)g.A + (long long)n * g.lda + c;
-      else lo[q] = mm_weight_row<BMAP>(g, n) + c;
+      lo[q] = mm_weight_row<BMAP>(g, n) + c;
     }
   }
   auto issue = [&](unsigned char* st, int kt) {
@@ -198,11 +178,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       if (q < QA) {
-        const uint16_t* src = (AL == A_FC && !TRANS && k0 >= g.d) ? hi[q] + k0 : lo[q] + k0;
-        // the LM head's weights stream once per launch: non-temporal, so they
-        // do not push the draft rows and the layer weights out of the caches
-        if (TRANS) dma16_nt(src, sb + dst[q]);
-        else dma16(src, sb + dst[q]);
+        dma16((AL == A_FC && k0 >= g.d) ? hi[q] + k0 : lo[q] + k0, sb + dst[q]);
       } else {
         dma16(lo[q] + k0, sb + dst[q]);
       }
@@ -294,43 +270,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
 
   // lane l holds C[32 i + 8 (r/4) + 4 (l/32) + r%4][32 j + l%32] of the wave tile
   const int rbase = wm * WTM + 4 * (l >> 5), cbase = wn * WTN + (l & 31);
-  if constexpr (EPI == E_ARGMAX) {
-    static_assert(TRANS, "the LM head runs transposed");
-    // column = draft row n, tile rows = vocabulary entries m
-    __syncthreads();  // every fragment read is done and no DMA is in flight: the stages are free
-    uint64_t* s_best = reinterpret_cast<uint64_t*>(st0);  // [WM][BN]
-    static_assert(WM * BN * 8 <= STAGE, "argmax scratch fits one stage");
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = n0 + cbase + 32 * j;
-      uint64_t best = 0ull;
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
-          if (m < Mk) {
-            if (g.logits && n < Nk) g.logits[(long long)n * g.ldl + m] = acc[i][j][r];
-            const uint64_t k = argmax_key(acc[i][j][r], m);
-            best = k > best ? k : best;
-          }
-        }
-      const uint32_t olo = __shfl_xor(uint32_t(best), 32, 64), ohi = __shfl_xor(uint32_t(best >> 32), 32, 64);
-      const uint64_t other = (uint64_t(ohi) << 32) | olo;
-      best = other > best ? other : best;
-      if (l < 32) s_best[wm * BN + cbase + 32 * j] = best;
-    }
-    __syncthreads();
-    for (int c = tid; c < BN; c += 64 * NW) {
-      const int n = n0 + c;
-      if (n < Nk) {
-        uint64_t b = s_best[c];
-#pragma unroll
-        for (int v = 1; v < WM; ++v) b = s_best[v * BN + c] > b ? s_best[v * BN + c] : b;
-        g.keys[(long long)n * g.parts + mt] = b;
-      }
-    }
-  } else if constexpr (EPI == E_PART) {
+  if constexpr (EPI == E_PART) {
     float* P = g.part + (long long)ks * g.M * g.N;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -381,7 +321,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
         }
       }
   } else {
-    static_assert(EPI == E_PART, "epilogues: argmax, partial sums, store, residual, SiLU.mul");
+    static_assert(EPI == E_PART, "epilogues: partial sums, store, residual, SiLU.mul");
   }
 }
 
@@ -500,68 +440,19 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-#ifndef PE_MM_LM_VARIANT
-#define PE_MM_LM_VARIANT 1
-#endif
-#ifndef PE_MM_DENSE_VARIANT
-#define PE_MM_DENSE_VARIANT 0
-#endif
+// Dense tiles.  The default is 128 x 128 (four waves of 64 x 64, two
+// workgroups per CU).  256 x 256 tiles (eight waves of 128 x 64, one
+// workgroup per CU) move half the operand bytes per flop through the caches;
+// measured at c=64 they pay off only for gate/up (896 x 15360 x 2880: 90 us
+// against 102), where they still fill the chip: the other products, with
+// 2880-5120 output columns, run 20-30% slower on them (fewer, split tiles).
+struct TileSmall { static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, WGPC = 2; };
+struct TileLarge { static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, WGPC = 1; };
+constexpr int kDKT = 64, kDS = 2;
 
-// LM head tiles (transposed): BM vocabulary rows x BN draft rows.
-struct LmTile { int bm, bn; };
-static LmTile mm_lm_tile(int D) {
-#if PE_MM_LM_VARIANT == 0 || PE_MM_LM_VARIANT == 4
-  if (D > 256) return {128, 448};
-#elif PE_MM_LM_VARIANT == 3
-  if (D > 256) return {256, 160};
-#else
-  if (D > 256) return {256, 224};
-#endif
-  if (D > 128) return {128, 256};
-  return {128, 128};
-}
-
-int mm_argmax_parts(int M, int N) { return (N + mm_lm_tile(M).bm - 1) / mm_lm_tile(M).bm; }
-
-template <int BM, int BN, int WM, int WN, int KT, int S>
-static hipError_t mm_lm(const GemmArgs& g, hipStream_t st) {
-  const int mtiles = (g.N + BM - 1) / BM, ntiles = (g.M + BN - 1) / BN;
-  if (g.parts != mtiles) return hipErrorInvalidValue;
-  const int grid = ntiles * ((mtiles + 7) / 8) * 8;
-  hipLaunchKernelGGL((mm_kernel<E_ARGMAX, A_PLAIN, B_PLAIN, BM, BN, WM, WN, true, KT, S, WM * WN / 4>), dim3(grid),
-                     dim3(64 * WM * WN), 0, st, g, mtiles, ntiles);
-  return hipGetLastError();
-}
-
-static hipError_t mm_lm_any(const GemmArgs& g, hipStream_t st) {
-  const LmTile t = mm_lm_tile(g.M);
-  if (t.bn == 128) return mm_lm<128, 128, 4, 2, 64, 2>(g, st);
-  if (t.bn == 256) return mm_lm<128, 256, 4, 2, 64, 2>(g, st);
-#if PE_MM_LM_VARIANT == 0
-  return mm_lm<128, 448, 4, 2, 64, 2>(g, st);
-#elif PE_MM_LM_VARIANT == 1
-  return mm_lm<256, 224, 8, 1, 32, 4>(g, st);
-#elif PE_MM_LM_VARIANT == 2
-  return mm_lm<256, 224, 8, 1, 32, 5>(g, st);
-#elif PE_MM_LM_VARIANT == 3
-  return mm_lm<256, 160, 8, 1, 64, 3>(g, st);
-#else
-  return mm_lm<128, 448, 4, 2, 32, 4>(g, st);
-#endif
-}
-
-// Dense tiles: 128 x 128, four waves of 64 x 64.
-#if PE_MM_DENSE_VARIANT == 0
-constexpr int kDKT = 64, kDS = 2, kDWgPerCu = 2;
-#elif PE_MM_DENSE_VARIANT == 1
-constexpr int kDKT = 64, kDS = 3, kDWgPerCu = 1;
-#else
-constexpr int kDKT = 32, kDS = 4, kDWgPerCu = 2;
-#endif
-
-template <int EPI, int AL, int BMAP>
+template <int EPI, int AL, int BMAP, class T>
 static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
-  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
+  constexpr int BM = T::BM, BN = T::BN, WM = T::WM, WN = T::WN, kDWgPerCu = T::WGPC;
   const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN, nk = g.K / kDKT;
   const long long tiles = (long long)mtiles * ntiles, slots = (long long)kDWgPerCu * num_cus;
   // the QKV epilogue always runs on fp32 sums (one split at least); other
@@ -580,7 +471,7 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
   const long long per = (long long)mtiles * ((ntiles + 7) / 8) * 8;
   if constexpr (EPI != E_QKV) {
     if (ks == 1) {
-      hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, false, kDKT, kDS, 2>), dim3(unsigned(per)),
+      hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, kDKT, kDS, 2>), dim3(unsigned(per)),
                          dim3(64 * WM * WN), 0, st, g, mtiles, ntiles);
       return hipGetLastError();
     }
@@ -588,7 +479,7 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
   if (!g.part || (long long)g.M * g.N * ks > g.part_cap) return hipErrorInvalidValue;
   GemmArgs gp = g;
   gp.ksplit = int(ks);
-  hipLaunchKernelGGL((mm_kernel<E_PART, AL, BMAP, BM, BN, WM, WN, false, kDKT, kDS, 2>), dim3(unsigned(per * ks)),
+  hipLaunchKernelGGL((mm_kernel<E_PART, AL, BMAP, BM, BN, WM, WN, kDKT, kDS, 2>), dim3(unsigned(per * ks)),
                      dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -601,16 +492,18 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
 hipError_t launch_mm(int aload, int bmap, int epi, const GemmArgs& g, int num_cus, hipStream_t st) {
   if (g.M <= 0) return hipSuccess;
   if (g.K % 64) return hipErrorInvalidValue;  // whole 64-wide k-tiles (and fc halves)
-  if (epi == E_ARGMAX) {
-    if (aload != A_PLAIN || bmap != B_PLAIN) return hipErrorInvalidValue;
-    return mm_lm_any(g, st);
-  }
   if (g.N % 64) return hipErrorInvalidValue;  // whole 64-column pair blocks
-  if (aload == A_FC && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_FC, B_PLAIN>(g, num_cus, st);
-  if (aload == A_PLAIN && bmap == B_QKV && epi == E_QKV) return mm_dense<E_QKV, A_PLAIN, B_QKV>(g, num_cus, st);
-  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_RESID) return mm_dense<E_RESID, A_PLAIN, B_PLAIN>(g, num_cus, st);
-  if (aload == A_PLAIN && bmap == B_GATEUP && epi == E_SILU) return mm_dense<E_SILU, A_PLAIN, B_GATEUP>(g, num_cus, st);
-  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_PLAIN, B_PLAIN>(g, num_cus, st);
+  using S = TileSmall;
+  if (aload == A_FC && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_FC, B_PLAIN, S>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_QKV && epi == E_QKV) return mm_dense<E_QKV, A_PLAIN, B_QKV, S>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_RESID) return mm_dense<E_RESID, A_PLAIN, B_PLAIN, S>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_GATEUP && epi == E_SILU) {
+    // large tiles while they still cover three quarters of the CUs
+    const long long large = (long long)((g.M + TileLarge::BM - 1) / TileLarge::BM) * ((g.N + TileLarge::BN - 1) / TileLarge::BN);
+    if (4 * large >= 3LL * num_cus) return mm_dense<E_SILU, A_PLAIN, B_GATEUP, TileLarge>(g, num_cus, st);
+    return mm_dense<E_SILU, A_PLAIN, B_GATEUP, S>(g, num_cus, st);
+  }
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_PLAIN, B_PLAIN, S>(g, num_cus, st);
   return hipErrorInvalidValue;
 }
 
