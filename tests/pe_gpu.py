@@ -12,12 +12,19 @@ GAP = 1e-2                                  # top-2 gap above which tokens must 
 
 
 def logit_tol(w):
-    """Logit bound for workload w.  In bf16, once the GPU (fp32
-    accumulation) and the fp64 oracle round one stored value of a row to
-    different neighbours, the row's later bf16 values differ at the one-ulp
-    level; each layer's residual adds contribute independent noise of that
-    size, so the bound grows as sqrt(layers) (measured: ~1% of RMS at one
-    layer, 2.2-3.2% at four).  fp32 rounds nothing and keeps its bound."""
+    """Logit bound for workload w: the stated 2e-2 x RMS in bf16 and 1e-4 x
+    RMS in fp32 for one decoder layer (every 20B-class workload; measured
+    <= 1.5% in bf16, 0.00000 in fp32).
+
+    A relaxation, on record: deeper bf16 drafters are checked at
+    2e-2 x sqrt(layers).  Once the GPU (fp32 accumulation) and the fp64
+    oracle round one stored value of a row to different neighbours, the
+    row's later bf16 values differ at the one-ulp level and the residual
+    stream carries that through every later layer.  Measured: 2.2-2.4% of
+    RMS at three and four layers (d = 256), 2.7-3.2% for the 4-layer
+    d = 2048 K-sweep drafter, which therefore MISSES the stated 2e-2 bound;
+    the widened check keeps its layer loop covered.  fp32 rounds nothing and
+    keeps 1e-4 at any depth."""
     if w.dtype == "bf16":
         return LOGIT_TOL["bf16"] * float(np.sqrt(w.layers))
     return LOGIT_TOL["f32"]
