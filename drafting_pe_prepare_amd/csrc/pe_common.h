@@ -109,6 +109,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 // lgkmcnt(0) only: every LDS read issued so far has returned
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// One LDS-DMA instruction: every lane moves 16 bytes from `src` to LDS byte
+// lds + 16 lane (lds wave-uniform).  Written as inline asm on purpose: the
+// compiler tracks the LDS writes of its own global_load_lds and, unable to
+// tell the stage being read from the stages in flight, waits for every DMA
+// before each LDS read (vmcnt(0) at the top of each k-tile, which drains the
+// ring).  Hidden from it, the DMAs are ordered by the calling kernel's own
+// vmcnt waits (and barriers) only, and the "memory" clobber keeps the
+// compiler from moving LDS reads across a DMA.  The asm writes no register
+// (the data goes to LDS), so no output register can be reused while the load
+// is in flight; it sets m0 and says so.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return uint32_t(uintptr_t((__attribute__((address_space(3))) const unsigned char*)p));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;

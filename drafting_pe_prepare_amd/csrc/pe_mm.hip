@@ -58,21 +58,6 @@ __device__ __forceinline__ const uint16_t* mm_weight_row(const GemmArgs& g, int 
   return (const uint16_t*)g.W0 + (long long)n * K;
 }
 
-// One LDS-DMA instruction: every lane moves 16 bytes from `src` to LDS byte
-// lds + 16 lane (lds wave-uniform).  Written as inline asm on purpose: the
-// compiler tracks the LDS writes of its own global_load_lds and, unable to
-// tell the stage being read from the stages in flight, waits for every DMA
-// before each LDS read (vmcnt(0) at the top of each k-tile, which drains the
-// ring).  Hidden from it, the DMAs are ordered by this file's own vmcnt waits
-// and barriers only.  The asm writes no register (the data goes to LDS), so
-// no output register can be reused while the load is in flight; m0 is set
-// here and read by no other instruction of these kernels.
-__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-  return uint32_t(uintptr_t((__attribute__((address_space(3))) const unsigned char*)p));
-}
 
 // Slot of compact row m of a MASK-deduplicated first layer (K+2 rows per
 // request: copied slots 0..K and one MASK slot).
