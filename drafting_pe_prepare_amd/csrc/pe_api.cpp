@@ -77,6 +77,7 @@ struct pe_ctx {
   int groups_max = 0;            // slot groups the attention buffers are sized for
   void* xc = nullptr;  // [B(K+2), d] first-layer fc output on the MASK-deduplicated rows (bf16)
   float* splitk = nullptr;      // split-K GEMM partials (bf16 storage)
+  int32_t* rmap = nullptr;      // [R] non-rejected slots of a large-batch pass, then their count
   long long splitk_cap = 0;     // floats
   double* rope_turns = nullptr;  // RoPE frequencies in turns per position
   void* lm_packed = nullptr;  // fragment-order copy of the LM head (bf16)
@@ -152,7 +153,7 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->plan_off, c->rope_turns, c->lm_packed, c->splitk, c->group_lens,
+                  c->part_o, c->part_ml, c->plan_off, c->rope_turns, c->lm_packed, c->splitk, c->group_lens, c->rmap,
                   c->sample_lse, c->sample_keys, c->sample_parts};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
@@ -319,6 +320,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {reinterpret_cast<void**>(&c->keys), key_slots * 8, "argmax keys"},
       {reinterpret_cast<void**>(&c->err), 16, "err"},
       {reinterpret_cast<void**>(&c->rope_turns), size_t(k.head_dim / 2) * 8, "rope"},
+      {reinterpret_cast<void**>(&c->rmap), (R + 1) * 4, "row map"},
       {reinterpret_cast<void**>(&c->ar_ids), R1 * 4, "ar ids"},
       {reinterpret_cast<void**>(&c->ar_pos), R1 * 4, "ar positions"},
       {reinterpret_cast<void**>(&c->ar_rows), size_t(k.max_num_seqs) * 4, "ar rows"},
@@ -555,6 +557,15 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   g0.part_cap = ctx->splitk_cap;
   g0.nact = ctx->nact;
   g0.rpr = S;
+  // the large-batch dense products compute only the non-rejected slots: a
+  // rejected slot's outputs are never read (no KV write, no attention, not a
+  // draft row); the map comes from the batch's rejected mask
+  if (dt == PE_BF16 && R > pe::kMmMinRows) {
+    Timed tm(ctx, PE_PH_FC);
+    PE_HIP(pe::launch_compact_rows(R, P.rej, ctx->rmap, ctx->rmap + R, st), "row map");
+    g0.rmap = ctx->rmap;
+    g0.rcount = ctx->rmap + R;
+  }
 
   // a dense GEMM with its fused epilogue
   auto dense = [&](int aload, int bmap, int epi, const pe::GemmArgs& g, const char* what) -> pe_status {
@@ -589,6 +600,8 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.rpr = Kc + 2;
       g.dedup_k = Kc;
       g.out = ctx->xc;
+      g.rmap = nullptr;
+      g.rcount = nullptr;
     }
     if ((ds = dense(pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, "fc")) != PE_OK) return ds;
   }
@@ -618,6 +631,8 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
         g.M = Rc;
         g.rpr = Kc + 2;
         g.dedup_k = Kc;
+        g.rmap = nullptr;
+        g.rcount = nullptr;
       }
       if ((ds = dense(pe::A_PLAIN, pe::B_QKV, pe::E_QKV, g, "qkv")) != PE_OK) return ds;
     }
@@ -713,6 +728,8 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     g.Wp = ctx->lm_packed;
     g.keys = ctx->keys; g.logits = P.logits; g.ldl = P.ldl;
     g.rpr = P.Kd;
+    g.rmap = nullptr;  // draft rows are never rejected
+    g.rcount = nullptr;
     g.parts = pe::gemm_argmax_parts(dt, D, k.vocab, d, ctx->num_cus);
     g.seq_lens = P.seq_lens; g.Kd = P.Kd;
     {

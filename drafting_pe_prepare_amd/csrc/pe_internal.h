@@ -102,6 +102,8 @@ hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void*
 // bf16 RMSNorm of the compact rows of a MASK-deduplicated first layer (K+2
 // per request, see GemmArgs::dedup_k) that also writes each raw row x[m] to
 // its slots of the full layout: x_full[s] = x[dedup_row(s, K)] for all B*2K s.
+// The non-rejected rows of a batch of R slots, in order: rmap[0..*count).
+hipError_t launch_compact_rows(int R, const uint8_t* rejected, int32_t* rmap, int32_t* count, hipStream_t st);
 hipError_t launch_rmsnorm_expand(int rows, int d, const void* x, const void* gain, void* out, void* x_full,
                                  int K, float eps, hipStream_t st);
 
@@ -144,6 +146,12 @@ struct GemmArgs {
   // rows (rpr rows per request) are computed; later rows are inactive padding
   const int32_t* nact;
   int rpr;
+  // row map (large-batch kernels): when set, compact row m < *rcount stands
+  // for row rmap[m] of A and of the output, and rows past *rcount are not
+  // computed (the forward pass maps the non-rejected slots, whose outputs are
+  // the only ones anything reads).  Not combined with dedup_k.
+  const int32_t* rmap;
+  const int32_t* rcount;
 };
 // rows of an M-row operand with rpr rows per request that belong to active requests
 __device__ __forceinline__ int active_rows(const int32_t* nact, int rpr, int M) {

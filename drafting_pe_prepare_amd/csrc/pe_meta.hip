@@ -357,6 +357,39 @@ __global__ __launch_bounds__(256) void verify_kernel(int B, int K, const int32_t
   }
 }
 
+// The non-rejected slots of a batch, in order (the rows the large-batch
+// dense products compute; a rejected slot's outputs are never read: it makes
+// no KV write, attends to nothing and is no draft row).  One 1024-thread
+// workgroup: thread t counts its contiguous run of slots, a block-wide scan
+// gives each run's first output index, then the runs are written.
+__global__ __launch_bounds__(1024) void compact_rows_kernel(int R, const uint8_t* __restrict__ rej,
+                                                            int32_t* __restrict__ rmap, int32_t* __restrict__ count) {
+  __shared__ int s_w[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int per = (R + 1023) / 1024, r0 = min(R, t * per), r1 = min(R, r0 + per);
+  int n = 0;
+  for (int r = r0; r < r1; ++r) n += rej[r] ? 0 : 1;
+  int inc = n;  // inclusive scan inside the wave, then across the 16 waves
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int v = 0; v < w; ++v) base += s_w[v];
+  int at = base + inc - n;
+  for (int r = r0; r < r1; ++r)
+    if (!rej[r]) rmap[at++] = r;
+  if (t == 1023) *count = base + inc;
+}
+
+hipError_t launch_compact_rows(int R, const uint8_t* rejected, int32_t* rmap, int32_t* count, hipStream_t st) {
+  if (R <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, st, R, rejected, rmap, count);
+  return hipGetLastError();
+}
+
 hipError_t launch_verify(int B, int K, const int32_t* t, const int32_t* g, int32_t* acc,
                          int32_t* bonus, const int32_t* nact, hipStream_t st) {
   if (B <= 0) return hipSuccess;

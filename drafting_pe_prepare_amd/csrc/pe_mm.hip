@@ -114,8 +114,11 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
     if (nt >= ntiles) return;
   }
   const int m0 = mt * BM, n0 = nt * BN;
-  // rows of inactive requests (occupancy below the captured batch) are skipped
+  // rows of inactive requests (occupancy below the captured batch) are skipped,
+  // and with a row map the tiles past the mapped rows
   if (m0 >= active_rows(g.nact, g.rpr, Mk)) return;
+  const int cnt = g.rmap ? *g.rcount : Mk;  // rows computed (compact rows with a map)
+  if (m0 >= cnt) return;
   const int nkt = g.K / KT;
   const int kb = ks * nkt / ksplit, nk = (ks + 1) * nkt / ksplit - kb;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -141,7 +144,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
     const int r = RPG * j + l / CPR;
     const int c = ((l % CPR) ^ mm_swz<RB>(r)) * 8;
     if (isa) {
-      const int m = min(m0 + r, Mk - 1);
+      const int m = g.rmap ? g.rmap[min(m0 + r, cnt - 1)] : min(m0 + r, Mk - 1);
       if (AL == A_FC) {
         const int sl = g.dedup_k ? dedup_slot(m, g.dedup_k) : m;
         int id = g.ids[sl];
@@ -262,7 +265,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
-        if (m >= g.M) continue;
+        if (m >= cnt) continue;
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int n = n0 + cbase + 32 * j;
@@ -274,8 +277,9 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
-        if (m >= g.M) continue;
+        const int mc = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+        if (mc >= cnt) continue;
+        const int m = g.rmap ? g.rmap[mc] : mc;
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int n = n0 + cbase + 32 * j;
@@ -294,8 +298,9 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
-        if (m >= g.M) continue;
+        const int mc = m0 + rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+        if (mc >= cnt) continue;
+        const int m = g.rmap ? g.rmap[mc] : mc;
 #pragma unroll
         for (int q = 0; q < TJ / 2; ++q) {
           const int n = n0 + cbase + 64 * q;  // gate column
@@ -322,6 +327,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
 template <int EPI>
 __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, int rpr) {
   rows = active_rows(g.nact, rpr, rows);  // rows of inactive requests are skipped
+  if (g.rmap) rows = min(rows, *g.rcount);  // compact rows: sums at m, output row rmap[m]
   const int KS = g.ksplit;
   const long long MN = (long long)g.M * g.N;
   const long long stride = (long long)gridDim.x * blockDim.x;
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
       const int m = int(e / per_row), n = int(e % per_row) * 8;
       float v[8];
       sum8(m, n, v);
-      const long long o = (long long)m * g.ldo + n;
+      const long long o = (long long)(g.rmap ? g.rmap[m] : m) * g.ldo + n;
       if constexpr (EPI == E_RESID) {
         const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + o);
         const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
@@ -365,15 +371,18 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
       sum8(m, 64 * t + 32 + c0, up);
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = gt[u] / (1.0f + expf(-gt[u])) * up[u];
-      *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)m * g.ldo + 32 * t + c0) = pack8(v);
+      *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)(g.rmap ? g.rmap[m] : m) * g.ldo + 32 * t + c0) =
+          pack8(v);
     }
   } else {
     static_assert(EPI == E_QKV, "split-K epilogues: store, residual, SiLU.mul, QKV");
     constexpr int hd = 64;  // bf16 storage implies head_dim 64 (checked at context creation)
     const int per_row = g.N / 16;  // 8 pairs per thread, 4 per 64-column head
     for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
-      const int m = int(e / per_row), pc = int(e % per_row), nb = (pc >> 2) * 64, c0 = (pc & 3) * 8;
-      const int cm = g.dedup_k ? dedup_row(m, g.dedup_k) : m;
+      const int mr = int(e / per_row), pc = int(e % per_row), nb = (pc >> 2) * 64, c0 = (pc & 3) * 8;
+      // sums of compact row cm, written to slot m
+      const int cm = g.dedup_k ? dedup_row(mr, g.dedup_k) : mr;
+      const int m = g.rmap ? g.rmap[mr] : mr;
       float lo[8], hi[8];
       sum8(cm, nb + c0, lo);
       sum8(cm, nb + 32 + c0, hi);
