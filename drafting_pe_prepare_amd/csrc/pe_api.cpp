@@ -402,7 +402,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       return s;
     }
     // the MASK-deduplicated first-layer fc rows of a parallel step (large batches)
-    if (size_t(k.max_num_seqs) * (k.K + 2) > 64 && k.K >= 3) {
+    if (size_t(k.max_num_seqs) * (k.K + 2) > size_t(pe::kMmMinRows) && k.K >= 3) {
       if ((s = alloc(&c->xc, size_t(k.max_num_seqs) * (k.K + 2) * k.d * 2, "deduplicated fc rows")) != PE_OK) {
         free_ctx(c);
         return s;

@@ -16,9 +16,9 @@
 //  * LM head with M <= 16 rows: lmhead_wide keeps the rows in LDS, gives every
 //    wave whole 16-column tiles over the full K, and keeps a running argmax key
 //    per row in registers -- logits never reach memory unless asked for.
-//  * M > 64: gemm_tiled, 128x128x64 LDS-tiled, double-buffered, 4 waves of
-//    64x64; workgroups that share a weight tile are placed on one XCD (one L2)
-//    back to back.
+//  * 65..256 rows: gemm_tiled, 128x128x64 LDS-tiled, double-buffered, 4 waves
+//    of 64x64; workgroups that share a weight tile are placed on one XCD (one
+//    L2) back to back.  More rows run on pe_mm.hip.
 //  * Epilogues run on an fp32 tile staged in LDS, so every variant shares them.
 //    Column pairs that an epilogue needs together (RoPE rotate-half partners,
 //    gate/up partners) are placed 16 logical columns apart inside one 32-column
@@ -945,7 +945,7 @@ hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_
 //  * Dense, up to 16 rows: split-K over waves (weights from the fragment-order copy).
 //  * Dense, 17..64 rows: tiled 64x128 when there are >= 32 column tiles,
 //    split-K otherwise (few tiles leave most CUs idle).
-//  * Dense, more rows: tiled 128x128 with two stages and two workgroups per CU
+//  * Dense, 65..256 rows (more: pe_mm.hip): tiled 128x128 with two stages and two workgroups per CU
 //    when those tiles outnumber the CUs; otherwise 64x128 tiles (three stages,
 //    two workgroups per CU), which spread a small grid over more CUs (fc, O and
 //    down at c=64, cache-cold weights: 50/38/69 us against 59/43/76 us).

@@ -194,13 +194,15 @@ struct AttnArgs {
   int grid;                       // persistent grid size
   int slots;                      // workgroups resident at once (2 per CU)
 };
-// ---- large-batch dense products (more than 64 rows) --------------------------
+// ---- large-batch dense products (more than 256 rows) -------------------------
 // Dense products with more rows than PE_MM_MIN_ROWS run on launch_mm, smaller
-// ones on the kernels of pe_gemm.hip.  The LM head stays on pe_gemm.hip at
-// every size: at 448 rows x 201088 x 2880 its 16x16x32 ring (224 x 256 tiles)
-// measured 524-568 us against 572-692 us for the best 32x32x16 tiles.
+// ones on the kernels of pe_gemm.hip (the 4-layer d=2048 drafter at 96-224
+// rows: K=5 796 -> 735 us, K=7 815 -> 758 us per step with the 16x16x32 ring
+// of pe_gemm.hip instead of launch_mm).  The LM head stays on pe_gemm.hip at
+// every size: at 448 rows x 201088 x 2880 its ring (224 x 256 tiles) measured
+// 524-568 us against 572-692 us for the best 32x32x16 tiles.
 #ifndef PE_MM_MIN_ROWS
-#define PE_MM_MIN_ROWS 64
+#define PE_MM_MIN_ROWS 256
 #endif
 constexpr int kMmMinRows = PE_MM_MIN_ROWS;
 // 32x32x16 MFMA tiles; QKV and gate/up pair their epilogue columns 32 apart

@@ -1,4 +1,4 @@
-// Dense contractions of the drafter at larger batch (more than 64 rows):
+// Dense contractions of the drafter at larger batch (more than 256 rows):
 // out[m, n] = sum_k A[m, k] W[n, k] with a fused epilogue.  "P-EAGLE: parallel
 // speculative decoding in vLLM", Architecture and mechanism, Step 2: fc over
 // concat(emb, h) and the N-layer Transformer, over all K positions of every

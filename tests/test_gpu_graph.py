@@ -99,13 +99,13 @@ def check_against_oracle(w, prm, inp, g, n, requests=None):
 @pytest.mark.parametrize("case", ["bf16_large", "f32_small"])
 def test_one_capture_serves_every_occupancy(case):
     """Captured once at B = max_num_seqs, replayed at occupancies B, 1, 7, 0
-    and B again.  bf16_large: 20 requests x 14 slots (280 forward rows: the
-    large-batch GEMMs with MASK-deduplicated first layer, 140 draft rows);
+    and B again.  bf16_large: 32 requests x 14 slots (448 forward rows: the
+    large-batch GEMMs with MASK-deduplicated first layer, 224 draft rows);
     request 15 carries an invalid accepted count, reported only while it is
     active.  f32_small: 3 requests of the 64-token fp32 drafter."""
     if case == "bf16_large":
-        w = SMALL_BF16.with_(K=7, batch=20, accepted="uniform", prefix=("uniform", 40, 400))
-        plan = [20, 1, 7, 0, 20]
+        w = SMALL_BF16.with_(K=7, batch=32, accepted="uniform", prefix=("uniform", 40, 400))
+        plan = [32, 1, 7, 0, 32]
         bad = 15
     else:
         w = configs.TINY.with_(K=4, batch=3, accepted="uniform", prefix=("uniform", 40, 200))

@@ -8,7 +8,7 @@ Two relaxations of the stated criteria, on record (pe_gpu):
     max(1e-2, 2 x the measured max logit error) (about 0.03 at the 20B
     shapes); in the band (1e-2, 2 err] two logits within the error bound can
     change order, so there the GPU token must be near-maximal instead.  The
-    band is counted (246 rows over the GPU suite, 1 drafting the other
+    band is counted (252 rows over the GPU suite, 1 drafting the other
     near-maximal token) and printed at the end of the session;
   * deeper bf16 drafters are checked at 2e-2 x sqrt(layers); the 4-layer
     K-sweep drafter measures 2.7-3.2% of RMS and misses the stated 2e-2."""
@@ -150,13 +150,16 @@ def test_small_bf16_lm_head_tiles_cut_between_waves(d, vocab, B):
     _full_check(w, seed=85 + B)
 
 
-@pytest.mark.parametrize("K,B,d,seed", [(7, 40, 256, 88), (4, 72, 512, 89), (3, 43, 256, 97), (2, 64, 256, 98)])
+@pytest.mark.parametrize("K,B,d,seed", [(7, 40, 256, 88), (4, 72, 512, 89), (3, 60, 256, 99), (3, 43, 256, 97),
+                                        (2, 72, 256, 98)])
 def test_small_bf16_large_batch_gemms(K, B, d, seed):
-    """560, 576, 258 and 256 forward rows: the large-batch 32x32-MFMA GEMMs
-    (fc and residual products store from registers, RoPE/KV write and
-    SiLU.mul on split fp32 sums where the tiles are few).  For K >= 3 the
-    first layer's fc and QKV products run on K+2 rows per request (one row
-    for the K-1 MASK slots), K = 2 keeps every slot."""
+    """560, 576, 360, 258 and 288 forward rows: the large-batch 32x32-MFMA
+    GEMMs (fc and residual products store from registers, RoPE/KV write and
+    SiLU.mul on split fp32 sums where the tiles are few, rejected slots
+    skipped through the row map).  Where the K+2 rows per request of the
+    first layer still exceed 256 (the first three cases) its fc and QKV
+    products run on them (one row for the K-1 MASK slots); 43 requests at
+    K = 3 (215 such rows) and K = 2 keep every slot."""
     w = SMALL_BF16.with_(K=K, batch=B, d=d, weight_std=1 / np.sqrt(d), accepted="uniform",
                          prefix=("uniform", 30, 200))
     _full_check(w, seed)
@@ -389,12 +392,12 @@ def test_step_graph_replays_match_eager(case):
     drafter inputs, tokens, logits, verification, KV cache and error word.
     The last replay is also checked against the oracle directly (the fused
     preparation + copy and argmax + verification kernels run only in the
-    graph).  The 280-row case runs the large-batch GEMMs with the first
+    graph).  The 448-row case runs the large-batch GEMMs with the first
     layer's MASK slots deduplicated."""
     if case == "f32":
         w = configs.TINY.with_(K=5, batch=3, accepted="uniform", prefix=("uniform", 40, 200))
     elif case == "bf16_large":
-        w = SMALL_BF16.with_(K=7, batch=20, accepted="uniform", prefix=("uniform", 40, 400))
+        w = SMALL_BF16.with_(K=7, batch=32, accepted="uniform", prefix=("uniform", 40, 400))
     else:
         w = SMALL_BF16.with_(K=7, batch=6, accepted="uniform", prefix=("uniform", 40, 400))
     st = Setup(w, seed=11)
