@@ -67,8 +67,8 @@ __device__ __forceinline__ int dedup_slot(int m, int K) { return (m / (K + 2)) *
 // The tiled kernel.  BM x BN output tile, WM x WN waves of (BM/WM) x (BN/WN).
 // KT: k-tile width (64: 128-byte stage rows, 32: 64-byte rows); S: stages in
 // the LDS ring, so S-1 k-tiles are in flight while one is consumed.
-// E_PART: the grid holds g.ksplit copies of the tile grid, copy s summing
-// k-tiles [s nk / ksplit, (s+1) nk / ksplit) into fp32 partials.
+// With a split (mm_plan), workgroup b takes copy s = b / per of the tile
+// grid, summing k-tiles [s nk / ks, (s+1) nk / ks) into fp32 partials.
 // ---------------------------------------------------------------------------
 // Stage row r (RB bytes) keeps its 16-byte chunk c at slot c ^ swz(r): the
 // 16 rows one clock of a fragment read touches then fall on distinct banks of
@@ -78,9 +78,39 @@ __device__ __forceinline__ int mm_swz(int r) {
   return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
+// The split of a product over k, chosen from the rows it computes (on the
+// device: with a row map the count is known only there).  T output tiles
+// (column tiles rounded up to whole groups of 8, see the block mapping) run
+// in one round of `slots` workgroups: ks = floor(slots / T) splits, so that
+// T * ks <= slots, at least PE_MM_SPLIT_MIN_KTILES k-tiles each and within the
+// partial-sum buffer (cap_splits copies of [M][N]).  With ks == 1 the kernel
+// runs the fused epilogue itself, unless `force_part` (the QKV product, whose
+// RoPE + KV-write epilogue runs on the fp32 sums).
+struct MmPlan { int mt, per, ks; };
+__host__ __device__ inline MmPlan mm_plan(int rows, int BM, int ntiles, int nkt, int slots, int cap_splits) {
+  MmPlan p;
+  p.mt = (rows + BM - 1) / BM;
+  p.per = p.mt * ((ntiles + 7) / 8) * 8;
+  p.ks = 1;
+  if (p.per > 0 && p.per < slots) {
+    int ks = slots / p.per;
+    const int kmax = nkt / PE_MM_SPLIT_MIN_KTILES;
+    ks = ks < kmax ? ks : kmax;
+    ks = ks < cap_splits ? ks : cap_splits;
+    p.ks = ks > 1 ? ks : 1;
+  }
+  return p;
+}
+// rows the product computes: the active requests' rows, and with a row map
+// the mapped (compact) rows
+__device__ __forceinline__ int mm_rows(const GemmArgs& g) {
+  const int r = active_rows(g.nact, g.rpr, g.M);
+  return g.rmap ? min(r, *g.rcount) : r;
+}
+
 template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int KT, int S, int OCC>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
+void mm_kernel(GemmArgs g, int ntiles, int slots, int cap_splits) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN, TI = WTM / 32, TJ = WTN / 32;
   static_assert(TI * 32 * WM == BM && TJ * 32 * WN == BN, "whole 32x32 tiles per wave");
@@ -98,28 +128,26 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
       st3[S > 3 ? STAGE : 16], st4[S > 4 ? STAGE : 16];
 
   const int Mk = g.M, Nk = g.N;
+  const int cnt = mm_rows(g);  // rows computed (compact rows with a map)
+  const int nkt = g.K / KT;
+  const MmPlan plan = mm_plan(cnt, BM, ntiles, g.K / 64, slots, cap_splits);
+  const bool part = EPI == E_QKV || plan.ks > 1;  // fp32 partial sums instead of the fused epilogue
+  // one item per workgroup: the tiles fit in one round when split
+  // (T * ks <= slots), otherwise the grid covers every tile
   int bid = blockIdx.x, ks = 0, mt, nt;
-  const int ksplit = EPI == E_PART ? g.ksplit : 1;
-  if (EPI == E_PART) {
-    const int per = mtiles * ((ntiles + 7) / 8) * 8;
-    ks = bid / per;
-    bid -= ks * per;
-  }
+  if (bid >= plan.per * plan.ks) return;  // the grid covers the largest plan
+  ks = bid / plan.per;
+  bid -= ks * plan.per;
   // workgroups that share a weight tile run back to back on one XCD
   // (workgroup b runs on XCD b % 8)
   {
     const int j = bid >> 3;
-    mt = j % mtiles;
-    nt = (j / mtiles) * 8 + (bid & 7);
+    mt = j % plan.mt;
+    nt = (j / plan.mt) * 8 + (bid & 7);
     if (nt >= ntiles) return;
   }
   const int m0 = mt * BM, n0 = nt * BN;
-  // rows of inactive requests (occupancy below the captured batch) are skipped,
-  // and with a row map the tiles past the mapped rows
-  if (m0 >= active_rows(g.nact, g.rpr, Mk)) return;
-  const int cnt = g.rmap ? *g.rcount : Mk;  // rows computed (compact rows with a map)
-  if (m0 >= cnt) return;
-  const int nkt = g.K / KT;
+  const int ksplit = plan.ks;
   const int kb = ks * nkt / ksplit, nk = (ks + 1) * nkt / ksplit - kb;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wm = w / WN, wn = w % WN;
@@ -258,7 +286,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
 
   // lane l holds C[32 i + 8 (r/4) + 4 (l/32) + r%4][32 j + l%32] of the wave tile
   const int rbase = wm * WTM + 4 * (l >> 5), cbase = wn * WTN + (l & 31);
-  if constexpr (EPI == E_PART) {
+  if (part) {
     float* P = g.part + (long long)ks * g.M * g.N;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -272,7 +300,9 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
           if (n < g.N) P[(long long)m * g.N + n] = acc[i][j][r];
         }
       }
-  } else if constexpr (EPI == E_STORE || EPI == E_RESID) {
+    return;
+  }
+  if constexpr (EPI == E_STORE || EPI == E_RESID) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -311,7 +341,7 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
         }
       }
   } else {
-    static_assert(EPI == E_PART, "epilogues: partial sums, store, residual, SiLU.mul");
+    static_assert(EPI == E_QKV, "epilogues: partial sums, store, residual, SiLU.mul");
   }
 }
 
@@ -324,11 +354,16 @@ void mm_kernel(GemmArgs g, int mtiles, int ntiles) {
 // position row).  With dedup_k the QKV epilogue covers all `rows` slots of the
 // parallel layout, slot s reading the sums of compact row dedup_row(s).
 // ---------------------------------------------------------------------------
+// The split is the product kernel's (mm_plan over the same arguments); with
+// ks == 1 that kernel ran the epilogue itself and this one has nothing to do.
 template <int EPI>
-__global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, int rpr) {
+__global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, int rpr, int BM, int ntiles,
+                                                        int slots, int cap_splits) {
+  const MmPlan plan = mm_plan(mm_rows(g), BM, ntiles, g.K / 64, slots, cap_splits);
+  if (EPI != E_QKV && plan.ks == 1) return;
   rows = active_rows(g.nact, rpr, rows);  // rows of inactive requests are skipped
   if (g.rmap) rows = min(rows, *g.rcount);  // compact rows: sums at m, output row rmap[m]
-  const int KS = g.ksplit;
+  const int KS = plan.ks;
   const long long MN = (long long)g.M * g.N;
   const long long stride = (long long)gridDim.x * blockDim.x;
   auto sum8 = [&](int m, int n, float (&v)[8]) {
@@ -447,39 +482,30 @@ constexpr int kDKT = 64, kDS = 2;
 template <int EPI, int AL, int BMAP, class T>
 static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
   constexpr int BM = T::BM, BN = T::BN, WM = T::WM, WN = T::WN, kDWgPerCu = T::WGPC;
-  const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN, nk = g.K / kDKT;
-  const long long tiles = (long long)mtiles * ntiles, slots = (long long)kDWgPerCu * num_cus;
+  const int ntiles = (g.N + BN - 1) / BN, slots = kDWgPerCu * num_cus;
   // the QKV epilogue always runs on fp32 sums (one split at least); other
-  // products split over k when their tiles leave workgroup slots idle
-  long long ks = 1;
-  if (tiles < slots && g.part) {
-    ks = (slots + tiles - 1) / tiles;
-    ks = std::min<long long>(ks, nk * kDKT / 64 / PE_MM_SPLIT_MIN_KTILES);
-    ks = std::min<long long>(ks, g.part_cap / ((long long)g.M * g.N));
-    ks = std::max<long long>(ks, 1);
-  }
+  // products split over k (mm_plan, on the device) when their tiles leave
+  // workgroup slots idle
+  const long long cap = g.part ? g.part_cap / ((long long)g.M * g.N) : 0;
+  const int cap_splits = int(std::min<long long>(cap, 64));
+  if (EPI == E_QKV && cap_splits < 1) return hipErrorInvalidValue;
+  const MmPlan full = mm_plan(g.M, BM, ntiles, g.K / 64, slots, cap_splits);
+  const bool can_split = cap_splits >= 2 && g.K / 64 >= 2 * PE_MM_SPLIT_MIN_KTILES;
+  // the grid covers the plan of every row count up to M: at most `slots`
+  // items when split, at most the tiles of M rows otherwise
+  const int grid = can_split ? std::max(full.per, slots) : full.per;
+  hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, kDKT, kDS, 2>), dim3(unsigned(grid)),
+                     dim3(64 * WM * WN), 0, st, g, ntiles, slots, cap_splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || (EPI != E_QKV && !can_split)) return e;
   // rows the epilogue covers: every slot of a MASK-deduplicated QKV product
   const bool expand = EPI == E_QKV && g.dedup_k;
   const int rows = expand ? g.M / (g.dedup_k + 2) * (2 * g.dedup_k) : g.M;
   const int epi_rpr = expand ? 2 * g.dedup_k : g.rpr;
-  const long long per = (long long)mtiles * ((ntiles + 7) / 8) * 8;
-  if constexpr (EPI != E_QKV) {
-    if (ks == 1) {
-      hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, kDKT, kDS, 2>), dim3(unsigned(per)),
-                         dim3(64 * WM * WN), 0, st, g, mtiles, ntiles);
-      return hipGetLastError();
-    }
-  }
-  if (!g.part || (long long)g.M * g.N * ks > g.part_cap) return hipErrorInvalidValue;
-  GemmArgs gp = g;
-  gp.ksplit = int(ks);
-  hipLaunchKernelGGL((mm_kernel<E_PART, AL, BMAP, BM, BN, WM, WN, kDKT, kDS, 2>), dim3(unsigned(per * ks)),
-                     dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const long long work = (long long)rows * (EPI == E_QKV || EPI == E_SILU ? g.N / 16 : g.N / 8);
   const long long blocks = std::min<long long>((work + 255) / 256, 8LL * num_cus);
-  hipLaunchKernelGGL(mm_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, st, gp, rows, epi_rpr);
+  hipLaunchKernelGGL(mm_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, st, g, rows, epi_rpr, BM, ntiles,
+                     slots, cap_splits);
   return hipGetLastError();
 }
 
