@@ -96,16 +96,32 @@ def step_work(w, inp):
     bytes_ += w.layers * int(seq.sum()) * kvrow          # KV read
     bytes_ += w.layers * int((a + K).sum()) * kvrow      # KV write (valid slots)
     valid = int((a + K).sum())
-    qd, kvd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
-    dense = 2 * d * d + w.layers * (qd * d + 2 * kvd * d + d * qd + 3 * w.mlp * d)
-    flops = 2 * valid * dense + 2 * B * K * w.vocab * d
-    # attention: each valid slot at position q scores and mixes q+1 positions
-    att = 0
-    for r in range(B):
-        pos = list(range(p0[r], p0[r] + a[r] + 1)) + [p0[r] + a[r] + m for m in range(1, K)]
-        att += sum(q + 1 for q in pos)
-    flops += w.layers * 4 * w.head_dim * w.n_q_heads * att
-    return {"bytes": bytes_, "flops": flops, "weight_bytes": sum(wb.values())}
+    # Work whose results reach an output (draft tokens, KV writes): fc, the
+    # norms and the QKV product of every valid slot in every layer; attention,
+    # O and the MLP of every valid slot below the last layer, and of the draft
+    # rows alone in the last one (the other slots' results there are never read)
+    fl = attention_mlp_flops(w, [list(range(p0[r], p0[r] + a[r] + 1)) + [p0[r] + a[r] + m for m in range(1, K)]
+                                 for r in range(B)],
+                             [list(range(p0[r] + a[r], p0[r] + a[r] + K)) for r in range(B)])
+    return {"bytes": bytes_, "flops": fl + 2 * B * K * w.vocab * d, "weight_bytes": sum(wb.values())}
+
+
+def attention_mlp_flops(w, valid_pos, draft_pos, ctx_len=None):
+    """Drafter flops below the LM head: valid_pos[r] / draft_pos[r] are the
+    positions of request r's valid slots and draft rows; a slot at position q
+    attends to q+1 positions (ctx_len[r] each when given: a bidirectional
+    block).  fc + QKV on every valid slot of every layer; attention, O and MLP
+    on the valid slots below the last layer and on the draft rows in it."""
+    d, qd, kvd = w.d, w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    pre, post = qd * d + 2 * kvd * d, d * qd + 3 * w.mlp * d
+    nvalid = sum(len(p) for p in valid_pos)
+    ndraft = sum(len(p) for p in draft_pos)
+    att = lambda sets: sum((ctx_len[r] * len(ps)) if ctx_len is not None else sum(q + 1 for q in ps)
+                           for r, ps in enumerate(sets))
+    flops = 2 * nvalid * (2 * d * d + w.layers * pre)
+    flops += 2 * nvalid * (w.layers - 1) * post + 2 * ndraft * post
+    flops += 4 * w.head_dim * w.n_q_heads * ((w.layers - 1) * att(valid_pos) + att(draft_pos))
+    return flops
 
 
 def ar_work(w, inp):
@@ -406,11 +422,9 @@ def prefill(w, prm, dev, prompt, steps, warmup):
     n_prof = max(3, steps // 4)
     phases = {p: round(ms / n_prof * 1e3, 2) for p, (ms, n) in prof.items() if n}
     print(f"[bench] prefill {prompt}: {us:.1f} us/round", file=sys.stderr, flush=True)
-    valid = prompt + K - 1
-    qd, kvd, d = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim, w.d
-    dense = 2 * d * d + w.layers * (qd * d + 2 * kvd * d + d * qd + 3 * w.mlp * d)
-    att = sum(q + 1 for q in range(valid))
-    flops = 2 * valid * dense + 2 * B * K * w.vocab * d + w.layers * 4 * w.head_dim * w.n_q_heads * att
+    valid = prompt + K - 1  # prompt positions 0..prompt-1 (the last is the NTP slot), then K-1 MASK slots
+    flops = attention_mlp_flops(w, [list(range(valid))], [list(range(prompt - 1, valid))]) \
+        + 2 * B * K * w.vocab * w.d
     ctx.close()
     return {"workload": f"{w.name} drafting round after a {prompt}-position prompt (B=1, K={K}, S={S})",
             "us_per_round": us, "prompt_positions_per_s": prompt / (us * 1e-6),
@@ -497,9 +511,13 @@ def dflash(w, prm, dev, steps, warmup):
     p0 = inp["prefix"].astype(np.int64)
     ctx_len = p0 + acc + K + 2                       # attended positions per request
     layer_w = qd * d + 2 * kvd * d + d * qd + 3 * w.mlp * d
-    rows_inj, rows = int((acc + 1).sum()), B * (K + 1)
-    flops = (w.layers * (2 * rows_inj * 2 * kvd * d + 2 * rows * layer_w
-                         + 4 * w.head_dim * w.n_q_heads * (K + 1) * int(ctx_len.sum()))
+    rows_inj = int((acc + 1).sum())
+    # block rows (no fc: embedding input): QKV on all K+1 block slots, and
+    # attention, O and MLP on the K draft rows alone in the last layer
+    blk = [list(range(K + 1))] * B
+    flops = (w.layers * 2 * rows_inj * 2 * kvd * d
+             + attention_mlp_flops(w, blk, [list(range(1, K + 1))] * B, ctx_len=[int(c) for c in ctx_len])
+             - 2 * B * (K + 1) * 2 * d * d  # no fc in the block pass
              + 2 * B * K * w.vocab * d)
     nbytes = 2 * (w.layers * (2 * kvd * d + layer_w) + w.vocab * d) \
         + 2 * w.layers * 2 * kvd * int(ctx_len.sum())

@@ -78,6 +78,8 @@ struct pe_ctx {
   void* xc = nullptr;  // [B(K+2), d] first-layer fc output on the MASK-deduplicated rows (bf16)
   float* splitk = nullptr;      // split-K GEMM partials (bf16 storage)
   int32_t* rmap = nullptr;      // [R] non-rejected slots of a large-batch pass, then their count
+  int32_t* dmap = nullptr;      // [D] non-rejected draft rows of a large-batch pass, then their count
+  uint8_t* qskip = nullptr;     // [R] last-layer attention: 0 for the non-rejected draft rows
   long long splitk_cap = 0;     // floats
   double* rope_turns = nullptr;  // RoPE frequencies in turns per position
   void* lm_packed = nullptr;  // fragment-order copy of the LM head (bf16)
@@ -153,7 +155,7 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->plan_off, c->rope_turns, c->lm_packed, c->splitk, c->group_lens, c->rmap,
+                  c->part_o, c->part_ml, c->plan_off, c->rope_turns, c->lm_packed, c->splitk, c->group_lens, c->rmap, c->dmap, c->qskip,
                   c->sample_lse, c->sample_keys, c->sample_parts};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
@@ -321,6 +323,8 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {reinterpret_cast<void**>(&c->err), 16, "err"},
       {reinterpret_cast<void**>(&c->rope_turns), size_t(k.head_dim / 2) * 8, "rope"},
       {reinterpret_cast<void**>(&c->rmap), (R + 1) * 4, "row map"},
+      {reinterpret_cast<void**>(&c->dmap), (D + 1) * 4, "draft row map"},
+      {reinterpret_cast<void**>(&c->qskip), R, "last-layer query mask"},
       {reinterpret_cast<void**>(&c->ar_ids), R1 * 4, "ar ids"},
       {reinterpret_cast<void**>(&c->ar_pos), R1 * 4, "ar positions"},
       {reinterpret_cast<void**>(&c->ar_rows), size_t(k.max_num_seqs) * 4, "ar rows"},
@@ -567,6 +571,16 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     g0.rcount = ctx->rmap + R;
   }
 
+  // The last layer after its QKV product (which writes every valid slot's
+  // KV): only the draft rows feed the LM head, so attention keeps only their
+  // queries and the O product, MLP norm and MLP run on their rows alone (the
+  // large-batch kernels, through a row map of the non-rejected draft rows).
+  const bool draft_only = dt == PE_BF16 && R > pe::kMmMinRows && D > pe::kMmMinRows && P.draft_rows;
+  if (draft_only) {
+    Timed tm(ctx, PE_PH_FC);
+    PE_HIP(pe::launch_draft_map(R, D, P.draft_rows, P.rej, ctx->dmap, ctx->dmap + D, ctx->qskip, st), "draft map");
+  }
+
   // a dense GEMM with its fused epilogue
   auto dense = [&](int aload, int bmap, int epi, const pe::GemmArgs& g, const char* what) -> pe_status {
     PE_HIP(pe::launch_gemm(dt, aload, bmap, epi, g, ctx->num_cus, st), what);
@@ -608,6 +622,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   for (int l = 0; l < k.layers; ++l) {
     const pe_layer_weights& L = ctx->layers[l];
     const bool first_dd = l == 0 && dd;
+    const bool last_draft = draft_only && l == k.layers - 1;
     {
       Timed tm(ctx, PE_PH_NORM);
       if (first_dd)
@@ -643,7 +658,8 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       a.block_size = k.block_size; a.max_blocks = max_blocks; a.num_slots = num_slots;
       a.scale = 1.0f / std::sqrt(float(k.head_dim));
       a.q = ctx->q; a.kcache = k_cache[l]; a.vcache = v_cache[l];
-      a.positions = P.attn_pos ? P.attn_pos : P.pos; a.rej = P.rej; a.seq_lens = P.seq_lens;
+      a.positions = P.attn_pos ? P.attn_pos : P.pos; a.seq_lens = P.seq_lens;
+      a.rej = last_draft ? ctx->qskip : P.rej;  // queries computed: valid slots (last layer: draft rows)
       a.bt = block_table; a.out = ctx->attn;
       a.part_o = ctx->part_o; a.part_ml = ctx->part_ml; a.plan_off = ctx->plan_off;
       a.target_items = ctx->target_items;
@@ -688,12 +704,17 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.A = ctx->attn; g.lda = qd;
       g.W0 = L.wo; g.Wp = packed(ctx, l, 1);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
+      if (last_draft) { g.M = R; g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
       Timed tm(ctx, PE_PH_O);
       if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "o proj")) != PE_OK) return ds;
     }
     {
       Timed tm(ctx, PE_PH_NORM);
-      PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.mlp_norm, ctx->u, nullptr, R, k.rms_eps, st), "mlp norm");
+      if (last_draft)  // the draft rows, in place
+        PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, L.mlp_norm, ctx->u, P.draft_rows, R, k.rms_eps, st, true),
+               "mlp norm");
+      else
+        PE_HIP(pe::launch_rmsnorm(dt, R, d, ctx->x, L.mlp_norm, ctx->u, nullptr, R, k.rms_eps, st), "mlp norm");
     }
     {
       pe::GemmArgs g = g0;
@@ -701,6 +722,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.A = ctx->u; g.lda = d;
       g.W0 = L.w_gate; g.W1 = L.w_up; g.Wp = packed(ctx, l, 2);
       g.out = ctx->mlp; g.ldo = k.mlp;
+      if (last_draft) { g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
       Timed tm(ctx, PE_PH_GATEUP);
       if ((ds = dense(pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, "gate/up")) != PE_OK) return ds;
     }
@@ -710,6 +732,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.A = ctx->mlp; g.lda = k.mlp;
       g.W0 = L.w_down; g.Wp = packed(ctx, l, 3);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
+      if (last_draft) { g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
       Timed tm(ctx, PE_PH_DOWN);
       if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "down")) != PE_OK) return ds;
     }

@@ -44,6 +44,15 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c)
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%32][8(l/32)..+8]
+// and B[8(l/32)..+8][l%32]; register i of the result holds
+// C[8(i/4) + 4(l/32) + i%4][l%32].
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
+
 // Streaming 16-byte load for data read once (weights): non-temporal hint.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream(const void* p) {

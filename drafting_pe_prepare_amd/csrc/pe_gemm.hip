@@ -872,6 +872,188 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 LM head, 17..128 rows: a deep ring of 32-wide k-steps in MFMA
+// fragment order
+// ---------------------------------------------------------------------------
+// WGPC persistent workgroups per CU, each over an equal, contiguous range of
+// 16-column tiles (so no round of tiles runs on a few CUs while the rest
+// idle), taken in chunks of at most 16 tiles (256 columns) with all M <= BM
+// rows.  Each stage
+// holds one 32-wide k-step of both operands as 1 KB fragment blocks: block
+// (16-row tile t) has lane l's 16 bytes at 16 l, i.e. rows 16t + l%16 and
+// k-chunk l/16, which is the operand layout of v_mfma_f32_16x16x32_bf16, so
+// every fragment read is one contiguous 1 KB per wave (no bank conflicts, no
+// swizzle).  The weight blocks come from the fragment-order copy (each DMA
+// instruction moves one whole 1 KB block); the row blocks gather 16 rows x
+// 64 B of the row-major operand.  A stage is (BM + 256) x 64 B, so several
+// k-steps per CU are in flight (two workgroups of three stages, or one of
+// six): with 17..128 rows a k-step is little MFMA work, and the weight stream
+// from HBM needs that depth to hide its latency.  The
+// pipeline runs across chunk boundaries (step gs = chunk * ksteps + k-step);
+// at a chunk's last k-step the tile's row maxima fold into a running
+// (value, index) key per row, written once per workgroup at the end.
+// Fragment reads run one k-step ahead of the MFMAs.
+template <int BM, int WM, int WN, int S, int WGPC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN * WGPC / 4, WM * WN * WGPC / 4)))
+void lmhead_ring_kernel(GemmArgs g) {
+  constexpr int BN = 256, CT = BN / 16, NW = WM * WN, NT = 64 * NW;
+  constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;  // MFMA tiles per wave
+  static_assert(TI * 16 * WM == BM && TJ * 16 * WN == BN, "whole MFMA tiles per wave");
+  static_assert(NT >= BM, "one thread per row keeps the row's running key");
+  constexpr int NA = BM / 16, NB = CT, NBLK = NA + NB;  // fragment blocks per stage
+  constexpr int Q = (NBLK + NW - 1) / NW;              // DMAs per wave per stage
+  constexpr int STAGE = NBLK * 1024;
+  static_assert(S >= 3 && S <= 7 && WGPC * (S * STAGE + WN * BM * 8) <= 160 * 1024, "rings fit the LDS");
+  static_assert((S - 1) * Q < 64, "ring depth within the vmcnt range");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[S * STAGE];
+  __shared__ uint64_t s_best[WN * BM];
+
+  if (active_rows(g.nact, g.rpr, g.M) <= 0) return;
+  const int ksteps = g.K / 32, ntw = g.N / 16, G = gridDim.x, gid = blockIdx.x;
+  const int t0 = int((long long)gid * ntw / G), nt = int((long long)(gid + 1) * ntw / G) - t0;
+  const int nch = (nt + CT - 1) / CT, total = nch * ksteps;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
+  const int wm = w / WN, wn = w % WN;
+  auto chunk_first = [&](int c) { return t0 + c * nt / nch; };
+
+  // DMA q of this wave fills block j = w + NW q of each stage (a wave whose
+  // block would lie past the last one repeats its first: the same bytes to
+  // the same place, so every wave issues Q DMAs per stage and one vmcnt
+  // serves all).  Row block t: lane l loads A[16t + l%16][32 s + 8 (l/16)];
+  // weight block u: the fragment-order copy's block (tile u of the chunk, s),
+  // past the chunk's last tile that tile again (its columns are not used).
+  const uint16_t* asrc[Q];
+  int wu_[Q];
+  uint32_t dst[Q];
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int j = wu + NW * q < NBLK ? wu + NW * q : wu;
+    dst[q] = uint32_t(j * 1024);
+    wu_[q] = j - NA;
+    asrc[q] = (const uint16_t*)g.A + (long long)min(16 * j + col, g.M - 1) * g.lda + 8 * kg;
+  }
+  const uint16_t* Wp = (const uint16_t*)g.Wp + 8 * l;
+  const uint32_t base = lds_addr(ring);
+  auto issue = [&](int slot, int gs) {
+    const int c = gs / ksteps, s = gs - c * ksteps;
+    const int c0 = chunk_first(c), c1 = chunk_first(c + 1);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const void* src = wu_[q] < 0 ? (const void*)(asrc[q] + 32 * s)
+                                   : (const void*)(Wp + ((long long)min(c0 + wu_[q], c1 - 1) * ksteps + s) * 512);
+      dma16(src, base + slot * STAGE + dst[q]);
+    }
+  };
+  // at most n later steps of this wave's DMAs still in flight
+  auto wait_steps = [&](int n) {
+    if (n >= 6) wait_vmcnt<(S > 6 ? 6 : 0) * Q>();
+    else if (n == 5) wait_vmcnt<(S > 5 ? 5 : 0) * Q>();
+    else if (n == 4) wait_vmcnt<(S > 4 ? 4 : 0) * Q>();
+    else if (n == 3) wait_vmcnt<(S > 3 ? 3 : 0) * Q>();
+    else if (n == 2) wait_vmcnt<2 * Q>();
+    else if (n == 1) wait_vmcnt<Q>();
+    else wait_vmcnt<0>();
+  };
+
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int aoff = wm * TI * 1024 + 16 * l, boff = (NA + wn * TJ) * 1024 + 16 * l;
+  uint4 fa[2][TI], fb[2][TJ];
+  auto read = [&](int buf, const unsigned char* st) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa[buf][i] = *reinterpret_cast<const uint4*>(st + aoff + i * 1024);
+#pragma unroll
+    for (int jj = 0; jj < TJ; ++jj) fb[buf][jj] = *reinterpret_cast<const uint4*>(st + boff + jj * 1024);
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = mfma16(fa[buf][i], fb[buf][jj], acc[i][jj]);
+  };
+  uint64_t run = 0ull;  // thread tid < BM: the running key of row tid
+  // after a chunk's last k-step: lane (kg, col) holds C[row 4kg + r of MFMA
+  // tile i][column col of tile jj]; the row maxima over the chunk's columns
+  // fold into `run`, and the accumulators restart
+  auto fold = [&](int c) {
+    const int c0 = chunk_first(c), ncol = (chunk_first(c + 1) - c0) * 16;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lrow = wm * (BM / WM) + i * 16 + kg * 4 + r;
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int jj = 0; jj < TJ; ++jj) {
+          const int cc = (wn * TJ + jj) * 16 + col, n = c0 * 16 + cc;
+          if (cc < ncol) {
+            if (g.logits && lrow < g.M) g.logits[(long long)lrow * g.ldl + n] = acc[i][jj][r];
+            const uint64_t k = argmax_key(acc[i][jj][r], n);
+            best = k > best ? k : best;
+          }
+        }
+        for (int o = 1; o < 16; o <<= 1) {
+          const uint64_t k = shfl_xor_u64(best, o);
+          best = k > best ? k : best;
+        }
+        if (col == 0) s_best[wn * BM + lrow] = best;
+      }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the keys are in LDS (lgkmcnt(0)); a plain barrier, so the DMAs in
+    // flight stay in flight
+    wait_lgkm0();
+    asm volatile("s_barrier" ::: "memory");
+    if (tid < BM) {
+#pragma unroll
+      for (int v = 0; v < WN; ++v) run = s_best[v * BM + tid] > run ? s_best[v * BM + tid] : run;
+    }
+    // s_best is written again only after the next chunk's k-steps, each of
+    // which passes a barrier
+  };
+
+  // prologue: every slot filled, step 0 read
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+    if (j < total) issue(j, j);
+  wait_steps(total - 1 < S - 1 ? total - 1 : S - 1);
+  asm volatile("s_barrier" ::: "memory");
+  read(0, ring);
+  // step gs: its fragments are in registers (buffer gs & 1)
+  int slot = 0, ks = 0, ch = 0;
+  auto iter = [&](int gs, int buf) {
+    if (gs + 1 < total) {
+      const int later = total - 2 - gs;
+      wait_steps(later < S - 2 ? later : S - 2);  // step gs+1 has landed (this wave's part)
+      // everyone's part has landed, and everyone has read step gs's slot
+      // (before this barrier), which the next DMA refills
+      asm volatile("s_barrier" ::: "memory");
+      if (gs + S < total) issue(slot, gs + S);
+      slot = slot + 1 == S ? 0 : slot + 1;
+      read(buf ^ 1, ring + slot * STAGE);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(buf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (++ks == ksteps) {
+      fold(ch++);
+      ks = 0;
+    }
+  };
+  for (int gs = 0; gs < total; gs += 2) {
+    iter(gs, 0);
+    if (gs + 1 < total) iter(gs + 1, 1);
+  }
+  if (tid < BM && tid < g.M) g.keys[(long long)tid * g.parts + gid] = run;
+}
+
+// ---------------------------------------------------------------------------
 // fp32: plain FMA, 16x32 output tile per workgroup
 // ---------------------------------------------------------------------------
 template <int EPI, int AL, int BMAP>
@@ -949,11 +1131,15 @@ hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_
 //    when those tiles outnumber the CUs; otherwise 64x128 tiles (three stages,
 //    two workgroups per CU), which spread a small grid over more CUs (fc, O and
 //    down at c=64, cache-cold weights: 50/38/69 us against 59/43/76 us).
-enum Variant { V_WIDE, V_SKINNY, V_A64, V_A128, V_A224, V_A256, V_D64, V_D128S2 };
+#ifndef PE_LM_RING
+#define PE_LM_RING 1
+#endif
+enum Variant { V_WIDE, V_RING, V_SKINNY, V_A64, V_A128, V_A224, V_A256, V_D64, V_D128S2 };
 static Variant pick(int epi, int M, int N, int K, int num_cus) {
   if (epi == E_ARGMAX) {
     const size_t wide_lds = size_t(M) * (K / 8 + 1) * 16;
     if (M <= 16 && wide_lds <= 140 * 1024) return V_WIDE;
+    if (PE_LM_RING && M <= 128 && K % 32 == 0) return V_RING;
     if (M <= 64) return V_A64;
     if (M > 384 && M <= 448) return V_A224;  // two 224-row tiles instead of 256 + 192 valid rows
     return M <= 128 ? V_A128 : V_A256;
@@ -969,6 +1155,7 @@ int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus) {
   if (dtype != 1) return (N + 31) / 32;
   switch (pick(E_ARGMAX, M, N, K, num_cus)) {
     case V_WIDE: return std::min(num_cus, N / 16);
+    case V_RING: return std::min((M <= 64 ? 2 : 1) * num_cus, N / 16);  // run_ring's grid
     case V_SKINNY: return (N + 15) / 16;
     default: return (N + kArgmaxBN - 1) / kArgmaxBN;
   }
@@ -1254,12 +1441,33 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
   return hipGetLastError();
 }
 
+// LM head on the deep ring (17..256 rows; needs the fragment-order copy)
+template <int BM, int WM, int WN, int S, int WGPC>
+static hipError_t run_ring(const GemmArgs& g, int num_cus, hipStream_t st) {
+  const int grid = std::min(WGPC * num_cus, g.N / 16);
+  if (g.parts != grid || g.M > BM || g.K % 32 || g.N % 16 || !g.Wp) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((lmhead_ring_kernel<BM, WM, WN, S, WGPC>), dim3(grid), dim3(64 * WM * WN), 0, st, g);
+  return hipGetLastError();
+}
+
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
   if (EPI != E_ARGMAX && g.M > kMmMinRows) return launch_mm(AL, BMAP, EPI, g, num_cus, st);
   if (g.dedup_k) return hipErrorInvalidValue;  // compact first-layer rows: large batches only
   const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);
   if constexpr (EPI == E_ARGMAX) {
+    // 17..128 rows: the deep ring (K sweep, K = 3, 5, 7: 157 -> 153, 170 ->
+    // 158, 174 -> 160 us); 129..256 rows measured slower on it (four 32 KB
+    // stages: 198 -> 206, 205 -> 217 us) and stay on the 64-wide ring
+    if (v == V_RING) {
+      if (!g.Wp || AL != A_PLAIN || BMAP != B_PLAIN) return hipErrorInvalidValue;
+      // up to 64 rows: two workgroups per CU, each a three-stage ring of
+      // four waves (K sweep, 48 rows: 155 -> 127 us); 65..128 rows: one
+      // workgroup of eight waves and six stages (two of four waves and three
+      // stages measured 446 us against 158)
+      if (g.M <= 64) return run_ring<64, 1, 4, 3, 2>(g, num_cus, st);
+      return run_ring<128, 2, 4, 6, 1>(g, num_cus, st);
+    }
     switch (v) {
       case V_WIDE: return run_wide_any(g, num_cus, st);
       // workgroups per CU: two 64-row tiles (80 KB of LDS each), one otherwise

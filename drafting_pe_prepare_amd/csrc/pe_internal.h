@@ -97,13 +97,18 @@ hipError_t launch_ar_next(const ArArgs& a, hipStream_t st);
 
 // ---- normalisation --------------------------------------------------------
 // out[i] = x[row(i)] * rsqrt(mean(x^2) + eps) * gain; row(i) = rows_idx ? rows_idx[i] : i
+// (scatter: out[row(i)] instead of out[i])
 hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void* gain, void* out,
-                          const int32_t* rows_idx, int rows_bound, float eps, hipStream_t st);
+                          const int32_t* rows_idx, int rows_bound, float eps, hipStream_t st, bool scatter = false);
 // bf16 RMSNorm of the compact rows of a MASK-deduplicated first layer (K+2
 // per request, see GemmArgs::dedup_k) that also writes each raw row x[m] to
 // its slots of the full layout: x_full[s] = x[dedup_row(s, K)] for all B*2K s.
 // The non-rejected rows of a batch of R slots, in order: rmap[0..*count).
 hipError_t launch_compact_rows(int R, const uint8_t* rejected, int32_t* rmap, int32_t* count, hipStream_t st);
+// The non-rejected draft rows (draft_rows[0..D) in order): dmap[0..*count),
+// and qskip[s] = 0 for exactly those slots (1 elsewhere).
+hipError_t launch_draft_map(int R, int D, const int32_t* draft_rows, const uint8_t* rejected, int32_t* dmap,
+                            int32_t* count, uint8_t* qskip, hipStream_t st);
 hipError_t launch_rmsnorm_expand(int rows, int d, const void* x, const void* gain, void* out, void* x_full,
                                  int K, float eps, hipStream_t st);
 
@@ -152,6 +157,9 @@ struct GemmArgs {
   // the only ones anything reads).  Not combined with dedup_k.
   const int32_t* rmap;
   const int32_t* rcount;
+  // rows the tile shape is chosen for (0: M); with a row map the count is
+  // known only on the device, and this is its expected size
+  int plan_rows;
 };
 // rows of an M-row operand with rpr rows per request that belong to active requests
 __device__ __forceinline__ int active_rows(const int32_t* nact, int rpr, int M) {

@@ -384,6 +384,51 @@ __global__ __launch_bounds__(1024) void compact_rows_kernel(int R, const uint8_t
   if (t == 1023) *count = base + inc;
 }
 
+// The non-rejected draft rows of a batch, in draft-row order: dmap[0..*count),
+// and a query mask for the last layer's attention, qskip[s] = 0 exactly for
+// those slots.  Only the draft rows feed the LM head, so after the last
+// layer's QKV product (which writes every valid slot's KV) the attention
+// rows, O product and MLP of the other slots are never read.  One workgroup.
+__global__ __launch_bounds__(1024) void draft_map_kernel(int R, int D, const int32_t* __restrict__ draft_rows,
+                                                         const uint8_t* __restrict__ rej, int32_t* __restrict__ dmap,
+                                                         int32_t* __restrict__ count, uint8_t* __restrict__ qskip) {
+  __shared__ int s_w[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int s = t; s < R; s += 1024) qskip[s] = 1;
+  __syncthreads();  // the draft rows' clears below land after every set
+  const int per = (D + 1023) / 1024, i0 = min(D, t * per), i1 = min(D, i0 + per);
+  auto live = [&](int i) {
+    const int s = draft_rows[i];
+    return s >= 0 && s < R && !rej[s];
+  };
+  int n = 0;
+  for (int i = i0; i < i1; ++i) n += live(i) ? 1 : 0;
+  int inc = n;  // inclusive scan inside the wave, then across the 16 waves
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int v = 0; v < w; ++v) base += s_w[v];
+  int at = base + inc - n;
+  for (int i = i0; i < i1; ++i)
+    if (live(i)) {
+      const int s = draft_rows[i];
+      dmap[at++] = s;
+      qskip[s] = 0;
+    }
+  if (t == 1023) *count = base + inc;
+}
+
+hipError_t launch_draft_map(int R, int D, const int32_t* draft_rows, const uint8_t* rejected, int32_t* dmap,
+                            int32_t* count, uint8_t* qskip, hipStream_t st) {
+  if (R <= 0 || D <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(draft_map_kernel, dim3(1), dim3(1024), 0, st, R, D, draft_rows, rejected, dmap, count, qskip);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact_rows(int R, const uint8_t* rejected, int32_t* rmap, int32_t* count, hipStream_t st) {
   if (R <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, st, R, rejected, rmap, count);

@@ -36,12 +36,6 @@
 
 namespace pe {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                  0, 0, 0);
-}
 
 // logical weight row n of the 32-apart pairings (see above)
 template <int BMAP>
@@ -477,6 +471,8 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
 // 2880-5120 output columns, run 20-30% slower on them (fewer, split tiles).
 struct TileSmall { static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, WGPC = 2; };
 struct TileLarge { static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, WGPC = 1; };
+struct TileMid { static constexpr int BM = 192, BN = 256, WM = 2, WN = 4, WGPC = 1; };
+struct TileWide { static constexpr int BM = 256, BN = 128, WM = 2, WN = 2, WGPC = 1; };
 constexpr int kDKT = 64, kDS = 2;
 
 template <int EPI, int AL, int BMAP, class T>
@@ -509,21 +505,55 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
   return hipGetLastError();
 }
 
+#ifndef PE_MM_T_FC
+#define PE_MM_T_FC 0
+#endif
+#ifndef PE_MM_T_QKV
+#define PE_MM_T_QKV 0
+#endif
+#ifndef PE_MM_T_RESID
+#define PE_MM_T_RESID 0
+#endif
+#ifndef PE_MM_T_GU
+#define PE_MM_T_GU -1
+#endif
+template <int EPI, int AL, int BMAP>
+static hipError_t mm_tiles(int tile, const GemmArgs& g, int num_cus, hipStream_t st) {
+  switch (tile) {
+    case 1: return mm_dense<EPI, AL, BMAP, TileLarge>(g, num_cus, st);
+    case 2: return mm_dense<EPI, AL, BMAP, TileMid>(g, num_cus, st);
+    case 3: return mm_dense<EPI, AL, BMAP, TileWide>(g, num_cus, st);
+    default: return mm_dense<EPI, AL, BMAP, TileSmall>(g, num_cus, st);
+  }
+}
+
 hipError_t launch_mm(int aload, int bmap, int epi, const GemmArgs& g, int num_cus, hipStream_t st) {
   if (g.M <= 0) return hipSuccess;
   if (g.K % 64) return hipErrorInvalidValue;  // whole 64-wide k-tiles (and fc halves)
   if (g.N % 64) return hipErrorInvalidValue;  // whole 64-column pair blocks
-  using S = TileSmall;
-  if (aload == A_FC && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_FC, B_PLAIN, S>(g, num_cus, st);
-  if (aload == A_PLAIN && bmap == B_QKV && epi == E_QKV) return mm_dense<E_QKV, A_PLAIN, B_QKV, S>(g, num_cus, st);
-  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_RESID) return mm_dense<E_RESID, A_PLAIN, B_PLAIN, S>(g, num_cus, st);
+  if (aload == A_FC && bmap == B_PLAIN && epi == E_STORE) return mm_tiles<E_STORE, A_FC, B_PLAIN>(PE_MM_T_FC, g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_QKV && epi == E_QKV) return mm_tiles<E_QKV, A_PLAIN, B_QKV>(PE_MM_T_QKV, g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_RESID) return mm_tiles<E_RESID, A_PLAIN, B_PLAIN>(PE_MM_T_RESID, g, num_cus, st);
   if (aload == A_PLAIN && bmap == B_GATEUP && epi == E_SILU) {
-    // large tiles while they still cover three quarters of the CUs
-    const long long large = (long long)((g.M + TileLarge::BM - 1) / TileLarge::BM) * ((g.N + TileLarge::BN - 1) / TileLarge::BN);
-    if (4 * large >= 3LL * num_cus) return mm_dense<E_SILU, A_PLAIN, B_GATEUP, TileLarge>(g, num_cus, st);
-    return mm_dense<E_SILU, A_PLAIN, B_GATEUP, S>(g, num_cus, st);
+    int t = PE_MM_T_GU;
+    if (t < 0) {
+      // The tile shape with the least work per CU: rounds of workgroups x
+      // output area per CU and round (two 128x128 workgroups, or one of
+      // 192x256 or 256x256 per CU).  Measured at c=64 (672 rows): 192x256
+      // one round 80 us, 256x256 one round 91 us, 128x128 two rounds 105 us,
+      // i.e. the same time per unit of area on all three.
+      const long long rows = g.plan_rows > 0 ? g.plan_rows : g.M;
+      auto cost = [&](int bm, int bn, int wgpc) {
+        const long long tiles = ((rows + bm - 1) / bm) * ((g.N + bn - 1) / bn), slots = (long long)wgpc * num_cus;
+        return ((tiles + slots - 1) / slots) * (long long)bm * bn * wgpc;
+      };
+      const long long cs = cost(TileSmall::BM, TileSmall::BN, TileSmall::WGPC), cm = cost(TileMid::BM, TileMid::BN, 1),
+                      cl = cost(TileLarge::BM, TileLarge::BN, 1);
+      t = cs <= cm && cs <= cl ? 0 : (cm <= cl ? 2 : 1);
+    }
+    return mm_tiles<E_SILU, A_PLAIN, B_GATEUP>(t, g, num_cus, st);
   }
-  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_PLAIN, B_PLAIN, S>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_PLAIN, B_PLAIN, TileSmall>(g, num_cus, st);
   return hipErrorInvalidValue;
 }
 

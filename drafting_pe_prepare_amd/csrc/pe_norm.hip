@@ -19,13 +19,17 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const T* __restrict
                                                       T* __restrict__ out,
                                                       const int32_t* __restrict__ rows_idx,
                                                       int rows_bound, float eps,
-                                                      T* __restrict__ x_full = nullptr, int expand_k = 0) {
+                                                      T* __restrict__ x_full = nullptr, int expand_k = 0,
+                                                      bool scatter = false) {
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
   const int i = blockIdx.x;
   int src = rows_idx ? rows_idx[i] : i;
-  if (src < 0 || src >= rows_bound) src = 0;
+  if (src < 0 || src >= rows_bound) {
+    if (scatter) return;  // no row to write
+    src = 0;
+  }
   const T* xr = x + (long long)src * d;
-  T* yr = out + (long long)i * d;
+  T* yr = out + (long long)(scatter ? src : i) * d;
   const int nc = d / V;
   uint4 xs[NCH], gs[NCH];
 #pragma unroll
@@ -89,15 +93,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const T* __restrict
 }
 
 hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void* gain, void* out,
-                          const int32_t* rows_idx, int rows_bound, float eps, hipStream_t st) {
+                          const int32_t* rows_idx, int rows_bound, float eps, hipStream_t st, bool scatter) {
   if (rows <= 0) return hipSuccess;
   if (dtype == 1)
     hipLaunchKernelGGL((rmsnorm_kernel<uint16_t, 2>), dim3(rows), dim3(256), 0, st, d,
                        (const uint16_t*)x, (const uint16_t*)gain, (uint16_t*)out, rows_idx,
-                       rows_bound, eps);
+                       rows_bound, eps, (uint16_t*)nullptr, 0, scatter);
   else
     hipLaunchKernelGGL((rmsnorm_kernel<float, 2>), dim3(rows), dim3(256), 0, st, d, (const float*)x,
-                       (const float*)gain, (float*)out, rows_idx, rows_bound, eps);
+                       (const float*)gain, (float*)out, rows_idx, rows_bound, eps, (float*)nullptr, 0, scatter);
   return hipGetLastError();
 }
 
