@@ -76,8 +76,8 @@ __device__ __forceinline__ int mm_swz(int r) {
 // device: with a row map the count is known only there).  T output tiles
 // (column tiles rounded up to whole groups of 8, see the block mapping) run
 // in one round of `slots` workgroups: ks = floor(slots / T) splits, so that
-// T * ks <= slots, at least PE_MM_SPLIT_MIN_KTILES k-tiles each and within the
-// partial-sum buffer (cap_splits copies of [M][N]).  With ks == 1 the kernel
+// T * ks <= slots, at least PE_MM_SPLIT_MIN_KTILES k-tiles each and within
+// the partial-sum buffer (cap_splits copies of [M][N]).  With ks == 1 the kernel
 // runs the fused epilogue itself, unless `force_part` (the QKV product, whose
 // RoPE + KV-write epilogue runs on the fp32 sums).
 struct MmPlan { int mt, per, ks; };
@@ -87,6 +87,9 @@ __host__ __device__ inline MmPlan mm_plan(int rows, int BM, int ntiles, int nkt,
   p.per = p.mt * ((ntiles + 7) / 8) * 8;
   p.ks = 1;
   if (p.per > 0 && p.per < slots) {
+    // (two splits for tiles filling more than half the slots, one and a half
+    // rounds, measured slower or level: K sweep gate/up 181 -> 202 us,
+    // largest graph fc 109 -> 125 us, drafting round after a prompt -13 us)
     int ks = slots / p.per;
     const int kmax = nkt / PE_MM_SPLIT_MIN_KTILES;
     ks = ks < kmax ? ks : kmax;
@@ -485,11 +488,14 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
   const long long cap = g.part ? g.part_cap / ((long long)g.M * g.N) : 0;
   const int cap_splits = int(std::min<long long>(cap, 64));
   if (EPI == E_QKV && cap_splits < 1) return hipErrorInvalidValue;
-  const MmPlan full = mm_plan(g.M, BM, ntiles, g.K / 64, slots, cap_splits);
   const bool can_split = cap_splits >= 2 && g.K / 64 >= 2 * PE_MM_SPLIT_MIN_KTILES;
-  // the grid covers the plan of every row count up to M: at most `slots`
-  // items when split, at most the tiles of M rows otherwise
-  const int grid = can_split ? std::max(full.per, slots) : full.per;
+  // the grid covers the plan of every row count up to M (the device plans
+  // from the rows it finds): the most items of any number of row tiles
+  int grid = 0;
+  for (int mt = 1; mt <= (g.M + BM - 1) / BM; ++mt) {
+    const MmPlan p = mm_plan(mt * BM, BM, ntiles, g.K / 64, slots, cap_splits);
+    grid = std::max(grid, p.per * p.ks);
+  }
   hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, kDKT, kDS, 2>), dim3(unsigned(grid)),
                      dim3(64 * WM * WN), 0, st, g, ntiles, slots, cap_splits);
   hipError_t e = hipGetLastError();
