@@ -92,7 +92,7 @@ struct pe_ctx {
   uint8_t* ar_rej = nullptr;
   int64_t* ar_slots = nullptr;
   void* ar_hidden = nullptr;
-  int target_items = 1024;
+  int attn_grid = 512;
   long long items_max = 0;
   // step graph
   const int32_t* nact = nullptr;  // occupancy of the step being captured (NULL: every request active)
@@ -279,13 +279,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
     free_ctx(c);
     return hipfail(e, "device query");
   }
-#ifndef PE_ATTN_SMALLQ_DIV
-#define PE_ATTN_SMALLQ_DIV 2  // fewer split-KV items when a KV head has at most four query tiles
-#endif
-#ifndef PE_ATTN_ITEMS_PER_CU
-#define PE_ATTN_ITEMS_PER_CU 4
-#endif
-  c->target_items = PE_ATTN_ITEMS_PER_CU * c->num_cus;  // split-KV work items per attention launch
+  c->attn_grid = 2 * c->num_cus;  // attention workgroups: two 512-thread workgroups per CU
 
   const pe_config& k = c->cfg;
   // rows: a decode round (2K slots per request) or a prefill batch
@@ -305,7 +299,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   // a group's; a prefill batch may bring any S with S*G <= 512
   size_t QN = Sd * G <= 512 ? size_t(Sd) * G : size_t(c->attn_group) * G;
   if (k.max_prefill_slots > 0) QN = 512;
-  c->items_max = pe::attn_max_items(c->groups_max, k.n_kv_heads, c->target_items);
+  c->items_max = pe::attn_max_items(c->groups_max, k.n_kv_heads, c->attn_grid);
   // partial argmax keys: the most any LM-head launch can need (B*K draft rows
   // of a parallel pass, B of a sequential one)
   size_t key_slots = 0;
@@ -343,7 +337,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
   if (k.dtype == PE_BF16) {
     if ((s = alloc(&c->part_o, size_t(c->items_max) * QN * k.head_dim * 4, "attn partials")) != PE_OK ||
         (s = alloc(&c->part_ml, size_t(c->items_max) * QN * 2 * 4, "attn stats")) != PE_OK ||
-        (s = alloc(&c->plan_off, size_t(pe::kAttnMaxB + 1) * 4, "attn plan")) != PE_OK) {
+        (s = alloc(&c->plan_off, size_t(pe::kAttnMaxB + 2) * 4, "attn plan")) != PE_OK) {
       free_ctx(c);
       return s;
     }
@@ -662,13 +656,11 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       a.rej = last_draft ? ctx->qskip : P.rej;  // queries computed: valid slots (last layer: draft rows)
       a.bt = block_table; a.out = ctx->attn;
       a.part_o = ctx->part_o; a.part_ml = ctx->part_ml; a.plan_off = ctx->plan_off;
-      a.target_items = ctx->target_items;
       a.vpr = 1;
       const int G = k.n_q_heads / k.n_kv_heads;
-      // an item with at most four 16-query tiles does little work per position,
-      // so its fixed cost (plan, queries, block ids, DMA ramp-up) weighs more:
-      // fewer, longer items
-      if ((S * G + 15) / 16 <= 4) a.target_items = ctx->target_items / PE_ATTN_SMALLQ_DIV;
+      // the steps of all (request, KV head) streams are cut into equal ranges,
+      // one per workgroup
+      a.grid = ctx->attn_grid;
       if (dt == PE_BF16 && S * G > 512) {
         // groups of attn_group consecutive slots attend as requests of their
         // own (same block table row, context up to the group's last position)
@@ -684,17 +676,8 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
                "attention group lengths");
         a.seq_lens = ctx->group_lens;
       }
-      // Items go to workgroups statically (item i to workgroup i mod grid, one
-      // split plan per workgroup), two 512-thread workgroups per CU.  With at
-      // least four (request, KV head) pairs per workgroup the items are mostly
-      // whole requests of varied length; then one workgroup per item lets the
-      // hardware hand them out as workgroups finish (largest graph: attention
-      // 767 -> 690 us; c=64 and the K sweep were slower that way).
-      long long grid = 2LL * ctx->num_cus;
-      const long long mx = pe::attn_max_items(a.B, k.n_kv_heads, ctx->target_items);
-      a.slots = int(grid);
-      if ((long long)a.B * k.n_kv_heads >= 4 * grid) grid = mx;
-      a.grid = int(grid < mx ? grid : mx);
+      if (pe::attn_max_items(a.B, k.n_kv_heads, a.grid) > ctx->items_max)
+        return fail(PE_ERR_UNSUPPORTED, "attention: %d requests exceed the partial buffers", a.B);
       Timed tm(ctx, PE_PH_ATTN);
       PE_HIP(pe::launch_attention(dt, a, st), "attention");
     }

@@ -8,11 +8,13 @@
 // (rejected slots never wrote, so they are never read as their own slot).
 //
 // gfx950 design (bf16, head_dim 64)
-//  * Work item = (request, KV chunk, KV head).  All S*G queries of one KV head
-//    (S slots x G query heads of the group) share every K/V tile, so the item
-//    streams its chunk once; chunk size is chosen on the device from the
-//    batch's total context so that about `target_items` items exist
-//    (split-KV), and a merge kernel combines the fp32 partials.
+//  * Stream = (request, KV head): all S*G queries of one KV head (S slots x G
+//    query heads of the group) share every K/V tile, so a stream is read
+//    once.  The streams' 64-position steps are laid end to end and cut into
+//    equal contiguous ranges, one per workgroup (split-KV); a workgroup runs
+//    each stream piece of its range and writes fp32 partials, and a merge
+//    kernel combines a stream's pieces.  Equal ranges keep every workgroup
+//    equally busy whatever the mix of context lengths.
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16:
 //    a lane then holds 8 consecutive positions of one query, which is exactly
 //    the B operand of O^T = V^T P^T, so the softmax stays in registers with no
@@ -29,11 +31,8 @@
 #include "pe_common.h"
 #include "pe_internal.h"
 
-#ifndef PE_ATTN_MIN_CH
-#define PE_ATTN_MIN_CH 128  // shortest split-KV chunk (positions, a multiple of 64)
-#endif
-#ifndef PE_ATTN_FILL_CH
-#define PE_ATTN_FILL_CH 512  // chunks stay at least this long while they still fill every workgroup slot
+#ifndef PE_ATTN_MIN_STEPS
+#define PE_ATTN_MIN_STEPS 2  // shortest range per workgroup (64-position steps)
 #endif
 
 namespace pe {
@@ -47,37 +46,25 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Split-KV plan: total context -> chunk size CH (a multiple of 64); off[r] =
-// first chunk of request r.  CH aims at `target` items, but is at least the
-// context per resident workgroup (`slots`) clamped to [PE_ATTN_MIN_CH,
-// PE_ATTN_FILL_CH]: an item pays a fixed cost (plan, queries, block ids, DMA
-// ramp-up), so a chunk only shrinks below PE_ATTN_FILL_CH while the workgroup
-// slots would otherwise go idle.  Any blockDim that is a multiple of 64 and
-// <= 512.
-__device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, int slots, int* off,
-                          int& CH) {
-  __shared__ long long s_tot[8];
+// Steps of one stream of a request with context L: 64-position steps,
+// rounded up to a multiple of PE_ATTN_MIN_STEPS so that short ranges start
+// on stream boundaries (a range that straddled two streams would pay the
+// fixed cost of a piece twice); a padded step past L is empty.
+__device__ __forceinline__ int attn_steps(int L) {
+  const int n = (max(L, 0) + 63) >> 6;
+  return (n + PE_ATTN_MIN_STEPS - 1) / PE_ATTN_MIN_STEPS * PE_ATTN_MIN_STEPS;
+}
+
+// Step plan: off[r] = steps of the requests before r (one KV head), off[B] =
+// the total.  Any blockDim that is a multiple of 64 and <= 512.
+__device__ void attn_plan(const int32_t* seq_lens, int B, int* off) {
   __shared__ int s_wsum[8];
-  const int tid = threadIdx.x, nt = blockDim.x, nw = nt >> 6, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wid = tid >> 6;
   // thread tid owns requests [r0, r1)
   const int per = (B + nt - 1) / nt, r0 = min(B, tid * per), r1 = min(B, r0 + per);
-  long long tot = 0;
-  for (int r = r0; r < r1; ++r) tot += max(seq_lens[r], 0);
-  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
-  if (lane == 0) s_tot[wid] = tot;
-  __syncthreads();
-  tot = 0;
-  for (int w = 0; w < nw; ++w) tot += s_tot[w];
-  long long ch = (tot * Hkv + target - 1) / (target > 0 ? target : 1);
-  long long fill = (tot * Hkv + slots - 1) / (slots > 0 ? slots : 1);
-  fill = fill < PE_ATTN_MIN_CH ? PE_ATTN_MIN_CH : (fill > PE_ATTN_FILL_CH ? PE_ATTN_FILL_CH : fill);
-  ch = ch > fill ? ch : fill;
-  ch = (ch + 63) / 64 * 64;
-  if (ch > (1 << 30)) ch = 1 << 30;
-  CH = int(ch);
   int sum = 0;
-  for (int r = r0; r < r1; ++r) sum += (max(seq_lens[r], 0) + CH - 1) / CH;
-  // block-wide exclusive prefix of the chunk counts: a shuffle scan inside
+  for (int r = r0; r < r1; ++r) sum += attn_steps(seq_lens[r]);
+  // block-wide exclusive prefix of the step counts: a shuffle scan inside
   // each wave, then the totals of the waves before it
   int inc = sum;
   for (int o = 1; o < 64; o <<= 1) {
@@ -91,15 +78,27 @@ __device__ void attn_plan(const int32_t* seq_lens, int B, int Hkv, int target, i
   int run = base + inc - sum;
   for (int r = r0; r < r1; ++r) {
     off[r] = run;
-    run += (max(seq_lens[r], 0) + CH - 1) / CH;
+    run += attn_steps(seq_lens[r]);
   }
   if (tid == nt - 1) off[B] = base + inc;
   __syncthreads();
 }
 
-long long attn_max_items(int B, int Hkv, int target_items) {
-  return (long long)target_items + (long long)(B + 1) * Hkv;
+// Workgroups that get a range: all of the grid, but no range shorter than
+// PE_ATTN_MIN_STEPS steps (each piece pays a fixed cost: queries, block ids,
+// DMA ramp-up), and never more than the steps (so every workgroup's range is
+// non-empty and a stream's pieces are consecutive workgroups).
+__device__ __forceinline__ int attn_ranges(long long P, int grid) {
+  const long long g = P / PE_ATTN_MIN_STEPS;
+  return int(g < 1 ? 1 : (g < grid ? g : grid));
 }
+
+// Stream s = r*Hkv + g covers global steps [Hkv*off[r] + g*n_r, ... + n_r),
+// n_r = off[r+1] - off[r]; workgroup w of Gw covers [ceil(w P / Gw),
+// ceil((w+1) P / Gw)), so step x lies in workgroup floor(x Gw / P).  The
+// piece of stream s in workgroup w has partial index s + w, so a stream's
+// pieces are consecutive and at most B*Hkv + Gw partials exist.
+long long attn_max_items(int B, int Hkv, int grid) { return (long long)B * Hkv + grid; }
 
 // LDS tiles of one 32-position step for one KV head.
 //  K: 32 positions x 128 B; chunk c (16 B, 8 dims) of position p sits at
@@ -119,12 +118,13 @@ __device__ __forceinline__ void attn_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One workgroup of 8 waves per (request, chunk, KV head) item.  A step covers
-// 64 positions (two 32-position halves).  Every step each wave issues two
-// 1 KB LDS DMAs three steps ahead: K rows 8(w%4).. of half w/4 and V lines
-// 8(w%4).. of half w/4, so up to three 16 KB steps are in flight per
-// workgroup.  Then each wave runs its QPW query tiles of 16 (S*G queries = S
-// slots x G heads of the group) against the shared tiles.
+// Persistent workgroups of 8 waves, each over its equal range of steps (one
+// or more stream pieces).  A step covers 64 positions (two 32-position
+// halves).  Every step each wave issues two 1 KB LDS DMAs three steps ahead:
+// K rows 8(w%4).. of half w/4 and V lines 8(w%4).. of half w/4, so up to
+// three 16 KB steps are in flight per workgroup.  Then each wave runs its QPW
+// query tiles of 16 (S*G queries = S slots x G heads of the group) against
+// the shared tiles.
 template <int QPW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QPW == 1 ? 4 : 1, QPW == 1 ? 4 : 2)))
 void attn_partial_kernel(AttnArgs a) {
@@ -134,12 +134,16 @@ void attn_partial_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char v0[2 * HALF], v1[2 * HALF], v2[2 * HALF], v3[2 * HALF];
   constexpr int WIN = 8192;                 // positions per block-id window
   __shared__ int s_bt[WIN / 16 + 2];        // block ids of the window (block_size >= 16)
-  int CH;
-  attn_plan(a.seq_lens, a.B, a.Hkv, a.target_items, a.slots, s_off, CH);
-  if (blockIdx.x == 0)  // the merge kernel reads the plan instead of recomputing it
+  attn_plan(a.seq_lens, a.B, s_off);
+  const long long P = (long long)s_off[a.B] * a.Hkv;
+  const int Gw = attn_ranges(P, gridDim.x);
+  if (blockIdx.x == 0) {  // the merge kernel reads the plan instead of recomputing it
     for (int r = threadIdx.x; r <= a.B; r += blockDim.x) a.plan_off[r] = s_off[r];
+    if (threadIdx.x == 0) a.plan_off[a.B + 1] = Gw;
+  }
+  if ((int)blockIdx.x >= Gw) return;
   const int G = a.Hq / a.Hkv, QN = a.S * G, QT = (QN + 15) >> 4;
-  const int total = s_off[a.B] * a.Hkv;
+  const long long x1 = ((long long)(blockIdx.x + 1) * P + Gw - 1) / Gw;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
   const float sl2 = a.scale * 1.4426950408889634f;
   const uint16_t* Q = (const uint16_t*)a.q;
@@ -171,16 +175,23 @@ void attn_partial_kernel(AttnArgs a) {
                            : w == 4 ? v0 : w == 5 ? v1 : w == 6 ? v2 : v3;
   float* const s_ot = reinterpret_cast<float*>(sto);
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int rc = item / a.Hkv, g = item - rc * a.Hkv;
+  for (long long x = ((long long)blockIdx.x * P + Gw - 1) / Gw; x < x1;) {
+    // the stream piece starting at global step x: request r is the last one
+    // whose streams start at or before x (it has steps, since the next
+    // request's streams start after x)
     int lo = 0, hi = a.B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_off[mid] <= rc) lo = mid; else hi = mid;
+      if ((long long)s_off[mid] * a.Hkv <= x) lo = mid; else hi = mid;
     }
-    const int r = lo, chunk = rc - s_off[r];
+    const int r = lo, nr = s_off[r + 1] - s_off[r];
+    const int within = int(x - (long long)s_off[r] * a.Hkv);
+    const int g = within / nr, st0 = within - g * nr;
+    const int st1 = int(min((long long)nr, st0 + (x1 - x)));
+    x += st1 - st0;
+    const long long item = (long long)r * a.Hkv + g + blockIdx.x;  // partial index
     const int L = a.seq_lens[r];
-    const int cb = chunk * CH, ce = min(L, cb + CH);
+    const int cb = st0 * 64, ce = min(L, st1 * 64);  // empty (cb >= ce) for a padded step: the partial is zero
     const int32_t* btr = a.bt + (long long)(r / a.vpr) * a.max_blocks;
 
     // query tiles of this wave
@@ -392,6 +403,21 @@ void attn_partial_kernel(AttnArgs a) {
   }
 }
 
+// The partials of stream (r, g): first index and count (0 when the request
+// has no context).  Workgroup w holds the piece of every stream its range
+// meets, at index s + w.
+__device__ __forceinline__ int attn_pieces(const int32_t* off, int B, int Hkv, int r, int g,
+                                           long long& first) {
+  const int nr = off[r + 1] - off[r];
+  if (nr <= 0) return 0;
+  const long long P = (long long)off[B] * Hkv;
+  const int Gw = off[B + 1];
+  const long long x0 = (long long)off[r] * Hkv + (long long)g * nr, xe = x0 + nr - 1;
+  const int wlo = int(x0 * Gw / P), whi = int(xe * Gw / P);
+  first = (long long)r * Hkv + g + wlo;
+  return whi - wlo + 1;
+}
+
 // One wave per (slot, query head): lane = dim.  Lanes first share out the
 // chunks to find the max, then every chunk's weight is broadcast and the
 // weighted partial rows are summed with independent loads.
@@ -405,9 +431,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const int row = int(x / a.Hq), h = int(x % a.Hq);
     const int r = row / a.S, s = row % a.S, g = h / G, q = s * G + (h % G);
     uint16_t* dst = out + (long long)row * a.Hq * 64 + h * 64 + l;
-    if (a.rej[row] || a.seq_lens[r] <= 0) { *dst = 0; continue; }
-    const int c0 = s_off[r], nc = s_off[r + 1] - c0;
-    auto ml = [&](int ch) { return a.part_ml + ((long long)((c0 + ch) * a.Hkv + g) * QN + q) * 2; };
+    long long i0 = 0;
+    const int nc = a.rej[row] ? 0 : attn_pieces(s_off, a.B, a.Hkv, r, g, i0);
+    if (nc == 0) { *dst = 0; continue; }
+    auto ml = [&](int ch) { return a.part_ml + ((i0 + ch) * QN + q) * 2; };
     float M = -INFINITY;
     for (int ch = l; ch < nc; ch += 64) M = fmaxf(M, ml(ch)[0]);
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
@@ -426,7 +453,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll 4
         for (int j = 0; j < n; ++j) {
           const float wj = __shfl(wl, j, 64);
-          const long long it = (long long)(c0 + base + j) * a.Hkv + g;
+          const long long it = i0 + base + j;
           O += wj * a.part_o[(it * QN + q) * 64 + l];
         }
       }
@@ -457,9 +484,10 @@ __global__ __launch_bounds__(256) void attn_merge_group_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < G; ++j) O[j] = 0.f;
     float L = 0.f;
-    if (!a.rej[row] && a.seq_lens[r] > 0) {
-      const int c0 = s_off[r], nc = s_off[r + 1] - c0;
-      auto item = [&](int ch) { return (long long)(c0 + ch) * a.Hkv + g; };
+    long long i0 = 0;
+    const int nc = a.rej[row] ? 0 : attn_pieces(s_off, a.B, a.Hkv, r, g, i0);
+    if (nc > 0) {
+      auto item = [&](int ch) { return i0 + ch; };
       // unrolled so that the chunks' loads are in flight together
       float M = -INFINITY;
 #pragma unroll 8

@@ -196,11 +196,9 @@ struct AttnArgs {
   const int32_t* positions; const uint8_t* rej; const int32_t* seq_lens; const int32_t* bt;
   void* out;                      // [B*S, Hq*hd]
   float* part_o; float* part_ml;  // split-KV partials (bf16 path)
-  int32_t* plan_off;              // [B+1] first item row of each request, written by the partial kernel for the merge
+  int32_t* plan_off;              // [B+2] steps before each request, then the workgroups with a range; written by the partial kernel for the merge
   int vpr;                        // consecutive (virtual) requests per block-table row
-  int target_items;               // desired work items per launch
-  int grid;                       // persistent grid size
-  int slots;                      // workgroups resident at once (2 per CU)
+  int grid;                       // workgroups of the partial kernel (each takes an equal range of steps)
 };
 // ---- large-batch dense products (more than 256 rows) -------------------------
 // Dense products with more rows than PE_MM_MIN_ROWS run on launch_mm, smaller
@@ -224,7 +222,8 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 // capped by the request's seq_len (0 when the group has none).
 hipError_t launch_attn_group_lens(int Bv, int Sv, int vpr, const int32_t* positions, const uint8_t* rej,
                                   const int32_t* seq_lens, int32_t* out, hipStream_t st);
-// Upper bound on split-KV work items for B requests (sizes the partials).
-long long attn_max_items(int B, int Hkv, int target_items);
+// Split-KV partials of a launch over B requests with `grid` workgroups
+// (sizes the partial buffers).
+long long attn_max_items(int B, int Hkv, int grid);
 
 }  // namespace pe
