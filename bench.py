@@ -213,14 +213,18 @@ def measure(w, steps, warmup, prm=None, dev=None, label="", with_ar=True):
           file=sys.stderr, flush=True)
 
     # per-replay distribution (HIP events around each replay, after the timed
-    # region), then the same with the caches flushed before every replay: a
-    # 512 MiB in-place add on the stream ahead of the step evicts L2 and the
-    # 256 MB Infinity Cache, so the step starts with every weight in HBM
+    # region), then the same with the caches flushed before every replay.
+    # Reading 512 MiB on the stream ahead of the step (a max over the buffer)
+    # evicts L2 and the 256 MB Infinity Cache, so the step starts with every
+    # weight in HBM: the state after a target forward pass, which reads its
+    # weights and writes little.  An in-place add over the same buffer also
+    # leaves the caches full of dirty lines, whose write-back the step then
+    # pays as well: reported beside it as the write-flushed case.
     def replay_us(n, flush=None):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         for a, b in evs:
             if flush is not None:
-                flush.add_(1)
+                flush()
             a.record(stream)
             pb.pe_step_graph(ctx, B, args)
             b.record(stream)
@@ -228,12 +232,15 @@ def measure(w, steps, warmup, prm=None, dev=None, label="", with_ar=True):
         return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
     dist = replay_us(min(200, max(50, steps)))
     flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
-    cold = replay_us(min(50, max(20, steps // 4)), flush_buf)
-    del flush_buf
+    flush_words = flush_buf.view(torch.int32)
+    ncold = min(50, max(20, steps // 4))
+    cold = replay_us(ncold, lambda: torch.amax(flush_words))
+    cold_w = replay_us(ncold, lambda: flush_buf.add_(1))
+    del flush_buf, flush_words
     err = pb.pe_get_device_error(ctx)
     assert err == (0, -1), f"device error word {err}"
     print(f"[bench] {label} replays: median {np.median(dist):.1f} us, cache-flushed median "
-          f"{np.median(cold):.1f} us", file=sys.stderr, flush=True)
+          f"{np.median(cold):.1f} us (write-flushed {np.median(cold_w):.1f} us)", file=sys.stderr, flush=True)
 
     # the sequential comparison: the same kernels as K drafting passes, one graph
     ar = None
@@ -309,7 +316,13 @@ def measure(w, steps, warmup, prm=None, dev=None, label="", with_ar=True):
         "cache_flushed": {"replays": int(cold.size), "median_us": float(np.median(cold)),
                           "p10_us": float(np.percentile(cold, 10)), "p90_us": float(np.percentile(cold, 90)),
                           "value": B * K / (float(np.median(cold)) * 1e-6),
-                          "flush": "512 MiB in-place add on the stream before each replay (not timed)"},
+                          "flush": "max over a 512 MiB buffer on the stream before each replay (not timed): "
+                                   "L2 and Infinity Cache hold other, clean data",
+                          "write_flushed": {"median_us": float(np.median(cold_w)),
+                                            "p10_us": float(np.percentile(cold_w, 10)),
+                                            "p90_us": float(np.percentile(cold_w, 90)),
+                                            "flush": "512 MiB in-place add before each replay: the caches "
+                                                     "also hold dirty lines the step must write back"}},
         "eager_us_per_step": eager_ms * 1e3,
         "roofline": roof,
         "step": {"algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],

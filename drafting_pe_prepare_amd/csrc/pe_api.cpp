@@ -80,6 +80,7 @@ struct pe_ctx {
   int32_t* rmap = nullptr;      // [R] non-rejected slots of a large-batch pass, then their count
   int32_t* dmap = nullptr;      // [D] non-rejected draft rows of a large-batch pass, then their count
   uint8_t* qskip = nullptr;     // [R] last-layer attention: 0 for the non-rejected draft rows
+  float* ssq = nullptr;         // [16][d/16] per-tile sums of squares of x (RMSNorm folded into small-batch products)
   long long splitk_cap = 0;     // floats
   double* rope_turns = nullptr;  // RoPE frequencies in turns per position
   void* lm_packed = nullptr;  // fragment-order copy of the LM head (bf16)
@@ -155,7 +156,7 @@ void free_ctx(pe_ctx* c) {
   for (auto& r : c->recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   void* bufs[] = {c->x, c->u, c->q, c->attn, c->mlp, c->z, c->keys, c->err,
-                  c->part_o, c->part_ml, c->plan_off, c->rope_turns, c->lm_packed, c->splitk, c->group_lens, c->rmap, c->dmap, c->qskip,
+                  c->part_o, c->part_ml, c->plan_off, c->rope_turns, c->lm_packed, c->splitk, c->group_lens, c->rmap, c->dmap, c->qskip, c->ssq,
                   c->sample_lse, c->sample_keys, c->sample_parts};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
@@ -352,6 +353,10 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
     // sums over every row when larger)
     c->splitk_cap = std::max<long long>(16LL << 20, (long long)R * (qd + 2 * k.n_kv_heads * k.head_dim));
     if ((s = alloc(&c->splitk, size_t(c->splitk_cap) * 4, "split-K partials")) != PE_OK) {
+      free_ctx(c);
+      return s;
+    }
+    if ((s = alloc(&c->ssq, size_t(16) * pe::kSsqMaxParts * 4, "row sums of squares")) != PE_OK) {
       free_ctx(c);
       return s;
     }
@@ -575,6 +580,20 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     PE_HIP(pe::launch_draft_map(R, D, P.draft_rows, P.rej, ctx->dmap, ctx->dmap + D, ctx->qskip, st), "draft map");
   }
 
+  // RMSNorm folded into the small-batch products (at most 16 rows: every dense
+  // product runs on gemm_skinny): fc, O and down also write per-tile sums of
+  // squares of the x rows they store, and QKV and gate/up read x through the
+  // norm, so the attention and MLP norms need no launch of their own
+  const bool fold = pe::gemm_folds_norm(dt, R, d) && ctx->ssq && d % 16 == 0;
+  auto ssq_out = [&](pe::GemmArgs& g) {
+    if (fold) { g.ssq_out = ctx->ssq; g.ssq_n = d / 16; }
+  };
+  auto norm_in = [&](pe::GemmArgs& g, const void* gain) {
+    g.A = ctx->x;
+    g.ssq_in = ctx->ssq; g.ssq_n = d / 16;
+    g.norm_gain = gain; g.norm_eps = k.rms_eps;
+  };
+
   // a dense GEMM with its fused epilogue
   auto dense = [&](int aload, int bmap, int epi, const pe::GemmArgs& g, const char* what) -> pe_status {
     PE_HIP(pe::launch_gemm(dt, aload, bmap, epi, g, ctx->num_cus, st), what);
@@ -611,13 +630,15 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.rmap = nullptr;
       g.rcount = nullptr;
     }
+    ssq_out(g);
     if ((ds = dense(pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, "fc")) != PE_OK) return ds;
   }
   for (int l = 0; l < k.layers; ++l) {
     const pe_layer_weights& L = ctx->layers[l];
     const bool first_dd = l == 0 && dd;
     const bool last_draft = draft_only && l == k.layers - 1;
-    {
+    const bool fold_attn = fold && (l > 0 || !P.embed_input);  // the embedding gather writes no sums
+    if (!fold_attn) {
       Timed tm(ctx, PE_PH_NORM);
       if (first_dd)
         PE_HIP(pe::launch_rmsnorm_expand(Rc, d, ctx->xc, L.attn_norm, ctx->u, ctx->x, Kc, k.rms_eps, st),
@@ -634,6 +655,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.positions = P.pos; g.slots = P.slots;
       g.qout = ctx->q; g.kcache = k_cache[l]; g.vcache = v_cache[l];
       g.rope_turns = ctx->rope_turns;
+      if (fold_attn) norm_in(g, L.attn_norm);
       Timed tm(ctx, PE_PH_QKV);
       if (first_dd) {
         // compact rows; the epilogue covers every slot
@@ -688,10 +710,11 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.wo; g.Wp = packed(ctx, l, 1);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       if (last_draft) { g.M = R; g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
+      ssq_out(g);
       Timed tm(ctx, PE_PH_O);
       if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "o proj")) != PE_OK) return ds;
     }
-    {
+    if (!fold) {
       Timed tm(ctx, PE_PH_NORM);
       if (last_draft)  // the draft rows, in place
         PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, L.mlp_norm, ctx->u, P.draft_rows, R, k.rms_eps, st, true),
@@ -706,6 +729,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.w_gate; g.W1 = L.w_up; g.Wp = packed(ctx, l, 2);
       g.out = ctx->mlp; g.ldo = k.mlp;
       if (last_draft) { g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
+      if (fold) norm_in(g, L.mlp_norm);
       Timed tm(ctx, PE_PH_GATEUP);
       if ((ds = dense(pe::A_PLAIN, pe::B_GATEUP, pe::E_SILU, g, "gate/up")) != PE_OK) return ds;
     }
@@ -716,6 +740,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.W0 = L.w_down; g.Wp = packed(ctx, l, 3);
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       if (last_draft) { g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
+      ssq_out(g);  // the next layer's attention norm
       Timed tm(ctx, PE_PH_DOWN);
       if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "down")) != PE_OK) return ds;
     }

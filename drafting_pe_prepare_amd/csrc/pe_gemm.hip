@@ -317,7 +317,15 @@ __global__ __launch_bounds__(256) void argmax_tokens_kernel(int M, int Kd, int p
 // ---------------------------------------------------------------------------
 // bf16, M <= 64: split-K across the waves of a workgroup
 // ---------------------------------------------------------------------------
-template <int EPI, int AL, int BMAP, int MT, int NTW, int U>
+// NRM (one row tile, A_PLAIN): the A rows are x and the operand is their
+// RMSNorm, bf16((x * rs) * gain).  rs comes from the producer's per-tile sums
+// of squares (GemmArgs::ssq_in): LDS DMAs issued ahead of the first batch of
+// weights stage them (from byte 0, read only before every wave's first
+// batch ends) and the norm's gain (past the wave-partial and tile buffers,
+// which early waves fill while later ones still read the gain), and once
+// that batch has landed each row's partials are summed in a fixed order.
+// Kept in LDS, the gain takes no registers beside the batch.
+template <int EPI, int AL, int BMAP, int MT, int NTW, int U, int NRM>
 __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
   extern __shared__ float smem[];
   const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -352,19 +360,85 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // NRM: the 16 x ssq_n partial sums and the K gains go to LDS first (wave
+  // w's lanes move bytes [1 KB w, 1 KB (w + 1)) of each; 16 ssq_n <= 256 nw
+  // and 2 K <= 1 KB nw, checked on the host)
+  constexpr int PER = MT * NTW * 256;  // floats of one wave's partial tile
+  constexpr int LDT = NTW * 16 + 4;    // row stride of the staged output tile
+  const int kGainOff = (nw * PER + MT * 16 * LDT + 3) & ~3;  // floats: past both
+  // two DMAs per wave, unconditional so that every wave's vmcnt counts them
+  // (a lane past the end re-reads the last chunk into its own, unused slot);
+  // issued inside the first batch, after its A chunks and before its weights
+  auto stage_norm = [&]() {
+    const int e = (w * 64 + l) * 4;
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform: the DMA's LDS base goes to m0
+    dma16(g.ssq_in + min(e, 16 * g.ssq_n - 4), lds_addr((const unsigned char*)(smem + wu * 256)));
+    dma16((const uint16_t*)g.norm_gain + 2 * min(e, g.K / 2 - 4),
+          lds_addr((const unsigned char*)(smem + kGainOff + wu * 256)));
+  };
+  float rs = 1.f;
+  const uint16_t* gain = reinterpret_cast<const uint16_t*>(smem + kGainOff) + kg * 8;
+
   const uint4 zero = {0u, 0u, 0u, 0u};
   // U k-steps of loads in flight per batch, then their MFMAs
   for (int ks = ks0; ks < ks1; ks += U) {
     const int n = min(U, ks1 - ks);
     uint4 b[U][NTW], a[U][MT];
+    if constexpr (NRM) {
+      // the batch's A chunks, then its weights, every load unconditional (a
+      // step past the wave's range re-reads its last one; no MFMA uses it),
+      // so that waiting for the A chunks leaves exactly U*NTW loads in flight
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (u < n) {
-        const int k = (ks + u) * 32;
+      for (int u = 0; u < U; ++u) {
+        const int kk = ks + min(u, n - 1);
+        a[u][0] = ld16(ar[0].at(kk * 32 + kg * 8, g.d));  // row 0 stands in for rows past M
+      }
+      if (ks == ks0) stage_norm();
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) b[u][t] = ld16(wp[t] + (ks + u) * wstep);  // plain: stays cache-resident
+      for (int u = 0; u < U; ++u) {
+        const int kk = ks + min(u, n - 1);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? ld16(ar[mt].at(k + kg * 8, g.d)) : zero;
+        for (int t = 0; t < NTW; ++t) b[u][t] = ld16(wp[t] + kk * wstep);
+      }
+      wait_vmcnt<U * NTW>();  // A chunks landed (and, first time, the DMAs); weights in flight
+      if (ks == ks0) {  // every wave's first batch: the rows' rs
+        const float* sq = smem;  // free until the wave partials are reduced below
+        __shared__ float s_rs[16];
+        asm volatile("s_barrier" ::: "memory");  // no fence: the weights stay in flight
+        for (int i = w; i < 16; i += nw) {
+          float sacc = 0.f;
+          for (int p = l; p < g.ssq_n; p += 64) sacc += sq[i * g.ssq_n + p];
+          sacc = wave_sum(sacc);
+          // rows past M were never written by the producer: any rs (their A is zero)
+          if (l == 0) s_rs[i] = i < g.M ? rsqrtf(sacc / float(g.K) + g.norm_eps) : 1.f;
+        }
+        wait_lgkm0();
+        asm volatile("s_barrier" ::: "memory");
+        rs = s_rs[col];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u < n) {
+          const uint4 gv = *reinterpret_cast<const uint4*>(gain + (ks + u) * 32);
+          const uint16_t* e = reinterpret_cast<const uint16_t*>(&a[u][0]);
+          const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            o[q] = f2bf2(bf2f(e[2 * q]) * rs * bf2f(ge[2 * q]), bf2f(e[2 * q + 1]) * rs * bf2f(ge[2 * q + 1]));
+          a[u][0] = av[0] ? uint4{o[0], o[1], o[2], o[3]} : zero;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u < n) {
+          const int k = (ks + u) * 32;
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) b[u][t] = ld16(wp[t] + (ks + u) * wstep);  // plain: stays cache-resident
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? ld16(ar[mt].at(k + kg * 8, g.d)) : zero;
+        }
       }
     }
 #pragma unroll
@@ -379,7 +453,6 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
   }
 
   // fixed-order reduction of the wave partials
-  constexpr int PER = MT * NTW * 256;
   float* red = smem;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -388,7 +461,6 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[w * PER + ((mt * NTW + t) * 4 + i) * 64 + l] = acc[mt][t][i];
   __syncthreads();
-  constexpr int LDT = NTW * 16 + 4;
   float* tile = smem + nw * PER;
   for (int e = threadIdx.x; e < PER; e += blockDim.x) {
     float s = 0.f;
@@ -398,8 +470,33 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(GemmArgs g) {
     tile[(mt * 16 + (lane >> 4) * 4 + i) * LDT + t * 16 + (lane & 15)] = s;
   }
   __syncthreads();
-  if (EPI == E_ARGMAX) {
+  if constexpr (EPI == E_ARGMAX) {
     epilogue_argmax(g, tile, LDT, 0, MT * 16, n0, NTW * 16, blockIdx.x);
+  } else if constexpr ((EPI == E_STORE || EPI == E_RESID) && MT == 1 && NTW == 1) {
+    if (g.ssq_out) {
+      // store, keep the stored (rounded) values, then each row's sum of squares
+      const int mrows = min(16, g.M), ncols = min(16, g.N - n0);
+      for (int e = threadIdx.x; e < mrows * ncols; e += blockDim.x) {
+        const int i = e / ncols, c = e - i * ncols;
+        const long long o = (long long)i * g.ldo + n0 + c;
+        float v = tile[i * LDT + c];
+        if (EPI == E_RESID) v += bf2f(((const uint16_t*)g.resid)[o]);
+        const uint16_t h = f2bf(v);
+        ((uint16_t*)g.out)[o] = h;
+        tile[i * LDT + c] = bf2f(h);
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < mrows) {
+        float sacc = 0.f;
+        for (int c = 0; c < ncols; ++c) {
+          const float v = tile[threadIdx.x * LDT + c];
+          sacc += v * v;
+        }
+        g.ssq_out[(long long)threadIdx.x * g.ssq_n + blockIdx.x] = sacc;
+      }
+    } else {
+      epilogue<uint16_t, EPI>(g, tile, LDT, 0, MT * 16, n0, NTW * 16);
+    }
   } else {
     epilogue<uint16_t, EPI>(g, tile, LDT, 0, MT * 16, n0, NTW * 16);
   }
@@ -1161,6 +1258,10 @@ int gemm_argmax_parts(int dtype, int M, int N, int K, int num_cus) {
   }
 }
 
+bool gemm_folds_norm(int dtype, int M, int K) {
+  return dtype == 1 && M >= 1 && M <= 16 && K >= 32 && K % 32 == 0 && K / 16 <= kSsqMaxParts;
+}
+
 template <int EPI, int AL, int BMAP, int MT>
 static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
   constexpr int NTW = BMAP == B_PLAIN ? 1 : (BMAP == B_GATEUP && MT == 1) ? PE_SKINNY_NTW_GU : 2;
@@ -1169,14 +1270,36 @@ static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
   int nw = ksteps / 4;
   nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
   while (nw > 1 && nw * MT * NTW > 128) --nw;
-  const size_t lds = size_t(nw) * MT * NTW * 256 * 4 + size_t(MT * 16) * (NTW * 16 + 4) * 4;
+  size_t lds = size_t(nw) * MT * NTW * 256 * 4 + size_t(MT * 16) * (NTW * 16 + 4) * 4;
   const int grid = (g.N + NTW * 16 - 1) / (NTW * 16);
   if (EPI == E_ARGMAX && g.parts != grid) return hipErrorInvalidValue;
-  auto fn = gemm_skinny_kernel<EPI, AL, BMAP, MT, NTW, U>;
-  hipError_t e = set_lds(fn, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * nw), lds, st, g);
-  return hipGetLastError();
+  // folded RMSNorm: the producer writes one partial per 16-column tile
+  if (g.ssq_out && (MT != 1 || NTW != 1 || !(EPI == E_STORE || EPI == E_RESID) || g.ssq_n != grid))
+    return hipErrorInvalidValue;
+  auto launch = [&](auto fn) -> hipError_t {
+    hipError_t e = set_lds(fn, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * nw), lds, st, g);
+    return hipGetLastError();
+  };
+  if (g.norm_gain) {
+    if constexpr (MT == 1 && AL == A_PLAIN && (EPI == E_QKV || EPI == E_SILU)) {
+      if (!g.ssq_in || g.ssq_n < 1 || g.ssq_n > kSsqMaxParts || 16 * g.ssq_n > 256 * nw || 2 * g.K > 1024 * nw ||
+          g.K % 32 || g.M > 16)
+        return hipErrorInvalidValue;
+      // partials from byte 0 (their DMA slots, 1 KB per wave, lie inside the
+      // partial-reduction buffer); gains past that buffer and the tile, with
+      // room for every wave's 1 KB DMA slot
+      lds = (lds + 15) / 16 * 16 + std::max(size_t(g.K) * 2, size_t(1024) * nw);
+      // a batch of k-steps fewer than without the norm (its LDS reads and
+      // temporaries need the registers): QKV at K = 2880 keeps one batch per wave
+      constexpr int UN = NTW >= 4 ? U - 1 : U - 2;
+      return launch(gemm_skinny_kernel<EPI, AL, BMAP, MT, NTW, UN, 1>);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  return launch(gemm_skinny_kernel<EPI, AL, BMAP, MT, NTW, U, 0>);
 }
 
 template <int U>
@@ -1477,6 +1600,7 @@ static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
       default: return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN, 4, 2, 2>(g, st, num_cus);
     }
   } else {
+    if ((g.norm_gain || g.ssq_out) && v != V_SKINNY) return hipErrorInvalidValue;  // folded norm: small batches only
     switch (v) {
       case V_SKINNY:
         if (g.M <= 16) return run_skinny<EPI, AL, BMAP, 1>(g, st);

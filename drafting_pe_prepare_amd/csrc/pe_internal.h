@@ -160,7 +160,23 @@ struct GemmArgs {
   // rows the tile shape is chosen for (0: M); with a row map the count is
   // known only on the device, and this is its expected size
   int plan_rows;
+  // RMSNorm folded into small-batch products (at most 16 rows, every dense
+  // product on gemm_skinny).  A producer of x (E_STORE / E_RESID) with
+  // ssq_out set also writes, for each 16-column tile p of its output, the sum
+  // of squares of every stored (rounded) row: ssq_out[row * ssq_n + p].  A
+  // consumer (A_PLAIN) with norm_gain set reads its A rows x through the
+  // norm: rs = rsqrt(sum_p ssq_in[row * ssq_n + p] / K + norm_eps), operand
+  // bf16((x * rs) * gain), as rmsnorm_kernel would have stored it.
+  float* ssq_out;
+  const float* ssq_in;
+  const void* norm_gain;
+  float norm_eps;
+  int ssq_n;
 };
+// Whether a product of M rows can take its RMSNorm folded in (see GemmArgs):
+// bf16, at most 16 rows, K % 32 == 0, K / 16 <= kSsqMaxParts partial sums.
+constexpr int kSsqMaxParts = 256;
+bool gemm_folds_norm(int dtype, int M, int K);
 // rows of an M-row operand with rpr rows per request that belong to active requests
 __device__ __forceinline__ int active_rows(const int32_t* nact, int rpr, int M) {
   if (!nact) return M;
