@@ -180,6 +180,28 @@ def step_inputs(w: Workload, seed: int = None, kv: bool = True, extra: int = 0) 
     return out
 
 
+def round_ring(w: Workload, inp: dict, n: int, seed: int = None) -> dict:
+    """n rounds of the per-round draws, for rotating a step's inputs between
+    timed replays: accepted counts, bonus and verify tokens, target tokens.
+    Round 0 is `inp` itself (step_inputs' draw); rounds 1..n-1 are drawn like
+    it from streams of their own.  Prefix lengths, block tables, hidden
+    states and the KV pool stay those of `inp`."""
+    s = w.seed if seed is None else seed
+    B, K = w.batch, w.K
+    keys = ("num_accepted", "bonus_tokens", "verify_tokens", "target_tokens")
+    out = {k: [np.asarray(inp[k], dtype=np.int32)] for k in keys}
+    for i in range(1, n):
+        if w.accepted == "uniform":
+            a = integers(s, f"ring{i}.num_accepted", 0, K + 1, (B,))
+        else:
+            a = np.full(B, int(w.accepted), dtype=np.int32)
+        out["num_accepted"].append(a)
+        out["bonus_tokens"].append(integers(s, f"ring{i}.bonus", 0, w.vocab - 1, (B,)))
+        out["verify_tokens"].append(integers(s, f"ring{i}.verify_tokens", 0, w.vocab - 1, (B, K + 1)))
+        out["target_tokens"].append(integers(s, f"ring{i}.target_tokens", 0, w.vocab - 1, (B, K + 1)))
+    return {k: np.stack(v) for k, v in out.items()}
+
+
 def prefill_inputs(w: Workload, S: int, lens, start, seed: int = None, kv: bool = True) -> dict:
     """Inputs of a drafting round that follows a prompt (or a chunk of one):
     per request a chunk of prompt tokens, its length n, the position c0 it

@@ -175,3 +175,25 @@ def test_gather_mask_rows_are_h_shared_and_copies_are_exact():
             np.testing.assert_array_equal(Hd[s], hs)
         else:
             np.testing.assert_array_equal(Hd[s], H[src])
+
+
+def test_replay_ring_rounds_are_valid_inputs():
+    """Every round of the pre-drawn ring the bench rotates through is a batch
+    the preparation accepts with no error (accepted counts in 0..K, token ids
+    in range), round 0 is the step's own draw, and the rounds differ."""
+    from drafting_pe_prepare_amd import configs, synth
+    for w in (configs.C1, configs.C64):
+        inp = synth.step_inputs(w, kv=False)
+        ring = synth.round_ring(w, inp, 32)
+        B, K = w.batch, w.K
+        assert ring["num_accepted"].shape == (32, B)
+        assert ring["verify_tokens"].shape == (32, B, K + 1)
+        np.testing.assert_array_equal(ring["num_accepted"][0], inp["num_accepted"])
+        np.testing.assert_array_equal(ring["target_tokens"][0], inp["target_tokens"])
+        assert len({tuple(r.tolist()) for r in ring["verify_tokens"].reshape(32, -1)}) == 32
+        for i in (0, 1, 31):
+            out = O.prepare(ring["verify_tokens"][i], inp["verify_positions"], ring["num_accepted"][i],
+                            ring["bonus_tokens"][i], inp["block_table"], inp["num_kv_blocks"], K,
+                            w.vocab, w.vocab - 1, w.block_size)
+            assert out["error_kinds"] == 0
+            assert np.all((ring["num_accepted"][i] >= 0) & (ring["num_accepted"][i] <= K))
