@@ -405,7 +405,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       return s;
     }
     // the MASK-deduplicated first-layer fc rows of a parallel step (large batches)
-    if (size_t(k.max_num_seqs) * (k.K + 2) > size_t(pe::kMmMinRows) && k.K >= 3) {
+    if (size_t(k.max_num_seqs) * (k.K + 2) > size_t(pe::kRowMapMinRows) && k.K >= 3) {
       if ((s = alloc(&c->xc, size_t(k.max_num_seqs) * (k.K + 2) * k.d * 2, "deduplicated fc rows")) != PE_OK) {
         free_ctx(c);
         return s;
@@ -560,10 +560,10 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   g0.part_cap = ctx->splitk_cap;
   g0.nact = ctx->nact;
   g0.rpr = S;
-  // the large-batch dense products compute only the non-rejected slots: a
+  // the dense products above 64 rows compute only the non-rejected slots: a
   // rejected slot's outputs are never read (no KV write, no attention, not a
   // draft row); the map comes from the batch's rejected mask
-  if (dt == PE_BF16 && R > pe::kMmMinRows) {
+  if (dt == PE_BF16 && R > pe::kRowMapMinRows) {
     Timed tm(ctx, PE_PH_FC);
     PE_HIP(pe::launch_compact_rows(R, P.rej, ctx->rmap, ctx->rmap + R, st), "row map");
     g0.rmap = ctx->rmap;
@@ -572,9 +572,9 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
 
   // The last layer after its QKV product (which writes every valid slot's
   // KV): only the draft rows feed the LM head, so attention keeps only their
-  // queries and the O product, MLP norm and MLP run on their rows alone (the
-  // large-batch kernels, through a row map of the non-rejected draft rows).
-  const bool draft_only = dt == PE_BF16 && R > pe::kMmMinRows && D > pe::kMmMinRows && P.draft_rows;
+  // queries and the O product, MLP norm and MLP run on their rows alone
+  // (through a row map of the non-rejected draft rows).
+  const bool draft_only = dt == PE_BF16 && R > pe::kRowMapMinRows && D > pe::kRowMapMinRows && P.draft_rows;
   if (draft_only) {
     Timed tm(ctx, PE_PH_FC);
     PE_HIP(pe::launch_draft_map(R, D, P.draft_rows, P.rej, ctx->dmap, ctx->dmap + D, ctx->qskip, st), "draft map");
@@ -608,7 +608,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   // one MASK slot), the norm writes the fc rows out to every slot, and the QKV
   // epilogue (RoPE at each slot's own position, KV write) runs for every slot.
   const int Kc = k.K, Rc = B * (Kc + 2);
-  const bool dd = P.parallel_layout && dt == PE_BF16 && ctx->xc && Kc >= 3 && Rc > pe::kMmMinRows;
+  const bool dd = P.parallel_layout && dt == PE_BF16 && ctx->xc && Kc >= 3 && Rc > pe::kRowMapMinRows;
 
   if (P.embed_input) {
     Timed tm(ctx, PE_PH_GATHER);

@@ -654,10 +654,31 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz64(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
+// Split of a dense tiled product with a row map, chosen on the device from the
+// rows it computes (the map's count is known only there): the T = row tiles x
+// column tiles (in whole groups of 8, see the block mapping) run as
+// ks = floor(slots / T) copies over k when T < slots, each of at least
+// PE_SPLITK_MIN_KTILES k-tiles and within `cap` copies of the partial buffer.
+struct TilePlan { int mt, per, ks; };
+__host__ __device__ inline TilePlan tile_plan(int rows, int BM, int ntiles, int nk, int slots, int cap) {
+  TilePlan p;
+  p.mt = (rows + BM - 1) / BM;
+  p.per = p.mt * ((ntiles + 7) / 8) * 8;
+  p.ks = 1;
+  if (slots > 0 && p.per > 0 && p.per < slots) {
+    int ks = slots / p.per;
+    const int kmax = nk / PE_SPLITK_MIN_KTILES;
+    ks = ks < kmax ? ks : kmax;
+    ks = ks < cap ? ks : cap;
+    p.ks = ks > 1 ? ks : 1;
+  }
+  return p;
+}
+
 
 template <int EPI, int AL, int BMAP, int BM, int BN, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
+void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0, int dslots, int dcap) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int TI = BM / WM / 16, TJ = BN / WN / 16;   // MFMA tiles per wave
   // DMA instructions per wave per k-tile; A's row groups may not split evenly
@@ -677,12 +698,32 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
   // summing k-tiles [ks nk / ksplit, (ks + 1) nk / ksplit); the copies are
   // multiples of 8 workgroups, so the XCD of a workgroup is unchanged
   int bid = blockIdx.x, ks = 0, kbase = 0, nk = g.K / 64, mt, nt;
+  // rows computed: those of active requests (occupancy below the captured
+  // batch skips the rest) and, with a row map, the compact rows, compact row
+  // m standing for row rmap[m] of A and of the output; tiles past them exit
+  int rows = active_rows(g.nact, g.rpr, g.M);
+  if (g.rmap) rows = min(rows, *g.rcount);
+  int mtg = mtiles;        // row tiles of the block mapping
+  bool part = EPI == E_PART;  // write fp32 partials instead of the epilogue
   if constexpr (EPI == E_PART) {
     const int per = mtiles * ((ntiles + 7) / 8) * 8;
     ks = bid / per;
     bid -= ks * per;
     kbase = ks * nk / g.ksplit;
     nk = (ks + 1) * nk / g.ksplit - kbase;
+  } else if constexpr (EPI != E_ARGMAX) {
+    if (dslots > 0) {  // the split is planned here, from the rows computed
+      const TilePlan p = tile_plan(rows, BM, ntiles, nk, dslots, dcap);
+      if (bid >= p.per * p.ks) return;
+      mtg = p.mt;
+      if (p.ks > 1) {
+        part = true;
+        ks = bid / p.per;
+        bid -= ks * p.per;
+        kbase = ks * nk / p.ks;
+        nk = (ks + 1) * nk / p.ks - kbase;
+      }
+    }
   }
   // LM head with a split tail (E_ARGMAX, tail0 < ntiles): column tiles
   // [0, tail0) run whole; each tile of [tail0, ntiles) runs as ksplit k-range
@@ -702,13 +743,13 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
     nk = (ks + 1) * nk / g.ksplit - kbase;
   } else {
     const int j = bid >> 3;
-    mt = j % mtiles;
-    nt = (j / mtiles) * 8 + (bid & 7);
+    mt = j % mtg;
+    nt = (j / mtg) * 8 + (bid & 7);
     if (nt >= tail0) return;  // padding workgroup of the XCD-aligned grid
   }
   const int m0 = mt * BM, n0 = nt * BN;
-  // rows of inactive requests (occupancy below the captured batch) are skipped
-  if (m0 >= active_rows(g.nact, g.rpr, g.M)) return;
+  if (m0 >= rows) return;
+  auto out_row = [&](int m) { return g.rmap ? g.rmap[m] : m; };
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
   const int wm = w / WN, wn = w % WN;
 
@@ -718,7 +759,7 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
   const uint16_t* bp[LB];
   const int lr = l >> 3, lc = ((l & 7) ^ (lr & 7)) * 8;  // rows are 8-aligned: row & 7 == lr
 #pragma unroll
-  for (int i = 0; i < LA; ++i) ar[i].init(g, min(m0 + 8 * (w + NW * i) + lr, g.M - 1));
+  for (int i = 0; i < LA; ++i) ar[i].init(g, out_row(min(m0 + 8 * (w + NW * i) + lr, rows - 1)));
 #pragma unroll
   for (int i = 0; i < LB; ++i) bp[i] = weight_row<uint16_t, BMAP>(g, min(n0 + 8 * (w + NW * i) + lr, g.N - 1)) + lc;
   auto issue = [&](unsigned char* st, int kt) {
@@ -815,20 +856,22 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
   }
 
   // lane (kg, col) holds C[row 4kg + r of MFMA tile i][col of tile jj]
-  if constexpr (EPI == E_PART) {
+  if (EPI != E_ARGMAX && part) {
     float* P = g.part + (long long)ks * g.M * g.N;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * (BM / WM) + i * 16 + kg * 4 + r;
-        if (m >= g.M) continue;
+        if (m >= rows) continue;  // partials by compact row: the reduction maps them
 #pragma unroll
         for (int jj = 0; jj < TJ; ++jj) {
           const int n = n0 + wn * (BN / WN) + jj * 16 + col;
           if (n < g.N) P[(long long)m * g.N + n] = acc[i][jj][r];
         }
       }
+  } else if constexpr (EPI == E_PART) {
+    // (always split: handled above)
   } else if constexpr (EPI == E_ARGMAX) {
     if (tail) {
       // partial tile [BM][BN] of piece ks of tail tile (nt - tail0, mt)
@@ -908,7 +951,7 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
       for (int e = l; e < WTM * SEG; e += 64) {
         const int rr = e / SEG, sg = e % SEG, q = sg >> 1, c0 = (sg & 1) * 8;
         const int m = mw + rr;
-        if (m >= g.M || nw0 + 32 * q >= g.N) continue;
+        if (m >= rows || nw0 + 32 * q >= g.N) continue;
         float v[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -917,18 +960,18 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
         }
         uint4 o;
         o.x = f2bf2(v[0], v[1]); o.y = f2bf2(v[2], v[3]); o.z = f2bf2(v[4], v[5]); o.w = f2bf2(v[6], v[7]);
-        *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)m * g.ldo + (nw0 >> 1) + 16 * q + c0) = o;
+        *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)out_row(m) * g.ldo + (nw0 >> 1) + 16 * q + c0) = o;
       }
     } else {
       constexpr int SEG = WTN / 8;
       for (int e = l; e < WTM * SEG; e += 64) {
         const int rr = e / SEG, c0 = (e % SEG) * 8;
         const int m = mw + rr, n = nw0 + c0;
-        if (m >= g.M || n >= g.N) continue;
+        if (m >= rows || n >= g.N) continue;
         const float4 a0 = *reinterpret_cast<const float4*>(ct + cpos(rr, c0));
         const float4 a1 = *reinterpret_cast<const float4*>(ct + cpos(rr, c0 + 4));
         float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const long long o = (long long)m * g.ldo + n;
+        const long long o = (long long)out_row(m) * g.ldo + n;
         if constexpr (EPI == E_RESID) {
           const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + o);
           const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
@@ -948,8 +991,9 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0) {
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * (BM / WM) + i * 16 + kg * 4 + r;
-        if (m >= g.M) continue;
+        const int mc = m0 + wm * (BM / WM) + i * 16 + kg * 4 + r;
+        if (mc >= rows) continue;
+        const int m = out_row(mc);
         if (EPI == E_STORE || EPI == E_RESID) {
 #pragma unroll
           for (int jj = 0; jj < TJ; ++jj) {
@@ -1273,6 +1317,7 @@ static hipError_t run_skinny(const GemmArgs& g, hipStream_t st) {
   size_t lds = size_t(nw) * MT * NTW * 256 * 4 + size_t(MT * 16) * (NTW * 16 + 4) * 4;
   const int grid = (g.N + NTW * 16 - 1) / (NTW * 16);
   if (EPI == E_ARGMAX && g.parts != grid) return hipErrorInvalidValue;
+  if (g.rmap) return hipErrorInvalidValue;  // row maps: the tiled and large-batch kernels only
   // folded RMSNorm: the producer writes one partial per 16-column tile
   if (g.ssq_out && (MT != 1 || NTW != 1 || !(EPI == E_STORE || EPI == E_RESID) || g.ssq_n != grid))
     return hipErrorInvalidValue;
@@ -1402,7 +1447,7 @@ static hipError_t run_tiled(const GemmArgs& g, hipStream_t st, int slots = 0) {
   const int ntail = (ntiles - tail0) * ks;
   const int grid = mtiles * ((tail0 + 7) / 8) * 8 + (ntail ? mtiles * ((ntail + 7) / 8) * 8 : 0);
   hipLaunchKernelGGL((gemm_tiled_kernel<EPI, AL, BMAP, BM, BN, WM, WN, S>), dim3(grid),
-                     dim3(64 * WM * WN), 0, st, ga, mtiles, ntiles, tail0);
+                     dim3(64 * WM * WN), 0, st, ga, mtiles, ntiles, tail0, 0, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !ntail) return e;
   if constexpr (EPI == E_ARGMAX) {
@@ -1419,10 +1464,17 @@ static hipError_t run_tiled(const GemmArgs& g, hipStream_t st, int slots = 0) {
 // have fused runs on the sum.  Store / residual: 8 consecutive columns per
 // thread; SiLU.mul: 8 outputs from 8 gate and 8 up columns; QKV: one RoPE pair.
 template <int EPI>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
-  const int KS = g.ksplit;
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int BM, int ntiles, int dslots, int dcap) {
+  // with a row map: partial row m (compact) is output row rmap[m]; rows past
+  // the compact count were not computed
+  const int rows = g.rmap ? min(g.M, *g.rcount) : g.M;
+  // a split planned on the device (dslots > 0): the same plan as the product's
+  const int KS = dslots > 0 ? tile_plan(min(rows, active_rows(g.nact, g.rpr, g.M)), BM, ntiles, g.K / 64, dslots, dcap).ks
+                            : g.ksplit;
+  if (KS <= 1) return;  // the product ran its epilogue itself
   const long long MN = (long long)g.M * g.N;
   const long long stride = (long long)gridDim.x * blockDim.x;
+  auto out_row = [&](int m) { return g.rmap ? g.rmap[m] : m; };
   auto sum8 = [&](int m, int n, float (&v)[8]) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) v[t] = 0.f;
@@ -1435,11 +1487,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   };
   if constexpr (EPI == E_STORE || EPI == E_RESID) {
     const int per_row = g.N / 8;
-    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)g.M * per_row; e += stride) {
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
       const int m = int(e / per_row), n = int(e % per_row) * 8;
       float v[8];
       sum8(m, n, v);
-      const long long o = (long long)m * g.ldo + n;
+      const long long o = (long long)out_row(m) * g.ldo + n;
       if constexpr (EPI == E_RESID) {
         const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + o);
         const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
@@ -1456,7 +1508,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   } else if constexpr (EPI == E_SILU) {
     // logical columns (32q + c, 32q + 16 + c) -> output column 16q + c
     const int per_row = g.N / 16;
-    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)g.M * per_row; e += stride) {
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
       const int m = int(e / per_row), pc = int(e % per_row), q = pc >> 1, c0 = (pc & 1) * 8;
       float gt[8], up[8], v[8];
       sum8(m, 32 * q + c0, gt);
@@ -1465,7 +1517,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
       for (int t = 0; t < 8; ++t) v[t] = gt[t] / (1.0f + expf(-gt[t])) * up[t];
       uint4 o;
       o.x = f2bf2(v[0], v[1]); o.y = f2bf2(v[2], v[3]); o.z = f2bf2(v[4], v[5]); o.w = f2bf2(v[6], v[7]);
-      *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)m * g.ldo + 16 * q + c0) = o;
+      *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)out_row(m) * g.ldo + 16 * q + c0) = o;
     }
   } else {
     static_assert(EPI == E_QKV, "split-K epilogues: store, residual, SiLU.mul, QKV");
@@ -1473,9 +1525,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
     // partners 16 further, so q and k leave as 16-byte stores (V is d-major
     // inside a block: one element per position row)
     const int per_row = g.N / 16;
-    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)g.M * per_row; e += stride) {
-      const int m = int(e / per_row), pr = int(e % per_row), nb = (pr >> 1) * 32, c0 = (pr & 1) * 8;
-      const int cm = g.dedup_k ? dedup_row(m, g.dedup_k) : m;  // row of the sums (one split then)
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
+      const int mr = int(e / per_row), pr = int(e % per_row), nb = (pr >> 1) * 32, c0 = (pr & 1) * 8;
+      const int cm = g.dedup_k ? dedup_row(mr, g.dedup_k) : mr;  // row of the sums (one split then)
+      const int m = out_row(mr);  // row of the positions, slots and q rows
       float lo[8], hi[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) lo[t] = hi[t] = 0.f;
@@ -1544,6 +1597,29 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
   if (g.K % 64) return hipErrorInvalidValue;
   const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN, nk = g.K / 64;
   const long long tiles = (long long)mtiles * ntiles, target = (long long)PE_SPLITK_WG_PER_CU * num_cus;
+  const long long work = (long long)g.M * (EPI == E_QKV || EPI == E_SILU ? g.N / 16 : g.N / 8);
+  const long long blocks = std::min<long long>((work + 255) / 256, 8LL * num_cus);
+  if (g.rmap) {
+    // row map: the rows are counted on the device, which plans the split; the
+    // grid covers the largest plan of any row count up to M
+    const int slots = int(target);
+    const long long capl = g.part ? std::min<long long>(g.part_cap / ((long long)g.M * g.N), 64) : 0;
+    const int cap = int(capl);
+    const bool can_split = g.part && g.N % 32 == 0 && nk / PE_SPLITK_MIN_KTILES >= 2 && cap >= 2;
+    const int dslots = can_split ? slots : 0;
+    long long grid = 0;
+    for (int mt = 1; mt <= mtiles; ++mt) {
+      const TilePlan p = tile_plan(mt * BM, BM, ntiles, nk, dslots, cap);
+      grid = std::max<long long>(grid, (long long)p.per * p.ks);
+    }
+    hipLaunchKernelGGL((gemm_tiled_kernel<EPI, AL, BMAP, BM, BN, WM, WN, S>), dim3(unsigned(grid)),
+                       dim3(64 * WM * WN), 0, st, g, mtiles, ntiles, ntiles, dslots, cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !can_split) return e;
+    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, st, g, BM, ntiles, dslots,
+                       cap);
+    return hipGetLastError();
+  }
   long long ks = 1;
   if (g.part && tiles < num_cus && g.N % 32 == 0) {
     ks = (target + tiles - 1) / tiles;
@@ -1555,12 +1631,10 @@ static hipError_t run_tiled_dense(const GemmArgs& g, int num_cus, hipStream_t st
   gp.ksplit = int(ks);
   const long long per = (long long)mtiles * ((ntiles + 7) / 8) * 8;
   hipLaunchKernelGGL((gemm_tiled_kernel<E_PART, AL, BMAP, BM, BN, WM, WN, S>), dim3(unsigned(per * ks)),
-                     dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles, ntiles);
+                     dim3(64 * WM * WN), 0, st, gp, mtiles, ntiles, ntiles, 0, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long work = (long long)g.M * (EPI == E_QKV || EPI == E_SILU ? g.N / 16 : g.N / 8);
-  const long long blocks = std::min<long long>((work + 255) / 256, 8LL * num_cus);
-  hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, st, gp);
+  hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(unsigned(blocks)), dim3(256), 0, st, gp, BM, ntiles, 0, 0);
   return hipGetLastError();
 }
 
@@ -1575,7 +1649,8 @@ static hipError_t run_ring(const GemmArgs& g, int num_cus, hipStream_t st) {
 
 template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
-  if (EPI != E_ARGMAX && g.M > kMmMinRows) return launch_mm(AL, BMAP, EPI, g, num_cus, st);
+  if (EPI != E_ARGMAX && (g.M > kMmMinRows || (g.M > kRowMapMinRows && EPI != E_SILU)))
+    return launch_mm(AL, BMAP, EPI, g, num_cus, st);
   if (g.dedup_k) return hipErrorInvalidValue;  // compact first-layer rows: large batches only
   const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);
   if constexpr (EPI == E_ARGMAX) {

@@ -217,16 +217,20 @@ struct AttnArgs {
   int grid;                       // workgroups of the partial kernel (each takes an equal range of steps)
 };
 // ---- large-batch dense products (more than 256 rows) -------------------------
-// Dense products with more rows than PE_MM_MIN_ROWS run on launch_mm, smaller
-// ones on the kernels of pe_gemm.hip (the 4-layer d=2048 drafter at 96-224
-// rows: K=5 796 -> 735 us, K=7 815 -> 758 us per step with the 16x16x32 ring
-// of pe_gemm.hip instead of launch_mm).  The LM head stays on pe_gemm.hip at
-// every size: at 448 rows x 201088 x 2880 its ring (224 x 256 tiles) measured
-// 524-568 us against 572-692 us for the best 32x32x16 tiles.
+// Dense products with more rows than PE_MM_MIN_ROWS run on launch_mm; from
+// kRowMapMinRows + 1 rows up so do all but gate/up (a four-stage ring of
+// 64 x 128 tiles, see pe_mm.hip); smaller ones, and gate/up up to
+// PE_MM_MIN_ROWS rows, on the kernels of pe_gemm.hip.  The LM head stays on
+// pe_gemm.hip at every size: at 448 rows x 201088 x 2880 its ring (224 x 256
+// tiles) measured 524-568 us against 572-692 us for the best 32x32x16 tiles.
 #ifndef PE_MM_MIN_ROWS
 #define PE_MM_MIN_ROWS 256
 #endif
 constexpr int kMmMinRows = PE_MM_MIN_ROWS;
+// Row maps (GemmArgs::rmap: rejected slots skipped, the last layer's draft
+// rows only) from this many rows up: such products run on gemm_tiled (65..256
+// rows) or the large-batch kernels, never on gemm_skinny.
+constexpr int kRowMapMinRows = 64;
 // 32x32x16 MFMA tiles; QKV and gate/up pair their epilogue columns 32 apart
 // (see pe_mm.hip).  E_QKV runs on fp32 sums (g.part); with g.dedup_k the
 // product covers the K+2 compact rows per request and the epilogue every slot.

@@ -472,11 +472,18 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
 // measured at c=64 they pay off only for gate/up (896 x 15360 x 2880: 90 us
 // against 102), where they still fill the chip: the other products, with
 // 2880-5120 output columns, run 20-30% slower on them (fewer, split tiles).
-struct TileSmall { static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, WGPC = 2; };
-struct TileLarge { static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, WGPC = 1; };
-struct TileMid { static constexpr int BM = 192, BN = 256, WM = 2, WN = 4, WGPC = 1; };
-struct TileWide { static constexpr int BM = 256, BN = 128, WM = 2, WN = 2, WGPC = 1; };
-constexpr int kDKT = 64, kDS = 2;
+struct TileSmall { static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, WGPC = 2, S = 2, OCC = 2; };
+struct TileLarge { static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, WGPC = 1, S = 2, OCC = 2; };
+struct TileMid { static constexpr int BM = 192, BN = 256, WM = 2, WN = 4, WGPC = 1, S = 2, OCC = 2; };
+struct TileWide { static constexpr int BM = 256, BN = 128, WM = 2, WN = 2, WGPC = 1, S = 2, OCC = 2; };
+// 65..256 rows (fc, QKV, O, down; the K-sweep drafter): 64 x 128 tiles, one
+// workgroup of four waves per CU with a four-stage ring, so three k-tiles are
+// in flight when each workgroup has few rows of work per k-tile.  Measured on
+// the K-sweep drafter (K = 7): down 94 -> 86, QKV 84 -> 80, fc 36 -> 30 us
+// against the 16x16x32 tiled kernel; gate/up, with enough tiles for two
+// workgroups per CU, stays there (133 against 156 us).
+struct TileDeep { static constexpr int BM = 64, BN = 128, WM = 2, WN = 2, WGPC = 1, S = 4, OCC = 1; };
+constexpr int kDKT = 64;
 
 template <int EPI, int AL, int BMAP, class T>
 static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
@@ -496,7 +503,7 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
     const MmPlan p = mm_plan(mt * BM, BM, ntiles, g.K / 64, slots, cap_splits);
     grid = std::max(grid, p.per * p.ks);
   }
-  hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, kDKT, kDS, 2>), dim3(unsigned(grid)),
+  hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, kDKT, T::S, T::OCC>), dim3(unsigned(grid)),
                      dim3(64 * WM * WN), 0, st, g, ntiles, slots, cap_splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (EPI != E_QKV && !can_split)) return e;
@@ -525,6 +532,7 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
 #endif
 template <int EPI, int AL, int BMAP>
 static hipError_t mm_tiles(int tile, const GemmArgs& g, int num_cus, hipStream_t st) {
+  if (g.M <= kMmMinRows) return mm_dense<EPI, AL, BMAP, TileDeep>(g, num_cus, st);
   switch (tile) {
     case 1: return mm_dense<EPI, AL, BMAP, TileLarge>(g, num_cus, st);
     case 2: return mm_dense<EPI, AL, BMAP, TileMid>(g, num_cus, st);
@@ -559,7 +567,7 @@ hipError_t launch_mm(int aload, int bmap, int epi, const GemmArgs& g, int num_cu
     }
     return mm_tiles<E_SILU, A_PLAIN, B_GATEUP>(t, g, num_cus, st);
   }
-  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_STORE) return mm_dense<E_STORE, A_PLAIN, B_PLAIN, TileSmall>(g, num_cus, st);
+  if (aload == A_PLAIN && bmap == B_PLAIN && epi == E_STORE) return mm_tiles<E_STORE, A_PLAIN, B_PLAIN>(0, g, num_cus, st);
   return hipErrorInvalidValue;
 }
 

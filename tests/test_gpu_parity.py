@@ -87,8 +87,12 @@ def test_small_bf16_gqa8(K, B, seed):
 
 
 @pytest.mark.parametrize("dtype,layers,K,B,seed", [("f32", 2, 3, 2, 71), ("bf16", 3, 4, 3, 72),
-                                                   ("bf16", 4, 1, 16, 73)])
+                                                   ("bf16", 4, 1, 16, 73), ("bf16", 2, 7, 10, 74),
+                                                   ("bf16", 3, 5, 9, 75)])
 def test_small_multilayer(dtype, layers, K, B, seed):
+    """Several layers; (K=7, B=10) and (K=5, B=9) are 140 and 90 slots: the
+    65..256-row tiled products skip rejected slots through a row map, and the
+    last layer (70 draft rows at K=7) computes its draft rows only."""
     base = configs.TINY if dtype == "f32" else SMALL_BF16
     w = base.with_(K=K, batch=B, layers=layers, accepted="uniform", prefix=("uniform", 30, 300))
     _full_check(w, seed)
