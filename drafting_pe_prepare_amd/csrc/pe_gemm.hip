@@ -644,15 +644,18 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
 // row, 16 bytes per lane.  Rows split into half lines (32-wide k-tiles) stream
 // ~1.4x slower through this path (measured on a loads-only copy of the loop).
 // LDS: tile row r takes 128 bytes and its 16-byte chunk c sits at slot
-// c ^ (r & 7), so the 8 lanes of a fragment-read phase hit 8 distinct slots.
-// Every fragment row of a wave has r & 7 == col & 7, so fragment i is one base
-// offset plus i * 2 KB.
+// c ^ ((r >> 1) & 7).  gfx950 serves a 16-byte LDS read 16 lanes per clock
+// over 64 banks (256 bytes); the 16 lanes of a fragment read take rows
+// r0 .. r0+15 at one chunk, and under this key those fall on 16 distinct
+// 16-byte bank groups (with c ^ (r & 7), rows r and r + 8 shared one: a
+// two-way conflict on every read).  Fragment rows r0 + 16i share (r >> 1) & 7,
+// so fragment i is one base offset plus i * 2 KB.
 //
 // A k-tile feeds two 32-wide MFMA substeps; the fragments of the next substep
 // are read while the MFMAs of the current one run, and there is one barrier
 // per k-tile.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz64(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+__device__ __forceinline__ int swz64(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 // Split of a dense tiled product with a row map, chosen on the device from the
 // rows it computes (the map's count is known only there): the T = row tiles x
@@ -753,22 +756,29 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0, int dslots
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, kg = l >> 4;
   const int wm = w / WN, wn = w % WN;
 
-  // DMA instruction i of this wave fills tile rows 8 (w + NW i) .. +7; lane l
-  // takes row + l/8 and LDS slot l%8, i.e. global chunk (l%8) ^ (row & 7)
+  // DMA instruction i of this wave fills tile rows r = 8 (w + NW i) + l/8
+  // (lane l), LDS slot l%8, i.e. global chunk (l%8) ^ ((r >> 1) & 7); since
+  // the group starts 8-aligned, (r >> 1) & 7 = 4 ((w + NW i) & 1) + (l/8) / 2
   ARow<uint16_t, AL> ar[LA];
   const uint16_t* bp[LB];
-  const int lr = l >> 3, lc = ((l & 7) ^ (lr & 7)) * 8;  // rows are 8-aligned: row & 7 == lr
+  const int lr = l >> 3;
+  auto lchunk = [&](int i) { return ((l & 7) ^ ((((w + NW * i) & 1) << 2) | (lr >> 1))) * 8; };
+  int lca[LA];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) ar[i].init(g, out_row(min(m0 + 8 * (w + NW * i) + lr, rows - 1)));
+  for (int i = 0; i < LA; ++i) {
+    ar[i].init(g, out_row(min(m0 + 8 * (w + NW * i) + lr, rows - 1)));
+    lca[i] = lchunk(i);
+  }
 #pragma unroll
-  for (int i = 0; i < LB; ++i) bp[i] = weight_row<uint16_t, BMAP>(g, min(n0 + 8 * (w + NW * i) + lr, g.N - 1)) + lc;
+  for (int i = 0; i < LB; ++i)
+    bp[i] = weight_row<uint16_t, BMAP>(g, min(n0 + 8 * (w + NW * i) + lr, g.N - 1)) + lchunk(i);
   auto issue = [&](unsigned char* st, int kt) {
     const int k0 = (kbase + kt) * 64;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
       if (LA_EVEN || w + NW * i < BM / 8)
         __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void*)ar[i].at(k0 + lc, g.d),
+            (__attribute__((address_space(1))) void*)ar[i].at(k0 + lca[i], g.d),
             (__attribute__((address_space(3))) void*)(st + (w + NW * i) * 1024), 16, 0, 0);
     // the LM head's weights stream once per launch: non-temporal (cache
     // policy nt), so they do not push A and the layer weights out of the caches
