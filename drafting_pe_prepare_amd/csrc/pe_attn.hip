@@ -100,24 +100,17 @@ __device__ __forceinline__ int attn_ranges(long long P, int grid) {
 // pieces are consecutive and at most B*Hkv + Gw partials exist.
 long long attn_max_items(int B, int Hkv, int grid) { return (long long)B * Hkv + grid; }
 
-// LDS tiles of one 32-position step for one KV head.  gfx950 serves a
-// 16-byte LDS read 16 lanes per clock over 64 banks (256 bytes), so the 16
-// rows one clock of a fragment read touches must fall in 16 distinct 16-byte
-// bank groups.
+// LDS tiles of one 32-position step for one KV head.
 //  K: 32 positions x 128 B; chunk c (16 B, 8 dims) of position p sits at
-//     p*128 + (c ^ kswz(p))*16.  A score fragment's 16 lanes read positions
-//     8(r/4) + 4t + r%4 (r = 0..15) at one chunk: p's parity picks the half
-//     of the window and kswz, a bijection on each parity class of those 16
-//     positions, the group inside it.
-//  V: 64 dims x 64 B (d-major: 32 positions x 2 B per dim row), two dim rows
-//     per 128-byte line q; chunk c of row 2q + h sits at line slot
-//     (4h | c) ^ ((q >> 1) & 3), so dim rows r = 0..15 of one clock (lines
-//     0..7) fill the 16 groups.
-__device__ __forceinline__ int kswz(int p) { return ((p >> 1) & 1) | (((p >> 3) & 3) << 1); }
-__device__ __forceinline__ int vkey(int q) { return (q >> 1) & 3; }
+//     p*128 + (c ^ kswz(p))*16.  kswz makes the 8 rows a score fragment read
+//     together (positions 8(r/4) + 4t + r%4, r = 0..7) land in 8 distinct
+//     16-byte bank groups.
+//  V: 64 dims x 64 B (d-major: 32 positions x 2 B per dim row), laid out with
+//     the same pair-of-rows swizzle as the GEMM tiles (vswz).
+__device__ __forceinline__ int kswz(int p) { return (p & 3) | (((p >> 3) & 1) << 2); }
 __device__ __forceinline__ int vswz(int row, int c) {
   const int q = row >> 1;
-  return q * 128 + ((((row & 1) << 2) | c) ^ vkey(q)) * 16;
+  return q * 128 + ((((row & 1) << 2) | c) ^ (q & 3)) * 16;
 }
 
 template <int N>
@@ -174,7 +167,7 @@ void attn_partial_kernel(AttnArgs a) {
   // chunk kch; V line of dims vd, chunk vch
   const int dh = w >> 2, ww = w & 3;
   const int kpos = 8 * ww + (l >> 3), kch = (l & 7) ^ kswz(kpos);
-  const int vline = 8 * ww + (l >> 3), vx = (l & 7) ^ vkey(vline);
+  const int vline = 8 * ww + (l >> 3), vx = (l & 7) ^ (vline & 3);
   const int vd = 2 * vline + (vx >> 2), vch = vx & 3;
   // each wave's partial-output transpose buffer reuses one stage object once
   // an item's positions are done (64 x 17 floats per wave)
