@@ -96,17 +96,24 @@ def check_against_oracle(w, prm, inp, g, n, requests=None):
         np.testing.assert_array_equal(g["bonus"][:n], bon)
 
 
-@pytest.mark.parametrize("case", ["bf16_large", "f32_small"])
+@pytest.mark.parametrize("case", ["bf16_large", "bf16_mid", "f32_small"])
 def test_one_capture_serves_every_occupancy(case):
     """Captured once at B = max_num_seqs, replayed at occupancies B, 1, 7, 0
     and B again.  bf16_large: 32 requests x 14 slots (448 forward rows: the
     large-batch GEMMs with MASK-deduplicated first layer, 224 draft rows);
     request 15 carries an invalid accepted count, reported only while it is
-    active.  f32_small: 3 requests of the 64-token fp32 drafter."""
+    active.  bf16_mid: 12 requests x 14 slots, two layers (168 forward rows,
+    84 draft rows: the 65..256-row products on row maps with the split
+    planned on the device, MASK deduplication, the draft-rows-only last
+    layer).  f32_small: 3 requests of the 64-token fp32 drafter."""
     if case == "bf16_large":
         w = SMALL_BF16.with_(K=7, batch=32, accepted="uniform", prefix=("uniform", 40, 400))
         plan = [32, 1, 7, 0, 32]
         bad = 15
+    elif case == "bf16_mid":
+        w = SMALL_BF16.with_(K=7, batch=12, layers=2, accepted="uniform", prefix=("uniform", 40, 400))
+        plan = [12, 1, 5, 0, 12]
+        bad = 4
     else:
         w = configs.TINY.with_(K=4, batch=3, accepted="uniform", prefix=("uniform", 40, 200))
         plan = [3, 1, 0, 2]
