@@ -1285,7 +1285,10 @@ hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_
 #ifndef PE_LM_RING
 #define PE_LM_RING 1
 #endif
-enum Variant { V_WIDE, V_RING, V_SKINNY, V_A64, V_A128, V_A224, V_A256, V_D64, V_D128S2 };
+enum Variant { V_WIDE, V_RING, V_SKINNY, V_A64, V_A128, V_A192, V_A224, V_A256, V_D64, V_D128S2 };
+#ifndef PE_LM_A192
+#define PE_LM_A192 1
+#endif
 static Variant pick(int epi, int M, int N, int K, int num_cus) {
   if (epi == E_ARGMAX) {
     const size_t wide_lds = size_t(M) * (K / 8 + 1) * 16;
@@ -1293,6 +1296,7 @@ static Variant pick(int epi, int M, int N, int K, int num_cus) {
     if (PE_LM_RING && M <= 128 && K % 32 == 0) return V_RING;
     if (M <= 64) return V_A64;
     if (M > 384 && M <= 448) return V_A224;  // two 224-row tiles instead of 256 + 192 valid rows
+    if (PE_LM_A192 && M > 128 && M <= 192) return V_A192;  // one 192-row tile, not 256 with 64+ idle rows
     return M <= 128 ? V_A128 : V_A256;
   }
   if (M <= 16) return V_SKINNY;
@@ -1681,6 +1685,7 @@ static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
       // workgroups per CU: two 64-row tiles (80 KB of LDS each), one otherwise
       case V_A64: return run_tiled<EPI, AL, BMAP, 64, kArgmaxBN, 1, 4, 2>(g, st, 2 * num_cus);
       case V_A128: return run_tiled<EPI, AL, BMAP, 128, kArgmaxBN, 2, 4, 2>(g, st, num_cus);
+      case V_A192: return run_tiled<EPI, AL, BMAP, 192, kArgmaxBN, 2, 4, 2>(g, st, num_cus);
       case V_A224: return run_tiled<EPI, AL, BMAP, 224, kArgmaxBN, 2, 4, 2>(g, st, num_cus);
       default: return run_tiled<EPI, AL, BMAP, 256, kArgmaxBN, 4, 2, 2>(g, st, num_cus);
     }

@@ -177,10 +177,11 @@ def test_small_bf16_lm_head_224_row_tiles(B, seed):
 
 
 @pytest.mark.parametrize("K,B,vocab,seed", [(7, 64, 33200, 93), (5, 16, 65904, 94), (3, 16, 131504, 95),
-                                             (7, 32, 65904, 96)])
+                                             (7, 32, 65904, 96), (11, 16, 65904, 98), (9, 15, 33200, 100)])
 def test_small_bf16_lm_head_split_tail(K, B, vocab, seed):
     """LM heads whose last round of vocabulary tiles would hold only a few
-    tiles (448, 80, 48 and 224 draft rows: 224-, 128-, 64- and 256-row tiles):
+    tiles (448, 80, 48, 224, 176 and 135 draft rows: 224-, 128-, 64-, 256- and
+    192-row tiles, the last two ragged):
     the last column tiles run as k-range pieces whose fp32 partial tiles are
     summed in split order before the row argmax (ragged last tile)."""
     w = SMALL_BF16.with_(K=K, batch=B, d=1024, vocab=vocab, mlp=1024, weight_std=1 / 32,
