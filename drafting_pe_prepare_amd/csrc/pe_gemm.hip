@@ -1289,6 +1289,7 @@ enum Variant { V_WIDE, V_RING, V_SKINNY, V_A64, V_A128, V_A192, V_A224, V_A256, 
 #ifndef PE_LM_A192
 #define PE_LM_A192 1
 #endif
+
 static Variant pick(int epi, int M, int N, int K, int num_cus) {
   if (epi == E_ARGMAX) {
     const size_t wide_lds = size_t(M) * (K / 8 + 1) * 16;
@@ -1678,6 +1679,10 @@ static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
       // workgroup of eight waves and six stages (two of four waves and three
       // stages measured 446 us against 158)
       if (g.M <= 64) return run_ring<64, 1, 4, 3, 2>(g, num_cus, st);
+      // 65..96 rows on 96-row stages (K sweep K = 5, 80 rows: 165 -> 153 us
+      // against the 128-row ring; two workgroups of four waves and three
+      // stages measured 236 us)
+      if (g.M <= 96) return run_ring<96, 2, 4, 6, 1>(g, num_cus, st);
       return run_ring<128, 2, 4, 6, 1>(g, num_cus, st);
     }
     switch (v) {
