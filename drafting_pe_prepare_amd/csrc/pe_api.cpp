@@ -588,6 +588,14 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   auto ssq_out = [&](pe::GemmArgs& g) {
     if (fold) { g.ssq_out = ctx->ssq; g.ssq_n = d / 16; }
   };
+  // Above 64 rows the O and down products run on the large-batch kernels,
+  // whose split-K sum writes each output row whole: it also writes the
+  // following RMSNorm (the MLP norm after O, the next layer's attention norm
+  // after down), so those norms need no launch of their own either
+  const bool post_norm = dt == PE_BF16 && R > pe::kRowMapMinRows && !fold && d <= 4096;
+  auto norm_after = [&](pe::GemmArgs& g, const void* gain) {
+    g.nrm_out = ctx->u; g.nrm_gain = gain; g.norm_eps = k.rms_eps;
+  };
   auto norm_in = [&](pe::GemmArgs& g, const void* gain) {
     g.A = ctx->x;
     g.ssq_in = ctx->ssq; g.ssq_n = d / 16;
@@ -638,7 +646,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     const bool first_dd = l == 0 && dd;
     const bool last_draft = draft_only && l == k.layers - 1;
     const bool fold_attn = fold && (l > 0 || !P.embed_input);  // the embedding gather writes no sums
-    if (!fold_attn) {
+    if (!fold_attn && !(post_norm && l > 0)) {  // (after layer 0, the down product wrote it)
       Timed tm(ctx, PE_PH_NORM);
       if (first_dd)
         PE_HIP(pe::launch_rmsnorm_expand(Rc, d, ctx->xc, L.attn_norm, ctx->u, ctx->x, Kc, k.rms_eps, st),
@@ -711,10 +719,11 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       if (last_draft) { g.M = R; g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
       ssq_out(g);
+      if (post_norm) norm_after(g, L.mlp_norm);
       Timed tm(ctx, PE_PH_O);
       if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "o proj")) != PE_OK) return ds;
     }
-    if (!fold) {
+    if (!fold && !post_norm) {
       Timed tm(ctx, PE_PH_NORM);
       if (last_draft)  // the draft rows, in place
         PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, L.mlp_norm, ctx->u, P.draft_rows, R, k.rms_eps, st, true),
@@ -741,6 +750,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.out = ctx->x; g.resid = ctx->x; g.ldo = d;
       if (last_draft) { g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
       ssq_out(g);  // the next layer's attention norm
+      if (post_norm && l + 1 < k.layers) norm_after(g, ctx->layers[l + 1].attn_norm);
       Timed tm(ctx, PE_PH_DOWN);
       if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "down")) != PE_OK) return ds;
     }

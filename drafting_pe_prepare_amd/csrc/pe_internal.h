@@ -172,6 +172,13 @@ struct GemmArgs {
   const void* norm_gain;
   float norm_eps;
   int ssq_n;
+  // RMSNorm fused after a large-batch residual product (E_RESID on
+  // launch_mm): with nrm_out set, the product's split-K sum also normalises
+  // every output row it writes, nrm_out[row] = bf16((x * rs) * nrm_gain) with
+  // rs = rsqrt(mean(x^2) + norm_eps) over the stored (rounded) x, as
+  // rmsnorm_kernel would have.
+  void* nrm_out;
+  const void* nrm_gain;
 };
 // Whether a product of M rows can take its RMSNorm folded in (see GemmArgs):
 // bf16, at most 16 rows, K % 32 == 0, K / 16 <= kSsqMaxParts partial sums.

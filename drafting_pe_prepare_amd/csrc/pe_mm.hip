@@ -463,6 +463,101 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
   }
 }
 
+// Split-K sum + residual with the following RMSNorm (GemmArgs::nrm_out): one
+// 256-thread workgroup per output row, thread t over 8-column chunks t and
+// t + 256.  The rounded row x (the split sum plus the residual, or with no
+// split the row the product stored) stays in registers, its squares are
+// summed over the workgroup in a fixed order, and the normalised row goes out
+// beside it.
+template <int MAXC>
+__global__ __launch_bounds__(256) void mm_resid_norm_kernel(GemmArgs g, int rows, int rpr, int BM, int ntiles,
+                                                            int slots, int cap_splits) {
+  __shared__ float s_ss[4];
+  const MmPlan plan = mm_plan(mm_rows(g), BM, ntiles, g.K / 64, slots, cap_splits);
+  rows = active_rows(g.nact, rpr, rows);
+  if (g.rmap) rows = min(rows, *g.rcount);
+  const int KS = plan.ks;
+  const long long MN = (long long)g.M * g.N;
+  const int tid = threadIdx.x, nch = g.N / 8;
+  for (int m = blockIdx.x; m < rows; m += gridDim.x) {
+    const long long row = g.rmap ? g.rmap[m] : m;
+    uint16_t* xr = (uint16_t*)g.out + row * g.ldo;
+    float x[MAXC][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int c = tid + 256 * j;
+      if (c < nch) {
+        uint4 xv;
+        if (KS > 1) {
+          const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + row * g.ldo + 8 * c);
+          float v[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) v[t] = 0.f;
+          // the split's partials in a fixed order, four loads in flight
+          for (int k0 = 0; k0 < KS; k0 += 2) {
+            float4 a[2][2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              const int k = min(k0 + kk, KS - 1);
+              const float* p = g.part + k * MN + (long long)m * g.N + 8 * c;
+              a[kk][0] = *reinterpret_cast<const float4*>(p);
+              a[kk][1] = *reinterpret_cast<const float4*>(p + 4);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              if (k0 + kk < KS) {
+                v[0] += a[kk][0].x; v[1] += a[kk][0].y; v[2] += a[kk][0].z; v[3] += a[kk][0].w;
+                v[4] += a[kk][1].x; v[5] += a[kk][1].y; v[6] += a[kk][1].z; v[7] += a[kk][1].w;
+              }
+            }
+          }
+          const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v[2 * t] += __uint_as_float(rw[t] << 16);
+            v[2 * t + 1] += __uint_as_float(rw[t] & 0xFFFF0000u);
+          }
+          xv = uint4{f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
+          *reinterpret_cast<uint4*>(xr + 8 * c) = xv;
+        } else {
+          xv = *reinterpret_cast<const uint4*>(xr + 8 * c);  // stored by the product's own epilogue
+        }
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          x[j][2 * t] = __uint_as_float(xw[t] << 16);
+          x[j][2 * t + 1] = __uint_as_float(xw[t] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ss += x[j][t] * x[j][t];
+      }
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = ((s_ss[0] + s_ss[1]) + s_ss[2]) + s_ss[3];
+    __syncthreads();  // s_ss is written again for the next row
+    const float rs = rsqrtf(tot / float(g.N) + g.norm_eps);
+    uint16_t* ur = (uint16_t*)g.nrm_out + row * g.ldo;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int c = tid + 256 * j;
+      if (c < nch) {
+        const uint4 gv = *reinterpret_cast<const uint4*>((const uint16_t*)g.nrm_gain + 8 * c);
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          o[t] = f2bf2(x[j][2 * t] * rs * __uint_as_float(gw[t] << 16),
+                       x[j][2 * t + 1] * rs * __uint_as_float(gw[t] & 0xFFFF0000u));
+        *reinterpret_cast<uint4*>(ur + 8 * c) = uint4{o[0], o[1], o[2], o[3]};
+      }
+    }
+  }
+}
+constexpr int kNormMaxChunks = 2;  // rows of up to 2 x 256 x 8 = 4096 columns
+
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
@@ -506,7 +601,17 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
   hipLaunchKernelGGL((mm_kernel<EPI, AL, BMAP, BM, BN, WM, WN, kDKT, T::S, T::OCC>), dim3(unsigned(grid)),
                      dim3(64 * WM * WN), 0, st, g, ntiles, slots, cap_splits);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || (EPI != E_QKV && !can_split)) return e;
+  if (e != hipSuccess) return e;
+  if constexpr (EPI == E_RESID) {
+    if (g.nrm_out) {  // the split sum (or, unsplit, the stored rows) and the following RMSNorm
+      if (g.N % 8 || g.N > 2048 * kNormMaxChunks || g.ldo != g.N) return hipErrorInvalidValue;
+      const long long blocks = std::min<long long>(g.M, 16LL * num_cus);
+      hipLaunchKernelGGL(mm_resid_norm_kernel<kNormMaxChunks>, dim3(unsigned(blocks)), dim3(256), 0, st, g, g.M,
+                         g.rpr, BM, ntiles, slots, cap_splits);
+      return hipGetLastError();
+    }
+  }
+  if (EPI != E_QKV && !can_split) return e;
   // rows the epilogue covers: every slot of a MASK-deduplicated QKV product
   const bool expand = EPI == E_QKV && g.dedup_k;
   const int rows = expand ? g.M / (g.dedup_k + 2) * (2 * g.dedup_k) : g.M;
