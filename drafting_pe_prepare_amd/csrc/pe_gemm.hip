@@ -1286,9 +1286,6 @@ hipError_t launch_pack_frag16(int bmap, const GemmArgs& g, void* out, hipStream_
 #define PE_LM_RING 1
 #endif
 enum Variant { V_WIDE, V_RING, V_SKINNY, V_A64, V_A128, V_A192, V_A224, V_A256, V_D64, V_D128S2 };
-#ifndef PE_LM_A192
-#define PE_LM_A192 1
-#endif
 
 static Variant pick(int epi, int M, int N, int K, int num_cus) {
   if (epi == E_ARGMAX) {
@@ -1297,7 +1294,7 @@ static Variant pick(int epi, int M, int N, int K, int num_cus) {
     if (PE_LM_RING && M <= 128 && K % 32 == 0) return V_RING;
     if (M <= 64) return V_A64;
     if (M > 384 && M <= 448) return V_A224;  // two 224-row tiles instead of 256 + 192 valid rows
-    if (PE_LM_A192 && M > 128 && M <= 192) return V_A192;  // one 192-row tile, not 256 with 64+ idle rows
+    if (M > 128 && M <= 192) return V_A192;  // one 192-row tile, not 256 with 64+ idle rows
     return M <= 128 ? V_A128 : V_A256;
   }
   if (M <= 16) return V_SKINNY;
