@@ -79,6 +79,27 @@ __device__ __forceinline__ int argmax_key_index(uint64_t k) {
   return int(0xFFFFFFFFu - uint32_t(k & 0xFFFFFFFFull));
 }
 
+// Maximum of v over the 16 lanes of its row (lanes 16q .. 16q+15), in every
+// lane of the row: four DPP row permutes (swap pairs, swap pairs of pairs,
+// mirror each half-row, mirror the row), each combined with a max.  DPP moves
+// are VALU operands: no LDS round trip and no wait.  Every lane of the row
+// must be active.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+  return v;
+}
+// Largest argmax key over the 16 lanes of a row: the largest value word, then
+// the largest index word among the lanes that hold that value (the 64-bit
+// maximum, as two 32-bit row maxima).
+__device__ __forceinline__ uint64_t row16_max_key(uint64_t k) {
+  const uint32_t hi = row16_max_u32(uint32_t(k >> 32));
+  const uint32_t lo = row16_max_u32(uint32_t(k >> 32) == hi ? uint32_t(k) : 0u);
+  return (uint64_t(hi) << 32) | lo;
+}
+
 // Philox4x32-10 ("Parallel random numbers: as easy as 1, 2, 3", Salmon,
 // Moraes, Dror, Shaw, SC 2011): the four output words for counter
 // (c0, c1, 0, stream) under the 64-bit key `seed`.  Ten rounds of two 32x32

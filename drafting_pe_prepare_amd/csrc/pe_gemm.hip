@@ -620,10 +620,7 @@ __global__ __launch_bounds__(512) void lmhead_wide_kernel(GemmArgs g) {
   // row maxima: 16 lanes per row group, then across waves, one atomic per row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    for (int o = 1; o < 16; o <<= 1) {
-      const uint64_t k = shfl_xor_u64(best[i], o);
-      best[i] = k > best[i] ? k : best[i];
-    }
+    best[i] = row16_max_key(best[i]);
     if (col == 0) s_best[w][kg * 4 + i] = best[i];
   }
   __syncthreads();
@@ -914,10 +911,7 @@ void gemm_tiled_kernel(GemmArgs g, int mtiles, int ntiles, int tail0, int dslots
             best = k > best ? k : best;
           }
         }
-        for (int o = 1; o < 16; o <<= 1) {
-          const uint64_t k = shfl_xor_u64(best, o);
-          best = k > best ? k : best;
-        }
+        best = row16_max_key(best);
         if (col == 0) s_best[wn * BM + lrow] = best;
       }
     __syncthreads();
@@ -1147,10 +1141,7 @@ void lmhead_ring_kernel(GemmArgs g) {
             best = k > best ? k : best;
           }
         }
-        for (int o = 1; o < 16; o <<= 1) {
-          const uint64_t k = shfl_xor_u64(best, o);
-          best = k > best ? k : best;
-        }
+        best = row16_max_key(best);
         if (col == 0) s_best[wn * BM + lrow] = best;
       }
 #pragma unroll
