@@ -162,4 +162,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sums of split-K partials: acc[v] = sum over k = 0 .. KS-1 of the float4 at
+// p + k * stride + off[v], added in split order (k ascending, from zero), so
+// the sums do not depend on how the loads are batched.  The loads of up to
+// eight splits (all NV vectors of each) are issued before the first add: one
+// memory round trip per eight splits, where a load-add loop waits once per
+// split.
+template <int NV>
+__device__ __forceinline__ void sum_splits(const float* p, long long stride, int KS, const long long (&off)[NV],
+                                           float4 (&acc)[NV]) {
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < KS; k0 += 8) {
+    float4 a[8][NV];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      if (k0 + kk < KS)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) a[kk][v] = *reinterpret_cast<const float4*>(p + (k0 + kk) * stride + off[v]);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      if (k0 + kk < KS)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          acc[v].x += a[kk][v].x;
+          acc[v].y += a[kk][v].y;
+          acc[v].z += a[kk][v].z;
+          acc[v].w += a[kk][v].w;
+        }
+  }
+}
+
 }  // namespace pe

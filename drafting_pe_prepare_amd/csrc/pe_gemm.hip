@@ -1412,11 +1412,10 @@ __global__ __launch_bounds__(256) void argmax_tail_kernel(GemmArgs g, int mtiles
   const int mt = tt % mtiles, nt = tail0 + tt / mtiles, m = mt * BM + lrow;
   if (m >= g.M) return;
   const float* P = g.part + (long long)tt * g.ksplit * (BM * BN) + lrow * BN + 4 * l;
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < g.ksplit; ++s) {
-    const float4 p = *reinterpret_cast<const float4*>(P + (long long)s * (BM * BN));
-    v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
-  }
+  const long long off[1] = {0};
+  float4 sm[1];
+  sum_splits<1>(P, BM * BN, g.ksplit, off, sm);  // the pieces in split order
+  const float v[4] = {sm[0].x, sm[0].y, sm[0].z, sm[0].w};
   const int n0 = nt * BN + 4 * l;
   uint64_t best = 0ull;
 #pragma unroll
@@ -1478,22 +1477,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int BM, 
   const long long MN = (long long)g.M * g.N;
   const long long stride = (long long)gridDim.x * blockDim.x;
   auto out_row = [&](int m) { return g.rmap ? g.rmap[m] : m; };
-  auto sum8 = [&](int m, int n, float (&v)[8]) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = 0.f;
-    for (int k = 0; k < KS; ++k) {
-      const float* p = g.part + k * MN + (long long)m * g.N + n;
-      const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
-      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-      v[4] += c.x; v[5] += c.y; v[6] += c.z; v[7] += c.w;
-    }
+  // 8 consecutive sums from two float4 sums
+  auto to8 = [](const float4& a, const float4& b, float (&v)[8]) {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   };
   if constexpr (EPI == E_STORE || EPI == E_RESID) {
     const int per_row = g.N / 8;
     for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
       const int m = int(e / per_row), n = int(e % per_row) * 8;
+      const long long b = (long long)m * g.N + n, off[2] = {b, b + 4};
+      float4 sm[2];
+      sum_splits<2>(g.part, MN, KS, off, sm);
       float v[8];
-      sum8(m, n, v);
+      to8(sm[0], sm[1], v);
       const long long o = (long long)out_row(m) * g.ldo + n;
       if constexpr (EPI == E_RESID) {
         const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + o);
@@ -1513,9 +1510,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int BM, 
     const int per_row = g.N / 16;
     for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
       const int m = int(e / per_row), pc = int(e % per_row), q = pc >> 1, c0 = (pc & 1) * 8;
+      const long long b = (long long)m * g.N + 32 * q + c0, off[4] = {b, b + 4, b + 16, b + 20};
+      float4 sm[4];
+      sum_splits<4>(g.part, MN, KS, off, sm);
       float gt[8], up[8], v[8];
-      sum8(m, 32 * q + c0, gt);
-      sum8(m, 32 * q + 16 + c0, up);
+      to8(sm[0], sm[1], gt);
+      to8(sm[2], sm[3], up);
 #pragma unroll
       for (int t = 0; t < 8; ++t) v[t] = gt[t] / (1.0f + expf(-gt[t])) * up[t];
       uint4 o;
@@ -1532,18 +1532,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int BM, 
       const int mr = int(e / per_row), pr = int(e % per_row), nb = (pr >> 1) * 32, c0 = (pr & 1) * 8;
       const int cm = g.dedup_k ? dedup_row(mr, g.dedup_k) : mr;  // row of the sums (one split then)
       const int m = out_row(mr);  // row of the positions, slots and q rows
+      const long long b = (long long)cm * g.N + nb + c0, off[4] = {b, b + 4, b + 16, b + 20};
+      float4 sm[4];
+      sum_splits<4>(g.part, MN, KS, off, sm);
       float lo[8], hi[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) lo[t] = hi[t] = 0.f;
-      for (int k = 0; k < KS; ++k) {
-        const float* p = g.part + k * MN + (long long)cm * g.N + nb + c0;
-        const float4 a0 = *reinterpret_cast<const float4*>(p), a1 = *reinterpret_cast<const float4*>(p + 4);
-        const float4 b0 = *reinterpret_cast<const float4*>(p + 16), b1 = *reinterpret_cast<const float4*>(p + 20);
-        lo[0] += a0.x; lo[1] += a0.y; lo[2] += a0.z; lo[3] += a0.w;
-        lo[4] += a1.x; lo[5] += a1.y; lo[6] += a1.z; lo[7] += a1.w;
-        hi[0] += b0.x; hi[1] += b0.y; hi[2] += b0.z; hi[3] += b0.w;
-        hi[4] += b1.x; hi[5] += b1.y; hi[6] += b1.z; hi[7] += b1.w;
-      }
+      to8(sm[0], sm[1], lo);
+      to8(sm[2], sm[3], hi);
       constexpr int hd = 64;  // bf16 storage implies head_dim 64 (checked at context creation)
       if (nb < g.nq + g.nk) {
         const bool isq = nb < g.nq;

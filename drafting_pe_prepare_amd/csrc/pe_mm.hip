@@ -363,15 +363,10 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
   const int KS = plan.ks;
   const long long MN = (long long)g.M * g.N;
   const long long stride = (long long)gridDim.x * blockDim.x;
-  auto sum8 = [&](int m, int n, float (&v)[8]) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = 0.f;
-    for (int k = 0; k < KS; ++k) {
-      const float* p = g.part + k * MN + (long long)m * g.N + n;
-      const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
-      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-      v[4] += c.x; v[5] += c.y; v[6] += c.z; v[7] += c.w;
-    }
+  // 8 consecutive sums from two float4 sums
+  auto to8 = [](const float4& a, const float4& b, float (&v)[8]) {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   };
   auto pack8 = [](const float (&v)[8]) {
     return uint4{f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
@@ -380,8 +375,11 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
     const int per_row = g.N / 8;
     for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
       const int m = int(e / per_row), n = int(e % per_row) * 8;
+      const long long b = (long long)m * g.N + n, off[2] = {b, b + 4};
+      float4 sm[2];
+      sum_splits<2>(g.part, MN, KS, off, sm);
       float v[8];
-      sum8(m, n, v);
+      to8(sm[0], sm[1], v);
       const long long o = (long long)(g.rmap ? g.rmap[m] : m) * g.ldo + n;
       if constexpr (EPI == E_RESID) {
         const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + o);
@@ -398,9 +396,12 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
     const int per_row = g.N / 16;  // 8 outputs per thread, 32 per 64-column block
     for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < (long long)rows * per_row; e += stride) {
       const int m = int(e / per_row), pc = int(e % per_row), t = pc >> 2, c0 = (pc & 3) * 8;
+      const long long b = (long long)m * g.N + 64 * t + c0, off[4] = {b, b + 4, b + 32, b + 36};
+      float4 sm[4];
+      sum_splits<4>(g.part, MN, KS, off, sm);
       float gt[8], up[8], v[8];
-      sum8(m, 64 * t + c0, gt);
-      sum8(m, 64 * t + 32 + c0, up);
+      to8(sm[0], sm[1], gt);
+      to8(sm[2], sm[3], up);
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = gt[u] / (1.0f + expf(-gt[u])) * up[u];
       *reinterpret_cast<uint4*>((uint16_t*)g.out + (long long)(g.rmap ? g.rmap[m] : m) * g.ldo + 32 * t + c0) =
@@ -415,9 +416,12 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
       // sums of compact row cm, written to slot m
       const int cm = g.dedup_k ? dedup_row(mr, g.dedup_k) : mr;
       const int m = g.rmap ? g.rmap[mr] : mr;
+      const long long b = (long long)cm * g.N + nb + c0, off[4] = {b, b + 4, b + 32, b + 36};
+      float4 sm[4];
+      sum_splits<4>(g.part, MN, KS, off, sm);
       float lo[8], hi[8];
-      sum8(cm, nb + c0, lo);
-      sum8(cm, nb + 32 + c0, hi);
+      to8(sm[0], sm[1], lo);
+      to8(sm[2], sm[3], hi);
       if (nb < g.nq + g.nk) {
         const bool isq = nb < g.nq;
         const int head = (isq ? nb : nb - g.nq) / hd;
@@ -482,55 +486,61 @@ __global__ __launch_bounds__(256) void mm_resid_norm_kernel(GemmArgs g, int rows
   for (int m = blockIdx.x; m < rows; m += gridDim.x) {
     const long long row = g.rmap ? g.rmap[m] : m;
     uint16_t* xr = (uint16_t*)g.out + row * g.ldo;
-    float x[MAXC][8];
-    float ss = 0.f;
+    // this thread's chunks tid + 256 j (a chunk past the row re-reads the
+    // last one, so every load has a valid address; its results are unused);
+    // the gains, the residual and every split's partials are all in flight
+    // before the first add
+    int cc[MAXC];
+    uint4 gv[MAXC];
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
-      const int c = tid + 256 * j;
-      if (c < nch) {
-        uint4 xv;
-        if (KS > 1) {
-          const uint4 rv = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + row * g.ldo + 8 * c);
-          float v[8];
+      cc[j] = min(tid + 256 * j, nch - 1);
+      gv[j] = *reinterpret_cast<const uint4*>((const uint16_t*)g.nrm_gain + 8 * cc[j]);
+    }
+    float x[MAXC][8];
+    float ss = 0.f;
+    auto unpack = [](const uint4& u, float (&f)[8]) {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-          for (int t = 0; t < 8; ++t) v[t] = 0.f;
-          // the split's partials in a fixed order, four loads in flight
-          for (int k0 = 0; k0 < KS; k0 += 2) {
-            float4 a[2][2];
+      for (int t = 0; t < 4; ++t) {
+        f[2 * t] = __uint_as_float(w[t] << 16);
+        f[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+      }
+    };
+    if (KS > 1) {
+      uint4 rv[MAXC];
+      long long off[2 * MAXC];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              const int k = min(k0 + kk, KS - 1);
-              const float* p = g.part + k * MN + (long long)m * g.N + 8 * c;
-              a[kk][0] = *reinterpret_cast<const float4*>(p);
-              a[kk][1] = *reinterpret_cast<const float4*>(p + 4);
-            }
+      for (int j = 0; j < MAXC; ++j) {
+        rv[j] = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + row * g.ldo + 8 * cc[j]);
+        off[2 * j] = (long long)m * g.N + 8 * cc[j];
+        off[2 * j + 1] = off[2 * j] + 4;
+      }
+      float4 sm[2 * MAXC];
+      sum_splits<2 * MAXC>(g.part, MN, KS, off, sm);  // the split's partials in a fixed order
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              if (k0 + kk < KS) {
-                v[0] += a[kk][0].x; v[1] += a[kk][0].y; v[2] += a[kk][0].z; v[3] += a[kk][0].w;
-                v[4] += a[kk][1].x; v[5] += a[kk][1].y; v[6] += a[kk][1].z; v[7] += a[kk][1].w;
-              }
-            }
-          }
-          const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+      for (int j = 0; j < MAXC; ++j) {
+        if (tid + 256 * j < nch) {
+          float r[8];
+          unpack(rv[j], r);
+          const float v[8] = {sm[2 * j].x + r[0],     sm[2 * j].y + r[1],     sm[2 * j].z + r[2],
+                              sm[2 * j].w + r[3],     sm[2 * j + 1].x + r[4], sm[2 * j + 1].y + r[5],
+                              sm[2 * j + 1].z + r[6], sm[2 * j + 1].w + r[7]};
+          const uint4 xv = uint4{f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
+          *reinterpret_cast<uint4*>(xr + 8 * cc[j]) = xv;
+          unpack(xv, x[j]);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            v[2 * t] += __uint_as_float(rw[t] << 16);
-            v[2 * t + 1] += __uint_as_float(rw[t] & 0xFFFF0000u);
-          }
-          xv = uint4{f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
-          *reinterpret_cast<uint4*>(xr + 8 * c) = xv;
-        } else {
-          xv = *reinterpret_cast<const uint4*>(xr + 8 * c);  // stored by the product's own epilogue
+          for (int t = 0; t < 8; ++t) ss += x[j][t] * x[j][t];
         }
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      }
+    } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          x[j][2 * t] = __uint_as_float(xw[t] << 16);
-          x[j][2 * t + 1] = __uint_as_float(xw[t] & 0xFFFF0000u);
+      for (int j = 0; j < MAXC; ++j) {
+        if (tid + 256 * j < nch) {
+          unpack(*reinterpret_cast<const uint4*>(xr + 8 * cc[j]), x[j]);  // stored by the product's own epilogue
+#pragma unroll
+          for (int t = 0; t < 8; ++t) ss += x[j][t] * x[j][t];
         }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) ss += x[j][t] * x[j][t];
       }
     }
     ss = wave_sum(ss);
@@ -542,16 +552,14 @@ __global__ __launch_bounds__(256) void mm_resid_norm_kernel(GemmArgs g, int rows
     uint16_t* ur = (uint16_t*)g.nrm_out + row * g.ldo;
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
-      const int c = tid + 256 * j;
-      if (c < nch) {
-        const uint4 gv = *reinterpret_cast<const uint4*>((const uint16_t*)g.nrm_gain + 8 * c);
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      if (tid + 256 * j < nch) {
+        const uint32_t gw[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
         uint32_t o[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           o[t] = f2bf2(x[j][2 * t] * rs * __uint_as_float(gw[t] << 16),
                        x[j][2 * t + 1] * rs * __uint_as_float(gw[t] & 0xFFFF0000u));
-        *reinterpret_cast<uint4*>(ur + 8 * c) = uint4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<uint4*>(ur + 8 * cc[j]) = uint4{o[0], o[1], o[2], o[3]};
       }
     }
   }
