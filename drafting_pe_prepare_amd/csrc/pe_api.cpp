@@ -78,7 +78,7 @@ struct pe_ctx {
   void* xc = nullptr;  // [B(K+2), d] first-layer fc output on the MASK-deduplicated rows (bf16)
   float* splitk = nullptr;      // split-K GEMM partials (bf16 storage)
   int32_t* rmap = nullptr;      // [R] non-rejected slots of a large-batch pass, then their count
-  int32_t* dmap = nullptr;      // [D] non-rejected draft rows of a large-batch pass, then their count
+  int32_t* dmap = nullptr;      // [2D+1] non-rejected draft rows of a large-batch pass, their count, their draft indices
   uint8_t* qskip = nullptr;     // [R] last-layer attention: 0 for the non-rejected draft rows
   float* ssq = nullptr;         // [16][d/16] per-tile sums of squares of x (RMSNorm folded into small-batch products)
   long long splitk_cap = 0;     // floats
@@ -318,7 +318,7 @@ pe_status pe_create(const pe_config* cfg, const pe_weights* w, void* stream, pe_
       {reinterpret_cast<void**>(&c->err), 16, "err"},
       {reinterpret_cast<void**>(&c->rope_turns), size_t(k.head_dim / 2) * 8, "rope"},
       {reinterpret_cast<void**>(&c->rmap), (R + 1) * 4, "row map"},
-      {reinterpret_cast<void**>(&c->dmap), (D + 1) * 4, "draft row map"},
+      {reinterpret_cast<void**>(&c->dmap), (2 * D + 1) * 4, "draft row map"},
       {reinterpret_cast<void**>(&c->qskip), R, "last-layer query mask"},
       {reinterpret_cast<void**>(&c->ar_ids), R1 * 4, "ar ids"},
       {reinterpret_cast<void**>(&c->ar_pos), R1 * 4, "ar positions"},
@@ -575,9 +575,22 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   // queries and the O product, MLP norm and MLP run on their rows alone
   // (through a row map of the non-rejected draft rows).
   const bool draft_only = dt == PE_BF16 && R > pe::kRowMapMinRows && D > pe::kRowMapMinRows && P.draft_rows;
+  // Above 64 rows the O and down products run on the large-batch kernels,
+  // whose split-K sum writes each output row whole: it also writes the
+  // following RMSNorm (the MLP norm after O, the next layer's attention norm
+  // after down, and after the last layer's down on the draft rows the final
+  // norm, into z at each row's draft index), so those norms need no launch of
+  // their own.  The draft rows it does not compute (rejected: padded
+  // requests) get zero rows in z.
+  // (above 64 rows no norm is folded into the small-batch products)
+  const bool post_norm = dt == PE_BF16 && R > pe::kRowMapMinRows && d <= 4096;
+  const bool final_fused = post_norm && draft_only;
+  int32_t* const dpos = ctx->dmap + D + 1;
   if (draft_only) {
     Timed tm(ctx, PE_PH_FC);
-    PE_HIP(pe::launch_draft_map(R, D, P.draft_rows, P.rej, ctx->dmap, ctx->dmap + D, ctx->qskip, st), "draft map");
+    PE_HIP(pe::launch_draft_map(R, D, P.draft_rows, P.rej, ctx->dmap, ctx->dmap + D, dpos, ctx->qskip,
+                                final_fused ? ctx->z : nullptr, d, st),
+           "draft map");
   }
 
   // RMSNorm folded into the small-batch products (at most 16 rows: every dense
@@ -588,11 +601,6 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   auto ssq_out = [&](pe::GemmArgs& g) {
     if (fold) { g.ssq_out = ctx->ssq; g.ssq_n = d / 16; }
   };
-  // Above 64 rows the O and down products run on the large-batch kernels,
-  // whose split-K sum writes each output row whole: it also writes the
-  // following RMSNorm (the MLP norm after O, the next layer's attention norm
-  // after down), so those norms need no launch of their own either
-  const bool post_norm = dt == PE_BF16 && R > pe::kRowMapMinRows && !fold && d <= 4096;
   auto norm_after = [&](pe::GemmArgs& g, const void* gain) {
     g.nrm_out = ctx->u; g.nrm_gain = gain; g.norm_eps = k.rms_eps;
   };
@@ -751,11 +759,16 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       if (last_draft) { g.rmap = ctx->dmap; g.rcount = ctx->dmap + D; g.plan_rows = D; }
       ssq_out(g);  // the next layer's attention norm
       if (post_norm && l + 1 < k.layers) norm_after(g, ctx->layers[l + 1].attn_norm);
+      if (final_fused && last_draft) {  // the final norm, at the draft indices
+        norm_after(g, ctx->w.final_norm);
+        g.nrm_out = ctx->z;
+        g.nrm_rows = dpos;
+      }
       Timed tm(ctx, PE_PH_DOWN);
       if ((ds = dense(pe::A_PLAIN, pe::B_PLAIN, pe::E_RESID, g, "down")) != PE_OK) return ds;
     }
   }
-  {
+  if (!final_fused) {
     Timed tm(ctx, PE_PH_NORM);
     PE_HIP(pe::launch_rmsnorm(dt, D, d, ctx->x, ctx->w.final_norm, ctx->z, P.draft_rows, R,
                               k.rms_eps, st),

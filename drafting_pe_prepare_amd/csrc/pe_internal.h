@@ -106,9 +106,12 @@ hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void*
 // The non-rejected rows of a batch of R slots, in order: rmap[0..*count).
 hipError_t launch_compact_rows(int R, const uint8_t* rejected, int32_t* rmap, int32_t* count, hipStream_t st);
 // The non-rejected draft rows (draft_rows[0..D) in order): dmap[0..*count),
-// and qskip[s] = 0 for exactly those slots (1 elsewhere).
+// their draft indices dpos[0..*count) (draft_rows[dpos[m]] = dmap[m]), and
+// qskip[s] = 0 for exactly those slots (1 elsewhere).  With z set (bf16,
+// [D, d]), the rows of z at the other draft indices are zeroed (the fused
+// final norm writes the non-rejected ones only).
 hipError_t launch_draft_map(int R, int D, const int32_t* draft_rows, const uint8_t* rejected, int32_t* dmap,
-                            int32_t* count, uint8_t* qskip, hipStream_t st);
+                            int32_t* count, int32_t* dpos, uint8_t* qskip, void* z, int d, hipStream_t st);
 hipError_t launch_rmsnorm_expand(int rows, int d, const void* x, const void* gain, void* out, void* x_full,
                                  int K, float eps, hipStream_t st);
 
@@ -176,9 +179,11 @@ struct GemmArgs {
   // launch_mm): with nrm_out set, the product's split-K sum also normalises
   // every output row it writes, nrm_out[row] = bf16((x * rs) * nrm_gain) with
   // rs = rsqrt(mean(x^2) + norm_eps) over the stored (rounded) x, as
-  // rmsnorm_kernel would have.
+  // rmsnorm_kernel would have.  With nrm_rows set, compact row m's
+  // normalised row goes to nrm_out[nrm_rows[m]] instead.
   void* nrm_out;
   const void* nrm_gain;
+  const int32_t* nrm_rows;
 };
 // Whether a product of M rows can take its RMSNorm folded in (see GemmArgs):
 // bf16, at most 16 rows, K % 32 == 0, K / 16 <= kSsqMaxParts partial sums.

@@ -391,7 +391,8 @@ __global__ __launch_bounds__(1024) void compact_rows_kernel(int R, const uint8_t
 // rows, O product and MLP of the other slots are never read.  One workgroup.
 __global__ __launch_bounds__(1024) void draft_map_kernel(int R, int D, const int32_t* __restrict__ draft_rows,
                                                          const uint8_t* __restrict__ rej, int32_t* __restrict__ dmap,
-                                                         int32_t* __restrict__ count, uint8_t* __restrict__ qskip) {
+                                                         int32_t* __restrict__ count, int32_t* __restrict__ dpos,
+                                                         uint8_t* __restrict__ qskip, uint4* __restrict__ z, int zc) {
   __shared__ int s_w[16];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   for (int s = t; s < R; s += 1024) qskip[s] = 1;
@@ -416,16 +417,20 @@ __global__ __launch_bounds__(1024) void draft_map_kernel(int R, int D, const int
   for (int i = i0; i < i1; ++i)
     if (live(i)) {
       const int s = draft_rows[i];
+      dpos[at] = i;
       dmap[at++] = s;
       qskip[s] = 0;
+    } else if (z) {
+      for (int c = 0; c < zc; ++c) z[(long long)i * zc + c] = uint4{0u, 0u, 0u, 0u};
     }
   if (t == 1023) *count = base + inc;
 }
 
 hipError_t launch_draft_map(int R, int D, const int32_t* draft_rows, const uint8_t* rejected, int32_t* dmap,
-                            int32_t* count, uint8_t* qskip, hipStream_t st) {
-  if (R <= 0 || D <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(draft_map_kernel, dim3(1), dim3(1024), 0, st, R, D, draft_rows, rejected, dmap, count, qskip);
+                            int32_t* count, int32_t* dpos, uint8_t* qskip, void* z, int d, hipStream_t st) {
+  if (R <= 0 || D <= 0 || (z && (d <= 0 || d % 8))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(draft_map_kernel, dim3(1), dim3(1024), 0, st, R, D, draft_rows, rejected, dmap, count, dpos,
+                     qskip, (uint4*)z, z ? d / 8 : 0);
   return hipGetLastError();
 }
 

@@ -549,7 +549,7 @@ __global__ __launch_bounds__(256) void mm_resid_norm_kernel(GemmArgs g, int rows
     const float tot = ((s_ss[0] + s_ss[1]) + s_ss[2]) + s_ss[3];
     __syncthreads();  // s_ss is written again for the next row
     const float rs = rsqrtf(tot / float(g.N) + g.norm_eps);
-    uint16_t* ur = (uint16_t*)g.nrm_out + row * g.ldo;
+    uint16_t* ur = (uint16_t*)g.nrm_out + (g.nrm_rows ? (long long)g.nrm_rows[m] : row) * g.ldo;
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
       if (tid + 256 * j < nch) {
