@@ -647,6 +647,10 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
       g.rcount = nullptr;
     }
     ssq_out(g);
+    if (post_norm) {  // the first layer's attention norm (and the MASK rows' expansion) in its sum
+      norm_after(g, ctx->layers[0].attn_norm);
+      if (dd) g.nrm_xfull = ctx->x;
+    }
     if ((ds = dense(pe::A_FC, pe::B_PLAIN, pe::E_STORE, g, "fc")) != PE_OK) return ds;
   }
   for (int l = 0; l < k.layers; ++l) {
@@ -654,7 +658,8 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
     const bool first_dd = l == 0 && dd;
     const bool last_draft = draft_only && l == k.layers - 1;
     const bool fold_attn = fold && (l > 0 || !P.embed_input);  // the embedding gather writes no sums
-    if (!fold_attn && !(post_norm && l > 0)) {  // (after layer 0, the down product wrote it)
+    // (with post_norm the fc product, or after layer 0 the down product, wrote it)
+    if (!fold_attn && !(post_norm && (l > 0 || !P.embed_input))) {
       Timed tm(ctx, PE_PH_NORM);
       if (first_dd)
         PE_HIP(pe::launch_rmsnorm_expand(Rc, d, ctx->xc, L.attn_norm, ctx->u, ctx->x, Kc, k.rms_eps, st),

@@ -1648,6 +1648,7 @@ template <int EPI, int AL, int BMAP>
 static hipError_t run_bf16(const GemmArgs& g, int num_cus, hipStream_t st) {
   if (EPI != E_ARGMAX && (g.M > kMmMinRows || (g.M > kRowMapMinRows && EPI != E_SILU)))
     return launch_mm(AL, BMAP, EPI, g, num_cus, st);
+  if (g.nrm_out) return hipErrorInvalidValue;  // the fused following norm: large-batch kernels only
   if (g.dedup_k) return hipErrorInvalidValue;  // compact first-layer rows: large batches only
   const Variant v = pick(EPI, g.M, g.N, g.K, num_cus);
   if constexpr (EPI == E_ARGMAX) {

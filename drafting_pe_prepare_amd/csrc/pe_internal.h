@@ -180,10 +180,14 @@ struct GemmArgs {
   // every output row it writes, nrm_out[row] = bf16((x * rs) * nrm_gain) with
   // rs = rsqrt(mean(x^2) + norm_eps) over the stored (rounded) x, as
   // rmsnorm_kernel would have.  With nrm_rows set, compact row m's
-  // normalised row goes to nrm_out[nrm_rows[m]] instead.
+  // normalised row goes to nrm_out[nrm_rows[m]] instead.  A store product
+  // (E_STORE) takes it too (no residual); with dedup_k and nrm_xfull set, each
+  // stored row x also goes to its slots of the full layout,
+  // nrm_xfull[s] = x[dedup_row(s, dedup_k)].
   void* nrm_out;
   const void* nrm_gain;
   const int32_t* nrm_rows;
+  void* nrm_xfull;
 };
 // Whether a product of M rows can take its RMSNorm folded in (see GemmArgs):
 // bf16, at most 16 rows, K % 32 == 0, K / 16 <= kSsqMaxParts partial sums.

@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) void mm_reduce_kernel(GemmArgs g, int rows, in
 // split the row the product stored) stays in registers, its squares are
 // summed over the workgroup in a fixed order, and the normalised row goes out
 // beside it.
-template <int MAXC>
+template <int EPI, int MAXC>
 __global__ __launch_bounds__(256) void mm_resid_norm_kernel(GemmArgs g, int rows, int rpr, int BM, int ntiles,
                                                             int slots, int cap_splits) {
   __shared__ float s_ss[4];
@@ -507,12 +507,14 @@ __global__ __launch_bounds__(256) void mm_resid_norm_kernel(GemmArgs g, int rows
         f[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
       }
     };
+    uint4 xp[MAXC];  // the stored row, as bf16
     if (KS > 1) {
       uint4 rv[MAXC];
       long long off[2 * MAXC];
 #pragma unroll
       for (int j = 0; j < MAXC; ++j) {
-        rv[j] = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + row * g.ldo + 8 * cc[j]);
+        if constexpr (EPI == E_RESID)
+          rv[j] = *reinterpret_cast<const uint4*>((const uint16_t*)g.resid + row * g.ldo + 8 * cc[j]);
         off[2 * j] = (long long)m * g.N + 8 * cc[j];
         off[2 * j + 1] = off[2 * j] + 4;
       }
@@ -521,26 +523,41 @@ __global__ __launch_bounds__(256) void mm_resid_norm_kernel(GemmArgs g, int rows
 #pragma unroll
       for (int j = 0; j < MAXC; ++j) {
         if (tid + 256 * j < nch) {
-          float r[8];
-          unpack(rv[j], r);
-          const float v[8] = {sm[2 * j].x + r[0],     sm[2 * j].y + r[1],     sm[2 * j].z + r[2],
-                              sm[2 * j].w + r[3],     sm[2 * j + 1].x + r[4], sm[2 * j + 1].y + r[5],
-                              sm[2 * j + 1].z + r[6], sm[2 * j + 1].w + r[7]};
-          const uint4 xv = uint4{f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
-          *reinterpret_cast<uint4*>(xr + 8 * cc[j]) = xv;
-          unpack(xv, x[j]);
+          float v[8] = {sm[2 * j].x,     sm[2 * j].y,     sm[2 * j].z,     sm[2 * j].w,
+                        sm[2 * j + 1].x, sm[2 * j + 1].y, sm[2 * j + 1].z, sm[2 * j + 1].w};
+          if constexpr (EPI == E_RESID) {
+            float r[8];
+            unpack(rv[j], r);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) ss += x[j][t] * x[j][t];
+            for (int t = 0; t < 8; ++t) v[t] += r[t];
+          }
+          xp[j] = uint4{f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
+          *reinterpret_cast<uint4*>(xr + 8 * cc[j]) = xp[j];
         }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < MAXC; ++j) {
-        if (tid + 256 * j < nch) {
-          unpack(*reinterpret_cast<const uint4*>(xr + 8 * cc[j]), x[j]);  // stored by the product's own epilogue
+      for (int j = 0; j < MAXC; ++j)
+        if (tid + 256 * j < nch) xp[j] = *reinterpret_cast<const uint4*>(xr + 8 * cc[j]);  // the product stored it
+    }
 #pragma unroll
-          for (int t = 0; t < 8; ++t) ss += x[j][t] * x[j][t];
-        }
+    for (int j = 0; j < MAXC; ++j) {
+      if (tid + 256 * j < nch) {
+        unpack(xp[j], x[j]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ss += x[j][t] * x[j][t];
+      }
+    }
+    if (g.dedup_k > 0 && g.nrm_xfull) {
+      // compact row m of a MASK-deduplicated layer: its slot, or the
+      // request's K-1 MASK slots for its last row
+      const int K = g.dedup_k, r = m / (K + 2), jj = m - r * (K + 2);
+      const int s0 = r * 2 * K + jj, ns = jj == K + 1 ? K - 1 : 1;
+      for (int t = 0; t < ns; ++t) {
+        uint16_t* xf = (uint16_t*)g.nrm_xfull + (long long)(s0 + t) * g.ldo;
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j)
+          if (tid + 256 * j < nch) *reinterpret_cast<uint4*>(xf + 8 * cc[j]) = xp[j];
       }
     }
     ss = wave_sum(ss);
@@ -610,11 +627,12 @@ static hipError_t mm_dense(const GemmArgs& g, int num_cus, hipStream_t st) {
                      dim3(64 * WM * WN), 0, st, g, ntiles, slots, cap_splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (EPI == E_RESID) {
+  if constexpr (EPI == E_RESID || EPI == E_STORE) {
     if (g.nrm_out) {  // the split sum (or, unsplit, the stored rows) and the following RMSNorm
-      if (g.N % 8 || g.N > 2048 * kNormMaxChunks || g.ldo != g.N) return hipErrorInvalidValue;
+      if (g.N % 8 || g.N > 2048 * kNormMaxChunks || g.ldo != g.N || (g.nrm_xfull && g.rmap))
+        return hipErrorInvalidValue;
       const long long blocks = std::min<long long>(g.M, 16LL * num_cus);
-      hipLaunchKernelGGL(mm_resid_norm_kernel<kNormMaxChunks>, dim3(unsigned(blocks)), dim3(256), 0, st, g, g.M,
+      hipLaunchKernelGGL((mm_resid_norm_kernel<EPI, kNormMaxChunks>), dim3(unsigned(blocks)), dim3(256), 0, st, g, g.M,
                          g.rpr, BM, ntiles, slots, cap_splits);
       return hipGetLastError();
     }
