@@ -560,15 +560,6 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   g0.part_cap = ctx->splitk_cap;
   g0.nact = ctx->nact;
   g0.rpr = S;
-  // the dense products above 64 rows compute only the non-rejected slots: a
-  // rejected slot's outputs are never read (no KV write, no attention, not a
-  // draft row); the map comes from the batch's rejected mask
-  if (dt == PE_BF16 && R > pe::kRowMapMinRows) {
-    Timed tm(ctx, PE_PH_FC);
-    PE_HIP(pe::launch_compact_rows(R, P.rej, ctx->rmap, ctx->rmap + R, st), "row map");
-    g0.rmap = ctx->rmap;
-    g0.rcount = ctx->rmap + R;
-  }
 
   // The last layer after its QKV product (which writes every valid slot's
   // KV): only the draft rows feed the LM head, so attention keeps only their
@@ -581,16 +572,21 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   // after down, and after the last layer's down on the draft rows the final
   // norm, into z at each row's draft index), so those norms need no launch of
   // their own.  The draft rows it does not compute (rejected: padded
-  // requests) get zero rows in z.
-  // (above 64 rows no norm is folded into the small-batch products)
+  // requests) get zero rows in z.  (Above 64 rows no norm is folded into the
+  // small-batch products.)
   const bool post_norm = dt == PE_BF16 && R > pe::kRowMapMinRows && d <= 4096;
   const bool final_fused = post_norm && draft_only;
   int32_t* const dpos = ctx->dmap + D + 1;
-  if (draft_only) {
+  // the dense products above 64 rows compute only the non-rejected slots: a
+  // rejected slot's outputs are never read (no KV write, no attention, not a
+  // draft row); the map comes from the batch's rejected mask
+  if (dt == PE_BF16 && R > pe::kRowMapMinRows) {
     Timed tm(ctx, PE_PH_FC);
-    PE_HIP(pe::launch_draft_map(R, D, P.draft_rows, P.rej, ctx->dmap, ctx->dmap + D, dpos, ctx->qskip,
-                                final_fused ? ctx->z : nullptr, d, st),
-           "draft map");
+    PE_HIP(pe::launch_row_maps(R, P.rej, ctx->rmap, ctx->rmap + R, D, draft_only ? P.draft_rows : nullptr, ctx->dmap,
+                               ctx->dmap + D, dpos, ctx->qskip, final_fused ? ctx->z : nullptr, d, st),
+           "row maps");
+    g0.rmap = ctx->rmap;
+    g0.rcount = ctx->rmap + R;
   }
 
   // RMSNorm folded into the small-batch products (at most 16 rows: every dense

@@ -103,15 +103,16 @@ hipError_t launch_rmsnorm(int dtype, int rows, int d, const void* x, const void*
 // bf16 RMSNorm of the compact rows of a MASK-deduplicated first layer (K+2
 // per request, see GemmArgs::dedup_k) that also writes each raw row x[m] to
 // its slots of the full layout: x_full[s] = x[dedup_row(s, K)] for all B*2K s.
-// The non-rejected rows of a batch of R slots, in order: rmap[0..*count).
-hipError_t launch_compact_rows(int R, const uint8_t* rejected, int32_t* rmap, int32_t* count, hipStream_t st);
-// The non-rejected draft rows (draft_rows[0..D) in order): dmap[0..*count),
-// their draft indices dpos[0..*count) (draft_rows[dpos[m]] = dmap[m]), and
-// qskip[s] = 0 for exactly those slots (1 elsewhere).  With z set (bf16,
-// [D, d]), the rows of z at the other draft indices are zeroed (the fused
-// final norm writes the non-rejected ones only).
-hipError_t launch_draft_map(int R, int D, const int32_t* draft_rows, const uint8_t* rejected, int32_t* dmap,
-                            int32_t* count, int32_t* dpos, uint8_t* qskip, void* z, int d, hipStream_t st);
+// One launch, two maps.  The non-rejected rows of a batch of R slots, in
+// order: rmap[0..*rcount).  With draft_rows set, also the non-rejected draft
+// rows (draft_rows[0..D) in order): dmap[0..*dcount), their draft indices
+// dpos[0..*dcount) (draft_rows[dpos[m]] = dmap[m]), and qskip[s] = 0 for
+// exactly those slots (1 elsewhere); with z set too (bf16, [D, d]), the rows
+// of z at the other draft indices are zeroed (the fused final norm writes the
+// non-rejected ones only).
+hipError_t launch_row_maps(int R, const uint8_t* rejected, int32_t* rmap, int32_t* rcount, int D,
+                           const int32_t* draft_rows, int32_t* dmap, int32_t* dcount, int32_t* dpos, uint8_t* qskip,
+                           void* z, int d, hipStream_t st);
 hipError_t launch_rmsnorm_expand(int rows, int d, const void* x, const void* gain, void* out, void* x_full,
                                  int K, float eps, hipStream_t st);
 

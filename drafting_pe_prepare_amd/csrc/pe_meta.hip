@@ -362,8 +362,8 @@ __global__ __launch_bounds__(256) void verify_kernel(int B, int K, const int32_t
 // no KV write, attends to nothing and is no draft row).  One 1024-thread
 // workgroup: thread t counts its contiguous run of slots, a block-wide scan
 // gives each run's first output index, then the runs are written.
-__global__ __launch_bounds__(1024) void compact_rows_kernel(int R, const uint8_t* __restrict__ rej,
-                                                            int32_t* __restrict__ rmap, int32_t* __restrict__ count) {
+__device__ void compact_rows(int R, const uint8_t* __restrict__ rej, int32_t* __restrict__ rmap,
+                             int32_t* __restrict__ count) {
   __shared__ int s_w[16];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int per = (R + 1023) / 1024, r0 = min(R, t * per), r1 = min(R, r0 + per);
@@ -389,10 +389,9 @@ __global__ __launch_bounds__(1024) void compact_rows_kernel(int R, const uint8_t
 // those slots.  Only the draft rows feed the LM head, so after the last
 // layer's QKV product (which writes every valid slot's KV) the attention
 // rows, O product and MLP of the other slots are never read.  One workgroup.
-__global__ __launch_bounds__(1024) void draft_map_kernel(int R, int D, const int32_t* __restrict__ draft_rows,
-                                                         const uint8_t* __restrict__ rej, int32_t* __restrict__ dmap,
-                                                         int32_t* __restrict__ count, int32_t* __restrict__ dpos,
-                                                         uint8_t* __restrict__ qskip, uint4* __restrict__ z, int zc) {
+__device__ void draft_map(int R, int D, const int32_t* __restrict__ draft_rows, const uint8_t* __restrict__ rej,
+                          int32_t* __restrict__ dmap, int32_t* __restrict__ count, int32_t* __restrict__ dpos,
+                          uint8_t* __restrict__ qskip, uint4* __restrict__ z, int zc) {
   __shared__ int s_w[16];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   for (int s = t; s < R; s += 1024) qskip[s] = 1;
@@ -426,17 +425,25 @@ __global__ __launch_bounds__(1024) void draft_map_kernel(int R, int D, const int
   if (t == 1023) *count = base + inc;
 }
 
-hipError_t launch_draft_map(int R, int D, const int32_t* draft_rows, const uint8_t* rejected, int32_t* dmap,
-                            int32_t* count, int32_t* dpos, uint8_t* qskip, void* z, int d, hipStream_t st) {
-  if (R <= 0 || D <= 0 || (z && (d <= 0 || d % 8))) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(draft_map_kernel, dim3(1), dim3(1024), 0, st, R, D, draft_rows, rejected, dmap, count, dpos,
-                     qskip, (uint4*)z, z ? d / 8 : 0);
-  return hipGetLastError();
+// Both maps in one launch: workgroup 0 the row map, workgroup 1 (when the
+// draft map is asked for) the draft map; they read the same mask and write
+// disjoint outputs.
+__global__ __launch_bounds__(1024) void row_maps_kernel(int R, const uint8_t* __restrict__ rej,
+                                                        int32_t* __restrict__ rmap, int32_t* __restrict__ rcount,
+                                                        int D, const int32_t* __restrict__ draft_rows,
+                                                        int32_t* __restrict__ dmap, int32_t* __restrict__ dcount,
+                                                        int32_t* __restrict__ dpos, uint8_t* __restrict__ qskip,
+                                                        uint4* __restrict__ z, int zc) {
+  if (blockIdx.x == 0) compact_rows(R, rej, rmap, rcount);
+  else draft_map(R, D, draft_rows, rej, dmap, dcount, dpos, qskip, z, zc);
 }
 
-hipError_t launch_compact_rows(int R, const uint8_t* rejected, int32_t* rmap, int32_t* count, hipStream_t st) {
-  if (R <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, st, R, rejected, rmap, count);
+hipError_t launch_row_maps(int R, const uint8_t* rejected, int32_t* rmap, int32_t* rcount, int D,
+                           const int32_t* draft_rows, int32_t* dmap, int32_t* dcount, int32_t* dpos, uint8_t* qskip,
+                           void* z, int d, hipStream_t st) {
+  if (R <= 0 || (draft_rows && D <= 0) || (z && (d <= 0 || d % 8))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_maps_kernel, dim3(draft_rows ? 2 : 1), dim3(1024), 0, st, R, rejected, rmap, rcount, D,
+                     draft_rows, dmap, dcount, dpos, qskip, (uint4*)z, z ? d / 8 : 0);
   return hipGetLastError();
 }
 
