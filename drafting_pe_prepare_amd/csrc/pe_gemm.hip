@@ -1080,14 +1080,30 @@ void lmhead_ring_kernel(GemmArgs g) {
   }
   const uint16_t* Wp = (const uint16_t*)g.Wp + 8 * l;
   const uint32_t base = lds_addr(ring);
-  auto issue = [&](int slot, int gs) {
-    const int c = gs / ksteps, s = gs - c * ksteps;
+  // The DMAs run through the steps in order (the prologue's, then one step
+  // ahead of each k-step), so the issue position (chunk ic, k-step is) is
+  // kept as counters, and each DMA's source at k-step 0 of the chunk (src0)
+  // and its advance per k-step (32 elements of a row, or one 512-element
+  // weight block) are set once per chunk: no division on the per-step path.
+  int ic = 0, is = 0;
+  const uint16_t* src0[Q];
+  int adv[Q];
+  auto set_chunk = [&](int c) {
     const int c0 = chunk_first(c), c1 = chunk_first(c + 1);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-      const void* src = wu_[q] < 0 ? (const void*)(asrc[q] + 32 * s)
-                                   : (const void*)(Wp + ((long long)min(c0 + wu_[q], c1 - 1) * ksteps + s) * 512);
-      dma16(src, base + slot * STAGE + dst[q]);
+      const bool isa = wu_[q] < 0;
+      src0[q] = isa ? asrc[q] : Wp + (long long)min(c0 + wu_[q], c1 - 1) * ksteps * 512;
+      adv[q] = isa ? 32 : 512;
+    }
+  };
+  set_chunk(0);
+  auto issue = [&](int slot) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) dma16(src0[q] + (long long)is * adv[q], base + slot * STAGE + dst[q]);
+    if (++is == ksteps) {
+      is = 0;
+      if (++ic < nch) set_chunk(ic);
     }
   };
   // at most n later steps of this wave's DMAs still in flight
@@ -1163,7 +1179,7 @@ void lmhead_ring_kernel(GemmArgs g) {
   // prologue: every slot filled, step 0 read
 #pragma unroll
   for (int j = 0; j < S; ++j)
-    if (j < total) issue(j, j);
+    if (j < total) issue(j);
   wait_steps(total - 1 < S - 1 ? total - 1 : S - 1);
   asm volatile("s_barrier" ::: "memory");
   read(0, ring);
@@ -1176,7 +1192,7 @@ void lmhead_ring_kernel(GemmArgs g) {
       // everyone's part has landed, and everyone has read step gs's slot
       // (before this barrier), which the next DMA refills
       asm volatile("s_barrier" ::: "memory");
-      if (gs + S < total) issue(slot, gs + S);
+      if (gs + S < total) issue(slot);  // step gs + S
       slot = slot + 1 == S ? 0 : slot + 1;
       read(buf ^ 1, ring + slot * STAGE);
     }
