@@ -34,10 +34,16 @@
 #ifndef PE_ATTN_MIN_STEPS
 #define PE_ATTN_MIN_STEPS 2  // shortest range per workgroup (64-position steps)
 #endif
+#ifndef PE_ATTN_LAZY
+#define PE_ATTN_LAZY 1
+#endif
 
 namespace pe {
 
 constexpr int kMaxB = kAttnMaxB;
+// Largest excess (base 2) of a score over the running max that leaves the
+// max in place as the exponent's reference (p up to 2^8).
+constexpr float kLazyMax = 8.f;
 
 // Orders this wave's LDS writes before its later LDS reads (and the reverse)
 // without a workgroup barrier.
@@ -324,10 +330,31 @@ void attn_partial_kernel(AttnArgs a) {
               mloc = fmaxf(mloc, v[t]);
             }
           }
-          mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-          mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-          const float mnew = fmaxf(m[qq], mloc * sl2);
-          const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+          float mref;
+#if PE_ATTN_LAZY
+          // (not with four query tiles per wave: the extra live values spill)
+          if (QPW <= 2 && !__ballot(mloc * sl2 > m[qq] + kLazyMax)) {
+            // no score of the half exceeds the running max by more than
+            // kLazyMax (base 2): it stays the exponent's reference, so p <=
+            // 2^kLazyMax, and neither the maximum across the query's lanes
+            // nor a rescale is needed (a lane whose scores are all masked so
+            // far keeps -inf and a reference of 0, its p being 0)
+            mref = m[qq] == -INFINITY ? 0.f : m[qq];
+          } else
+#endif
+          {
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            const float mnew = fmaxf(m[qq], mloc * sl2);
+            mref = (mnew == -INFINITY) ? 0.f : mnew;
+            if (__ballot(mnew != m[qq])) {  // some query's running max moved: rescale
+              const float alpha = __builtin_amdgcn_exp2f(m[qq] - mref);
+              osum[qq] = osum[qq] * alpha;
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) o[qq][dt] = o[qq][dt] * alpha;
+            }
+            m[qq] = mnew;
+          }
           // P = hi + lo, both bf16: the PV product sees P to ~16 bits, and so
           // does the row sum, taken by the same MFMAs on an all-ones tile.
           // exp2 of a non-positive argument: v_exp_f32 flushes results below
@@ -340,13 +367,6 @@ void attn_partial_kernel(AttnArgs a) {
             ph[jj] = f2bf2(p0, p1);
             pl[jj] = f2bf2(p0 - __uint_as_float(ph[jj] << 16), p1 - __uint_as_float(ph[jj] & 0xFFFF0000u));
           }
-          if (__ballot(mnew != m[qq])) {  // some query's running max moved: rescale
-            const float alpha = __builtin_amdgcn_exp2f(m[qq] - mref);
-            osum[qq] = osum[qq] * alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[qq][dt] = o[qq][dt] * alpha;
-          }
-          m[qq] = mnew;
           const uint4 pfh = {ph[0], ph[1], ph[2], ph[3]};
           const uint4 pfl = {pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
