@@ -8,7 +8,7 @@ Two relaxations of the stated criteria, on record (pe_gpu):
     max(1e-2, 2 x the measured max logit error) (about 0.03 at the 20B
     shapes); in the band (1e-2, 2 err] two logits within the error bound can
     change order, so there the GPU token must be near-maximal instead.  The
-    band is counted (303 rows over the GPU suite, 1 drafting the other
+    band is counted (296 rows over the GPU suite, 1 drafting the other
     near-maximal token) and printed at the end of the session;
   * deeper bf16 drafters are checked at 2e-2 x sqrt(layers); the 4-layer
     K-sweep drafter measures 2.7-3.2% of RMS and misses the stated 2e-2."""
