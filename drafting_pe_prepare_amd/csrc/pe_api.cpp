@@ -19,6 +19,14 @@
 #include "pe.h"
 #include "pe_internal.h"
 
+// Products of more rows than this write the following RMSNorm in their
+// split-K sums on the large-batch kernels (up to 16 rows the small-batch
+// products fold it in instead).  From 17 rows, against separate norm
+// launches: K sweep K = 1 (32 rows) 504 -> 482 us.
+#ifndef PE_POSTNORM_MIN_ROWS
+#define PE_POSTNORM_MIN_ROWS 16
+#endif
+
 
 namespace {
 
@@ -566,15 +574,15 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   // queries and the O product, MLP norm and MLP run on their rows alone
   // (through a row map of the non-rejected draft rows).
   const bool draft_only = dt == PE_BF16 && R > pe::kRowMapMinRows && D > pe::kRowMapMinRows && P.draft_rows;
-  // Above 64 rows the O and down products run on the large-batch kernels,
+  // Above 16 rows the fc, O and down products run on the large-batch kernels,
   // whose split-K sum writes each output row whole: it also writes the
   // following RMSNorm (the MLP norm after O, the next layer's attention norm
   // after down, and after the last layer's down on the draft rows the final
   // norm, into z at each row's draft index), so those norms need no launch of
   // their own.  The draft rows it does not compute (rejected: padded
-  // requests) get zero rows in z.  (Above 64 rows no norm is folded into the
+  // requests) get zero rows in z.  (Above 16 rows no norm is folded into the
   // small-batch products.)
-  const bool post_norm = dt == PE_BF16 && R > pe::kRowMapMinRows && d <= 4096;
+  const bool post_norm = dt == PE_BF16 && R > PE_POSTNORM_MIN_ROWS && d <= 4096;
   const bool final_fused = post_norm && draft_only;
   int32_t* const dpos = ctx->dmap + D + 1;
   // the dense products above 64 rows compute only the non-rejected slots: a
@@ -608,7 +616,10 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
 
   // a dense GEMM with its fused epilogue
   auto dense = [&](int aload, int bmap, int epi, const pe::GemmArgs& g, const char* what) -> pe_status {
-    PE_HIP(pe::launch_gemm(dt, aload, bmap, epi, g, ctx->num_cus, st), what);
+    if (g.nrm_out)  // the following norm in the split-K sum: the large-batch kernels at any row count
+      PE_HIP(pe::launch_mm(aload, bmap, epi, g, ctx->num_cus, st), what);
+    else
+      PE_HIP(pe::launch_gemm(dt, aload, bmap, epi, g, ctx->num_cus, st), what);
     return PE_OK;
   };
   pe_status ds = PE_OK;
