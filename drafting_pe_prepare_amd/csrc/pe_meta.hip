@@ -268,7 +268,7 @@ hipError_t launch_prefill_prepare(const PrefillArgs& a, hipStream_t st) {
 // One workgroup per request: wave 0 prepares the request's slots while every
 // thread loads its first PG_CHUNKS 16-byte chunks of the request's 2K
 // draft-hidden rows (source row r(K+1)+j for copied slot j, h_shared for the
-// MASK slots); after the verdict the rows are stored (an invalid request's
+// MASK slots); once the request is validated the rows are stored (an invalid request's
 // copied slots take h_shared, as its -1 map says), and chunks beyond the first
 // batch are copied in a loop.  One workgroup per request rather than per slot:
 // a launch of many small workgroups is limited by how fast they are
