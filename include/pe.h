@@ -182,10 +182,11 @@ pe_status pe_gather_hidden(pe_ctx* ctx, int32_t B, const pe_batch* batch,
  *   V cache layer l: [num_kv_blocks, n_kv_heads, head_dim, block_size]
  *                    (d-major inside a block)
  * draft_tokens [B*K] int32 out (t_1..t_K per request, -1 for padding).
- * logits: NULL, or [B*K, vocab] float32 out (debug/parity; costs bandwidth).
+ * logits: NULL, or [B*K, vocab] float32 out (debug/parity; costs bandwidth);
+ * the rows of a padded request are unspecified.
  * batch must come from pe_prepare and draft_hidden from pe_gather_hidden:
  * the K-1 MASK slots of a request then carry the same input (emb(mask),
- * h_shared), and from 256 bf16 forward rows with K >= 3 the first layer's fc
+ * h_shared), and in bf16 with K >= 3 and B*(K+2) > 64 the first layer's fc
  * and QKV products compute it once per request (RoPE and the KV write still
  * run per slot). */
 pe_status pe_draft_forward(pe_ctx* ctx, int32_t B, const pe_batch* batch,
