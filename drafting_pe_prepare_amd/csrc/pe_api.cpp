@@ -573,7 +573,7 @@ static pe_status forward_pass(pe_ctx* ctx, const Pass& P, const int32_t* block_t
   // KV): only the draft rows feed the LM head, so attention keeps only their
   // queries and the O product, MLP norm and MLP run on their rows alone
   // (through a row map of the non-rejected draft rows).
-  const bool draft_only = dt == PE_BF16 && R > pe::kRowMapMinRows && D > pe::kRowMapMinRows && P.draft_rows;
+  const bool draft_only = dt == PE_BF16 && R > pe::kRowMapMinRows && P.draft_rows;
   // Above 16 rows the fc, O and down products run on the large-batch kernels,
   // whose split-K sum writes each output row whole: it also writes the
   // following RMSNorm (the MLP norm after O, the next layer's attention norm
